@@ -1,0 +1,273 @@
+/*
+ * pkv.h - C ABI of libpkv: paged KV cache and paged attention on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The KV cache of every sequence is split into fixed-size blocks of
+ * `block_size` tokens that sit anywhere in one global pool; a per-sequence
+ * block table maps logical block j to a physical block id.  Pages cited:
+ *   [kongchang] kongchang.com, "vLLM架构深度解析：PagedAttention如何实现高吞吐LLM推理"
+ *   [cnnetsun]  cnnetsun.cn/a/1845762, "别再让GPU内存拖后腿了：vLLM的PagedAttention如何像操作系统一样管理KV Cache"
+ *   [aisoosoo]  aisoosoo.com, "vLLM：大模型推理的加速引擎，PagedAttention 颠覆显存管理"
+ *   [nxbn]      m.nxbn.cn/news/200425 (VLLM walkthrough, numbered sections 一..六)
+ *
+ * Conventions for every call:
+ *   - Every call returns a pkv_status; 0 is success.  On failure
+ *     pkv_last_error() returns a message for the calling thread.  No C++
+ *     exception crosses this boundary and no call aborts the process.
+ *   - "host" pointers are CPU memory owned by the caller; "device" pointers
+ *     are GPU memory (for example torch tensors) owned by the caller.  The
+ *     library keeps no pointer after a call returns and allocates no device
+ *     memory: scratch space is a caller-provided workspace.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Device
+ *     calls only enqueue work; they return before it finishes.
+ *   - Device-side layouts (all contiguous, row-major):
+ *       cache   k_cache / v_cache   [num_blocks][num_kv_heads][block_size][head_dim]
+ *       scales  k_scale / v_scale   float [num_blocks][num_kv_heads] (int8 only)
+ *       tables  block_tables        int32 [num_seqs][max_blocks_per_seq], -1 padded
+ *     Position p of a sequence lives in block table[p / block_size] at row
+ *     p % block_size ([cnnetsun] §2.1; [nxbn] §2.2); slot = block *
+ *     block_size + row addresses one token row of the pool.
+ *   - Arguments are validated on the host before anything is enqueued.  With
+ *     the environment variable PKV_VALIDATE=1 the device index arrays
+ *     (slots, tables, lengths, copy pairs) are also copied back and checked,
+ *     which synchronises the stream; kernels in any case skip table entries
+ *     and slots outside the pool instead of reading or writing out of bounds.
+ *   - The block manager is not thread-safe; device calls may be made from any
+ *     thread.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t pkv_status;
+#define PKV_OK 0
+#define PKV_ERR_INVALID 1        /* bad argument or state; nothing changed       */
+#define PKV_ERR_OUT_OF_BLOCKS 2  /* pool cannot satisfy the request; nothing changed */
+#define PKV_ERR_UNSUPPORTED 3    /* valid but not implemented (dtype, head_dim...) */
+#define PKV_ERR_DEVICE 4         /* a HIP call failed                              */
+#define PKV_ERR_INTERNAL 5
+
+typedef int32_t pkv_dtype;
+#define PKV_F32 0
+#define PKV_F16 1
+#define PKV_BF16 2
+#define PKV_I8 3   /* KV storage only: symmetric codes with per-(block, kv head) fp32 scales */
+
+/* Decode kernel choice. */
+#define PKV_ALGO_AUTO 0
+#define PKV_ALGO_WAVE 1   /* wavefront dot products + shuffle reductions (any dtype) */
+#define PKV_ALGO_MFMA 2   /* matrix cores over a query-head group (bf16/f16 q)      */
+
+/* Thread-local description of the last failure of this thread. */
+const char* pkv_last_error(void);
+const char* pkv_version(void);
+
+/* ------------------------------------------------------------------------
+ * Block manager (host).  A fixed pool of `num_blocks` blocks with a free list
+ * used as a stack and a reference count per block ([cnnetsun] §2.1 and §2.2;
+ * [kongchang] section "KV Cache内存共享").  Blocks are taken only when tokens
+ * arrive, so a sequence of n tokens holds ceil(n / block_size) blocks
+ * ([kongchang] section "PagedAttention带来的性能收益"), and return to the
+ * pool when their count reaches zero ([nxbn] §2.3).
+ * ---------------------------------------------------------------------- */
+typedef struct pkv_bm pkv_bm;
+
+/* init_free_order: host int32[num_blocks], a permutation of 0..num_blocks-1
+ * giving the initial free list bottom-to-top (allocation pops from the top,
+ * i.e. the end), or NULL for 0..num_blocks-1.  *out receives the handle,
+ * which the caller releases with pkv_bm_destroy.  INVALID for a non-positive
+ * size or a bad permutation. */
+pkv_status pkv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* init_free_order,
+                         pkv_bm** out);
+void pkv_bm_destroy(pkv_bm* bm);
+
+/* Pop n blocks (refcount 1 each); ids_out: host int32[n] in pop order.
+ * OUT_OF_BLOCKS (state unchanged) when fewer than n are free. */
+pkv_status pkv_bm_alloc(pkv_bm* bm, int32_t n, int32_t* ids_out);
+/* incref needs an allocated block; decref pushes the block back on the free
+ * list when its count reaches 0.  INVALID for an unknown or free block. */
+pkv_status pkv_bm_incref(pkv_bm* bm, int32_t block);
+pkv_status pkv_bm_decref(pkv_bm* bm, int32_t block);
+int32_t pkv_bm_num_free(const pkv_bm* bm);
+/* free_list: host int32[num_blocks] (bottom to top, *free_len entries used);
+ * refcounts: host int32[num_blocks].  Either may be NULL. */
+pkv_status pkv_bm_get_state(const pkv_bm* bm, int32_t* free_list, int32_t* free_len,
+                            int32_t* refcounts);
+
+typedef struct pkv_bm_stats {
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t free_blocks;
+  int32_t used_blocks;     /* refcount > 0 */
+  int32_t shared_blocks;   /* refcount > 1 */
+  int32_t num_seqs;
+  int64_t logical_blocks;  /* sum over live sequences of their table lengths */
+  int64_t tokens;          /* sum over live sequences of their lengths */
+  int64_t waste_slots;     /* logical_blocks * block_size - tokens */
+} pkv_bm_stats;
+/* Usage figures for monitoring ([cnnetsun] §4.2 lists page utilisation and
+ * share ratio; [kongchang] section "显存浪费的三种形式" names the waste). */
+pkv_status pkv_bm_stats_get(const pkv_bm* bm, pkv_bm_stats* out);
+
+/* ------------------------------------------------------------------------
+ * Sequences (host).  Sequence ids count up from 0 and are never reused.
+ * ---------------------------------------------------------------------- */
+/* New sequence holding num_tokens positions (ceil(num_tokens/block_size)
+ * blocks, logical order = pop order).  OUT_OF_BLOCKS leaves no trace. */
+pkv_status pkv_seq_create(pkv_bm* bm, int32_t num_tokens, int64_t* seq_out);
+/* Child sharing every block of the parent (each block's count + 1): parallel
+ * sampling and beam search share history until they diverge ([kongchang]
+ * section "KV Cache内存共享"). */
+pkv_status pkv_seq_fork(pkv_bm* bm, int64_t parent, int64_t* child_out);
+/* Append num_tokens positions; slots_out: host int32[num_tokens] receives
+ * their slots.  If the partly filled tail block is shared (count > 1) it is
+ * first replaced by a new block (copy-on-write): *cow_src / *cow_dst receive
+ * (shared block, new block), which the caller must copy with
+ * pkv_copy_blocks before writing the new rows; otherwise both are -1.  A full
+ * tail never needs a copy.  All-or-nothing: OUT_OF_BLOCKS changes nothing. */
+pkv_status pkv_seq_append(pkv_bm* bm, int64_t seq, int32_t num_tokens, int32_t* slots_out,
+                          int32_t* cow_src, int32_t* cow_dst);
+/* One new position for each of n distinct sequences, handled in the order
+ * given (so of k beams sharing a partly filled tail the first k-1 copy and
+ * the last writes in place).  slots_out: host int32[n]; cow_pairs_out: host
+ * int32[n][2] receives *num_cow_out (src, dst) pairs.  All-or-nothing. */
+pkv_status pkv_seq_append_batch(pkv_bm* bm, const int64_t* seqs, int32_t n, int32_t* slots_out,
+                                int32_t* cow_pairs_out, int32_t* num_cow_out);
+/* Slots of positions [start, start+count) of a sequence (host int32[count]). */
+pkv_status pkv_seq_slots(const pkv_bm* bm, int64_t seq, int32_t start, int32_t count,
+                         int32_t* slots_out);
+pkv_status pkv_seq_len(const pkv_bm* bm, int64_t seq, int32_t* len_out);
+/* Drop a sequence: decref its blocks in logical order. */
+pkv_status pkv_seq_free(pkv_bm* bm, int64_t seq);
+/* Block tables and lengths of n sequences: tables_out host
+ * int32[n][max_blocks] (-1 padded), lens_out host int32[n].  INVALID if a
+ * table is longer than max_blocks. */
+pkv_status pkv_seq_export(const pkv_bm* bm, const int64_t* seqs, int32_t n, int32_t max_blocks,
+                          int32_t* tables_out, int32_t* lens_out);
+
+/* ------------------------------------------------------------------------
+ * reshape_and_cache (device).  Only the new tokens' K/V are computed each
+ * step and appended to the cache ([nxbn] section 一); each token's row goes to
+ * the slot the block table gives it ([nxbn] §2.2).
+ *   key, value    device [num_tokens][num_kv_heads][head_dim] in `dtype`,
+ *                 consecutive tokens `key_stride` / `value_stride` elements
+ *                 apart (0 = num_kv_heads * head_dim, i.e. contiguous)
+ *   slot_mapping  device int32[num_tokens]; a negative slot skips the row.
+ *                 Slots must be distinct (validated with PKV_VALIDATE=1).
+ *   dtype         F32, F16 or BF16 (cache and inputs share it); the copy is
+ *                 bit-exact.
+ * ---------------------------------------------------------------------- */
+pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                                 const int32_t* slot_mapping, int32_t num_tokens,
+                                 int64_t key_stride, int64_t value_stride, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                 pkv_dtype dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * copy_blocks (device): the data copy of copy-on-write ([kongchang] section
+ * "KV Cache内存共享").  For each pair (src, dst): K[dst] = K[src],
+ * V[dst] = V[src], and for I8 storage k_scale[dst] = k_scale[src], same for
+ * v_scale (scales may be NULL otherwise).
+ *   pairs   device int32[num_pairs][2].  Destinations must be distinct and
+ *           never a source of the same call (validated with PKV_VALIDATE=1).
+ * Bit-exact. */
+pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                           const int32_t* pairs, int32_t num_pairs, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                           pkv_dtype dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Paged decode attention (device).  One query token per sequence, at
+ * position context_lens[s] - 1, attends keys [0, context_lens[s]) (the
+ * current token's K/V is already in the cache).  For each table entry the
+ * query is scored against that block, the scores of all blocks take one
+ * softmax after scaling, and the blocks' value rows are summed with those
+ * weights ([cnnetsun] §3.1).  Query head h reads KV head h / (Hq / Hkv).
+ *   out            device [num_seqs][num_q_heads][head_dim] in out_dtype
+ *                  (F32, or the q dtype); rows with context 0 are zero.
+ *   q              device [num_seqs][num_q_heads][head_dim], q_dtype F32/F16/BF16
+ *   k_cache,v_cache device pool in kv_dtype: F32/F16/BF16 (same as q) or I8
+ *                  with k_scale/v_scale device float[num_blocks][num_kv_heads]
+ *   block_tables   device int32[num_seqs][max_blocks_per_seq]
+ *   context_lens   device int32[num_seqs], each <= max_context_len
+ *                  <= max_blocks_per_seq * block_size
+ *   scale          multiplies q.k before the softmax (1/sqrt(head_dim) in
+ *                  the usual case)
+ *   partition_tokens  0: one workgroup covers a whole context; otherwise a
+ *                  multiple of block_size: contexts are split into partitions
+ *                  of that many tokens, each producing a partial result
+ *                  (max, sum, unnormalised output) that a reduce kernel
+ *                  merges.  Results are deterministic for a fixed value.
+ *   algo           PKV_ALGO_*; AUTO picks MFMA for grouped heads with
+ *                  16-bit q, else the wavefront kernel.
+ *   workspace      device scratch of at least
+ *                  pkv_decode_workspace_bytes(...) bytes (may be NULL when
+ *                  that is 0), 256-byte aligned.
+ * Supported: head_dim 64 or 128, block_size 16, num_q_heads a multiple of
+ * num_kv_heads with a group of at most 16.  Others: UNSUPPORTED. */
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_context_len, int32_t partition_tokens);
+
+pkv_status pkv_paged_attention_decode(
+    void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype, const void* k_cache,
+    const void* v_cache, pkv_dtype kv_dtype, const float* k_scale, const float* v_scale,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+    int32_t partition_tokens, int32_t algo, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The two halves of pkv_paged_attention_decode, for callers that schedule
+ * them separately.  _partials runs the main kernel only: sequences that fit
+ * in one partition get their final output row, the others leave partial
+ * results in the workspace.  _reduce merges those partials (log-sum-exp
+ * rescaling of each partition's max and sum) into `out`; it reads
+ * context_lens to know each sequence's partition count.  Same arguments and
+ * rules as above; with partition_tokens 0 the reduce is a no-op. */
+pkv_status pkv_paged_attention_decode_partials(
+    void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype, const void* k_cache,
+    const void* v_cache, pkv_dtype kv_dtype, const float* k_scale, const float* v_scale,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+    int32_t partition_tokens, int32_t algo, void* workspace, size_t workspace_bytes, void* stream);
+
+pkv_status pkv_paged_attention_reduce(void* out, pkv_dtype out_dtype, const int32_t* context_lens,
+                                      int32_t max_context_len, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t head_dim,
+                                      int32_t partition_tokens, const void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Chunked prefill attention (device).  Long prompts are processed in chunks
+ * that share a batch with decode steps ([nxbn] §3.2; [cnnetsun] §4.1 turns
+ * chunking on).  Sequence s owns query rows query_start_loc[s] ..
+ * query_start_loc[s+1]-1, its last qlen positions: row i sits at position
+ * context_lens[s] - qlen + i and attends keys [0, that position] (causal over
+ * absolute positions).  The chunk's own K/V must already be in the cache
+ * (pkv_reshape_and_cache first).
+ *   out, q         device [num_query_tokens][num_q_heads][head_dim]
+ *   query_start_loc device int32[num_seqs + 1], non-decreasing, from 0
+ *   context_lens   device int32[num_seqs], each >= its chunk length
+ *   max_query_len  the largest chunk (sizes the launch)
+ * q_dtype F16/BF16 with kv_dtype equal to it (MFMA path), or F32 throughout
+ * (wavefront path, one query row at a time).  Supported head_dim 64/128,
+ * block_size 16, group (num_q_heads / num_kv_heads) of any size. */
+pkv_status pkv_paged_attention_prefill(
+    void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype, const void* k_cache,
+    const void* v_cache, pkv_dtype kv_dtype, const float* k_scale, const float* v_scale,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* query_start_loc,
+    const int32_t* context_lens, int32_t max_query_len, int32_t max_context_len, int32_t num_seqs,
+    int32_t num_query_tokens, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t num_blocks, float scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

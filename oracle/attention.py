@@ -38,6 +38,8 @@ def gather(cache: np.ndarray, table_row: np.ndarray, n: int, block_size: int,
     """
     pos = np.arange(int(n))
     blocks = np.asarray(table_row)[pos // block_size]
+    if blocks.size and (blocks.min() < 0 or blocks.max() >= cache.shape[0]):
+        raise ValueError("a table entry inside the context names no block of the pool")
     rows = np.asarray(cache)[blocks, :, pos % block_size, :].astype(np.float64)
     if scale is not None:
         rows = rows * np.asarray(scale, dtype=np.float64)[blocks][:, :, None]

@@ -1,0 +1,294 @@
+"""pkv: paged KV cache and paged attention for AMD Instinct MI355X (gfx950).
+
+A thin binding of libpkv's C ABI (``include/pkv.h``): every function here
+carries the C name, checks and marshals its arguments (torch tensors for
+device memory, numpy arrays for host memory, torch's current HIP stream) and
+calls the library.  All work happens in the library: the host block manager
+in C++ and every device step in hand-written gfx950 HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+from ._lib import (PKV_ALGO_AUTO, PKV_ALGO_MFMA, PKV_ALGO_WAVE, PKV_BF16, PKV_ERR_DEVICE,  # noqa
+                   PKV_ERR_INTERNAL, PKV_ERR_INVALID, PKV_ERR_OUT_OF_BLOCKS, PKV_ERR_UNSUPPORTED,
+                   PKV_F16, PKV_F32, PKV_I8, PKV_OK, LIB_PATH, PkvBmStats, PkvError,
+                   PkvOutOfBlocks, check, load)
+
+__all__ = [n for n in dir() if n.startswith("pkv_") or n.startswith("PKV_")]
+
+
+def _i32p(a: np.ndarray):
+    return a.ctypes.data_as(C.POINTER(C.c_int32))
+
+
+def _i64p(a: np.ndarray):
+    return a.ctypes.data_as(C.POINTER(C.c_int64))
+
+
+# --------------------------------------------------------------------------
+# host block manager
+# --------------------------------------------------------------------------
+def pkv_version() -> str:
+    return load().pkv_version().decode()
+
+
+def pkv_bm_create(num_blocks: int, block_size: int,
+                  init_free_order: Optional[Sequence[int]] = None) -> C.c_void_p:
+    h = C.c_void_p()
+    order = None
+    if init_free_order is not None:
+        order = np.ascontiguousarray(init_free_order, dtype=np.int32)
+        if order.shape != (num_blocks,):
+            raise ValueError("init_free_order must have num_blocks entries")
+    check(load().pkv_bm_create(num_blocks, block_size, _i32p(order) if order is not None else None,
+                               C.byref(h)))
+    return h
+
+
+def pkv_bm_destroy(bm) -> None:
+    load().pkv_bm_destroy(bm)
+
+
+def pkv_bm_alloc(bm, n: int) -> np.ndarray:
+    ids = np.empty(max(n, 0), np.int32)
+    check(load().pkv_bm_alloc(bm, n, _i32p(ids)))
+    return ids
+
+
+def pkv_bm_incref(bm, block: int) -> None:
+    check(load().pkv_bm_incref(bm, block))
+
+
+def pkv_bm_decref(bm, block: int) -> None:
+    check(load().pkv_bm_decref(bm, block))
+
+
+def pkv_bm_num_free(bm) -> int:
+    return load().pkv_bm_num_free(bm)
+
+
+def pkv_bm_get_state(bm, num_blocks: int) -> Tuple[np.ndarray, np.ndarray]:
+    free = np.empty(num_blocks, np.int32)
+    rc = np.empty(num_blocks, np.int32)
+    n = C.c_int32()
+    check(load().pkv_bm_get_state(bm, _i32p(free), C.byref(n), _i32p(rc)))
+    return free[:n.value].copy(), rc
+
+
+def pkv_bm_stats_get(bm) -> dict:
+    s = PkvBmStats()
+    check(load().pkv_bm_stats_get(bm, C.byref(s)))
+    return {f: getattr(s, f) for f, _ in PkvBmStats._fields_}
+
+
+def pkv_seq_create(bm, num_tokens: int) -> int:
+    sid = C.c_int64()
+    check(load().pkv_seq_create(bm, num_tokens, C.byref(sid)))
+    return sid.value
+
+
+def pkv_seq_fork(bm, parent: int) -> int:
+    sid = C.c_int64()
+    check(load().pkv_seq_fork(bm, parent, C.byref(sid)))
+    return sid.value
+
+
+def pkv_seq_append(bm, seq: int, num_tokens: int = 1):
+    """Returns (slots int32[num_tokens], (cow_src, cow_dst) or None)."""
+    slots = np.empty(max(num_tokens, 0), np.int32)
+    src, dst = C.c_int32(-1), C.c_int32(-1)
+    check(load().pkv_seq_append(bm, seq, num_tokens, _i32p(slots), C.byref(src), C.byref(dst)))
+    return slots, ((src.value, dst.value) if src.value >= 0 else None)
+
+
+def pkv_seq_append_batch(bm, seqs: Sequence[int]):
+    """Returns (slots int32[n], cow pairs int32[k, 2])."""
+    s = np.ascontiguousarray(seqs, dtype=np.int64)
+    slots = np.empty(len(s), np.int32)
+    pairs = np.empty((max(len(s), 1), 2), np.int32)
+    k = C.c_int32(0)
+    check(load().pkv_seq_append_batch(bm, _i64p(s), len(s), _i32p(slots), _i32p(pairs),
+                                      C.byref(k)))
+    return slots, pairs[:k.value].copy()
+
+
+def pkv_seq_slots(bm, seq: int, start: int, count: int) -> np.ndarray:
+    out = np.empty(max(count, 0), np.int32)
+    check(load().pkv_seq_slots(bm, seq, start, count, _i32p(out)))
+    return out
+
+
+def pkv_seq_len(bm, seq: int) -> int:
+    n = C.c_int32()
+    check(load().pkv_seq_len(bm, seq, C.byref(n)))
+    return n.value
+
+
+def pkv_seq_free(bm, seq: int) -> None:
+    check(load().pkv_seq_free(bm, seq))
+
+
+def pkv_seq_export(bm, seqs: Sequence[int], max_blocks: int) -> Tuple[np.ndarray, np.ndarray]:
+    s = np.ascontiguousarray(seqs, dtype=np.int64)
+    tables = np.empty((len(s), max_blocks), np.int32)
+    lens = np.empty(len(s), np.int32)
+    check(load().pkv_seq_export(bm, _i64p(s), len(s), max_blocks, _i32p(tables), _i32p(lens)))
+    return tables, lens
+
+
+# --------------------------------------------------------------------------
+# device operations (torch tensors on the GPU)
+# --------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16,
+         torch.int8: PKV_I8}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _dev(t, name: str, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(t, stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(t.device)
+    return C.c_void_p(s.cuda_stream)
+
+
+def pkv_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None) -> None:
+    """key/value [T, Hkv, D] (row stride from the tensor), caches [NB, Hkv, BS, D]."""
+    torch = _torch()
+    T, hkv, d = key.shape
+    nb, hkv2, bs, d2 = k_cache.shape
+    if (hkv, d) != (hkv2, d2) or value.shape != key.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    if key.dtype != k_cache.dtype or value.dtype != k_cache.dtype:
+        raise TypeError("key, value and cache must share a dtype")
+    for t, n in ((key, "key"), (value, "value")):
+        if t.stride(2) != 1 or t.stride(1) != d:
+            raise ValueError(f"{n} rows must be [Hkv, D] contiguous")
+    if slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be [T]")
+    check(load().pkv_reshape_and_cache(
+        C.c_void_p(key.data_ptr()), C.c_void_p(value.data_ptr()), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), _dev(slot_mapping, "slot_mapping", torch.int32), T,
+        key.stride(0), value.stride(0), hkv, d, bs, nb, _dtype_code(k_cache),
+        _stream(k_cache, stream)))
+
+
+def pkv_copy_blocks(k_cache, v_cache, pairs, k_scale=None, v_scale=None, stream=None) -> None:
+    """pairs: int32 [n, 2] device tensor of (src, dst)."""
+    torch = _torch()
+    nb, hkv, bs, d = k_cache.shape
+    n = pairs.shape[0] if pairs.dim() == 2 else 0
+    check(load().pkv_copy_blocks(
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(k_scale, "k_scale", torch.float32),
+        _dev(v_scale, "v_scale", torch.float32), _dev(pairs, "pairs", torch.int32), n, hkv, d, bs,
+        nb, _dtype_code(k_cache), _stream(k_cache, stream)))
+
+
+def pkv_decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
+                               max_context_len: int, partition_tokens: int) -> int:
+    return load().pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
+                                             partition_tokens)
+
+
+def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                 partition_tokens, algo, k_scale, v_scale, workspace, stream):
+    torch = _torch()
+    S, hq, d = q.shape
+    nb, hkv, bs, d2 = k_cache.shape
+    if out.shape != q.shape or d2 != d or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables must be [S, MB] and context_lens [S]")
+    need = pkv_decode_workspace_bytes(S, hq, d, max_context_len, partition_tokens)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = C.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return (_dev(out, "out"), _dtype_code(out), _dev(q, "q"), _dtype_code(q),
+            _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dtype_code(k_cache),
+            _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32),
+            _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+            _dev(context_lens, "context_lens", torch.int32), int(max_context_len), S, hq, hkv, d,
+            bs, nb, float(scale), int(partition_tokens), int(algo), ws_ptr, ws_len,
+            _stream(q, stream)), workspace
+
+
+def pkv_paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
+                               max_context_len: int, scale: float, partition_tokens: int = 0,
+                               algo: int = PKV_ALGO_AUTO, k_scale=None, v_scale=None,
+                               workspace=None, stream=None):
+    """out, q: [S, Hq, D]; caches [NB, Hkv, 16, D]; block_tables int32 [S, MB];
+    context_lens int32 [S].  Returns the workspace tensor used (or None)."""
+    args, ws = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens,
+                            max_context_len, scale, partition_tokens, algo, k_scale, v_scale,
+                            workspace, stream)
+    check(load().pkv_paged_attention_decode(*args))
+    return ws
+
+
+def pkv_paged_attention_decode_partials(out, q, k_cache, v_cache, block_tables, context_lens,
+                                        max_context_len: int, scale: float,
+                                        partition_tokens: int = 0, algo: int = PKV_ALGO_AUTO,
+                                        k_scale=None, v_scale=None, workspace=None, stream=None):
+    args, ws = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens,
+                            max_context_len, scale, partition_tokens, algo, k_scale, v_scale,
+                            workspace, stream)
+    check(load().pkv_paged_attention_decode_partials(*args))
+    return ws
+
+
+def pkv_paged_attention_reduce(out, context_lens, max_context_len: int, partition_tokens: int,
+                               workspace, stream=None) -> None:
+    torch = _torch()
+    S, hq, d = out.shape
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    check(load().pkv_paged_attention_reduce(
+        _dev(out, "out"), _dtype_code(out), _dev(context_lens, "context_lens", torch.int32),
+        int(max_context_len), S, hq, d, int(partition_tokens),
+        C.c_void_p(workspace.data_ptr()) if workspace is not None else None, ws_len,
+        _stream(out, stream)))
+
+
+def pkv_paged_attention_prefill(out, q, k_cache, v_cache, block_tables, query_start_loc,
+                                context_lens, max_query_len: int, max_context_len: int,
+                                scale: float, k_scale=None, v_scale=None, stream=None) -> None:
+    """out, q: [Tq, Hq, D]; query_start_loc int32 [S+1]; context_lens int32 [S]."""
+    torch = _torch()
+    Tq, hq, d = q.shape
+    nb, hkv, bs, d2 = k_cache.shape
+    S = context_lens.shape[0]
+    if out.shape != q.shape or d2 != d or query_start_loc.shape != (S + 1,):
+        raise ValueError("shape mismatch")
+    check(load().pkv_paged_attention_prefill(
+        _dev(out, "out"), _dtype_code(out), _dev(q, "q"), _dtype_code(q), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), _dtype_code(k_cache), _dev(k_scale, "k_scale", torch.float32),
+        _dev(v_scale, "v_scale", torch.float32), _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(query_start_loc, "query_start_loc", torch.int32),
+        _dev(context_lens, "context_lens", torch.int32), int(max_query_len), int(max_context_len),
+        S, Tq, hq, hkv, d, bs, nb, float(scale), _stream(q, stream)))
+
+
+__all__ = sorted(set(__all__) | {n for n in dir() if n.startswith("pkv_")})

@@ -1,0 +1,331 @@
+// C entry points of paged attention: argument checks, workspace layout and
+// the choice between the wavefront and matrix-core kernels.
+#include <cmath>
+#include <vector>
+
+#include "attention_common.h"
+#include "host_checks.h"
+
+namespace pkv {
+pkv_status launch_decode_wave(const AttnArgs& a, pkv_dtype q_dt, pkv_dtype kv_dt, int D,
+                              int group, hipStream_t st);
+pkv_status launch_reduce(const AttnArgs& a, int D, hipStream_t st);
+pkv_status launch_decode_mfma(const AttnArgs& a, pkv_dtype q_dt, pkv_dtype kv_dt, int D,
+                              int group, hipStream_t st);
+pkv_status launch_prefill_mfma(const AttnArgs& a, pkv_dtype q_dt, int D, int group,
+                               int max_query_len, hipStream_t st);
+}  // namespace pkv
+
+using namespace pkv;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int num_partitions(int32_t max_ctx, int32_t part_tokens) {
+  if (part_tokens <= 0) return 1;
+  int64_t p = (static_cast<int64_t>(max_ctx) + part_tokens - 1) / part_tokens;
+  return static_cast<int>(std::max<int64_t>(p, 1));
+}
+
+struct WsLayout {
+  size_t o_bytes = 0, ml_bytes = 0, total = 0;
+};
+
+WsLayout workspace_layout(int64_t rows, int64_t hq, int64_t D, int parts) {
+  WsLayout w;
+  if (parts <= 1) return w;
+  w.o_bytes = align_up(static_cast<size_t>(rows * hq * parts * D) * sizeof(float));
+  w.ml_bytes = align_up(static_cast<size_t>(rows * hq * parts * 2) * sizeof(float));
+  w.total = w.o_bytes + w.ml_bytes;
+  return w;
+}
+
+int out_kind_of(pkv_dtype out_dt) {
+  return out_dt == PKV_F32 ? kOutF32 : out_dt == PKV_BF16 ? kOutBF16 : kOutF16;
+}
+
+// Shared checks of decode and prefill arguments.
+pkv_status check_common(const char* who, void* out, pkv_dtype out_dt, const void* q,
+                        pkv_dtype q_dt, const void* kc, const void* vc, pkv_dtype kv_dt,
+                        const float* ks, const float* vs, const int32_t* tables, int32_t mb,
+                        const int32_t* lens, int32_t max_ctx, int32_t S, int32_t hq, int32_t hkv,
+                        int32_t D, int32_t bs, int32_t nb, float scale) {
+  if (S < 0 || hq <= 0 || hkv <= 0 || nb <= 0 || mb < 0 || max_ctx < 0)
+    return fail(PKV_ERR_INVALID, "%s: bad sizes (S=%d Hq=%d Hkv=%d NB=%d MB=%d max_ctx=%d)", who,
+                S, hq, hkv, nb, mb, max_ctx);
+  if (hq % hkv != 0)
+    return fail(PKV_ERR_INVALID, "%s: num_q_heads %d is not a multiple of num_kv_heads %d", who,
+                hq, hkv);
+  if (D != 64 && D != 128) return fail(PKV_ERR_UNSUPPORTED, "%s: head_dim %d (64 or 128)", who, D);
+  if (bs != 16) return fail(PKV_ERR_UNSUPPORTED, "%s: block_size %d (16 only)", who, bs);
+  if (static_cast<int64_t>(max_ctx) > static_cast<int64_t>(mb) * bs)
+    return fail(PKV_ERR_INVALID, "%s: max_context_len %d exceeds max_blocks_per_seq * block_size",
+                who, max_ctx);
+  if (q_dt != PKV_F32 && q_dt != PKV_F16 && q_dt != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: q dtype %s", who, dtype_name(q_dt));
+  if (kv_dt != q_dt && kv_dt != PKV_I8)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: kv dtype %s with q dtype %s", who, dtype_name(kv_dt),
+                dtype_name(q_dt));
+  if (out_dt != PKV_F32 && out_dt != q_dt)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: out dtype must be f32 or the q dtype", who);
+  if (kv_dt == PKV_I8 && (!ks || !vs))
+    return fail(PKV_ERR_INVALID, "%s: int8 KV needs k_scale and v_scale", who);
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID, "%s: scale is not finite", who);
+  if (S > 0 && (!out || !q || !kc || !vc || !tables || !lens))
+    return fail(PKV_ERR_INVALID, "%s: NULL pointer", who);
+  if (!aligned(kc, 16) || !aligned(vc, 16) || !aligned(q, 16) || !aligned(out, 4))
+    return fail(PKV_ERR_INVALID, "%s: q, k_cache and v_cache must be 16-byte aligned", who);
+  return PKV_OK;
+}
+
+// PKV_VALIDATE=1: lengths within bounds, and every table entry a sequence
+// reads names a block of the pool.
+pkv_status deep_check_tables(const char* who, const int32_t* tables, int32_t mb,
+                             const int32_t* lens, int32_t max_ctx, int32_t S, int32_t nb,
+                             void* stream, std::vector<int32_t>* lens_out = nullptr) {
+  std::vector<int32_t> L, T;
+  pkv_status st = fetch_i32(lens, S, stream, L);
+  if (st) return st;
+  st = fetch_i32(tables, static_cast<size_t>(S) * mb, stream, T);
+  if (st) return st;
+  for (int32_t s = 0; s < S; ++s) {
+    if (L[s] < 0 || L[s] > max_ctx)
+      return fail(PKV_ERR_INVALID, "%s: context_lens[%d] = %d outside [0, %d]", who, s, L[s],
+                  max_ctx);
+    for (int32_t j = 0; j < (L[s] + 15) / 16; ++j) {
+      int32_t b = T[static_cast<size_t>(s) * mb + j];
+      if (b < 0 || b >= nb)
+        return fail(PKV_ERR_INVALID, "%s: block_tables[%d][%d] = %d outside the pool", who, s, j,
+                    b);
+    }
+  }
+  if (lens_out) *lens_out = std::move(L);
+  return PKV_OK;
+}
+
+bool use_mfma(int32_t algo, pkv_dtype q_dt, int group) {
+  const bool able = (q_dt == PKV_BF16 || q_dt == PKV_F16) && group <= 16;
+  if (algo == PKV_ALGO_MFMA) return able;
+  if (algo == PKV_ALGO_WAVE) return false;
+  return able && group >= 4;
+}
+
+enum class DecodePart { kAll, kMain, kReduce };
+
+pkv_status decode_impl(DecodePart which, void* out, pkv_dtype out_dt, const void* q,
+                       pkv_dtype q_dt, const void* kc, const void* vc, pkv_dtype kv_dt,
+                       const float* ks, const float* vs, const int32_t* tables, int32_t mb,
+                       const int32_t* lens, int32_t max_ctx, int32_t S, int32_t hq, int32_t hkv,
+                       int32_t D, int32_t bs, int32_t nb, float scale, int32_t part_tokens,
+                       int32_t algo, void* ws, size_t ws_bytes, void* stream) {
+  const char* who = "paged_attention_decode";
+  pkv_status st = check_common(who, out, out_dt, q, q_dt, kc, vc, kv_dt, ks, vs, tables, mb, lens,
+                               max_ctx, S, hq, hkv, D, bs, nb, scale);
+  if (st) return st;
+  if (part_tokens < 0 || part_tokens % 16 != 0)
+    return fail(PKV_ERR_INVALID, "%s: partition_tokens %d must be 0 or a multiple of 16", who,
+                part_tokens);
+  if (algo < PKV_ALGO_AUTO || algo > PKV_ALGO_MFMA)
+    return fail(PKV_ERR_INVALID, "%s: unknown algo %d", who, algo);
+  const int group = hq / hkv;
+  if (algo == PKV_ALGO_MFMA && !use_mfma(algo, q_dt, group))
+    return fail(PKV_ERR_UNSUPPORTED, "%s: MFMA path needs 16-bit q and a group of at most 16",
+                who);
+  if (S == 0) return PKV_OK;
+  const int parts = num_partitions(max_ctx, part_tokens);
+  const WsLayout w = workspace_layout(S, hq, D, parts);
+  if (w.total > 0 && (!ws || ws_bytes < w.total || !aligned(ws, kAlign)))
+    return fail(PKV_ERR_INVALID, "%s: workspace needs %zu bytes, 256-byte aligned (got %zu)", who,
+                w.total, ws_bytes);
+  if (deep_validation() && which != DecodePart::kReduce) {
+    st = deep_check_tables(who, tables, mb, lens, max_ctx, S, nb, stream);
+    if (st) return st;
+  }
+  AttnArgs a{};
+  a.out = out;
+  a.part_o = parts > 1 ? static_cast<float*>(ws) : nullptr;
+  a.part_ml = parts > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + w.o_bytes) : nullptr;
+  a.q = q;
+  a.kc = kc;
+  a.vc = vc;
+  a.ks = kv_dt == PKV_I8 ? ks : nullptr;
+  a.vs = kv_dt == PKV_I8 ? vs : nullptr;
+  a.tables = tables;
+  a.lens = lens;
+  a.qsl = nullptr;
+  a.max_blocks = mb;
+  a.max_ctx = max_ctx;
+  a.num_seqs = S;
+  a.num_rows = S;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.num_blocks = nb;
+  a.num_parts = parts;
+  // Without a split one partition covers the longest context.
+  a.part_tokens = parts > 1 ? part_tokens : std::max(16, (max_ctx + 15) / 16 * 16);
+  a.out_kind = out_kind_of(out_dt);
+  a.scale_log2 = scale * kLog2e;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (which != DecodePart::kReduce) {
+    st = use_mfma(algo, q_dt, group) ? launch_decode_mfma(a, q_dt, kv_dt, D, group, hs)
+                                     : launch_decode_wave(a, q_dt, kv_dt, D, group, hs);
+    if (st) return st;
+  }
+  if (which != DecodePart::kMain && parts > 1) return launch_reduce(a, D, hs);
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_context_len, int32_t partition_tokens) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
+  return workspace_layout(num_seqs, num_q_heads, head_dim,
+                          num_partitions(max_context_len, partition_tokens))
+      .total;
+}
+
+pkv_status pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void* q,
+                                      pkv_dtype q_dtype, const void* k_cache, const void* v_cache,
+                                      pkv_dtype kv_dtype, const float* k_scale,
+                                      const float* v_scale, const int32_t* block_tables,
+                                      int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                      int32_t max_context_len, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t num_blocks, float scale,
+                                      int32_t partition_tokens, int32_t algo, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  PKV_GUARD({
+    return decode_impl(DecodePart::kAll, out, out_dtype, q, q_dtype, k_cache, v_cache, kv_dtype,
+                       k_scale, v_scale, block_tables, max_blocks_per_seq, context_lens,
+                       max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                       num_blocks, scale, partition_tokens, algo, workspace, workspace_bytes,
+                       stream);
+  })
+}
+
+pkv_status pkv_paged_attention_decode_partials(
+    void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype, const void* k_cache,
+    const void* v_cache, pkv_dtype kv_dtype, const float* k_scale, const float* v_scale,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+    int32_t partition_tokens, int32_t algo, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  PKV_GUARD({
+    return decode_impl(DecodePart::kMain, out, out_dtype, q, q_dtype, k_cache, v_cache, kv_dtype,
+                       k_scale, v_scale, block_tables, max_blocks_per_seq, context_lens,
+                       max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                       num_blocks, scale, partition_tokens, algo, workspace, workspace_bytes,
+                       stream);
+  })
+}
+
+pkv_status pkv_paged_attention_reduce(void* out, pkv_dtype out_dtype, const int32_t* context_lens,
+                                      int32_t max_context_len, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t head_dim,
+                                      int32_t partition_tokens, const void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  PKV_GUARD({
+    const char* who = "paged_attention_reduce";
+    if (num_seqs < 0 || num_q_heads <= 0 || (head_dim != 64 && head_dim != 128) ||
+        max_context_len < 0 || partition_tokens < 0 || partition_tokens % 16)
+      return fail(PKV_ERR_INVALID, "%s: bad sizes", who);
+    if (out_dtype != PKV_F32 && out_dtype != PKV_BF16 && out_dtype != PKV_F16)
+      return fail(PKV_ERR_UNSUPPORTED, "%s: out dtype", who);
+    const int parts = num_partitions(max_context_len, partition_tokens);
+    if (num_seqs == 0 || parts <= 1) return PKV_OK;
+    const WsLayout w = workspace_layout(num_seqs, num_q_heads, head_dim, parts);
+    if (!out || !context_lens || !workspace || workspace_bytes < w.total ||
+        !aligned(workspace, kAlign))
+      return fail(PKV_ERR_INVALID, "%s: NULL pointer or workspace smaller than %zu bytes", who,
+                  w.total);
+    AttnArgs a{};
+    a.out = out;
+    a.part_o = static_cast<float*>(const_cast<void*>(workspace));
+    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(workspace)) +
+                                         w.o_bytes);
+    a.lens = context_lens;
+    a.max_blocks = (max_context_len + 15) / 16 + 1;
+    a.max_ctx = max_context_len;
+    a.num_seqs = num_seqs;
+    a.num_rows = num_seqs;
+    a.hq = num_q_heads;
+    a.hkv = num_q_heads;
+    a.num_parts = parts;
+    a.part_tokens = partition_tokens;
+    a.out_kind = out_kind_of(out_dtype);
+    return launch_reduce(a, head_dim, static_cast<hipStream_t>(stream));
+  })
+}
+
+pkv_status pkv_paged_attention_prefill(
+    void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype, const void* k_cache,
+    const void* v_cache, pkv_dtype kv_dtype, const float* k_scale, const float* v_scale,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* query_start_loc,
+    const int32_t* context_lens, int32_t max_query_len, int32_t max_context_len, int32_t num_seqs,
+    int32_t num_query_tokens, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t num_blocks, float scale, void* stream) {
+  PKV_GUARD({
+    const char* who = "paged_attention_prefill";
+    pkv_status st = check_common(who, out, out_dtype, q, q_dtype, k_cache, v_cache, kv_dtype,
+                                 k_scale, v_scale, block_tables, max_blocks_per_seq, context_lens,
+                                 max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                 block_size, num_blocks, scale);
+    if (st) return st;
+    if (num_query_tokens < 0 || max_query_len < 0 || max_query_len > max_context_len)
+      return fail(PKV_ERR_INVALID, "%s: bad query sizes", who);
+    if (num_seqs > 0 && !query_start_loc)
+      return fail(PKV_ERR_INVALID, "%s: query_start_loc is NULL", who);
+    if (kv_dtype == PKV_I8)
+      return fail(PKV_ERR_UNSUPPORTED, "%s: int8 KV is a decode-only storage here", who);
+    if (num_seqs == 0 || num_query_tokens == 0) return PKV_OK;
+    if (deep_validation()) {
+      std::vector<int32_t> L, Q;
+      st = deep_check_tables(who, block_tables, max_blocks_per_seq, context_lens,
+                             max_context_len, num_seqs, num_blocks, stream, &L);
+      if (st) return st;
+      st = fetch_i32(query_start_loc, num_seqs + 1, stream, Q);
+      if (st) return st;
+      if (Q[0] != 0 || Q[num_seqs] != num_query_tokens)
+        return fail(PKV_ERR_INVALID, "%s: query_start_loc must run from 0 to %d", who,
+                    num_query_tokens);
+      for (int32_t s = 0; s < num_seqs; ++s) {
+        const int32_t ql = Q[s + 1] - Q[s];
+        if (ql < 0 || ql > max_query_len || ql > L[s])
+          return fail(PKV_ERR_INVALID, "%s: chunk %d has length %d (context %d, max %d)", who,
+                      s, ql, L[s], max_query_len);
+      }
+    }
+    AttnArgs a{};
+    a.out = out;
+    a.q = q;
+    a.kc = k_cache;
+    a.vc = v_cache;
+    a.tables = block_tables;
+    a.lens = context_lens;
+    a.qsl = query_start_loc;
+    a.max_blocks = max_blocks_per_seq;
+    a.max_ctx = max_context_len;
+    a.num_seqs = num_seqs;
+    a.num_rows = num_query_tokens;
+    a.hq = num_q_heads;
+    a.hkv = num_kv_heads;
+    a.num_blocks = num_blocks;
+    a.num_parts = 1;
+    a.part_tokens = std::max(16, (max_context_len + 15) / 16 * 16);
+    a.out_kind = out_kind_of(out_dtype);
+    a.scale_log2 = scale * kLog2e;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const int group = num_q_heads / num_kv_heads;
+    if (q_dtype == PKV_F32) return launch_decode_wave(a, q_dtype, kv_dtype, head_dim, group, hs);
+    return launch_prefill_mfma(a, q_dtype, head_dim, group, max_query_len, hs);
+  })
+}
+
+}  // extern "C"

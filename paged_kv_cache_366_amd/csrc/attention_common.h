@@ -1,0 +1,113 @@
+// Arguments and small helpers shared by the paged attention kernels.
+#pragma once
+
+#include "device_common.h"
+
+namespace pkv {
+
+// Output element kinds (runtime: the store is once per output element).
+enum OutKind : int { kOutF32 = 0, kOutBF16 = 1, kOutF16 = 2 };
+
+struct AttnArgs {
+  void* out;                 // [rows][Hq][D] final output
+  float* part_o;             // [rows][Hq][num_parts][D] partial outputs (NULL: no split)
+  float* part_ml;            // [rows][Hq][num_parts][2] partial (max, sum), log2 domain
+  const void* q;             // [rows][Hq][D]
+  const void* kc;            // [NB][Hkv][16][D]
+  const void* vc;
+  const float* ks;           // [NB][Hkv] int8 scales (NULL otherwise)
+  const float* vs;
+  const int32_t* tables;     // [S][MB]
+  const int32_t* lens;       // [S]
+  const int32_t* qsl;        // [S+1] query_start_loc; NULL means one query row per sequence
+  int max_blocks;            // MB
+  int max_ctx;
+  int num_seqs;              // S
+  int num_rows;              // S (decode) or Tq (prefill)
+  int hq, hkv, num_blocks;
+  int num_parts;             // partitions per row in the grid (1 = no split)
+  int part_tokens;           // tokens per partition (multiple of 16)
+  int out_kind;
+  float scale_log2;          // scale * log2(e): scores are kept in the log2 domain
+};
+
+// Which sequence a query row belongs to, and that row's context (the
+// number of keys it attends).  Decode: row s, keys [0, lens[s]).  Chunked
+// prefill: row i of sequence s's chunk sits at position lens[s] - qlen + i
+// and attends keys [0, that position].  The result is clamped to what the
+// table and max_ctx can address, so no read leaves the table row.
+__device__ __forceinline__ void row_context(const AttnArgs& a, int row, int& seq, int& ctx) {
+  if (a.qsl == nullptr) {
+    seq = row;
+    ctx = a.lens[row];
+  } else {
+    int lo = 0, hi = a.num_seqs - 1;  // largest s with qsl[s] <= row
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.qsl[mid] <= row) lo = mid; else hi = mid - 1;
+    }
+    seq = lo;
+    const int qlen = a.qsl[seq + 1] - a.qsl[seq];
+    ctx = a.lens[seq] - qlen + (row - a.qsl[seq]) + 1;
+  }
+  const int cap = min(a.max_ctx, a.max_blocks * 16);
+  ctx = max(0, min(ctx, cap));
+}
+
+__device__ __forceinline__ void store_out(const AttnArgs& a, int64_t idx, float v) {
+  if (a.out_kind == kOutF32)
+    static_cast<float*>(a.out)[idx] = v;
+  else if (a.out_kind == kOutBF16)
+    static_cast<uint16_t*>(a.out)[idx] = static_cast<uint16_t>(f32_to_bf16_bits(v));
+  else
+    static_cast<uint16_t*>(a.out)[idx] = f32_to_f16_bits(v);
+}
+
+// Merge of two (max, sum) softmax states in the log2 domain: returns the
+// factors that rescale each side to the common max.  A side that has seen
+// no key yet has max -inf and gets factor 0.
+__device__ __forceinline__ void merge_factors(float m1, float m2, float& m, float& f1, float& f2) {
+  m = fmaxf(m1, m2);
+  const float ms = (m == kNegInf) ? 0.f : m;
+  f1 = fast_exp2(m1 - ms);
+  f2 = fast_exp2(m2 - ms);
+}
+
+// Final merge of a workgroup: NW wavefronts each left, per head row g, a
+// softmax state (max m, sum l) and an unnormalised output row o[D] in LDS.
+// Rescales them to the common max and either writes the normalised output
+// (the row's context fits one partition) or the partition's partial state.
+template <int NW, int NH, int D>
+__device__ __forceinline__ void finish_rows(const AttnArgs& a, const float (&sm_o)[NW][NH][D],
+                                            const float (&sm_m)[NW][NH],
+                                            const float (&sm_l)[NW][NH], int nheads, int row,
+                                            int hbase, int part, int nparts) {
+  for (int idx = threadIdx.x; idx < nheads * D; idx += blockDim.x) {
+    const int g = idx / D;
+    const int d = idx % D;
+    float M = sm_m[0][g];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_m[w][g]);
+    const float ms = (M == kNegInf) ? 0.f : M;
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = fast_exp2(sm_m[w][g] - ms);
+      L += sm_l[w][g] * f;
+      O += sm_o[w][g][d] * f;
+    }
+    const int64_t orow = static_cast<int64_t>(row) * a.hq + hbase + g;
+    if (nparts <= 1) {
+      store_out(a, orow * D + d, L > 0.f ? O / L : 0.f);
+    } else {
+      const int64_t pi = orow * a.num_parts + part;
+      a.part_o[pi * D + d] = O;
+      if (d == 0) {
+        a.part_ml[pi * 2] = M;
+        a.part_ml[pi * 2 + 1] = L;
+      }
+    }
+  }
+}
+
+}  // namespace pkv

@@ -1,0 +1,375 @@
+// Host block manager: a fixed pool of KV blocks with a LIFO free list, one
+// reference count per block, and sequences that own block tables.
+//
+// The pool and its stack-like free list follow the allocate() sketch of
+// cnnetsun.cn "别再让GPU内存拖后腿了…" §2.1 (ids start in ascending order and
+// are taken from the end); sharing through reference counts and
+// copy-on-write follow kongchang.com "vLLM架构深度解析…", section
+// "KV Cache内存共享", and aisoosoo.com "vLLM：大模型推理的加速引擎…", section
+// "技术亮点"; blocks return to the pool when a request ends (m.nxbn.cn §2.3).
+//
+// Every mutating call is all-or-nothing: it first works out how many blocks
+// it needs, fails with PKV_ERR_OUT_OF_BLOCKS before touching anything, and
+// only then changes state.
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <stdexcept>
+#include <unordered_map>
+#include <vector>
+
+#include "status.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+struct Sequence {
+  std::vector<int32_t> table;  // logical block j -> physical id
+  int32_t len = 0;
+};
+
+}  // namespace
+
+namespace pkv {
+
+pkv_status fail(pkv_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+pkv_status ok() { return PKV_OK; }
+
+}  // namespace pkv
+
+struct pkv_bm {
+  int32_t num_blocks = 0;
+  int32_t block_size = 0;
+  std::vector<int32_t> free_list;  // bottom .. top; pop from the back
+  std::vector<int32_t> rc;
+  std::unordered_map<int64_t, Sequence> seqs;
+  int64_t next_seq = 0;
+
+  int32_t blocks_for(int64_t tokens) const {
+    return static_cast<int32_t>((tokens + block_size - 1) / block_size);
+  }
+  bool allocated(int32_t b) const { return b >= 0 && b < num_blocks && rc[b] > 0; }
+  int32_t pop() {
+    int32_t b = free_list.back();
+    free_list.pop_back();
+    rc[b] = 1;
+    return b;
+  }
+  void release(int32_t b) {
+    if (--rc[b] == 0) free_list.push_back(b);
+  }
+  Sequence* find(int64_t id) {
+    auto it = seqs.find(id);
+    return it == seqs.end() ? nullptr : &it->second;
+  }
+  const Sequence* find(int64_t id) const {
+    auto it = seqs.find(id);
+    return it == seqs.end() ? nullptr : &it->second;
+  }
+  // Blocks an append of `n` tokens to `s` will take, given the current
+  // count of its tail block (`tail_rc`, ignored when the tail is full).
+  int64_t append_need(const Sequence& s, int64_t n, int32_t tail_rc) const {
+    if (n <= 0) return 0;
+    int64_t need = blocks_for(s.len + n) - blocks_for(s.len);
+    if (s.len % block_size != 0 && tail_rc > 1) need += 1;  // copy-on-write
+    return need;
+  }
+  // One position; the caller has checked that enough blocks are free.
+  int32_t append_one(Sequence& s, int32_t* cow_src, int32_t* cow_dst) {
+    if (s.len % block_size == 0) {
+      s.table.push_back(pop());
+    } else if (rc[s.table.back()] > 1) {
+      int32_t src = s.table.back();
+      int32_t dst = pop();
+      *cow_src = src;
+      *cow_dst = dst;
+      release(src);  // count > 1, so it stays allocated
+      s.table.back() = dst;
+    }
+    int32_t slot = s.table[s.len / block_size] * block_size + s.len % block_size;
+    s.len += 1;
+    return slot;
+  }
+};
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+const char* pkv_version(void) { return "pkv 0.1 (gfx950)"; }
+
+pkv_status pkv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* init_free_order,
+                         pkv_bm** out) {
+  PKV_GUARD({
+    if (!out) return pkv::fail(PKV_ERR_INVALID, "out is NULL");
+    *out = nullptr;
+    if (num_blocks <= 0 || block_size <= 0)
+      return pkv::fail(PKV_ERR_INVALID, "num_blocks (%d) and block_size (%d) must be positive",
+                       num_blocks, block_size);
+    auto* bm = new pkv_bm();
+    bm->num_blocks = num_blocks;
+    bm->block_size = block_size;
+    bm->rc.assign(num_blocks, 0);
+    bm->free_list.resize(num_blocks);
+    if (init_free_order) {
+      std::vector<char> seen(num_blocks, 0);
+      for (int32_t i = 0; i < num_blocks; ++i) {
+        int32_t b = init_free_order[i];
+        if (b < 0 || b >= num_blocks || seen[b]) {
+          delete bm;
+          return pkv::fail(PKV_ERR_INVALID, "init_free_order is not a permutation (entry %d = %d)",
+                           i, b);
+        }
+        seen[b] = 1;
+        bm->free_list[i] = b;
+      }
+    } else {
+      for (int32_t i = 0; i < num_blocks; ++i) bm->free_list[i] = i;
+    }
+    *out = bm;
+    return PKV_OK;
+  })
+}
+
+void pkv_bm_destroy(pkv_bm* bm) { delete bm; }
+
+pkv_status pkv_bm_alloc(pkv_bm* bm, int32_t n, int32_t* ids_out) {
+  PKV_GUARD({
+    if (!bm) return pkv::fail(PKV_ERR_INVALID, "bm is NULL");
+    if (n < 0 || (n > 0 && !ids_out)) return pkv::fail(PKV_ERR_INVALID, "bad count or output");
+    if (static_cast<size_t>(n) > bm->free_list.size())
+      return pkv::fail(PKV_ERR_OUT_OF_BLOCKS, "need %d blocks, %zu free", n, bm->free_list.size());
+    for (int32_t i = 0; i < n; ++i) ids_out[i] = bm->pop();
+    return PKV_OK;
+  })
+}
+
+pkv_status pkv_bm_incref(pkv_bm* bm, int32_t block) {
+  if (!bm) return pkv::fail(PKV_ERR_INVALID, "bm is NULL");
+  if (!bm->allocated(block)) return pkv::fail(PKV_ERR_INVALID, "block %d is not allocated", block);
+  bm->rc[block] += 1;
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_decref(pkv_bm* bm, int32_t block) {
+  PKV_GUARD({
+    if (!bm) return pkv::fail(PKV_ERR_INVALID, "bm is NULL");
+    if (!bm->allocated(block))
+      return pkv::fail(PKV_ERR_INVALID, "block %d is not allocated", block);
+    bm->release(block);
+    return PKV_OK;
+  })
+}
+
+int32_t pkv_bm_num_free(const pkv_bm* bm) {
+  return bm ? static_cast<int32_t>(bm->free_list.size()) : -1;
+}
+
+pkv_status pkv_bm_get_state(const pkv_bm* bm, int32_t* free_list, int32_t* free_len,
+                            int32_t* refcounts) {
+  if (!bm) return pkv::fail(PKV_ERR_INVALID, "bm is NULL");
+  if (free_list && !bm->free_list.empty())
+    std::memcpy(free_list, bm->free_list.data(), bm->free_list.size() * sizeof(int32_t));
+  if (free_len) *free_len = static_cast<int32_t>(bm->free_list.size());
+  if (refcounts) std::memcpy(refcounts, bm->rc.data(), bm->rc.size() * sizeof(int32_t));
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_stats_get(const pkv_bm* bm, pkv_bm_stats* out) {
+  if (!bm || !out) return pkv::fail(PKV_ERR_INVALID, "NULL argument");
+  pkv_bm_stats s{};
+  s.num_blocks = bm->num_blocks;
+  s.block_size = bm->block_size;
+  s.free_blocks = static_cast<int32_t>(bm->free_list.size());
+  for (int32_t r : bm->rc) {
+    s.used_blocks += r > 0;
+    s.shared_blocks += r > 1;
+  }
+  s.num_seqs = static_cast<int32_t>(bm->seqs.size());
+  for (const auto& kv : bm->seqs) {
+    s.logical_blocks += static_cast<int64_t>(kv.second.table.size());
+    s.tokens += kv.second.len;
+  }
+  s.waste_slots = s.logical_blocks * bm->block_size - s.tokens;
+  *out = s;
+  return PKV_OK;
+}
+
+pkv_status pkv_seq_create(pkv_bm* bm, int32_t num_tokens, int64_t* seq_out) {
+  PKV_GUARD({
+    if (!bm || !seq_out) return pkv::fail(PKV_ERR_INVALID, "NULL argument");
+    if (num_tokens < 0) return pkv::fail(PKV_ERR_INVALID, "negative length %d", num_tokens);
+    int32_t nb = bm->blocks_for(num_tokens);
+    if (static_cast<size_t>(nb) > bm->free_list.size())
+      return pkv::fail(PKV_ERR_OUT_OF_BLOCKS, "need %d blocks, %zu free", nb,
+                       bm->free_list.size());
+    Sequence s;
+    s.table.reserve(nb);
+    s.len = num_tokens;
+    for (int32_t i = 0; i < nb; ++i) s.table.push_back(bm->pop());
+    int64_t id = bm->next_seq++;
+    bm->seqs.emplace(id, std::move(s));
+    *seq_out = id;
+    return PKV_OK;
+  })
+}
+
+pkv_status pkv_seq_fork(pkv_bm* bm, int64_t parent, int64_t* child_out) {
+  PKV_GUARD({
+    if (!bm || !child_out) return pkv::fail(PKV_ERR_INVALID, "NULL argument");
+    const Sequence* p = bm->find(parent);
+    if (!p) return pkv::fail(PKV_ERR_INVALID, "unknown sequence %lld", (long long)parent);
+    Sequence c = *p;
+    for (int32_t b : c.table) bm->rc[b] += 1;
+    int64_t id = bm->next_seq++;
+    bm->seqs.emplace(id, std::move(c));
+    *child_out = id;
+    return PKV_OK;
+  })
+}
+
+pkv_status pkv_seq_append(pkv_bm* bm, int64_t seq, int32_t num_tokens, int32_t* slots_out,
+                          int32_t* cow_src, int32_t* cow_dst) {
+  PKV_GUARD({
+    if (!bm) return pkv::fail(PKV_ERR_INVALID, "bm is NULL");
+    Sequence* s = bm->find(seq);
+    if (!s) return pkv::fail(PKV_ERR_INVALID, "unknown sequence %lld", (long long)seq);
+    if (num_tokens < 0 || (num_tokens > 0 && !slots_out))
+      return pkv::fail(PKV_ERR_INVALID, "bad count or output");
+    if (static_cast<int64_t>(s->len) + num_tokens > INT32_MAX / 2)
+      return pkv::fail(PKV_ERR_INVALID, "sequence too long");
+    int32_t tail_rc = s->table.empty() ? 0 : bm->rc[s->table.back()];
+    int64_t need = bm->append_need(*s, num_tokens, tail_rc);
+    if (need > static_cast<int64_t>(bm->free_list.size()))
+      return pkv::fail(PKV_ERR_OUT_OF_BLOCKS, "need %lld blocks, %zu free", (long long)need,
+                       bm->free_list.size());
+    int32_t src = -1, dst = -1;
+    for (int32_t i = 0; i < num_tokens; ++i) slots_out[i] = bm->append_one(*s, &src, &dst);
+    if (cow_src) *cow_src = src;
+    if (cow_dst) *cow_dst = dst;
+    return PKV_OK;
+  })
+}
+
+pkv_status pkv_seq_append_batch(pkv_bm* bm, const int64_t* seqs, int32_t n, int32_t* slots_out,
+                                int32_t* cow_pairs_out, int32_t* num_cow_out) {
+  PKV_GUARD({
+    if (!bm) return pkv::fail(PKV_ERR_INVALID, "bm is NULL");
+    if (n < 0 || (n > 0 && (!seqs || !slots_out || !cow_pairs_out)))
+      return pkv::fail(PKV_ERR_INVALID, "bad count or NULL array");
+    std::vector<Sequence*> ss(n);
+    std::unordered_map<int64_t, int> seen;
+    for (int32_t i = 0; i < n; ++i) {
+      ss[i] = bm->find(seqs[i]);
+      if (!ss[i]) return pkv::fail(PKV_ERR_INVALID, "unknown sequence %lld", (long long)seqs[i]);
+      if (seen[seqs[i]]++)
+        return pkv::fail(PKV_ERR_INVALID, "sequence %lld appears twice", (long long)seqs[i]);
+    }
+    // Count the blocks the batch needs, tracking the count drops that earlier
+    // copies cause on a tail shared with later members of the batch.
+    std::unordered_map<int32_t, int32_t> rc_after;
+    int64_t need = 0;
+    for (int32_t i = 0; i < n; ++i) {
+      const Sequence& s = *ss[i];
+      if (s.len % bm->block_size == 0) {
+        need += 1;
+        continue;
+      }
+      int32_t tail = s.table.back();
+      auto it = rc_after.find(tail);
+      int32_t r = it == rc_after.end() ? bm->rc[tail] : it->second;
+      if (r > 1) {
+        need += 1;
+        rc_after[tail] = r - 1;
+      }
+    }
+    if (need > static_cast<int64_t>(bm->free_list.size()))
+      return pkv::fail(PKV_ERR_OUT_OF_BLOCKS, "need %lld blocks, %zu free", (long long)need,
+                       bm->free_list.size());
+    int32_t ncow = 0;
+    for (int32_t i = 0; i < n; ++i) {
+      int32_t src = -1, dst = -1;
+      slots_out[i] = bm->append_one(*ss[i], &src, &dst);
+      if (src >= 0) {
+        cow_pairs_out[2 * ncow] = src;
+        cow_pairs_out[2 * ncow + 1] = dst;
+        ++ncow;
+      }
+    }
+    if (num_cow_out) *num_cow_out = ncow;
+    return PKV_OK;
+  })
+}
+
+pkv_status pkv_seq_slots(const pkv_bm* bm, int64_t seq, int32_t start, int32_t count,
+                         int32_t* slots_out) {
+  if (!bm) return pkv::fail(PKV_ERR_INVALID, "bm is NULL");
+  const Sequence* s = bm->find(seq);
+  if (!s) return pkv::fail(PKV_ERR_INVALID, "unknown sequence %lld", (long long)seq);
+  if (start < 0 || count < 0 || static_cast<int64_t>(start) + count > s->len ||
+      (count > 0 && !slots_out))
+    return pkv::fail(PKV_ERR_INVALID, "positions [%d, %d) outside [0, %d)", start, start + count,
+                     s->len);
+  for (int32_t i = 0; i < count; ++i) {
+    int32_t p = start + i;
+    slots_out[i] = s->table[p / bm->block_size] * bm->block_size + p % bm->block_size;
+  }
+  return PKV_OK;
+}
+
+pkv_status pkv_seq_len(const pkv_bm* bm, int64_t seq, int32_t* len_out) {
+  if (!bm || !len_out) return pkv::fail(PKV_ERR_INVALID, "NULL argument");
+  const Sequence* s = bm->find(seq);
+  if (!s) return pkv::fail(PKV_ERR_INVALID, "unknown sequence %lld", (long long)seq);
+  *len_out = s->len;
+  return PKV_OK;
+}
+
+pkv_status pkv_seq_free(pkv_bm* bm, int64_t seq) {
+  PKV_GUARD({
+    if (!bm) return pkv::fail(PKV_ERR_INVALID, "bm is NULL");
+    auto it = bm->seqs.find(seq);
+    if (it == bm->seqs.end())
+      return pkv::fail(PKV_ERR_INVALID, "unknown sequence %lld", (long long)seq);
+    for (int32_t b : it->second.table) bm->release(b);
+    bm->seqs.erase(it);
+    return PKV_OK;
+  })
+}
+
+pkv_status pkv_seq_export(const pkv_bm* bm, const int64_t* seqs, int32_t n, int32_t max_blocks,
+                          int32_t* tables_out, int32_t* lens_out) {
+  if (!bm) return pkv::fail(PKV_ERR_INVALID, "bm is NULL");
+  if (n < 0 || max_blocks < 0 || (n > 0 && (!seqs || (!tables_out && max_blocks > 0))))
+    return pkv::fail(PKV_ERR_INVALID, "bad count or NULL array");
+  for (int32_t i = 0; i < n; ++i) {
+    const Sequence* s = bm->find(seqs[i]);
+    if (!s) return pkv::fail(PKV_ERR_INVALID, "unknown sequence %lld", (long long)seqs[i]);
+    if (static_cast<int64_t>(s->table.size()) > max_blocks)
+      return pkv::fail(PKV_ERR_INVALID, "sequence %lld holds %zu blocks > max_blocks %d",
+                       (long long)seqs[i], s->table.size(), max_blocks);
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const Sequence* s = bm->find(seqs[i]);
+    int32_t* row = tables_out ? tables_out + static_cast<int64_t>(i) * max_blocks : nullptr;
+    if (row) {
+      std::fill(row, row + max_blocks, -1);
+      std::copy(s->table.begin(), s->table.end(), row);
+    }
+    if (lens_out) lens_out[i] = s->len;
+  }
+  return PKV_OK;
+}
+
+}  // extern "C"

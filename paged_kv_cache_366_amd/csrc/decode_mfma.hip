@@ -1,0 +1,324 @@
+// Paged decode attention on the matrix cores, for query-head groups that
+// share one KV head (grouped-query attention) and 16-bit queries; KV in the
+// same 16-bit type or int8 with per-(block, KV head) scales.
+//
+// Same computation as the wavefront kernel (cnnetsun.cn "别再让GPU内存拖后腿了…"
+// §3.1: per-block scores, one softmax, weighted sum of value rows; int8 storage
+// is the compression of §3.2).  With G query heads reading every K/V element,
+// scoring and accumulation are dense products of a [G x D] query block with a
+// [D x 16] key tile and of a [G x 16] weight block with a [16 x D] value tile,
+// so they run on MFMA and the VALU keeps only the softmax and conversions.
+//
+// Per wavefront, one 16-token tile of one KV head:
+//   scores^T [16 tok x 16 heads] = K [16 x D] . Q^T [D x 16]
+//       v_mfma_f32_16x16x32 (bf16 or f16), D/32 of them.  Lane (t = l%16,
+//       kg = l/16) loads 8 consecutive elements of key row t, which is the
+//       A operand as it sits in memory; Q^T (B operand, lane = head l%16) stays
+//       in registers.  Heads beyond G are zero rows.
+//   The result leaves lane (h = l%16, kg) with the scores of head h for
+//   tokens 4kg..4kg+3: the online softmax of head h (max across the four kg
+//   lanes) needs two cross-lane steps, and those four weights are already the
+//   B operand of the next product.
+//   out^T [D x 16 heads] += V^T [D x 16 tok] . P^T [16 tok x 16 heads]
+//       v_mfma_f32_16x16x16, D/16 of them.  Lane (m = l%16, kg) loads the
+//       D/16 elements m*D/16.. of value rows 4kg..4kg+3 (four fully used
+//       256-byte rows per load instruction) and regroups them with v_perm so
+//       product j sees elements m*D/16 + j of those four rows.  The
+//       accumulator of head h stays in lanes h, so the rescale by the softmax
+//       correction is lane-local.
+//   Weights enter the product as a bf16 (or f16) pair hi + lo, hi = p rounded
+//   and lo = p - hi rounded, which keeps about 16 mantissa bits at the cost
+//   of a second MFMA per product; decode is HBM-bound, so it is free.
+// Four wavefronts take the partition's tiles round-robin, two tiles in flight
+// each, and merge through LDS at the end.
+#include "attention_common.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kUnroll = 2;
+
+template <typename T> struct Mx;
+template <> struct Mx<BF16> {
+  __device__ __forceinline__ static f32x4 k32(const u32x4& a, const u32x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static f32x4 k16(const u32x2& a, const u32x2& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+  }
+  // Two floats -> packed pair (round to nearest even).
+  __device__ __forceinline__ static uint32_t pack(float lo, float hi) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 v;
+    v.x = static_cast<__bf16>(lo);
+    v.y = static_cast<__bf16>(hi);
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  __device__ __forceinline__ static float lo(uint32_t w) { return bf16_lo(w); }
+  __device__ __forceinline__ static float hi(uint32_t w) { return bf16_hi(w); }
+  // Exact 16-bit image of an integer in [-128, 127] held as float.
+  __device__ __forceinline__ static uint32_t int_bits(float x) { return __float_as_uint(x) >> 16; }
+};
+template <> struct Mx<F16> {
+  __device__ __forceinline__ static f32x4 k32(const u32x4& a, const u32x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static f32x4 k16(const u32x2& a, const u32x2& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static uint32_t pack(float lo, float hi) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    f16x2 v;
+    v.x = static_cast<_Float16>(lo);
+    v.y = static_cast<_Float16>(hi);
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  __device__ __forceinline__ static float lo(uint32_t w) { return f16_lo(w); }
+  __device__ __forceinline__ static float hi(uint32_t w) { return f16_hi(w); }
+  __device__ __forceinline__ static uint32_t int_bits(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+  }
+};
+
+// Loads of 4, 8 or 16 bytes into the low dwords of a u32x4.
+template <int B>
+__device__ __forceinline__ u32x4 load_bytes(const uint8_t* p) {
+  u32x4 r = {0u, 0u, 0u, 0u};
+  if constexpr (B == 16) {
+    r = *reinterpret_cast<const u32x4*>(p);
+  } else if constexpr (B == 8) {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+    r.x = v.x;
+    r.y = v.y;
+  } else {
+    r.x = *reinterpret_cast<const uint32_t*>(p);
+  }
+  return r;
+}
+
+__device__ __forceinline__ uint32_t dw(const u32x4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// Element j of a chunk of 16-bit values, as the low 16 bits.
+__device__ __forceinline__ uint32_t half_of(const u32x4& v, int j) {
+  const uint32_t w = dw(v, j >> 1);
+  return (j & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+template <typename QT, typename KT, int D>
+__global__ __launch_bounds__(256) void decode_mfma_kernel(AttnArgs a, int group) {
+  constexpr bool kInt8 = (KT::bytes == 1);
+  constexpr int NK = D / 32;                  // QK products per tile
+  constexpr int NV = D / 16;                  // PV products per tile (= elements per lane row)
+  constexpr int KB = 8 * KT::bytes;           // bytes of one lane's K chunk
+  constexpr int VB = NV * KT::bytes;          // bytes of one lane's V chunk
+  constexpr int ROW = D * KT::bytes;          // bytes of one token row
+  constexpr int TILE = 16 * ROW;
+  using M = Mx<QT>;
+
+  const int part = blockIdx.x % a.num_parts;
+  const int row = blockIdx.x / a.num_parts;
+  const int kvh = blockIdx.y;
+  const int hbase = kvh * group;
+
+  int seq, ctx;
+  row_context(a, row, seq, ctx);
+  const int nparts = (ctx + a.part_tokens - 1) / a.part_tokens;
+  if (part >= max(nparts, 1)) return;
+  const int t0 = part * a.part_tokens;
+  const int t1 = min(ctx, t0 + a.part_tokens);
+  const int b0 = t0 >> 4;
+  const int nb = ((t1 + 15) >> 4) - b0;
+
+  const int wave = wave_uniform(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15;   // head (B/D operand column) or token / dim row (A operand)
+  const int kg = lane >> 4;
+
+  // Q^T operand: head r16, elements 32kk + 8kg .. +7.
+  u32x4 qop[NK];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q);
+    const bool live = r16 < group;
+    const int64_t qrow = (static_cast<int64_t>(row) * a.hq + hbase + (live ? r16 : 0)) * D;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      u32x4 v = *reinterpret_cast<const u32x4*>(qp + qrow + 32 * kk + 8 * kg);
+      qop[kk] = live ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  float m = kNegInf, l = 0.f;
+  f32x4 acc[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int32_t* trow = a.tables + static_cast<int64_t>(seq) * a.max_blocks;
+  const uint8_t* kc = static_cast<const uint8_t*>(a.kc);
+  const uint8_t* vc = static_cast<const uint8_t*>(a.vc);
+  // lane offsets inside a tile
+  const int koff = r16 * ROW + 8 * kg * KT::bytes;          // + kk * 32 elements
+  const int voff = (4 * kg) * ROW + r16 * VB;               // + e * ROW
+
+  for (int base = wave; base < nb; base += kWaves * kUnroll) {
+    u32x4 kr[kUnroll][NK], vr[kUnroll][4];
+    int phys[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int bi = base + u * kWaves;
+      int p = -1;
+      if (bi < nb) {
+        p = trow[b0 + bi];
+        if (p < 0 || p >= a.num_blocks) p = -1;
+      }
+      phys[u] = p;
+      if (p >= 0) {
+        const int64_t toff = (static_cast<int64_t>(p) * a.hkv + kvh) * TILE;
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk)
+          kr[u][kk] = load_bytes<KB>(kc + toff + koff + kk * 32 * KT::bytes);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vr[u][e] = load_bytes<VB>(vc + toff + voff + e * ROW);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int bi = base + u * kWaves;
+      if (bi >= nb) break;
+      const int p = phys[u];
+      const int tpos = (b0 + bi) * 16;
+      float kscale = 1.f, vscale = 1.f;
+      if (kInt8 && p >= 0) {
+        kscale = a.ks[static_cast<int64_t>(p) * a.hkv + kvh];
+        vscale = a.vs[static_cast<int64_t>(p) * a.hkv + kvh];
+      }
+      // ---- scores^T = K . Q^T
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        u32x4 kop;
+        if constexpr (kInt8) {
+          const uint32_t w0 = kr[u][kk].x, w1 = kr[u][kk].y;
+          float x[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) { x[i] = i8_at(w0, i); x[4 + i] = i8_at(w1, i); }
+          kop = u32x4{M::int_bits(x[0]) | (M::int_bits(x[1]) << 16),
+                      M::int_bits(x[2]) | (M::int_bits(x[3]) << 16),
+                      M::int_bits(x[4]) | (M::int_bits(x[5]) << 16),
+                      M::int_bits(x[6]) | (M::int_bits(x[7]) << 16)};
+        } else {
+          kop = kr[u][kk];
+        }
+        s = M::k32(kop, qop[kk], s);
+      }
+      const float sc = kscale * a.scale_log2;
+      float sv[4];
+      float tmax = kNegInf;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool valid = (p >= 0) && (tpos + 4 * kg + i < t1);
+        sv[i] = valid ? s[i] * sc : kNegInf;
+        tmax = fmaxf(tmax, sv[i]);
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float mn = fmaxf(m, tmax);
+      const float ms = (mn == kNegInf) ? 0.f : mn;
+      const float alpha = fast_exp2(m - ms);
+      m = mn;
+      float pw[4];
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pw[i] = fast_exp2(sv[i] - ms);
+        psum += pw[i];
+      }
+      l = l * alpha + psum;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) acc[j] *= alpha;
+      // ---- P^T operand as hi + lo pairs
+      float pv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pv[i] = pw[i] * vscale;
+      const uint32_t h01 = M::pack(pv[0], pv[1]);
+      const uint32_t h23 = M::pack(pv[2], pv[3]);
+      const u32x2 phi = {h01, h23};
+      const u32x2 plo = {M::pack(pv[0] - M::lo(h01), pv[1] - M::hi(h01)),
+                         M::pack(pv[2] - M::lo(h23), pv[3] - M::hi(h23))};
+      // ---- out^T += V^T . P^T; value rows past the context are zeroed first
+      u32x4 vrow[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool valid = (p >= 0) && (tpos + 4 * kg + e < t1);
+        vrow[e] = valid ? vr[u][e] : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        u32x2 vop;
+        if constexpr (kInt8) {
+          uint32_t b[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) b[e] = M::int_bits(i8_at(dw(vrow[e], j >> 2), j & 3));
+          vop = u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
+        } else {
+          vop = u32x2{half_of(vrow[0], j) | (half_of(vrow[1], j) << 16),
+                      half_of(vrow[2], j) | (half_of(vrow[3], j) << 16)};
+        }
+        acc[j] = M::k16(vop, phi, acc[j]);
+        acc[j] = M::k16(vop, plo, acc[j]);
+      }
+    }
+  }
+
+  // Sum of each head's weights over its four lanes.
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+
+  __shared__ float sm_o[kWaves][16][D];
+  __shared__ float sm_m[kWaves][16];
+  __shared__ float sm_l[kWaves][16];
+  // acc[j][i] of lane (h, kg) is element NV*(4kg + i) + j of head h's row.
+#pragma unroll
+  for (int j = 0; j < NV; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm_o[wave][r16][NV * (4 * kg + i) + j] = acc[j][i];
+  if (kg == 0) {
+    sm_m[wave][r16] = m;
+    sm_l[wave][r16] = l;
+  }
+  __syncthreads();
+  finish_rows<kWaves, 16, D>(a, sm_o, sm_m, sm_l, group, row, hbase, part, nparts);
+}
+
+template <typename QT, typename KT>
+pkv_status launch_qk(const AttnArgs& a, int D, int group, hipStream_t st) {
+  dim3 grid(a.num_parts * a.num_rows, a.hkv);
+  if (D == 64)
+    hipLaunchKernelGGL((decode_mfma_kernel<QT, KT, 64>), grid, dim3(256), 0, st, a, group);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<QT, KT, 128>), grid, dim3(256), 0, st, a, group);
+  PKV_LAUNCH_CHECK("paged attention (MFMA)");
+  return PKV_OK;
+}
+
+}  // namespace
+
+pkv_status launch_decode_mfma(const AttnArgs& a, pkv_dtype q_dt, pkv_dtype kv_dt, int D,
+                              int group, hipStream_t st) {
+  if (group > 16) return fail(PKV_ERR_UNSUPPORTED, "MFMA decode: group %d > 16", group);
+  if (q_dt == PKV_BF16)
+    return kv_dt == PKV_I8 ? launch_qk<BF16, I8>(a, D, group, st)
+                           : launch_qk<BF16, BF16>(a, D, group, st);
+  if (q_dt == PKV_F16)
+    return kv_dt == PKV_I8 ? launch_qk<F16, I8>(a, D, group, st)
+                           : launch_qk<F16, F16>(a, D, group, st);
+  return fail(PKV_ERR_UNSUPPORTED, "MFMA decode needs 16-bit q");
+}
+
+}  // namespace pkv

@@ -1,0 +1,85 @@
+"""The built library loads on a machine without a GPU and exports every
+function include/pkv.h declares (no device call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("pkv_bm_create", "pkv_seq_append", "pkv_reshape_and_cache", "pkv_copy_blocks",
+                 "pkv_paged_attention_decode", "pkv_paged_attention_reduce",
+                 "pkv_paged_attention_prefill"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    import paged_kv_cache_366_amd as pkv
+    lib = pkv.load()
+    raw = ctypes.CDLL(pkv.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(raw, n)]
+    assert not missing, missing
+    from paged_kv_cache_366_amd._lib import SIGNATURES
+    assert set(SIGNATURES) == set(declared_functions())
+    assert lib.pkv_version().decode().startswith("pkv")
+
+
+def test_binding_exposes_the_same_names():
+    import paged_kv_cache_366_amd as pkv
+    for n in declared_functions():
+        if n in ("pkv_last_error",):
+            continue
+        assert hasattr(pkv, n), n
+
+
+def test_device_entry_points_reject_bad_arguments_without_a_gpu():
+    """Argument checks run on the host before any HIP call."""
+    import paged_kv_cache_366_amd as pkv
+    from paged_kv_cache_366_amd._lib import PKV_BF16, PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED
+    lib = pkv.load()
+    # head_dim 96 is unsupported
+    st = lib.pkv_paged_attention_decode(None, PKV_BF16, None, PKV_BF16, None, None, PKV_BF16,
+                                        None, None, None, 8, None, 128, 1, 8, 8, 96, 16, 10,
+                                        0.1, 0, 0, None, 0, None)
+    assert st == PKV_ERR_UNSUPPORTED
+    # Hq not a multiple of Hkv
+    st = lib.pkv_paged_attention_decode(None, PKV_BF16, None, PKV_BF16, None, None, PKV_BF16,
+                                        None, None, None, 8, None, 128, 1, 6, 4, 128, 16, 10,
+                                        0.1, 0, 0, None, 0, None)
+    assert st == PKV_ERR_INVALID
+    assert b"multiple" in lib.pkv_last_error()
+    # partition size not a multiple of the block size
+    st = lib.pkv_paged_attention_decode(None, PKV_BF16, None, PKV_BF16, None, None, PKV_BF16,
+                                        None, None, None, 8, None, 128, 1, 8, 8, 128, 16, 10,
+                                        0.1, 40, 0, None, 0, None)
+    assert st == PKV_ERR_INVALID
+    # max_context_len larger than the table can address
+    st = lib.pkv_paged_attention_decode(None, PKV_BF16, None, PKV_BF16, None, None, PKV_BF16,
+                                        None, None, None, 8, None, 129, 1, 8, 8, 128, 16, 10,
+                                        0.1, 0, 0, None, 0, None)
+    assert st == PKV_ERR_INVALID
+    # int8 reshape_and_cache is not provided
+    st = lib.pkv_reshape_and_cache(None, None, None, None, None, 4, 0, 0, 8, 128, 16, 10, 3, None)
+    assert st == PKV_ERR_UNSUPPORTED
+
+
+def test_workspace_size_formula():
+    import paged_kv_cache_366_amd as pkv
+    assert pkv.pkv_decode_workspace_bytes(64, 32, 128, 2048, 0) == 0
+    assert pkv.pkv_decode_workspace_bytes(64, 32, 128, 512, 512) == 0
+    n = pkv.pkv_decode_workspace_bytes(16, 64, 128, 32768, 512)
+    parts = 64
+    o = 16 * 64 * parts * 128 * 4
+    ml = 16 * 64 * parts * 2 * 4
+    assert n == -(-o // 256) * 256 + -(-ml // 256) * 256

@@ -120,6 +120,13 @@ def test_context_zero_gives_zero_row(tiny):
     assert np.all(out[2] == 0)
 
 
+def test_table_entry_outside_the_pool_is_rejected(tiny):
+    bad = tiny.block_tables.copy()
+    bad[1, 2] = -1
+    with pytest.raises(ValueError):
+        A.decode(tiny.q, tiny.k_cache, tiny.v_cache, bad, tiny.context_lens, tiny.scale)
+
+
 def test_two_tokens_match_logistic_closed_form():
     c = W.decode_case(11, 1, 1, 1, 16, lens=[2], dtype="f32", num_blocks=1, keep_logical=True)
     K = c.k_logical[0][:, 0].astype(np.float64)
