@@ -1,0 +1,306 @@
+"""Benchmark of one paged decode step at the LLaMA-7B attention shape on one GPU.
+
+    python bench.py [--steps K] [--warmup W] [--partition P] [--algo auto|wave|mfma]
+                    [--no-cpu-baseline] [--calib-copy-mib M]
+
+Workload (7B-shape decode, bf16): 64 sequences, 32 query heads = 32 KV heads,
+head_dim 128, 16-token blocks, context lengths uniform on [128, 2048] (each
+includes the token being decoded), a pool of ceil(1.25 x the blocks needed)
+blocks whose free list starts as a seeded random permutation, q/K/V drawn
+N(0, 1) in fp32 and rounded to bf16.
+
+Set-up (untimed): the C++ block manager creates each sequence with its
+n - 1 cached tokens and appends the current token (slot mapping); the pool
+is filled along the exported block tables; the current token's K/V rows are
+held back and handed to reshape_and_cache inside the step.
+
+One step (timed, inputs resident in HBM): reshape_and_cache of the 64 new
+K/V rows through the slot mapping -> split-K paged decode attention (main
+kernel) -> partition reduce.  HIP events on the launch stream bracket each
+kernel; the main kernel's average duration gives the roofline figure.
+
+The printed JSON line carries the step throughput in KV GB/s (algorithmic
+bytes: K/V rows every sequence attends to, q, out, the table entries and
+lengths read, and the new rows moved by reshape_and_cache), the roofline of
+the main decode kernel, and the CPU oracle timed on the host over the same
+batch as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BLOCK = 16
+
+# HBM traffic of the main decode kernel per launch, from rocprofv3 --pmc
+# FETCH_SIZE and WRITE_SIZE on this workload (seed 1, partition 256),
+# calibrated against a device copy of known size.  Valid only for the kernel
+# sources whose hash is recorded; a changed kernel reports null.
+TRAFFIC = {
+    "sources_sha1": None,
+    "bytes_per_launch": None,
+}
+KERNEL_SOURCES = ("decode_wave.hip", "attention_common.h", "device_common.h")
+
+
+def kernel_sources_sha1() -> str:
+    h = hashlib.sha1()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_366_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+class Workload:
+    """7B-shape decode batch, built through the library's block manager."""
+
+    def __init__(self, seed: int = 1, num_seqs: int = 64, heads: int = 32, head_dim: int = 128,
+                 len_range=(128, 2048)):
+        import paged_kv_cache_366_amd as pkv
+        from synth import workloads as W
+
+        rng = np.random.default_rng(seed)
+        self.S, self.H, self.D = num_seqs, heads, head_dim
+        lens = W.draw_lengths(rng, num_seqs, *len_range)
+        nb = W.pool_size(lens)
+        perm = W.draw_permutation(rng, nb)
+        t0 = time.perf_counter()
+        bm = pkv.pkv_bm_create(nb, BLOCK, perm)
+        seqs = [pkv.pkv_seq_create(bm, int(n) - 1) for n in lens]
+        t1 = time.perf_counter()
+        slots, cow = pkv.pkv_seq_append_batch(bm, seqs)
+        self.max_blocks = int(max(W.blocks_for(n) for n in lens))
+        tables, lens_bm = pkv.pkv_seq_export(bm, seqs, self.max_blocks)
+        t2 = time.perf_counter()
+        assert len(cow) == 0 and np.array_equal(lens_bm, lens)
+        self.host_bm = {"create_us": (t1 - t0) * 1e6, "append_export_us": (t2 - t1) * 1e6}
+        self.bm, self.seqs = bm, seqs
+        q = W.draw_normal(rng, (num_seqs, heads, head_dim), "bf16")
+        kc, vc, _, _ = W.draw_paged_kv(rng, tables, lens, nb, heads, head_dim, "bf16")
+        self.lens, self.tables, self.slots, self.q = lens, tables, slots, q
+        self.kc_full, self.vc_full = kc, vc          # with the current token (oracle side)
+        blk, row = slots // BLOCK, slots % BLOCK
+        self.new_k = kc[blk, :, row, :].copy()       # [S, H, D]
+        self.new_v = vc[blk, :, row, :].copy()
+        self.num_blocks = nb
+        self.scale = np.float32(1.0 / math.sqrt(head_dim))
+
+    # algorithmic bytes (bf16 everywhere, fp32 output)
+    def kv_bytes(self) -> int:
+        return int(self.lens.astype(np.int64).sum()) * self.H * self.D * 2 * 2
+
+    def main_kernel_bytes(self) -> int:
+        tbl = int(sum(W_blocks(n) for n in self.lens)) * 4
+        return self.kv_bytes() + self.S * self.H * self.D * 2 + tbl + self.S * 4
+
+    def step_bytes(self) -> int:
+        out = self.S * self.H * self.D * 4
+        rc = self.S * self.H * self.D * 2 * 2 * 2 + self.S * 4   # read new K,V + write them
+        return self.main_kernel_bytes() + out + rc
+
+
+def W_blocks(n) -> int:
+    return -(-int(n) // BLOCK)
+
+
+def to_dev_bf16(x, torch):
+    from synth import workloads as W
+    bits = W.storage_array(x, "bf16").view(np.int16)
+    return torch.from_numpy(bits).to("cuda").view(torch.bfloat16)
+
+
+def cpu_baseline(wl: Workload, min_seconds: float = 10.0, max_reps: int = 8):
+    """The oracle over the whole batch, repeated until at least min_seconds."""
+    from oracle import attention as A
+
+    reps, wall, cpu = 0, 0.0, 0.0
+    out = None
+    while reps < max_reps and (wall < min_seconds or reps == 0):
+        c0, t0 = time.process_time(), time.perf_counter()
+        out = A.decode(wl.q, wl.kc_full, wl.vc_full, wl.tables, wl.lens, wl.scale)
+        wall += time.perf_counter() - t0
+        cpu += time.process_time() - c0
+        reps += 1
+    per_call = wall / reps
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - informational only
+        blas = None
+    res = {
+        "value": wl.kv_bytes() / per_call / 1e9,
+        "unit": "GB/s",
+        "cores": max(1, int(math.ceil(cpu / wall - 0.05))),
+        "kind": "oracle",
+        "sample": f"full batch ({wl.S} sequences, {int(wl.lens.sum())} context tokens) x {reps} "
+                  f"passes of the float64 oracle, {per_call:.2f} s per pass",
+        "tokens_per_s": wl.S / per_call,
+        "host_cores_visible": len(os.sched_getaffinity(0)),
+        "blas_threads": blas,
+    }
+    return res, out
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--partition", type=int, default=256,
+                    help="split-K partition size in tokens (0 = no split)")
+    ap.add_argument("--algo", choices=("auto", "wave", "mfma"), default="auto")
+    ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one device-to-device copy of this many MiB (a known-size "
+                         "kernel for scaling rocprofv3 byte counters)")
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {a.gpus}); the paged decode path has no "
+              "multi-GPU mode in this build", file=sys.stderr)
+        return 2
+
+    import torch
+    import paged_kv_cache_366_amd as pkv
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    pkv.load()
+    algo = {"auto": pkv.PKV_ALGO_AUTO, "wave": pkv.PKV_ALGO_WAVE, "mfma": pkv.PKV_ALGO_MFMA}[a.algo]
+
+    print("[bench] building the 7B-shape decode workload on the host", file=sys.stderr, flush=True)
+    wl = Workload(seed=a.seed)
+    dev = "cuda"
+    kc = to_dev_bf16(wl.kc_full, torch)
+    vc = to_dev_bf16(wl.vc_full, torch)
+    blk, row = wl.slots // BLOCK, wl.slots % BLOCK
+    kc[torch.from_numpy(blk.astype(np.int64)).to(dev), :, torch.from_numpy(row.astype(np.int64)).to(dev), :] = float("nan")
+    vc[torch.from_numpy(blk.astype(np.int64)).to(dev), :, torch.from_numpy(row.astype(np.int64)).to(dev), :] = float("nan")
+    q = to_dev_bf16(wl.q, torch)
+    new_k = to_dev_bf16(wl.new_k, torch)
+    new_v = to_dev_bf16(wl.new_v, torch)
+    slots = torch.from_numpy(wl.slots.astype(np.int32)).to(dev)
+    tables = torch.from_numpy(wl.tables).to(dev)
+    lens = torch.from_numpy(wl.lens).to(dev)
+    max_ctx = int(wl.lens.max())
+    out = torch.empty((wl.S, wl.H, wl.D), dtype=torch.float32, device=dev)
+    ws_bytes = pkv.pkv_decode_workspace_bytes(wl.S, wl.H, wl.D, max_ctx, a.partition)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        pkv.pkv_reshape_and_cache(new_k, new_v, kc, vc, slots)
+        if ev is not None:
+            ev[1].record(stream)
+        pkv.pkv_paged_attention_decode_partials(out, q, kc, vc, tables, lens, max_ctx,
+                                                float(wl.scale), a.partition, algo,
+                                                workspace=ws)
+        if ev is not None:
+            ev[2].record(stream)
+        pkv.pkv_paged_attention_reduce(out, lens, max_ctx, a.partition, ws)
+        if ev is not None:
+            ev[3].record(stream)
+
+    print(f"[bench] warmup {a.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
+    print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    rc_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    main_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    red_ms = [e[2].elapsed_time(e[3]) for e in evs]
+
+    if a.calib_copy_mib:
+        n = a.calib_copy_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    ms_per_step = wall * 1e3 / a.steps
+    main_avg = float(np.mean(main_ms))
+    step_bytes = wl.step_bytes()
+    main_bytes = wl.main_kernel_bytes()
+    achieved = main_bytes / (main_avg * 1e-3) / 1e9
+    traffic = None
+    if TRAFFIC["sources_sha1"] == kernel_sources_sha1() and TRAFFIC["bytes_per_launch"]:
+        traffic = TRAFFIC["bytes_per_launch"]
+
+    result = {
+        "metric": "paged decode attention: KV GB/s (% of HBM peak) + tokens/s at 7B shape",
+        "value": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "7B-shape paged decode, bf16 KV and q, fp32 accumulate: 64 sequences, "
+                        "32 heads MHA, head_dim 128, block_size 16, contexts U[128, 2048], "
+                        "pool 1.25x, random placement; step = reshape_and_cache + decode + reduce",
+            "num_seqs": wl.S, "heads": wl.H, "head_dim": wl.D, "block_size": BLOCK,
+            "context_tokens": int(wl.lens.sum()), "num_blocks": wl.num_blocks,
+            "partition_tokens": a.partition, "algo": a.algo, "seed": a.seed,
+        },
+        "tokens_per_s": wl.S / (ms_per_step * 1e-3),
+        "hbm_frac_step": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "kernel_ms": {"reshape_and_cache": float(np.mean(rc_ms)), "decode_main": main_avg,
+                      "decode_main_median": float(np.median(main_ms)),
+                      "reduce": float(np.mean(red_ms))},
+        "bytes": {"step": step_bytes, "decode_main": main_bytes, "kv": wl.kv_bytes()},
+        "roofline": {
+            "kernel": "decode_wave_kernel (split-K main)",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+        },
+        "host_block_manager_us": wl.host_bm,
+        "cpu_baseline": None,
+    }
+
+    if not a.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on the same batch", file=sys.stderr, flush=True)
+        cb, ref = cpu_baseline(wl)
+        result["cpu_baseline"] = cb
+        got = out.cpu().numpy().astype(np.float64)
+        result["max_abs_err_vs_oracle"] = float(np.abs(got - ref).max())
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
