@@ -45,12 +45,13 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BLOCK = 16
 
 # HBM traffic of the main decode kernel per launch, from rocprofv3 --pmc
-# FETCH_SIZE and WRITE_SIZE on this workload (seed 1, partition 256),
-# calibrated against a device copy of known size.  Valid only for the kernel
+# FETCH_SIZE (546,140 KiB, scaled by 1 / 0.50004: the factor an elementwise
+# kernel that reads exactly 1 GiB shows) plus WRITE_SIZE (4,860 KiB, factor
+# 1.0) on this workload (seed 1, partition 256).  Valid only for the kernel
 # sources whose hash is recorded; a changed kernel reports null.
 TRAFFIC = {
-    "sources_sha1": None,
-    "bytes_per_launch": None,
+    "sources_sha1": "f33ccb9fb0077f413454454b958fa31dfeed21ea",
+    "bytes_per_launch": 1092193 * 1024 + 4860 * 1024,
 }
 KERNEL_SOURCES = ("decode_wave.hip", "attention_common.h", "device_common.h")
 
@@ -164,8 +165,8 @@ def main(argv=None) -> int:
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
-                    help="also run one device-to-device copy of this many MiB (a known-size "
-                         "kernel for scaling rocprofv3 byte counters)")
+                    help="also run one elementwise kernel that reads and writes this many MiB "
+                         "(a known-size kernel for scaling rocprofv3 byte counters)")
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {a.gpus}); the paged decode path has no "
@@ -235,11 +236,12 @@ def main(argv=None) -> int:
     red_ms = [e[2].elapsed_time(e[3]) for e in evs]
 
     if a.calib_copy_mib:
+        # an elementwise kernel that reads and writes exactly n bytes
         n = a.calib_copy_mib * (1 << 20)
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        torch.bitwise_not(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
 

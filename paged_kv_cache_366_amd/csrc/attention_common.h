@@ -31,28 +31,78 @@ struct AttnArgs {
   float scale_log2;          // scale * log2(e): scores are kept in the log2 domain
 };
 
-// Which sequence a query row belongs to, and that row's context (the
-// number of keys it attends).  Decode: row s, keys [0, lens[s]).  Chunked
-// prefill: row i of sequence s's chunk sits at position lens[s] - qlen + i
-// and attends keys [0, that position].  The result is clamped to what the
-// table and max_ctx can address, so no read leaves the table row.
-__device__ __forceinline__ void row_context(const AttnArgs& a, int row, int& seq, int& ctx) {
-  if (a.qsl == nullptr) {
-    seq = row;
-    ctx = a.lens[row];
-  } else {
-    int lo = 0, hi = a.num_seqs - 1;  // largest s with qsl[s] <= row
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.qsl[mid] <= row) lo = mid; else hi = mid - 1;
-    }
-    seq = lo;
+// Which sequence a query row belongs to.  Decode: row s is sequence s.
+// Chunked prefill: the sequence whose query range [qsl[s], qsl[s+1]) holds
+// the row.
+__device__ __forceinline__ int row_seq(const AttnArgs& a, int row) {
+  if (a.qsl == nullptr) return row;
+  int lo = 0, hi = a.num_seqs - 1;  // largest s with qsl[s] <= row
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.qsl[mid] <= row) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// The number of keys a query row attends.  Decode: keys [0, lens[s]).
+// Chunked prefill: row i of sequence s's chunk sits at position
+// lens[s] - qlen + i and attends keys [0, that position].  The result is
+// clamped to what the table and max_ctx can address, so no read leaves the
+// table row.
+__device__ __forceinline__ int row_ctx(const AttnArgs& a, int row, int seq) {
+  int ctx = a.lens[seq];
+  if (a.qsl != nullptr) {
     const int qlen = a.qsl[seq + 1] - a.qsl[seq];
-    ctx = a.lens[seq] - qlen + (row - a.qsl[seq]) + 1;
+    ctx = ctx - qlen + (row - a.qsl[seq]) + 1;
   }
   const int cap = min(a.max_ctx, a.max_blocks * 16);
-  ctx = max(0, min(ctx, cap));
+  return max(0, min(ctx, cap));
 }
+
+__device__ __forceinline__ void row_context(const AttnArgs& a, int row, int& seq, int& ctx) {
+  seq = row_seq(a, row);
+  ctx = row_ctx(a, row, seq);
+}
+
+// Workgroups of the decode kernels.  Each owns one (query row, context
+// partition, head group); the head group varies fastest along the grid.
+// The tiles of all KV heads of one block are adjacent in the pool, so the
+// workgroups that run together read neighbouring 4 KiB tiles of a few
+// blocks, and their reads spread over every memory channel.  (With the head
+// as the slow index, concurrent reads all sit at one offset modulo the
+// block stride and crowd a few channels: on MI355X that costs about a
+// quarter of the bandwidth.)
+constexpr int kDecodeWaves = 4;
+
+struct WgCoord {
+  int row, part, hg;
+};
+__device__ __forceinline__ WgCoord wg_coord(int ngroups, int num_parts) {
+  WgCoord c;
+  const int bid = blockIdx.x;
+  c.hg = bid % ngroups;
+  const int rest = bid / ngroups;
+  c.part = rest % num_parts;
+  c.row = rest / num_parts;
+  return c;
+}
+
+// Block-table entries of one wavefront's share of a partition.  Wave w of
+// the workgroup takes the partition's blocks w, w + 4, w + 8, ...; its k-th
+// block is entry `b0 + w + 4k` of the table row.  Lane i holds the entry
+// for k = k0 + i, so one vector load covers 64 of the wave's blocks and
+// each step reads its block id with a lane read, off the load path.
+// Entries at or past `bmax` (the end of the partition or of the table row)
+// are not read.
+struct TableChunk {
+  int entry = -1;
+  __device__ __forceinline__ void fetch(const int32_t* trow, int b0, int wave, int k0, int bmax) {
+    const int bi = wave + kDecodeWaves * (k0 + static_cast<int>(threadIdx.x & 63));
+    entry = bi < bmax ? trow[b0 + bi] : -1;
+  }
+  // Entry of the wave's block k (k0 <= k < k0 + 64); k is wave-uniform.
+  __device__ __forceinline__ int get(int k) const { return __builtin_amdgcn_readlane(entry, k & 63); }
+};
 
 __device__ __forceinline__ void store_out(const AttnArgs& a, int64_t idx, float v) {
   if (a.out_kind == kOutF32)

@@ -36,8 +36,12 @@
 namespace pkv {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kUnroll = 2;
+constexpr int kWaves = kDecodeWaves;
+#ifndef PKV_MFMA_UNROLL
+#define PKV_MFMA_UNROLL 2
+#endif
+constexpr int kUnroll = PKV_MFMA_UNROLL;   // tiles of K and V in flight per wavefront
+static_assert(64 % kUnroll == 0, "the unroll must divide the table chunk");
 
 template <typename T> struct Mx;
 template <> struct Mx<BF16> {
@@ -122,24 +126,24 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttnArgs a, int group)
   constexpr int TILE = 16 * ROW;
   using M = Mx<QT>;
 
-  const int part = blockIdx.x % a.num_parts;
-  const int row = blockIdx.x / a.num_parts;
-  const int kvh = blockIdx.y;
-  const int hbase = kvh * group;
-
-  int seq, ctx;
-  row_context(a, row, seq, ctx);
-  const int nparts = (ctx + a.part_tokens - 1) / a.part_tokens;
-  if (part >= max(nparts, 1)) return;
-  const int t0 = part * a.part_tokens;
-  const int t1 = min(ctx, t0 + a.part_tokens);
-  const int b0 = t0 >> 4;
-  const int nb = ((t1 + 15) >> 4) - b0;
-
   const int wave = wave_uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15;   // head (B/D operand column) or token / dim row (A operand)
   const int kg = lane >> 4;
+
+  const WgCoord wc = wg_coord(a.hkv, a.num_parts);
+  const int part = wc.part;
+  const int row = wc.row;
+  const int kvh = wc.hg;
+  const int hbase = kvh * group;
+
+  // Table entries, q and the context length go out together.
+  const int seq = row_seq(a, row);
+  const int b0 = (part * a.part_tokens) >> 4;
+  const int bmax = min(a.part_tokens >> 4, a.max_blocks - b0);
+  const int32_t* trow = a.tables + static_cast<int64_t>(seq) * a.max_blocks;
+  TableChunk tc;
+  tc.fetch(trow, b0, wave, 0, bmax);
 
   // Q^T operand: head r16, elements 32kk + 8kg .. +7.
   u32x4 qop[NK];
@@ -154,27 +158,34 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttnArgs a, int group)
     }
   }
 
+  const int ctx = row_ctx(a, row, seq);
+  const int nparts = (ctx + a.part_tokens - 1) / a.part_tokens;
+  if (part >= max(nparts, 1)) return;
+  const int t0 = part * a.part_tokens;
+  const int t1 = min(ctx, t0 + a.part_tokens);
+  const int nb = ((t1 + 15) >> 4) - b0;
+  const int nbw = nb > wave ? (nb - wave + kWaves - 1) / kWaves : 0;   // this wave's tiles
+
   float m = kNegInf, l = 0.f;
   f32x4 acc[NV];
 #pragma unroll
   for (int j = 0; j < NV; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int32_t* trow = a.tables + static_cast<int64_t>(seq) * a.max_blocks;
   const uint8_t* kc = static_cast<const uint8_t*>(a.kc);
   const uint8_t* vc = static_cast<const uint8_t*>(a.vc);
   // lane offsets inside a tile
   const int koff = r16 * ROW + 8 * kg * KT::bytes;          // + kk * 32 elements
   const int voff = (4 * kg) * ROW + r16 * VB;               // + e * ROW
 
-  for (int base = wave; base < nb; base += kWaves * kUnroll) {
+  for (int k = 0; k < nbw; k += kUnroll) {
+    if (k > 0 && (k & 63) == 0) tc.fetch(trow, b0, wave, k, bmax);
     u32x4 kr[kUnroll][NK], vr[kUnroll][4];
     int phys[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int bi = base + u * kWaves;
       int p = -1;
-      if (bi < nb) {
-        p = trow[b0 + bi];
+      if (k + u < nbw) {
+        p = tc.get(k + u);
         if (p < 0 || p >= a.num_blocks) p = -1;
       }
       phys[u] = p;
@@ -189,10 +200,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttnArgs a, int group)
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int bi = base + u * kWaves;
-      if (bi >= nb) break;
+      if (k + u >= nbw) break;
       const int p = phys[u];
-      const int tpos = (b0 + bi) * 16;
+      const int tpos = (b0 + wave + kWaves * (k + u)) * 16;
       float kscale = 1.f, vscale = 1.f;
       if (kInt8 && p >= 0) {
         kscale = a.ks[static_cast<int64_t>(p) * a.hkv + kvh];
@@ -298,7 +308,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttnArgs a, int group)
 
 template <typename QT, typename KT>
 pkv_status launch_qk(const AttnArgs& a, int D, int group, hipStream_t st) {
-  dim3 grid(a.num_parts * a.num_rows, a.hkv);
+  dim3 grid(a.num_parts * a.num_rows * a.hkv);
   if (D == 64)
     hipLaunchKernelGGL((decode_mfma_kernel<QT, KT, 64>), grid, dim3(256), 0, st, a, group);
   else

@@ -19,16 +19,77 @@
 // with the token's score.  The lanes that hold token t's K chunk also load
 // its V chunk, so the softmax weight never leaves its lanes: the PV product
 // accumulates per lane, and rows, then wavefronts, are merged once at the
-// end.  Wavefronts take blocks round-robin and keep two blocks of K and V
-// (16 KiB) in flight each, which with several workgroups per CU keeps enough
-// bytes outstanding to run HBM-bound.
+// end.  Wavefronts take blocks round-robin, one block of K and V in flight
+// each; the kernel stays at 63 VGPRs so eight wavefronts share a SIMD.
+// For 16-bit keys the score uses packed dot2 instructions on the raw pairs,
+// and only the partly filled last block of a context pays for per-row
+// masking.
+//
+// Workgroups are ordered with the head group fastest (see wg_coord): the
+// KV-head tiles of one block are adjacent in the pool, so concurrent
+// workgroups spread their reads over all memory channels.
+#include <type_traits>
+
 #include "attention_common.h"
 
 namespace pkv {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kUnroll = 2;
+constexpr int kWaves = kDecodeWaves;
+
+// Dot product of one 16-byte chunk of 16-bit keys with the matching q
+// chunk, both as packed pairs: v_dot2 forms the two exact products and adds
+// them to the fp32 accumulator, two elements per instruction and no
+// separate widening.
+template <typename T> struct PackedDot { static constexpr bool ok = false; };
+template <> struct PackedDot<BF16> {
+  static constexpr bool ok = true;
+  typedef __bf16 x2 __attribute__((ext_vector_type(2)));
+  __device__ __forceinline__ static float step(uint32_t k, uint32_t q, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(x2, k), __builtin_bit_cast(x2, q), acc,
+                                           false);
+  }
+};
+template <> struct PackedDot<F16> {
+  static constexpr bool ok = true;
+  typedef _Float16 x2 __attribute__((ext_vector_type(2)));
+  __device__ __forceinline__ static float step(uint32_t k, uint32_t q, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(x2, k), __builtin_bit_cast(x2, q), acc, false);
+  }
+};
+template <typename T>
+__device__ __forceinline__ float chunk_dot(const u32x4& k, const u32x4& q) {
+  float acc = PackedDot<T>::step(k.x, q.x, 0.f);
+  acc = PackedDot<T>::step(k.y, q.y, acc);
+  acc = PackedDot<T>::step(k.z, q.z, acc);
+  return PackedDot<T>::step(k.w, q.w, acc);
+}
+
+// Unpack one dword of stored values to floats (exact widening).
+template <typename T> struct UnpackDw;
+template <> struct UnpackDw<F32> {
+  static constexpr int n = 1;
+  __device__ __forceinline__ static void run(uint32_t w, float* x) { x[0] = __uint_as_float(w); }
+};
+template <> struct UnpackDw<BF16> {
+  static constexpr int n = 2;
+  __device__ __forceinline__ static void run(uint32_t w, float* x) { x[0] = bf16_lo(w); x[1] = bf16_hi(w); }
+};
+template <> struct UnpackDw<F16> {
+  static constexpr int n = 2;
+  __device__ __forceinline__ static void run(uint32_t w, float* x) { x[0] = f16_lo(w); x[1] = f16_hi(w); }
+};
+template <> struct UnpackDw<I8> {
+  static constexpr int n = 4;
+  __device__ __forceinline__ static void run(uint32_t w, float* x) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[k] = i8_at(w, k);
+  }
+};
+
+__device__ __forceinline__ uint32_t dword(const u32x4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
 
 template <typename QT, typename KT, int D, int G>
 __global__ __launch_bounds__(256) void decode_wave_kernel(AttnArgs a) {
@@ -41,39 +102,53 @@ __global__ __launch_bounds__(256) void decode_wave_kernel(AttnArgs a) {
   static_assert(C >= 4 && C <= 64 && NL >= 1, "unsupported head_dim / dtype");
   constexpr bool kInt8 = (EB == 1);
 
-  const int part = blockIdx.x % a.num_parts;
-  const int row = blockIdx.x / a.num_parts;
-  const int hgroups = a.hq / G;                       // workgroups per row along y
-  const int hbase = blockIdx.y * G;                   // first query head
+  const WgCoord wc = wg_coord(a.hq / G, a.num_parts);
+  const int part = wc.part;
+  const int row = wc.row;
+  const int hbase = wc.hg * G;                        // first query head
   const int kvh = hbase / (a.hq / a.hkv);
-  (void)hgroups;
-
-  int seq, ctx;
-  row_context(a, row, seq, ctx);
-  const int nparts = (ctx + a.part_tokens - 1) / a.part_tokens;
-  if (part >= max(nparts, 1)) return;
-
-  const int t0 = part * a.part_tokens;
-  const int t1 = min(ctx, t0 + a.part_tokens);
-  const int b0 = t0 >> 4;
-  const int nb = ((t1 + 15) >> 4) - b0;
 
   const int wave = wave_uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int c = lane % C;
   const int u = lane / C;
 
-  // q slice of every head of the group: elements [c*E, c*E + E).
+  // The table entries, q and the context length do not depend on each
+  // other: their loads go out together.
+  const int seq = row_seq(a, row);
+  const int b0 = (part * a.part_tokens) >> 4;
+  const int bmax = min(a.part_tokens >> 4, a.max_blocks - b0);
+  const int32_t* trow = a.tables + static_cast<int64_t>(seq) * a.max_blocks;
+  TableChunk tc;
+  tc.fetch(trow, b0, wave, 0, bmax);
+
+  // q slice of every head of the group: elements [c*E, c*E + E), as
+  // floats, or as the raw 16-byte chunk when keys and q share a 16-bit type.
+  constexpr bool kPacked = PackedDot<KT>::ok && std::is_same<QT, KT>::value;
   float qf[G][E];
+  u32x4 qpk[G];
   {
     const typename QT::raw* qp = static_cast<const typename QT::raw*>(a.q);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int64_t off = (static_cast<int64_t>(row) * a.hq + hbase + g) * D + c * E;
+      if constexpr (kPacked) {
+        qpk[g] = *reinterpret_cast<const u32x4*>(qp + off);
+      } else {
 #pragma unroll
-      for (int e = 0; e < E; ++e) qf[g][e] = load_elem<QT>(qp, off + e);
+        for (int e = 0; e < E; ++e) qf[g][e] = load_elem<QT>(qp, off + e);
+      }
     }
   }
+
+  const int ctx = row_ctx(a, row, seq);
+  const int nparts = (ctx + a.part_tokens - 1) / a.part_tokens;
+  if (part >= max(nparts, 1)) return;
+
+  const int t0 = part * a.part_tokens;
+  const int t1 = min(ctx, t0 + a.part_tokens);
+  const int nb = ((t1 + 15) >> 4) - b0;
+  const int nbw = nb > wave ? (nb - wave + kWaves - 1) / kWaves : 0;   // this wave's blocks
 
   float m[G], l[G], o[G][E];
 #pragma unroll
@@ -84,93 +159,122 @@ __global__ __launch_bounds__(256) void decode_wave_kernel(AttnArgs a) {
     for (int e = 0; e < E; ++e) o[g][e] = 0.f;
   }
 
-  const int32_t* trow = a.tables + static_cast<int64_t>(seq) * a.max_blocks;
   const uint8_t* kbase = static_cast<const uint8_t*>(a.kc) + lane * 16;
   const uint8_t* vbase = static_cast<const uint8_t*>(a.vc) + lane * 16;
 
-  for (int base = wave; base < nb; base += kWaves * kUnroll) {
-    u32x4 kr[kUnroll][NL], vr[kUnroll][NL];
-    int phys[kUnroll];
+  // One block: scores of this lane's tokens for every head, the online
+  // softmax update, and the weighted sum of the value rows.  `masked` is set
+  // only for the partly filled last block of the context: its rows past the
+  // context may hold anything (NaN included), so they are zeroed, not just
+  // given zero weight.  Whole blocks run without any per-row test.
+  auto block_step = [&](auto masked_tag, const u32x4 (&kr)[NL], const u32x4 (&vr)[NL], int tpos,
+                        float ksc, float vsc) {
+    constexpr bool masked = decltype(masked_tag)::value;
+    float s[G][NL];
 #pragma unroll
-    for (int k = 0; k < kUnroll; ++k) {
-      const int bi = base + k * kWaves;
-      int p = -1;
-      if (bi < nb) {
-        p = trow[b0 + bi];
-        if (p < 0 || p >= a.num_blocks) p = -1;   // outside the pool: treated as masked
-      }
-      phys[k] = p;
-      if (p >= 0) {
-        const int64_t toff = (static_cast<int64_t>(p) * a.hkv + kvh) * TILE;
-#pragma unroll
-        for (int j = 0; j < NL; ++j) {
-          kr[k][j] = *reinterpret_cast<const u32x4*>(kbase + toff + j * 1024);
-          vr[k][j] = *reinterpret_cast<const u32x4*>(vbase + toff + j * 1024);
-        }
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < kUnroll; ++k) {
-      const int bi = base + k * kWaves;
-      if (bi >= nb) break;
-      const int p = phys[k];
-      const int tpos = (b0 + bi) * 16;
-      float kscale = 1.f, vscale = 1.f;
-      if (kInt8 && p >= 0) {
-        kscale = a.ks[static_cast<int64_t>(p) * a.hkv + kvh];
-        vscale = a.vs[static_cast<int64_t>(p) * a.hkv + kvh];
-      }
-      // scores of this lane's NL tokens for every head
-      float s[G][NL];
-#pragma unroll
-      for (int j = 0; j < NL; ++j) {
-        float kx[E];
-        Unpack<KT>::run(kr[k][j], kx);
-        const int tok = tpos + j * TPL + u;
-        const bool valid = (p >= 0) && tok < t1;
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float part_dot = 0.f;
-#pragma unroll
-          for (int e = 0; e < E; ++e) part_dot = fmaf(qf[g][e], kx[e], part_dot);
-          const float dot = group_sum<C>(part_dot);
-          s[g][j] = valid ? dot * kscale * a.scale_log2 : kNegInf;
-        }
-      }
-      float pw[G][NL];
+    for (int j = 0; j < NL; ++j) {
+      const bool valid = !masked || (tpos + j * TPL + u < t1);
+      float kx[E];
+      if constexpr (!kPacked) Unpack<KT>::run(kr[j], kx);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        float tmax = s[g][0];
+        float part_dot = 0.f;
+        if constexpr (kPacked) {
+          part_dot = chunk_dot<KT>(kr[j], qpk[g]);
+        } else {
 #pragma unroll
-        for (int j = 1; j < NL; ++j) tmax = fmaxf(tmax, s[g][j]);
-        const float mn = fmaxf(m[g], tmax);
-        const float ms = (mn == kNegInf) ? 0.f : mn;
-        const float alpha = fast_exp2(m[g] - ms);
-        float psum = 0.f;
-#pragma unroll
-        for (int j = 0; j < NL; ++j) {
-          pw[g][j] = fast_exp2(s[g][j] - ms);
-          psum += pw[g][j];
+          for (int e = 0; e < E; ++e) part_dot = fmaf(qf[g][e], kx[e], part_dot);
         }
-        l[g] = l[g] * alpha + psum;
-        m[g] = mn;
-#pragma unroll
-        for (int e = 0; e < E; ++e) o[g][e] *= alpha;
-      }
-#pragma unroll
-      for (int j = 0; j < NL; ++j) {
-        float vx[E];
-        Unpack<KT>::run(vr[k][j], vx);
-        const int tok = tpos + j * TPL + u;
-        const bool valid = (p >= 0) && tok < t1;
-#pragma unroll
-        for (int e = 0; e < E; ++e) vx[e] = valid ? vx[e] * vscale : 0.f;
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int e = 0; e < E; ++e) o[g][e] = fmaf(pw[g][j], vx[e], o[g][e]);
+        const float dot = group_sum<C>(part_dot);
+        s[g][j] = valid ? dot * (ksc * a.scale_log2) : kNegInf;
       }
     }
+    float pw[G][NL];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float tmax = s[g][0];
+#pragma unroll
+      for (int j = 1; j < NL; ++j) tmax = fmaxf(tmax, s[g][j]);
+      const float mn = fmaxf(m[g], tmax);
+      const float ms = (mn == kNegInf) ? 0.f : mn;
+      const float alpha = fast_exp2(m[g] - ms);
+      float psum = 0.f;
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        pw[g][j] = fast_exp2(s[g][j] - ms);
+        psum += pw[g][j];
+      }
+      l[g] = l[g] * alpha + psum;
+      m[g] = mn;
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[g][e] *= alpha;
+      if (kInt8) {
+#pragma unroll
+        for (int j = 0; j < NL; ++j) pw[g][j] *= vsc;   // per-block value scale
+      }
+    }
+    constexpr int ND = UnpackDw<KT>::n;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const bool valid = !masked || (tpos + j * TPL + u < t1);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        float vx[ND];
+        UnpackDw<KT>::run(dword(vr[j], d), vx);
+#pragma unroll
+        for (int i = 0; i < ND; ++i) {
+          if (masked) vx[i] = valid ? vx[i] : 0.f;
+#pragma unroll
+          for (int g = 0; g < G; ++g) o[g][d * ND + i] = fmaf(pw[g][j], vx[i], o[g][d * ND + i]);
+        }
+      }
+    }
+  };
+
+  // Loads of one block's K and V tiles; false for a table entry outside the
+  // pool, which is skipped as if masked.
+  auto load_block = [&](int k, u32x4 (&kr)[NL], u32x4 (&vr)[NL], float& ksc, float& vsc) {
+    if (k > 0 && (k & 63) == 0) tc.fetch(trow, b0, wave, k, bmax);
+    const int p = tc.get(k);
+    if (p < 0 || p >= a.num_blocks) return false;
+    const int64_t toff = (static_cast<int64_t>(p) * a.hkv + kvh) * TILE;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      kr[j] = *reinterpret_cast<const u32x4*>(kbase + toff + j * 1024);
+      vr[j] = *reinterpret_cast<const u32x4*>(vbase + toff + j * 1024);
+    }
+    ksc = vsc = 1.f;
+    if (kInt8) {
+      ksc = a.ks[static_cast<int64_t>(p) * a.hkv + kvh];
+      vsc = a.vs[static_cast<int64_t>(p) * a.hkv + kvh];
+    }
+    return true;
+  };
+
+  // The wave's blocks are partition blocks wave, wave + 4, ...; all are
+  // whole except possibly the partition's last block, which is then the
+  // wave's last.  One block's K and V (8 KiB at bf16 / head_dim 128) are in
+  // flight per wave; at 63 VGPRs eight waves share a SIMD, so a CU keeps
+  // about 256 KiB of loads outstanding.
+  const bool partial_tail = (t1 & 15) != 0;
+  const int nwhole = nb - (partial_tail ? 1 : 0);
+  const int kwhole = nwhole > wave ? (nwhole - wave + kWaves - 1) / kWaves : 0;
+  const int kall = kwhole + ((partial_tail && (nb - 1) % kWaves == wave) ? 1 : 0);
+  auto step = [&](int k, bool ok, const u32x4 (&kr)[NL], const u32x4 (&vr)[NL], float ksc,
+                  float vsc) {
+    if (!ok) return;
+    const int tpos = (b0 + wave + kWaves * k) * 16;
+    if (k < kwhole)
+      block_step(std::false_type{}, kr, vr, tpos, ksc, vsc);
+    else
+      block_step(std::true_type{}, kr, vr, tpos, ksc, vsc);
+  };
+#pragma unroll 1
+  for (int k = 0; k < kall; ++k) {
+    u32x4 kr[NL], vr[NL];
+    float ksc = 1.f, vsc = 1.f;
+    const bool ok = load_block(k, kr, vr, ksc, vsc);
+    step(k, ok, kr, vr, ksc, vsc);
   }
 
   // Merge the token-row groups of the wavefront (lanes c, c+C, c+2C, ...).
@@ -239,7 +343,7 @@ pkv_status launch_d(const AttnArgs& a, int group, hipStream_t st) {
   // the largest of those dividing it (each workgroup then re-reads the KV).
   int gw = 1;
   for (int c : {8, 4, 2}) if (group % c == 0) { gw = c; break; }
-  dim3 grid(a.num_parts * a.num_rows, a.hq / gw);
+  dim3 grid(a.num_parts * a.num_rows * (a.hq / gw));
   switch (gw) {
     case 1: hipLaunchKernelGGL((decode_wave_kernel<QT, KT, D, 1>), grid, dim3(256), 0, st, a); break;
     case 2: hipLaunchKernelGGL((decode_wave_kernel<QT, KT, D, 2>), grid, dim3(256), 0, st, a); break;
