@@ -32,6 +32,7 @@
 // Four wavefronts take the partition's tiles round-robin, two tiles in flight
 // each, and merge through LDS at the end.
 #include "attention_common.h"
+#include "mfma_common.h"
 
 namespace pkv {
 namespace {
@@ -42,78 +43,6 @@ constexpr int kWaves = kDecodeWaves;
 #endif
 constexpr int kUnroll = PKV_MFMA_UNROLL;   // tiles of K and V in flight per wavefront
 static_assert(64 % kUnroll == 0, "the unroll must divide the table chunk");
-
-template <typename T> struct Mx;
-template <> struct Mx<BF16> {
-  __device__ __forceinline__ static f32x4 k32(const u32x4& a, const u32x4& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  }
-  __device__ __forceinline__ static f32x4 k16(const u32x2& a, const u32x2& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
-                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
-  }
-  // Two floats -> packed pair (round to nearest even).
-  __device__ __forceinline__ static uint32_t pack(float lo, float hi) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    bf16x2 v;
-    v.x = static_cast<__bf16>(lo);
-    v.y = static_cast<__bf16>(hi);
-    return __builtin_bit_cast(uint32_t, v);
-  }
-  __device__ __forceinline__ static float lo(uint32_t w) { return bf16_lo(w); }
-  __device__ __forceinline__ static float hi(uint32_t w) { return bf16_hi(w); }
-  // Exact 16-bit image of an integer in [-128, 127] held as float.
-  __device__ __forceinline__ static uint32_t int_bits(float x) { return __float_as_uint(x) >> 16; }
-};
-template <> struct Mx<F16> {
-  __device__ __forceinline__ static f32x4 k32(const u32x4& a, const u32x4& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  }
-  __device__ __forceinline__ static f32x4 k16(const u32x2& a, const u32x2& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
-                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
-  }
-  __device__ __forceinline__ static uint32_t pack(float lo, float hi) {
-    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-    f16x2 v;
-    v.x = static_cast<_Float16>(lo);
-    v.y = static_cast<_Float16>(hi);
-    return __builtin_bit_cast(uint32_t, v);
-  }
-  __device__ __forceinline__ static float lo(uint32_t w) { return f16_lo(w); }
-  __device__ __forceinline__ static float hi(uint32_t w) { return f16_hi(w); }
-  __device__ __forceinline__ static uint32_t int_bits(float x) {
-    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
-  }
-};
-
-// Loads of 4, 8 or 16 bytes into the low dwords of a u32x4.
-template <int B>
-__device__ __forceinline__ u32x4 load_bytes(const uint8_t* p) {
-  u32x4 r = {0u, 0u, 0u, 0u};
-  if constexpr (B == 16) {
-    r = *reinterpret_cast<const u32x4*>(p);
-  } else if constexpr (B == 8) {
-    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
-    r.x = v.x;
-    r.y = v.y;
-  } else {
-    r.x = *reinterpret_cast<const uint32_t*>(p);
-  }
-  return r;
-}
-
-__device__ __forceinline__ uint32_t dw(const u32x4& v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
-
-// Element j of a chunk of 16-bit values, as the low 16 bits.
-__device__ __forceinline__ uint32_t half_of(const u32x4& v, int j) {
-  const uint32_t w = dw(v, j >> 1);
-  return (j & 1) ? (w >> 16) : (w & 0xffffu);
-}
 
 template <typename QT, typename KT, int D>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(AttnArgs a, int group) {

@@ -1,0 +1,89 @@
+// Matrix-core helpers shared by the gfx950 attention kernels: the 16-bit
+// MFMA shapes used, packing of fp32 pairs to 16-bit operands, and element
+// access within 16-byte chunks.
+//
+// Operand layouts (wave64), as the kernels use them:
+//   v_mfma_f32_16x16x32_{bf16,f16}: lane l holds A[row l%16][8*(l/16) .. +7]
+//     and B[8*(l/16) .. +7][col l%16]; the result D[4*(l/16) + i][col l%16]
+//     sits in element i of the lane's f32x4.
+//   v_mfma_f32_16x16x16{bf16_1k,f16}: the same with 4 elements per lane:
+//     A[row l%16][4*(l/16) .. +3], B[4*(l/16) .. +3][col l%16].
+#pragma once
+
+#include "device_common.h"
+
+namespace pkv {
+
+template <typename T> struct Mx;
+template <> struct Mx<BF16> {
+  __device__ __forceinline__ static f32x4 k32(const u32x4& a, const u32x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static f32x4 k16(const u32x2& a, const u32x2& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+  }
+  // Two floats -> packed pair (round to nearest even).
+  __device__ __forceinline__ static uint32_t pack(float lo, float hi) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 v;
+    v.x = static_cast<__bf16>(lo);
+    v.y = static_cast<__bf16>(hi);
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  __device__ __forceinline__ static float lo(uint32_t w) { return bf16_lo(w); }
+  __device__ __forceinline__ static float hi(uint32_t w) { return bf16_hi(w); }
+  // Exact 16-bit image of an integer in [-128, 127] held as float.
+  __device__ __forceinline__ static uint32_t int_bits(float x) { return __float_as_uint(x) >> 16; }
+};
+template <> struct Mx<F16> {
+  __device__ __forceinline__ static f32x4 k32(const u32x4& a, const u32x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static f32x4 k16(const u32x2& a, const u32x2& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static uint32_t pack(float lo, float hi) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    f16x2 v;
+    v.x = static_cast<_Float16>(lo);
+    v.y = static_cast<_Float16>(hi);
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  __device__ __forceinline__ static float lo(uint32_t w) { return f16_lo(w); }
+  __device__ __forceinline__ static float hi(uint32_t w) { return f16_hi(w); }
+  __device__ __forceinline__ static uint32_t int_bits(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+  }
+};
+
+// Loads of 4, 8 or 16 bytes into the low dwords of a u32x4.
+template <int B>
+__device__ __forceinline__ u32x4 load_bytes(const uint8_t* p) {
+  u32x4 r = {0u, 0u, 0u, 0u};
+  if constexpr (B == 16) {
+    r = *reinterpret_cast<const u32x4*>(p);
+  } else if constexpr (B == 8) {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+    r.x = v.x;
+    r.y = v.y;
+  } else {
+    r.x = *reinterpret_cast<const uint32_t*>(p);
+  }
+  return r;
+}
+
+__device__ __forceinline__ uint32_t dw(const u32x4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// Element j of a chunk of 16-bit values, as the low 16 bits.
+__device__ __forceinline__ uint32_t half_of(const u32x4& v, int j) {
+  const uint32_t w = dw(v, j >> 1);
+  return (j & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+}  // namespace pkv

@@ -1,8 +1,242 @@
-// Placeholder until the matrix-core prefill kernel lands.
+// Chunked prefill attention on the matrix cores (gfx950), 16-bit q and KV.
+//
+// Long prompts are processed in chunks that share a batch with decode steps
+// (m.nxbn.cn §3.2; cnnetsun.cn "别再让GPU内存拖后腿了…" §4.1 turns chunking
+// on).  Row i of sequence s's chunk of length qlen sits at absolute position
+// P_i = context_lens[s] - qlen + i and attends keys [0, P_i] through the
+// block table: per-block scores, one softmax over them, and the weighted sum
+// of the value rows (cnnetsun.cn §3.1), with the chunk's own K/V already
+// written to the cache.
+//
+// Layout.  A workgroup of 4 wavefronts owns 64 consecutive rows of one
+// sequence's chunk for one query head; wavefront w takes rows 16w..16w+15.
+// Every row of the workgroup reads the same keys, so each 16-token K and V
+// tile is loaded once into LDS (double-buffered, rows padded by 16 bytes so
+// the 16 key rows a wavefront reads at one column fall in different banks)
+// and all four wavefronts read it there.  Per tile and wavefront:
+//   S^T [16 keys x 16 rows] = K [16 x D] . Q^T [D x 16]      (D/32 MFMA 16x16x32)
+//   online softmax per row (column): max over the lane's 4 keys, then across
+//   the four lane groups; the row's weights stay in the lanes that hold them,
+//   which is exactly the B operand of the next product;
+//   O^T [D x 16 rows] += V^T [D x 16 keys] . P^T [16 keys x 16 rows]
+//       (D/16 MFMA 16x16x16, weights as a 16-bit hi + lo pair)
+// Lane (m, g) reads the D/16 elements m*D/16.. of key rows 4g..4g+3 from
+// LDS, so product j sees element m*D/16 + j; at the end the lane holds 32
+// contiguous output elements of its row.
+//
+// Causality: a key t is used by row i when t <= P_i; rows past the chunk are
+// idle, and a wavefront skips tiles past its last row's position.  Key rows
+// past the workgroup's last position (the unwritten tail of the last block)
+// are stored to LDS as zeros, so no garbage enters the products; a table
+// entry outside the pool makes its whole tile masked.
+//
+// Grid order: the query head is the fastest index, so (with a head count
+// that is a multiple of 8) all tiles of one (sequence, head) go to the same
+// XCD and share the K/V lines it caches in L2.
 #include "attention_common.h"
+#include "mfma_common.h"
 
 namespace pkv {
-pkv_status launch_prefill_mfma(const AttnArgs&, pkv_dtype, int, int, int, hipStream_t) {
-  return fail(PKV_ERR_UNSUPPORTED, "MFMA prefill not built");
+namespace {
+
+constexpr int kPrefillWaves = 4;
+constexpr int kRowsPerWave = 16;
+constexpr int kTileRows = kPrefillWaves * kRowsPerWave;   // query rows per workgroup
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnArgs a, int max_tiles) {
+  constexpr int NK = D / 32;              // QK products per tile
+  constexpr int NV = D / 16;              // PV products per tile = elements of a lane's V chunk
+  constexpr int VB = NV * 2;              // bytes of a lane's V chunk
+  constexpr int ROWB = D * 2;             // bytes of a K/V row
+  constexpr int LROW = ROWB + 16;         // LDS row stride
+  constexpr int CHUNKS = ROWB / 16;       // 16-byte chunks per row
+  constexpr int TILE_CHUNKS = 16 * CHUNKS;
+  constexpr int LPT = (2 * TILE_CHUNKS + 255) / 256;   // K+V chunks per thread per tile
+  using M = Mx<T>;
+
+  const int hq = a.hq;
+  const int h = blockIdx.x % hq;
+  const int rest = blockIdx.x / hq;
+  const int tile = rest % max_tiles;
+  const int seq = rest / max_tiles;
+  const int qs = a.qsl[seq];
+  const int qlen = a.qsl[seq + 1] - qs;
+  if (tile * kTileRows >= qlen) return;
+  const int kvh = h / (hq / a.hkv);
+  const int cap = min(a.max_ctx, a.max_blocks * 16);   // keys the table row can address
+  const int base_pos = a.lens[seq] - qlen;             // position of the chunk's row 0
+
+  const int wave = wave_uniform(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15;
+  const int kg = lane >> 4;
+
+  const int q0 = tile * kTileRows + wave * kRowsPerWave;   // first row of this wave
+  const int qi = q0 + r16;                                 // this lane's row (column of S^T)
+  const bool qlive = qi < qlen;
+  const int qlast = qlive ? min(base_pos + qi, cap - 1) : -1;   // last key of the row
+  const int wrows = min(kRowsPerWave, qlen - q0);
+  const int wlast = wrows > 0 ? min(base_pos + q0 + wrows - 1, cap - 1) : -1;
+  const int tlast = min(base_pos + min(qlen, (tile + 1) * kTileRows) - 1, cap - 1);
+  const int nblk = tlast >= 0 ? (tlast >> 4) + 1 : 0;
+
+  // Q^T operand: row qi, elements 32kk + 8kg .. +7.
+  u32x4 qop[NK];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q);
+    const int64_t qrow = (static_cast<int64_t>(qs + (qlive ? qi : 0)) * hq + h) * D;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qp + qrow + 32 * kk + 8 * kg);
+      qop[kk] = qlive ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  __shared__ __align__(16) uint8_t sk[2][16 * LROW];
+  __shared__ __align__(16) uint8_t sv[2][16 * LROW];
+
+  const int32_t* trow = a.tables + static_cast<int64_t>(seq) * a.max_blocks;
+  const uint8_t* kc = static_cast<const uint8_t*>(a.kc);
+  const uint8_t* vc = static_cast<const uint8_t*>(a.vc);
+  const int64_t head_off = static_cast<int64_t>(kvh) * 16 * ROWB;
+
+  // Tile b of the context into registers: K chunks first, then V.  Rows past
+  // the workgroup's last key, and every row of a block outside the pool,
+  // become zeros.
+  u32x4 ld[LPT];
+  auto gload = [&](int b) {
+    const int p = trow[b];
+    const bool ok = p >= 0 && p < a.num_blocks;
+    const int64_t toff = static_cast<int64_t>(p) * a.hkv * 16 * ROWB + head_off;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      const int which = c / TILE_CHUNKS;
+      const int rc = c % TILE_CHUNKS;
+      const int row = rc / CHUNKS;
+      const bool live = ok && c < 2 * TILE_CHUNKS && b * 16 + row <= tlast;
+      ld[i] = u32x4{0u, 0u, 0u, 0u};
+      if (live) {
+        const uint8_t* src = (which == 0 ? kc : vc) + toff + row * ROWB + (rc % CHUNKS) * 16;
+        ld[i] = *reinterpret_cast<const u32x4*>(src);
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      if (c < 2 * TILE_CHUNKS) {
+        const int which = c / TILE_CHUNKS;
+        const int rc = c % TILE_CHUNKS;
+        uint8_t* dst = (which == 0 ? sk[buf] : sv[buf]) + (rc / CHUNKS) * LROW + (rc % CHUNKS) * 16;
+        *reinterpret_cast<u32x4*>(dst) = ld[i];
+      }
+    }
+  };
+
+  float m = kNegInf, l = 0.f;
+  f32x4 acc[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (nblk > 0) gload(0);
+#pragma unroll 1
+  for (int b = 0; b < nblk; ++b) {
+    const int buf = b & 1;
+    sstore(buf);
+    __syncthreads();
+    if (b + 1 < nblk) gload(b + 1);   // in flight while this tile is computed
+    const int kb = b * 16;
+    const int p = trow[b];
+    if (p < 0 || p >= a.num_blocks || kb > wlast) continue;   // wave-uniform
+    // ---- S^T = K . Q^T
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      const u32x4 kop = *reinterpret_cast<const u32x4*>(sk[buf] + r16 * LROW + (32 * kk + 8 * kg) * 2);
+      s = M::k32(kop, qop[kk], s);
+    }
+    float sc[4];
+    float tmax = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = kb + 4 * kg + i;
+      sc[i] = t <= qlast ? s[i] * a.scale_log2 : kNegInf;
+      tmax = fmaxf(tmax, sc[i]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float mn = fmaxf(m, tmax);
+    const float ms = (mn == kNegInf) ? 0.f : mn;
+    const float alpha = fast_exp2(m - ms);
+    m = mn;
+    float pw[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pw[i] = fast_exp2(sc[i] - ms);
+      psum += pw[i];
+    }
+    l = l * alpha + psum;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) acc[j] *= alpha;
+    // ---- P^T operand as hi + lo pairs
+    const uint32_t h01 = M::pack(pw[0], pw[1]);
+    const uint32_t h23 = M::pack(pw[2], pw[3]);
+    const u32x2 phi = {h01, h23};
+    const u32x2 plo = {M::pack(pw[0] - M::lo(h01), pw[1] - M::hi(h01)),
+                       M::pack(pw[2] - M::lo(h23), pw[3] - M::hi(h23))};
+    // ---- O^T += V^T . P^T
+    u32x4 vrow[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vrow[e] = load_bytes<VB>(sv[buf] + (4 * kg + e) * LROW + r16 * VB);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const u32x2 vop = {half_of(vrow[0], j) | (half_of(vrow[1], j) << 16),
+                         half_of(vrow[2], j) | (half_of(vrow[3], j) << 16)};
+      acc[j] = M::k16(vop, phi, acc[j]);
+      acc[j] = M::k16(vop, plo, acc[j]);
+    }
+  }
+
+  // Each lane summed the weights of its 4 keys per tile; add the 4 groups.
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (!qlive) return;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const int64_t orow = (static_cast<int64_t>(qs + qi) * hq + h) * D;
+  // acc[j][i] is element NV*(4kg + i) + j of the row.
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NV; ++j) store_out(a, orow + NV * (4 * kg + i) + j, acc[j][i] * inv);
 }
+
+template <typename T>
+pkv_status launch_t(const AttnArgs& a, int D, int max_tiles, hipStream_t st) {
+  const int64_t wgs = static_cast<int64_t>(a.num_seqs) * max_tiles * a.hq;
+  if (wgs > 0x7fffffff / 256) return fail(PKV_ERR_UNSUPPORTED, "prefill: launch too large");
+  dim3 grid(static_cast<unsigned>(wgs));
+  if (D == 64)
+    hipLaunchKernelGGL((prefill_mfma_kernel<T, 64>), grid, dim3(256), 0, st, a, max_tiles);
+  else
+    hipLaunchKernelGGL((prefill_mfma_kernel<T, 128>), grid, dim3(256), 0, st, a, max_tiles);
+  PKV_LAUNCH_CHECK("chunked prefill (MFMA)");
+  return PKV_OK;
+}
+
+}  // namespace
+
+pkv_status launch_prefill_mfma(const AttnArgs& a, pkv_dtype q_dt, int D, int group,
+                               int max_query_len, hipStream_t st) {
+  (void)group;
+  if (max_query_len <= 0 || a.num_seqs <= 0) return PKV_OK;
+  const int max_tiles = (max_query_len + kTileRows - 1) / kTileRows;
+  if (q_dt == PKV_BF16) return launch_t<BF16>(a, D, max_tiles, st);
+  if (q_dt == PKV_F16) return launch_t<F16>(a, D, max_tiles, st);
+  return fail(PKV_ERR_UNSUPPORTED, "MFMA prefill needs 16-bit q");
+}
+
 }  // namespace pkv
