@@ -154,42 +154,68 @@ def cpu_baseline(wl: Workload, min_seconds: float = 10.0, max_reps: int = 8):
     return res, out
 
 
-def main(argv=None) -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--partition", type=int, default=256,
-                    help="split-K partition size in tokens (0 = no split)")
-    ap.add_argument("--algo", choices=("auto", "wave", "mfma"), default="auto")
-    ap.add_argument("--seed", type=int, default=1)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--calib-copy-mib", type=int, default=0,
-                    help="also run one elementwise kernel that reads and writes this many MiB "
-                         "(a known-size kernel for scaling rocprofv3 byte counters)")
-    a = ap.parse_args(argv)
-    if a.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {a.gpus}); the paged decode path has no "
-              "multi-GPU mode in this build", file=sys.stderr)
-        return 2
+# ---------------------------------------------------------------------------
+# timing
+# ---------------------------------------------------------------------------
+def run_timed(torch, step, steps: int, warmup: int, nseg: int):
+    """Warm up, then time `steps` calls of step(events) between two device
+    synchronisations.  step records nseg + 1 events on the launch stream
+    around its kernels; returns (ms per step, [per-segment ms lists])."""
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nseg + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    segs = [[e[j].elapsed_time(e[j + 1]) for e in evs] for j in range(nseg)]
+    return wall * 1e3 / steps, segs
 
-    import torch
-    import paged_kv_cache_366_amd as pkv
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        return 2
-    pkv.load()
-    algo = {"auto": pkv.PKV_ALGO_AUTO, "wave": pkv.PKV_ALGO_WAVE, "mfma": pkv.PKV_ALGO_MFMA}[a.algo]
+def calibration_kernel(torch, mib: int) -> None:
+    """An elementwise kernel that reads and writes exactly mib MiB."""
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
 
+
+def base_result(a, metric, value, unit, ms_per_step, dtype, config):
+    return {
+        "metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+        "config": config,
+    }
+
+
+def roofline(kernel, bound, achieved, peak, unit, traffic=None):
+    return {"kernel": kernel, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+            "frac": achieved / peak, "traffic": traffic}
+
+
+METRIC = "paged decode attention: KV GB/s (% of HBM peak) + tokens/s at 7B shape"
+BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16/f16 matrix peak, published
+
+
+# ---------------------------------------------------------------------------
+# 7B-shape decode (the headline line)
+# ---------------------------------------------------------------------------
+def bench_decode7b(a, torch, pkv, algo):
     print("[bench] building the 7B-shape decode workload on the host", file=sys.stderr, flush=True)
     wl = Workload(seed=a.seed)
     dev = "cuda"
     kc = to_dev_bf16(wl.kc_full, torch)
     vc = to_dev_bf16(wl.vc_full, torch)
-    blk, row = wl.slots // BLOCK, wl.slots % BLOCK
-    kc[torch.from_numpy(blk.astype(np.int64)).to(dev), :, torch.from_numpy(row.astype(np.int64)).to(dev), :] = float("nan")
-    vc[torch.from_numpy(blk.astype(np.int64)).to(dev), :, torch.from_numpy(row.astype(np.int64)).to(dev), :] = float("nan")
+    blk = torch.from_numpy((wl.slots // BLOCK).astype(np.int64)).to(dev)
+    row = torch.from_numpy((wl.slots % BLOCK).astype(np.int64)).to(dev)
+    kc[blk, :, row, :] = float("nan")     # the step's cache write must fill these
+    vc[blk, :, row, :] = float("nan")
     q = to_dev_bf16(wl.q, torch)
     new_k = to_dev_bf16(wl.new_k, torch)
     new_v = to_dev_bf16(wl.new_v, torch)
@@ -203,7 +229,7 @@ def main(argv=None) -> int:
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
 
-    def step(ev=None):
+    def step(ev):
         if ev is not None:
             ev[0].record(stream)
         pkv.pkv_reshape_and_cache(new_k, new_v, kc, vc, slots)
@@ -218,34 +244,11 @@ def main(argv=None) -> int:
         if ev is not None:
             ev[3].record(stream)
 
-    print(f"[bench] warmup {a.warmup} steps", file=sys.stderr, flush=True)
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
-    print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(a.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    rc_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    main_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    red_ms = [e[2].elapsed_time(e[3]) for e in evs]
-
+    print(f"[bench] warmup {a.warmup}, timing {a.steps} steps", file=sys.stderr, flush=True)
+    ms_per_step, (rc_ms, main_ms, red_ms) = run_timed(torch, step, a.steps, a.warmup, 3)
     if a.calib_copy_mib:
-        # an elementwise kernel that reads and writes exactly n bytes
-        n = a.calib_copy_mib * (1 << 20)
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        torch.bitwise_not(src, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_kernel(torch, a.calib_copy_mib)
 
-    ms_per_step = wall * 1e3 / a.steps
     main_avg = float(np.mean(main_ms))
     step_bytes = wl.step_bytes()
     main_bytes = wl.main_kernel_bytes()
@@ -253,53 +256,402 @@ def main(argv=None) -> int:
     traffic = None
     if TRAFFIC["sources_sha1"] == kernel_sources_sha1() and TRAFFIC["bytes_per_launch"]:
         traffic = TRAFFIC["bytes_per_launch"]
-
-    result = {
-        "metric": "paged decode attention: KV GB/s (% of HBM peak) + tokens/s at 7B shape",
-        "value": step_bytes / (ms_per_step * 1e-3) / 1e9,
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": a.steps,
-        "warmup": a.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {
-            "workload": "7B-shape paged decode, bf16 KV and q, fp32 accumulate: 64 sequences, "
-                        "32 heads MHA, head_dim 128, block_size 16, contexts U[128, 2048], "
-                        "pool 1.25x, random placement; step = reshape_and_cache + decode + reduce",
-            "num_seqs": wl.S, "heads": wl.H, "head_dim": wl.D, "block_size": BLOCK,
-            "context_tokens": int(wl.lens.sum()), "num_blocks": wl.num_blocks,
-            "partition_tokens": a.partition, "algo": a.algo, "seed": a.seed,
-        },
+    result = base_result(a, METRIC, step_bytes / (ms_per_step * 1e-3) / 1e9, "GB/s", ms_per_step,
+                         "bf16", {
+        "workload": "7B-shape paged decode, bf16 KV and q, fp32 accumulate: 64 sequences, "
+                    "32 heads MHA, head_dim 128, block_size 16, contexts U[128, 2048], "
+                    "pool 1.25x, random placement; step = reshape_and_cache + decode + reduce",
+        "num_seqs": wl.S, "heads": wl.H, "head_dim": wl.D, "block_size": BLOCK,
+        "context_tokens": int(wl.lens.sum()), "num_blocks": wl.num_blocks,
+        "partition_tokens": a.partition, "algo": a.algo, "seed": a.seed})
+    result.update({
         "tokens_per_s": wl.S / (ms_per_step * 1e-3),
         "hbm_frac_step": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "kernel_ms": {"reshape_and_cache": float(np.mean(rc_ms)), "decode_main": main_avg,
                       "decode_main_median": float(np.median(main_ms)),
                       "reduce": float(np.mean(red_ms))},
         "bytes": {"step": step_bytes, "decode_main": main_bytes, "kv": wl.kv_bytes()},
-        "roofline": {
-            "kernel": "decode_wave_kernel (split-K main)",
-            "bound": "hbm",
-            "achieved": achieved,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS,
-            "traffic": traffic,
-        },
+        "roofline": roofline("decode_wave_kernel (split-K main)", "hbm", achieved, HBM_PEAK_GBS,
+                             "GB/s", traffic),
         "host_block_manager_us": wl.host_bm,
         "cpu_baseline": None,
-    }
-
+    })
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle on the same batch", file=sys.stderr, flush=True)
         cb, ref = cpu_baseline(wl)
         result["cpu_baseline"] = cb
         got = out.cpu().numpy().astype(np.float64)
         result["max_abs_err_vs_oracle"] = float(np.abs(got - ref).max())
+    return result
+
+
+# ---------------------------------------------------------------------------
+# long-context grouped-query decode
+# ---------------------------------------------------------------------------
+def bench_gqa(a, torch, pkv, algo, int8: bool):
+    from synth import workloads as W
+    print("[bench] building the long-context GQA workload on the host", file=sys.stderr,
+          flush=True)
+    c = W.gqa_long_decode(seed=4, int8=int8)
+    dev = "cuda"
+    if int8:
+        kc = torch.from_numpy(c.k_i8).to(dev)
+        vc = torch.from_numpy(c.v_i8).to(dev)
+        ks = torch.from_numpy(c.k_scale).to(dev)
+        vs = torch.from_numpy(c.v_scale).to(dev)
+    else:
+        kc, vc = to_dev_bf16(c.k_cache, torch), to_dev_bf16(c.v_cache, torch)
+        ks = vs = None
+    q = to_dev_bf16(c.q, torch)
+    tables = torch.from_numpy(c.block_tables).to(dev)
+    lens = torch.from_numpy(c.context_lens).to(dev)
+    S, hq, D = c.q.shape
+    hkv = c.kv_heads
+    max_ctx = int(c.context_lens.max())
+    part = a.partition if a.partition_set else 512
+    out = torch.empty((S, hq, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(pkv.pkv_decode_workspace_bytes(S, hq, D, max_ctx, part), 1),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def step(ev):
+        if ev is not None:
+            ev[0].record(stream)
+        pkv.pkv_paged_attention_decode_partials(out, q, kc, vc, tables, lens, max_ctx,
+                                                float(c.scale), part, algo, k_scale=ks,
+                                                v_scale=vs, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+        pkv.pkv_paged_attention_reduce(out, lens, max_ctx, part, ws)
+        if ev is not None:
+            ev[2].record(stream)
+
+    ms_per_step, (main_ms, red_ms) = run_timed(torch, step, a.steps, a.warmup, 2)
+    tokens = int(c.context_lens.astype(np.int64).sum())
+    eb = 1 if int8 else 2
+    kv = tokens * hkv * D * eb * 2
+    nblk = sum(W.blocks_for(n) for n in c.context_lens)
+    main_bytes = kv + S * hq * D * 2 + nblk * 4 + S * 4 + (nblk * hkv * 8 if int8 else 0)
+    step_bytes = main_bytes + S * hq * D * 4
+    main_avg = float(np.mean(main_ms))
+    achieved = main_bytes / (main_avg * 1e-3) / 1e9
+    # sampled parity of this run's output against the oracle, one row at a time
+    from oracle import attention as A
+    rng = np.random.default_rng(1)
+    G = hq // hkv
+    got = out.cpu().numpy()
+    err = 0.0
+    src_k, src_v = (c.k_i8, c.v_i8) if int8 else (c.k_cache, c.v_cache)
+    sk, sv = (c.k_scale, c.v_scale) if int8 else (None, None)
+    for s_, h_ in zip(rng.integers(0, S, 6), rng.integers(0, hq, 6)):
+        n = int(c.context_lens[s_])
+        K = A.gather(src_k, c.block_tables[s_], n, BLOCK, sk)[:, h_ // G]
+        V = A.gather(src_v, c.block_tables[s_], n, BLOCK, sv)[:, h_ // G]
+        err = max(err, float(np.abs(got[s_, h_] - A.attend(c.q[s_, h_], K, V, c.scale)).max()))
+    result = base_result(a, METRIC, step_bytes / (ms_per_step * 1e-3) / 1e9, "GB/s", ms_per_step,
+                         "int8-kv/bf16" if int8 else "bf16", {
+        "workload": f"long-context GQA decode, {'int8 KV with per-block fp32 scales' if int8 else 'bf16 KV'}: "
+                    "16 sequences, 64 query heads over 8 KV heads, head_dim 128, "
+                    "contexts U[8192, 32768], split-K partitions + reduce",
+        "context_tokens": tokens, "partition_tokens": part, "algo": a.algo})
+    result.update({
+        "tokens_per_s": S / (ms_per_step * 1e-3),
+        "kernel_ms": {"decode_main": main_avg, "reduce": float(np.mean(red_ms))},
+        "bytes": {"step": step_bytes, "decode_main": main_bytes, "kv": kv},
+        "roofline": roofline("decode_mfma_kernel (split-K main)" if algo != pkv.PKV_ALGO_WAVE
+                             else "decode_wave_kernel (split-K main)", "hbm", achieved,
+                             HBM_PEAK_GBS, "GB/s"),
+        "max_abs_err_vs_oracle_sampled": err,
+        "cpu_baseline": None,
+    })
+    return result
+
+
+# ---------------------------------------------------------------------------
+# continuous-batching mixed step: decode sequences + prefill chunks
+# ---------------------------------------------------------------------------
+def bench_mixed(a, torch, pkv, algo):
+    from synth import workloads as W
+    print("[bench] building the mixed-step workload on the host", file=sys.stderr, flush=True)
+    ms = W.mixed_step(seed=2)
+    dev = "cuda"
+    nb, hkv, D, hq = ms.num_blocks, ms.kv_heads, ms.head_dim, ms.q_heads
+    bm = pkv.pkv_bm_create(nb, BLOCK, ms.perm)
+    kc = torch.full((nb, hkv, BLOCK, D), float("nan"), dtype=torch.bfloat16, device=dev)
+    vc = kc.clone()
+    seqs = []
+    for s_ in range(len(ms.prior)):
+        sid = pkv.pkv_seq_create(bm, int(ms.prior[s_]))
+        if ms.prior[s_]:
+            sl = pkv.pkv_seq_slots(bm, sid, 0, int(ms.prior[s_]))
+            pkv.pkv_reshape_and_cache(to_dev_bf16(ms.prior_k[s_], torch),
+                                      to_dev_bf16(ms.prior_v[s_], torch), kc, vc,
+                                      torch.from_numpy(sl).to(dev))
+        seqs.append(sid)
+    t0 = time.perf_counter()
+    slots = np.concatenate([pkv.pkv_seq_append(bm, sid, int(ms.new[s_]))[0]
+                            for s_, sid in enumerate(seqs)])
+    lens_all = ms.prior + ms.new
+    tables, lens = pkv.pkv_seq_export(bm, seqs, W.blocks_for(int(lens_all.max())))
+    host_us = (time.perf_counter() - t0) * 1e6
+    dec = np.flatnonzero(ms.new == 1)
+    pre = np.flatnonzero(ms.new > 1)
+    starts = np.concatenate([[0], np.cumsum(ms.new)])
+    rows_p = np.concatenate([np.arange(starts[s_], starts[s_ + 1]) for s_ in pre])
+    qdev = to_dev_bf16(ms.q, torch)
+    q_d = qdev[torch.from_numpy(starts[dec]).to(dev)].contiguous()
+    q_p = qdev[torch.from_numpy(rows_p).to(dev)].contiguous()
+    new_k, new_v = to_dev_bf16(ms.new_k, torch), to_dev_bf16(ms.new_v, torch)
+    slots_d = torch.from_numpy(slots.astype(np.int32)).to(dev)
+    t_d = torch.from_numpy(np.ascontiguousarray(tables[dec])).to(dev)
+    l_d = torch.from_numpy(np.ascontiguousarray(lens[dec])).to(dev)
+    t_p = torch.from_numpy(np.ascontiguousarray(tables[pre])).to(dev)
+    l_p = torch.from_numpy(np.ascontiguousarray(lens[pre])).to(dev)
+    qsl = np.concatenate([[0], np.cumsum(ms.new[pre])]).astype(np.int32)
+    qsl_d = torch.from_numpy(qsl).to(dev)
+    mc_d, mc_p, mq = int(lens[dec].max()), int(lens[pre].max()), int(ms.new[pre].max())
+    part = a.partition
+    out_d = torch.empty(q_d.shape, dtype=torch.float32, device=dev)
+    out_p = torch.empty(q_p.shape, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(pkv.pkv_decode_workspace_bytes(len(dec), hq, D, mc_d, part), 1),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def step(ev):
+        if ev is not None:
+            ev[0].record(stream)
+        pkv.pkv_reshape_and_cache(new_k, new_v, kc, vc, slots_d)
+        if ev is not None:
+            ev[1].record(stream)
+        pkv.pkv_paged_attention_decode_partials(out_d, q_d, kc, vc, t_d, l_d, mc_d,
+                                                float(ms.scale), part, algo, workspace=ws)
+        pkv.pkv_paged_attention_reduce(out_d, l_d, mc_d, part, ws)
+        if ev is not None:
+            ev[2].record(stream)
+        pkv.pkv_paged_attention_prefill(out_p, q_p, kc, vc, t_p, qsl_d, l_p, mq, mc_p,
+                                        float(ms.scale))
+        if ev is not None:
+            ev[3].record(stream)
+
+    ms_per_step, (rc_ms, dec_ms, pre_ms) = run_timed(torch, step, a.steps, a.warmup, 3)
+    T = int(ms.new.sum())
+    kv_dec = int(lens[dec].astype(np.int64).sum()) * hkv * D * 4
+    kv_pre = int(lens[pre].astype(np.int64).sum()) * hkv * D * 4
+    rc_bytes = T * hkv * D * 2 * 2 * 2
+    dec_bytes = kv_dec + len(dec) * hq * D * (2 + 4)
+    pre_bytes = kv_pre + len(rows_p) * hq * D * (2 + 4)
+    step_bytes = rc_bytes + dec_bytes + pre_bytes
+    flops = 0
+    for s_ in pre:
+        n, ql = int(lens[s_]), int(ms.new[s_])
+        flops += sum(n - ql + i + 1 for i in range(ql)) * hq * D * 4
+    pre_avg = float(np.mean(pre_ms))
+    dec_avg = float(np.mean(dec_ms))
+    # sampled parity: a few prefill rows and decode rows against the oracle
+    from oracle import attention as A
+    rng = np.random.default_rng(0)
+    got_p, got_d = out_p.cpu().numpy(), out_d.cpu().numpy()
+    err = 0.0
+    for j, s_ in enumerate(pre):
+        n, ql = int(lens[s_]), int(ms.new[s_])
+        K = gather_dev_all(kc, tables[s_], n, torch)
+        V = gather_dev_all(vc, tables[s_], n, torch)
+        for i in (0, ql // 2, ql - 1):
+            h_ = int(rng.integers(0, hq))
+            P = n - ql + i
+            ref = A.attend(ms.q[rows_p[qsl[j] + i], h_], K[:P + 1, h_], V[:P + 1, h_], ms.scale)
+            err = max(err, float(np.abs(got_p[qsl[j] + i, h_] - ref).max()))
+    for j in rng.choice(len(dec), 4, replace=False):
+        s_ = dec[j]
+        n = int(lens[s_])
+        K = gather_dev_all(kc, tables[s_], n, torch)
+        V = gather_dev_all(vc, tables[s_], n, torch)
+        h_ = int(rng.integers(0, hq))
+        ref = A.attend(ms.q[starts[s_], h_], K[:, h_], V[:, h_], ms.scale)
+        err = max(err, float(np.abs(got_d[j, h_] - ref).max()))
+    pkv.pkv_bm_destroy(bm)
+    result = base_result(a, METRIC, step_bytes / (ms_per_step * 1e-3) / 1e9, "GB/s", ms_per_step,
+                         "bf16", {
+        "workload": "continuous-batching mixed step, bf16: 48 decode sequences (contexts "
+                    "U[64, 4096]) + 4 prefill chunks of 512 causal rows over 0/512/1024/1536 "
+                    "cached tokens; 32 heads x 128; step = reshape_and_cache of 2096 rows + "
+                    "decode + reduce + chunked prefill",
+        "partition_tokens": part, "algo": a.algo})
+    result.update({
+        "tokens_per_s": (len(dec) + len(rows_p)) / (ms_per_step * 1e-3),
+        "kernel_ms": {"reshape_and_cache": float(np.mean(rc_ms)), "decode_and_reduce": dec_avg,
+                      "prefill": pre_avg},
+        "bytes": {"step": step_bytes, "decode": dec_bytes, "prefill_unique": pre_bytes,
+                  "reshape_and_cache": rc_bytes},
+        "prefill_gflop": flops / 1e9,
+        "roofline": roofline("decode_wave_kernel + reduce (decode part)", "hbm",
+                             dec_bytes / (dec_avg * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
+        "roofline_prefill": roofline("prefill_mfma_kernel", "mfma",
+                                     flops / (pre_avg * 1e-3) / 1e12, BF16_MFMA_PEAK_TFLOPS,
+                                     "TFLOP/s"),
+        "host_block_manager_us": {"append_export_us": host_us},
+        "max_abs_err_vs_oracle_sampled": err,
+        "cpu_baseline": None,
+    })
+    return result
+
+
+def gather_dev_all(cache, table_row, n, torch):
+    """Rows [0, n) of every KV head of a bf16 device pool through one table
+    row, read back as float64 [n, heads, D] for the oracle's per-row check."""
+    nb = -(-n // BLOCK)
+    idx = torch.from_numpy(np.asarray(table_row[:nb], np.int64)).to(cache.device)
+    rows = cache[idx].float().permute(0, 2, 1, 3).reshape(nb * BLOCK, cache.shape[1], -1)[:n]
+    return rows.cpu().numpy().astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# shared prefix + beam search with copy-on-write
+# ---------------------------------------------------------------------------
+def bench_beam(a, torch, pkv, algo):
+    from synth import workloads as W
+    print("[bench] building the shared-prefix beam workload on the host", file=sys.stderr,
+          flush=True)
+    bc = W.beam_cow(seed=3)
+    dev = "cuda"
+    nb, hkv, D, hq = bc.num_blocks, bc.kv_heads, bc.head_dim, bc.q_heads
+    bm = pkv.pkv_bm_create(nb, BLOCK, bc.perm)
+    kc = torch.full((nb, hkv, BLOCK, D), float("nan"), dtype=torch.bfloat16, device=dev)
+    vc = kc.clone()
+
+    def write(sl, k, v):
+        pkv.pkv_reshape_and_cache(to_dev_bf16(k, torch), to_dev_bf16(v, torch), kc, vc,
+                                  torch.from_numpy(np.asarray(sl, np.int32)).to(dev))
+
+    root = pkv.pkv_seq_create(bm, bc.prefix_len)
+    write(pkv.pkv_seq_slots(bm, root, 0, bc.prefix_len), bc.prefix_k, bc.prefix_v)
+    reqs = []
+    for r, n in enumerate(bc.request_lens):
+        s_ = pkv.pkv_seq_fork(bm, root)
+        write(pkv.pkv_seq_append(bm, s_, int(n))[0], bc.req_k[r], bc.req_v[r])
+        reqs.append(s_)
+    pkv.pkv_seq_free(bm, root)
+    beams = []
+    for s_ in reqs:
+        beams += [pkv.pkv_seq_fork(bm, s_) for _ in range(bc.beam_width - 1)] + [s_]
+    t0 = time.perf_counter()
+    slots, pairs = pkv.pkv_seq_append_batch(bm, beams)
+    mb = W.blocks_for(bc.prefix_len + int(bc.request_lens.max()) + 1)
+    tables, lens = pkv.pkv_seq_export(bm, beams, mb)
+    host_us = (time.perf_counter() - t0) * 1e6
+    stats = pkv.pkv_bm_stats_get(bm)
+    pairs_d = torch.from_numpy(np.ascontiguousarray(pairs, np.int32).reshape(-1, 2)).to(dev)
+    slots_d = torch.from_numpy(slots.astype(np.int32)).to(dev)
+    bk, bv = to_dev_bf16(bc.beam_k, torch), to_dev_bf16(bc.beam_v, torch)
+    q = to_dev_bf16(bc.q, torch)
+    t_d, l_d = torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev)
+    S = len(beams)
+    mc = int(lens.max())
+    part = a.partition
+    out = torch.empty((S, hq, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(pkv.pkv_decode_workspace_bytes(S, hq, D, mc, part), 1),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def step(ev):
+        if ev is not None:
+            ev[0].record(stream)
+        pkv.pkv_copy_blocks(kc, vc, pairs_d)
+        pkv.pkv_reshape_and_cache(bk, bv, kc, vc, slots_d)
+        if ev is not None:
+            ev[1].record(stream)
+        pkv.pkv_paged_attention_decode_partials(out, q, kc, vc, t_d, l_d, mc, float(bc.scale),
+                                                part, algo, workspace=ws)
+        pkv.pkv_paged_attention_reduce(out, l_d, mc, part, ws)
+        if ev is not None:
+            ev[2].record(stream)
+
+    ms_per_step, (cow_ms, dec_ms) = run_timed(torch, step, a.steps, a.warmup, 2)
+    logical = int(lens.astype(np.int64).sum()) * hkv * D * 4
+    unique_blocks = len(set(int(b) for s_ in range(S) for b in tables[s_, :W.blocks_for(lens[s_])]))
+    unique = unique_blocks * hkv * BLOCK * D * 4
+    dec_avg = float(np.mean(dec_ms))
+    from oracle import attention as A
+    got = out.cpu().numpy()
+    rng = np.random.default_rng(0)
+    err = 0.0
+    for s_ in rng.choice(S, 6, replace=False):
+        n = int(lens[s_])
+        K = gather_dev_all(kc, tables[s_], n, torch)
+        V = gather_dev_all(vc, tables[s_], n, torch)
+        h_ = int(rng.integers(0, hq))
+        ref = A.attend(bc.q[s_, h_], K[:, h_], V[:, h_], bc.scale)
+        err = max(err, float(np.abs(got[s_, h_] - ref).max()))
+    pkv.pkv_bm_destroy(bm)
+    result = base_result(a, METRIC, logical / (dec_avg * 1e-3) / 1e9, "GB/s (logical)",
+                         ms_per_step, "bf16", {
+        "workload": "shared-prefix beam search with copy-on-write, bf16: 16 requests sharing a "
+                    "1024-token prefix, 1-200 own tokens, beam width 4; step = copy_blocks of the "
+                    "shared partial tails + reshape_and_cache of 64 tokens + decode + reduce",
+        "partition_tokens": part, "algo": a.algo, "cow_pairs": int(len(pairs))})
+    result.update({
+        "tokens_per_s": S / (ms_per_step * 1e-3),
+        "kernel_ms": {"copy_blocks_and_reshape": float(np.mean(cow_ms)),
+                      "decode_and_reduce": dec_avg},
+        "bytes": {"logical_kv": logical, "unique_kv": unique},
+        "note": "logical bytes count shared blocks once per beam; the unique working set "
+                "fits the 256 MB MALL, so logical GB/s may exceed the HBM peak",
+        "roofline": roofline("decode_wave_kernel + reduce (logical bytes)", "hbm",
+                             logical / (dec_avg * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
+        "block_manager": {"append_export_us": host_us, **stats},
+        "max_abs_err_vs_oracle_sampled": err,
+        "cpu_baseline": None,
+    })
+    return result
+
+
+WORKLOADS = ("decode7b", "mixed", "beam", "gqa", "gqa-int8")
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", choices=WORKLOADS, default="decode7b",
+                    help="decode7b is the headline line; the others measure the other kernels")
+    ap.add_argument("--partition", type=int, default=None,
+                    help="split-K partition size in tokens (0 = no split); default 256, or 512 "
+                         "for the long-context GQA workloads")
+    ap.add_argument("--algo", choices=("auto", "wave", "mfma"), default="auto")
+    ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one elementwise kernel that reads and writes this many MiB "
+                         "(a known-size kernel for scaling rocprofv3 byte counters)")
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {a.gpus}); this build has no "
+              "multi-GPU mode", file=sys.stderr)
+        return 2
+    a.partition_set = a.partition is not None
+    if a.partition is None:
+        a.partition = 256
+
+    import torch
+    import paged_kv_cache_366_amd as pkv
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    pkv.load()
+    algo = {"auto": pkv.PKV_ALGO_AUTO, "wave": pkv.PKV_ALGO_WAVE, "mfma": pkv.PKV_ALGO_MFMA}[a.algo]
+    if a.workload == "decode7b":
+        result = bench_decode7b(a, torch, pkv, algo)
+    elif a.workload == "mixed":
+        result = bench_mixed(a, torch, pkv, algo)
+    elif a.workload == "beam":
+        result = bench_beam(a, torch, pkv, algo)
+    else:
+        result = bench_gqa(a, torch, pkv, algo, int8=(a.workload == "gqa-int8"))
     print(json.dumps(result), flush=True)
     return 0
 
