@@ -143,14 +143,11 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttnArgs a, int group)
       for (int kk = 0; kk < NK; ++kk) {
         u32x4 kop;
         if constexpr (kInt8) {
-          const uint32_t w0 = kr[u][kk].x, w1 = kr[u][kk].y;
-          float x[8];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) { x[i] = i8_at(w0, i); x[4 + i] = i8_at(w1, i); }
-          kop = u32x4{M::int_bits(x[0]) | (M::int_bits(x[1]) << 16),
-                      M::int_bits(x[2]) | (M::int_bits(x[3]) << 16),
-                      M::int_bits(x[4]) | (M::int_bits(x[5]) << 16),
-                      M::int_bits(x[6]) | (M::int_bits(x[7]) << 16)};
+          const uint32_t w0 = kr[u][kk].x ^ 0x80808080u, w1 = kr[u][kk].y ^ 0x80808080u;
+          kop = u32x4{M::int_pair(i8_exact(w0, 0), i8_exact(w0, 1)),
+                      M::int_pair(i8_exact(w0, 2), i8_exact(w0, 3)),
+                      M::int_pair(i8_exact(w1, 0), i8_exact(w1, 1)),
+                      M::int_pair(i8_exact(w1, 2), i8_exact(w1, 3))};
         } else {
           kop = kr[u][kk];
         }
@@ -167,50 +164,63 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttnArgs a, int group)
       }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float mn = fmaxf(m, tmax);
-      const float ms = (mn == kNegInf) ? 0.f : mn;
-      const float alpha = fast_exp2(m - ms);
-      m = mn;
-      float pw[4];
-      float psum = 0.f;
+      const bool grow = tmax > m + kRescaleSlack;
+      if (__any(grow)) {   // rare after the first tiles: skips the accumulator rescale
+        const float mn = grow ? tmax : m;
+        const float alpha = grow ? fast_exp2(m - mn) : 1.f;
+        m = mn;
+        l *= alpha;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pw[i] = fast_exp2(sv[i] - ms);
-        psum += pw[i];
+        for (int j = 0; j < NV; ++j) acc[j] *= alpha;
       }
-      l = l * alpha + psum;
-#pragma unroll
-      for (int j = 0; j < NV; ++j) acc[j] *= alpha;
-      // ---- P^T operand as hi + lo pairs
+      const float ms = (m == kNegInf) ? 0.f : m;
       float pv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pv[i] = pw[i] * vscale;
+      for (int i = 0; i < 4; ++i) {
+        const float pw = fast_exp2(sv[i] - ms);
+        l += pw;
+        pv[i] = pw * vscale;
+      }
+      // ---- P^T operand as hi + lo pairs
       const uint32_t h01 = M::pack(pv[0], pv[1]);
       const uint32_t h23 = M::pack(pv[2], pv[3]);
       const u32x2 phi = {h01, h23};
       const u32x2 plo = {M::pack(pv[0] - M::lo(h01), pv[1] - M::hi(h01)),
                          M::pack(pv[2] - M::lo(h23), pv[3] - M::hi(h23))};
-      // ---- out^T += V^T . P^T; value rows past the context are zeroed first
+      // K = 32 of one product: the lane's 4 keys with the hi weights, then
+      // the same 4 keys with the lo weights (the A operand repeats them)
+      const u32x4 pcat = {phi.x, phi.y, plo.x, plo.y};
+      // ---- out^T += V^T . P^T.  Value rows past the context (only in the
+      // partly filled last block) may hold anything: they are zeroed.
       u32x4 vrow[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool valid = (p >= 0) && (tpos + 4 * kg + e < t1);
-        vrow[e] = valid ? vr[u][e] : u32x4{0u, 0u, 0u, 0u};
-      }
+      for (int e = 0; e < 4; ++e) vrow[e] = vr[u][e];
+      if (!(p >= 0 && tpos + 16 <= t1)) {
 #pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        u32x2 vop;
-        if constexpr (kInt8) {
-          uint32_t b[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) b[e] = M::int_bits(i8_at(dw(vrow[e], j >> 2), j & 3));
-          vop = u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
-        } else {
-          vop = u32x2{half_of(vrow[0], j) | (half_of(vrow[1], j) << 16),
-                      half_of(vrow[2], j) | (half_of(vrow[3], j) << 16)};
+        for (int e = 0; e < 4; ++e) {
+          const bool valid = (p >= 0) && (tpos + 4 * kg + e < t1);
+          vrow[e] = valid ? vrow[e] : u32x4{0u, 0u, 0u, 0u};
         }
-        acc[j] = M::k16(vop, phi, acc[j]);
-        acc[j] = M::k16(vop, plo, acc[j]);
+      }
+      if constexpr (kInt8) {
+        // sign-flipped codes: each widens with one byte-select add and one convert
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vrow[e] ^= u32x4{0x80808080u, 0x80808080u, 0x80808080u, 0x80808080u};
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          const uint32_t v01 = M::int_pair(i8_exact(dw(vrow[0], j >> 2), j & 3),
+                                           i8_exact(dw(vrow[1], j >> 2), j & 3));
+          const uint32_t v23 = M::int_pair(i8_exact(dw(vrow[2], j >> 2), j & 3),
+                                           i8_exact(dw(vrow[3], j >> 2), j & 3));
+          acc[j] = M::k32(u32x4{v01, v23, v01, v23}, pcat, acc[j]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          const uint32_t v01 = pair_of(vrow[0], vrow[1], j);
+          const uint32_t v23 = pair_of(vrow[2], vrow[3], j);
+          acc[j] = M::k32(u32x4{v01, v23, v01, v23}, pcat, acc[j]);
+        }
       }
     }
   }

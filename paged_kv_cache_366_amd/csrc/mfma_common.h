@@ -36,6 +36,10 @@ template <> struct Mx<BF16> {
   __device__ __forceinline__ static float hi(uint32_t w) { return bf16_hi(w); }
   // Exact 16-bit image of an integer in [-128, 127] held as float.
   __device__ __forceinline__ static uint32_t int_bits(float x) { return __float_as_uint(x) >> 16; }
+  // Two such integers as one operand dword (lo, hi): their high halves.
+  __device__ __forceinline__ static uint32_t int_pair(float lo, float hi) {
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+  }
 };
 template <> struct Mx<F16> {
   __device__ __forceinline__ static f32x4 k32(const u32x4& a, const u32x4& b, const f32x4& c) {
@@ -58,6 +62,9 @@ template <> struct Mx<F16> {
   __device__ __forceinline__ static uint32_t int_bits(float x) {
     return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
   }
+  __device__ __forceinline__ static uint32_t int_pair(float lo, float hi) {
+    return pack(lo, hi);   // exact: |x| <= 128 is an f16 value
+  }
 };
 
 // Loads of 4, 8 or 16 bytes into the low dwords of a u32x4.
@@ -79,6 +86,25 @@ __device__ __forceinline__ u32x4 load_bytes(const uint8_t* p) {
 __device__ __forceinline__ uint32_t dw(const u32x4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
+
+// Element j of chunk x in the low half and element j of chunk y in the high
+// half of one dword (one v_perm_b32).
+__device__ __forceinline__ uint32_t pair_of(const u32x4& x, const u32x4& y, int j) {
+  return __builtin_amdgcn_perm(dw(y, j >> 1), dw(x, j >> 1), (j & 1) ? 0x07060302u : 0x05040100u);
+}
+
+// Signed byte k of a dword, exactly, as float: the byte with its sign bit
+// flipped is an unsigned value (v_cvt_f32_ubyte), less 128.
+__device__ __forceinline__ float i8_exact(uint32_t flipped, int k) {
+  return static_cast<float>((flipped >> (8 * k)) & 0xffu) - 128.f;
+}
+
+// Lazy rescaling of an online softmax: the running reference max moves only
+// when a new score exceeds it by more than this (log2 units), so weights
+// stay below 2^8 (far from fp32 overflow) and the accumulators are rescaled
+// only on the rare blocks that raise the max that much.  The result is the
+// same softmax up to rounding: the reference cancels in the final division.
+constexpr float kRescaleSlack = 8.f;
 
 // Element j of a chunk of 16-bit values, as the low 16 bits.
 __device__ __forceinline__ uint32_t half_of(const u32x4& v, int j) {

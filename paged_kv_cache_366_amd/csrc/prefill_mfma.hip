@@ -40,29 +40,40 @@ namespace pkv {
 namespace {
 
 constexpr int kPrefillWaves = 4;
-constexpr int kRowsPerWave = 16;
-constexpr int kTileRows = kPrefillWaves * kRowsPerWave;   // query rows per workgroup
+#ifndef PKV_PREFILL_DEPTH
+#define PKV_PREFILL_DEPTH 1
+#endif
+#ifndef PKV_PREFILL_RTILES
+#define PKV_PREFILL_RTILES 1
+#endif
+constexpr int kDepth = PKV_PREFILL_DEPTH;     // blocks whose global loads are in flight
+constexpr int kRowTiles = PKV_PREFILL_RTILES; // 16-row tiles per wavefront
+constexpr int kTileRows = kPrefillWaves * 16 * kRowTiles;   // query rows per workgroup
 
-template <typename T, int D>
+template <typename T, int D, int P, int R>
 __global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnArgs a, int max_tiles) {
-  constexpr int NK = D / 32;              // QK products per tile
-  constexpr int NV = D / 16;              // PV products per tile = elements of a lane's V chunk
+  constexpr int NK = D / 32;              // QK products per block and row tile
+  constexpr int NV = D / 16;              // PV products per block and row tile
   constexpr int VB = NV * 2;              // bytes of a lane's V chunk
   constexpr int ROWB = D * 2;             // bytes of a K/V row
   constexpr int LROW = ROWB + 16;         // LDS row stride
   constexpr int CHUNKS = ROWB / 16;       // 16-byte chunks per row
   constexpr int TILE_CHUNKS = 16 * CHUNKS;
-  constexpr int LPT = (2 * TILE_CHUNKS + 255) / 256;   // K+V chunks per thread per tile
+  constexpr int LPT = (2 * TILE_CHUNKS + 255) / 256;   // K+V chunks per thread per block
+  constexpr int WROWS = 16 * R;           // rows per wavefront
+  constexpr int TROWS = kPrefillWaves * WROWS;
   using M = Mx<T>;
 
+  // Workgroup -> (sequence, row tile, head), head fastest; within a
+  // sequence the last row tiles (the most keys) are dispatched first.
   const int hq = a.hq;
   const int h = blockIdx.x % hq;
   const int rest = blockIdx.x / hq;
-  const int tile = rest % max_tiles;
+  const int tile = max_tiles - 1 - rest % max_tiles;
   const int seq = rest / max_tiles;
   const int qs = a.qsl[seq];
   const int qlen = a.qsl[seq + 1] - qs;
-  if (tile * kTileRows >= qlen) return;
+  if (tile * TROWS >= qlen) return;
   const int kvh = h / (hq / a.hkv);
   const int cap = min(a.max_ctx, a.max_blocks * 16);   // keys the table row can address
   const int base_pos = a.lens[seq] - qlen;             // position of the chunk's row 0
@@ -72,24 +83,33 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnArgs a, int max_t
   const int r16 = lane & 15;
   const int kg = lane >> 4;
 
-  const int q0 = tile * kTileRows + wave * kRowsPerWave;   // first row of this wave
-  const int qi = q0 + r16;                                 // this lane's row (column of S^T)
-  const bool qlive = qi < qlen;
-  const int qlast = qlive ? min(base_pos + qi, cap - 1) : -1;   // last key of the row
-  const int wrows = min(kRowsPerWave, qlen - q0);
+  const int q0 = tile * TROWS + wave * WROWS;   // first row of this wave
+  int qlast[R];                                 // last key of the lane's row in each row tile
+  bool qlive[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int qi = q0 + 16 * r + r16;
+    qlive[r] = qi < qlen;
+    qlast[r] = qlive[r] ? min(base_pos + qi, cap - 1) : -1;
+  }
+  const int wrows = min(WROWS, qlen - q0);
   const int wlast = wrows > 0 ? min(base_pos + q0 + wrows - 1, cap - 1) : -1;
-  const int tlast = min(base_pos + min(qlen, (tile + 1) * kTileRows) - 1, cap - 1);
+  const int tlast = min(base_pos + min(qlen, (tile + 1) * TROWS) - 1, cap - 1);
   const int nblk = tlast >= 0 ? (tlast >> 4) + 1 : 0;
 
-  // Q^T operand: row qi, elements 32kk + 8kg .. +7.
-  u32x4 qop[NK];
+  // Q^T operands: row q0 + 16r + r16, elements 32kk + 8kg .. +7.
+  u32x4 qop[R][NK];
   {
     const uint16_t* qp = static_cast<const uint16_t*>(a.q);
-    const int64_t qrow = (static_cast<int64_t>(qs + (qlive ? qi : 0)) * hq + h) * D;
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(qp + qrow + 32 * kk + 8 * kg);
-      qop[kk] = qlive ? v : u32x4{0u, 0u, 0u, 0u};
+    for (int r = 0; r < R; ++r) {
+      const int qi = q0 + 16 * r + r16;
+      const int64_t qrow = (static_cast<int64_t>(qs + (qlive[r] ? qi : 0)) * hq + h) * D;
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(qp + qrow + 32 * kk + 8 * kg);
+        qop[r][kk] = qlive[r] ? v : u32x4{0u, 0u, 0u, 0u};
+      }
     }
   }
 
@@ -103,10 +123,12 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnArgs a, int max_t
 
   // Tile b of the context into registers: K chunks first, then V.  Rows past
   // the workgroup's last key, and every row of a block outside the pool,
-  // become zeros.
-  u32x4 ld[LPT];
-  auto gload = [&](int b) {
-    const int p = trow[b];
+  // become zeros.  P blocks are in flight: slot u of the ring holds block
+  // b with b % P == u, so after unrolling every index is static.
+  u32x4 ld[P][LPT];
+  auto gload = [&](int b, u32x4 (&rg)[LPT]) {
+    int p = -1;
+    if (b < nblk) p = trow[b];
     const bool ok = p >= 0 && p < a.num_blocks;
     const int64_t toff = static_cast<int64_t>(p) * a.hkv * 16 * ROWB + head_off;
 #pragma unroll
@@ -115,15 +137,13 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnArgs a, int max_t
       const int which = c / TILE_CHUNKS;
       const int rc = c % TILE_CHUNKS;
       const int row = rc / CHUNKS;
-      const bool live = ok && c < 2 * TILE_CHUNKS && b * 16 + row <= tlast;
-      ld[i] = u32x4{0u, 0u, 0u, 0u};
-      if (live) {
-        const uint8_t* src = (which == 0 ? kc : vc) + toff + row * ROWB + (rc % CHUNKS) * 16;
-        ld[i] = *reinterpret_cast<const u32x4*>(src);
-      }
+      rg[i] = u32x4{0u, 0u, 0u, 0u};
+      if (ok && c < 2 * TILE_CHUNKS && b * 16 + row <= tlast)
+        rg[i] = *reinterpret_cast<const u32x4*>((which == 0 ? kc : vc) + toff + row * ROWB +
+                                                (rc % CHUNKS) * 16);
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int buf, const u32x4 (&rg)[LPT]) {
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int c = threadIdx.x + 256 * i;
@@ -131,87 +151,126 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnArgs a, int max_t
         const int which = c / TILE_CHUNKS;
         const int rc = c % TILE_CHUNKS;
         uint8_t* dst = (which == 0 ? sk[buf] : sv[buf]) + (rc / CHUNKS) * LROW + (rc % CHUNKS) * 16;
-        *reinterpret_cast<u32x4*>(dst) = ld[i];
+        *reinterpret_cast<u32x4*>(dst) = rg[i];
       }
     }
   };
 
-  float m = kNegInf, l = 0.f;
-  f32x4 acc[NV];
+  float m[R], l[R];
+  f32x4 acc[R][NV];
 #pragma unroll
-  for (int j = 0; j < NV; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int r = 0; r < R; ++r) {
+    m[r] = kNegInf;
+    l[r] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) acc[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
-  if (nblk > 0) gload(0);
-#pragma unroll 1
-  for (int b = 0; b < nblk; ++b) {
-    const int buf = b & 1;
-    sstore(buf);
-    __syncthreads();
-    if (b + 1 < nblk) gload(b + 1);   // in flight while this tile is computed
+  // One block: its tile from LDS buffer `buf`, for each of the wave's row
+  // tiles.  The K operands and the V operand are read and built once and
+  // serve every row tile.
+  auto compute = [&](int b, int buf) {
     const int kb = b * 16;
     const int p = trow[b];
-    if (p < 0 || p >= a.num_blocks || kb > wlast) continue;   // wave-uniform
+    if (p < 0 || p >= a.num_blocks || kb > wlast) return;   // wave-uniform
     // ---- S^T = K . Q^T
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    f32x4 s[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) s[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
-      const u32x4 kop = *reinterpret_cast<const u32x4*>(sk[buf] + r16 * LROW + (32 * kk + 8 * kg) * 2);
-      s = M::k32(kop, qop[kk], s);
-    }
-    float sc[4];
-    float tmax = kNegInf;
+      const u32x4 kop =
+          *reinterpret_cast<const u32x4*>(sk[buf] + r16 * LROW + (32 * kk + 8 * kg) * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = kb + 4 * kg + i;
-      sc[i] = t <= qlast ? s[i] * a.scale_log2 : kNegInf;
-      tmax = fmaxf(tmax, sc[i]);
+      for (int r = 0; r < R; ++r) s[r] = M::k32(kop, qop[r][kk], s[r]);
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float mn = fmaxf(m, tmax);
-    const float ms = (mn == kNegInf) ? 0.f : mn;
-    const float alpha = fast_exp2(m - ms);
-    m = mn;
-    float pw[4];
-    float psum = 0.f;
+    // ---- online softmax per row, lazily rescaled; P^T as hi + lo pairs
+    u32x4 pcat[R];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pw[i] = fast_exp2(sc[i] - ms);
-      psum += pw[i];
+    for (int r = 0; r < R; ++r) {
+      float sc[4];
+      float tmax = kNegInf;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = kb + 4 * kg + i;
+        sc[i] = t <= qlast[r] ? s[r][i] * a.scale_log2 : kNegInf;
+        tmax = fmaxf(tmax, sc[i]);
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const bool grow = tmax > m[r] + kRescaleSlack;
+      if (__any(grow)) {   // rare after the first blocks
+        const float mn = grow ? tmax : m[r];
+        const float alpha = grow ? fast_exp2(m[r] - mn) : 1.f;
+        m[r] = mn;
+        l[r] *= alpha;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) acc[r][j] *= alpha;
+      }
+      const float ms = (m[r] == kNegInf) ? 0.f : m[r];
+      float pw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pw[i] = fast_exp2(sc[i] - ms);
+        l[r] += pw[i];
+      }
+      const uint32_t h01 = M::pack(pw[0], pw[1]);
+      const uint32_t h23 = M::pack(pw[2], pw[3]);
+      // K = 32 of one product: the lane's 4 keys with the hi weights, then
+      // the same 4 keys with the lo weights (the A operand repeats them)
+      pcat[r] = u32x4{h01, h23, M::pack(pw[0] - M::lo(h01), pw[1] - M::hi(h01)),
+                      M::pack(pw[2] - M::lo(h23), pw[3] - M::hi(h23))};
     }
-    l = l * alpha + psum;
-#pragma unroll
-    for (int j = 0; j < NV; ++j) acc[j] *= alpha;
-    // ---- P^T operand as hi + lo pairs
-    const uint32_t h01 = M::pack(pw[0], pw[1]);
-    const uint32_t h23 = M::pack(pw[2], pw[3]);
-    const u32x2 phi = {h01, h23};
-    const u32x2 plo = {M::pack(pw[0] - M::lo(h01), pw[1] - M::hi(h01)),
-                       M::pack(pw[2] - M::lo(h23), pw[3] - M::hi(h23))};
     // ---- O^T += V^T . P^T
     u32x4 vrow[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) vrow[e] = load_bytes<VB>(sv[buf] + (4 * kg + e) * LROW + r16 * VB);
+    for (int e = 0; e < 4; ++e)
+      vrow[e] = load_bytes<VB>(sv[buf] + (4 * kg + e) * LROW + r16 * VB);
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      const u32x2 vop = {half_of(vrow[0], j) | (half_of(vrow[1], j) << 16),
-                         half_of(vrow[2], j) | (half_of(vrow[3], j) << 16)};
-      acc[j] = M::k16(vop, phi, acc[j]);
-      acc[j] = M::k16(vop, plo, acc[j]);
+      const uint32_t v01 = pair_of(vrow[0], vrow[1], j);
+      const uint32_t v23 = pair_of(vrow[2], vrow[3], j);
+      const u32x4 vop = {v01, v23, v01, v23};
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r][j] = M::k32(vop, pcat[r], acc[r][j]);
+    }
+  };
+
+#pragma unroll
+  for (int u = 0; u < P; ++u) gload(u, ld[u]);
+  // Block b: its registers go to LDS buffer b & 1 (the other buffer may
+  // still be read by slower waves for block b - 1), one barrier, then the
+  // freed registers start loading block b + P.
+#pragma unroll 1
+  for (int b0 = 0; b0 < nblk; b0 += P) {
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      const int b = b0 + u;
+      if (b < nblk) {
+        sstore(b & 1, ld[u]);
+        __syncthreads();
+        gload(b + P, ld[u]);
+        compute(b, b & 1);
+      }
     }
   }
 
-  // Each lane summed the weights of its 4 keys per tile; add the 4 groups.
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  if (!qlive) return;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  const int64_t orow = (static_cast<int64_t>(qs + qi) * hq + h) * D;
-  // acc[j][i] is element NV*(4kg + i) + j of the row.
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int r = 0; r < R; ++r) {
+    // Each lane summed the weights of its 4 keys per block; add the 4 groups.
+    float lr = l[r];
+    lr += __shfl_xor(lr, 16);
+    lr += __shfl_xor(lr, 32);
+    if (!qlive[r]) continue;
+    const float inv = lr > 0.f ? 1.f / lr : 0.f;
+    const int64_t orow = (static_cast<int64_t>(qs + q0 + 16 * r + r16) * hq + h) * D;
+    // acc[r][j][i] is element NV*(4kg + i) + j of the row.
 #pragma unroll
-    for (int j = 0; j < NV; ++j) store_out(a, orow + NV * (4 * kg + i) + j, acc[j][i] * inv);
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NV; ++j)
+        store_out(a, orow + NV * (4 * kg + i) + j, acc[r][j][i] * inv);
+  }
 }
 
 template <typename T>
@@ -220,9 +279,11 @@ pkv_status launch_t(const AttnArgs& a, int D, int max_tiles, hipStream_t st) {
   if (wgs > 0x7fffffff / 256) return fail(PKV_ERR_UNSUPPORTED, "prefill: launch too large");
   dim3 grid(static_cast<unsigned>(wgs));
   if (D == 64)
-    hipLaunchKernelGGL((prefill_mfma_kernel<T, 64>), grid, dim3(256), 0, st, a, max_tiles);
+    hipLaunchKernelGGL((prefill_mfma_kernel<T, 64, kDepth, kRowTiles>), grid, dim3(256), 0, st, a,
+                       max_tiles);
   else
-    hipLaunchKernelGGL((prefill_mfma_kernel<T, 128>), grid, dim3(256), 0, st, a, max_tiles);
+    hipLaunchKernelGGL((prefill_mfma_kernel<T, 128, kDepth, kRowTiles>), grid, dim3(256), 0, st,
+                       a, max_tiles);
   PKV_LAUNCH_CHECK("chunked prefill (MFMA)");
   return PKV_OK;
 }
