@@ -127,12 +127,14 @@ __device__ __forceinline__ void merge_factors(float m1, float m2, float& m, floa
 // softmax state (max m, sum l) and an unnormalised output row o[D] in LDS.
 // Rescales them to the common max and either writes the normalised output
 // (the row's context fits one partition) or the partition's partial state.
+// Threads first, first + stride, ... share the elements.
 template <int NW, int NH, int D>
 __device__ __forceinline__ void finish_rows(const AttnArgs& a, const float (&sm_o)[NW][NH][D],
                                             const float (&sm_m)[NW][NH],
                                             const float (&sm_l)[NW][NH], int nheads, int row,
-                                            int hbase, int part, int nparts) {
-  for (int idx = threadIdx.x; idx < nheads * D; idx += blockDim.x) {
+                                            int hbase, int part, int nparts, int first,
+                                            int stride) {
+  for (int idx = first; idx < nheads * D; idx += stride) {
     const int g = idx / D;
     const int d = idx % D;
     float M = sm_m[0][g];

@@ -242,7 +242,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttnArgs a, int group)
     sm_l[wave][r16] = l;
   }
   __syncthreads();
-  finish_rows<kWaves, 16, D>(a, sm_o, sm_m, sm_l, group, row, hbase, part, nparts);
+  finish_rows<kWaves, 16, D>(a, sm_o, sm_m, sm_l, group, row, hbase, part, nparts,
+                             threadIdx.x, blockDim.x);
 }
 
 template <typename QT, typename KT>

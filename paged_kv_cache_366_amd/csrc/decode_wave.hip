@@ -144,6 +144,10 @@ __global__ __launch_bounds__(256) void decode_wave_kernel(AttnArgs a) {
   const int ctx = row_ctx(a, row, seq);
   const int nparts = (ctx + a.part_tokens - 1) / a.part_tokens;
   if (part >= max(nparts, 1)) return;
+  // Arrival counter of the final merge (below).
+  __shared__ int sm_arrived;
+  if (threadIdx.x == 0) sm_arrived = 0;
+  __syncthreads();
 
   const int t0 = part * a.part_tokens;
   const int t1 = min(ctx, t0 + a.part_tokens);
@@ -293,7 +297,10 @@ __global__ __launch_bounds__(256) void decode_wave_kernel(AttnArgs a) {
     }
   }
 
-  // Merge the wavefronts through LDS.
+  // Merge the wavefronts through LDS.  Each wave leaves its state there and
+  // counts itself in; the last to arrive merges all four and writes, the
+  // others end at once (no barrier: a wave with fewer blocks does not wait
+  // for the slowest, and its slot frees for the next workgroup).
   __shared__ float sm_o[kWaves][G][D];
   __shared__ float sm_m[kWaves][G];
   __shared__ float sm_l[kWaves][G];
@@ -308,9 +315,13 @@ __global__ __launch_bounds__(256) void decode_wave_kernel(AttnArgs a) {
       }
     }
   }
-  __syncthreads();
-
-  finish_rows<kWaves, G, D>(a, sm_o, sm_m, sm_l, G, row, hbase, part, nparts);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  int arrived = 0;
+  if (lane == 0) arrived = atomicAdd(&sm_arrived, 1);
+  arrived = __shfl(arrived, 0);
+  if (arrived != kWaves - 1) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  finish_rows<kWaves, G, D>(a, sm_o, sm_m, sm_l, G, row, hbase, part, nparts, lane, 64);
 }
 
 // Merge of the partitions of one (row, head): log-sum-exp rescaling of each
