@@ -13,7 +13,9 @@ the definition states:
     prefill, grouped heads, int8 storage with per-block scales);
   * ``allocator`` - the block manager: LIFO free list, reference counts,
     sequences, fork and copy-on-write on append;
-  * ``cache_ops`` - writing new K/V rows into slots, and whole-block copies.
+  * ``cache_ops`` - writing new K/V rows into slots, and whole-block copies;
+  * ``quantize``  - int8 storage of whole blocks with per-(block, KV head)
+    scales.
 
 Pages cited (each by its address; titles as published):
   [kongchang]  kongchang.com, "vLLM架构深度解析：PagedAttention如何实现高吞吐LLM推理"
@@ -25,4 +27,4 @@ Every function is pinned by a CPU test against something other than itself
 (library routines, closed forms, invariants, brute force, the pages' printed
 allocator behaviour); no function here is "parity unpinned".
 """
-from . import allocator, attention, cache_ops  # noqa: F401
+from . import allocator, attention, cache_ops, quantize  # noqa: F401
