@@ -608,7 +608,59 @@ def bench_beam(a, torch, pkv, algo):
     return result
 
 
-WORKLOADS = ("decode7b", "mixed", "beam", "gqa", "gqa-int8")
+# ---------------------------------------------------------------------------
+# int8 storage of a long-context pool (whole blocks)
+# ---------------------------------------------------------------------------
+def bench_quantize(a, torch, pkv):
+    from synth import workloads as W
+    print("[bench] building the long-context pool on the host", file=sys.stderr, flush=True)
+    c = W.gqa_long_decode(seed=4)
+    dev = "cuda"
+    nb, hkv, D = c.num_blocks, c.kv_heads, c.head_dim
+    owned = [(int(c.block_tables[s_, j]), int(min(BLOCK, n - BLOCK * j)))
+             for s_, n in enumerate(c.context_lens) for j in range(W.blocks_for(n))]
+    blocks = torch.from_numpy(np.array([b for b, _ in owned], np.int32)).to(dev)
+    filled_h = np.array([f for _, f in owned], np.int32)
+    filled = torch.from_numpy(filled_h).to(dev)
+    sk, sv = to_dev_bf16(c.k_cache, torch), to_dev_bf16(c.v_cache, torch)
+    dk = torch.zeros((nb, hkv, BLOCK, D), dtype=torch.int8, device=dev)
+    dv = torch.zeros_like(dk)
+    ks = torch.zeros((nb, hkv), dtype=torch.float32, device=dev)
+    vs = torch.zeros_like(ks)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def step(ev):
+        if ev is not None:
+            ev[0].record(stream)
+        pkv.pkv_quantize_blocks(sk, sv, dk, dv, ks, vs, blocks, filled)
+        if ev is not None:
+            ev[1].record(stream)
+
+    ms_per_step, (q_ms,) = run_timed(torch, step, a.steps, a.warmup, 1)
+    rows = int(filled_h.sum())
+    nlisted = len(owned)
+    # read the filled rows of K and V once (bf16), write every row's int8 code
+    # and one fp32 scale per (block, head), K and V
+    nbytes = rows * hkv * D * 2 * 2 + nlisted * hkv * BLOCK * D * 2 + nlisted * hkv * 4 * 2
+    avg = float(np.mean(q_ms))
+    result = base_result(a, METRIC, nbytes / (ms_per_step * 1e-3) / 1e9, "GB/s", ms_per_step,
+                         "bf16->int8", {
+        "workload": "int8 storage of a long-context pool: every owned block of 16 sequences x "
+                    "8 KV heads x 128, contexts U[8192, 32768], bf16 -> int8 codes + per-(block, "
+                    "head) fp32 scales",
+        "blocks": nlisted})
+    result.update({
+        "kernel_ms": {"quantize_blocks": avg},
+        "bytes": {"per_call": nbytes},
+        "roofline": roofline("quantize_blocks_kernel", "hbm", nbytes / (avg * 1e-3) / 1e9,
+                             HBM_PEAK_GBS, "GB/s"),
+        "cpu_baseline": None,
+    })
+    return result
+
+
+WORKLOADS = ("decode7b", "mixed", "beam", "gqa", "gqa-int8", "quantize")
 
 
 def main(argv=None) -> int:
@@ -650,6 +702,8 @@ def main(argv=None) -> int:
         result = bench_mixed(a, torch, pkv, algo)
     elif a.workload == "beam":
         result = bench_beam(a, torch, pkv, algo)
+    elif a.workload == "quantize":
+        result = bench_quantize(a, torch, pkv)
     else:
         result = bench_gqa(a, torch, pkv, algo, int8=(a.workload == "gqa-int8"))
     print(json.dumps(result), flush=True)

@@ -183,6 +183,36 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* 
                            pkv_dtype dtype, void* stream);
 
 /* ------------------------------------------------------------------------
+ * quantize_blocks (device): int8 storage of whole blocks.  cnnetsun.cn §3.2
+ * (内存压缩技术) lists INT8 KV at a quarter of fp32's bytes, and §4.3
+ * (典型场景优化策略) keeps the historical pages of long documents in INT8.
+ * For each listed block b (dst block b <- src block b) and KV head h, over
+ * the first filled[i] rows of the tile:
+ *     s = max|x| / 127                      (float32, IEEE division)
+ *     code = rint(x / s), clamped to [-127, 127]  (ties to even)
+ * rows past filled[i] get code 0; a block whose scale is below the smallest
+ * normal float32 (values all below ~1.5e-36) stores s = 0 and all-zero codes;
+ * filled[i] == 0 leaves block b untouched.  The result is bit-exact: every
+ * step is float32 arithmetic.  The int8 pool then serves decode through
+ * pkv_paged_attention_decode with kv_dtype I8.
+ *   src_k, src_v   device pools [num_blocks][num_kv_heads][block_size][head_dim]
+ *                  in src_dtype (F32, F16 or BF16), finite values
+ *   dst_k, dst_v   device int8 pools of the same shape (may be other tensors
+ *                  than the sources, never overlapping them)
+ *   k_scale, v_scale device float[num_blocks][num_kv_heads], written for the
+ *                  listed blocks
+ *   blocks, filled device int32[num_listed]: distinct block ids, and filled
+ *                  row counts in [0, block_size] (validated with PKV_VALIDATE=1;
+ *                  otherwise ids outside the pool are skipped and counts are
+ *                  clamped to block_size)
+ * Requires head_dim * element size to be a multiple of 16 bytes. */
+pkv_status pkv_quantize_blocks(const void* src_k, const void* src_v, pkv_dtype src_dtype,
+                               int8_t* dst_k, int8_t* dst_v, float* k_scale, float* v_scale,
+                               const int32_t* blocks, const int32_t* filled, int32_t num_listed,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, void* stream);
+
+/* ------------------------------------------------------------------------
  * Paged decode attention (device).  One query token per sequence, at
  * position context_lens[s] - 1, attends keys [0, context_lens[s]) (the
  * current token's K/V is already in the cache).  For each table entry the

@@ -207,6 +207,30 @@ def pkv_copy_blocks(k_cache, v_cache, pairs, k_scale=None, v_scale=None, stream=
         nb, _dtype_code(k_cache), _stream(k_cache, stream)))
 
 
+def pkv_quantize_blocks(src_k, src_v, dst_k, dst_v, k_scale, v_scale, blocks, filled,
+                        stream=None) -> None:
+    """src pools [NB, Hkv, BS, D] (f32/f16/bf16) -> int8 pools of the same shape
+    and float32 scales [NB, Hkv], for the listed blocks (int32 [n] device
+    tensors of block ids and filled row counts)."""
+    torch = _torch()
+    nb, hkv, bs, d = src_k.shape
+    if src_v.shape != src_k.shape or dst_k.shape != src_k.shape or dst_v.shape != src_k.shape:
+        raise ValueError("pools must share one shape")
+    if src_v.dtype != src_k.dtype:
+        raise TypeError("src_k and src_v must share a dtype")
+    if k_scale.shape != (nb, hkv) or v_scale.shape != (nb, hkv):
+        raise ValueError("scales must be [num_blocks, num_kv_heads]")
+    n = blocks.shape[0]
+    if filled.shape != (n,):
+        raise ValueError("blocks and filled must have one entry per listed block")
+    check(load().pkv_quantize_blocks(
+        _dev(src_k, "src_k"), _dev(src_v, "src_v"), _dtype_code(src_k),
+        _dev(dst_k, "dst_k", torch.int8), _dev(dst_v, "dst_v", torch.int8),
+        _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32),
+        _dev(blocks, "blocks", torch.int32), _dev(filled, "filled", torch.int32), n, hkv, d, bs,
+        nb, _stream(src_k, stream)))
+
+
 def pkv_decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
                                max_context_len: int, partition_tokens: int) -> int:
     return load().pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,

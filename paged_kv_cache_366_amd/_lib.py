@@ -49,6 +49,8 @@ SIGNATURES = {
     "pkv_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i32, _i32, _i32,
                                      _i32, _i32, _vp]),
     "pkv_copy_blocks": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pkv_quantize_blocks": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                   _i32, _i32, _vp]),
     "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pkv_paged_attention_decode": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp,
                                           _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,

@@ -78,6 +78,111 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
   }
 }
 
+// Int8 storage of whole blocks: one wavefront per (listed block, KV head,
+// K or V) tile.  The first pass takes max |x| over the filled rows, the
+// second writes the codes (from registers for tiles up to 4 KiB); every
+// step is the float32 arithmetic of the encoding: s = a / 127, code =
+// rint(x / s) clamped to [-127, 127], rows past the filled count 0, a
+// subnormal scale counting as zero.
+constexpr float kSmallestNormal = 1.17549435e-38f;
+
+__device__ __forceinline__ float wave_absmax(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void quantize_blocks_kernel(
+    const uint8_t* __restrict__ src_k, const uint8_t* __restrict__ src_v,
+    int8_t* __restrict__ dst_k, int8_t* __restrict__ dst_v, float* __restrict__ ks,
+    float* __restrict__ vs, const int32_t* __restrict__ blocks,
+    const int32_t* __restrict__ filled, int n, int hkv, int head_dim, int block_size,
+    int num_blocks) {
+  constexpr int E = 16 / T::bytes;                 // elements per 16-byte chunk
+  const int tile = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (tile >= n * hkv * 2) return;
+  const int which = tile & 1;
+  const int h = (tile >> 1) % hkv;
+  const int i = (tile >> 1) / hkv;
+  const int b = blocks[i];
+  const int f = min(filled[i], block_size);
+  if (b < 0 || b >= num_blocks || f <= 0) return;
+  const int64_t elems = static_cast<int64_t>(block_size) * head_dim;
+  const int64_t tix = static_cast<int64_t>(b) * hkv + h;
+  const uint8_t* src = (which ? src_v : src_k) + tix * elems * T::bytes;
+  int8_t* dst = (which ? dst_v : dst_k) + tix * elems;
+  const int filled_chunks = f * head_dim / E;
+  const int all_chunks = block_size * head_dim / E;
+
+  // Tiles of up to 256 chunks (16 rows of 128 bf16 or 64 fp32 values) stay
+  // in registers between the two passes; larger ones are read again.
+  constexpr int kKeep = 4;
+  const bool keep = all_chunks <= 64 * kKeep;
+  u32x4 held[kKeep];
+  float amax = 0.f;
+  if (keep) {
+#pragma unroll
+    for (int k = 0; k < kKeep; ++k) {
+      const int c = lane + 64 * k;
+      held[k] = u32x4{0u, 0u, 0u, 0u};
+      if (c < filled_chunks) held[k] = *reinterpret_cast<const u32x4*>(src + c * 16);
+    }
+#pragma unroll
+    for (int k = 0; k < kKeep; ++k) {
+      float x[E];
+      Unpack<T>::run(held[k], x);
+#pragma unroll
+      for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(x[e]));
+    }
+  } else {
+    for (int c = lane; c < filled_chunks; c += 64) {
+      float x[E];
+      Unpack<T>::run(*reinterpret_cast<const u32x4*>(src + c * 16), x);
+#pragma unroll
+      for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(x[e]));
+    }
+  }
+  amax = wave_absmax(amax);
+  float sc = amax / 127.f;
+  if (!(sc >= kSmallestNormal)) sc = 0.f;
+
+  auto encode = [&](int c, const u32x4& w) {
+    int8_t q[E];
+    if (c < filled_chunks && sc > 0.f) {
+      float x[E];
+      Unpack<T>::run(w, x);
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        q[e] = static_cast<int8_t>(fminf(fmaxf(rintf(x[e] / sc), -127.f), 127.f));
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) q[e] = 0;
+    }
+    int8_t* d = dst + static_cast<int64_t>(c) * E;
+    if constexpr (E == 8) {
+      *reinterpret_cast<uint64_t*>(d) = __builtin_bit_cast(uint64_t, q);
+    } else {
+      *reinterpret_cast<uint32_t*>(d) = __builtin_bit_cast(uint32_t, q);
+    }
+  };
+  if (keep) {
+#pragma unroll
+    for (int k = 0; k < kKeep; ++k) {
+      const int c = lane + 64 * k;
+      if (c < all_chunks) encode(c, held[k]);
+    }
+  } else {
+    for (int c = lane; c < all_chunks; c += 64) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (c < filled_chunks) w = *reinterpret_cast<const u32x4*>(src + c * 16);
+      encode(c, w);
+    }
+  }
+  if (lane == 0) (which ? vs : ks)[tix] = sc;
+}
+
 }  // namespace
 }  // namespace pkv
 
@@ -182,6 +287,70 @@ extern "C" pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, float* k_sca
                        dtype == PKV_I8 ? k_scale : nullptr, dtype == PKV_I8 ? v_scale : nullptr,
                        pairs, block_bytes, num_kv_heads, num_blocks);
     PKV_LAUNCH_CHECK("copy_blocks");
+    return PKV_OK;
+  })
+}
+
+extern "C" pkv_status pkv_quantize_blocks(const void* src_k, const void* src_v,
+                                          pkv_dtype src_dtype, int8_t* dst_k, int8_t* dst_v,
+                                          float* k_scale, float* v_scale, const int32_t* blocks,
+                                          const int32_t* filled, int32_t num_listed,
+                                          int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t block_size, int32_t num_blocks, void* stream) {
+  PKV_GUARD({
+    const char* who = "quantize_blocks";
+    if (src_dtype != PKV_F32 && src_dtype != PKV_F16 && src_dtype != PKV_BF16)
+      return fail(PKV_ERR_UNSUPPORTED, "%s: source dtype %s (f32, f16 or bf16)", who,
+                  dtype_name(src_dtype));
+    if (num_listed < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        num_blocks <= 0)
+      return fail(PKV_ERR_INVALID, "%s: bad sizes", who);
+    if (num_listed == 0) return PKV_OK;
+    if (!src_k || !src_v || !dst_k || !dst_v || !k_scale || !v_scale || !blocks || !filled)
+      return fail(PKV_ERR_INVALID, "%s: NULL pointer", who);
+    const int eb = dtype_bytes(src_dtype);
+    if ((head_dim * eb) % 16 != 0)
+      return fail(PKV_ERR_UNSUPPORTED, "%s: head_dim * element size must be a multiple of 16",
+                  who);
+    if (!aligned(src_k, 16) || !aligned(src_v, 16) || !aligned(dst_k, 8) || !aligned(dst_v, 8))
+      return fail(PKV_ERR_INVALID, "%s: pools must be 16-byte (source) / 8-byte (int8) aligned",
+                  who);
+    if (static_cast<int64_t>(num_listed) * num_kv_heads * 2 > 0x7fffffffLL)
+      return fail(PKV_ERR_UNSUPPORTED, "%s: too many tiles", who);
+    if (deep_validation()) {
+      std::vector<int32_t> bl, fl;
+      pkv_status st = fetch_i32(blocks, num_listed, stream, bl);
+      if (st) return st;
+      st = fetch_i32(filled, num_listed, stream, fl);
+      if (st) return st;
+      std::unordered_set<int32_t> seen;
+      for (int32_t i = 0; i < num_listed; ++i) {
+        if (bl[i] < 0 || bl[i] >= num_blocks)
+          return fail(PKV_ERR_INVALID, "%s: blocks[%d] = %d outside the pool", who, i, bl[i]);
+        if (fl[i] < 0 || fl[i] > block_size)
+          return fail(PKV_ERR_INVALID, "%s: filled[%d] = %d outside [0, %d]", who, i, fl[i],
+                      block_size);
+        if (!seen.insert(bl[i]).second)
+          return fail(PKV_ERR_INVALID, "%s: block %d listed twice", who, bl[i]);
+      }
+    }
+    const int64_t tiles = static_cast<int64_t>(num_listed) * num_kv_heads * 2;
+    const dim3 grid(static_cast<unsigned>((tiles + 3) / 4));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const uint8_t* sk = static_cast<const uint8_t*>(src_k);
+    const uint8_t* sv = static_cast<const uint8_t*>(src_v);
+    auto launch = [&](auto tag) {
+      hipLaunchKernelGGL(quantize_blocks_kernel<decltype(tag)>, grid, dim3(kThreads), 0, st, sk,
+                         sv, dst_k, dst_v, k_scale, v_scale, blocks, filled, num_listed,
+                         num_kv_heads, head_dim, block_size, num_blocks);
+    };
+    if (src_dtype == PKV_BF16)
+      launch(BF16{});
+    else if (src_dtype == PKV_F16)
+      launch(F16{});
+    else
+      launch(F32{});
+    PKV_LAUNCH_CHECK("quantize_blocks");
     return PKV_OK;
   })
 }

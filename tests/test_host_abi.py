@@ -72,6 +72,15 @@ def test_device_entry_points_reject_bad_arguments_without_a_gpu():
     # int8 reshape_and_cache is not provided
     st = lib.pkv_reshape_and_cache(None, None, None, None, None, 4, 0, 0, 8, 128, 16, 10, 3, None)
     assert st == PKV_ERR_UNSUPPORTED
+    # quantize_blocks: int8 source, NULL pointers, odd row bytes
+    st = lib.pkv_quantize_blocks(None, None, 3, None, None, None, None, None, None, 4, 8, 128, 16,
+                                 10, None)
+    assert st == PKV_ERR_UNSUPPORTED
+    st = lib.pkv_quantize_blocks(None, None, PKV_BF16, None, None, None, None, None, None, 4, 8,
+                                 128, 16, 10, None)
+    assert st == PKV_ERR_INVALID
+    assert lib.pkv_quantize_blocks(None, None, PKV_BF16, None, None, None, None, None, None, 0, 8,
+                                   128, 16, 10, None) == 0
 
 
 def test_workspace_size_formula():
