@@ -660,7 +660,62 @@ def bench_quantize(a, torch, pkv):
     return result
 
 
-WORKLOADS = ("decode7b", "mixed", "beam", "gqa", "gqa-int8", "quantize")
+# ---------------------------------------------------------------------------
+# preemption by swapping: blocks device -> pinned host -> device
+# ---------------------------------------------------------------------------
+def bench_swap(a, torch, pkv):
+    from synth import workloads as W
+    print("[bench] building the 7B-shape pool on the host", file=sys.stderr, flush=True)
+    wl = Workload(seed=a.seed)
+    dev = "cuda"
+    kc, vc = to_dev_bf16(wl.kc_full, torch), to_dev_bf16(wl.vc_full, torch)
+    # the 16 longest sequences are preempted: all their blocks go to host memory
+    order = np.argsort(-wl.lens)[:16]
+    own = np.concatenate([wl.tables[s_, :W.blocks_for(wl.lens[s_])] for s_ in order]).astype(np.int32)
+    n = len(own)
+    shape = (n,) + tuple(kc.shape[1:])
+    hk = torch.empty(shape, dtype=torch.bfloat16).pin_memory()
+    hv = torch.empty(shape, dtype=torch.bfloat16).pin_memory()
+    out_pairs = np.stack([own, np.arange(n, dtype=np.int32)], 1)
+    in_pairs = np.stack([np.arange(n, dtype=np.int32), own], 1)
+    # staging for 256 blocks per round (64 MiB): gather/scatter on the
+    # device, long runs over PCIe
+    ws = torch.empty(pkv.pkv_swap_workspace_bytes(256, kc.shape[1], kc.shape[3], BLOCK,
+                                                  pkv.PKV_BF16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def step(ev):
+        if ev is not None:
+            ev[0].record(stream)
+        pkv.pkv_swap_blocks(hk, hv, kc, vc, out_pairs, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+        pkv.pkv_swap_blocks(kc, vc, hk, hv, in_pairs, workspace=ws)
+        if ev is not None:
+            ev[2].record(stream)
+
+    ms_per_step, (out_ms, in_ms) = run_timed(torch, step, a.steps, a.warmup, 2)
+    nbytes = n * int(np.prod(kc.shape[1:])) * 2 * 2          # K and V, one direction
+    o, i_ = float(np.mean(out_ms)), float(np.mean(in_ms))
+    result = base_result(a, METRIC, 2 * nbytes / (ms_per_step * 1e-3) / 1e9, "GB/s", ms_per_step,
+                         "bf16", {
+        "workload": "preemption by swapping at the 7B shape: every block of the 16 longest "
+                    "sequences (32 heads x 128, bf16) to pinned host memory and back",
+        "blocks": n})
+    result.update({
+        "kernel_ms": {"swap_out": o, "swap_in": i_},
+        "bytes": {"per_direction": nbytes},
+        "gbs": {"device_to_host": nbytes / (o * 1e-3) / 1e9, "host_to_device": nbytes / (i_ * 1e-3) / 1e9},
+        "roofline": None,
+        "note": "DMA over PCIe; the pages quote 32-64 GB/s for PCIe (kongchang.com, section "
+                "on preemption)",
+        "cpu_baseline": None,
+    })
+    return result
+
+
+WORKLOADS = ("decode7b", "mixed", "beam", "gqa", "gqa-int8", "quantize", "swap")
 
 
 def main(argv=None) -> int:
@@ -704,6 +759,8 @@ def main(argv=None) -> int:
         result = bench_beam(a, torch, pkv, algo)
     elif a.workload == "quantize":
         result = bench_quantize(a, torch, pkv)
+    elif a.workload == "swap":
+        result = bench_swap(a, torch, pkv)
     else:
         result = bench_gqa(a, torch, pkv, algo, int8=(a.workload == "gqa-int8"))
     print(json.dumps(result), flush=True)

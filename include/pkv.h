@@ -183,6 +183,44 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* 
                            pkv_dtype dtype, void* stream);
 
 /* ------------------------------------------------------------------------
+ * swap_blocks: preemption by swapping moves a preempted request's KV blocks
+ * over PCIe from GPU memory to CPU memory and back when it resumes
+ * ([kongchang] section "抢占与恢复机制"; cold pages may live in host memory,
+ * [cnnetsun] §2.3).  For each pair (s, d): block d of the destination pool
+ * receives block s of the source pool (K, V, and for I8 storage the
+ * per-(block, kv head) scales); other destination blocks are unchanged.
+ *   dst_*, src_*   pools [num_blocks][num_kv_heads][block_size][head_dim] in
+ *                  `dtype`, each in device memory or in pinned host memory
+ *                  (hipHostMalloc; pageable host memory works but copies
+ *                  synchronously); the two pools never overlap
+ *   *_scale        float [num_blocks][num_kv_heads], I8 only (else NULL)
+ *   pairs          HOST int32[num_pairs][2] (source block, destination block);
+ *                  always validated: ids inside their pools, destinations
+ *                  distinct (INVALID otherwise, nothing copied)
+ *   workspace      device scratch, 256-byte aligned, or NULL.  Between device
+ *                  and host pools the scattered device blocks are gathered
+ *                  into it (or scattered from it) by a copy kernel, so the
+ *                  PCIe side moves runs of consecutive host blocks; it holds
+ *                  as many blocks per round as fit (at least one block, else
+ *                  INVALID), pkv_swap_workspace_bytes(n, ...) covers n pairs
+ *                  in one round.  With NULL, each run of consecutive pairs
+ *                  is one DMA copy.  Between two device pools the copy is a
+ *                  kernel (block ids through the workspace when given).
+ * The copies run asynchronously on `stream` (DMA engines for host memory);
+ * the caller keeps the host pool and the workspace alive until the stream
+ * has passed them.  Bit-exact. */
+pkv_status pkv_swap_blocks(void* dst_k, void* dst_v, float* dst_k_scale, float* dst_v_scale,
+                           int32_t dst_num_blocks, const void* src_k, const void* src_v,
+                           const float* src_k_scale, const float* src_v_scale,
+                           int32_t src_num_blocks, const int32_t* pairs, int32_t num_pairs,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           pkv_dtype dtype, void* workspace, size_t workspace_bytes,
+                           void* stream);
+/* Workspace bytes for swapping up to max_pairs blocks in one round. */
+size_t pkv_swap_workspace_bytes(int32_t max_pairs, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t block_size, pkv_dtype dtype);
+
+/* ------------------------------------------------------------------------
  * quantize_blocks (device): int8 storage of whole blocks.  cnnetsun.cn §3.2
  * (内存压缩技术) lists INT8 KV at a quarter of fp32's bytes, and §4.3
  * (典型场景优化策略) keeps the historical pages of long documents in INT8.

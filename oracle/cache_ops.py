@@ -9,6 +9,11 @@
   contents of the shared one before the writer appends ([kongchang] section
   "KV Cache内存共享").  Each (src, dst) pair copies K, V and, for int8
   storage, the per-block scales.
+* ``swap_blocks``: preemption by swapping moves a preempted request's KV
+  blocks from GPU memory to CPU memory and back when it resumes
+  ([kongchang] section "抢占与恢复机制"; cold pages go to host memory in
+  [cnnetsun] §2.3).  Each (src, dst) pair copies block src of one pool to
+  block dst of another pool (K, V and, for int8 storage, the scales).
 
 Both return new arrays and leave the inputs untouched.
 """
@@ -47,3 +52,21 @@ def copy_blocks(k_cache: np.ndarray, v_cache: np.ndarray, pairs: Sequence[Tuple[
         if vs is not None:
             vs[int(dst)] = v_scale[int(src)]
     return kc, vc, ks, vs
+
+
+def swap_blocks(dst_k: np.ndarray, dst_v: np.ndarray, src_k: np.ndarray, src_v: np.ndarray,
+                pairs: Sequence[Tuple[int, int]], dst_ks: Optional[np.ndarray] = None,
+                dst_vs: Optional[np.ndarray] = None, src_ks: Optional[np.ndarray] = None,
+                src_vs: Optional[np.ndarray] = None):
+    """Copies of the destination pools with ``dst[d] = src[s]`` for every
+    (s, d) pair; every other destination block keeps its contents."""
+    dk, dv = dst_k.copy(), dst_v.copy()
+    dks = None if dst_ks is None else dst_ks.copy()
+    dvs = None if dst_vs is None else dst_vs.copy()
+    for s, d in pairs:
+        dk[int(d)] = src_k[int(s)]
+        dv[int(d)] = src_v[int(s)]
+        if dks is not None:
+            dks[int(d)] = src_ks[int(s)]
+            dvs[int(d)] = src_vs[int(s)]
+    return dk, dv, dks, dvs

@@ -207,6 +207,41 @@ def pkv_copy_blocks(k_cache, v_cache, pairs, k_scale=None, v_scale=None, stream=
         nb, _dtype_code(k_cache), _stream(k_cache, stream)))
 
 
+def pkv_swap_workspace_bytes(max_pairs: int, num_kv_heads: int, head_dim: int, block_size: int,
+                             dtype_code: int) -> int:
+    return load().pkv_swap_workspace_bytes(max_pairs, num_kv_heads, head_dim, block_size,
+                                           dtype_code)
+
+
+def pkv_swap_blocks(dst_k, dst_v, src_k, src_v, pairs, dst_k_scale=None, dst_v_scale=None,
+                    src_k_scale=None, src_v_scale=None, workspace=None, stream=None) -> None:
+    """Block d of the destination pools <- block s of the source pools for each
+    (s, d) row of `pairs` (host int32 [n, 2]).  Pools are torch tensors
+    [NB, Hkv, BS, D] on the GPU or in pinned host memory; `workspace` is an
+    optional uint8 GPU tensor (see pkv_swap_workspace_bytes)."""
+    torch = _torch()
+    if dst_k.shape[1:] != src_k.shape[1:] or dst_v.shape != dst_k.shape or src_v.shape != src_k.shape:
+        raise ValueError("pools must share [Hkv, BS, D]")
+    if not (dst_k.dtype == dst_v.dtype == src_k.dtype == src_v.dtype):
+        raise TypeError("pools must share a dtype")
+    for t, n in ((dst_k, "dst_k"), (dst_v, "dst_v"), (src_k, "src_k"), (src_v, "src_v")):
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+        if not (t.is_cuda or t.is_pinned()):
+            raise ValueError(f"{n} must be a GPU tensor or pinned host memory")
+    p = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
+    _, hkv, bs, d = src_k.shape
+    ptr = lambda t: None if t is None else C.c_void_p(t.data_ptr())
+    dev = dst_k if dst_k.is_cuda else src_k
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if workspace is not None and not workspace.is_cuda:
+        raise ValueError("workspace must be a GPU tensor")
+    check(load().pkv_swap_blocks(
+        ptr(dst_k), ptr(dst_v), ptr(dst_k_scale), ptr(dst_v_scale), dst_k.shape[0], ptr(src_k),
+        ptr(src_v), ptr(src_k_scale), ptr(src_v_scale), src_k.shape[0], _i32p(p), p.shape[0],
+        hkv, d, bs, _dtype_code(src_k), ptr(workspace), ws_len, _stream(dev, stream)))
+
+
 def pkv_quantize_blocks(src_k, src_v, dst_k, dst_v, k_scale, v_scale, blocks, filled,
                         stream=None) -> None:
     """src pools [NB, Hkv, BS, D] (f32/f16/bf16) -> int8 pools of the same shape

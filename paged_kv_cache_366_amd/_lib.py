@@ -49,6 +49,9 @@ SIGNATURES = {
     "pkv_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i32, _i32, _i32,
                                      _i32, _i32, _vp]),
     "pkv_copy_blocks": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pkv_swap_blocks": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _pi32, _i32,
+                               _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
+    "pkv_swap_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pkv_quantize_blocks": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                    _i32, _i32, _vp]),
     "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),

@@ -11,6 +11,7 @@
 // kernel touches a slot or block outside the pool whatever the index arrays
 // hold.
 #include <unordered_set>
+#include <vector>
 
 #include "device_common.h"
 #include "host_checks.h"
@@ -183,6 +184,32 @@ __global__ __launch_bounds__(kThreads) void quantize_blocks_kernel(
   if (lane == 0) (which ? vs : ks)[tix] = sc;
 }
 
+// Block copies between two pools (or a pool and a packed staging area):
+// block k of the list goes from src block src_ids[k] (or k) to dst block
+// dst_ids[k] (or k).  grid (block of the list, K or V, 16 KiB chunk).
+__global__ __launch_bounds__(kThreads) void copy_list_kernel(
+    uint8_t* __restrict__ dst_k, uint8_t* __restrict__ dst_v, const uint8_t* __restrict__ src_k,
+    const uint8_t* __restrict__ src_v, const int32_t* __restrict__ dst_ids,
+    const int32_t* __restrict__ src_ids, int64_t block_bytes) {
+  const int k = blockIdx.x;
+  const int64_t d = dst_ids ? dst_ids[k] : k;
+  const int64_t s = src_ids ? src_ids[k] : k;
+  const uint8_t* src = (blockIdx.y == 0 ? src_k : src_v) + s * block_bytes;
+  uint8_t* dst = (blockIdx.y == 0 ? dst_k : dst_v) + d * block_bytes;
+  const int64_t start = static_cast<int64_t>(blockIdx.z) * kCopyChunkBytes;
+  u32x4 buf[kCopyUnroll];
+#pragma unroll
+  for (int i = 0; i < kCopyUnroll; ++i) {
+    const int64_t o = start + (static_cast<int64_t>(i) * kThreads + threadIdx.x) * 16;
+    if (o < block_bytes) buf[i] = *reinterpret_cast<const u32x4*>(src + o);
+  }
+#pragma unroll
+  for (int i = 0; i < kCopyUnroll; ++i) {
+    const int64_t o = start + (static_cast<int64_t>(i) * kThreads + threadIdx.x) * 16;
+    if (o < block_bytes) *reinterpret_cast<u32x4*>(dst + o) = buf[i];
+  }
+}
+
 }  // namespace
 }  // namespace pkv
 
@@ -351,6 +378,218 @@ extern "C" pkv_status pkv_quantize_blocks(const void* src_k, const void* src_v,
     else
       launch(F32{});
     PKV_LAUNCH_CHECK("quantize_blocks");
+    return PKV_OK;
+  })
+}
+
+// swap_blocks.  Device <-> host swaps go through the DMA engines in
+// contiguous runs: with a workspace, the scattered device blocks are first
+// gathered into it (or scattered from it) by a copy kernel at HBM speed, so
+// the PCIe side moves long runs; without one, each run of consecutive pairs
+// is one copy.  Device <-> device swaps run the copy kernel directly.
+namespace {
+
+bool is_device_memory(const void* p) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();   // pageable host memory is unknown to the runtime
+    return false;
+  }
+  return attr.type == hipMemoryTypeDevice;
+}
+
+}  // namespace
+
+extern "C" size_t pkv_swap_workspace_bytes(int32_t max_pairs, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size,
+                                           pkv_dtype dtype) {
+  const int eb = dtype_bytes(dtype);
+  if (max_pairs <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || eb == 0)
+    return 0;
+  const size_t bb = static_cast<size_t>(num_kv_heads) * block_size * head_dim * eb;
+  const size_t per = 2 * bb + (dtype == PKV_I8 ? 2 * sizeof(float) * num_kv_heads : 0);
+  return 256 + static_cast<size_t>(max_pairs) * (sizeof(int32_t) + per + 64);
+}
+
+extern "C" pkv_status pkv_swap_blocks(void* dst_k, void* dst_v, float* dst_k_scale,
+                                      float* dst_v_scale, int32_t dst_num_blocks,
+                                      const void* src_k, const void* src_v,
+                                      const float* src_k_scale, const float* src_v_scale,
+                                      int32_t src_num_blocks, const int32_t* pairs,
+                                      int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, pkv_dtype dtype, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  PKV_GUARD({
+    const char* who = "swap_blocks";
+    const int eb = dtype_bytes(dtype);
+    if (eb == 0) return fail(PKV_ERR_INVALID, "%s: unknown dtype", who);
+    if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        dst_num_blocks <= 0 || src_num_blocks <= 0)
+      return fail(PKV_ERR_INVALID, "%s: bad sizes", who);
+    if (num_pairs == 0) return PKV_OK;
+    if (!dst_k || !dst_v || !src_k || !src_v || !pairs)
+      return fail(PKV_ERR_INVALID, "%s: NULL pointer", who);
+    const bool scales = dtype == PKV_I8;
+    if (scales && (!dst_k_scale || !dst_v_scale || !src_k_scale || !src_v_scale))
+      return fail(PKV_ERR_INVALID, "%s: int8 pools need all four scale arrays", who);
+    std::unordered_set<int32_t> seen_dst;
+    for (int32_t i = 0; i < num_pairs; ++i) {
+      const int32_t s_ = pairs[2 * i], d_ = pairs[2 * i + 1];
+      if (s_ < 0 || s_ >= src_num_blocks || d_ < 0 || d_ >= dst_num_blocks)
+        return fail(PKV_ERR_INVALID, "%s: pair %d (%d -> %d) outside the pools", who, i, s_, d_);
+      if (!seen_dst.insert(d_).second)
+        return fail(PKV_ERR_INVALID, "%s: block %d is the destination of two pairs", who, d_);
+    }
+    const size_t bb = static_cast<size_t>(num_kv_heads) * block_size * head_dim * eb;
+    const size_t sb = static_cast<size_t>(num_kv_heads) * sizeof(float);
+    if (bb % 16 != 0 || !aligned(dst_k, 16) || !aligned(dst_v, 16) || !aligned(src_k, 16) ||
+        !aligned(src_v, 16))
+      return fail(PKV_ERR_INVALID, "%s: pools must be 16-byte aligned with 16-byte blocks", who);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool src_dev = is_device_memory(src_k) && is_device_memory(src_v);
+    const bool dst_dev = is_device_memory(dst_k) && is_device_memory(dst_v);
+    const int64_t chunks = (static_cast<int64_t>(bb) + kCopyChunkBytes - 1) / kCopyChunkBytes;
+    if (chunks > 65535) return fail(PKV_ERR_UNSUPPORTED, "%s: blocks too large", who);
+
+    auto memcpy_runs = [&](void* d_base, const void* s_base, size_t unit, const int32_t* dl,
+                           const int32_t* sl, int32_t n, int32_t d_stride, int32_t s_stride) {
+      // copies list entries k (dst id dl[k*d_stride] or k, src id sl[k*s_stride] or k),
+      // merged into runs where both sides continue
+      for (int32_t i = 0; i < n;) {
+        const int32_t d0 = dl ? dl[i * d_stride] : i, s0 = sl ? sl[i * s_stride] : i;
+        int32_t len = 1;
+        while (i + len < n && (dl ? dl[(i + len) * d_stride] : i + len) == d0 + len &&
+               (sl ? sl[(i + len) * s_stride] : i + len) == s0 + len)
+          ++len;
+        const hipError_t e = hipMemcpyAsync(static_cast<char*>(d_base) + unit * d0,
+                                            static_cast<const char*>(s_base) + unit * s0,
+                                            unit * len, hipMemcpyDefault, st);
+        if (e != hipSuccess) return e;
+        i += len;
+      }
+      return hipSuccess;
+    };
+
+    hipError_t e = hipSuccess;
+    if (src_dev && dst_dev) {
+      // both pools on the device: the copy kernel, ids through the workspace
+      // when there is one, else one copy per run
+      if (workspace && workspace_bytes >= 256 + static_cast<size_t>(num_pairs) * 8 &&
+          aligned(workspace, 256)) {
+        int32_t* ids = static_cast<int32_t*>(workspace);
+        {
+          // source ids, then destination ids
+          std::vector<int32_t> sd(2 * static_cast<size_t>(num_pairs));
+          for (int32_t i = 0; i < num_pairs; ++i) {
+            sd[i] = pairs[2 * i];
+            sd[num_pairs + i] = pairs[2 * i + 1];
+          }
+          e = hipMemcpyAsync(ids, sd.data(), sd.size() * sizeof(int32_t), hipMemcpyHostToDevice, st);
+          if (e == hipSuccess) {
+            hipLaunchKernelGGL(copy_list_kernel, dim3(num_pairs, 2, static_cast<unsigned>(chunks)),
+                               dim3(kThreads), 0, st, static_cast<uint8_t*>(dst_k),
+                               static_cast<uint8_t*>(dst_v), static_cast<const uint8_t*>(src_k),
+                               static_cast<const uint8_t*>(src_v), ids + num_pairs, ids,
+                               static_cast<int64_t>(bb));
+            e = hipGetLastError();
+          }
+        }
+        if (e == hipSuccess && scales) {
+          e = memcpy_runs(dst_k_scale, src_k_scale, sb, pairs + 1, pairs, num_pairs, 2, 2);
+          if (e == hipSuccess)
+            e = memcpy_runs(dst_v_scale, src_v_scale, sb, pairs + 1, pairs, num_pairs, 2, 2);
+        }
+      } else {
+        e = memcpy_runs(dst_k, src_k, bb, pairs + 1, pairs, num_pairs, 2, 2);
+        if (e == hipSuccess) e = memcpy_runs(dst_v, src_v, bb, pairs + 1, pairs, num_pairs, 2, 2);
+        if (e == hipSuccess && scales) {
+          e = memcpy_runs(dst_k_scale, src_k_scale, sb, pairs + 1, pairs, num_pairs, 2, 2);
+          if (e == hipSuccess)
+            e = memcpy_runs(dst_v_scale, src_v_scale, sb, pairs + 1, pairs, num_pairs, 2, 2);
+        }
+      }
+    } else if (src_dev != dst_dev && workspace && aligned(workspace, 256)) {
+      // device <-> host through staging: per chunk of C pairs, the ids, then
+      // C packed K blocks, C packed V blocks (and their scales)
+      const size_t per = 2 * bb + (scales ? 2 * sb : 0);
+      const size_t avail = workspace_bytes > 256 ? workspace_bytes - 256 : 0;
+      int64_t cap = static_cast<int64_t>(avail / (sizeof(int32_t) + per + 64));
+      if (cap < 1) return fail(PKV_ERR_INVALID, "%s: workspace smaller than one block", who);
+      cap = std::min<int64_t>(cap, num_pairs);
+      uint8_t* ws = static_cast<uint8_t*>(workspace);
+      int32_t* ids = reinterpret_cast<int32_t*>(ws);
+      const size_t ids_bytes = (static_cast<size_t>(cap) * sizeof(int32_t) + 255) / 256 * 256;
+      uint8_t* stage_k = ws + ids_bytes;
+      uint8_t* stage_v = stage_k + cap * bb;
+      float* stage_ks = reinterpret_cast<float*>(stage_v + cap * bb);
+      float* stage_vs = stage_ks + cap * num_kv_heads;
+      std::vector<int32_t> dev_ids(static_cast<size_t>(cap)), host_ids(static_cast<size_t>(cap));
+      for (int32_t start = 0; start < num_pairs && e == hipSuccess; start += cap) {
+        const int32_t cnt = static_cast<int32_t>(std::min<int64_t>(cap, num_pairs - start));
+        for (int32_t k = 0; k < cnt; ++k) {
+          const int32_t s_ = pairs[2 * (start + k)], d_ = pairs[2 * (start + k) + 1];
+          dev_ids[k] = src_dev ? s_ : d_;
+          host_ids[k] = src_dev ? d_ : s_;
+        }
+        e = hipMemcpyAsync(ids, dev_ids.data(), cnt * sizeof(int32_t), hipMemcpyHostToDevice, st);
+        if (e != hipSuccess) break;
+        const dim3 grid(cnt, 2, static_cast<unsigned>(chunks));
+        if (src_dev) {
+          // gather on the device, then long runs over PCIe
+          hipLaunchKernelGGL(copy_list_kernel, grid, dim3(kThreads), 0, st, stage_k, stage_v,
+                             static_cast<const uint8_t*>(src_k), static_cast<const uint8_t*>(src_v),
+                             nullptr, ids, static_cast<int64_t>(bb));
+          e = hipGetLastError();
+          if (e == hipSuccess && scales) {
+            e = memcpy_runs(stage_ks, src_k_scale, sb, nullptr, dev_ids.data(), cnt, 1, 1);
+            if (e == hipSuccess)
+              e = memcpy_runs(stage_vs, src_v_scale, sb, nullptr, dev_ids.data(), cnt, 1, 1);
+          }
+          if (e == hipSuccess)
+            e = memcpy_runs(dst_k, stage_k, bb, host_ids.data(), nullptr, cnt, 1, 1);
+          if (e == hipSuccess)
+            e = memcpy_runs(dst_v, stage_v, bb, host_ids.data(), nullptr, cnt, 1, 1);
+          if (e == hipSuccess && scales) {
+            e = memcpy_runs(dst_k_scale, stage_ks, sb, host_ids.data(), nullptr, cnt, 1, 1);
+            if (e == hipSuccess)
+              e = memcpy_runs(dst_v_scale, stage_vs, sb, host_ids.data(), nullptr, cnt, 1, 1);
+          }
+        } else {
+          // long runs over PCIe into staging, then scatter on the device
+          e = memcpy_runs(stage_k, src_k, bb, nullptr, host_ids.data(), cnt, 1, 1);
+          if (e == hipSuccess) e = memcpy_runs(stage_v, src_v, bb, nullptr, host_ids.data(), cnt, 1, 1);
+          if (e == hipSuccess && scales) {
+            e = memcpy_runs(stage_ks, src_k_scale, sb, nullptr, host_ids.data(), cnt, 1, 1);
+            if (e == hipSuccess)
+              e = memcpy_runs(stage_vs, src_v_scale, sb, nullptr, host_ids.data(), cnt, 1, 1);
+          }
+          if (e == hipSuccess) {
+            hipLaunchKernelGGL(copy_list_kernel, grid, dim3(kThreads), 0, st,
+                               static_cast<uint8_t*>(dst_k), static_cast<uint8_t*>(dst_v),
+                               stage_k, stage_v, ids, nullptr, static_cast<int64_t>(bb));
+            e = hipGetLastError();
+          }
+          if (e == hipSuccess && scales) {
+            e = memcpy_runs(dst_k_scale, stage_ks, sb, dev_ids.data(), nullptr, cnt, 1, 1);
+            if (e == hipSuccess)
+              e = memcpy_runs(dst_v_scale, stage_vs, sb, dev_ids.data(), nullptr, cnt, 1, 1);
+          }
+        }
+        // the host-side id vectors are reused by the next chunk: the copies
+        // above read them at call time (pageable sources are staged by the
+        // runtime before hipMemcpyAsync returns)
+      }
+    } else {
+      e = memcpy_runs(dst_k, src_k, bb, pairs + 1, pairs, num_pairs, 2, 2);
+      if (e == hipSuccess) e = memcpy_runs(dst_v, src_v, bb, pairs + 1, pairs, num_pairs, 2, 2);
+      if (e == hipSuccess && scales) {
+        e = memcpy_runs(dst_k_scale, src_k_scale, sb, pairs + 1, pairs, num_pairs, 2, 2);
+        if (e == hipSuccess)
+          e = memcpy_runs(dst_v_scale, src_v_scale, sb, pairs + 1, pairs, num_pairs, 2, 2);
+      }
+    }
+    if (e != hipSuccess)
+      return fail(PKV_ERR_DEVICE, "%s: copy failed: %s", who, hipGetErrorString(e));
     return PKV_OK;
   })
 }

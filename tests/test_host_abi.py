@@ -81,6 +81,27 @@ def test_device_entry_points_reject_bad_arguments_without_a_gpu():
     assert st == PKV_ERR_INVALID
     assert lib.pkv_quantize_blocks(None, None, PKV_BF16, None, None, None, None, None, None, 0, 8,
                                    128, 16, 10, None) == 0
+    # swap_blocks validates its host pairs before any copy (dummy non-NULL pools)
+    import ctypes as C
+    import numpy as np
+    buf = C.c_void_p(1)
+    pairs = np.array([[0, 9]], np.int32)            # destination outside a 4-block pool
+    st = lib.pkv_swap_blocks(buf, buf, None, None, 4, buf, buf, None, None, 4,
+                             pairs.ctypes.data_as(C.POINTER(C.c_int32)), 1, 8, 128, 16,
+                             PKV_BF16, None, 0, None)
+    assert st == PKV_ERR_INVALID
+    pairs = np.array([[0, 1], [2, 1]], np.int32)    # one destination twice
+    st = lib.pkv_swap_blocks(buf, buf, None, None, 4, buf, buf, None, None, 4,
+                             pairs.ctypes.data_as(C.POINTER(C.c_int32)), 2, 8, 128, 16,
+                             PKV_BF16, None, 0, None)
+    assert st == PKV_ERR_INVALID and b"two pairs" in lib.pkv_last_error()
+    st = lib.pkv_swap_blocks(buf, buf, None, None, 4, buf, buf, None, None, 4,
+                             pairs.ctypes.data_as(C.POINTER(C.c_int32)), 1, 8, 128, 16, 3,
+                             None, 0, None)
+    assert st == PKV_ERR_INVALID                     # int8 without scales
+    # one round of 10 bf16 blocks: ids + 2 x 10 x 8*16*128*2 bytes + slack
+    n = lib.pkv_swap_workspace_bytes(10, 8, 128, 16, PKV_BF16)
+    assert n >= 10 * (4 + 2 * 8 * 16 * 128 * 2) + 256
 
 
 def test_workspace_size_formula():

@@ -78,3 +78,25 @@ def test_parent_output_unchanged_by_children_copy_on_write():
         K = A.gather(kc, tk[i], lk[i], bs)
         assert np.array_equal(K[:37], pk.astype(np.float64))
         assert np.array_equal(K[37], nk[i].astype(np.float64))
+
+
+def test_swap_blocks_round_trip_and_untouched_blocks():
+    rng = np.random.default_rng(5)
+    dev_k = rng.standard_normal((12, 2, 16, 4)).astype(np.float32)
+    dev_v = rng.standard_normal((12, 2, 16, 4)).astype(np.float32)
+    host_k = np.full((5, 2, 16, 4), np.nan, np.float32)
+    host_v = host_k.copy()
+    out = [(7, 0), (2, 1), (11, 4)]               # device block -> host block
+    hk, hv, _, _ = C.swap_blocks(host_k, host_v, dev_k, dev_v, out)
+    for s, d in out:
+        assert np.array_equal(hk[d], dev_k[s]) and np.array_equal(hv[d], dev_v[s])
+    assert np.isnan(hk[[2, 3]]).all()             # host blocks not named stay as they were
+    # swap back into other device blocks: the rows come back bit for bit
+    back = [(0, 3), (1, 9), (4, 5)]
+    nk = np.zeros_like(dev_k)
+    nv = np.zeros_like(dev_v)
+    k2, v2, _, _ = C.swap_blocks(nk, nv, hk, hv, back)
+    for (s_dev, h), (h2, d_new) in zip(out, back):
+        assert h == h2
+        assert np.array_equal(k2[d_new], dev_k[s_dev]) and np.array_equal(v2[d_new], dev_v[s_dev])
+    assert not k2[[0, 1, 2, 4, 6, 7, 8, 10, 11]].any()
