@@ -26,6 +26,26 @@ Readings where the pages are silent (each one also holds in the C++ manager):
     four beams sharing a partly filled tail the first three copy and the last
     writes in place;
   * sequence ids count up from 0 and are never reused.
+
+Prefix caching: when several requests start with the same tokens (a system
+prompt), their KV pages are reused instead of stored again
+([cnnetsun] §2.2, the share_prefix sketch keyed by a hash of the prefix;
+[aisoosoo] section "技术亮点": the scheduler hashes the prompt's tokens and
+equal prefixes reuse KV pages without recomputation).  Readings:
+  * the unit is a full block: block j of a sequence is found under the key
+    (physical block of its logical block j - 1, or none for j = 0; the
+    block_size token ids of block j), compared exactly (no false sharing);
+  * seq_create_cached walks the prompt's full blocks and shares the longest
+    run found from block 0 (each shared block's count + 1), then allocates
+    the rest (all-or-nothing); it reports how many leading positions already
+    hold their KV (block_size x shared blocks);
+  * seq_publish registers a sequence's full blocks once the caller has
+    written their KV; a key already present keeps its block (first writer
+    wins), and a block is registered at most once;
+  * an entry lives while its block is allocated: the cache holds no count of
+    its own, and a block whose count reaches 0 leaves the cache;
+  * lookup statistics count every full block of each cached create (looked
+    up) and the ones shared (hits).
 """
 from __future__ import annotations
 
@@ -61,6 +81,10 @@ class BlockManagerModel:
         self.tables: Dict[int, List[int]] = {}
         self.lens: Dict[int, int] = {}
         self.next_seq = 0
+        self.cache: Dict[Tuple[int, Tuple[int, ...]], int] = {}
+        self.cache_key: Dict[int, Tuple[int, Tuple[int, ...]]] = {}
+        self.lookups = 0
+        self.hits = 0
 
     # ---------------------------------------------------------------- blocks
     def alloc(self, k: int) -> List[int]:
@@ -88,6 +112,9 @@ class BlockManagerModel:
         self.rc[b] -= 1
         if self.rc[b] == 0:
             self.free.append(b)
+            key = self.cache_key.pop(b, None)
+            if key is not None:
+                del self.cache[key]
 
     def num_free(self) -> int:
         return len(self.free)
@@ -108,6 +135,54 @@ class BlockManagerModel:
         self.tables[sid] = blocks
         self.lens[sid] = num_tokens
         return sid
+
+    def seq_create_cached(self, tokens: Sequence[int]) -> Tuple[int, int]:
+        """New sequence over ``tokens``; returns (sequence id, positions whose
+        KV is already in shared blocks)."""
+        tokens = [int(t) for t in tokens]
+        bs = self.block_size
+        shared: List[int] = []
+        parent = -1
+        for j in range(len(tokens) // bs):
+            b = self.cache.get((parent, tuple(tokens[j * bs:(j + 1) * bs])))
+            if b is None:
+                break
+            shared.append(b)
+            parent = b
+        need = -(-len(tokens) // bs) - len(shared)
+        fresh = self.alloc(need)            # raises before any change
+        for b in shared:
+            self.rc[b] += 1
+        sid = self.next_seq
+        self.next_seq += 1
+        self.tables[sid] = shared + fresh
+        self.lens[sid] = len(tokens)
+        self.lookups += len(tokens) // bs
+        self.hits += len(shared)
+        return sid, len(shared) * bs
+
+    def seq_publish(self, sid: int, tokens: Sequence[int]) -> int:
+        """Register the full blocks covered by ``tokens`` (the sequence's
+        first len(tokens) positions); returns how many were newly
+        registered."""
+        table = self._seq(sid)
+        tokens = [int(t) for t in tokens]
+        if len(tokens) > self.lens[sid]:
+            raise Invalid("more tokens than the sequence holds")
+        bs = self.block_size
+        added = 0
+        for j in range(len(tokens) // bs):
+            key = (table[j - 1] if j else -1, tuple(tokens[j * bs:(j + 1) * bs]))
+            b = table[j]
+            if key in self.cache or b in self.cache_key:
+                continue
+            self.cache[key] = b
+            self.cache_key[b] = key
+            added += 1
+        return added
+
+    def prefix_stats(self) -> dict:
+        return {"cached_blocks": len(self.cache), "lookups": self.lookups, "hits": self.hits}
 
     def seq_fork(self, parent: int) -> int:
         table = self._seq(parent)

@@ -189,3 +189,82 @@ def test_free_returns_blocks_in_logical_order():
     bm.seq_free(a)
     assert bm.state()[0] == [0, 1, 2, 3, 4, 7, 6, 5]
     assert bm.alloc(2) == [5, 6]
+
+
+# ------------------------------------------------------------ prefix caching
+def test_prefix_cache_golden():
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "prefix_cache.json")))
+    m = BlockManagerModel(g["num_blocks"], g["block_size"])
+    ids = {}
+    for st in g["steps"]:
+        if st["op"] == "create_cached":
+            sid, cached = m.seq_create_cached(st["tokens"])
+            ids[st["name"]] = sid
+            assert m.tables[sid] == st["table"] and cached == st["cached"], st
+        elif st["op"] == "publish":
+            assert m.seq_publish(ids[st["name"]], st["tokens"]) == st["added"]
+        elif st["op"] == "free":
+            m.seq_free(ids[st["name"]])
+            assert m.free == st["free_after"], st
+        else:
+            ps = m.prefix_stats()
+            assert (ps["lookups"], ps["hits"], ps["cached_blocks"]) == (
+                st["lookups"], st["hits"], st["cached_blocks"])
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_prefix_cache_never_shares_different_prefixes(seed):
+    """Random creates from a few prompt families, publishes, forks, appends
+    and frees.  Whenever two live sequences hold the same physical block at
+    logical index j, they agree on every token up to the end of block j;
+    cache entries name live blocks only; counts recount by brute force."""
+    rng = np.random.default_rng(seed)
+    bs = 4
+    m = BlockManagerModel(64, bs, list(rng.permutation(64)))
+    toks = {}
+    families = [list(rng.integers(0, 5, 24)) for _ in range(3)]
+    for _ in range(200):
+        op = rng.integers(0, 5)
+        try:
+            if op <= 1 or not m.tables:
+                f = families[rng.integers(0, 3)]
+                n = int(rng.integers(1, 24))
+                tail = list(rng.integers(0, 5, int(rng.integers(0, 6))))
+                t = f[:n] + tail
+                sid, cached = m.seq_create_cached(t)
+                assert cached % bs == 0 and cached <= len(t)
+                toks[sid] = t
+            elif op == 2:
+                sid = int(rng.choice(list(m.tables)))
+                m.seq_publish(sid, toks[sid][:int(rng.integers(0, len(toks[sid]) + 1))])
+            elif op == 3:
+                sid = int(rng.choice(list(m.tables)))
+                new = [int(x) for x in rng.integers(0, 5, int(rng.integers(1, 4)))]
+                m.seq_append(sid, len(new))
+                toks[sid] = toks[sid] + new
+            else:
+                sid = int(rng.choice(list(m.tables)))
+                m.seq_free(sid)
+                del toks[sid]
+        except OutOfBlocks:
+            pass
+        # invariants
+        for b, key in m.cache_key.items():
+            assert m.rc[b] > 0 and m.cache[key] == b
+        count = [0] * 64
+        for t in m.tables.values():
+            for b in t:
+                count[b] += 1
+        assert count == m.rc
+        live = list(m.tables)
+        for i in live:
+            for k in live:
+                if i >= k:
+                    continue
+                ti, tk = m.tables[i], m.tables[k]
+                for j in range(min(len(ti), len(tk))):
+                    if ti[j] == tk[j]:
+                        end = min((j + 1) * bs, m.lens[i], m.lens[k])
+                        assert toks[i][:end] == toks[k][:end], (i, k, j)
