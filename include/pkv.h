@@ -152,6 +152,39 @@ pkv_status pkv_seq_export(const pkv_bm* bm, const int64_t* seqs, int32_t n, int3
                           int32_t* tables_out, int32_t* lens_out);
 
 /* ------------------------------------------------------------------------
+ * Prefix caching (host).  Requests that begin with the same tokens (a system
+ * prompt) share the KV pages of that prefix instead of storing it again:
+ * [cnnetsun] §2.2 (share_prefix: find the prefix by its hash, attach to its
+ * pages through reference counts) and [aisoosoo] section "技术亮点" (equal
+ * prompt prefixes reuse KV pages without recomputation).  The unit is a full
+ * block; block j is indexed under (physical block j-1, or -1 for j = 0; its
+ * block_size token ids), compared exactly.  An index entry lives as long as
+ * its block is allocated and holds no count of its own.
+ * ---------------------------------------------------------------------- */
+/* New sequence of num_tokens positions (tokens: host int32[num_tokens], the
+ * token ids).  Its leading full blocks found in the index are shared (each
+ * count + 1), walking from block 0 and stopping at the first miss; the rest
+ * are popped as in pkv_seq_create.  *cached_out (may be NULL) receives the
+ * number of leading positions whose K/V already sit in shared blocks
+ * (block_size x shared blocks): the caller computes and writes only
+ * positions [*cached_out, num_tokens).  All-or-nothing. */
+pkv_status pkv_seq_create_cached(pkv_bm* bm, const int32_t* tokens, int32_t num_tokens,
+                                 int64_t* seq_out, int32_t* cached_out);
+/* Index the full blocks among the first num_tokens positions of a sequence
+ * (tokens: host int32[num_tokens], its token ids), to be called once their
+ * K/V are written.  A key already indexed keeps its block and a block is
+ * indexed at most once.  *added_out (may be NULL) receives the number of new
+ * entries.  INVALID if num_tokens exceeds the sequence's length. */
+pkv_status pkv_seq_publish(pkv_bm* bm, int64_t seq, const int32_t* tokens, int32_t num_tokens,
+                           int32_t* added_out);
+/* Lookup figures for the share-ratio health metric of [cnnetsun] §4.2:
+ * *lookups = full prompt blocks looked up by pkv_seq_create_cached since
+ * creation, *hits = those found, *cached_blocks = entries now indexed.
+ * Any output may be NULL. */
+pkv_status pkv_bm_prefix_stats(const pkv_bm* bm, int64_t* lookups, int64_t* hits,
+                               int32_t* cached_blocks);
+
+/* ------------------------------------------------------------------------
  * reshape_and_cache (device).  Only the new tokens' K/V are computed each
  * step and appended to the cache ([nxbn] section 一); each token's row goes to
  * the slot the block table gives it ([nxbn] §2.2).

@@ -140,6 +140,29 @@ def pkv_seq_export(bm, seqs: Sequence[int], max_blocks: int) -> Tuple[np.ndarray
     return tables, lens
 
 
+def pkv_seq_create_cached(bm, tokens) -> Tuple[int, int]:
+    """Returns (sequence id, leading positions already cached)."""
+    t = np.ascontiguousarray(tokens, dtype=np.int32)
+    sid, cached = C.c_int64(), C.c_int32()
+    check(load().pkv_seq_create_cached(bm, _i32p(t), len(t), C.byref(sid), C.byref(cached)))
+    return sid.value, cached.value
+
+
+def pkv_seq_publish(bm, seq: int, tokens) -> int:
+    """Index the sequence's full blocks under ``tokens``; returns the number
+    of new entries."""
+    t = np.ascontiguousarray(tokens, dtype=np.int32)
+    added = C.c_int32()
+    check(load().pkv_seq_publish(bm, seq, _i32p(t), len(t), C.byref(added)))
+    return added.value
+
+
+def pkv_bm_prefix_stats(bm) -> dict:
+    lookups, hits, cached = C.c_int64(), C.c_int64(), C.c_int32()
+    check(load().pkv_bm_prefix_stats(bm, C.byref(lookups), C.byref(hits), C.byref(cached)))
+    return {"cached_blocks": cached.value, "lookups": lookups.value, "hits": hits.value}
+
+
 # --------------------------------------------------------------------------
 # device operations (torch tensors on the GPU)
 # --------------------------------------------------------------------------

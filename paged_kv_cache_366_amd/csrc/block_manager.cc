@@ -11,6 +11,18 @@
 // Every mutating call is all-or-nothing: it first works out how many blocks
 // it needs, fails with PKV_ERR_OUT_OF_BLOCKS before touching anything, and
 // only then changes state.
+//
+// Prefix caching (cnnetsun.cn §2.2, share_prefix looks a prompt prefix up by
+// a hash and attaches to its pages; aisoosoo.com section "技术亮点", equal
+// prompt prefixes reuse KV pages): each full block that a sequence publishes
+// is indexed under (physical block before it, or -1 for the first; its
+// block_size token ids).  Chaining through the previous physical block makes
+// one entry stand for the whole prefix up to it, so a lookup walks a prompt
+// block by block and stops at the first miss.  The index keys on a 64-bit
+// hash but every candidate's tokens are compared, so two prefixes never
+// share a block by collision.  An entry lives exactly as long as its block
+// is allocated: freeing the block (count 0) drops it, and the cache holds no
+// reference of its own.
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
@@ -29,6 +41,28 @@ struct Sequence {
   std::vector<int32_t> table;  // logical block j -> physical id
   int32_t len = 0;
 };
+
+// Index key of one published block.
+struct PrefixKey {
+  uint64_t hash = 0;
+  int32_t parent = -1;
+  std::vector<int32_t> tokens;
+};
+
+// splitmix64's finaliser (Steele, Lea and Flood, "Fast splittable
+// pseudorandom number generators", OOPSLA 2014) as the mixing step.
+uint64_t mix64(uint64_t x) {
+  x += 0x9e3779b97f4a7c15ull;
+  x = (x ^ (x >> 30)) * 0xbf58476d1ce4e5b9ull;
+  x = (x ^ (x >> 27)) * 0x94d049bb133111ebull;
+  return x ^ (x >> 31);
+}
+
+uint64_t prefix_hash(int32_t parent, const int32_t* tokens, int32_t n) {
+  uint64_t h = mix64(static_cast<uint64_t>(static_cast<int64_t>(parent) + 1));
+  for (int32_t i = 0; i < n; ++i) h = mix64(h ^ static_cast<uint32_t>(tokens[i]));
+  return h;
+}
 
 }  // namespace
 
@@ -55,6 +89,11 @@ struct pkv_bm {
   std::vector<int32_t> rc;
   std::unordered_map<int64_t, Sequence> seqs;
   int64_t next_seq = 0;
+  // prefix cache: hash -> block, and block -> its key
+  std::unordered_multimap<uint64_t, int32_t> prefix_index;
+  std::unordered_map<int32_t, PrefixKey> prefix_keys;
+  int64_t prefix_lookups = 0;
+  int64_t prefix_hits = 0;
 
   int32_t blocks_for(int64_t tokens) const {
     return static_cast<int32_t>((tokens + block_size - 1) / block_size);
@@ -67,7 +106,33 @@ struct pkv_bm {
     return b;
   }
   void release(int32_t b) {
-    if (--rc[b] == 0) free_list.push_back(b);
+    if (--rc[b] == 0) {
+      free_list.push_back(b);
+      if (!prefix_keys.empty()) unpublish(b);
+    }
+  }
+  void unpublish(int32_t b) {
+    auto k = prefix_keys.find(b);
+    if (k == prefix_keys.end()) return;
+    auto range = prefix_index.equal_range(k->second.hash);
+    for (auto it = range.first; it != range.second; ++it) {
+      if (it->second == b) {
+        prefix_index.erase(it);
+        break;
+      }
+    }
+    prefix_keys.erase(k);
+  }
+  // Block indexed under (parent, tokens[0..block_size)), or -1.
+  int32_t lookup(int32_t parent, const int32_t* tokens, uint64_t h) const {
+    auto range = prefix_index.equal_range(h);
+    for (auto it = range.first; it != range.second; ++it) {
+      const PrefixKey& k = prefix_keys.at(it->second);
+      if (k.parent == parent &&
+          std::equal(k.tokens.begin(), k.tokens.end(), tokens))
+        return it->second;
+    }
+    return -1;
   }
   Sequence* find(int64_t id) {
     auto it = seqs.find(id);
@@ -223,6 +288,82 @@ pkv_status pkv_seq_create(pkv_bm* bm, int32_t num_tokens, int64_t* seq_out) {
     *seq_out = id;
     return PKV_OK;
   })
+}
+
+pkv_status pkv_seq_create_cached(pkv_bm* bm, const int32_t* tokens, int32_t num_tokens,
+                                 int64_t* seq_out, int32_t* cached_out) {
+  PKV_GUARD({
+    if (!bm || !seq_out || (num_tokens > 0 && !tokens))
+      return pkv::fail(PKV_ERR_INVALID, "NULL argument");
+    if (num_tokens < 0) return pkv::fail(PKV_ERR_INVALID, "negative length %d", num_tokens);
+    const int32_t bs = bm->block_size;
+    const int32_t full = num_tokens / bs;
+    std::vector<int32_t> shared;
+    int32_t parent = -1;
+    for (int32_t j = 0; j < full && !bm->prefix_index.empty(); ++j) {
+      const int32_t* t = tokens + static_cast<int64_t>(j) * bs;
+      int32_t b = bm->lookup(parent, t, prefix_hash(parent, t, bs));
+      if (b < 0) break;
+      shared.push_back(b);
+      parent = b;
+    }
+    int32_t need = bm->blocks_for(num_tokens) - static_cast<int32_t>(shared.size());
+    if (static_cast<size_t>(need) > bm->free_list.size())
+      return pkv::fail(PKV_ERR_OUT_OF_BLOCKS, "need %d blocks, %zu free", need,
+                       bm->free_list.size());
+    for (int32_t b : shared) bm->rc[b] += 1;
+    Sequence s;
+    s.table = std::move(shared);
+    s.len = num_tokens;
+    const int32_t hit = static_cast<int32_t>(s.table.size());
+    for (int32_t i = 0; i < need; ++i) s.table.push_back(bm->pop());
+    int64_t id = bm->next_seq++;
+    bm->seqs.emplace(id, std::move(s));
+    bm->prefix_lookups += full;
+    bm->prefix_hits += hit;
+    *seq_out = id;
+    if (cached_out) *cached_out = hit * bs;
+    return PKV_OK;
+  })
+}
+
+pkv_status pkv_seq_publish(pkv_bm* bm, int64_t seq, const int32_t* tokens, int32_t num_tokens,
+                           int32_t* added_out) {
+  PKV_GUARD({
+    if (!bm || (num_tokens > 0 && !tokens)) return pkv::fail(PKV_ERR_INVALID, "NULL argument");
+    const Sequence* s = bm->find(seq);
+    if (!s) return pkv::fail(PKV_ERR_INVALID, "unknown sequence %lld", (long long)seq);
+    if (num_tokens < 0 || num_tokens > s->len)
+      return pkv::fail(PKV_ERR_INVALID, "%d tokens for a sequence of %d", num_tokens, s->len);
+    const int32_t bs = bm->block_size;
+    int32_t added = 0;
+    for (int32_t j = 0; j < num_tokens / bs; ++j) {
+      const int32_t b = s->table[j];
+      const int32_t parent = j ? s->table[j - 1] : -1;
+      const int32_t* t = tokens + static_cast<int64_t>(j) * bs;
+      if (bm->prefix_keys.count(b)) continue;
+      const uint64_t h = prefix_hash(parent, t, bs);
+      if (bm->lookup(parent, t, h) >= 0) continue;
+      PrefixKey k;
+      k.hash = h;
+      k.parent = parent;
+      k.tokens.assign(t, t + bs);
+      bm->prefix_keys.emplace(b, std::move(k));
+      bm->prefix_index.emplace(h, b);
+      ++added;
+    }
+    if (added_out) *added_out = added;
+    return PKV_OK;
+  })
+}
+
+pkv_status pkv_bm_prefix_stats(const pkv_bm* bm, int64_t* lookups, int64_t* hits,
+                               int32_t* cached_blocks) {
+  if (!bm) return pkv::fail(PKV_ERR_INVALID, "bm is NULL");
+  if (lookups) *lookups = bm->prefix_lookups;
+  if (hits) *hits = bm->prefix_hits;
+  if (cached_blocks) *cached_blocks = static_cast<int32_t>(bm->prefix_keys.size());
+  return PKV_OK;
 }
 
 pkv_status pkv_seq_fork(pkv_bm* bm, int64_t parent, int64_t* child_out) {

@@ -152,3 +152,116 @@ def test_bad_arguments_and_messages():
         assert pkv.pkv_seq_len(bm, a) == 5
     finally:
         pkv.pkv_bm_destroy(bm)
+
+
+# ------------------------------------------------------------ prefix caching
+pops = st.lists(st.tuples(st.sampled_from(["cached", "cached", "publish", "append", "fork",
+                                           "free", "create"]),
+                          st.integers(0, 1 << 30), st.integers(0, 30)),
+                min_size=1, max_size=60)
+
+
+@settings(max_examples=200, deadline=None)
+@given(pops, st.integers(4, 48), st.sampled_from([1, 2, 4, 16]), st.integers(0, 1 << 30))
+def test_prefix_cache_matches_model(seq, nblocks, bs, seed):
+    """Prompts drawn from a few families over a 3-token alphabet (so prefixes
+    collide often); the C++ index and the model agree on tables, cached
+    counts, publish counts, statistics and the whole pool state throughout."""
+    rng = np.random.default_rng(seed)
+    order = list(rng.permutation(nblocks).astype(np.int32))
+    families = [list(rng.integers(0, 3, 40)) for _ in range(3)]
+    p = Pair(nblocks, bs, order)
+    live, toks = [], {}
+    try:
+        for op, pick, n in seq:
+            if op == "cached" or (op == "create" and not live):
+                t = families[pick % 3][:n] + list(rng.integers(0, 3, pick % 4))
+                rc, rm = both(lambda: pkv.pkv_seq_create_cached(p.bm, t),
+                              lambda: p.model.seq_create_cached(t))
+                if rc is not None:
+                    assert rc == rm
+                    live.append(rc[0])
+                    toks[rc[0]] = t
+            elif op == "create":
+                rc, rm = both(lambda: pkv.pkv_seq_create(p.bm, n), lambda: p.model.seq_create(n))
+                if rc is not None:
+                    live.append(rc)
+                    toks[rc] = list(rng.integers(0, 3, n))
+            elif op == "publish" and live:
+                sid = live[pick % len(live)]
+                k = min(n + pick % 7, len(toks[sid]) + (pick % 11 == 0))   # sometimes too many
+                t = (toks[sid] + [0])[:k]
+                rc, rm = both(lambda: pkv.pkv_seq_publish(p.bm, sid, t),
+                              lambda: p.model.seq_publish(sid, t))
+                assert rc == rm
+            elif op == "append" and live:
+                sid = live[pick % len(live)]
+                m = 1 + n % 5
+                rc, rm = both(lambda: pkv.pkv_seq_append(p.bm, sid, m)[0],
+                              lambda: p.model.seq_append(sid, m)[0])
+                if rc is not None:
+                    assert list(rc) == list(rm)
+                    toks[sid] = toks[sid] + list(rng.integers(0, 3, m))
+            elif op == "fork" and live:
+                sid = live[pick % len(live)]
+                rc, rm = both(lambda: pkv.pkv_seq_fork(p.bm, sid), lambda: p.model.seq_fork(sid))
+                live.append(rc)
+                toks[rc] = list(toks[sid])
+            elif op == "free" and live:
+                sid = live.pop(pick % len(live))
+                both(lambda: pkv.pkv_seq_free(p.bm, sid), lambda: p.model.seq_free(sid))
+            p.same_state()
+            assert pkv.pkv_bm_prefix_stats(p.bm) == p.model.prefix_stats()
+    finally:
+        p.close()
+
+
+def test_prefix_cache_golden_through_the_abi():
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "prefix_cache.json")))
+    bm = pkv.pkv_bm_create(g["num_blocks"], g["block_size"])
+    ids = {}
+    try:
+        for st_ in g["steps"]:
+            if st_["op"] == "create_cached":
+                sid, cached = pkv.pkv_seq_create_cached(bm, st_["tokens"])
+                ids[st_["name"]] = sid
+                t, _ = pkv.pkv_seq_export(bm, [sid], len(st_["table"]))
+                assert list(t[0]) == st_["table"] and cached == st_["cached"], st_
+            elif st_["op"] == "publish":
+                assert pkv.pkv_seq_publish(bm, ids[st_["name"]], st_["tokens"]) == st_["added"]
+            elif st_["op"] == "free":
+                pkv.pkv_seq_free(bm, ids[st_["name"]])
+                free, _ = pkv.pkv_bm_get_state(bm, g["num_blocks"])
+                assert list(free) == st_["free_after"], st_
+            else:
+                ps = pkv.pkv_bm_prefix_stats(bm)
+                assert (ps["lookups"], ps["hits"], ps["cached_blocks"]) == (
+                    st_["lookups"], st_["hits"], st_["cached_blocks"])
+    finally:
+        pkv.pkv_bm_destroy(bm)
+
+
+def test_prefix_cache_collision_does_not_share():
+    # many distinct one-block prompts: every publish is a new entry and each
+    # prompt finds exactly its own block (tokens are compared, not hashes)
+    bm = pkv.pkv_bm_create(4096, 2)
+    try:
+        seen = {}
+        for a in range(60):
+            for b in range(60):
+                sid, cached = pkv.pkv_seq_create_cached(bm, [a, b])
+                assert cached == 0
+                assert pkv.pkv_seq_publish(bm, sid, [a, b]) == 1
+                seen[(a, b)] = sid
+        tables, _ = pkv.pkv_seq_export(bm, list(seen.values()), 1)
+        block_of = dict(zip(seen, tables[:, 0]))
+        for (a, b), blk in list(block_of.items())[::97]:
+            sid, cached = pkv.pkv_seq_create_cached(bm, [a, b, 7])
+            t, _ = pkv.pkv_seq_export(bm, [sid], 2)
+            assert cached == 2 and t[0, 0] == blk
+            pkv.pkv_seq_free(bm, sid)
+        assert pkv.pkv_bm_prefix_stats(bm)["cached_blocks"] == 3600
+    finally:
+        pkv.pkv_bm_destroy(bm)
