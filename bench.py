@@ -715,7 +715,141 @@ def bench_swap(a, torch, pkv):
     return result
 
 
-WORKLOADS = ("decode7b", "mixed", "beam", "gqa", "gqa-int8", "quantize", "swap")
+# ---------------------------------------------------------------------------
+# prefix caching: admission of requests that share a system prompt
+# ---------------------------------------------------------------------------
+def bench_prefix(a, torch, pkv, algo):
+    from synth import workloads as W
+    print("[bench] building the shared-system-prompt workload on the host", file=sys.stderr,
+          flush=True)
+    c = W.prefix_sharing(seed=6, draw_q=False, pool_factor=2.2)
+    dev = "cuda"
+    R, nb, hkv, D, hq = len(c.prompts), c.num_blocks, c.kv_heads, c.head_dim, c.q_heads
+    lens = np.array([len(p) for p in c.prompts], np.int32)
+    bm = pkv.pkv_bm_create(nb, BLOCK, c.perm)
+    kc = torch.full((nb, hkv, BLOCK, D), float("nan"), dtype=torch.bfloat16, device=dev)
+    vc = kc.clone()
+    kd = [to_dev_bf16(k, torch) for k in c.k]
+    vd = [to_dev_bf16(v, torch) for v in c.v]
+    g = torch.Generator(device=dev)
+    g.manual_seed(6)
+    qd = [torch.randn((int(n), hq, D), generator=g, device=dev).to(torch.bfloat16) for n in lens]
+
+    def i32d(x):
+        return torch.from_numpy(np.ascontiguousarray(x, np.int32)).to(dev)
+
+    # request 0 computes the system prompt and publishes it
+    sid0, _ = pkv.pkv_seq_create_cached(bm, c.prompts[0])
+    pkv.pkv_reshape_and_cache(kd[0], vd[0], kc, vc, i32d(pkv.pkv_seq_slots(bm, sid0, 0, int(lens[0]))))
+    pkv.pkv_seq_publish(bm, sid0, c.prompts[0])
+    rest = list(range(1, R))
+    # host cost of admission: create from tokens + slot lookup, then free
+    reps = 20
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        ids = []
+        for r in rest:
+            sid, cached = pkv.pkv_seq_create_cached(bm, c.prompts[r])
+            pkv.pkv_seq_slots(bm, sid, cached, int(lens[r]) - cached)
+            ids.append(sid)
+        for sid in ids:
+            pkv.pkv_seq_free(bm, sid)
+    admit_us = (time.perf_counter() - t0) * 1e6 / (reps * len(rest))
+    # the admitted batch, with the cache and (same requests, same pool) without
+    sids, cached = zip(*[pkv.pkv_seq_create_cached(bm, c.prompts[r]) for r in rest])
+    plain = [pkv.pkv_seq_create(bm, int(lens[r])) for r in rest]
+    stats = pkv.pkv_bm_prefix_stats(bm)
+    mb = W.blocks_for(int(lens.max()))
+
+    def batch(seq_ids, starts):
+        rows = [int(lens[r]) - st for r, st in zip(rest, starts)]
+        slots = np.concatenate([pkv.pkv_seq_slots(bm, sid, st, n)
+                                for sid, st, n in zip(seq_ids, starts, rows)])
+        tables, _ = pkv.pkv_seq_export(bm, list(seq_ids), mb)
+        qsl = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+        return {
+            "k": torch.cat([kd[r][st:] for r, st in zip(rest, starts)]),
+            "v": torch.cat([vd[r][st:] for r, st in zip(rest, starts)]),
+            "q": torch.cat([qd[r][st:] for r, st in zip(rest, starts)]),
+            "slots": i32d(slots), "tables": i32d(tables), "qsl": i32d(qsl),
+            "lens": i32d(lens[rest]), "rows": rows, "max_q": max(rows),
+            "tables_h": tables, "qsl_h": qsl,
+        }
+
+    hit = batch(sids, cached)
+    full = batch(plain, [0] * len(rest))
+    for b in (hit, full):
+        b["out"] = torch.empty(b["q"].shape, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    mc = int(lens.max())
+    torch.cuda.synchronize()
+
+    def run(b):
+        pkv.pkv_reshape_and_cache(b["k"], b["v"], kc, vc, b["slots"])
+        pkv.pkv_paged_attention_prefill(b["out"], b["q"], kc, vc, b["tables"], b["qsl"], b["lens"],
+                                        b["max_q"], mc, float(c.scale))
+
+    def step(ev):
+        if ev is not None:
+            ev[0].record(stream)
+        run(hit)
+        if ev is not None:
+            ev[1].record(stream)
+        run(full)
+        if ev is not None:
+            ev[2].record(stream)
+
+    ms_per_step, (hit_ms, full_ms) = run_timed(torch, step, a.steps, a.warmup, 2)
+    h_avg, f_avg = float(np.mean(hit_ms)), float(np.mean(full_ms))
+    prompt_tokens = int(lens[rest].sum())
+    # the cached rows give the same result as computing them
+    diff = 0.0
+    got_h, got_f = hit["out"].cpu().numpy(), full["out"].cpu().numpy()
+    for j, r in enumerate(rest):
+        a_, n_ = int(hit["qsl_h"][j]), hit["rows"][j]
+        b_ = int(full["qsl_h"][j]) + cached[j]
+        diff = max(diff, float(np.abs(got_h[a_:a_ + n_] - got_f[b_:b_ + n_]).max()))
+    from oracle import attention as A
+    rng = np.random.default_rng(0)
+    err = 0.0
+    for j in rng.choice(len(rest), 4, replace=False):
+        r, n = rest[j], int(lens[rest[j]])
+        K = gather_dev_all(kc, hit["tables_h"][j], n, torch)
+        V = gather_dev_all(vc, hit["tables_h"][j], n, torch)
+        for i in (0, hit["rows"][j] - 1):
+            P = cached[j] + i
+            h_ = int(rng.integers(0, hq))
+            qrow = qd[r][P, h_].float().cpu().numpy()
+            ref = A.attend(qrow, K[:P + 1, h_ // (hq // hkv)], V[:P + 1, h_ // (hq // hkv)],
+                           c.scale)
+            err = max(err, float(np.abs(got_h[int(hit["qsl_h"][j]) + i, h_] - ref).max()))
+    flops = sum(sum(range(int(n) - rows + 1, int(n) + 1)) * hq * D * 4
+                for n, rows in zip(lens[rest], hit["rows"]))
+    saved = sum(cached) * hkv * D * 2 * 2
+    pkv.pkv_bm_destroy(bm)
+    result = base_result(a, METRIC, prompt_tokens / (h_avg * 1e-3), "prompt tokens/s (effective)",
+                         ms_per_step, "bf16", {
+        "workload": "prefix caching at the 7B shape (32 heads x 128, bf16): 31 requests sharing "
+                    "a 1024-token system prompt already in the cache, 64-256 own tokens each; "
+                    "admission = reshape_and_cache + prefill of the uncached rows, against the "
+                    "same requests computed in full",
+        "requests": len(rest)})
+    result.update({
+        "kernel_ms": {"with_prefix_cache": h_avg, "without": f_avg},
+        "speedup": f_avg / h_avg,
+        "rows": {"computed": int(sum(hit["rows"])), "without_cache": int(sum(full["rows"]))},
+        "prefix_cache": {**stats, "cached_tokens": int(sum(cached)),
+                         "kv_bytes_not_stored": saved, "admit_us_per_request": admit_us},
+        "roofline": roofline("prefill_mfma_kernel + reshape_and_cache (cached step)", "mfma",
+                             flops / (h_avg * 1e-3) / 1e12, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s"),
+        "max_abs_diff_cached_vs_full": diff,
+        "max_abs_err_vs_oracle_sampled": err,
+        "cpu_baseline": None,
+    })
+    return result
+
+
+WORKLOADS = ("decode7b", "mixed", "beam", "gqa", "gqa-int8", "quantize", "swap", "prefix")
 
 
 def main(argv=None) -> int:
@@ -761,6 +895,8 @@ def main(argv=None) -> int:
         result = bench_quantize(a, torch, pkv)
     elif a.workload == "swap":
         result = bench_swap(a, torch, pkv)
+    elif a.workload == "prefix":
+        result = bench_prefix(a, torch, pkv, algo)
     else:
         result = bench_gqa(a, torch, pkv, algo, int8=(a.workload == "gqa-int8"))
     print(json.dumps(result), flush=True)

@@ -44,8 +44,9 @@ struct Sequence {
 
 // Index key of one published block.
 struct PrefixKey {
-  uint64_t hash = 0;
+  bool indexed = false;
   int32_t parent = -1;
+  uint64_t hash = 0;
   std::vector<int32_t> tokens;
 };
 
@@ -58,9 +59,14 @@ uint64_t mix64(uint64_t x) {
   return x ^ (x >> 31);
 }
 
+// Two token ids per mixing step.
 uint64_t prefix_hash(int32_t parent, const int32_t* tokens, int32_t n) {
   uint64_t h = mix64(static_cast<uint64_t>(static_cast<int64_t>(parent) + 1));
-  for (int32_t i = 0; i < n; ++i) h = mix64(h ^ static_cast<uint32_t>(tokens[i]));
+  int32_t i = 0;
+  for (; i + 1 < n; i += 2)
+    h = mix64(h ^ (static_cast<uint64_t>(static_cast<uint32_t>(tokens[i + 1])) << 32 |
+                   static_cast<uint32_t>(tokens[i])));
+  if (i < n) h = mix64(h ^ static_cast<uint32_t>(tokens[i]));
   return h;
 }
 
@@ -91,7 +97,8 @@ struct pkv_bm {
   int64_t next_seq = 0;
   // prefix cache: hash -> block, and block -> its key
   std::unordered_multimap<uint64_t, int32_t> prefix_index;
-  std::unordered_map<int32_t, PrefixKey> prefix_keys;
+  std::vector<PrefixKey> prefix_keys;  // per block; sized on the first publish
+  int32_t prefix_count = 0;
   int64_t prefix_lookups = 0;
   int64_t prefix_hits = 0;
 
@@ -108,26 +115,28 @@ struct pkv_bm {
   void release(int32_t b) {
     if (--rc[b] == 0) {
       free_list.push_back(b);
-      if (!prefix_keys.empty()) unpublish(b);
+      if (prefix_count) unpublish(b);
     }
   }
+  bool indexed(int32_t b) const { return prefix_count && prefix_keys[b].indexed; }
   void unpublish(int32_t b) {
-    auto k = prefix_keys.find(b);
-    if (k == prefix_keys.end()) return;
-    auto range = prefix_index.equal_range(k->second.hash);
+    PrefixKey& k = prefix_keys[b];
+    if (!k.indexed) return;
+    auto range = prefix_index.equal_range(k.hash);
     for (auto it = range.first; it != range.second; ++it) {
       if (it->second == b) {
         prefix_index.erase(it);
         break;
       }
     }
-    prefix_keys.erase(k);
+    k.indexed = false;
+    --prefix_count;
   }
   // Block indexed under (parent, tokens[0..block_size)), or -1.
   int32_t lookup(int32_t parent, const int32_t* tokens, uint64_t h) const {
     auto range = prefix_index.equal_range(h);
     for (auto it = range.first; it != range.second; ++it) {
-      const PrefixKey& k = prefix_keys.at(it->second);
+      const PrefixKey& k = prefix_keys[it->second];
       if (k.parent == parent &&
           std::equal(k.tokens.begin(), k.tokens.end(), tokens))
         return it->second;
@@ -341,15 +350,17 @@ pkv_status pkv_seq_publish(pkv_bm* bm, int64_t seq, const int32_t* tokens, int32
       const int32_t b = s->table[j];
       const int32_t parent = j ? s->table[j - 1] : -1;
       const int32_t* t = tokens + static_cast<int64_t>(j) * bs;
-      if (bm->prefix_keys.count(b)) continue;
+      if (bm->indexed(b)) continue;
       const uint64_t h = prefix_hash(parent, t, bs);
       if (bm->lookup(parent, t, h) >= 0) continue;
-      PrefixKey k;
+      if (bm->prefix_keys.empty()) bm->prefix_keys.resize(bm->num_blocks);
+      PrefixKey& k = bm->prefix_keys[b];
+      k.indexed = true;
       k.hash = h;
       k.parent = parent;
       k.tokens.assign(t, t + bs);
-      bm->prefix_keys.emplace(b, std::move(k));
       bm->prefix_index.emplace(h, b);
+      ++bm->prefix_count;
       ++added;
     }
     if (added_out) *added_out = added;
@@ -362,7 +373,7 @@ pkv_status pkv_bm_prefix_stats(const pkv_bm* bm, int64_t* lookups, int64_t* hits
   if (!bm) return pkv::fail(PKV_ERR_INVALID, "bm is NULL");
   if (lookups) *lookups = bm->prefix_lookups;
   if (hits) *hits = bm->prefix_hits;
-  if (cached_blocks) *cached_blocks = static_cast<int32_t>(bm->prefix_keys.size());
+  if (cached_blocks) *cached_blocks = bm->prefix_count;
   return PKV_OK;
 }
 

@@ -428,3 +428,70 @@ def distinct_slots(rng: np.random.Generator, num_slots: int, count: int,
     if skip_fraction > 0:
         slots[rng.random(count) < skip_fraction] = -1
     return slots
+
+
+# --------------------------------------------------------------------------
+# prefix sharing: requests that start with (part of) one system prompt
+# --------------------------------------------------------------------------
+@dataclass
+class PrefixCase:
+    """Request r holds tokens ``prompts[r]``: the first ``shared_lens[r]``
+    tokens of one system prompt, then tokens of its own.  K/V rows follow the
+    tokens: a position whose token prefix equals the system prompt's holds the
+    system prompt's row, every other position a fresh draw.  Own tokens of
+    request r come from the id range [vocab * (r + 1), vocab * (r + 2)), so
+    two requests' token sequences agree exactly on their common system-prompt
+    part and differ right after it."""
+    dtype: str
+    perm: np.ndarray
+    num_blocks: int
+    kv_heads: int
+    q_heads: int
+    head_dim: int
+    shared_lens: np.ndarray     # int32 [R]
+    prompts: List[np.ndarray]   # int32 token ids, per request
+    k: List[np.ndarray]         # per request [n_r, Hkv, D]
+    v: List[np.ndarray]
+    q: Optional[List[np.ndarray]]   # per request [n_r, Hq, D], or None
+    next_k: np.ndarray          # [R, Hkv, D] one decode token per request
+    next_v: np.ndarray
+    next_q: np.ndarray          # [R, Hq, D]
+    scale: np.float32
+
+
+def prefix_sharing(seed: int = 6, num_requests: int = 32, system_len: int = 1024,
+                   own_lens=(64, 256), shared_lens: Optional[Sequence[int]] = None,
+                   q_heads: int = 32, kv_heads: int = 32, head_dim: int = 128,
+                   dtype: str = "bf16", draw_q: bool = True, vocab: int = 32000,
+                   pool_factor: float = 1.25) -> PrefixCase:
+    """Draw order: own lengths, pool permutation, system tokens, system K then
+    V, then per request its own tokens, K, V (and queries of every position),
+    then the decode token's K, V and query of each request.  By default every
+    request shares the whole system prompt."""
+    rng = np.random.default_rng(seed)
+    own = draw_lengths(rng, num_requests, own_lens[0], own_lens[1])
+    sl = (np.full(num_requests, system_len, np.int32) if shared_lens is None
+          else np.asarray(shared_lens, np.int32))
+    assert len(sl) == num_requests and sl.max() <= system_len and own.min() >= 1
+    nb = max(1, int(np.ceil(pool_factor * sum(blocks_for(int(a + b) + 1)
+                                             for a, b in zip(sl, own)))))
+    perm = draw_permutation(rng, nb)
+    sys_tok = rng.integers(0, vocab, system_len).astype(np.int32)
+    sys_k = draw_normal(rng, (system_len, kv_heads, head_dim), dtype)
+    sys_v = draw_normal(rng, (system_len, kv_heads, head_dim), dtype)
+    prompts, ks, vs, qs = [], [], [], []
+    for r in range(num_requests):
+        m, n = int(sl[r]), int(own[r])
+        t = rng.integers(vocab * (r + 1), vocab * (r + 2), n).astype(np.int32)
+        k = draw_normal(rng, (n, kv_heads, head_dim), dtype)
+        v = draw_normal(rng, (n, kv_heads, head_dim), dtype)
+        prompts.append(np.concatenate([sys_tok[:m], t]))
+        ks.append(np.concatenate([sys_k[:m], k]))
+        vs.append(np.concatenate([sys_v[:m], v]))
+        if draw_q:
+            qs.append(draw_normal(rng, (m + n, q_heads, head_dim), dtype))
+    nk = draw_normal(rng, (num_requests, kv_heads, head_dim), dtype)
+    nv = draw_normal(rng, (num_requests, kv_heads, head_dim), dtype)
+    nq = draw_normal(rng, (num_requests, q_heads, head_dim), dtype)
+    return PrefixCase(dtype, perm, nb, kv_heads, q_heads, head_dim, sl, prompts, ks, vs,
+                      qs if draw_q else None, nk, nv, nq, np.float32(1.0 / np.sqrt(head_dim)))

@@ -46,3 +46,20 @@ def test_quantiser_extremes():
     assert q[0, 1] == -127 and np.abs(q).max() == 127
     q0, s0 = W.quantize_int8(np.zeros((3, 2), np.float32))
     assert s0 == 0 and not q0.any()
+
+
+def test_prefix_sharing_rows_follow_tokens():
+    c = W.prefix_sharing(seed=3, num_requests=5, system_len=40, own_lens=(1, 20),
+                         shared_lens=[40, 40, 17, 0, 33], q_heads=4, kv_heads=2, head_dim=16)
+    for r in range(5):
+        for s in range(5):
+            a, b = c.prompts[r], c.prompts[s]
+            m = min(len(a), len(b))
+            same = int(np.argmin(a[:m] == b[:m])) if not np.array_equal(a[:m], b[:m]) else m
+            # rows agree exactly where the token prefixes agree, and only there
+            assert np.array_equal(c.k[r][:same], c.k[s][:same])
+            assert np.array_equal(c.v[r][:same], c.v[s][:same])
+            if r != s and same < m:
+                assert not np.array_equal(c.k[r][same], c.k[s][same])
+            if r != s:
+                assert same == min(c.shared_lens[r], c.shared_lens[s])
