@@ -282,3 +282,15 @@ class BlockManagerModel:
         return {"num_blocks": self.num_blocks, "free": len(self.free), "used": used,
                 "shared": shared, "logical_blocks": logical, "waste_slots": waste,
                 "num_seqs": len(self.tables)}
+
+
+def adaptive_page_size(avg_seq_len: float) -> int:
+    """Block size for a workload whose sequences average ``avg_seq_len``
+    tokens: the rule [cnnetsun] §4.3 prints as an example (16 below 512
+    tokens, 32 below 2048, 64 otherwise).  Reading for inputs the rule does
+    not consider: NaN and negative averages get the smallest size."""
+    if not avg_seq_len >= 512:
+        return 16
+    if avg_seq_len < 2048:
+        return 32
+    return 64

@@ -268,3 +268,23 @@ def test_prefix_cache_never_shares_different_prefixes(seed):
                     if ti[j] == tk[j]:
                         end = min((j + 1) * bs, m.lens[i], m.lens[k])
                         assert toks[i][:end] == toks[k][:end], (i, k, j)
+
+
+# ------------------------------------------------------------ adaptive block size
+def test_adaptive_page_size_golden():
+    import json
+    import os
+    from oracle.allocator import adaptive_page_size
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "adaptive_block_size.json")))
+    for avg, want in g["cases"]:
+        assert adaptive_page_size(avg) == want, avg
+
+
+def test_adaptive_page_size_is_monotone_and_in_the_pages_range():
+    from oracle.allocator import adaptive_page_size
+    xs = np.sort(np.random.default_rng(0).uniform(0, 1e5, 2000))
+    sizes = [adaptive_page_size(x) for x in xs]
+    assert all(a <= b for a, b in zip(sizes, sizes[1:]))
+    assert set(sizes) == {16, 32, 64}
+    assert adaptive_page_size(float("nan")) == 16 and adaptive_page_size(-5) == 16
