@@ -68,31 +68,32 @@ class Workload:
     """7B-shape decode batch, built through the library's block manager."""
 
     def __init__(self, seed: int = 1, num_seqs: int = 64, heads: int = 32, head_dim: int = 128,
-                 len_range=(128, 2048)):
+                 len_range=(128, 2048), block_size: int = BLOCK):
         import paged_kv_cache_366_amd as pkv
         from synth import workloads as W
 
         rng = np.random.default_rng(seed)
-        self.S, self.H, self.D = num_seqs, heads, head_dim
+        self.S, self.H, self.D, self.bs = num_seqs, heads, head_dim, block_size
+        bs = block_size
         lens = W.draw_lengths(rng, num_seqs, *len_range)
-        nb = W.pool_size(lens)
+        nb = W.pool_size(lens, 1.25, bs)
         perm = W.draw_permutation(rng, nb)
         t0 = time.perf_counter()
-        bm = pkv.pkv_bm_create(nb, BLOCK, perm)
+        bm = pkv.pkv_bm_create(nb, bs, perm)
         seqs = [pkv.pkv_seq_create(bm, int(n) - 1) for n in lens]
         t1 = time.perf_counter()
         slots, cow = pkv.pkv_seq_append_batch(bm, seqs)
-        self.max_blocks = int(max(W.blocks_for(n) for n in lens))
+        self.max_blocks = int(max(W.blocks_for(n, bs) for n in lens))
         tables, lens_bm = pkv.pkv_seq_export(bm, seqs, self.max_blocks)
         t2 = time.perf_counter()
         assert len(cow) == 0 and np.array_equal(lens_bm, lens)
         self.host_bm = {"create_us": (t1 - t0) * 1e6, "append_export_us": (t2 - t1) * 1e6}
         self.bm, self.seqs = bm, seqs
         q = W.draw_normal(rng, (num_seqs, heads, head_dim), "bf16")
-        kc, vc, _, _ = W.draw_paged_kv(rng, tables, lens, nb, heads, head_dim, "bf16")
+        kc, vc, _, _ = W.draw_paged_kv(rng, tables, lens, nb, heads, head_dim, "bf16", bs)
         self.lens, self.tables, self.slots, self.q = lens, tables, slots, q
         self.kc_full, self.vc_full = kc, vc          # with the current token (oracle side)
-        blk, row = slots // BLOCK, slots % BLOCK
+        blk, row = slots // bs, slots % bs
         self.new_k = kc[blk, :, row, :].copy()       # [S, H, D]
         self.new_v = vc[blk, :, row, :].copy()
         self.num_blocks = nb
@@ -103,7 +104,7 @@ class Workload:
         return int(self.lens.astype(np.int64).sum()) * self.H * self.D * 2 * 2
 
     def main_kernel_bytes(self) -> int:
-        tbl = int(sum(W_blocks(n) for n in self.lens)) * 4
+        tbl = int(sum(W_blocks(n, self.bs) for n in self.lens)) * 4
         return self.kv_bytes() + self.S * self.H * self.D * 2 + tbl + self.S * 4
 
     def step_bytes(self) -> int:
@@ -112,8 +113,8 @@ class Workload:
         return self.main_kernel_bytes() + out + rc
 
 
-def W_blocks(n) -> int:
-    return -(-int(n) // BLOCK)
+def W_blocks(n, block_size: int = BLOCK) -> int:
+    return -(-int(n) // block_size)
 
 
 def to_dev_bf16(x, torch):
@@ -130,7 +131,8 @@ def cpu_baseline(wl: Workload, min_seconds: float = 10.0, max_reps: int = 8):
     out = None
     while reps < max_reps and (wall < min_seconds or reps == 0):
         c0, t0 = time.process_time(), time.perf_counter()
-        out = A.decode(wl.q, wl.kc_full, wl.vc_full, wl.tables, wl.lens, wl.scale)
+        out = A.decode(wl.q, wl.kc_full, wl.vc_full, wl.tables, wl.lens, wl.scale,
+                       block_size=wl.bs)
         wall += time.perf_counter() - t0
         cpu += time.process_time() - c0
         reps += 1
@@ -208,12 +210,12 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16/f16 matrix peak, published
 # ---------------------------------------------------------------------------
 def bench_decode7b(a, torch, pkv, algo):
     print("[bench] building the 7B-shape decode workload on the host", file=sys.stderr, flush=True)
-    wl = Workload(seed=a.seed)
+    wl = Workload(seed=a.seed, block_size=a.block_size)
     dev = "cuda"
     kc = to_dev_bf16(wl.kc_full, torch)
     vc = to_dev_bf16(wl.vc_full, torch)
-    blk = torch.from_numpy((wl.slots // BLOCK).astype(np.int64)).to(dev)
-    row = torch.from_numpy((wl.slots % BLOCK).astype(np.int64)).to(dev)
+    blk = torch.from_numpy((wl.slots // wl.bs).astype(np.int64)).to(dev)
+    row = torch.from_numpy((wl.slots % wl.bs).astype(np.int64)).to(dev)
     kc[blk, :, row, :] = float("nan")     # the step's cache write must fill these
     vc[blk, :, row, :] = float("nan")
     q = to_dev_bf16(wl.q, torch)
@@ -254,14 +256,15 @@ def bench_decode7b(a, torch, pkv, algo):
     main_bytes = wl.main_kernel_bytes()
     achieved = main_bytes / (main_avg * 1e-3) / 1e9
     traffic = None
-    if TRAFFIC["sources_sha1"] == kernel_sources_sha1() and TRAFFIC["bytes_per_launch"]:
+    if (TRAFFIC["sources_sha1"] == kernel_sources_sha1() and TRAFFIC["bytes_per_launch"]
+            and wl.bs == BLOCK):
         traffic = TRAFFIC["bytes_per_launch"]
     result = base_result(a, METRIC, step_bytes / (ms_per_step * 1e-3) / 1e9, "GB/s", ms_per_step,
                          "bf16", {
         "workload": "7B-shape paged decode, bf16 KV and q, fp32 accumulate: 64 sequences, "
-                    "32 heads MHA, head_dim 128, block_size 16, contexts U[128, 2048], "
+                    f"32 heads MHA, head_dim 128, block_size {wl.bs}, contexts U[128, 2048], "
                     "pool 1.25x, random placement; step = reshape_and_cache + decode + reduce",
-        "num_seqs": wl.S, "heads": wl.H, "head_dim": wl.D, "block_size": BLOCK,
+        "num_seqs": wl.S, "heads": wl.H, "head_dim": wl.D, "block_size": wl.bs,
         "context_tokens": int(wl.lens.sum()), "num_blocks": wl.num_blocks,
         "partition_tokens": a.partition, "algo": a.algo, "seed": a.seed})
     result.update({
@@ -274,6 +277,8 @@ def bench_decode7b(a, torch, pkv, algo):
         "roofline": roofline("decode_wave_kernel (split-K main)", "hbm", achieved, HBM_PEAK_GBS,
                              "GB/s", traffic),
         "host_block_manager_us": wl.host_bm,
+        "block_manager": {k: v for k, v in pkv.pkv_bm_stats_get(wl.bm).items()
+                          if k in ("num_blocks", "used_blocks", "logical_blocks", "waste_slots")},
         "cpu_baseline": None,
     })
     if not a.no_cpu_baseline:
@@ -863,6 +868,8 @@ def main(argv=None) -> int:
                     help="split-K partition size in tokens (0 = no split); default 256, or 512 "
                          "for the long-context GQA workloads")
     ap.add_argument("--algo", choices=("auto", "wave", "mfma"), default="auto")
+    ap.add_argument("--block-size", type=int, default=BLOCK, choices=(16, 32, 64, 128),
+                    help="KV block size of the decode7b workload (16 is the headline line)")
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,

@@ -151,6 +151,12 @@ pkv_status pkv_seq_free(pkv_bm* bm, int64_t seq);
 pkv_status pkv_seq_export(const pkv_bm* bm, const int64_t* seqs, int32_t n, int32_t max_blocks,
                           int32_t* tables_out, int32_t* lens_out);
 
+/* Block size for a workload whose sequences average avg_context_len tokens:
+ * 16 below 512, 32 below 2048, 64 otherwise (the adaptive_page_size rule of
+ * [cnnetsun] §4.3: small pages keep utilisation high for short sequences,
+ * larger ones cut table entries for long ones).  NaN or negative: 16. */
+int32_t pkv_adaptive_block_size(double avg_context_len);
+
 /* ------------------------------------------------------------------------
  * Prefix caching (host).  Requests that begin with the same tokens (a system
  * prompt) share the KV pages of that prefix instead of storing it again:
@@ -301,7 +307,7 @@ pkv_status pkv_quantize_blocks(const void* src_k, const void* src_v, pkv_dtype s
  *   scale          multiplies q.k before the softmax (1/sqrt(head_dim) in
  *                  the usual case)
  *   partition_tokens  0: one workgroup covers a whole context; otherwise a
- *                  multiple of block_size: contexts are split into partitions
+ *                  multiple of 16: contexts are split into partitions
  *                  of that many tokens, each producing a partial result
  *                  (max, sum, unnormalised output) that a reduce kernel
  *                  merges.  Results are deterministic for a fixed value.
@@ -310,7 +316,9 @@ pkv_status pkv_quantize_blocks(const void* src_k, const void* src_v, pkv_dtype s
  *   workspace      device scratch of at least
  *                  pkv_decode_workspace_bytes(...) bytes (may be NULL when
  *                  that is 0), 256-byte aligned.
- * Supported: head_dim 64 or 128, block_size 16, num_q_heads a multiple of
+ * Supported: head_dim 64 or 128; block_size 16, 32, 64 or 128 (the kernels
+ * walk a block as 16-row tiles; [cnnetsun] §4.3 gives 16-32 for many short
+ * conversations and 64-128 for long documents); num_q_heads a multiple of
  * num_kv_heads with a group of at most 16.  Others: UNSUPPORTED. */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_context_len, int32_t partition_tokens);
@@ -358,7 +366,7 @@ pkv_status pkv_paged_attention_reduce(void* out, pkv_dtype out_dtype, const int3
  *   max_query_len  the largest chunk (sizes the launch)
  * q_dtype F16/BF16 with kv_dtype equal to it (MFMA path), or F32 throughout
  * (wavefront path, one query row at a time).  Supported head_dim 64/128,
- * block_size 16, group (num_q_heads / num_kv_heads) of any size. */
+ * block_size 16/32/64/128, group (num_q_heads / num_kv_heads) of any size. */
 pkv_status pkv_paged_attention_prefill(
     void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype, const void* k_cache,
     const void* v_cache, pkv_dtype kv_dtype, const float* k_scale, const float* v_scale,

@@ -140,6 +140,10 @@ def pkv_seq_export(bm, seqs: Sequence[int], max_blocks: int) -> Tuple[np.ndarray
     return tables, lens
 
 
+def pkv_adaptive_block_size(avg_context_len: float) -> int:
+    return load().pkv_adaptive_block_size(float(avg_context_len))
+
+
 def pkv_seq_create_cached(bm, tokens) -> Tuple[int, int]:
     """Returns (sequence id, leading positions already cached)."""
     t = np.ascontiguousarray(tokens, dtype=np.int32)

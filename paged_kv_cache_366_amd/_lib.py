@@ -49,6 +49,7 @@ SIGNATURES = {
     "pkv_seq_create_cached": (_i32, [_vp, _pi32, _i32, _pi64, _pi32]),
     "pkv_seq_publish": (_i32, [_vp, _i64, _pi32, _i32, _pi32]),
     "pkv_bm_prefix_stats": (_i32, [_vp, _pi64, _pi64, _pi32]),
+    "pkv_adaptive_block_size": (_i32, [C.c_double]),
     "pkv_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i32, _i32, _i32,
                                      _i32, _i32, _vp]),
     "pkv_copy_blocks": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),

@@ -47,6 +47,19 @@ int out_kind_of(pkv_dtype out_dt) {
   return out_dt == PKV_F32 ? kOutF32 : out_dt == PKV_BF16 ? kOutBF16 : kOutF16;
 }
 
+// Block sizes the kernels walk as 1, 2, 4 or 8 tiles of 16 rows ([cnnetsun]
+// §2.1 and §4.3 name page sizes from 16 to 128): log2(block_size / 16), or
+// -1 for any other size.
+int block_shift(int32_t bs) {
+  switch (bs) {
+    case 16: return 0;
+    case 32: return 1;
+    case 64: return 2;
+    case 128: return 3;
+    default: return -1;
+  }
+}
+
 // Shared checks of decode and prefill arguments.
 pkv_status check_common(const char* who, void* out, pkv_dtype out_dt, const void* q,
                         pkv_dtype q_dt, const void* kc, const void* vc, pkv_dtype kv_dt,
@@ -60,7 +73,8 @@ pkv_status check_common(const char* who, void* out, pkv_dtype out_dt, const void
     return fail(PKV_ERR_INVALID, "%s: num_q_heads %d is not a multiple of num_kv_heads %d", who,
                 hq, hkv);
   if (D != 64 && D != 128) return fail(PKV_ERR_UNSUPPORTED, "%s: head_dim %d (64 or 128)", who, D);
-  if (bs != 16) return fail(PKV_ERR_UNSUPPORTED, "%s: block_size %d (16 only)", who, bs);
+  if (block_shift(bs) < 0)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: block_size %d (16, 32, 64 or 128)", who, bs);
   if (static_cast<int64_t>(max_ctx) > static_cast<int64_t>(mb) * bs)
     return fail(PKV_ERR_INVALID, "%s: max_context_len %d exceeds max_blocks_per_seq * block_size",
                 who, max_ctx);
@@ -85,7 +99,7 @@ pkv_status check_common(const char* who, void* out, pkv_dtype out_dt, const void
 // reads names a block of the pool.
 pkv_status deep_check_tables(const char* who, const int32_t* tables, int32_t mb,
                              const int32_t* lens, int32_t max_ctx, int32_t S, int32_t nb,
-                             void* stream, std::vector<int32_t>* lens_out = nullptr) {
+                             int32_t bs, void* stream, std::vector<int32_t>* lens_out = nullptr) {
   std::vector<int32_t> L, T;
   pkv_status st = fetch_i32(lens, S, stream, L);
   if (st) return st;
@@ -95,7 +109,7 @@ pkv_status deep_check_tables(const char* who, const int32_t* tables, int32_t mb,
     if (L[s] < 0 || L[s] > max_ctx)
       return fail(PKV_ERR_INVALID, "%s: context_lens[%d] = %d outside [0, %d]", who, s, L[s],
                   max_ctx);
-    for (int32_t j = 0; j < (L[s] + 15) / 16; ++j) {
+    for (int32_t j = 0; j < (L[s] + bs - 1) / bs; ++j) {
       int32_t b = T[static_cast<size_t>(s) * mb + j];
       if (b < 0 || b >= nb)
         return fail(PKV_ERR_INVALID, "%s: block_tables[%d][%d] = %d outside the pool", who, s, j,
@@ -141,7 +155,7 @@ pkv_status decode_impl(DecodePart which, void* out, pkv_dtype out_dt, const void
     return fail(PKV_ERR_INVALID, "%s: workspace needs %zu bytes, 256-byte aligned (got %zu)", who,
                 w.total, ws_bytes);
   if (deep_validation() && which != DecodePart::kReduce) {
-    st = deep_check_tables(who, tables, mb, lens, max_ctx, S, nb, stream);
+    st = deep_check_tables(who, tables, mb, lens, max_ctx, S, nb, bs, stream);
     if (st) return st;
   }
   AttnArgs a{};
@@ -157,6 +171,7 @@ pkv_status decode_impl(DecodePart which, void* out, pkv_dtype out_dt, const void
   a.lens = lens;
   a.qsl = nullptr;
   a.max_blocks = mb;
+  a.bs_shift = block_shift(bs);
   a.max_ctx = max_ctx;
   a.num_seqs = S;
   a.num_rows = S;
@@ -288,7 +303,7 @@ pkv_status pkv_paged_attention_prefill(
     if (deep_validation()) {
       std::vector<int32_t> L, Q;
       st = deep_check_tables(who, block_tables, max_blocks_per_seq, context_lens,
-                             max_context_len, num_seqs, num_blocks, stream, &L);
+                             max_context_len, num_seqs, num_blocks, block_size, stream, &L);
       if (st) return st;
       st = fetch_i32(query_start_loc, num_seqs + 1, stream, Q);
       if (st) return st;
@@ -311,6 +326,7 @@ pkv_status pkv_paged_attention_prefill(
     a.lens = context_lens;
     a.qsl = query_start_loc;
     a.max_blocks = max_blocks_per_seq;
+    a.bs_shift = block_shift(block_size);
     a.max_ctx = max_context_len;
     a.num_seqs = num_seqs;
     a.num_rows = num_query_tokens;

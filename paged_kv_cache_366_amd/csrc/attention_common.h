@@ -13,7 +13,7 @@ struct AttnArgs {
   float* part_o;             // [rows][Hq][num_parts][D] partial outputs (NULL: no split)
   float* part_ml;            // [rows][Hq][num_parts][2] partial (max, sum), log2 domain
   const void* q;             // [rows][Hq][D]
-  const void* kc;            // [NB][Hkv][16][D]
+  const void* kc;            // [NB][Hkv][16 << bs_shift][D]
   const void* vc;
   const float* ks;           // [NB][Hkv] int8 scales (NULL otherwise)
   const float* vs;
@@ -21,6 +21,7 @@ struct AttnArgs {
   const int32_t* lens;       // [S]
   const int32_t* qsl;        // [S+1] query_start_loc; NULL means one query row per sequence
   int max_blocks;            // MB
+  int bs_shift;              // block_size = 16 << bs_shift rows
   int max_ctx;
   int num_seqs;              // S
   int num_rows;              // S (decode) or Tq (prefill)
@@ -55,8 +56,18 @@ __device__ __forceinline__ int row_ctx(const AttnArgs& a, int row, int seq) {
     const int qlen = a.qsl[seq + 1] - a.qsl[seq];
     ctx = ctx - qlen + (row - a.qsl[seq]) + 1;
   }
-  const int cap = min(a.max_ctx, a.max_blocks * 16);
+  const int cap = min(a.max_ctx, a.max_blocks << (4 + a.bs_shift));
   return max(0, min(ctx, cap));
+}
+
+// The kernels walk a context in tiles of 16 rows.  A block of
+// 16 << bs_shift rows holds 1 << bs_shift of them: tile t of a sequence is in
+// table entry t >> bs_shift, and the (block, KV head) slab of rows is
+// contiguous, so the tile's index in units of 16 rows x head_dim is the one
+// returned here.
+__device__ __forceinline__ int64_t tile_index(const AttnArgs& a, int entry, int kvh, int t) {
+  return ((static_cast<int64_t>(entry) * a.hkv + kvh) << a.bs_shift) +
+         (t & ((1 << a.bs_shift) - 1));
 }
 
 __device__ __forceinline__ void row_context(const AttnArgs& a, int row, int& seq, int& ctx) {
@@ -88,19 +99,20 @@ __device__ __forceinline__ WgCoord wg_coord(int ngroups, int num_parts) {
 }
 
 // Block-table entries of one wavefront's share of a partition.  Wave w of
-// the workgroup takes the partition's blocks w, w + 4, w + 8, ...; its k-th
-// block is entry `b0 + w + 4k` of the table row.  Lane i holds the entry
-// for k = k0 + i, so one vector load covers 64 of the wave's blocks and
-// each step reads its block id with a lane read, off the load path.
-// Entries at or past `bmax` (the end of the partition or of the table row)
-// are not read.
+// the workgroup takes the partition's 16-row tiles w, w + 4, w + 8, ...; its
+// k-th tile is tile `b0 + w + 4k` of the sequence, in table entry
+// (b0 + w + 4k) >> bs_shift.  Lane i holds the entry for k = k0 + i, so one
+// vector load covers 64 of the wave's tiles and each step reads its block id
+// with a lane read, off the load path.  Tiles at or past `bmax` (the end of
+// the partition or of the table row) read no entry.
 struct TableChunk {
   int entry = -1;
-  __device__ __forceinline__ void fetch(const int32_t* trow, int b0, int wave, int k0, int bmax) {
+  __device__ __forceinline__ void fetch(const int32_t* trow, int b0, int wave, int k0, int bmax,
+                                        int bs_shift) {
     const int bi = wave + kDecodeWaves * (k0 + static_cast<int>(threadIdx.x & 63));
-    entry = bi < bmax ? trow[b0 + bi] : -1;
+    entry = bi < bmax ? trow[(b0 + bi) >> bs_shift] : -1;
   }
-  // Entry of the wave's block k (k0 <= k < k0 + 64); k is wave-uniform.
+  // Entry of the wave's tile k (k0 <= k < k0 + 64); k is wave-uniform.
   __device__ __forceinline__ int get(int k) const { return __builtin_amdgcn_readlane(entry, k & 63); }
 };
 

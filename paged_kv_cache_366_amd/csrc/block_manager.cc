@@ -299,6 +299,11 @@ pkv_status pkv_seq_create(pkv_bm* bm, int32_t num_tokens, int64_t* seq_out) {
   })
 }
 
+int32_t pkv_adaptive_block_size(double avg_context_len) {
+  if (!(avg_context_len >= 512.0)) return 16;  // NaN and negatives too
+  return avg_context_len < 2048.0 ? 32 : 64;
+}
+
 pkv_status pkv_seq_create_cached(pkv_bm* bm, const int32_t* tokens, int32_t num_tokens,
                                  int64_t* seq_out, int32_t* cached_out) {
   PKV_GUARD({

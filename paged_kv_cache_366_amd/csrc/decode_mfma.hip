@@ -69,10 +69,10 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttnArgs a, int group)
   // Table entries, q and the context length go out together.
   const int seq = row_seq(a, row);
   const int b0 = (part * a.part_tokens) >> 4;
-  const int bmax = min(a.part_tokens >> 4, a.max_blocks - b0);
+  const int bmax = min(a.part_tokens >> 4, (a.max_blocks << a.bs_shift) - b0);
   const int32_t* trow = a.tables + static_cast<int64_t>(seq) * a.max_blocks;
   TableChunk tc;
-  tc.fetch(trow, b0, wave, 0, bmax);
+  tc.fetch(trow, b0, wave, 0, bmax, a.bs_shift);
 
   // Q^T operand: head r16, elements 32kk + 8kg .. +7.
   u32x4 qop[NK];
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttnArgs a, int group)
   const int voff = (4 * kg) * ROW + r16 * VB;               // + e * ROW
 
   for (int k = 0; k < nbw; k += kUnroll) {
-    if (k > 0 && (k & 63) == 0) tc.fetch(trow, b0, wave, k, bmax);
+    if (k > 0 && (k & 63) == 0) tc.fetch(trow, b0, wave, k, bmax, a.bs_shift);
     u32x4 kr[kUnroll][NK], vr[kUnroll][4];
     int phys[kUnroll];
 #pragma unroll
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttnArgs a, int group)
       }
       phys[u] = p;
       if (p >= 0) {
-        const int64_t toff = (static_cast<int64_t>(p) * a.hkv + kvh) * TILE;
+        const int64_t toff = tile_index(a, p, kvh, b0 + wave + kWaves * (k + u)) * TILE;
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk)
           kr[u][kk] = load_bytes<KB>(kc + toff + koff + kk * 32 * KT::bytes);

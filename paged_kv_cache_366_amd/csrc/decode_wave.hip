@@ -117,10 +117,10 @@ __global__ __launch_bounds__(256) void decode_wave_kernel(AttnArgs a) {
   // other: their loads go out together.
   const int seq = row_seq(a, row);
   const int b0 = (part * a.part_tokens) >> 4;
-  const int bmax = min(a.part_tokens >> 4, a.max_blocks - b0);
+  const int bmax = min(a.part_tokens >> 4, (a.max_blocks << a.bs_shift) - b0);
   const int32_t* trow = a.tables + static_cast<int64_t>(seq) * a.max_blocks;
   TableChunk tc;
-  tc.fetch(trow, b0, wave, 0, bmax);
+  tc.fetch(trow, b0, wave, 0, bmax, a.bs_shift);
 
   // q slice of every head of the group: elements [c*E, c*E + E), as
   // floats, or as the raw 16-byte chunk when keys and q share a 16-bit type.
@@ -238,10 +238,10 @@ __global__ __launch_bounds__(256) void decode_wave_kernel(AttnArgs a) {
   // Loads of one block's K and V tiles; false for a table entry outside the
   // pool, which is skipped as if masked.
   auto load_block = [&](int k, u32x4 (&kr)[NL], u32x4 (&vr)[NL], float& ksc, float& vsc) {
-    if (k > 0 && (k & 63) == 0) tc.fetch(trow, b0, wave, k, bmax);
+    if (k > 0 && (k & 63) == 0) tc.fetch(trow, b0, wave, k, bmax, a.bs_shift);
     const int p = tc.get(k);
     if (p < 0 || p >= a.num_blocks) return false;
-    const int64_t toff = (static_cast<int64_t>(p) * a.hkv + kvh) * TILE;
+    const int64_t toff = tile_index(a, p, kvh, b0 + wave + kWaves * k) * TILE;
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
       kr[j] = *reinterpret_cast<const u32x4*>(kbase + toff + j * 1024);

@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnArgs a, int max_t
   const int qlen = a.qsl[seq + 1] - qs;
   if (tile * TROWS >= qlen) return;
   const int kvh = h / (hq / a.hkv);
-  const int cap = min(a.max_ctx, a.max_blocks * 16);   // keys the table row can address
+  const int cap = min(a.max_ctx, a.max_blocks << (4 + a.bs_shift));   // keys the table row can address
   const int base_pos = a.lens[seq] - qlen;             // position of the chunk's row 0
 
   const int wave = wave_uniform(threadIdx.x >> 6);
@@ -119,7 +119,6 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnArgs a, int max_t
   const int32_t* trow = a.tables + static_cast<int64_t>(seq) * a.max_blocks;
   const uint8_t* kc = static_cast<const uint8_t*>(a.kc);
   const uint8_t* vc = static_cast<const uint8_t*>(a.vc);
-  const int64_t head_off = static_cast<int64_t>(kvh) * 16 * ROWB;
 
   // Tile b of the context into registers: K chunks first, then V.  Rows past
   // the workgroup's last key, and every row of a block outside the pool,
@@ -128,9 +127,9 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnArgs a, int max_t
   u32x4 ld[P][LPT];
   auto gload = [&](int b, u32x4 (&rg)[LPT]) {
     int p = -1;
-    if (b < nblk) p = trow[b];
+    if (b < nblk) p = trow[b >> a.bs_shift];
     const bool ok = p >= 0 && p < a.num_blocks;
-    const int64_t toff = static_cast<int64_t>(p) * a.hkv * 16 * ROWB + head_off;
+    const int64_t toff = tile_index(a, p, kvh, b) * (16 * ROWB);
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int c = threadIdx.x + 256 * i;
@@ -171,7 +170,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnArgs a, int max_t
   // serve every row tile.
   auto compute = [&](int b, int buf) {
     const int kb = b * 16;
-    const int p = trow[b];
+    const int p = trow[b >> a.bs_shift];
     if (p < 0 || p >= a.num_blocks || kb > wlast) return;   // wave-uniform
     // ---- S^T = K . Q^T
     f32x4 s[R];

@@ -59,7 +59,7 @@ def test_device_entry_points_reject_bad_arguments_without_a_gpu():
                                         0.1, 0, 0, None, 0, None)
     assert st == PKV_ERR_INVALID
     assert b"multiple" in lib.pkv_last_error()
-    # partition size not a multiple of the block size
+    # partition size not a multiple of 16
     st = lib.pkv_paged_attention_decode(None, PKV_BF16, None, PKV_BF16, None, None, PKV_BF16,
                                         None, None, None, 8, None, 128, 1, 8, 8, 128, 16, 10,
                                         0.1, 40, 0, None, 0, None)
@@ -113,3 +113,37 @@ def test_workspace_size_formula():
     o = 16 * 64 * parts * 128 * 4
     ml = 16 * 64 * parts * 2 * 4
     assert n == -(-o // 256) * 256 + -(-ml // 256) * 256
+
+
+def test_block_sizes_accepted_and_refused_on_the_host():
+    import paged_kv_cache_366_amd as pkv
+    from paged_kv_cache_366_amd._lib import PKV_BF16, PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED
+    lib = pkv.load()
+
+    def decode(bs, max_ctx):
+        return lib.pkv_paged_attention_decode(None, PKV_BF16, None, PKV_BF16, None, None,
+                                              PKV_BF16, None, None, None, 8, None, max_ctx, 1, 8,
+                                              8, 128, bs, 10, 0.1, 0, 0, None, 0, None)
+    for bs in (8, 24, 48, 256):
+        assert decode(bs, 64) == PKV_ERR_UNSUPPORTED, bs
+        assert b"block_size" in lib.pkv_last_error()
+    for bs in (16, 32, 64, 128):
+        # passes the size checks, then stops at the NULL pointers
+        assert decode(bs, 8 * bs) == PKV_ERR_INVALID and b"NULL" in lib.pkv_last_error(), bs
+        # one token more than 8 table entries address
+        assert decode(bs, 8 * bs + 1) == PKV_ERR_INVALID
+        assert b"max_blocks_per_seq" in lib.pkv_last_error(), bs
+
+
+def test_adaptive_block_size_matches_the_oracle():
+    import json
+    import os
+    import numpy as np
+    import paged_kv_cache_366_amd as pkv
+    from oracle.allocator import adaptive_page_size
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "adaptive_block_size.json")))
+    xs = [c[0] for c in g["cases"]] + list(np.random.default_rng(1).uniform(-10, 5e4, 500))
+    xs += [float("nan"), -1.0, 511.9999999, 2047.9999999]
+    for x in xs:
+        assert pkv.pkv_adaptive_block_size(x) == adaptive_page_size(x), x
