@@ -27,6 +27,10 @@ HIP_FLAGS = [
     "-Wno-unused-function", "-Wno-unused-variable",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fgpu-flush-denormals-to-zero",
+    # MFMA accumulators in ordinary VGPRs: without this the compiler keeps
+    # them in AGPRs and copies all of them through VGPRs on every loop trip
+    # that may rescale them (the online softmax), and uses more registers.
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall"]
 

@@ -94,6 +94,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnArgs a, int max_t
   }
   const int wrows = min(WROWS, qlen - q0);
   const int wlast = wrows > 0 ? min(base_pos + q0 + wrows - 1, cap - 1) : -1;
+  const int wfirst = wrows > 0 ? min(base_pos + q0, cap - 1) : -1;   // first row's last key
   const int tlast = min(base_pos + min(qlen, (tile + 1) * TROWS) - 1, cap - 1);
   const int nblk = tlast >= 0 ? (tlast >> 4) + 1 : 0;
 
@@ -183,7 +184,11 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnArgs a, int max_t
 #pragma unroll
       for (int r = 0; r < R; ++r) s[r] = M::k32(kop, qop[r][kk], s[r]);
     }
-    // ---- online softmax per row, lazily rescaled; P^T as hi + lo pairs
+    // ---- online softmax per row, lazily rescaled; P^T as hi + lo pairs.
+    // Tiles wholly at or below the wave's first row position need no causal
+    // mask (the key rows past the workgroup's last key, zeros in LDS, only
+    // occur in tiles that reach past it).
+    const bool whole = kb + 15 <= wfirst;
     u32x4 pcat[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -192,13 +197,17 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnArgs a, int max_t
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = kb + 4 * kg + i;
-        sc[i] = t <= qlast[r] ? s[r][i] * a.scale_log2 : kNegInf;
+        sc[i] = (whole || t <= qlast[r]) ? s[r][i] * a.scale_log2 : kNegInf;
         tmax = fmaxf(tmax, sc[i]);
       }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const bool grow = tmax > m[r] + kRescaleSlack;
-      if (__any(grow)) {   // rare after the first blocks
+      // The running max of a row is shared by its four lane groups.  A lane
+      // whose keys stay within the slack of it changes nothing; only when
+      // some lane of the wave exceeds it are the row maxima taken across
+      // the lane groups (the same value in all four) and the row rescaled.
+      if (__any(tmax > m[r] + kRescaleSlack)) {   // rare after the first blocks
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const bool grow = tmax > m[r] + kRescaleSlack;
         const float mn = grow ? tmax : m[r];
         const float alpha = grow ? fast_exp2(m[r] - mn) : 1.f;
         m[r] = mn;
