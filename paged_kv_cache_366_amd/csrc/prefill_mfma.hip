@@ -10,48 +10,71 @@
 //
 // Layout.  A workgroup of 4 wavefronts owns 64 consecutive rows of one
 // sequence's chunk for one query head; wavefront w takes rows 16w..16w+15.
-// Every row of the workgroup reads the same keys, so each 16-token K and V
-// tile is loaded once into LDS (double-buffered, rows padded by 16 bytes so
+// Every row of the workgroup reads the same keys, so K and V go through LDS
+// in steps of two 16-row tiles (double-buffered, rows padded by 16 bytes so
 // the 16 key rows a wavefront reads at one column fall in different banks)
-// and all four wavefronts read it there.  Per tile and wavefront:
+// and all four wavefronts read them there.  Per tile and wavefront:
 //   S^T [16 keys x 16 rows] = K [16 x D] . Q^T [D x 16]      (D/32 MFMA 16x16x32)
-//   online softmax per row (column): max over the lane's 4 keys, then across
-//   the four lane groups; the row's weights stay in the lanes that hold them,
+//   online softmax per row (column), lazily rescaled: the row maximum across
+//   the four lane groups is taken only when some score outgrows the running
+//   one by the slack; the row's weights stay in the lanes that hold them,
 //   which is exactly the B operand of the next product;
 //   O^T [D x 16 rows] += V^T [D x 16 keys] . P^T [16 keys x 16 rows]
-//       (D/16 MFMA 16x16x16, weights as a 16-bit hi + lo pair)
+//       (D/16 MFMA 16x16x32, weights as a 16-bit hi + lo pair: K = 32 is the
+//       lane's 4 keys with the hi weights, then the same keys with the lo)
 // Lane (m, g) reads the D/16 elements m*D/16.. of key rows 4g..4g+3 from
 // LDS, so product j sees element m*D/16 + j; at the end the lane holds 32
 // contiguous output elements of its row.
 //
+// Loads: the next step's global loads are issued right after the barrier
+// and land in registers while the wavefronts compute; no branch guards them
+// (a block outside the pool reads a fixed in-pool address), so the wait
+// before the LDS store covers only that step's loads.
+//
 // Causality: a key t is used by row i when t <= P_i; rows past the chunk are
-// idle, and a wavefront skips tiles past its last row's position.  Key rows
-// past the workgroup's last position (the unwritten tail of the last block)
-// are stored to LDS as zeros, so no garbage enters the products; a table
-// entry outside the pool makes its whole tile masked.
+// idle, and a wavefront skips tiles past its last row's position; tiles
+// wholly at or below the wavefront's first row position skip the test.  Key
+// rows past the workgroup's last position (the unwritten tail of the last
+// block) are stored to LDS as zeros, so no garbage enters the products; a
+// table entry outside the pool makes its whole tile masked.
 //
 // Grid order: the query head is the fastest index, so (with a head count
 // that is a multiple of 8) all tiles of one (sequence, head) go to the same
 // XCD and share the K/V lines it caches in L2.
+//
+// Measured on MI355X (mixed step, four 512-row chunks): the loads, LDS
+// stores and barriers alone take about 60% of the kernel's time, at about
+// 6.6 TB/s of K/V delivered to the compute units, close to what streaming
+// reads reach; deeper prefetch, wider workgroups and wider steps move the
+// total by a few percent at most.
 #include "attention_common.h"
 #include "mfma_common.h"
 
 namespace pkv {
 namespace {
 
-constexpr int kPrefillWaves = 4;
+#ifndef PKV_PREFILL_WAVES
+#define PKV_PREFILL_WAVES 4
+#endif
+constexpr int kPrefillWaves = PKV_PREFILL_WAVES;   // wavefronts (16 rows each) per workgroup
+constexpr int kPrefillThreads = 64 * kPrefillWaves;
 #ifndef PKV_PREFILL_DEPTH
 #define PKV_PREFILL_DEPTH 1
 #endif
 #ifndef PKV_PREFILL_RTILES
 #define PKV_PREFILL_RTILES 1
 #endif
-constexpr int kDepth = PKV_PREFILL_DEPTH;     // blocks whose global loads are in flight
+#ifndef PKV_PREFILL_GROUP
+#define PKV_PREFILL_GROUP 2
+#endif
+// Tuning constants (the defaults measured best on MI355X):
+constexpr int kDepth = PKV_PREFILL_DEPTH;     // steps whose global loads are in flight
+constexpr int kGroup = PKV_PREFILL_GROUP;     // 16-key tiles per LDS step (one barrier)
 constexpr int kRowTiles = PKV_PREFILL_RTILES; // 16-row tiles per wavefront
 constexpr int kTileRows = kPrefillWaves * 16 * kRowTiles;   // query rows per workgroup
 
-template <typename T, int D, int P, int R>
-__global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnArgs a, int max_tiles) {
+template <typename T, int D, int P, int R, int G0>
+__global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs a, int max_tiles) {
   constexpr int NK = D / 32;              // QK products per block and row tile
   constexpr int NV = D / 16;              // PV products per block and row tile
   constexpr int VB = NV * 2;              // bytes of a lane's V chunk
@@ -59,7 +82,11 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnArgs a, int max_t
   constexpr int LROW = ROWB + 16;         // LDS row stride
   constexpr int CHUNKS = ROWB / 16;       // 16-byte chunks per row
   constexpr int TILE_CHUNKS = 16 * CHUNKS;
-  constexpr int LPT = (2 * TILE_CHUNKS + 255) / 256;   // K+V chunks per thread per block
+  constexpr int NT = kPrefillThreads;
+  // Blocks per LDS step: at least enough that every thread has a chunk.
+  constexpr int G = (G0 * 2 * TILE_CHUNKS >= NT) ? G0 : NT / (2 * TILE_CHUNKS);
+  constexpr int LPS = G * 2 * TILE_CHUNKS / NT;   // K+V chunks per thread per step
+  static_assert(G * 2 * TILE_CHUNKS == NT * LPS, "a step's K and V split evenly over the threads");
   constexpr int WROWS = 16 * R;           // rows per wavefront
   constexpr int TROWS = kPrefillWaves * WROWS;
   using M = Mx<T>;
@@ -114,8 +141,8 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnArgs a, int max_t
     }
   }
 
-  __shared__ __align__(16) uint8_t sk[2][16 * LROW];
-  __shared__ __align__(16) uint8_t sv[2][16 * LROW];
+  __shared__ __align__(16) uint8_t sk[2][G * 16 * LROW];
+  __shared__ __align__(16) uint8_t sv[2][G * 16 * LROW];
 
   const int32_t* trow = a.tables + static_cast<int64_t>(seq) * a.max_blocks;
   const uint8_t* kc = static_cast<const uint8_t*>(a.kc);
@@ -125,34 +152,51 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnArgs a, int max_t
   // the workgroup's last key, and every row of a block outside the pool,
   // become zeros.  P blocks are in flight: slot u of the ring holds block
   // b with b % P == u, so after unrolling every index is static.
-  u32x4 ld[P][LPT];
-  auto gload = [&](int b, u32x4 (&rg)[LPT]) {
-    int p = -1;
-    if (b < nblk) p = trow[b >> a.bs_shift];
-    const bool ok = p >= 0 && p < a.num_blocks;
-    const int64_t toff = tile_index(a, p, kvh, b) * (16 * ROWB);
+  u32x4 ld[P][LPS];
+  bool ld_ok[P][G];
+  // Loads of the G blocks of step st: chunk c of the step is block c / (2
+  // TILE_CHUNKS), K then V.  No branch around them and nothing consumes
+  // them before the LDS store, so the wait there covers only that step's
+  // loads and P steps really are in flight.  A block outside the pool (or
+  // past the table) reads the same bytes of the pool's first tile instead;
+  // the store turns it, and every row past the workgroup's last key, into
+  // zeros.
+  auto gload = [&](int st, u32x4 (&rg)[LPS], bool (&ok)[G]) {
+    int64_t toff[G];
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int c = threadIdx.x + 256 * i;
-      const int which = c / TILE_CHUNKS;
-      const int rc = c % TILE_CHUNKS;
-      const int row = rc / CHUNKS;
-      rg[i] = u32x4{0u, 0u, 0u, 0u};
-      if (ok && c < 2 * TILE_CHUNKS && b * 16 + row <= tlast)
-        rg[i] = *reinterpret_cast<const u32x4*>((which == 0 ? kc : vc) + toff + row * ROWB +
-                                                (rc % CHUNKS) * 16);
+    for (int g = 0; g < G; ++g) {
+      const int b = st * G + g;
+      const int p = trow[min(b, nblk - 1) >> a.bs_shift];
+      ok[g] = b < nblk && p >= 0 && p < a.num_blocks;
+      toff[g] = ok[g] ? tile_index(a, p, kvh, b) * (16 * ROWB) : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < LPS; ++i) {
+      const int c = threadIdx.x + NT * i;
+      const int g = c / (2 * TILE_CHUNKS);
+      const int rem = c % (2 * TILE_CHUNKS);
+      int64_t off = toff[0];
+#pragma unroll
+      for (int k = 1; k < G; ++k) off = g == k ? toff[k] : off;
+      rg[i] = *reinterpret_cast<const u32x4*>((rem < TILE_CHUNKS ? kc : vc) + off +
+                                              (rem % TILE_CHUNKS) * 16);
     }
   };
-  auto sstore = [&](int buf, const u32x4 (&rg)[LPT]) {
+  auto sstore = [&](int buf, const u32x4 (&rg)[LPS], int st, const bool (&ok)[G]) {
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int c = threadIdx.x + 256 * i;
-      if (c < 2 * TILE_CHUNKS) {
-        const int which = c / TILE_CHUNKS;
-        const int rc = c % TILE_CHUNKS;
-        uint8_t* dst = (which == 0 ? sk[buf] : sv[buf]) + (rc / CHUNKS) * LROW + (rc % CHUNKS) * 16;
-        *reinterpret_cast<u32x4*>(dst) = rg[i];
-      }
+    for (int i = 0; i < LPS; ++i) {
+      const int c = threadIdx.x + NT * i;
+      const int g = c / (2 * TILE_CHUNKS);
+      const int rem = c % (2 * TILE_CHUNKS);
+      const int which = rem / TILE_CHUNKS;
+      const int rc = rem % TILE_CHUNKS;
+      const int row = rc / CHUNKS;
+      bool okg = ok[0];
+#pragma unroll
+      for (int k = 1; k < G; ++k) okg = g == k ? ok[k] : okg;
+      const bool use = okg && (st * G + g) * 16 + row <= tlast;
+      uint8_t* dst = (which == 0 ? sk[buf] : sv[buf]) + (g * 16 + row) * LROW + (rc % CHUNKS) * 16;
+      *reinterpret_cast<u32x4*>(dst) = use ? rg[i] : u32x4{0u, 0u, 0u, 0u};
     }
   };
 
@@ -169,10 +213,11 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnArgs a, int max_t
   // One block: its tile from LDS buffer `buf`, for each of the wave's row
   // tiles.  The K operands and the V operand are read and built once and
   // serve every row tile.
-  auto compute = [&](int b, int buf) {
+  // `ok`: the block is in the pool (and b < nblk).
+  auto compute = [&](int b, int buf, bool ok) {
     const int kb = b * 16;
-    const int p = trow[b >> a.bs_shift];
-    if (p < 0 || p >= a.num_blocks || kb > wlast) return;   // wave-uniform
+    if (!ok || kb > wlast) return;   // wave-uniform
+    const int lrow0 = (b % G) * 16;   // the block's first row in the LDS step
     // ---- S^T = K . Q^T
     f32x4 s[R];
 #pragma unroll
@@ -180,7 +225,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnArgs a, int max_t
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
       const u32x4 kop =
-          *reinterpret_cast<const u32x4*>(sk[buf] + r16 * LROW + (32 * kk + 8 * kg) * 2);
+          *reinterpret_cast<const u32x4*>(sk[buf] + (lrow0 + r16) * LROW + (32 * kk + 8 * kg) * 2);
 #pragma unroll
       for (int r = 0; r < R; ++r) s[r] = M::k32(kop, qop[r][kk], s[r]);
     }
@@ -233,7 +278,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnArgs a, int max_t
     u32x4 vrow[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      vrow[e] = load_bytes<VB>(sv[buf] + (4 * kg + e) * LROW + r16 * VB);
+      vrow[e] = load_bytes<VB>(sv[buf] + (lrow0 + 4 * kg + e) * LROW + r16 * VB);
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       const uint32_t v01 = pair_of(vrow[0], vrow[1], j);
@@ -244,22 +289,29 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnArgs a, int max_t
     }
   };
 
+  const int nstep = (nblk + G - 1) / G;
+  if (nblk > 0) {   // (the loads below read table entries 0 .. nblk - 1 only)
 #pragma unroll
-  for (int u = 0; u < P; ++u) gload(u, ld[u]);
-  // Block b: its registers go to LDS buffer b & 1 (the other buffer may
-  // still be read by slower waves for block b - 1), one barrier, then the
-  // freed registers start loading block b + P.
+    for (int u = 0; u < P; ++u) gload(u, ld[u], ld_ok[u]);
+  }
+  // Step st: its registers go to LDS buffer st & 1 (the other buffer may
+  // still be read by slower waves for step st - 1), one barrier, then the
+  // freed registers start loading step st + P.  Whole groups of P steps, so
+  // no step is conditional (a step past the last block stores zeros and
+  // computes nothing).
 #pragma unroll 1
-  for (int b0 = 0; b0 < nblk; b0 += P) {
+  for (int s0 = 0; s0 < nstep; s0 += P) {
 #pragma unroll
     for (int u = 0; u < P; ++u) {
-      const int b = b0 + u;
-      if (b < nblk) {
-        sstore(b & 1, ld[u]);
-        __syncthreads();
-        gload(b + P, ld[u]);
-        compute(b, b & 1);
-      }
+      const int st = s0 + u;
+      bool ok[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) ok[g] = ld_ok[u][g];
+      sstore(st & 1, ld[u], st, ok);
+      __syncthreads();
+      gload(st + P, ld[u], ld_ok[u]);
+#pragma unroll
+      for (int g = 0; g < G; ++g) compute(st * G + g, st & 1, ok[g]);
     }
   }
 
@@ -284,13 +336,14 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnArgs a, int max_t
 template <typename T>
 pkv_status launch_t(const AttnArgs& a, int D, int max_tiles, hipStream_t st) {
   const int64_t wgs = static_cast<int64_t>(a.num_seqs) * max_tiles * a.hq;
-  if (wgs > 0x7fffffff / 256) return fail(PKV_ERR_UNSUPPORTED, "prefill: launch too large");
+  if (wgs > 0x7fffffff / kPrefillThreads)
+    return fail(PKV_ERR_UNSUPPORTED, "prefill: launch too large");
   dim3 grid(static_cast<unsigned>(wgs));
   if (D == 64)
-    hipLaunchKernelGGL((prefill_mfma_kernel<T, 64, kDepth, kRowTiles>), grid, dim3(256), 0, st, a,
+    hipLaunchKernelGGL((prefill_mfma_kernel<T, 64, kDepth, kRowTiles, kGroup>), grid, dim3(kPrefillThreads), 0, st, a,
                        max_tiles);
   else
-    hipLaunchKernelGGL((prefill_mfma_kernel<T, 128, kDepth, kRowTiles>), grid, dim3(256), 0, st,
+    hipLaunchKernelGGL((prefill_mfma_kernel<T, 128, kDepth, kRowTiles, kGroup>), grid, dim3(kPrefillThreads), 0, st,
                        a, max_tiles);
   PKV_LAUNCH_CHECK("chunked prefill (MFMA)");
   return PKV_OK;
