@@ -421,6 +421,9 @@ def bench_mixed(a, torch, pkv, algo):
     out_p = torch.empty(q_p.shape, dtype=torch.float32, device=dev)
     ws = torch.empty(max(pkv.pkv_decode_workspace_bytes(len(dec), hq, D, mc_d, part), 1),
                      dtype=torch.uint8, device=dev)
+    ppart = a.prefill_partition
+    ws_p = torch.empty(max(pkv.pkv_prefill_workspace_bytes(len(rows_p), hq, D, mc_p, ppart), 1),
+                       dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
 
@@ -436,7 +439,7 @@ def bench_mixed(a, torch, pkv, algo):
         if ev is not None:
             ev[2].record(stream)
         pkv.pkv_paged_attention_prefill(out_p, q_p, kc, vc, t_p, qsl_d, l_p, mq, mc_p,
-                                        float(ms.scale))
+                                        float(ms.scale), partition_tokens=ppart, workspace=ws_p)
         if ev is not None:
             ev[3].record(stream)
 
@@ -483,7 +486,8 @@ def bench_mixed(a, torch, pkv, algo):
                     "U[64, 4096]) + 4 prefill chunks of 512 causal rows over 0/512/1024/1536 "
                     "cached tokens; 32 heads x 128; step = reshape_and_cache of 2096 rows + "
                     "decode + reduce + chunked prefill",
-        "partition_tokens": part, "algo": a.algo})
+        "partition_tokens": part, "prefill_partition_tokens": a.prefill_partition,
+        "algo": a.algo})
     result.update({
         "tokens_per_s": (len(dec) + len(rows_p)) / (ms_per_step * 1e-3),
         "kernel_ms": {"reshape_and_cache": float(np.mean(rc_ms)), "decode_and_reduce": dec_avg,
@@ -785,6 +789,9 @@ def bench_prefix(a, torch, pkv, algo):
     full = batch(plain, [0] * len(rest))
     for b in (hit, full):
         b["out"] = torch.empty(b["q"].shape, dtype=torch.float32, device=dev)
+        b["ws"] = torch.empty(max(pkv.pkv_prefill_workspace_bytes(
+            b["q"].shape[0], hq, D, int(lens.max()), a.prefill_partition), 1),
+            dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     mc = int(lens.max())
     torch.cuda.synchronize()
@@ -792,7 +799,8 @@ def bench_prefix(a, torch, pkv, algo):
     def run(b):
         pkv.pkv_reshape_and_cache(b["k"], b["v"], kc, vc, b["slots"])
         pkv.pkv_paged_attention_prefill(b["out"], b["q"], kc, vc, b["tables"], b["qsl"], b["lens"],
-                                        b["max_q"], mc, float(c.scale))
+                                        b["max_q"], mc, float(c.scale),
+                                        partition_tokens=a.prefill_partition, workspace=b["ws"])
 
     def step(ev):
         if ev is not None:
@@ -838,7 +846,7 @@ def bench_prefix(a, torch, pkv, algo):
                     "a 1024-token system prompt already in the cache, 64-256 own tokens each; "
                     "admission = reshape_and_cache + prefill of the uncached rows, against the "
                     "same requests computed in full",
-        "requests": len(rest)})
+        "requests": len(rest), "prefill_partition_tokens": a.prefill_partition})
     result.update({
         "kernel_ms": {"with_prefix_cache": h_avg, "without": f_avg},
         "speedup": f_avg / h_avg,
@@ -854,7 +862,79 @@ def bench_prefix(a, torch, pkv, algo):
     return result
 
 
-WORKLOADS = ("decode7b", "mixed", "beam", "gqa", "gqa-int8", "quantize", "swap", "prefix")
+# ---------------------------------------------------------------------------
+# chunked prefill of a long document: short chunks over long cached contexts
+# ---------------------------------------------------------------------------
+def bench_prefill_long(a, torch, pkv, algo):
+    from synth import workloads as W
+    print("[bench] building the long-context prefill workload on the host", file=sys.stderr,
+          flush=True)
+    # 4 documents of 16,384 tokens whose last 64 tokens form this step's chunk
+    c = W.prefill_case(7, 32, 32, 128, [(16384 - 64, 64)] * 4, dtype="bf16")
+    dev = "cuda"
+    D, hq = 128, 32
+    kc, vc = to_dev_bf16(c.k_cache, torch), to_dev_bf16(c.v_cache, torch)
+    q = to_dev_bf16(c.q, torch)
+    t = torch.from_numpy(c.block_tables).to(dev)
+    l = torch.from_numpy(c.context_lens).to(dev)
+    qsl = torch.from_numpy(c.query_start_loc).to(dev)
+    mc, mq = int(c.context_lens.max()), 64
+    part = a.prefill_partition or 2048
+    out_s = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    out_n = torch.empty_like(out_s)
+    ws = torch.empty(max(pkv.pkv_prefill_workspace_bytes(q.shape[0], hq, D, mc, part), 1),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def step(ev):
+        if ev is not None:
+            ev[0].record(stream)
+        pkv.pkv_paged_attention_prefill(out_s, q, kc, vc, t, qsl, l, mq, mc, float(c.scale),
+                                        partition_tokens=part, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+        pkv.pkv_paged_attention_prefill(out_n, q, kc, vc, t, qsl, l, mq, mc, float(c.scale))
+        if ev is not None:
+            ev[2].record(stream)
+
+    ms_per_step, (split_ms, plain_ms) = run_timed(torch, step, a.steps, a.warmup, 2)
+    s_avg, n_avg = float(np.mean(split_ms)), float(np.mean(plain_ms))
+    flops = sum(sum(range(16384 - 64 + 1, 16384 + 1)) for _ in range(4)) * hq * D * 4
+    kv_bytes = 4 * 16384 * hq * D * 2 * 2
+    from oracle import attention as A
+    got = out_s.cpu().numpy()
+    rng = np.random.default_rng(0)
+    err = 0.0
+    for s_ in range(4):
+        K = gather_dev_all(kc, c.block_tables[s_], 16384, torch)
+        V = gather_dev_all(vc, c.block_tables[s_], 16384, torch)
+        for i in (0, 63):
+            h_ = int(rng.integers(0, hq))
+            P = 16384 - 64 + i
+            ref = A.attend(c.q[64 * s_ + i, h_], K[:P + 1, h_], V[:P + 1, h_], c.scale)
+            err = max(err, float(np.abs(got[64 * s_ + i, h_] - ref).max()))
+    result = base_result(a, METRIC, kv_bytes / (s_avg * 1e-3) / 1e9, "GB/s (K/V read)", ms_per_step,
+                         "bf16", {
+        "workload": "chunked prefill of long documents, bf16: 4 sequences of 16,384 tokens whose "
+                    "last 64 form the chunk, 32 heads x 128; split-K prefill (key partitions + "
+                    "reduce) against the same call without partitions",
+        "prefill_partition_tokens": part})
+    result.update({
+        "kernel_ms": {"split": s_avg, "no_split": n_avg},
+        "speedup": n_avg / s_avg,
+        "roofline": roofline("prefill_mfma_kernel + reduce (split-K)", "hbm",
+                             kv_bytes / (s_avg * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
+        "mfma_tflops": flops / (s_avg * 1e-3) / 1e12,
+        "max_abs_diff_split_vs_not": float((out_s - out_n).abs().max()),
+        "max_abs_err_vs_oracle_sampled": err,
+        "cpu_baseline": None,
+    })
+    return result
+
+
+WORKLOADS = ("decode7b", "mixed", "beam", "gqa", "gqa-int8", "quantize", "swap", "prefix",
+             "prefill-long")
 
 
 def main(argv=None) -> int:
@@ -868,6 +948,8 @@ def main(argv=None) -> int:
                     help="split-K partition size in tokens (0 = no split); default 256, or 512 "
                          "for the long-context GQA workloads")
     ap.add_argument("--algo", choices=("auto", "wave", "mfma"), default="auto")
+    ap.add_argument("--prefill-partition", type=int, default=0,
+                    help="key partition size of chunked prefill in tokens (0 = no split)")
     ap.add_argument("--block-size", type=int, default=BLOCK, choices=(16, 32, 64, 128),
                     help="KV block size of the decode7b workload (16 is the headline line)")
     ap.add_argument("--seed", type=int, default=1)
@@ -904,6 +986,8 @@ def main(argv=None) -> int:
         result = bench_swap(a, torch, pkv)
     elif a.workload == "prefix":
         result = bench_prefix(a, torch, pkv, algo)
+    elif a.workload == "prefill-long":
+        result = bench_prefill_long(a, torch, pkv, algo)
     else:
         result = bench_gqa(a, torch, pkv, algo, int8=(a.workload == "gqa-int8"))
     print(json.dumps(result), flush=True)

@@ -364,16 +364,29 @@ pkv_status pkv_paged_attention_reduce(void* out, pkv_dtype out_dtype, const int3
  *   query_start_loc device int32[num_seqs + 1], non-decreasing, from 0
  *   context_lens   device int32[num_seqs], each >= its chunk length
  *   max_query_len  the largest chunk (sizes the launch)
+ *   partition_tokens  0: one workgroup walks all keys of its rows; otherwise
+ *                  a multiple of 16: the keys are split into partitions of
+ *                  that many tokens, processed by separate workgroups (so a
+ *                  long context no longer serialises on one workgroup), and
+ *                  rows whose keys span several partitions are merged by the
+ *                  partition reduce (log-sum-exp, as for decode) before the
+ *                  call returns.  Results for a fixed value are deterministic.
+ *   workspace      device scratch of at least pkv_prefill_workspace_bytes(...)
+ *                  bytes (may be NULL when that is 0), 256-byte aligned.
  * q_dtype F16/BF16 with kv_dtype equal to it (MFMA path), or F32 throughout
  * (wavefront path, one query row at a time).  Supported head_dim 64/128,
  * block_size 16/32/64/128, group (num_q_heads / num_kv_heads) of any size. */
+size_t pkv_prefill_workspace_bytes(int32_t num_query_tokens, int32_t num_q_heads,
+                                   int32_t head_dim, int32_t max_context_len,
+                                   int32_t partition_tokens);
 pkv_status pkv_paged_attention_prefill(
     void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype, const void* k_cache,
     const void* v_cache, pkv_dtype kv_dtype, const float* k_scale, const float* v_scale,
     const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* query_start_loc,
     const int32_t* context_lens, int32_t max_query_len, int32_t max_context_len, int32_t num_seqs,
     int32_t num_query_tokens, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-    int32_t block_size, int32_t num_blocks, float scale, void* stream);
+    int32_t block_size, int32_t num_blocks, float scale, int32_t partition_tokens,
+    void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -358,23 +358,38 @@ def pkv_paged_attention_reduce(out, context_lens, max_context_len: int, partitio
         _stream(out, stream)))
 
 
+def pkv_prefill_workspace_bytes(num_query_tokens: int, num_q_heads: int, head_dim: int,
+                                max_context_len: int, partition_tokens: int) -> int:
+    return load().pkv_prefill_workspace_bytes(num_query_tokens, num_q_heads, head_dim,
+                                              max_context_len, partition_tokens)
+
+
 def pkv_paged_attention_prefill(out, q, k_cache, v_cache, block_tables, query_start_loc,
                                 context_lens, max_query_len: int, max_context_len: int,
-                                scale: float, k_scale=None, v_scale=None, stream=None) -> None:
-    """out, q: [Tq, Hq, D]; query_start_loc int32 [S+1]; context_lens int32 [S]."""
+                                scale: float, k_scale=None, v_scale=None, stream=None,
+                                partition_tokens: int = 0, workspace=None):
+    """out, q: [Tq, Hq, D]; query_start_loc int32 [S+1]; context_lens int32 [S].
+    Returns the workspace tensor used (or None)."""
     torch = _torch()
     Tq, hq, d = q.shape
     nb, hkv, bs, d2 = k_cache.shape
     S = context_lens.shape[0]
     if out.shape != q.shape or d2 != d or query_start_loc.shape != (S + 1,):
         raise ValueError("shape mismatch")
+    need = pkv_prefill_workspace_bytes(Tq, hq, d, int(max_context_len), int(partition_tokens))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = C.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     check(load().pkv_paged_attention_prefill(
         _dev(out, "out"), _dtype_code(out), _dev(q, "q"), _dtype_code(q), _dev(k_cache, "k_cache"),
         _dev(v_cache, "v_cache"), _dtype_code(k_cache), _dev(k_scale, "k_scale", torch.float32),
         _dev(v_scale, "v_scale", torch.float32), _dev(block_tables, "block_tables", torch.int32),
         block_tables.shape[1], _dev(query_start_loc, "query_start_loc", torch.int32),
         _dev(context_lens, "context_lens", torch.int32), int(max_query_len), int(max_context_len),
-        S, Tq, hq, hkv, d, bs, nb, float(scale), _stream(q, stream)))
+        S, Tq, hq, hkv, d, bs, nb, float(scale), int(partition_tokens), ws_ptr, ws_len,
+        _stream(q, stream)))
+    return workspace
 
 
 __all__ = sorted(set(__all__) | {n for n in dir() if n.startswith("pkv_")})

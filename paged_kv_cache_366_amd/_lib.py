@@ -69,7 +69,8 @@ SIGNATURES = {
                                           _vp]),
     "pkv_paged_attention_prefill": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp,
                                            _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
-                                           _i32, _i32, _i32, _f32, _vp]),
+                                           _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
+    "pkv_prefill_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
 }
 
 _lib = None

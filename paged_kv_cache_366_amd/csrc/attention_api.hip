@@ -205,6 +205,15 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
       .total;
 }
 
+size_t pkv_prefill_workspace_bytes(int32_t num_query_tokens, int32_t num_q_heads,
+                                   int32_t head_dim, int32_t max_context_len,
+                                   int32_t partition_tokens) {
+  if (num_query_tokens <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
+  return workspace_layout(num_query_tokens, num_q_heads, head_dim,
+                          num_partitions(max_context_len, partition_tokens))
+      .total;
+}
+
 pkv_status pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void* q,
                                       pkv_dtype q_dtype, const void* k_cache, const void* v_cache,
                                       pkv_dtype kv_dtype, const float* k_scale,
@@ -285,7 +294,8 @@ pkv_status pkv_paged_attention_prefill(
     const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* query_start_loc,
     const int32_t* context_lens, int32_t max_query_len, int32_t max_context_len, int32_t num_seqs,
     int32_t num_query_tokens, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-    int32_t block_size, int32_t num_blocks, float scale, void* stream) {
+    int32_t block_size, int32_t num_blocks, float scale, int32_t partition_tokens,
+    void* workspace, size_t workspace_bytes, void* stream) {
   PKV_GUARD({
     const char* who = "paged_attention_prefill";
     pkv_status st = check_common(who, out, out_dtype, q, q_dtype, k_cache, v_cache, kv_dtype,
@@ -299,6 +309,14 @@ pkv_status pkv_paged_attention_prefill(
       return fail(PKV_ERR_INVALID, "%s: query_start_loc is NULL", who);
     if (kv_dtype == PKV_I8)
       return fail(PKV_ERR_UNSUPPORTED, "%s: int8 KV is a decode-only storage here", who);
+    if (partition_tokens < 0 || partition_tokens % 16 != 0)
+      return fail(PKV_ERR_INVALID, "%s: partition_tokens %d must be 0 or a multiple of 16", who,
+                  partition_tokens);
+    const int parts = num_partitions(max_context_len, partition_tokens);
+    const WsLayout w = workspace_layout(num_query_tokens, num_q_heads, head_dim, parts);
+    if (w.total > 0 && (!workspace || workspace_bytes < w.total || !aligned(workspace, kAlign)))
+      return fail(PKV_ERR_INVALID, "%s: workspace needs %zu bytes, 256-byte aligned (got %zu)",
+                  who, w.total, workspace_bytes);
     if (num_seqs == 0 || num_query_tokens == 0) return PKV_OK;
     if (deep_validation()) {
       std::vector<int32_t> L, Q;
@@ -333,14 +351,22 @@ pkv_status pkv_paged_attention_prefill(
     a.hq = num_q_heads;
     a.hkv = num_kv_heads;
     a.num_blocks = num_blocks;
-    a.num_parts = 1;
-    a.part_tokens = std::max(16, (max_context_len + 15) / 16 * 16);
+    a.num_parts = parts;
+    a.part_tokens = parts > 1 ? partition_tokens : std::max(16, (max_context_len + 15) / 16 * 16);
+    a.part_o = parts > 1 ? static_cast<float*>(workspace) : nullptr;
+    a.part_ml =
+        parts > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + w.o_bytes) : nullptr;
     a.out_kind = out_kind_of(out_dtype);
     a.scale_log2 = scale * kLog2e;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const int group = num_q_heads / num_kv_heads;
-    if (q_dtype == PKV_F32) return launch_decode_wave(a, q_dtype, kv_dtype, head_dim, group, hs);
-    return launch_prefill_mfma(a, q_dtype, head_dim, group, max_query_len, hs);
+    pkv_status ls = q_dtype == PKV_F32
+                        ? launch_decode_wave(a, q_dtype, kv_dtype, head_dim, group, hs)
+                        : launch_prefill_mfma(a, q_dtype, head_dim, group, max_query_len, hs);
+    if (ls) return ls;
+    // Rows whose keys span several partitions left partial results; the
+    // decode reduce merges them (it finds each row's keys through qsl).
+    return parts > 1 ? launch_reduce(a, head_dim, hs) : PKV_OK;
   })
 }
 

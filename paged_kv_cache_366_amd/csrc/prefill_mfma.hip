@@ -96,8 +96,10 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
   const int hq = a.hq;
   const int h = blockIdx.x % hq;
   const int rest = blockIdx.x / hq;
-  const int tile = max_tiles - 1 - rest % max_tiles;
-  const int seq = rest / max_tiles;
+  const int part = rest % a.num_parts;   // key partition (split-K)
+  const int rest2 = rest / a.num_parts;
+  const int tile = max_tiles - 1 - rest2 % max_tiles;
+  const int seq = rest2 / max_tiles;
   const int qs = a.qsl[seq];
   const int qlen = a.qsl[seq + 1] - qs;
   if (tile * TROWS >= qlen) return;
@@ -124,6 +126,11 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
   const int wfirst = wrows > 0 ? min(base_pos + q0, cap - 1) : -1;   // first row's last key
   const int tlast = min(base_pos + min(qlen, (tile + 1) * TROWS) - 1, cap - 1);
   const int nblk = tlast >= 0 ? (tlast >> 4) + 1 : 0;
+  // This workgroup's key tiles: those of its partition, up to the last key.
+  const int ptiles = a.part_tokens >> 4;
+  const int b_begin = part * ptiles;
+  const int b_end = min(nblk, b_begin + ptiles);
+  if (b_begin >= b_end) return;   // no row of the tile has keys in this partition
 
   // Q^T operands: row q0 + 16r + r16, elements 32kk + 8kg .. +7.
   u32x4 qop[R][NK];
@@ -165,9 +172,9 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
     int64_t toff[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const int b = st * G + g;
-      const int p = trow[min(b, nblk - 1) >> a.bs_shift];
-      ok[g] = b < nblk && p >= 0 && p < a.num_blocks;
+      const int b = b_begin + st * G + g;
+      const int p = trow[min(b, b_end - 1) >> a.bs_shift];
+      ok[g] = b < b_end && p >= 0 && p < a.num_blocks;
       toff[g] = ok[g] ? tile_index(a, p, kvh, b) * (16 * ROWB) : 0;
     }
 #pragma unroll
@@ -194,7 +201,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
       bool okg = ok[0];
 #pragma unroll
       for (int k = 1; k < G; ++k) okg = g == k ? ok[k] : okg;
-      const bool use = okg && (st * G + g) * 16 + row <= tlast;
+      const bool use = okg && (b_begin + st * G + g) * 16 + row <= tlast;
       uint8_t* dst = (which == 0 ? sk[buf] : sv[buf]) + (g * 16 + row) * LROW + (rc % CHUNKS) * 16;
       *reinterpret_cast<u32x4*>(dst) = use ? rg[i] : u32x4{0u, 0u, 0u, 0u};
     }
@@ -213,11 +220,12 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
   // One block: its tile from LDS buffer `buf`, for each of the wave's row
   // tiles.  The K operands and the V operand are read and built once and
   // serve every row tile.
-  // `ok`: the block is in the pool (and b < nblk).
-  auto compute = [&](int b, int buf, bool ok) {
+  // `ok`: the block is in the pool (and in this workgroup's range); it sits
+  // in slot g of the LDS step.
+  auto compute = [&](int b, int buf, bool ok, int g) {
     const int kb = b * 16;
     if (!ok || kb > wlast) return;   // wave-uniform
-    const int lrow0 = (b % G) * 16;   // the block's first row in the LDS step
+    const int lrow0 = g * 16;   // the block's first row in the LDS step
     // ---- S^T = K . Q^T
     f32x4 s[R];
 #pragma unroll
@@ -289,8 +297,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
     }
   };
 
-  const int nstep = (nblk + G - 1) / G;
-  if (nblk > 0) {   // (the loads below read table entries 0 .. nblk - 1 only)
+  const int nstep = (b_end - b_begin + G - 1) / G;
+  {   // (the loads read table entries of blocks b_begin .. b_end - 1 only)
 #pragma unroll
     for (int u = 0; u < P; ++u) gload(u, ld[u], ld_ok[u]);
   }
@@ -311,7 +319,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
       __syncthreads();
       gload(st + P, ld[u], ld_ok[u]);
 #pragma unroll
-      for (int g = 0; g < G; ++g) compute(st * G + g, st & 1, ok[g]);
+      for (int g = 0; g < G; ++g) compute(b_begin + st * G + g, st & 1, ok[g], g);
     }
   }
 
@@ -322,20 +330,38 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
     lr += __shfl_xor(lr, 16);
     lr += __shfl_xor(lr, 32);
     if (!qlive[r]) continue;
-    const float inv = lr > 0.f ? 1.f / lr : 0.f;
-    const int64_t orow = (static_cast<int64_t>(qs + q0 + 16 * r + r16) * hq + h) * D;
-    // acc[r][j][i] is element NV*(4kg + i) + j of the row.
+    // Partitions the row's own keys span (as the reduce counts them): one
+    // means this workgroup (partition 0) writes the final row; more mean
+    // each partition leaves its unnormalised output and (max, sum).
+    const int rparts = a.num_parts > 1 ? (qlast[r] + a.part_tokens) / a.part_tokens : 1;
+    if (part >= max(rparts, 1)) continue;
+    const int64_t grow = static_cast<int64_t>(qs + q0 + 16 * r + r16) * hq + h;
+    if (rparts <= 1) {
+      const float inv = lr > 0.f ? 1.f / lr : 0.f;
+      // acc[r][j][i] is element NV*(4kg + i) + j of the row.
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < NV; ++j)
-        store_out(a, orow + NV * (4 * kg + i) + j, acc[r][j][i] * inv);
+        for (int j = 0; j < NV; ++j)
+          store_out(a, grow * D + NV * (4 * kg + i) + j, acc[r][j][i] * inv);
+    } else {
+      const int64_t slot = grow * a.num_parts + part;
+      float* po = a.part_o + slot * D;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NV; ++j) po[NV * (4 * kg + i) + j] = acc[r][j][i];
+      if (kg == 0) {
+        a.part_ml[slot * 2] = m[r];
+        a.part_ml[slot * 2 + 1] = lr;
+      }
+    }
   }
 }
 
 template <typename T>
 pkv_status launch_t(const AttnArgs& a, int D, int max_tiles, hipStream_t st) {
-  const int64_t wgs = static_cast<int64_t>(a.num_seqs) * max_tiles * a.hq;
+  const int64_t wgs = static_cast<int64_t>(a.num_seqs) * max_tiles * a.num_parts * a.hq;
   if (wgs > 0x7fffffff / kPrefillThreads)
     return fail(PKV_ERR_UNSUPPORTED, "prefill: launch too large");
   dim3 grid(static_cast<unsigned>(wgs));

@@ -214,3 +214,58 @@ def test_mixed_step_full_size_sampled():
     # 0/512/1024/1536 cached tokens, 32 heads x 128, bf16
     ms = W.mixed_step(seed=2)
     run_mixed_step(ms, sample_rows=6)
+
+
+# ------------------------------------------------------------ split-K prefill
+LONG_CHUNKS = [(0, 70), (300, 130), (1000, 64), (777, 1), (33, 0), (64, 200), (1500, 17)]
+
+
+def prefill_split(c, part, out_dtype=torch.float32, workspace=None):
+    qd = to_dev(c.q, c.dtype)
+    out = torch.empty(qd.shape, dtype=out_dtype, device=DEV)
+    ws = pkv.pkv_paged_attention_prefill(
+        out, qd, to_dev(c.k_cache, c.dtype), to_dev(c.v_cache, c.dtype), i32(c.block_tables),
+        i32(c.query_start_loc), i32(c.context_lens), int(np.diff(c.query_start_loc).max()),
+        int(c.context_lens.max()), float(c.scale), partition_tokens=part, workspace=workspace)
+    torch.cuda.synchronize()
+    return out, ws
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d", [("bf16", 8, 2, 128), ("f16", 4, 4, 64),
+                                            ("f32", 4, 2, 64)])
+def test_split_prefill_matches_oracle_and_unsplit(dtype, hq, hkv, d):
+    c = W.prefill_case(90 + d, hq, hkv, d, LONG_CHUNKS, dtype=dtype)
+    ref = oracle_prefill(c)
+    base, ws0 = prefill_split(c, 0)
+    assert ws0 is None
+    tol = TOL32 if dtype == "f32" else TOL16
+    for part in (16, 48, 256, 512):
+        out, ws = prefill_split(c, part)
+        assert ws is not None
+        got = out_f64(out)
+        assert np.abs(got - ref).max() <= tol, part
+        # splitting only reassociates fp32 sums
+        assert np.abs(got - out_f64(base)).max() <= 1e-5, part
+    # a partition covering every context is no split at all
+    same, ws = prefill_split(c, 2048)
+    assert ws is None and torch.equal(same, base)
+
+
+def test_split_prefill_bf16_output_and_determinism():
+    c = W.prefill_case(95, 8, 8, 128, LONG_CHUNKS, dtype="bf16")
+    of, _ = prefill_split(c, 256)
+    ob, _ = prefill_split(c, 256, out_dtype=torch.bfloat16)
+    assert torch.equal(ob.view(torch.int16), of.to(torch.bfloat16).view(torch.int16))
+    again, _ = prefill_split(c, 256)
+    assert torch.equal(again, of)
+
+
+def test_split_prefill_rejects_a_small_workspace():
+    c = W.prefill_case(96, 4, 4, 64, [(300, 20)], dtype="bf16")
+    need = pkv.pkv_prefill_workspace_bytes(20, 4, 64, 320, 64)
+    assert need > 0
+    small = torch.empty(need - 256, dtype=torch.uint8, device=DEV)
+    with pytest.raises(pkv.PkvError):
+        prefill_split(c, 64, workspace=small)
+    with pytest.raises(pkv.PkvError):
+        prefill_split(c, 40)          # not a multiple of 16
