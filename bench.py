@@ -704,7 +704,9 @@ def bench_swap(a, torch, pkv):
         if ev is not None:
             ev[2].record(stream)
 
+    pkv.pkv_swap_stats_get(reset=True)
     ms_per_step, (out_ms, in_ms) = run_timed(torch, step, a.steps, a.warmup, 2)
+    swap_stats = pkv.pkv_swap_stats_get(reset=True)   # warm-up and timed steps
     nbytes = n * int(np.prod(kc.shape[1:])) * 2 * 2          # K and V, one direction
     o, i_ = float(np.mean(out_ms)), float(np.mean(in_ms))
     result = base_result(a, METRIC, 2 * nbytes / (ms_per_step * 1e-3) / 1e9, "GB/s", ms_per_step,
@@ -719,6 +721,9 @@ def bench_swap(a, torch, pkv):
         "roofline": None,
         "note": "DMA over PCIe; the pages quote 32-64 GB/s for PCIe (kongchang.com, section "
                 "on preemption)",
+        "swap_stats": swap_stats,
+        "swapped_blocks_per_s": (swap_stats["blocks_to_host"] + swap_stats["blocks_to_device"])
+        / ((a.steps + a.warmup) * ms_per_step * 1e-3),
         "cpu_baseline": None,
     })
     return result

@@ -259,6 +259,21 @@ pkv_status pkv_swap_blocks(void* dst_k, void* dst_v, float* dst_k_scale, float* 
 size_t pkv_swap_workspace_bytes(int32_t max_pairs, int32_t num_kv_heads, int32_t head_dim,
                                 int32_t block_size, pkv_dtype dtype);
 
+/* Process-wide counters of pkv_swap_blocks, for the swap-rate health metric
+ * of [cnnetsun] §4.2 (page swaps per second; frequent swapping calls for
+ * larger pages): successful calls, blocks moved by direction, and bytes
+ * (K and V, with int8 scales).  The caller divides by its own clock.  A
+ * non-zero `reset` zeroes them after reading. */
+typedef struct pkv_swap_stats {
+  int64_t calls;
+  int64_t blocks_to_host;
+  int64_t blocks_to_device;
+  int64_t blocks_device_to_device;
+  int64_t blocks_host_to_host;
+  int64_t bytes;
+} pkv_swap_stats;
+pkv_status pkv_swap_stats_get(pkv_swap_stats* out, int32_t reset);
+
 /* ------------------------------------------------------------------------
  * quantize_blocks (device): int8 storage of whole blocks.  cnnetsun.cn §3.2
  * (内存压缩技术) lists INT8 KV at a quarter of fp32's bytes, and §4.3

@@ -15,7 +15,7 @@ import numpy as np
 
 from ._lib import (PKV_ALGO_AUTO, PKV_ALGO_MFMA, PKV_ALGO_WAVE, PKV_BF16, PKV_ERR_DEVICE,  # noqa
                    PKV_ERR_INTERNAL, PKV_ERR_INVALID, PKV_ERR_OUT_OF_BLOCKS, PKV_ERR_UNSUPPORTED,
-                   PKV_F16, PKV_F32, PKV_I8, PKV_OK, LIB_PATH, PkvBmStats, PkvError,
+                   PKV_F16, PKV_F32, PKV_I8, PKV_OK, LIB_PATH, PkvBmStats, PkvError, PkvSwapStats,
                    PkvOutOfBlocks, check, load)
 
 __all__ = [n for n in dir() if n.startswith("pkv_") or n.startswith("PKV_")]
@@ -232,6 +232,12 @@ def pkv_copy_blocks(k_cache, v_cache, pairs, k_scale=None, v_scale=None, stream=
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(k_scale, "k_scale", torch.float32),
         _dev(v_scale, "v_scale", torch.float32), _dev(pairs, "pairs", torch.int32), n, hkv, d, bs,
         nb, _dtype_code(k_cache), _stream(k_cache, stream)))
+
+
+def pkv_swap_stats_get(reset: bool = False) -> dict:
+    st = PkvSwapStats()
+    check(load().pkv_swap_stats_get(C.byref(st), 1 if reset else 0))
+    return {f: getattr(st, f) for f, _ in PkvSwapStats._fields_}
 
 
 def pkv_swap_workspace_bytes(max_pairs: int, num_kv_heads: int, head_dim: int, block_size: int,

@@ -20,6 +20,12 @@ _pi32 = C.POINTER(C.c_int32)
 _pi64 = C.POINTER(C.c_int64)
 
 
+class PkvSwapStats(C.Structure):
+    _fields_ = [("calls", _i64), ("blocks_to_host", _i64), ("blocks_to_device", _i64),
+                ("blocks_device_to_device", _i64), ("blocks_host_to_host", _i64),
+                ("bytes", _i64)]
+
+
 class PkvBmStats(C.Structure):
     _fields_ = [("num_blocks", _i32), ("block_size", _i32), ("free_blocks", _i32),
                 ("used_blocks", _i32), ("shared_blocks", _i32), ("num_seqs", _i32),
@@ -56,6 +62,7 @@ SIGNATURES = {
     "pkv_swap_blocks": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _pi32, _i32,
                                _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
     "pkv_swap_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pkv_swap_stats_get": (_i32, [C.POINTER(PkvSwapStats), _i32]),
     "pkv_quantize_blocks": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                    _i32, _i32, _vp]),
     "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),

@@ -10,6 +10,7 @@
 // chunks so each wavefront access is a fully used 1 KiB span, and neither
 // kernel touches a slot or block outside the pool whatever the index arrays
 // hold.
+#include <atomic>
 #include <unordered_set>
 #include <vector>
 
@@ -389,6 +390,18 @@ extern "C" pkv_status pkv_quantize_blocks(const void* src_k, const void* src_v,
 // is one copy.  Device <-> device swaps run the copy kernel directly.
 namespace {
 
+// Process-wide swap counters for the swap-rate health metric
+// (cnnetsun.cn "别再让GPU内存拖后腿了…" §4.2 lists page swaps per second,
+// with frequent swapping a sign that pages are too small).
+struct SwapCounters {
+  std::atomic<int64_t> calls{0}, to_host{0}, to_device{0}, device_to_device{0}, host_to_host{0},
+      bytes{0};
+};
+SwapCounters& swap_counters() {
+  static SwapCounters c;
+  return c;
+}
+
 bool is_device_memory(const void* p) {
   hipPointerAttribute_t attr;
   if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
@@ -590,6 +603,27 @@ extern "C" pkv_status pkv_swap_blocks(void* dst_k, void* dst_v, float* dst_k_sca
     }
     if (e != hipSuccess)
       return fail(PKV_ERR_DEVICE, "%s: copy failed: %s", who, hipGetErrorString(e));
+    SwapCounters& sc = swap_counters();
+    sc.calls.fetch_add(1);
+    (src_dev && !dst_dev   ? sc.to_host
+     : !src_dev && dst_dev ? sc.to_device
+     : src_dev             ? sc.device_to_device
+                           : sc.host_to_host).fetch_add(num_pairs);
+    sc.bytes.fetch_add(static_cast<int64_t>(num_pairs) * 2 * (bb + (scales ? sb : 0)));
     return PKV_OK;
   })
 }
+
+extern "C" pkv_status pkv_swap_stats_get(pkv_swap_stats* out, int32_t reset) {
+  if (!out) return fail(PKV_ERR_INVALID, "swap_stats: out is NULL");
+  SwapCounters& sc = swap_counters();
+  auto take = [&](std::atomic<int64_t>& c) { return reset ? c.exchange(0) : c.load(); };
+  out->calls = take(sc.calls);
+  out->blocks_to_host = take(sc.to_host);
+  out->blocks_to_device = take(sc.to_device);
+  out->blocks_device_to_device = take(sc.device_to_device);
+  out->blocks_host_to_host = take(sc.host_to_host);
+  out->bytes = take(sc.bytes);
+  return PKV_OK;
+}
+

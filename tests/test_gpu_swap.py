@@ -133,3 +133,23 @@ def test_decode_after_swap_round_trip_is_bit_identical():
     tables[s, :nblk] = free
     after = decode(tables)
     assert torch.equal(before, after)
+
+
+def test_swap_counters_count_blocks_and_bytes():
+    pkv.pkv_swap_stats_get(reset=True)
+    nb, hkv, d = 12, 2, 64
+    dk = torch.zeros((nb, hkv, 16, d), dtype=torch.bfloat16, device=DEV)
+    dv = torch.zeros_like(dk)
+    hk = host_pool((6, hkv, 16, d), torch.bfloat16)
+    hv = host_pool((6, hkv, 16, d), torch.bfloat16)
+    ws = workspace("large", hkv, d)
+    pkv.pkv_swap_blocks(hk, hv, dk, dv, np.array([[0, 0], [3, 1], [4, 2]], np.int32), workspace=ws)
+    pkv.pkv_swap_blocks(dk, dv, hk, hv, np.array([[0, 5], [1, 6]], np.int32), workspace=ws)
+    pkv.pkv_swap_blocks(dk, dv, dk, dv, np.array([[7, 8]], np.int32), workspace=ws)
+    torch.cuda.synchronize()
+    st = pkv.pkv_swap_stats_get(reset=True)
+    block = hkv * 16 * d * 2
+    assert st == {"calls": 3, "blocks_to_host": 3, "blocks_to_device": 2,
+                  "blocks_device_to_device": 1, "blocks_host_to_host": 0,
+                  "bytes": 6 * 2 * block}
+    assert pkv.pkv_swap_stats_get()["calls"] == 0

@@ -147,3 +147,11 @@ def test_adaptive_block_size_matches_the_oracle():
     xs += [float("nan"), -1.0, 511.9999999, 2047.9999999]
     for x in xs:
         assert pkv.pkv_adaptive_block_size(x) == adaptive_page_size(x), x
+
+
+def test_swap_counters_read_and_reset_without_a_gpu():
+    import paged_kv_cache_366_amd as pkv
+    st = pkv.pkv_swap_stats_get(reset=True)
+    assert set(st) == {"calls", "blocks_to_host", "blocks_to_device", "blocks_device_to_device",
+                       "blocks_host_to_host", "bytes"}
+    assert all(v == 0 for v in pkv.pkv_swap_stats_get().values())
