@@ -61,3 +61,72 @@ def quantize_blocks(pool: np.ndarray, codes: np.ndarray, scales: np.ndarray,
         for h in range(pool.shape[1]):
             out_codes[b, h], out_scales[b, h] = quantize_tile(pool[b, h], f)
     return out_codes, out_scales
+
+
+def runs_of(slots: Sequence[int], block_size: int):
+    """Split a slot mapping into runs: maximal stretches of consecutive
+    tokens whose slots are consecutive rows of one block.  Yields (first
+    token, block, first row, number of rows); slots < 0 are skipped."""
+    t, n = 0, len(slots)
+    while t < n:
+        s = int(slots[t])
+        if s < 0:
+            t += 1
+            continue
+        b, r = s // block_size, s % block_size
+        k = 1
+        while (t + k < n and int(slots[t + k]) >= 0 and int(slots[t + k]) // block_size == b
+               and int(slots[t + k]) == s + k):
+            k += 1
+        yield t, b, r, k
+        t += k
+
+
+def append_tile(codes: np.ndarray, scale: np.float32, row0: int, new_rows: np.ndarray):
+    """Quantise-on-write of one (block, KV head) tile: rows [0, row0) hold
+    codes under ``scale`` and ``new_rows`` (float32, exactly as stored) go to
+    rows row0, row0 + 1, ....  Returns the tile's new codes and scale.
+
+    Reading (the pages name INT8 KV but no encoding, cnnetsun.cn §3.2 and
+    §4.3): the scale only grows.  s_new = max(s_old, float32(a / 127)) with
+    a = max |new rows| (s_old counts as 0 when row0 == 0); a scale below the
+    smallest normal float32 counts as 0.  When the scale grows, each existing
+    code c is re-encoded from its value: rint(float32(float32(c * s_old) /
+    s_new)), clamped to [-127, 127]; new rows encode as rint(float32(x /
+    s_new)), clamped.  With row0 == 0 this is quantize_tile over the new
+    rows."""
+    codes = np.array(codes, dtype=np.int8, copy=True)
+    new_rows = np.asarray(new_rows, dtype=np.float32)
+    k = new_rows.shape[0]
+    s_old = np.float32(scale) if row0 > 0 else np.float32(0)
+    a = np.float32(np.max(np.abs(new_rows))) if k else np.float32(0)
+    s_new = max(s_old, np.float32(a / np.float32(127)))
+    if s_new < SMALLEST_NORMAL:
+        s_new = np.float32(0)
+    if s_new == 0:
+        codes[row0:row0 + k] = 0
+        return codes, np.float32(s_new if row0 == 0 else s_old)
+    if s_new > s_old and row0 > 0:
+        old = codes[:row0].astype(np.float32)
+        vals = (old * s_old).astype(np.float32)
+        codes[:row0] = np.clip(np.rint((vals / s_new).astype(np.float32)), -127, 127).astype(np.int8)
+    q = np.rint((new_rows / s_new).astype(np.float32))
+    codes[row0:row0 + k] = np.clip(q, -127, 127).astype(np.int8)
+    return codes, np.float32(s_new)
+
+
+def reshape_and_cache_int8(key: np.ndarray, value: np.ndarray, k_codes: np.ndarray,
+                           v_codes: np.ndarray, k_scale: np.ndarray, v_scale: np.ndarray,
+                           slots: Sequence[int], block_size: int):
+    """Write new tokens' K/V ``[T, H, D]`` (float32, exactly as stored) into
+    int8 pools ``[NB, H, BS, D]`` with per-(block, head) scales ``[NB, H]``,
+    run by run (see runs_of): each run's block takes its rows below the
+    run's first row as already written and encodes the run with
+    append_tile.  Returns new copies of the four arrays."""
+    kc, vc = np.array(k_codes, copy=True), np.array(v_codes, copy=True)
+    ks, vs = np.array(k_scale, np.float32, copy=True), np.array(v_scale, np.float32, copy=True)
+    for t0, b, r0, k in runs_of(slots, block_size):
+        for h in range(kc.shape[1]):
+            kc[b, h], ks[b, h] = append_tile(kc[b, h], ks[b, h], r0, key[t0:t0 + k, h])
+            vc[b, h], vs[b, h] = append_tile(vc[b, h], vs[b, h], r0, value[t0:t0 + k, h])
+    return kc, vc, ks, vs

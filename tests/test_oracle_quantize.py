@@ -72,3 +72,80 @@ def test_quantize_blocks_touches_only_listed_blocks():
         for h in range(2):
             c, s = Q.quantize_tile(pool[b, h], f)
             assert np.array_equal(c2[b, h], c) and s2[b, h] == s
+
+
+# ------------------------------------------------------------ quantise-on-write
+def _scale(text):
+    num, _, den = text.partition("/")
+    return np.float32(np.float32(float(num)) / np.float32(float(den))) if den else np.float32(float(num))
+
+
+def test_append_hand_worked_cases():
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "int8_append.json")))
+    for case in g["cases"]:
+        codes, s = np.zeros((4, 4), np.int8), np.float32(0)
+        for st in case["steps"]:
+            codes, s = Q.append_tile(codes, s, st["row0"], np.asarray(st["rows"], np.float32))
+            want = np.asarray(st["codes"], np.int8)
+            assert np.array_equal(codes[:len(want)], want), (case["name"], codes[:len(want)])
+            assert s == _scale(st["scale"]), (case["name"], s)
+
+
+def test_whole_block_write_is_the_block_encoder():
+    rng = np.random.default_rng(31)
+    for filled in (1, 7, 16):
+        x = (rng.standard_normal((16, 64)) * 3).astype(np.float32)
+        codes, s = Q.append_tile(np.full((16, 64), 99, np.int8), np.float32(5), 0, x[:filled])
+        ref_codes, ref_s = Q.quantize_tile(x, filled)
+        assert s == ref_s and np.array_equal(codes[:filled], ref_codes[:filled])
+
+
+def test_appends_stay_within_the_rounding_bound():
+    # token by token; each growth of the scale re-encodes the rows before it,
+    # adding at most half a step of the new scale (plus float rounding)
+    rng = np.random.default_rng(32)
+    for trial in range(20):
+        x = (rng.standard_normal((16, 32)) * rng.uniform(0.1, 10, (16, 1))).astype(np.float32)
+        codes, s = np.zeros((16, 32), np.int8), np.float32(0)
+        growths_after = np.zeros(16, np.int64)
+        for r in range(16):
+            s_prev = s
+            codes, s = Q.append_tile(codes, s, r, x[r:r + 1])
+            if r and s > s_prev:
+                growths_after[:r] += 1
+            assert s >= s_prev
+            # every code stays in range and the scale covers the new row
+            assert np.abs(codes).max() <= 127
+            assert np.abs(x[r]).max() <= 127 * s * (1 + 1e-6)
+        deq = codes.astype(np.float64) * np.float64(s)
+        bound = (growths_after + 1)[:, None] * 0.5 * np.float64(s) * (1 + 1e-5)
+        assert np.all(np.abs(deq - x) <= bound), trial
+
+
+def test_runs_of_slot_mappings():
+    assert list(Q.runs_of([5, 6, 7, 32, 33, -1, 8, 40], 16)) == [
+        (0, 0, 5, 3), (3, 2, 0, 2), (6, 0, 8, 1), (7, 2, 8, 1)]
+    # a run stops at a block edge and at a gap between rows
+    assert list(Q.runs_of([14, 15, 16, 18], 16)) == [(0, 0, 14, 2), (2, 1, 0, 1), (3, 1, 2, 1)]
+    assert list(Q.runs_of([], 16)) == []
+
+
+def test_reshape_and_cache_int8_decode_step_matches_tile_appends():
+    rng = np.random.default_rng(33)
+    nb, h, d = 6, 2, 8
+    kc = np.zeros((nb, h, 16, d), np.int8)
+    vc = np.zeros_like(kc)
+    ks = np.zeros((nb, h), np.float32)
+    vs = np.zeros_like(ks)
+    # two sequences: blocks 4 and 1, appended a token at a time
+    for step in range(20):
+        slots = [4 * 16 + step % 16 if step < 16 else 5 * 16 + step - 16, 1 * 16 + step % 16]
+        key = rng.standard_normal((2, h, d)).astype(np.float32)
+        val = rng.standard_normal((2, h, d)).astype(np.float32)
+        nkc, nvc, nks, nvs = Q.reshape_and_cache_int8(key, val, kc, vc, ks, vs, slots, 16)
+        for t, slot in enumerate(slots):
+            b, r = slot // 16, slot % 16
+            for hh in range(h):
+                c, s = Q.append_tile(kc[b, hh], ks[b, hh], r, key[t:t + 1, hh])
+                assert np.array_equal(nkc[b, hh], c) and nks[b, hh] == s
+        kc, vc, ks, vs = nkc, nvc, nks, nvs
