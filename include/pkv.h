@@ -208,6 +208,37 @@ pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_cac
                                  int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                  pkv_dtype dtype, void* stream);
 
+/* reshape_and_cache into int8 storage (quantise on write): the new tokens'
+ * K/V rows go into int8 pools with one fp32 scale per (block, KV head), the
+ * write side of the int8 decode path ([cnnetsun] §3.2 lists INT8 KV; §4.3
+ * turns it on for the historical pages).  The slot mapping splits into runs
+ * (consecutive tokens whose slots are consecutive rows of one block, as an
+ * append writes them); a run's block is taken as written below the run's
+ * first row.  The scale only grows, to max(old, max|new rows| / 127): when
+ * it grows, the existing codes are re-encoded from their values
+ * (code x old / new, rounded to nearest even, clamped to +-127), and the new
+ * rows are encoded with the new scale.  A run starting at row 0 ignores the
+ * old scale, so a whole block in one run is pkv_quantize_blocks exactly.
+ * Rows past the run are left as they are (decode masks them).
+ *   key, value     device [num_tokens][num_kv_heads][head_dim] in src_dtype
+ *                  (F32/F16/BF16), strides as for pkv_reshape_and_cache
+ *   k_codes, v_codes device int8 [num_blocks][num_kv_heads][block_size][head_dim]
+ *   k_scale, v_scale device float [num_blocks][num_kv_heads]
+ *   slot_mapping   device int32[num_tokens]; -1 skips a token.  A block may
+ *                  receive at most one run per call (PKV_VALIDATE=1 checks
+ *                  this and rejects slots outside the pool or repeated;
+ *                  otherwise such slots are skipped and two runs into one
+ *                  block give unspecified codes).
+ * head_dim must be a multiple of 16.  Bit-exact against the float32
+ * definition. */
+pkv_status pkv_reshape_and_cache_int8(const void* key, const void* value, pkv_dtype src_dtype,
+                                      int8_t* k_codes, int8_t* v_codes, float* k_scale,
+                                      float* v_scale, const int32_t* slot_mapping,
+                                      int32_t num_tokens, int64_t key_stride,
+                                      int64_t value_stride, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                      void* stream);
+
 /* ------------------------------------------------------------------------
  * copy_blocks (device): the data copy of copy-on-write ([kongchang] section
  * "KV Cache内存共享").  For each pair (src, dst): K[dst] = K[src],

@@ -223,6 +223,31 @@ def pkv_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=Non
         _stream(k_cache, stream)))
 
 
+def pkv_reshape_and_cache_int8(key, value, k_codes, v_codes, k_scale, v_scale, slot_mapping,
+                               stream=None) -> None:
+    """key/value [T, Hkv, D] (f32/f16/bf16, row stride from the tensor); int8
+    pools [NB, Hkv, BS, D] and float32 scales [NB, Hkv]."""
+    torch = _torch()
+    T, hkv, d = key.shape
+    nb, hkv2, bs, d2 = k_codes.shape
+    if (hkv, d) != (hkv2, d2) or value.shape != key.shape or v_codes.shape != k_codes.shape:
+        raise ValueError("shape mismatch")
+    if k_codes.dtype != torch.int8 or v_codes.dtype != torch.int8:
+        raise TypeError("code pools must be int8")
+    if k_scale.shape != (nb, hkv) or v_scale.shape != (nb, hkv):
+        raise ValueError("scales must be [NB, Hkv]")
+    for t, n in ((key, "key"), (value, "value")):
+        if t.stride(2) != 1 or t.stride(1) != d:
+            raise ValueError(f"{n} rows must be [Hkv, D] contiguous")
+    if slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be [T]")
+    check(load().pkv_reshape_and_cache_int8(
+        C.c_void_p(key.data_ptr()), C.c_void_p(value.data_ptr()), _dtype_code(key),
+        _dev(k_codes, "k_codes"), _dev(v_codes, "v_codes"), _dev(k_scale, "k_scale", torch.float32),
+        _dev(v_scale, "v_scale", torch.float32), _dev(slot_mapping, "slot_mapping", torch.int32), T,
+        key.stride(0), value.stride(0), hkv, d, bs, nb, _stream(k_codes, stream)))
+
+
 def pkv_copy_blocks(k_cache, v_cache, pairs, k_scale=None, v_scale=None, stream=None) -> None:
     """pairs: int32 [n, 2] device tensor of (src, dst)."""
     torch = _torch()

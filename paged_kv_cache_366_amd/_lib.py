@@ -58,6 +58,8 @@ SIGNATURES = {
     "pkv_adaptive_block_size": (_i32, [C.c_double]),
     "pkv_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i32, _i32, _i32,
                                      _i32, _i32, _vp]),
+    "pkv_reshape_and_cache_int8": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i64,
+                                          _i64, _i32, _i32, _i32, _i32, _vp]),
     "pkv_copy_blocks": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pkv_swap_blocks": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _pi32, _i32,
                                _i32, _i32, _i32, _i32, _vp, _sz, _vp]),

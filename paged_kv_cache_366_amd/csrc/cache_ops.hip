@@ -211,6 +211,95 @@ __global__ __launch_bounds__(kThreads) void copy_list_kernel(
   }
 }
 
+// Quantise-on-write: new tokens' K/V rows go into int8 pools with one scale
+// per (block, KV head).  The slot mapping splits into runs (consecutive
+// tokens whose slots are consecutive rows of one block); the first token of
+// a run leads it, and one wavefront per (run, head, K or V) takes the run's
+// block as written below the run's first row.  The scale only grows: to
+// max(old scale, max|new rows| / 127); when it grows, each existing code is
+// re-encoded from its value (code x old scale / new scale, rounded to
+// nearest even), and the new rows are encoded with the new scale.  Writing
+// a whole block in one run is the whole-block encoder exactly.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void reshape_and_cache_int8_kernel(
+    const uint8_t* __restrict__ key, const uint8_t* __restrict__ value,
+    int8_t* __restrict__ kc, int8_t* __restrict__ vc, float* __restrict__ ks,
+    float* __restrict__ vs, const int32_t* __restrict__ slots, int n, int64_t key_stride_b,
+    int64_t value_stride_b, int hkv, int head_dim, int block_size, int64_t num_slots) {
+  constexpr int E = 16 / T::bytes;                 // elements per 16-byte chunk
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (w >= static_cast<int64_t>(n) * hkv * 2) return;
+  const int which = static_cast<int>(w & 1);
+  const int h = static_cast<int>((w >> 1) % hkv);
+  const int t = static_cast<int>((w >> 1) / hkv);
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t b = slot / block_size;
+  const int r0 = static_cast<int>(slot % block_size);
+  if (t > 0 && r0 > 0 && slots[t - 1] == slot - 1) return;   // inside a run led earlier
+  int k = 1;                                                  // the run's rows
+  while (t + k < n && k < block_size - r0 && slots[t + k] == slot + k) ++k;
+
+  const int64_t tix = b * hkv + h;
+  int8_t* dst = (which ? vc : kc) + tix * block_size * head_dim;
+  float* scale = which ? vs : ks;
+  const uint8_t* src = (which ? value : key) + static_cast<int64_t>(h) * head_dim * T::bytes;
+  const int64_t stride = which ? value_stride_b : key_stride_b;
+  const int ch = head_dim / E;                     // 16-byte chunks per source row
+
+  float amax = 0.f;
+  for (int c = lane; c < k * ch; c += 64) {
+    float x[E];
+    Unpack<T>::run(*reinterpret_cast<const u32x4*>(src + (t + c / ch) * stride + (c % ch) * 16),
+                   x);
+#pragma unroll
+    for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(x[e]));
+  }
+  amax = wave_absmax(amax);
+  const float s_old = r0 > 0 ? scale[tix] : 0.f;
+  float s_new = fmaxf(s_old, amax / 127.f);
+  if (!(s_new >= kSmallestNormal)) s_new = 0.f;
+
+  if (s_new > s_old && r0 > 0) {
+    // existing rows: 16 codes per lane step
+    for (int o = lane * 16; o < r0 * head_dim; o += 64 * 16) {
+      struct Codes16 {
+        int8_t v[16];
+      };
+      const Codes16 old = __builtin_bit_cast(Codes16, *reinterpret_cast<const u32x4*>(dst + o));
+      int8_t q[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float y = static_cast<float>(old.v[e]) * s_old;
+        q[e] = static_cast<int8_t>(fminf(fmaxf(rintf(y / s_new), -127.f), 127.f));
+      }
+      *reinterpret_cast<u32x4*>(dst + o) = __builtin_bit_cast(u32x4, q);
+    }
+  }
+  for (int c = lane; c < k * ch; c += 64) {
+    const int i = c / ch;
+    int8_t q[E];
+    if (s_new > 0.f) {
+      float x[E];
+      Unpack<T>::run(*reinterpret_cast<const u32x4*>(src + (t + i) * stride + (c % ch) * 16), x);
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        q[e] = static_cast<int8_t>(fminf(fmaxf(rintf(x[e] / s_new), -127.f), 127.f));
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) q[e] = 0;
+    }
+    int8_t* d = dst + static_cast<int64_t>(r0 + i) * head_dim + (c % ch) * E;
+    if constexpr (E == 8) {
+      *reinterpret_cast<uint64_t*>(d) = __builtin_bit_cast(uint64_t, q);
+    } else {
+      *reinterpret_cast<uint32_t*>(d) = __builtin_bit_cast(uint32_t, q);
+    }
+  }
+  if (lane == 0) scale[tix] = s_new;
+}
+
 }  // namespace
 }  // namespace pkv
 
@@ -267,6 +356,75 @@ extern "C" pkv_status pkv_reshape_and_cache(const void* key, const void* value, 
                        static_cast<uint8_t*>(v_cache), slot_mapping, key_stride * eb,
                        value_stride * eb, num_kv_heads, head_bytes, block_size, num_slots);
     PKV_LAUNCH_CHECK("reshape_and_cache");
+    return PKV_OK;
+  })
+}
+
+extern "C" pkv_status pkv_reshape_and_cache_int8(
+    const void* key, const void* value, pkv_dtype src_dtype, int8_t* k_codes, int8_t* v_codes,
+    float* k_scale, float* v_scale, const int32_t* slot_mapping, int32_t num_tokens,
+    int64_t key_stride, int64_t value_stride, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t num_blocks, void* stream) {
+  PKV_GUARD({
+    const char* who = "reshape_and_cache_int8";
+    if (src_dtype != PKV_F32 && src_dtype != PKV_F16 && src_dtype != PKV_BF16)
+      return fail(PKV_ERR_UNSUPPORTED, "%s: source dtype %s (f32, f16 or bf16)", who,
+                  dtype_name(src_dtype));
+    if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        num_blocks <= 0)
+      return fail(PKV_ERR_INVALID, "%s: bad sizes", who);
+    if (head_dim % 16 != 0)
+      return fail(PKV_ERR_UNSUPPORTED, "%s: head_dim must be a multiple of 16", who);
+    if (num_tokens == 0) return PKV_OK;
+    if (!key || !value || !k_codes || !v_codes || !k_scale || !v_scale || !slot_mapping)
+      return fail(PKV_ERR_INVALID, "%s: NULL pointer", who);
+    const int eb = dtype_bytes(src_dtype);
+    if (key_stride == 0) key_stride = static_cast<int64_t>(num_kv_heads) * head_dim;
+    if (value_stride == 0) value_stride = static_cast<int64_t>(num_kv_heads) * head_dim;
+    if (key_stride < static_cast<int64_t>(num_kv_heads) * head_dim ||
+        value_stride < static_cast<int64_t>(num_kv_heads) * head_dim)
+      return fail(PKV_ERR_INVALID, "%s: row stride shorter than a row", who);
+    if ((key_stride * eb) % 16 || (value_stride * eb) % 16 || !aligned(key, 16) ||
+        !aligned(value, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16))
+      return fail(PKV_ERR_INVALID, "%s: pointers and strides must be 16-byte aligned", who);
+    const int64_t num_slots = static_cast<int64_t>(num_blocks) * block_size;
+    if (deep_validation()) {
+      std::vector<int32_t> s;
+      pkv_status st = fetch_i32(slot_mapping, num_tokens, stream, s);
+      if (st) return st;
+      std::unordered_set<int32_t> seen, run_blocks;
+      for (int32_t i = 0; i < num_tokens; ++i) {
+        if (s[i] < 0) continue;
+        if (s[i] >= num_slots)
+          return fail(PKV_ERR_INVALID, "slot_mapping[%d] = %d outside the pool (%lld slots)", i,
+                      s[i], (long long)num_slots);
+        if (!seen.insert(s[i]).second)
+          return fail(PKV_ERR_INVALID, "slot %d appears twice in slot_mapping", s[i]);
+        const bool leads = !(i > 0 && s[i] % block_size > 0 && s[i - 1] == s[i] - 1);
+        if (leads && !run_blocks.insert(s[i] / block_size).second)
+          return fail(PKV_ERR_INVALID, "%s: block %d gets two runs of rows in one call", who,
+                      s[i] / block_size);
+      }
+    }
+    const int64_t waves = static_cast<int64_t>(num_tokens) * num_kv_heads * 2;
+    const int64_t wgs = (waves + kThreads / 64 - 1) / (kThreads / 64);
+    if (wgs > 0x7fffffff) return fail(PKV_ERR_UNSUPPORTED, "%s: too many tokens", who);
+    auto launch = [&](auto tag) {
+      using T = decltype(tag);
+      hipLaunchKernelGGL(reshape_and_cache_int8_kernel<T>, dim3(static_cast<unsigned>(wgs)),
+                         dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                         static_cast<const uint8_t*>(key), static_cast<const uint8_t*>(value),
+                         k_codes, v_codes, k_scale, v_scale, slot_mapping, num_tokens,
+                         key_stride * eb, value_stride * eb, num_kv_heads, head_dim, block_size,
+                         num_slots);
+    };
+    if (src_dtype == PKV_BF16)
+      launch(BF16{});
+    else if (src_dtype == PKV_F16)
+      launch(F16{});
+    else
+      launch(F32{});
+    PKV_LAUNCH_CHECK("reshape_and_cache_int8");
     return PKV_OK;
   })
 }

@@ -126,3 +126,119 @@ def test_validation_rejects_bad_lists(monkeypatch):
         with pytest.raises(pkv.PkvError):
             pkv.pkv_quantize_blocks(pool, pool, dk, dk.clone(), sc, sc.clone(), i32(blocks),
                                     i32(filled))
+
+
+# ------------------------------------------------------------ quantise on write
+def gpu_int8_write(key, value, dtype, kc, vc, ks, vs, slots):
+    """One pkv_reshape_and_cache_int8 call on device copies; returns host
+    copies of the four pool arrays."""
+    dk, dv = torch.from_numpy(kc).to(DEV), torch.from_numpy(vc).to(DEV)
+    dks, dvs = torch.from_numpy(ks).to(DEV), torch.from_numpy(vs).to(DEV)
+    pkv.pkv_reshape_and_cache_int8(to_dev(key, dtype), to_dev(value, dtype), dk, dv, dks, dvs,
+                                   i32(slots))
+    torch.cuda.synchronize()
+    return dk.cpu().numpy(), dv.cpu().numpy(), dks.cpu().numpy(), dvs.cpu().numpy()
+
+
+@pytest.mark.parametrize("dtype,d,bs", [("bf16", 128, 16), ("f16", 64, 16), ("f32", 64, 16),
+                                        ("bf16", 64, 64)])
+def test_int8_write_prompts_then_decode_steps_bit_exact(dtype, d, bs):
+    rng = np.random.default_rng(40 + d + bs)
+    h, nseq = 3, 5
+    lens = [1, bs - 1, bs, 2 * bs + 3, 37]
+    nb = sum(W.blocks_for(n + 24, bs) for n in lens) + 4
+    order = rng.permutation(nb)
+    tables, off = [], 0
+    for n in lens:
+        k = W.blocks_for(n + 24, bs)
+        tables.append(order[off:off + k])
+        off += k
+    kc = rng.integers(-128, 128, (nb, h, bs, d)).astype(np.int8)   # stale codes everywhere
+    vc = rng.integers(-128, 128, (nb, h, bs, d)).astype(np.int8)
+    ks = rng.random((nb, h)).astype(np.float32)
+    vs = rng.random((nb, h)).astype(np.float32)
+    pos = [0] * nseq
+
+    def slots_for(s, count):
+        return [int(tables[s][(pos[s] + i) // bs]) * bs + (pos[s] + i) % bs for i in range(count)]
+
+    # the prompts in one call (sequence after sequence), values growing with
+    # the position so that later rows raise the scales
+    counts = lens
+    for step in range(25):
+        slots = sum((slots_for(s, counts[s]) for s in range(nseq)), [])
+        T = len(slots)
+        scale = np.float32(0.5 + 0.1 * step)
+        key = W.round_to(W.draw_normal(rng, (T, h, d), dtype) * scale, dtype)
+        val = W.draw_normal(rng, (T, h, d), dtype)
+        got = gpu_int8_write(key, val, dtype, kc, vc, ks, vs, np.asarray(slots, np.int32))
+        ref = Q.reshape_and_cache_int8(key, val, kc, vc, ks, vs, slots, bs)
+        for g, r, name in zip(got, ref, ("k codes", "v codes", "k scales", "v scales")):
+            assert np.array_equal(g.view(np.uint8) if g.dtype == np.int8 else g.view(np.uint32),
+                                  r.view(np.uint8) if r.dtype == np.int8 else r.view(np.uint32)), (
+                step, name)
+        kc, vc, ks, vs = ref
+        for s in range(nseq):
+            pos[s] += counts[s]
+        counts = [1] * nseq          # then one token per sequence per step
+
+
+def test_int8_write_of_whole_blocks_is_quantize_blocks():
+    rng = np.random.default_rng(50)
+    nb, h, d = 10, 4, 128
+    x = W.draw_normal(rng, (nb, h, 16, d), "bf16")
+    blocks = np.array([2, 7, 0, 5], np.int32)
+    # tokens of block b: rows 0..15 in order
+    key = np.concatenate([x[b].transpose(1, 0, 2) for b in blocks])       # [T, h, d]
+    slots = np.concatenate([b * 16 + np.arange(16) for b in blocks]).astype(np.int32)
+    z8 = np.zeros((nb, h, 16, d), np.int8)
+    zs = np.zeros((nb, h), np.float32)
+    kc, vc, ks, vs = gpu_int8_write(key, key, "bf16", z8, z8, zs, zs, slots)
+    ref_c, ref_s = Q.quantize_blocks(x, z8, zs, blocks, np.full(4, 16, np.int32))
+    assert np.array_equal(kc, ref_c) and np.array_equal(ks.view(np.uint32), ref_s.view(np.uint32))
+
+
+def test_decode_over_an_int8_pool_written_token_by_token():
+    rng = np.random.default_rng(51)
+    hq, hkv, d, bs = 8, 2, 128, 16
+    lens = np.array([17, 60, 200, 33], np.int32)
+    nb = sum(W.blocks_for(n) for n in lens) + 3
+    perm = rng.permutation(nb).astype(np.int32)
+    tables = W.place_by_permutation(lens, perm, bs)
+    kc = np.zeros((nb, hkv, bs, d), np.int8)
+    vc = np.zeros_like(kc)
+    ks = np.zeros((nb, hkv), np.float32)
+    vs = np.zeros_like(ks)
+    dk, dv = torch.from_numpy(kc).to(DEV), torch.from_numpy(vc).to(DEV)
+    dks, dvs = torch.from_numpy(ks).to(DEV), torch.from_numpy(vs).to(DEV)
+    for p in range(int(lens.max())):
+        live = [s for s in range(4) if p < lens[s]]
+        slots = np.array([tables[s][p // bs] * bs + p % bs for s in live], np.int32)
+        key = W.draw_normal(rng, (len(live), hkv, d), "bf16")
+        val = W.draw_normal(rng, (len(live), hkv, d), "bf16")
+        pkv.pkv_reshape_and_cache_int8(to_dev(key, "bf16"), to_dev(val, "bf16"), dk, dv, dks, dvs,
+                                       i32(slots))
+        kc, vc, ks, vs = Q.reshape_and_cache_int8(key, val, kc, vc, ks, vs, slots, bs)
+    torch.cuda.synchronize()
+    assert np.array_equal(dk.cpu().numpy(), kc) and np.array_equal(dvs.cpu().numpy(), vs)
+    q = W.draw_normal(rng, (4, hq, d), "bf16")
+    out = torch.empty((4, hq, d), dtype=torch.float32, device=DEV)
+    pkv.pkv_paged_attention_decode(out, to_dev(q, "bf16"), dk, dv, i32(tables), i32(lens),
+                                   int(lens.max()), float(1 / np.sqrt(d)), 64, k_scale=dks,
+                                   v_scale=dvs)
+    torch.cuda.synchronize()
+    ref = A.decode(q, kc, vc, tables, lens, np.float32(1 / np.sqrt(d)), k_scale=ks, v_scale=vs)
+    assert np.abs(out_f64(out) - ref).max() <= 2e-3
+
+
+def test_int8_write_validation(monkeypatch):
+    monkeypatch.setenv("PKV_VALIDATE", "1")
+    key = torch.zeros((3, 1, 64), dtype=torch.bfloat16, device=DEV)
+    codes = torch.zeros((4, 1, 16, 64), dtype=torch.int8, device=DEV)
+    sc = torch.zeros((4, 1), dtype=torch.float32, device=DEV)
+    for slots in ([5, 7, 9], [5, 6, 5], [5, 6, 64]):   # two runs in one block; repeat; outside
+        with pytest.raises(pkv.PkvError):
+            pkv.pkv_reshape_and_cache_int8(key, key, codes, codes.clone(), sc, sc.clone(),
+                                           i32(slots))
+    # consecutive rows of one block and a new block are fine
+    pkv.pkv_reshape_and_cache_int8(key, key, codes, codes.clone(), sc, sc.clone(), i32([5, 6, 16]))
