@@ -317,28 +317,46 @@ def bench_gqa(a, torch, pkv, algo, int8: bool):
     out = torch.empty((S, hq, D), dtype=torch.float32, device=dev)
     ws = torch.empty(max(pkv.pkv_decode_workspace_bytes(S, hq, D, max_ctx, part), 1),
                      dtype=torch.uint8, device=dev)
+    # the step's cache write: each sequence's current token (the last
+    # position) goes to its slot, into the int8 pool through quantise-on-write
+    # (its block's scale already covers it, so the write is the same every
+    # step) or into the bf16 pool
+    last = c.context_lens - 1
+    slot_h = np.array([c.block_tables[s_][p // BLOCK] * BLOCK + p % BLOCK
+                       for s_, p in enumerate(last)], np.int32)
+    new_k = to_dev_bf16(c.k_cache[slot_h // BLOCK, :, slot_h % BLOCK, :], torch)
+    new_v = to_dev_bf16(c.v_cache[slot_h // BLOCK, :, slot_h % BLOCK, :], torch)
+    slots_d = torch.from_numpy(slot_h).to(dev)
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
 
     def step(ev):
         if ev is not None:
             ev[0].record(stream)
+        if int8:
+            pkv.pkv_reshape_and_cache_int8(new_k, new_v, kc, vc, ks, vs, slots_d)
+        else:
+            pkv.pkv_reshape_and_cache(new_k, new_v, kc, vc, slots_d)
+        if ev is not None:
+            ev[1].record(stream)
         pkv.pkv_paged_attention_decode_partials(out, q, kc, vc, tables, lens, max_ctx,
                                                 float(c.scale), part, algo, k_scale=ks,
                                                 v_scale=vs, workspace=ws)
         if ev is not None:
-            ev[1].record(stream)
+            ev[2].record(stream)
         pkv.pkv_paged_attention_reduce(out, lens, max_ctx, part, ws)
         if ev is not None:
-            ev[2].record(stream)
+            ev[3].record(stream)
 
-    ms_per_step, (main_ms, red_ms) = run_timed(torch, step, a.steps, a.warmup, 2)
+    ms_per_step, (wr_ms, main_ms, red_ms) = run_timed(torch, step, a.steps, a.warmup, 3)
     tokens = int(c.context_lens.astype(np.int64).sum())
     eb = 1 if int8 else 2
     kv = tokens * hkv * D * eb * 2
     nblk = sum(W.blocks_for(n) for n in c.context_lens)
     main_bytes = kv + S * hq * D * 2 + nblk * 4 + S * 4 + (nblk * hkv * 8 if int8 else 0)
-    step_bytes = main_bytes + S * hq * D * 4
+    # + the cache write: bf16 rows read, rows written in the pool's type (and scales)
+    wr_bytes = S * hkv * D * 2 * 2 + S * hkv * D * eb * 2 + (S * hkv * 8 if int8 else 0)
+    step_bytes = main_bytes + S * hq * D * 4 + wr_bytes
     main_avg = float(np.mean(main_ms))
     achieved = main_bytes / (main_avg * 1e-3) / 1e9
     # sampled parity of this run's output against the oracle, one row at a time
@@ -358,11 +376,13 @@ def bench_gqa(a, torch, pkv, algo, int8: bool):
                          "int8-kv/bf16" if int8 else "bf16", {
         "workload": f"long-context GQA decode, {'int8 KV with per-block fp32 scales' if int8 else 'bf16 KV'}: "
                     "16 sequences, 64 query heads over 8 KV heads, head_dim 128, "
-                    "contexts U[8192, 32768], split-K partitions + reduce",
+                    "contexts U[8192, 32768]; step = cache write of each sequence's current "
+                    "token + split-K decode + reduce",
         "context_tokens": tokens, "partition_tokens": part, "algo": a.algo})
     result.update({
         "tokens_per_s": S / (ms_per_step * 1e-3),
-        "kernel_ms": {"decode_main": main_avg, "reduce": float(np.mean(red_ms))},
+        "kernel_ms": {"cache_write" + ("_int8" if int8 else ""): float(np.mean(wr_ms)),
+                      "decode_main": main_avg, "reduce": float(np.mean(red_ms))},
         "bytes": {"step": step_bytes, "decode_main": main_bytes, "kv": kv},
         "roofline": roofline("decode_mfma_kernel (split-K main)" if algo != pkv.PKV_ALGO_WAVE
                              else "decode_wave_kernel (split-K main)", "hbm", achieved,
