@@ -69,7 +69,7 @@ def test_device_entry_points_reject_bad_arguments_without_a_gpu():
                                         None, None, None, 8, None, 129, 1, 8, 8, 128, 16, 10,
                                         0.1, 0, 0, None, 0, None)
     assert st == PKV_ERR_INVALID
-    # int8 reshape_and_cache is not provided
+    # the plain reshape_and_cache takes no int8 pool (pkv_reshape_and_cache_int8 does)
     st = lib.pkv_reshape_and_cache(None, None, None, None, None, 4, 0, 0, 8, 128, 16, 10, 3, None)
     assert st == PKV_ERR_UNSUPPORTED
     # quantize_blocks: int8 source, NULL pointers, odd row bytes
