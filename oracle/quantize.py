@@ -1,20 +1,27 @@
-"""Int8 storage of whole KV blocks, as its definition — TEST INFRASTRUCTURE ONLY.
+"""Int8 and 4-bit storage of KV blocks, as its definition — TEST
+INFRASTRUCTURE ONLY.
 
 The cnnetsun.cn page ("别再让GPU内存拖后腿了…") lists INT8 KV in its memory
-compression table (§3.2 内存压缩技术: a quarter of fp32's bytes) and, for
-long documents, turns INT8 on for the historical pages (§4.3
-典型场景优化策略).  The encoding itself is not on the pages.  Reading taken
-here: symmetric codes per (block, KV head), over the block's filled rows,
+compression table (§3.2 内存压缩技术: a quarter of fp32's bytes) and 4-bit
+KV beside it (an eighth of fp32's bytes, 87.5% less); for long documents it
+turns INT8 on for the historical pages (§4.3 典型场景优化策略).  The encoding
+itself is not on the pages.  Reading taken here: symmetric codes per
+(block, KV head), over the block's filled rows, with Q = 127 for int8 and
+Q = 7 for 4-bit,
 
     a     = max |x|                          (float32)
-    s     = float32(a / 127)                 (IEEE division, nearest even)
+    s     = float32(a / Q)                   (IEEE division, nearest even)
     code  = 0                                   if s == 0
-          = clip(rint(float32(x / s)), -127, 127) otherwise
+          = clip(rint(float32(x / s)), -Q, Q)   otherwise
                                              (IEEE division; rint ties to even)
 
 and rows past the filled count get code 0.  A scale below the smallest
-normal float32 (a block whose values are all below about 1.5e-36) counts as
-zero: such a block stores all-zero codes.
+normal float32 (a block whose values are all below about 1.5e-36 times Q)
+counts as zero: such a block stores all-zero codes.
+
+4-bit codes are stored two to a byte: element 2i of a row in the low
+nibble of byte i and element 2i + 1 in the high nibble, each as a 4-bit
+two's complement value (-8 is never written).
 
 Everything is float32 arithmetic, as the definition states: the result is
 unique bit for bit.
@@ -26,11 +33,13 @@ from typing import Sequence, Tuple
 import numpy as np
 
 SMALLEST_NORMAL = np.float32(np.finfo(np.float32).tiny)
+INT8_MAX = 127   # largest int8 code
+INT4_MAX = 7     # largest 4-bit code
 
 
-def quantize_tile(x: np.ndarray, filled: int) -> Tuple[np.ndarray, np.float32]:
-    """Codes ``int8 [rows, D]`` and the scale of one (block, KV head) tile
-    whose first ``filled`` rows hold data."""
+def quantize_tile(x: np.ndarray, filled: int, qmax: int = INT8_MAX) -> Tuple[np.ndarray, np.float32]:
+    """Codes ``int8 [rows, D]`` in [-qmax, qmax] and the scale of one
+    (block, KV head) tile whose first ``filled`` rows hold data."""
     x = np.asarray(x, dtype=np.float32)
     codes = np.zeros(x.shape, dtype=np.int8)
     filled = int(filled)
@@ -38,16 +47,16 @@ def quantize_tile(x: np.ndarray, filled: int) -> Tuple[np.ndarray, np.float32]:
         return codes, np.float32(0)
     rows = x[:filled]
     a = np.float32(np.max(np.abs(rows)))
-    s = np.float32(a / np.float32(127))
+    s = np.float32(a / np.float32(qmax))
     if s < SMALLEST_NORMAL:
         return codes, np.float32(0)
     q = np.rint((rows / s).astype(np.float32))
-    codes[:filled] = np.clip(q, -127, 127).astype(np.int8)
+    codes[:filled] = np.clip(q, -qmax, qmax).astype(np.int8)
     return codes, s
 
 
 def quantize_blocks(pool: np.ndarray, codes: np.ndarray, scales: np.ndarray,
-                    blocks: Sequence[int], filled: Sequence[int]):
+                    blocks: Sequence[int], filled: Sequence[int], qmax: int = INT8_MAX):
     """Encode the listed blocks of a float pool ``[NB, H, BS, D]`` (values
     exactly as stored) into copies of an int8 pool and its ``[NB, H]``
     scales; blocks not listed keep what they held.  A filled count of 0
@@ -59,7 +68,7 @@ def quantize_blocks(pool: np.ndarray, codes: np.ndarray, scales: np.ndarray,
         if f <= 0:
             continue
         for h in range(pool.shape[1]):
-            out_codes[b, h], out_scales[b, h] = quantize_tile(pool[b, h], f)
+            out_codes[b, h], out_scales[b, h] = quantize_tile(pool[b, h], f, qmax)
     return out_codes, out_scales
 
 
@@ -82,17 +91,18 @@ def runs_of(slots: Sequence[int], block_size: int):
         t += k
 
 
-def append_tile(codes: np.ndarray, scale: np.float32, row0: int, new_rows: np.ndarray):
+def append_tile(codes: np.ndarray, scale: np.float32, row0: int, new_rows: np.ndarray,
+                qmax: int = INT8_MAX):
     """Quantise-on-write of one (block, KV head) tile: rows [0, row0) hold
     codes under ``scale`` and ``new_rows`` (float32, exactly as stored) go to
     rows row0, row0 + 1, ....  Returns the tile's new codes and scale.
 
     Reading (the pages name INT8 KV but no encoding, cnnetsun.cn §3.2 and
-    §4.3): the scale only grows.  s_new = max(s_old, float32(a / 127)) with
+    §4.3): the scale only grows.  s_new = max(s_old, float32(a / qmax)) with
     a = max |new rows| (s_old counts as 0 when row0 == 0); a scale below the
     smallest normal float32 counts as 0.  When the scale grows, each existing
     code c is re-encoded from its value: rint(float32(float32(c * s_old) /
-    s_new)), clamped to [-127, 127]; new rows encode as rint(float32(x /
+    s_new)), clamped to [-qmax, qmax]; new rows encode as rint(float32(x /
     s_new)), clamped.  With row0 == 0 this is quantize_tile over the new
     rows."""
     codes = np.array(codes, dtype=np.int8, copy=True)
@@ -100,7 +110,7 @@ def append_tile(codes: np.ndarray, scale: np.float32, row0: int, new_rows: np.nd
     k = new_rows.shape[0]
     s_old = np.float32(scale) if row0 > 0 else np.float32(0)
     a = np.float32(np.max(np.abs(new_rows))) if k else np.float32(0)
-    s_new = max(s_old, np.float32(a / np.float32(127)))
+    s_new = max(s_old, np.float32(a / np.float32(qmax)))
     if s_new < SMALLEST_NORMAL:
         s_new = np.float32(0)
     if s_new == 0:
@@ -109,15 +119,15 @@ def append_tile(codes: np.ndarray, scale: np.float32, row0: int, new_rows: np.nd
     if s_new > s_old and row0 > 0:
         old = codes[:row0].astype(np.float32)
         vals = (old * s_old).astype(np.float32)
-        codes[:row0] = np.clip(np.rint((vals / s_new).astype(np.float32)), -127, 127).astype(np.int8)
+        codes[:row0] = np.clip(np.rint((vals / s_new).astype(np.float32)), -qmax, qmax).astype(np.int8)
     q = np.rint((new_rows / s_new).astype(np.float32))
-    codes[row0:row0 + k] = np.clip(q, -127, 127).astype(np.int8)
+    codes[row0:row0 + k] = np.clip(q, -qmax, qmax).astype(np.int8)
     return codes, np.float32(s_new)
 
 
 def reshape_and_cache_int8(key: np.ndarray, value: np.ndarray, k_codes: np.ndarray,
                            v_codes: np.ndarray, k_scale: np.ndarray, v_scale: np.ndarray,
-                           slots: Sequence[int], block_size: int):
+                           slots: Sequence[int], block_size: int, qmax: int = INT8_MAX):
     """Write new tokens' K/V ``[T, H, D]`` (float32, exactly as stored) into
     int8 pools ``[NB, H, BS, D]`` with per-(block, head) scales ``[NB, H]``,
     run by run (see runs_of): each run's block takes its rows below the
@@ -127,6 +137,55 @@ def reshape_and_cache_int8(key: np.ndarray, value: np.ndarray, k_codes: np.ndarr
     ks, vs = np.array(k_scale, np.float32, copy=True), np.array(v_scale, np.float32, copy=True)
     for t0, b, r0, k in runs_of(slots, block_size):
         for h in range(kc.shape[1]):
-            kc[b, h], ks[b, h] = append_tile(kc[b, h], ks[b, h], r0, key[t0:t0 + k, h])
-            vc[b, h], vs[b, h] = append_tile(vc[b, h], vs[b, h], r0, value[t0:t0 + k, h])
+            kc[b, h], ks[b, h] = append_tile(kc[b, h], ks[b, h], r0, key[t0:t0 + k, h], qmax)
+            vc[b, h], vs[b, h] = append_tile(vc[b, h], vs[b, h], r0, value[t0:t0 + k, h], qmax)
     return kc, vc, ks, vs
+
+
+# ------------------------------------------------------------------ 4-bit
+def pack_int4(codes: np.ndarray) -> np.ndarray:
+    """Codes in [-8, 7], last axis even, to bytes: element 2i in the low
+    nibble of byte i, element 2i + 1 in the high nibble (two's complement)."""
+    c = np.asarray(codes).astype(np.int64)
+    if c.shape[-1] % 2:
+        raise ValueError("4-bit rows need an even length")
+    if c.size and (c.min() < -8 or c.max() > 7):
+        raise ValueError("4-bit codes lie in [-8, 7]")
+    lo = c[..., 0::2] & 0xF
+    hi = c[..., 1::2] & 0xF
+    return (lo | (hi << 4)).astype(np.uint8)
+
+
+def unpack_int4(packed: np.ndarray) -> np.ndarray:
+    """Inverse of pack_int4: bytes [..., D/2] to int8 codes [..., D]."""
+    b = np.asarray(packed, dtype=np.uint8).astype(np.int64)
+    lo, hi = b & 0xF, b >> 4
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), np.int64)
+    out[..., 0::2] = np.where(lo >= 8, lo - 16, lo)
+    out[..., 1::2] = np.where(hi >= 8, hi - 16, hi)
+    return out.astype(np.int8)
+
+
+def quantize_blocks_int4(pool: np.ndarray, packed: np.ndarray, scales: np.ndarray,
+                         blocks: Sequence[int], filled: Sequence[int]):
+    """quantize_blocks with 4-bit codes: ``packed`` is the uint8 pool
+    ``[NB, H, BS, D/2]``; returns new packed codes and scales."""
+    codes, sc = quantize_blocks(pool, unpack_int4(packed), scales, blocks, filled, INT4_MAX)
+    return pack_int4(codes), sc
+
+
+def reshape_and_cache_int4(key: np.ndarray, value: np.ndarray, k_packed: np.ndarray,
+                           v_packed: np.ndarray, k_scale: np.ndarray, v_scale: np.ndarray,
+                           slots: Sequence[int], block_size: int):
+    """reshape_and_cache_int8 into packed 4-bit pools ``[NB, H, BS, D/2]``."""
+    kc, vc, ks, vs = reshape_and_cache_int8(key, value, unpack_int4(k_packed), unpack_int4(v_packed),
+                                            k_scale, v_scale, slots, block_size, INT4_MAX)
+    return pack_int4(kc), pack_int4(vc), ks, vs
+
+
+def kv_bytes_per_token(layers: int, kv_heads: int, head_dim: int, bits: int) -> float:
+    """Bytes one token's K and V take over all layers with ``bits``-bit
+    elements (scales not counted): 2 x layers x kv_heads x head_dim x bits / 8
+    (kongchang.com, 自回归生成的内存开销, with the element width of the
+    cnnetsun.cn compression table, §3.2)."""
+    return 2 * layers * kv_heads * head_dim * bits / 8
