@@ -22,7 +22,8 @@
  *     calls only enqueue work; they return before it finishes.
  *   - Device-side layouts (all contiguous, row-major):
  *       cache   k_cache / v_cache   [num_blocks][num_kv_heads][block_size][head_dim]
- *       scales  k_scale / v_scale   float [num_blocks][num_kv_heads] (int8 only)
+ *               (I4: [num_blocks][num_kv_heads][block_size][head_dim / 2] bytes)
+ *       scales  k_scale / v_scale   float [num_blocks][num_kv_heads] (I8 and I4 only)
  *       tables  block_tables        int32 [num_seqs][max_blocks_per_seq], -1 padded
  *     Position p of a sequence lives in block table[p / block_size] at row
  *     p % block_size ([cnnetsun] §2.1; [nxbn] §2.2); slot = block *
@@ -58,6 +59,9 @@ typedef int32_t pkv_dtype;
 #define PKV_F16 1
 #define PKV_BF16 2
 #define PKV_I8 3   /* KV storage only: symmetric codes with per-(block, kv head) fp32 scales */
+#define PKV_I4 4   /* KV storage only: 4-bit symmetric codes in [-7, 7], two per byte
+                      (element 2i in the low nibble of byte i, element 2i + 1 in the
+                      high nibble, two's complement), per-(block, kv head) fp32 scales */
 
 /* Decode kernel choice. */
 #define PKV_ALGO_AUTO 0
@@ -239,11 +243,28 @@ pkv_status pkv_reshape_and_cache_int8(const void* key, const void* value, pkv_dt
                                       int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                       void* stream);
 
+/* reshape_and_cache into 4-bit storage: pkv_reshape_and_cache_int8 with
+ * codes in [-7, 7] packed two per byte as PKV_I4 states; the grow-only
+ * scale becomes max(old scale, max|new rows| / 7), existing codes are
+ * re-encoded to [-7, 7] when it grows ([cnnetsun] §3.2 lists 4-bit KV).
+ *   k_codes, v_codes device uint8 [num_blocks][num_kv_heads][block_size]
+ *                  [head_dim / 2], 16-byte aligned
+ * Other arguments, validation and the one-run-per-block rule as for
+ * pkv_reshape_and_cache_int8.  head_dim must be a multiple of 32.
+ * Bit-exact against the float32 definition. */
+pkv_status pkv_reshape_and_cache_int4(const void* key, const void* value, pkv_dtype src_dtype,
+                                      uint8_t* k_codes, uint8_t* v_codes, float* k_scale,
+                                      float* v_scale, const int32_t* slot_mapping,
+                                      int32_t num_tokens, int64_t key_stride,
+                                      int64_t value_stride, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                      void* stream);
+
 /* ------------------------------------------------------------------------
  * copy_blocks (device): the data copy of copy-on-write ([kongchang] section
  * "KV Cache内存共享").  For each pair (src, dst): K[dst] = K[src],
- * V[dst] = V[src], and for I8 storage k_scale[dst] = k_scale[src], same for
- * v_scale (scales may be NULL otherwise).
+ * V[dst] = V[src], and for I8 and I4 storage k_scale[dst] = k_scale[src],
+ * same for v_scale (scales may be NULL otherwise).
  *   pairs   device int32[num_pairs][2].  Destinations must be distinct and
  *           never a source of the same call (validated with PKV_VALIDATE=1).
  * Bit-exact. */
@@ -257,13 +278,13 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* 
  * over PCIe from GPU memory to CPU memory and back when it resumes
  * ([kongchang] section "抢占与恢复机制"; cold pages may live in host memory,
  * [cnnetsun] §2.3).  For each pair (s, d): block d of the destination pool
- * receives block s of the source pool (K, V, and for I8 storage the
+ * receives block s of the source pool (K, V, and for I8 and I4 storage the
  * per-(block, kv head) scales); other destination blocks are unchanged.
  *   dst_*, src_*   pools [num_blocks][num_kv_heads][block_size][head_dim] in
  *                  `dtype`, each in device memory or in pinned host memory
  *                  (hipHostMalloc; pageable host memory works but copies
  *                  synchronously); the two pools never overlap
- *   *_scale        float [num_blocks][num_kv_heads], I8 only (else NULL)
+ *   *_scale        float [num_blocks][num_kv_heads], I8 and I4 only (else NULL)
  *   pairs          HOST int32[num_pairs][2] (source block, destination block);
  *                  always validated: ids inside their pools, destinations
  *                  distinct (INVALID otherwise, nothing copied)
@@ -335,6 +356,21 @@ pkv_status pkv_quantize_blocks(const void* src_k, const void* src_v, pkv_dtype s
                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                int32_t num_blocks, void* stream);
 
+/* 4-bit storage of whole blocks: pkv_quantize_blocks with codes in [-7, 7]
+ * and s = max|x| / 7 (float32), packed two per byte as PKV_I4 states.
+ * [cnnetsun] §3.2 lists 4-bit KV at an eighth of fp32's bytes.  Arguments
+ * as for pkv_quantize_blocks, except
+ *   dst_k, dst_v   device uint8 pools [num_blocks][num_kv_heads][block_size]
+ *                  [head_dim / 2], 4-byte aligned
+ * head_dim must be even and head_dim * source element size a multiple of 16
+ * bytes.  Bit-exact against the float32 definition; the pool serves decode
+ * with kv_dtype I4. */
+pkv_status pkv_quantize_blocks_int4(const void* src_k, const void* src_v, pkv_dtype src_dtype,
+                                    uint8_t* dst_k, uint8_t* dst_v, float* k_scale,
+                                    float* v_scale, const int32_t* blocks, const int32_t* filled,
+                                    int32_t num_listed, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, int32_t num_blocks, void* stream);
+
 /* ------------------------------------------------------------------------
  * Paged decode attention (device).  One query token per sequence, at
  * position context_lens[s] - 1, attends keys [0, context_lens[s]) (the
@@ -345,8 +381,9 @@ pkv_status pkv_quantize_blocks(const void* src_k, const void* src_v, pkv_dtype s
  *   out            device [num_seqs][num_q_heads][head_dim] in out_dtype
  *                  (F32, or the q dtype); rows with context 0 are zero.
  *   q              device [num_seqs][num_q_heads][head_dim], q_dtype F32/F16/BF16
- *   k_cache,v_cache device pool in kv_dtype: F32/F16/BF16 (same as q) or I8
- *                  with k_scale/v_scale device float[num_blocks][num_kv_heads]
+ *   k_cache,v_cache device pool in kv_dtype: F32/F16/BF16 (same as q), I8 or
+ *                  I4 with k_scale/v_scale device float[num_blocks][num_kv_heads];
+ *                  a stored element is code * scale of its (block, kv head)
  *   block_tables   device int32[num_seqs][max_blocks_per_seq]
  *   context_lens   device int32[num_seqs], each <= max_context_len
  *                  <= max_blocks_per_seq * block_size

@@ -15,7 +15,7 @@ import numpy as np
 
 from ._lib import (PKV_ALGO_AUTO, PKV_ALGO_MFMA, PKV_ALGO_WAVE, PKV_BF16, PKV_ERR_DEVICE,  # noqa
                    PKV_ERR_INTERNAL, PKV_ERR_INVALID, PKV_ERR_OUT_OF_BLOCKS, PKV_ERR_UNSUPPORTED,
-                   PKV_F16, PKV_F32, PKV_I8, PKV_OK, LIB_PATH, PkvBmStats, PkvError, PkvSwapStats,
+                   PKV_F16, PKV_F32, PKV_I4, PKV_I8, PKV_OK, LIB_PATH, PkvBmStats, PkvError, PkvSwapStats,
                    PkvOutOfBlocks, check, load)
 
 __all__ = [n for n in dir() if n.startswith("pkv_") or n.startswith("PKV_")]
@@ -176,12 +176,18 @@ def _torch():
 
 
 def _dtype_code(t) -> int:
+    """Storage code of a tensor; uint8 tensors are 4-bit pools (two codes a byte)."""
     torch = _torch()
     m = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16,
-         torch.int8: PKV_I8}
+         torch.int8: PKV_I8, torch.uint8: PKV_I4}
     if t.dtype not in m:
         raise TypeError(f"unsupported dtype {t.dtype}")
     return m[t.dtype]
+
+
+def _pool_head_dim(pool) -> int:
+    """head_dim of a pool [NB, Hkv, BS, D] (4-bit pools: [NB, Hkv, BS, D / 2] bytes)."""
+    return pool.shape[3] * (2 if _dtype_code(pool) == PKV_I4 else 1)
 
 
 def _dev(t, name: str, dtype=None):
@@ -223,17 +229,16 @@ def pkv_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=Non
         _stream(k_cache, stream)))
 
 
-def pkv_reshape_and_cache_int8(key, value, k_codes, v_codes, k_scale, v_scale, slot_mapping,
-                               stream=None) -> None:
-    """key/value [T, Hkv, D] (f32/f16/bf16, row stride from the tensor); int8
-    pools [NB, Hkv, BS, D] and float32 scales [NB, Hkv]."""
+def _reshape_and_cache_codes(fn, code_dtype, key, value, k_codes, v_codes, k_scale, v_scale,
+                             slot_mapping, stream):
     torch = _torch()
     T, hkv, d = key.shape
-    nb, hkv2, bs, d2 = k_codes.shape
+    nb, hkv2, bs, _ = k_codes.shape
+    if k_codes.dtype != code_dtype or v_codes.dtype != code_dtype:
+        raise TypeError(f"code pools must be {code_dtype}")
+    d2 = _pool_head_dim(k_codes)
     if (hkv, d) != (hkv2, d2) or value.shape != key.shape or v_codes.shape != k_codes.shape:
         raise ValueError("shape mismatch")
-    if k_codes.dtype != torch.int8 or v_codes.dtype != torch.int8:
-        raise TypeError("code pools must be int8")
     if k_scale.shape != (nb, hkv) or v_scale.shape != (nb, hkv):
         raise ValueError("scales must be [NB, Hkv]")
     for t, n in ((key, "key"), (value, "value")):
@@ -241,17 +246,34 @@ def pkv_reshape_and_cache_int8(key, value, k_codes, v_codes, k_scale, v_scale, s
             raise ValueError(f"{n} rows must be [Hkv, D] contiguous")
     if slot_mapping.shape != (T,):
         raise ValueError("slot_mapping must be [T]")
-    check(load().pkv_reshape_and_cache_int8(
+    check(fn(
         C.c_void_p(key.data_ptr()), C.c_void_p(value.data_ptr()), _dtype_code(key),
         _dev(k_codes, "k_codes"), _dev(v_codes, "v_codes"), _dev(k_scale, "k_scale", torch.float32),
         _dev(v_scale, "v_scale", torch.float32), _dev(slot_mapping, "slot_mapping", torch.int32), T,
         key.stride(0), value.stride(0), hkv, d, bs, nb, _stream(k_codes, stream)))
 
 
+def pkv_reshape_and_cache_int8(key, value, k_codes, v_codes, k_scale, v_scale, slot_mapping,
+                               stream=None) -> None:
+    """key/value [T, Hkv, D] (f32/f16/bf16, row stride from the tensor); int8
+    pools [NB, Hkv, BS, D] and float32 scales [NB, Hkv]."""
+    _reshape_and_cache_codes(load().pkv_reshape_and_cache_int8, _torch().int8, key, value,
+                             k_codes, v_codes, k_scale, v_scale, slot_mapping, stream)
+
+
+def pkv_reshape_and_cache_int4(key, value, k_codes, v_codes, k_scale, v_scale, slot_mapping,
+                               stream=None) -> None:
+    """key/value [T, Hkv, D] (f32/f16/bf16, row stride from the tensor); 4-bit
+    pools uint8 [NB, Hkv, BS, D / 2] and float32 scales [NB, Hkv]."""
+    _reshape_and_cache_codes(load().pkv_reshape_and_cache_int4, _torch().uint8, key, value,
+                             k_codes, v_codes, k_scale, v_scale, slot_mapping, stream)
+
+
 def pkv_copy_blocks(k_cache, v_cache, pairs, k_scale=None, v_scale=None, stream=None) -> None:
     """pairs: int32 [n, 2] device tensor of (src, dst)."""
     torch = _torch()
-    nb, hkv, bs, d = k_cache.shape
+    nb, hkv, bs, _ = k_cache.shape
+    d = _pool_head_dim(k_cache)
     n = pairs.shape[0] if pairs.dim() == 2 else 0
     check(load().pkv_copy_blocks(
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(k_scale, "k_scale", torch.float32),
@@ -288,7 +310,8 @@ def pkv_swap_blocks(dst_k, dst_v, src_k, src_v, pairs, dst_k_scale=None, dst_v_s
         if not (t.is_cuda or t.is_pinned()):
             raise ValueError(f"{n} must be a GPU tensor or pinned host memory")
     p = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
-    _, hkv, bs, d = src_k.shape
+    _, hkv, bs, _ = src_k.shape
+    d = _pool_head_dim(src_k)
     ptr = lambda t: None if t is None else C.c_void_p(t.data_ptr())
     dev = dst_k if dst_k.is_cuda else src_k
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -300,14 +323,14 @@ def pkv_swap_blocks(dst_k, dst_v, src_k, src_v, pairs, dst_k_scale=None, dst_v_s
         hkv, d, bs, _dtype_code(src_k), ptr(workspace), ws_len, _stream(dev, stream)))
 
 
-def pkv_quantize_blocks(src_k, src_v, dst_k, dst_v, k_scale, v_scale, blocks, filled,
-                        stream=None) -> None:
-    """src pools [NB, Hkv, BS, D] (f32/f16/bf16) -> int8 pools of the same shape
-    and float32 scales [NB, Hkv], for the listed blocks (int32 [n] device
-    tensors of block ids and filled row counts)."""
+def _quantize_blocks(fn, code_dtype, src_k, src_v, dst_k, dst_v, k_scale, v_scale, blocks,
+                     filled, stream):
     torch = _torch()
     nb, hkv, bs, d = src_k.shape
-    if src_v.shape != src_k.shape or dst_k.shape != src_k.shape or dst_v.shape != src_k.shape:
+    if dst_k.dtype != code_dtype or dst_v.dtype != code_dtype:
+        raise TypeError(f"code pools must be {code_dtype}")
+    if (src_v.shape != src_k.shape or dst_v.shape != dst_k.shape
+            or dst_k.shape[:3] != src_k.shape[:3] or _pool_head_dim(dst_k) != d):
         raise ValueError("pools must share one shape")
     if src_v.dtype != src_k.dtype:
         raise TypeError("src_k and src_v must share a dtype")
@@ -316,12 +339,29 @@ def pkv_quantize_blocks(src_k, src_v, dst_k, dst_v, k_scale, v_scale, blocks, fi
     n = blocks.shape[0]
     if filled.shape != (n,):
         raise ValueError("blocks and filled must have one entry per listed block")
-    check(load().pkv_quantize_blocks(
+    check(fn(
         _dev(src_k, "src_k"), _dev(src_v, "src_v"), _dtype_code(src_k),
-        _dev(dst_k, "dst_k", torch.int8), _dev(dst_v, "dst_v", torch.int8),
+        _dev(dst_k, "dst_k", code_dtype), _dev(dst_v, "dst_v", code_dtype),
         _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32),
         _dev(blocks, "blocks", torch.int32), _dev(filled, "filled", torch.int32), n, hkv, d, bs,
         nb, _stream(src_k, stream)))
+
+
+def pkv_quantize_blocks(src_k, src_v, dst_k, dst_v, k_scale, v_scale, blocks, filled,
+                        stream=None) -> None:
+    """src pools [NB, Hkv, BS, D] (f32/f16/bf16) -> int8 pools of the same shape
+    and float32 scales [NB, Hkv], for the listed blocks (int32 [n] device
+    tensors of block ids and filled row counts)."""
+    _quantize_blocks(load().pkv_quantize_blocks, _torch().int8, src_k, src_v, dst_k, dst_v,
+                     k_scale, v_scale, blocks, filled, stream)
+
+
+def pkv_quantize_blocks_int4(src_k, src_v, dst_k, dst_v, k_scale, v_scale, blocks, filled,
+                             stream=None) -> None:
+    """src pools [NB, Hkv, BS, D] (f32/f16/bf16) -> 4-bit pools uint8
+    [NB, Hkv, BS, D / 2] and float32 scales [NB, Hkv], for the listed blocks."""
+    _quantize_blocks(load().pkv_quantize_blocks_int4, _torch().uint8, src_k, src_v, dst_k, dst_v,
+                     k_scale, v_scale, blocks, filled, stream)
 
 
 def pkv_decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
@@ -334,7 +374,8 @@ def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, max_conte
                  partition_tokens, algo, k_scale, v_scale, workspace, stream):
     torch = _torch()
     S, hq, d = q.shape
-    nb, hkv, bs, d2 = k_cache.shape
+    nb, hkv, bs, _ = k_cache.shape
+    d2 = _pool_head_dim(k_cache)
     if out.shape != q.shape or d2 != d or v_cache.shape != k_cache.shape:
         raise ValueError("shape mismatch")
     if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
@@ -357,8 +398,10 @@ def pkv_paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_l
                                max_context_len: int, scale: float, partition_tokens: int = 0,
                                algo: int = PKV_ALGO_AUTO, k_scale=None, v_scale=None,
                                workspace=None, stream=None):
-    """out, q: [S, Hq, D]; caches [NB, Hkv, 16, D]; block_tables int32 [S, MB];
-    context_lens int32 [S].  Returns the workspace tensor used (or None)."""
+    """out, q: [S, Hq, D]; caches [NB, Hkv, BS, D] (int8 codes: int8; 4-bit
+    codes: uint8 [NB, Hkv, BS, D / 2], both with float32 scales [NB, Hkv]);
+    block_tables int32 [S, MB]; context_lens int32 [S].  Returns the
+    workspace tensor used (or None)."""
     args, ws = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens,
                             max_context_len, scale, partition_tokens, algo, k_scale, v_scale,
                             workspace, stream)
@@ -403,7 +446,8 @@ def pkv_paged_attention_prefill(out, q, k_cache, v_cache, block_tables, query_st
     Returns the workspace tensor used (or None)."""
     torch = _torch()
     Tq, hq, d = q.shape
-    nb, hkv, bs, d2 = k_cache.shape
+    nb, hkv, bs, _ = k_cache.shape
+    d2 = _pool_head_dim(k_cache)
     S = context_lens.shape[0]
     if out.shape != q.shape or d2 != d or query_start_loc.shape != (S + 1,):
         raise ValueError("shape mismatch")

@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
 PKV_OK, PKV_ERR_INVALID, PKV_ERR_OUT_OF_BLOCKS, PKV_ERR_UNSUPPORTED, PKV_ERR_DEVICE, \
     PKV_ERR_INTERNAL = range(6)
-PKV_F32, PKV_F16, PKV_BF16, PKV_I8 = range(4)
+PKV_F32, PKV_F16, PKV_BF16, PKV_I8, PKV_I4 = range(5)
 PKV_ALGO_AUTO, PKV_ALGO_WAVE, PKV_ALGO_MFMA = range(3)
 
 _i32, _i64, _f32, _sz, _vp = C.c_int32, C.c_int64, C.c_float, C.c_size_t, C.c_void_p
@@ -60,6 +60,8 @@ SIGNATURES = {
                                      _i32, _i32, _vp]),
     "pkv_reshape_and_cache_int8": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i64,
                                           _i64, _i32, _i32, _i32, _i32, _vp]),
+    "pkv_reshape_and_cache_int4": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i64,
+                                          _i64, _i32, _i32, _i32, _i32, _vp]),
     "pkv_copy_blocks": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pkv_swap_blocks": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _pi32, _i32,
                                _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
@@ -67,6 +69,8 @@ SIGNATURES = {
     "pkv_swap_stats_get": (_i32, [C.POINTER(PkvSwapStats), _i32]),
     "pkv_quantize_blocks": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                    _i32, _i32, _vp]),
+    "pkv_quantize_blocks_int4": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                        _i32, _i32, _i32, _vp]),
     "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pkv_paged_attention_decode": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp,
                                           _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,

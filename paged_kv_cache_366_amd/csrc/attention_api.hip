@@ -80,13 +80,13 @@ pkv_status check_common(const char* who, void* out, pkv_dtype out_dt, const void
                 who, max_ctx);
   if (q_dt != PKV_F32 && q_dt != PKV_F16 && q_dt != PKV_BF16)
     return fail(PKV_ERR_UNSUPPORTED, "%s: q dtype %s", who, dtype_name(q_dt));
-  if (kv_dt != q_dt && kv_dt != PKV_I8)
+  if (kv_dt != q_dt && !has_scales(kv_dt))
     return fail(PKV_ERR_UNSUPPORTED, "%s: kv dtype %s with q dtype %s", who, dtype_name(kv_dt),
                 dtype_name(q_dt));
   if (out_dt != PKV_F32 && out_dt != q_dt)
     return fail(PKV_ERR_UNSUPPORTED, "%s: out dtype must be f32 or the q dtype", who);
-  if (kv_dt == PKV_I8 && (!ks || !vs))
-    return fail(PKV_ERR_INVALID, "%s: int8 KV needs k_scale and v_scale", who);
+  if (has_scales(kv_dt) && (!ks || !vs))
+    return fail(PKV_ERR_INVALID, "%s: %s KV needs k_scale and v_scale", who, dtype_name(kv_dt));
   if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID, "%s: scale is not finite", who);
   if (S > 0 && (!out || !q || !kc || !vc || !tables || !lens))
     return fail(PKV_ERR_INVALID, "%s: NULL pointer", who);
@@ -165,8 +165,8 @@ pkv_status decode_impl(DecodePart which, void* out, pkv_dtype out_dt, const void
   a.q = q;
   a.kc = kc;
   a.vc = vc;
-  a.ks = kv_dt == PKV_I8 ? ks : nullptr;
-  a.vs = kv_dt == PKV_I8 ? vs : nullptr;
+  a.ks = has_scales(kv_dt) ? ks : nullptr;
+  a.vs = has_scales(kv_dt) ? vs : nullptr;
   a.tables = tables;
   a.lens = lens;
   a.qsl = nullptr;
@@ -307,8 +307,9 @@ pkv_status pkv_paged_attention_prefill(
       return fail(PKV_ERR_INVALID, "%s: bad query sizes", who);
     if (num_seqs > 0 && !query_start_loc)
       return fail(PKV_ERR_INVALID, "%s: query_start_loc is NULL", who);
-    if (kv_dtype == PKV_I8)
-      return fail(PKV_ERR_UNSUPPORTED, "%s: int8 KV is a decode-only storage here", who);
+    if (has_scales(kv_dtype))
+      return fail(PKV_ERR_UNSUPPORTED, "%s: %s KV is a decode-only storage here", who,
+                  dtype_name(kv_dtype));
     if (partition_tokens < 0 || partition_tokens % 16 != 0)
       return fail(PKV_ERR_INVALID, "%s: partition_tokens %d must be 0 or a multiple of 16", who,
                   partition_tokens);

@@ -11,6 +11,7 @@
 // kernel touches a slot or block outside the pool whatever the index arrays
 // hold.
 #include <atomic>
+#include <type_traits>
 #include <unordered_set>
 #include <vector>
 
@@ -80,12 +81,13 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
   }
 }
 
-// Int8 storage of whole blocks: one wavefront per (listed block, KV head,
-// K or V) tile.  The first pass takes max |x| over the filled rows, the
-// second writes the codes (from registers for tiles up to 4 KiB); every
-// step is the float32 arithmetic of the encoding: s = a / 127, code =
-// rint(x / s) clamped to [-127, 127], rows past the filled count 0, a
-// subnormal scale counting as zero.
+// Int8 and 4-bit storage of whole blocks: one wavefront per (listed block,
+// KV head, K or V) tile.  The first pass takes max |x| over the filled rows,
+// the second writes the codes (from registers for tiles up to 4 KiB); every
+// step is the float32 arithmetic of the encoding: s = a / Q, code =
+// rint(x / s) clamped to [-Q, Q] (Q = 127 for int8, 7 for 4-bit), rows past
+// the filled count 0, a subnormal scale counting as zero.  4-bit codes are
+// stored two per byte, element 2i in the low nibble.
 constexpr float kSmallestNormal = 1.17549435e-38f;
 
 __device__ __forceinline__ float wave_absmax(float v) {
@@ -94,10 +96,61 @@ __device__ __forceinline__ float wave_absmax(float v) {
   return v;
 }
 
-template <typename T>
+template <int BITS> constexpr float kCodeMax = BITS == 8 ? 127.f : 7.f;
+
+// The code of x under scale s > 0 (float32 division, ties to even).
+template <int BITS>
+__device__ __forceinline__ int encode_one(float x, float s) {
+  return static_cast<int>(fminf(fmaxf(rintf(x / s), -kCodeMax<BITS>), kCodeMax<BITS>));
+}
+
+// Stores E codes at d: one byte each, or two per byte (4-bit).
+template <int BITS, int E>
+__device__ __forceinline__ void store_codes(uint8_t* d, const int (&q)[E]) {
+  if constexpr (BITS == 8) {
+    int8_t b[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) b[e] = static_cast<int8_t>(q[e]);
+    if constexpr (E == 16) {
+      *reinterpret_cast<u32x4*>(d) = __builtin_bit_cast(u32x4, b);
+    } else if constexpr (E == 8) {
+      *reinterpret_cast<uint64_t*>(d) = __builtin_bit_cast(uint64_t, b);
+    } else {
+      static_assert(E == 4, "chunk");
+      *reinterpret_cast<uint32_t*>(d) = __builtin_bit_cast(uint32_t, b);
+    }
+  } else {
+    static_assert(BITS == 4, "code width");
+    uint8_t b[E / 2];
+#pragma unroll
+    for (int i = 0; i < E / 2; ++i)
+      b[i] = static_cast<uint8_t>((q[2 * i] & 15) | ((q[2 * i + 1] & 15) << 4));
+    if constexpr (E == 32) {
+      *reinterpret_cast<u32x4*>(d) = __builtin_bit_cast(u32x4, b);
+    } else if constexpr (E == 8) {
+      *reinterpret_cast<uint32_t*>(d) = __builtin_bit_cast(uint32_t, b);
+    } else {
+      static_assert(E == 4, "chunk");
+      *reinterpret_cast<uint16_t*>(d) = __builtin_bit_cast(uint16_t, b);
+    }
+  }
+}
+
+// The 128 / BITS codes of 16 stored bytes, widened exactly.
+template <int BITS>
+__device__ __forceinline__ void load_codes(const u32x4& w, float (&c)[128 / BITS]) {
+  const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+  constexpr int P = 32 / BITS;   // codes per dword
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int k = 0; k < P; ++k) c[P * i + k] = BITS == 8 ? i8_at(a[i], k) : i4_at(a[i], k);
+}
+
+template <typename T, int BITS>
 __global__ __launch_bounds__(kThreads) void quantize_blocks_kernel(
     const uint8_t* __restrict__ src_k, const uint8_t* __restrict__ src_v,
-    int8_t* __restrict__ dst_k, int8_t* __restrict__ dst_v, float* __restrict__ ks,
+    uint8_t* __restrict__ dst_k, uint8_t* __restrict__ dst_v, float* __restrict__ ks,
     float* __restrict__ vs, const int32_t* __restrict__ blocks,
     const int32_t* __restrict__ filled, int n, int hkv, int head_dim, int block_size,
     int num_blocks) {
@@ -114,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void quantize_blocks_kernel(
   const int64_t elems = static_cast<int64_t>(block_size) * head_dim;
   const int64_t tix = static_cast<int64_t>(b) * hkv + h;
   const uint8_t* src = (which ? src_v : src_k) + tix * elems * T::bytes;
-  int8_t* dst = (which ? dst_v : dst_k) + tix * elems;
+  uint8_t* dst = (which ? dst_v : dst_k) + tix * elems * BITS / 8;
   const int filled_chunks = f * head_dim / E;
   const int all_chunks = block_size * head_dim / E;
 
@@ -147,27 +200,21 @@ __global__ __launch_bounds__(kThreads) void quantize_blocks_kernel(
     }
   }
   amax = wave_absmax(amax);
-  float sc = amax / 127.f;
+  float sc = amax / kCodeMax<BITS>;
   if (!(sc >= kSmallestNormal)) sc = 0.f;
 
   auto encode = [&](int c, const u32x4& w) {
-    int8_t q[E];
+    int q[E];
     if (c < filled_chunks && sc > 0.f) {
       float x[E];
       Unpack<T>::run(w, x);
 #pragma unroll
-      for (int e = 0; e < E; ++e)
-        q[e] = static_cast<int8_t>(fminf(fmaxf(rintf(x[e] / sc), -127.f), 127.f));
+      for (int e = 0; e < E; ++e) q[e] = encode_one<BITS>(x[e], sc);
     } else {
 #pragma unroll
       for (int e = 0; e < E; ++e) q[e] = 0;
     }
-    int8_t* d = dst + static_cast<int64_t>(c) * E;
-    if constexpr (E == 8) {
-      *reinterpret_cast<uint64_t*>(d) = __builtin_bit_cast(uint64_t, q);
-    } else {
-      *reinterpret_cast<uint32_t*>(d) = __builtin_bit_cast(uint32_t, q);
-    }
+    store_codes<BITS, E>(dst + static_cast<int64_t>(c) * E * BITS / 8, q);
   };
   if (keep) {
 #pragma unroll
@@ -211,19 +258,20 @@ __global__ __launch_bounds__(kThreads) void copy_list_kernel(
   }
 }
 
-// Quantise-on-write: new tokens' K/V rows go into int8 pools with one scale
-// per (block, KV head).  The slot mapping splits into runs (consecutive
-// tokens whose slots are consecutive rows of one block); the first token of
-// a run leads it, and one wavefront per (run, head, K or V) takes the run's
-// block as written below the run's first row.  The scale only grows: to
-// max(old scale, max|new rows| / 127); when it grows, each existing code is
-// re-encoded from its value (code x old scale / new scale, rounded to
-// nearest even), and the new rows are encoded with the new scale.  Writing
-// a whole block in one run is the whole-block encoder exactly.
-template <typename T>
-__global__ __launch_bounds__(kThreads) void reshape_and_cache_int8_kernel(
+// Quantise-on-write: new tokens' K/V rows go into int8 or 4-bit pools with
+// one scale per (block, KV head).  The slot mapping splits into runs
+// (consecutive tokens whose slots are consecutive rows of one block); the
+// first token of a run leads it, and one wavefront per (run, head, K or V)
+// takes the run's block as written below the run's first row.  The scale
+// only grows: to max(old scale, max|new rows| / Q); when it grows, each
+// existing code is re-encoded from its value (code x old scale / new scale,
+// rounded to nearest even), and the new rows are encoded with the new
+// scale.  Writing a whole block in one run is the whole-block encoder
+// exactly.
+template <typename T, int BITS>
+__global__ __launch_bounds__(kThreads) void reshape_and_cache_quant_kernel(
     const uint8_t* __restrict__ key, const uint8_t* __restrict__ value,
-    int8_t* __restrict__ kc, int8_t* __restrict__ vc, float* __restrict__ ks,
+    uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, float* __restrict__ ks,
     float* __restrict__ vs, const int32_t* __restrict__ slots, int n, int64_t key_stride_b,
     int64_t value_stride_b, int hkv, int head_dim, int block_size, int64_t num_slots) {
   constexpr int E = 16 / T::bytes;                 // elements per 16-byte chunk
@@ -242,7 +290,8 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_int8_kernel(
   while (t + k < n && k < block_size - r0 && slots[t + k] == slot + k) ++k;
 
   const int64_t tix = b * hkv + h;
-  int8_t* dst = (which ? vc : kc) + tix * block_size * head_dim;
+  const int row_b = head_dim * BITS / 8;           // bytes of one stored row
+  uint8_t* dst = (which ? vc : kc) + tix * block_size * row_b;
   float* scale = which ? vs : ks;
   const uint8_t* src = (which ? value : key) + static_cast<int64_t>(h) * head_dim * T::bytes;
   const int64_t stride = which ? value_stride_b : key_stride_b;
@@ -258,44 +307,34 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_int8_kernel(
   }
   amax = wave_absmax(amax);
   const float s_old = r0 > 0 ? scale[tix] : 0.f;
-  float s_new = fmaxf(s_old, amax / 127.f);
+  float s_new = fmaxf(s_old, amax / kCodeMax<BITS>);
   if (!(s_new >= kSmallestNormal)) s_new = 0.f;
 
   if (s_new > s_old && r0 > 0) {
-    // existing rows: 16 codes per lane step
-    for (int o = lane * 16; o < r0 * head_dim; o += 64 * 16) {
-      struct Codes16 {
-        int8_t v[16];
-      };
-      const Codes16 old = __builtin_bit_cast(Codes16, *reinterpret_cast<const u32x4*>(dst + o));
-      int8_t q[16];
+    // existing rows: 16 bytes (128 / BITS codes) per lane step
+    constexpr int N = 128 / BITS;
+    for (int o = lane * 16; o < r0 * row_b; o += 64 * 16) {
+      float old[N];
+      load_codes<BITS>(*reinterpret_cast<const u32x4*>(dst + o), old);
+      int q[N];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float y = static_cast<float>(old.v[e]) * s_old;
-        q[e] = static_cast<int8_t>(fminf(fmaxf(rintf(y / s_new), -127.f), 127.f));
-      }
-      *reinterpret_cast<u32x4*>(dst + o) = __builtin_bit_cast(u32x4, q);
+      for (int e = 0; e < N; ++e) q[e] = encode_one<BITS>(old[e] * s_old, s_new);
+      store_codes<BITS, N>(dst + o, q);
     }
   }
   for (int c = lane; c < k * ch; c += 64) {
     const int i = c / ch;
-    int8_t q[E];
+    int q[E];
     if (s_new > 0.f) {
       float x[E];
       Unpack<T>::run(*reinterpret_cast<const u32x4*>(src + (t + i) * stride + (c % ch) * 16), x);
 #pragma unroll
-      for (int e = 0; e < E; ++e)
-        q[e] = static_cast<int8_t>(fminf(fmaxf(rintf(x[e] / s_new), -127.f), 127.f));
+      for (int e = 0; e < E; ++e) q[e] = encode_one<BITS>(x[e], s_new);
     } else {
 #pragma unroll
       for (int e = 0; e < E; ++e) q[e] = 0;
     }
-    int8_t* d = dst + static_cast<int64_t>(r0 + i) * head_dim + (c % ch) * E;
-    if constexpr (E == 8) {
-      *reinterpret_cast<uint64_t*>(d) = __builtin_bit_cast(uint64_t, q);
-    } else {
-      *reinterpret_cast<uint32_t*>(d) = __builtin_bit_cast(uint32_t, q);
-    }
+    store_codes<BITS, E>(dst + static_cast<int64_t>(r0 + i) * row_b + (c % ch) * E * BITS / 8, q);
   }
   if (lane == 0) scale[tix] = s_new;
 }
@@ -360,72 +399,182 @@ extern "C" pkv_status pkv_reshape_and_cache(const void* key, const void* value, 
   })
 }
 
+namespace {
+
+// Quantise-on-write into int8 (BITS 8) or 4-bit (BITS 4) pools.
+pkv_status reshape_and_cache_quant(const char* who, int bits, const void* key, const void* value,
+                                   pkv_dtype src_dtype, uint8_t* k_codes, uint8_t* v_codes,
+                                   float* k_scale, float* v_scale, const int32_t* slot_mapping,
+                                   int32_t num_tokens, int64_t key_stride, int64_t value_stride,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int32_t num_blocks, void* stream) {
+  if (src_dtype != PKV_F32 && src_dtype != PKV_F16 && src_dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: source dtype %s (f32, f16 or bf16)", who,
+                dtype_name(src_dtype));
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      num_blocks <= 0)
+    return fail(PKV_ERR_INVALID, "%s: bad sizes", who);
+  // a stored row is whole 16-byte chunks
+  const int dim_step = bits == 8 ? 16 : 32;
+  if (head_dim % dim_step != 0)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: head_dim must be a multiple of %d", who, dim_step);
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !k_codes || !v_codes || !k_scale || !v_scale || !slot_mapping)
+    return fail(PKV_ERR_INVALID, "%s: NULL pointer", who);
+  const int eb = dtype_bytes(src_dtype);
+  if (key_stride == 0) key_stride = static_cast<int64_t>(num_kv_heads) * head_dim;
+  if (value_stride == 0) value_stride = static_cast<int64_t>(num_kv_heads) * head_dim;
+  if (key_stride < static_cast<int64_t>(num_kv_heads) * head_dim ||
+      value_stride < static_cast<int64_t>(num_kv_heads) * head_dim)
+    return fail(PKV_ERR_INVALID, "%s: row stride shorter than a row", who);
+  if ((key_stride * eb) % 16 || (value_stride * eb) % 16 || !aligned(key, 16) ||
+      !aligned(value, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16))
+    return fail(PKV_ERR_INVALID, "%s: pointers and strides must be 16-byte aligned", who);
+  const int64_t num_slots = static_cast<int64_t>(num_blocks) * block_size;
+  if (deep_validation()) {
+    std::vector<int32_t> s;
+    pkv_status st = fetch_i32(slot_mapping, num_tokens, stream, s);
+    if (st) return st;
+    std::unordered_set<int32_t> seen, run_blocks;
+    for (int32_t i = 0; i < num_tokens; ++i) {
+      if (s[i] < 0) continue;
+      if (s[i] >= num_slots)
+        return fail(PKV_ERR_INVALID, "slot_mapping[%d] = %d outside the pool (%lld slots)", i,
+                    s[i], (long long)num_slots);
+      if (!seen.insert(s[i]).second)
+        return fail(PKV_ERR_INVALID, "slot %d appears twice in slot_mapping", s[i]);
+      const bool leads = !(i > 0 && s[i] % block_size > 0 && s[i - 1] == s[i] - 1);
+      if (leads && !run_blocks.insert(s[i] / block_size).second)
+        return fail(PKV_ERR_INVALID, "%s: block %d gets two runs of rows in one call", who,
+                    s[i] / block_size);
+    }
+  }
+  const int64_t waves = static_cast<int64_t>(num_tokens) * num_kv_heads * 2;
+  const int64_t wgs = (waves + kThreads / 64 - 1) / (kThreads / 64);
+  if (wgs > 0x7fffffff) return fail(PKV_ERR_UNSUPPORTED, "%s: too many tokens", who);
+  auto launch = [&](auto tag, auto width) {
+    using T = decltype(tag);
+    hipLaunchKernelGGL((reshape_and_cache_quant_kernel<T, decltype(width)::value>),
+                       dim3(static_cast<unsigned>(wgs)), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const uint8_t*>(key),
+                       static_cast<const uint8_t*>(value), k_codes, v_codes, k_scale, v_scale,
+                       slot_mapping, num_tokens, key_stride * eb, value_stride * eb,
+                       num_kv_heads, head_dim, block_size, num_slots);
+  };
+  auto by_source = [&](auto width) {
+    if (src_dtype == PKV_BF16)
+      launch(BF16{}, width);
+    else if (src_dtype == PKV_F16)
+      launch(F16{}, width);
+    else
+      launch(F32{}, width);
+  };
+  if (bits == 8)
+    by_source(std::integral_constant<int, 8>{});
+  else
+    by_source(std::integral_constant<int, 4>{});
+  PKV_LAUNCH_CHECK(who);
+  return PKV_OK;
+}
+
+// Whole-block encoding into int8 (BITS 8) or 4-bit (BITS 4) pools.
+pkv_status quantize_blocks_impl(const char* who, int bits, const void* src_k, const void* src_v,
+                                pkv_dtype src_dtype, uint8_t* dst_k, uint8_t* dst_v,
+                                float* k_scale, float* v_scale, const int32_t* blocks,
+                                const int32_t* filled, int32_t num_listed, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                void* stream) {
+  if (src_dtype != PKV_F32 && src_dtype != PKV_F16 && src_dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: source dtype %s (f32, f16 or bf16)", who,
+                dtype_name(src_dtype));
+  if (num_listed < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      num_blocks <= 0)
+    return fail(PKV_ERR_INVALID, "%s: bad sizes", who);
+  if (num_listed == 0) return PKV_OK;
+  if (!src_k || !src_v || !dst_k || !dst_v || !k_scale || !v_scale || !blocks || !filled)
+    return fail(PKV_ERR_INVALID, "%s: NULL pointer", who);
+  const int eb = dtype_bytes(src_dtype);
+  if ((head_dim * eb) % 16 != 0)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: head_dim * element size must be a multiple of 16",
+                who);
+  // a 16-byte source chunk becomes 8 (16-bit source) or 4 (fp32) int8
+  // codes, or half as many bytes of 4-bit codes
+  const size_t dst_align = static_cast<size_t>(16 / eb) * bits / 8;
+  if (!aligned(src_k, 16) || !aligned(src_v, 16) || !aligned(dst_k, dst_align) ||
+      !aligned(dst_v, dst_align))
+    return fail(PKV_ERR_INVALID, "%s: pools must be 16-byte (source) / %zu-byte (codes) aligned",
+                who, dst_align);
+  if (static_cast<int64_t>(num_listed) * num_kv_heads * 2 > 0x7fffffffLL)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: too many tiles", who);
+  if (deep_validation()) {
+    std::vector<int32_t> bl, fl;
+    pkv_status st = fetch_i32(blocks, num_listed, stream, bl);
+    if (st) return st;
+    st = fetch_i32(filled, num_listed, stream, fl);
+    if (st) return st;
+    std::unordered_set<int32_t> seen;
+    for (int32_t i = 0; i < num_listed; ++i) {
+      if (bl[i] < 0 || bl[i] >= num_blocks)
+        return fail(PKV_ERR_INVALID, "%s: blocks[%d] = %d outside the pool", who, i, bl[i]);
+      if (fl[i] < 0 || fl[i] > block_size)
+        return fail(PKV_ERR_INVALID, "%s: filled[%d] = %d outside [0, %d]", who, i, fl[i],
+                    block_size);
+      if (!seen.insert(bl[i]).second)
+        return fail(PKV_ERR_INVALID, "%s: block %d listed twice", who, bl[i]);
+    }
+  }
+  const int64_t tiles = static_cast<int64_t>(num_listed) * num_kv_heads * 2;
+  const dim3 grid(static_cast<unsigned>((tiles + 3) / 4));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint8_t* sk = static_cast<const uint8_t*>(src_k);
+  const uint8_t* sv = static_cast<const uint8_t*>(src_v);
+  auto launch = [&](auto tag, auto width) {
+    hipLaunchKernelGGL((quantize_blocks_kernel<decltype(tag), decltype(width)::value>), grid,
+                       dim3(kThreads), 0, st, sk, sv, dst_k, dst_v, k_scale, v_scale, blocks,
+                       filled, num_listed, num_kv_heads, head_dim, block_size, num_blocks);
+  };
+  auto by_source = [&](auto width) {
+    if (src_dtype == PKV_BF16)
+      launch(BF16{}, width);
+    else if (src_dtype == PKV_F16)
+      launch(F16{}, width);
+    else
+      launch(F32{}, width);
+  };
+  if (bits == 8)
+    by_source(std::integral_constant<int, 8>{});
+  else
+    by_source(std::integral_constant<int, 4>{});
+  PKV_LAUNCH_CHECK(who);
+  return PKV_OK;
+}
+
+}  // namespace
+
 extern "C" pkv_status pkv_reshape_and_cache_int8(
     const void* key, const void* value, pkv_dtype src_dtype, int8_t* k_codes, int8_t* v_codes,
     float* k_scale, float* v_scale, const int32_t* slot_mapping, int32_t num_tokens,
     int64_t key_stride, int64_t value_stride, int32_t num_kv_heads, int32_t head_dim,
     int32_t block_size, int32_t num_blocks, void* stream) {
   PKV_GUARD({
-    const char* who = "reshape_and_cache_int8";
-    if (src_dtype != PKV_F32 && src_dtype != PKV_F16 && src_dtype != PKV_BF16)
-      return fail(PKV_ERR_UNSUPPORTED, "%s: source dtype %s (f32, f16 or bf16)", who,
-                  dtype_name(src_dtype));
-    if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
-        num_blocks <= 0)
-      return fail(PKV_ERR_INVALID, "%s: bad sizes", who);
-    if (head_dim % 16 != 0)
-      return fail(PKV_ERR_UNSUPPORTED, "%s: head_dim must be a multiple of 16", who);
-    if (num_tokens == 0) return PKV_OK;
-    if (!key || !value || !k_codes || !v_codes || !k_scale || !v_scale || !slot_mapping)
-      return fail(PKV_ERR_INVALID, "%s: NULL pointer", who);
-    const int eb = dtype_bytes(src_dtype);
-    if (key_stride == 0) key_stride = static_cast<int64_t>(num_kv_heads) * head_dim;
-    if (value_stride == 0) value_stride = static_cast<int64_t>(num_kv_heads) * head_dim;
-    if (key_stride < static_cast<int64_t>(num_kv_heads) * head_dim ||
-        value_stride < static_cast<int64_t>(num_kv_heads) * head_dim)
-      return fail(PKV_ERR_INVALID, "%s: row stride shorter than a row", who);
-    if ((key_stride * eb) % 16 || (value_stride * eb) % 16 || !aligned(key, 16) ||
-        !aligned(value, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16))
-      return fail(PKV_ERR_INVALID, "%s: pointers and strides must be 16-byte aligned", who);
-    const int64_t num_slots = static_cast<int64_t>(num_blocks) * block_size;
-    if (deep_validation()) {
-      std::vector<int32_t> s;
-      pkv_status st = fetch_i32(slot_mapping, num_tokens, stream, s);
-      if (st) return st;
-      std::unordered_set<int32_t> seen, run_blocks;
-      for (int32_t i = 0; i < num_tokens; ++i) {
-        if (s[i] < 0) continue;
-        if (s[i] >= num_slots)
-          return fail(PKV_ERR_INVALID, "slot_mapping[%d] = %d outside the pool (%lld slots)", i,
-                      s[i], (long long)num_slots);
-        if (!seen.insert(s[i]).second)
-          return fail(PKV_ERR_INVALID, "slot %d appears twice in slot_mapping", s[i]);
-        const bool leads = !(i > 0 && s[i] % block_size > 0 && s[i - 1] == s[i] - 1);
-        if (leads && !run_blocks.insert(s[i] / block_size).second)
-          return fail(PKV_ERR_INVALID, "%s: block %d gets two runs of rows in one call", who,
-                      s[i] / block_size);
-      }
-    }
-    const int64_t waves = static_cast<int64_t>(num_tokens) * num_kv_heads * 2;
-    const int64_t wgs = (waves + kThreads / 64 - 1) / (kThreads / 64);
-    if (wgs > 0x7fffffff) return fail(PKV_ERR_UNSUPPORTED, "%s: too many tokens", who);
-    auto launch = [&](auto tag) {
-      using T = decltype(tag);
-      hipLaunchKernelGGL(reshape_and_cache_int8_kernel<T>, dim3(static_cast<unsigned>(wgs)),
-                         dim3(kThreads), 0, static_cast<hipStream_t>(stream),
-                         static_cast<const uint8_t*>(key), static_cast<const uint8_t*>(value),
-                         k_codes, v_codes, k_scale, v_scale, slot_mapping, num_tokens,
-                         key_stride * eb, value_stride * eb, num_kv_heads, head_dim, block_size,
-                         num_slots);
-    };
-    if (src_dtype == PKV_BF16)
-      launch(BF16{});
-    else if (src_dtype == PKV_F16)
-      launch(F16{});
-    else
-      launch(F32{});
-    PKV_LAUNCH_CHECK("reshape_and_cache_int8");
-    return PKV_OK;
+    return reshape_and_cache_quant("reshape_and_cache_int8", 8, key, value, src_dtype,
+                                   reinterpret_cast<uint8_t*>(k_codes),
+                                   reinterpret_cast<uint8_t*>(v_codes), k_scale, v_scale,
+                                   slot_mapping, num_tokens, key_stride, value_stride,
+                                   num_kv_heads, head_dim, block_size, num_blocks, stream);
+  })
+}
+
+extern "C" pkv_status pkv_reshape_and_cache_int4(
+    const void* key, const void* value, pkv_dtype src_dtype, uint8_t* k_codes, uint8_t* v_codes,
+    float* k_scale, float* v_scale, const int32_t* slot_mapping, int32_t num_tokens,
+    int64_t key_stride, int64_t value_stride, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t num_blocks, void* stream) {
+  PKV_GUARD({
+    return reshape_and_cache_quant("reshape_and_cache_int4", 4, key, value, src_dtype, k_codes,
+                                   v_codes, k_scale, v_scale, slot_mapping, num_tokens,
+                                   key_stride, value_stride, num_kv_heads, head_dim, block_size,
+                                   num_blocks, stream);
   })
 }
 
@@ -441,10 +590,14 @@ extern "C" pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, float* k_sca
       return fail(PKV_ERR_INVALID, "copy_blocks: bad sizes");
     if (num_pairs == 0) return PKV_OK;
     if (!k_cache || !v_cache || !pairs) return fail(PKV_ERR_INVALID, "copy_blocks: NULL pointer");
-    if (dtype == PKV_I8 && (!k_scale || !v_scale))
-      return fail(PKV_ERR_INVALID, "copy_blocks: int8 storage needs k_scale and v_scale");
+    if (has_scales(dtype) && (!k_scale || !v_scale))
+      return fail(PKV_ERR_INVALID, "copy_blocks: %s storage needs k_scale and v_scale",
+                  dtype_name(dtype));
+    if (dtype == PKV_I4 && head_dim % 2)
+      return fail(PKV_ERR_INVALID, "copy_blocks: 4-bit rows need an even head_dim");
     if (num_kv_heads > 256) return fail(PKV_ERR_UNSUPPORTED, "copy_blocks: > 256 kv heads");
-    const int64_t block_bytes = static_cast<int64_t>(num_kv_heads) * block_size * head_dim * eb;
+    const int64_t block_bytes =
+        static_cast<int64_t>(num_kv_heads) * block_size * row_bytes(dtype, head_dim);
     if (block_bytes % 16 || !aligned(k_cache, 16) || !aligned(v_cache, 16))
       return fail(PKV_ERR_INVALID, "copy_blocks: blocks must be 16-byte multiples and aligned");
     if (deep_validation()) {
@@ -470,7 +623,7 @@ extern "C" pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, float* k_sca
     hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, 2, static_cast<unsigned>(chunks)),
                        dim3(kThreads), 0, static_cast<hipStream_t>(stream),
                        static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache),
-                       dtype == PKV_I8 ? k_scale : nullptr, dtype == PKV_I8 ? v_scale : nullptr,
+                       has_scales(dtype) ? k_scale : nullptr, has_scales(dtype) ? v_scale : nullptr,
                        pairs, block_bytes, num_kv_heads, num_blocks);
     PKV_LAUNCH_CHECK("copy_blocks");
     return PKV_OK;
@@ -484,60 +637,25 @@ extern "C" pkv_status pkv_quantize_blocks(const void* src_k, const void* src_v,
                                           int32_t num_kv_heads, int32_t head_dim,
                                           int32_t block_size, int32_t num_blocks, void* stream) {
   PKV_GUARD({
-    const char* who = "quantize_blocks";
-    if (src_dtype != PKV_F32 && src_dtype != PKV_F16 && src_dtype != PKV_BF16)
-      return fail(PKV_ERR_UNSUPPORTED, "%s: source dtype %s (f32, f16 or bf16)", who,
-                  dtype_name(src_dtype));
-    if (num_listed < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
-        num_blocks <= 0)
-      return fail(PKV_ERR_INVALID, "%s: bad sizes", who);
-    if (num_listed == 0) return PKV_OK;
-    if (!src_k || !src_v || !dst_k || !dst_v || !k_scale || !v_scale || !blocks || !filled)
-      return fail(PKV_ERR_INVALID, "%s: NULL pointer", who);
-    const int eb = dtype_bytes(src_dtype);
-    if ((head_dim * eb) % 16 != 0)
-      return fail(PKV_ERR_UNSUPPORTED, "%s: head_dim * element size must be a multiple of 16",
-                  who);
-    if (!aligned(src_k, 16) || !aligned(src_v, 16) || !aligned(dst_k, 8) || !aligned(dst_v, 8))
-      return fail(PKV_ERR_INVALID, "%s: pools must be 16-byte (source) / 8-byte (int8) aligned",
-                  who);
-    if (static_cast<int64_t>(num_listed) * num_kv_heads * 2 > 0x7fffffffLL)
-      return fail(PKV_ERR_UNSUPPORTED, "%s: too many tiles", who);
-    if (deep_validation()) {
-      std::vector<int32_t> bl, fl;
-      pkv_status st = fetch_i32(blocks, num_listed, stream, bl);
-      if (st) return st;
-      st = fetch_i32(filled, num_listed, stream, fl);
-      if (st) return st;
-      std::unordered_set<int32_t> seen;
-      for (int32_t i = 0; i < num_listed; ++i) {
-        if (bl[i] < 0 || bl[i] >= num_blocks)
-          return fail(PKV_ERR_INVALID, "%s: blocks[%d] = %d outside the pool", who, i, bl[i]);
-        if (fl[i] < 0 || fl[i] > block_size)
-          return fail(PKV_ERR_INVALID, "%s: filled[%d] = %d outside [0, %d]", who, i, fl[i],
-                      block_size);
-        if (!seen.insert(bl[i]).second)
-          return fail(PKV_ERR_INVALID, "%s: block %d listed twice", who, bl[i]);
-      }
-    }
-    const int64_t tiles = static_cast<int64_t>(num_listed) * num_kv_heads * 2;
-    const dim3 grid(static_cast<unsigned>((tiles + 3) / 4));
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    const uint8_t* sk = static_cast<const uint8_t*>(src_k);
-    const uint8_t* sv = static_cast<const uint8_t*>(src_v);
-    auto launch = [&](auto tag) {
-      hipLaunchKernelGGL(quantize_blocks_kernel<decltype(tag)>, grid, dim3(kThreads), 0, st, sk,
-                         sv, dst_k, dst_v, k_scale, v_scale, blocks, filled, num_listed,
-                         num_kv_heads, head_dim, block_size, num_blocks);
-    };
-    if (src_dtype == PKV_BF16)
-      launch(BF16{});
-    else if (src_dtype == PKV_F16)
-      launch(F16{});
-    else
-      launch(F32{});
-    PKV_LAUNCH_CHECK("quantize_blocks");
-    return PKV_OK;
+    return quantize_blocks_impl("quantize_blocks", 8, src_k, src_v, src_dtype,
+                                reinterpret_cast<uint8_t*>(dst_k),
+                                reinterpret_cast<uint8_t*>(dst_v), k_scale, v_scale, blocks,
+                                filled, num_listed, num_kv_heads, head_dim, block_size,
+                                num_blocks, stream);
+  })
+}
+
+extern "C" pkv_status pkv_quantize_blocks_int4(const void* src_k, const void* src_v,
+                                               pkv_dtype src_dtype, uint8_t* dst_k,
+                                               uint8_t* dst_v, float* k_scale, float* v_scale,
+                                               const int32_t* blocks, const int32_t* filled,
+                                               int32_t num_listed, int32_t num_kv_heads,
+                                               int32_t head_dim, int32_t block_size,
+                                               int32_t num_blocks, void* stream) {
+  PKV_GUARD({
+    return quantize_blocks_impl("quantize_blocks_int4", 4, src_k, src_v, src_dtype, dst_k, dst_v,
+                                k_scale, v_scale, blocks, filled, num_listed, num_kv_heads,
+                                head_dim, block_size, num_blocks, stream);
   })
 }
 
@@ -577,8 +695,8 @@ extern "C" size_t pkv_swap_workspace_bytes(int32_t max_pairs, int32_t num_kv_hea
   const int eb = dtype_bytes(dtype);
   if (max_pairs <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || eb == 0)
     return 0;
-  const size_t bb = static_cast<size_t>(num_kv_heads) * block_size * head_dim * eb;
-  const size_t per = 2 * bb + (dtype == PKV_I8 ? 2 * sizeof(float) * num_kv_heads : 0);
+  const size_t bb = static_cast<size_t>(num_kv_heads) * block_size * row_bytes(dtype, head_dim);
+  const size_t per = 2 * bb + (has_scales(dtype) ? 2 * sizeof(float) * num_kv_heads : 0);
   return 256 + static_cast<size_t>(max_pairs) * (sizeof(int32_t) + per + 64);
 }
 
@@ -600,9 +718,12 @@ extern "C" pkv_status pkv_swap_blocks(void* dst_k, void* dst_v, float* dst_k_sca
     if (num_pairs == 0) return PKV_OK;
     if (!dst_k || !dst_v || !src_k || !src_v || !pairs)
       return fail(PKV_ERR_INVALID, "%s: NULL pointer", who);
-    const bool scales = dtype == PKV_I8;
+    const bool scales = has_scales(dtype);
     if (scales && (!dst_k_scale || !dst_v_scale || !src_k_scale || !src_v_scale))
-      return fail(PKV_ERR_INVALID, "%s: int8 pools need all four scale arrays", who);
+      return fail(PKV_ERR_INVALID, "%s: %s pools need all four scale arrays", who,
+                  dtype_name(dtype));
+    if (dtype == PKV_I4 && head_dim % 2)
+      return fail(PKV_ERR_INVALID, "%s: 4-bit rows need an even head_dim", who);
     std::unordered_set<int32_t> seen_dst;
     for (int32_t i = 0; i < num_pairs; ++i) {
       const int32_t s_ = pairs[2 * i], d_ = pairs[2 * i + 1];
@@ -611,7 +732,7 @@ extern "C" pkv_status pkv_swap_blocks(void* dst_k, void* dst_v, float* dst_k_sca
       if (!seen_dst.insert(d_).second)
         return fail(PKV_ERR_INVALID, "%s: block %d is the destination of two pairs", who, d_);
     }
-    const size_t bb = static_cast<size_t>(num_kv_heads) * block_size * head_dim * eb;
+    const size_t bb = static_cast<size_t>(num_kv_heads) * block_size * row_bytes(dtype, head_dim);
     const size_t sb = static_cast<size_t>(num_kv_heads) * sizeof(float);
     if (bb % 16 != 0 || !aligned(dst_k, 16) || !aligned(dst_v, 16) || !aligned(src_k, 16) ||
         !aligned(src_v, 16))

@@ -1,6 +1,6 @@
 // Paged decode attention on the matrix cores, for query-head groups that
 // share one KV head (grouped-query attention) and 16-bit queries; KV in the
-// same 16-bit type or int8 with per-(block, KV head) scales.
+// same 16-bit type, or int8 or 4-bit codes with per-(block, KV head) scales.
 //
 // Same computation as the wavefront kernel (cnnetsun.cn "别再让GPU内存拖后腿了…"
 // §3.1: per-block scores, one softmax, weighted sum of value rows; int8 storage
@@ -26,6 +26,11 @@
 //       product j sees elements m*D/16 + j of those four rows.  The
 //       accumulator of head h stays in lanes h, so the rescale by the softmax
 //       correction is lane-local.
+//   4-bit keys: the contraction order over head_dim is free, so lane
+//   (t, kg) reads elements kg*D/4 .. +D/4-1 of key row t in one load (16
+//   bytes at head_dim 128) and Q^T takes the same elements; 4-bit values
+//   are read 4 (or 2) bytes per row.  Codes widen exactly to 16-bit
+//   operands (a signed bit-field extract and a convert each).
 //   Weights enter the product as a bf16 (or f16) pair hi + lo, hi = p rounded
 //   and lo = p - hi rounded, which keeps about 16 mantissa bits at the cost
 //   of a second MFMA per product; decode is HBM-bound, so it is free.
@@ -46,12 +51,15 @@ static_assert(64 % kUnroll == 0, "the unroll must divide the table chunk");
 
 template <typename QT, typename KT, int D>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(AttnArgs a, int group) {
-  constexpr bool kInt8 = (KT::bytes == 1);
+  constexpr bool kInt4 = (KT::bits == 4);
+  constexpr bool kInt8 = (KT::bits == 8);
+  constexpr bool kScaled = kInt4 || kInt8;    // codes with per-tile scales
   constexpr int NK = D / 32;                  // QK products per tile
   constexpr int NV = D / 16;                  // PV products per tile (= elements per lane row)
-  constexpr int KB = 8 * KT::bytes;           // bytes of one lane's K chunk
-  constexpr int VB = NV * KT::bytes;          // bytes of one lane's V chunk
-  constexpr int ROW = D * KT::bytes;          // bytes of one token row
+  constexpr int NKL = kInt4 ? 1 : NK;         // K loads per lane and tile
+  constexpr int KB = kInt4 ? D / 8 : 8 * KT::bytes;   // bytes of one lane's K load
+  constexpr int VB = NV * KT::bits / 8;       // bytes of one lane's V chunk
+  constexpr int ROW = D * KT::bits / 8;       // bytes of one token row
   constexpr int TILE = 16 * ROW;
   using M = Mx<QT>;
 
@@ -74,7 +82,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttnArgs a, int group)
   TableChunk tc;
   tc.fetch(trow, b0, wave, 0, bmax, a.bs_shift);
 
-  // Q^T operand: head r16, elements 32kk + 8kg .. +7.
+  // Q^T operand: head r16, elements 32kk + 8kg .. +7 (4-bit keys:
+  // kg*D/4 + 8kk .. +7, the elements that lane's key load holds).
   u32x4 qop[NK];
   {
     const uint16_t* qp = static_cast<const uint16_t*>(a.q);
@@ -82,7 +91,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttnArgs a, int group)
     const int64_t qrow = (static_cast<int64_t>(row) * a.hq + hbase + (live ? r16 : 0)) * D;
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
-      u32x4 v = *reinterpret_cast<const u32x4*>(qp + qrow + 32 * kk + 8 * kg);
+      const int e0 = kInt4 ? kg * (D / 4) + 8 * kk : 32 * kk + 8 * kg;
+      u32x4 v = *reinterpret_cast<const u32x4*>(qp + qrow + e0);
       qop[kk] = live ? v : u32x4{0u, 0u, 0u, 0u};
     }
   }
@@ -103,12 +113,12 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttnArgs a, int group)
   const uint8_t* kc = static_cast<const uint8_t*>(a.kc);
   const uint8_t* vc = static_cast<const uint8_t*>(a.vc);
   // lane offsets inside a tile
-  const int koff = r16 * ROW + 8 * kg * KT::bytes;          // + kk * 32 elements
-  const int voff = (4 * kg) * ROW + r16 * VB;               // + e * ROW
+  const int koff = r16 * ROW + (kInt4 ? kg * KB : 8 * kg * KT::bytes);   // + kk * 32 elements
+  const int voff = (4 * kg) * ROW + r16 * VB;                           // + e * ROW
 
   for (int k = 0; k < nbw; k += kUnroll) {
     if (k > 0 && (k & 63) == 0) tc.fetch(trow, b0, wave, k, bmax, a.bs_shift);
-    u32x4 kr[kUnroll][NK], vr[kUnroll][4];
+    u32x4 kr[kUnroll][NKL], vr[kUnroll][4];
     int phys[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -121,7 +131,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttnArgs a, int group)
       if (p >= 0) {
         const int64_t toff = tile_index(a, p, kvh, b0 + wave + kWaves * (k + u)) * TILE;
 #pragma unroll
-        for (int kk = 0; kk < NK; ++kk)
+        for (int kk = 0; kk < NKL; ++kk)
           kr[u][kk] = load_bytes<KB>(kc + toff + koff + kk * 32 * KT::bytes);
 #pragma unroll
         for (int e = 0; e < 4; ++e) vr[u][e] = load_bytes<VB>(vc + toff + voff + e * ROW);
@@ -133,7 +143,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttnArgs a, int group)
       const int p = phys[u];
       const int tpos = (b0 + wave + kWaves * (k + u)) * 16;
       float kscale = 1.f, vscale = 1.f;
-      if (kInt8 && p >= 0) {
+      if (kScaled && p >= 0) {
         kscale = a.ks[static_cast<int64_t>(p) * a.hkv + kvh];
         vscale = a.vs[static_cast<int64_t>(p) * a.hkv + kvh];
       }
@@ -142,7 +152,11 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttnArgs a, int group)
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
         u32x4 kop;
-        if constexpr (kInt8) {
+        if constexpr (kInt4) {
+          const uint32_t w = dw(kr[u][0], kk);
+          kop = u32x4{M::int_pair(i4_at(w, 0), i4_at(w, 1)), M::int_pair(i4_at(w, 2), i4_at(w, 3)),
+                      M::int_pair(i4_at(w, 4), i4_at(w, 5)), M::int_pair(i4_at(w, 6), i4_at(w, 7))};
+        } else if constexpr (kInt8) {
           const uint32_t w0 = kr[u][kk].x ^ 0x80808080u, w1 = kr[u][kk].y ^ 0x80808080u;
           kop = u32x4{M::int_pair(i8_exact(w0, 0), i8_exact(w0, 1)),
                       M::int_pair(i8_exact(w0, 2), i8_exact(w0, 3)),
@@ -202,7 +216,14 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttnArgs a, int group)
           vrow[e] = valid ? vrow[e] : u32x4{0u, 0u, 0u, 0u};
         }
       }
-      if constexpr (kInt8) {
+      if constexpr (kInt4) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          const uint32_t v01 = M::int_pair(i4_at(vrow[0].x, j), i4_at(vrow[1].x, j));
+          const uint32_t v23 = M::int_pair(i4_at(vrow[2].x, j), i4_at(vrow[3].x, j));
+          acc[j] = M::k32(u32x4{v01, v23, v01, v23}, pcat, acc[j]);
+        }
+      } else if constexpr (kInt8) {
         // sign-flipped codes: each widens with one byte-select add and one convert
 #pragma unroll
         for (int e = 0; e < 4; ++e) vrow[e] ^= u32x4{0x80808080u, 0x80808080u, 0x80808080u, 0x80808080u};
@@ -263,11 +284,13 @@ pkv_status launch_decode_mfma(const AttnArgs& a, pkv_dtype q_dt, pkv_dtype kv_dt
                               int group, hipStream_t st) {
   if (group > 16) return fail(PKV_ERR_UNSUPPORTED, "MFMA decode: group %d > 16", group);
   if (q_dt == PKV_BF16)
-    return kv_dt == PKV_I8 ? launch_qk<BF16, I8>(a, D, group, st)
-                           : launch_qk<BF16, BF16>(a, D, group, st);
+    return kv_dt == PKV_I8   ? launch_qk<BF16, I8>(a, D, group, st)
+           : kv_dt == PKV_I4 ? launch_qk<BF16, I4>(a, D, group, st)
+                             : launch_qk<BF16, BF16>(a, D, group, st);
   if (q_dt == PKV_F16)
-    return kv_dt == PKV_I8 ? launch_qk<F16, I8>(a, D, group, st)
-                           : launch_qk<F16, F16>(a, D, group, st);
+    return kv_dt == PKV_I8   ? launch_qk<F16, I8>(a, D, group, st)
+           : kv_dt == PKV_I4 ? launch_qk<F16, I4>(a, D, group, st)
+                             : launch_qk<F16, F16>(a, D, group, st);
   return fail(PKV_ERR_UNSUPPORTED, "MFMA decode needs 16-bit q");
 }
 

@@ -1,5 +1,7 @@
 // Paged decode attention, wavefront path (any storage dtype, small head
 // groups).  Also serves fp32 chunked prefill, one query row per workgroup.
+// 4-bit codes are read 8 bytes per lane (16 codes), so a lane holds as many
+// elements as with int8 and the register budget is the same.
 //
 // What it computes (cnnetsun.cn "别再让GPU内存拖后腿了…" §3.1): for each
 // block of the sequence's table, the query's scores against that block's
@@ -86,6 +88,13 @@ template <> struct UnpackDw<I8> {
     for (int k = 0; k < 4; ++k) x[k] = i8_at(w, k);
   }
 };
+template <> struct UnpackDw<I4> {
+  static constexpr int n = 8;
+  __device__ __forceinline__ static void run(uint32_t w, float* x) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = i4_at(w, k);
+  }
+};
 
 __device__ __forceinline__ uint32_t dword(const u32x4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
@@ -93,14 +102,16 @@ __device__ __forceinline__ uint32_t dword(const u32x4& v, int i) {
 
 template <typename QT, typename KT, int D, int G>
 __global__ __launch_bounds__(256) void decode_wave_kernel(AttnArgs a) {
-  constexpr int EB = KT::bytes;
-  constexpr int E = 16 / EB;           // elements per 16-byte chunk
-  constexpr int C = D / E;             // lanes per token row
-  constexpr int TPL = 64 / C;          // tokens per wavefront load
-  constexpr int NL = 16 / TPL;         // loads per 16-token tile
-  constexpr int TILE = 16 * D * EB;    // bytes of one (block, head) tile
+  // 4-bit codes are read as 8-byte chunks (16 codes, the register shape of
+  // an int8 chunk); everything else as 16-byte chunks.
+  constexpr int CB = KT::bits == 4 ? 8 : 16;    // bytes of one lane chunk
+  constexpr int E = CB * 8 / KT::bits;          // elements per chunk
+  constexpr int C = D / E;                      // lanes per token row
+  constexpr int TPL = 64 / C;                   // tokens per wavefront load
+  constexpr int NL = 16 / TPL;                  // loads per 16-token tile
+  constexpr int TILE = 16 * D * KT::bits / 8;   // bytes of one (block, head) tile
   static_assert(C >= 4 && C <= 64 && NL >= 1, "unsupported head_dim / dtype");
-  constexpr bool kInt8 = (EB == 1);
+  constexpr bool kScaled = (KT::bits <= 8);     // codes with per-tile scales
 
   const WgCoord wc = wg_coord(a.hq / G, a.num_parts);
   const int part = wc.part;
@@ -163,8 +174,8 @@ __global__ __launch_bounds__(256) void decode_wave_kernel(AttnArgs a) {
     for (int e = 0; e < E; ++e) o[g][e] = 0.f;
   }
 
-  const uint8_t* kbase = static_cast<const uint8_t*>(a.kc) + lane * 16;
-  const uint8_t* vbase = static_cast<const uint8_t*>(a.vc) + lane * 16;
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.kc) + lane * CB;
+  const uint8_t* vbase = static_cast<const uint8_t*>(a.vc) + lane * CB;
 
   // One block: scores of this lane's tokens for every head, the online
   // softmax update, and the weighted sum of the value rows.  `masked` is set
@@ -212,7 +223,7 @@ __global__ __launch_bounds__(256) void decode_wave_kernel(AttnArgs a) {
       m[g] = mn;
 #pragma unroll
       for (int e = 0; e < E; ++e) o[g][e] *= alpha;
-      if (kInt8) {
+      if (kScaled) {
 #pragma unroll
         for (int j = 0; j < NL; ++j) pw[g][j] *= vsc;   // per-block value scale
       }
@@ -222,7 +233,7 @@ __global__ __launch_bounds__(256) void decode_wave_kernel(AttnArgs a) {
     for (int j = 0; j < NL; ++j) {
       const bool valid = !masked || (tpos + j * TPL + u < t1);
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
+      for (int d = 0; d < CB / 4; ++d) {
         float vx[ND];
         UnpackDw<KT>::run(dword(vr[j], d), vx);
 #pragma unroll
@@ -244,11 +255,18 @@ __global__ __launch_bounds__(256) void decode_wave_kernel(AttnArgs a) {
     const int64_t toff = tile_index(a, p, kvh, b0 + wave + kWaves * k) * TILE;
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
-      kr[j] = *reinterpret_cast<const u32x4*>(kbase + toff + j * 1024);
-      vr[j] = *reinterpret_cast<const u32x4*>(vbase + toff + j * 1024);
+      if constexpr (CB == 16) {
+        kr[j] = *reinterpret_cast<const u32x4*>(kbase + toff + j * 64 * CB);
+        vr[j] = *reinterpret_cast<const u32x4*>(vbase + toff + j * 64 * CB);
+      } else {
+        const u32x2 k2 = *reinterpret_cast<const u32x2*>(kbase + toff + j * 64 * CB);
+        const u32x2 v2 = *reinterpret_cast<const u32x2*>(vbase + toff + j * 64 * CB);
+        kr[j] = u32x4{k2.x, k2.y, 0u, 0u};
+        vr[j] = u32x4{v2.x, v2.y, 0u, 0u};
+      }
     }
     ksc = vsc = 1.f;
-    if (kInt8) {
+    if (kScaled) {
       ksc = a.ks[static_cast<int64_t>(p) * a.hkv + kvh];
       vsc = a.vs[static_cast<int64_t>(p) * a.hkv + kvh];
     }
@@ -355,6 +373,11 @@ pkv_status launch_decode_wave(const AttnArgs& a, pkv_dtype q_dt, pkv_dtype kv_dt
     if (q_dt == PKV_BF16) return launch_qk<BF16, I8>(a, D, group, st);
     if (q_dt == PKV_F16) return launch_qk<F16, I8>(a, D, group, st);
     return launch_qk<F32, I8>(a, D, group, st);
+  }
+  if (kv_dt == PKV_I4) {
+    if (q_dt == PKV_BF16) return launch_qk<BF16, I4>(a, D, group, st);
+    if (q_dt == PKV_F16) return launch_qk<F16, I4>(a, D, group, st);
+    return launch_qk<F32, I4>(a, D, group, st);
   }
   if (q_dt == PKV_BF16) return launch_qk<BF16, BF16>(a, D, group, st);
   if (q_dt == PKV_F16) return launch_qk<F16, F16>(a, D, group, st);

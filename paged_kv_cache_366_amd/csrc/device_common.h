@@ -1,5 +1,5 @@
 // Device helpers shared by the gfx950 kernels of libpkv: storage types,
-// exact widening of 16-bit and 8-bit values, round-to-nearest-even
+// exact widening of 16-bit, 8-bit and 4-bit values, round-to-nearest-even
 // narrowing, DPP row reductions and the launch checks.
 #pragma once
 
@@ -18,11 +18,14 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
-// Storage tags.  The raw element type is what sits in memory.
-struct F32 { typedef float raw; static constexpr int bytes = 4; };
-struct F16 { typedef uint16_t raw; static constexpr int bytes = 2; };
-struct BF16 { typedef uint16_t raw; static constexpr int bytes = 2; };
-struct I8 { typedef int8_t raw; static constexpr int bytes = 1; };
+// Storage tags.  The raw element type is what sits in memory; `bits` is the
+// width of one element (I4 packs two codes per byte, element 2i in the low
+// nibble), and `bytes` the size of the raw type.
+struct F32 { typedef float raw; static constexpr int bytes = 4, bits = 32; };
+struct F16 { typedef uint16_t raw; static constexpr int bytes = 2, bits = 16; };
+struct BF16 { typedef uint16_t raw; static constexpr int bytes = 2, bits = 16; };
+struct I8 { typedef int8_t raw; static constexpr int bytes = 1, bits = 8; };
+struct I4 { typedef uint8_t raw; static constexpr int bytes = 1, bits = 4; };
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
@@ -38,6 +41,10 @@ __device__ __forceinline__ float f16_hi(uint32_t w) {
 // Signed byte k (0..3) of a dword, widened exactly.
 __device__ __forceinline__ float i8_at(uint32_t w, int k) {
   return static_cast<float>(static_cast<int32_t>(w << (24 - 8 * k)) >> 24);
+}
+// Signed nibble k (0..7) of a dword (two's complement), widened exactly.
+__device__ __forceinline__ float i4_at(uint32_t w, int k) {
+  return static_cast<float>(static_cast<int32_t>(w << (28 - 4 * k)) >> 28);
 }
 
 // fp32 -> bf16 bits, round to nearest, ties to even; NaN stays NaN.
@@ -74,6 +81,17 @@ template <> struct Unpack<F16> {
     const uint32_t a[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) { x[2 * i] = f16_lo(a[i]); x[2 * i + 1] = f16_hi(a[i]); }
+  }
+};
+// 4-bit storage is read in 8-byte chunks (16 codes): the low two dwords.
+template <> struct Unpack<I4> {
+  static constexpr int n = 16;
+  __device__ __forceinline__ static void run(const u32x4& w, float* x) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      x[k] = i4_at(w.x, k);
+      x[8 + k] = i4_at(w.y, k);
+    }
   }
 };
 template <> struct Unpack<I8> {

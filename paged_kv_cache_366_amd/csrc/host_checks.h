@@ -17,9 +17,18 @@ inline int dtype_bytes(pkv_dtype d) {
     case PKV_F16: return 2;
     case PKV_BF16: return 2;
     case PKV_I8: return 1;
+    case PKV_I4: return 1;   // raw byte; two elements share it (see row_bytes)
     default: return 0;
   }
 }
+
+// Bytes of one row of `n` elements (4-bit storage: n / 2, n even).
+inline int64_t row_bytes(pkv_dtype d, int64_t n) {
+  return d == PKV_I4 ? n / 2 : n * dtype_bytes(d);
+}
+
+// Storage with per-(block, kv head) scales beside the codes.
+inline bool has_scales(pkv_dtype d) { return d == PKV_I8 || d == PKV_I4; }
 
 inline const char* dtype_name(pkv_dtype d) {
   switch (d) {
@@ -27,6 +36,7 @@ inline const char* dtype_name(pkv_dtype d) {
     case PKV_F16: return "f16";
     case PKV_BF16: return "bf16";
     case PKV_I8: return "i8";
+    case PKV_I4: return "i4";
     default: return "?";
   }
 }

@@ -67,7 +67,7 @@ template <> struct Mx<F16> {
   }
 };
 
-// Loads of 4, 8 or 16 bytes into the low dwords of a u32x4.
+// Loads of 2, 4, 8 or 16 bytes into the low dwords of a u32x4.
 template <int B>
 __device__ __forceinline__ u32x4 load_bytes(const uint8_t* p) {
   u32x4 r = {0u, 0u, 0u, 0u};
@@ -77,8 +77,11 @@ __device__ __forceinline__ u32x4 load_bytes(const uint8_t* p) {
     const u32x2 v = *reinterpret_cast<const u32x2*>(p);
     r.x = v.x;
     r.y = v.y;
-  } else {
+  } else if constexpr (B == 4) {
     r.x = *reinterpret_cast<const uint32_t*>(p);
+  } else {
+    static_assert(B == 2, "load width");
+    r.x = *reinterpret_cast<const uint16_t*>(p);
   }
   return r;
 }

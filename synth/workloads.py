@@ -12,7 +12,10 @@ Storage conventions shared by both consumers:
   * the pool is ``[num_blocks, kv_heads, block_size, head_dim]``;
   * slots that no token was written to hold NaN (int8: code 127 in allocated
     blocks, code -128 and a NaN scale in blocks no sequence owns), so any read
-    of an unmasked slot shows up in the result.
+    of an unmasked slot shows up in the result;
+  * 4-bit pools are random bytes ``[num_blocks, kv_heads, block_size,
+    head_dim / 2]`` (every byte value, so every nibble) with scales drawn
+    per owned (block, kv_head) and NaN for blocks no sequence owns.
 """
 from __future__ import annotations
 
@@ -173,6 +176,11 @@ class PagedCase:
     v_i8: Optional[np.ndarray] = None
     k_scale: Optional[np.ndarray] = None   # float32 [NB, Hkv]
     v_scale: Optional[np.ndarray] = None
+    # 4-bit storage (present when kv is 4-bit): packed bytes and scales
+    k_i4: Optional[np.ndarray] = None      # uint8 [NB, Hkv, BS, D / 2]
+    v_i4: Optional[np.ndarray] = None
+    k_scale4: Optional[np.ndarray] = None  # float32 [NB, Hkv]
+    v_scale4: Optional[np.ndarray] = None
     extra: dict = field(default_factory=dict)
 
     @property
@@ -233,16 +241,36 @@ def int8_pool(cache: np.ndarray, tables: np.ndarray, lens,
     return codes, scales
 
 
+def random_int4_pool(rng: np.random.Generator, tables: np.ndarray, lens, num_blocks: int,
+                     kv_heads: int, head_dim: int, block_size: int = BLOCK_SIZE,
+                     scale_range: Tuple[float, float] = (0.1, 0.3)):
+    """A 4-bit pool as random bytes (uint8, every value) and float32 scales
+    drawn U[scale_range] for the (block, kv_head) tiles some sequence owns,
+    NaN elsewhere.  Draw order: bytes, then scales."""
+    codes = rng.integers(0, 256, (num_blocks, kv_heads, block_size, head_dim // 2),
+                         dtype=np.uint8)
+    drawn = rng.uniform(scale_range[0], scale_range[1], (num_blocks, kv_heads)).astype(np.float32)
+    scales = np.full((num_blocks, kv_heads), np.float32(np.nan), np.float32)
+    for s, n in enumerate(lens):
+        for j in range(blocks_for(int(n), block_size)):
+            b = int(tables[s, j])
+            scales[b] = drawn[b]
+    return codes, scales
+
+
 def decode_case(seed: int, num_seqs: int, q_heads: int, kv_heads: int, head_dim: int,
                 lens: Optional[Sequence[int]] = None, len_range: Optional[Tuple[int, int]] = None,
                 dtype: str = "bf16",
                 block_size: int = BLOCK_SIZE, pool_factor: float = 1.25,
                 num_blocks: Optional[int] = None, int8: bool = False,
-                keep_logical: bool = False, max_blocks: Optional[int] = None) -> PagedCase:
+                keep_logical: bool = False, max_blocks: Optional[int] = None,
+                int4: bool = False) -> PagedCase:
     """Decode input: one query per sequence, K/V already cached.
 
     Either ``lens`` lists the context lengths (each includes the current
-    token) or ``len_range=(lo, hi)`` draws them uniform on [lo, hi].
+    token) or ``len_range=(lo, hi)`` draws them uniform on [lo, hi].  With
+    ``int4`` a random 4-bit K pool then V pool are drawn after everything
+    else (random_int4_pool).
     """
     rng = np.random.default_rng(seed)
     if len_range is not None:
@@ -262,6 +290,11 @@ def decode_case(seed: int, num_seqs: int, q_heads: int, kv_heads: int, head_dim:
     if int8:
         case.k_i8, case.k_scale = int8_pool(k_cache, tables, lens_arr, block_size)
         case.v_i8, case.v_scale = int8_pool(v_cache, tables, lens_arr, block_size)
+    if int4:
+        case.k_i4, case.k_scale4 = random_int4_pool(rng, tables, lens_arr, nb, kv_heads, head_dim,
+                                                    block_size)
+        case.v_i4, case.v_scale4 = random_int4_pool(rng, tables, lens_arr, nb, kv_heads, head_dim,
+                                                    block_size)
     return case
 
 
@@ -309,10 +342,10 @@ def llama7b_decode(seed: int = 1, num_seqs: int = 64, lens=(128, 2048),
 
 
 def gqa_long_decode(seed: int = 4, num_seqs: int = 16, lens=(8192, 32768), int8: bool = False,
-                    keep_logical: bool = False) -> PagedCase:
+                    keep_logical: bool = False, int4: bool = False) -> PagedCase:
     """Long-context GQA decode: 64 query heads over 8 KV heads, head_dim 128."""
     return decode_case(seed, num_seqs, 64, 8, 128, len_range=lens, dtype="bf16", int8=int8,
-                       keep_logical=keep_logical)
+                       keep_logical=keep_logical, int4=int4)
 
 
 @dataclass
