@@ -293,10 +293,17 @@ def bench_decode7b(a, torch, pkv, algo):
 # ---------------------------------------------------------------------------
 # long-context grouped-query decode
 # ---------------------------------------------------------------------------
-def bench_gqa(a, torch, pkv, algo, int8: bool):
+def owned_blocks(c, W):
+    """(block, filled rows) of every block some sequence of case c owns."""
+    return [(int(c.block_tables[s_, j]), int(min(BLOCK, n - BLOCK * j)))
+            for s_, n in enumerate(c.context_lens) for j in range(W.blocks_for(n))]
+
+
+def bench_gqa(a, torch, pkv, algo, kv: str):
     from synth import workloads as W
     print("[bench] building the long-context GQA workload on the host", file=sys.stderr,
           flush=True)
+    int8, int4 = kv == "int8", kv == "int4"
     c = W.gqa_long_decode(seed=4, int8=int8)
     dev = "cuda"
     if int8:
@@ -304,6 +311,21 @@ def bench_gqa(a, torch, pkv, algo, int8: bool):
         vc = torch.from_numpy(c.v_i8).to(dev)
         ks = torch.from_numpy(c.k_scale).to(dev)
         vs = torch.from_numpy(c.v_scale).to(dev)
+    elif int4:
+        # the 4-bit pool is the block encoder's output over the bf16 pool
+        # (built before the timed region)
+        sk, sv = to_dev_bf16(c.k_cache, torch), to_dev_bf16(c.v_cache, torch)
+        nb_, hkv_, D_ = c.num_blocks, c.kv_heads, c.head_dim
+        kc = torch.zeros((nb_, hkv_, BLOCK, D_ // 2), dtype=torch.uint8, device=dev)
+        vc = torch.zeros_like(kc)
+        ks = torch.zeros((nb_, hkv_), dtype=torch.float32, device=dev)
+        vs = torch.zeros_like(ks)
+        own = owned_blocks(c, W)
+        pkv.pkv_quantize_blocks_int4(
+            sk, sv, kc, vc, ks, vs, torch.from_numpy(np.array([b for b, _ in own], np.int32)).to(dev),
+            torch.from_numpy(np.array([f for _, f in own], np.int32)).to(dev))
+        torch.cuda.synchronize()
+        del sk, sv
     else:
         kc, vc = to_dev_bf16(c.k_cache, torch), to_dev_bf16(c.v_cache, torch)
         ks = vs = None
@@ -318,9 +340,9 @@ def bench_gqa(a, torch, pkv, algo, int8: bool):
     ws = torch.empty(max(pkv.pkv_decode_workspace_bytes(S, hq, D, max_ctx, part), 1),
                      dtype=torch.uint8, device=dev)
     # the step's cache write: each sequence's current token (the last
-    # position) goes to its slot, into the int8 pool through quantise-on-write
-    # (its block's scale already covers it, so the write is the same every
-    # step) or into the bf16 pool
+    # position) goes to its slot, into the int8 or 4-bit pool through
+    # quantise-on-write (its block's scale already covers it, so the write is
+    # the same every step) or into the bf16 pool
     last = c.context_lens - 1
     slot_h = np.array([c.block_tables[s_][p // BLOCK] * BLOCK + p % BLOCK
                        for s_, p in enumerate(last)], np.int32)
@@ -335,6 +357,8 @@ def bench_gqa(a, torch, pkv, algo, int8: bool):
             ev[0].record(stream)
         if int8:
             pkv.pkv_reshape_and_cache_int8(new_k, new_v, kc, vc, ks, vs, slots_d)
+        elif int4:
+            pkv.pkv_reshape_and_cache_int4(new_k, new_v, kc, vc, ks, vs, slots_d)
         else:
             pkv.pkv_reshape_and_cache(new_k, new_v, kc, vc, slots_d)
         if ev is not None:
@@ -350,12 +374,13 @@ def bench_gqa(a, torch, pkv, algo, int8: bool):
 
     ms_per_step, (wr_ms, main_ms, red_ms) = run_timed(torch, step, a.steps, a.warmup, 3)
     tokens = int(c.context_lens.astype(np.int64).sum())
-    eb = 1 if int8 else 2
-    kv = tokens * hkv * D * eb * 2
+    bits = 8 if int8 else 4 if int4 else 16
+    scaled = int8 or int4
+    kvb = tokens * hkv * D * bits // 8 * 2
     nblk = sum(W.blocks_for(n) for n in c.context_lens)
-    main_bytes = kv + S * hq * D * 2 + nblk * 4 + S * 4 + (nblk * hkv * 8 if int8 else 0)
+    main_bytes = kvb + S * hq * D * 2 + nblk * 4 + S * 4 + (nblk * hkv * 8 if scaled else 0)
     # + the cache write: bf16 rows read, rows written in the pool's type (and scales)
-    wr_bytes = S * hkv * D * 2 * 2 + S * hkv * D * eb * 2 + (S * hkv * 8 if int8 else 0)
+    wr_bytes = S * hkv * D * 2 * 2 + S * hkv * D * bits // 8 * 2 + (S * hkv * 8 if scaled else 0)
     step_bytes = main_bytes + S * hq * D * 4 + wr_bytes
     main_avg = float(np.mean(main_ms))
     achieved = main_bytes / (main_avg * 1e-3) / 1e9
@@ -367,23 +392,41 @@ def bench_gqa(a, torch, pkv, algo, int8: bool):
     err = 0.0
     src_k, src_v = (c.k_i8, c.v_i8) if int8 else (c.k_cache, c.v_cache)
     sk, sv = (c.k_scale, c.v_scale) if int8 else (None, None)
+    if int4:
+        from oracle import quantize as Q
+
+        def rows4(cache, s_, g):
+            # the oracle's 4-bit encoding of this sequence's tiles, decoded
+            n = int(c.context_lens[s_])
+            out_rows = []
+            for j in range(W.blocks_for(n)):
+                f = min(BLOCK, n - BLOCK * j)
+                codes, sc = Q.quantize_tile(cache[c.block_tables[s_, j], g], f, Q.INT4_MAX)
+                out_rows.append(codes[:f].astype(np.float64) * np.float64(sc))
+            return np.concatenate(out_rows)
     for s_, h_ in zip(rng.integers(0, S, 6), rng.integers(0, hq, 6)):
         n = int(c.context_lens[s_])
-        K = A.gather(src_k, c.block_tables[s_], n, BLOCK, sk)[:, h_ // G]
-        V = A.gather(src_v, c.block_tables[s_], n, BLOCK, sv)[:, h_ // G]
+        if int4:
+            K, V = rows4(c.k_cache, s_, h_ // G), rows4(c.v_cache, s_, h_ // G)
+        else:
+            K = A.gather(src_k, c.block_tables[s_], n, BLOCK, sk)[:, h_ // G]
+            V = A.gather(src_v, c.block_tables[s_], n, BLOCK, sv)[:, h_ // G]
         err = max(err, float(np.abs(got[s_, h_] - A.attend(c.q[s_, h_], K, V, c.scale)).max()))
+    kv_text = {"int8": "int8 KV with per-block fp32 scales",
+               "int4": "4-bit KV (block encoder output) with per-block fp32 scales",
+               "bf16": "bf16 KV"}[kv]
     result = base_result(a, METRIC, step_bytes / (ms_per_step * 1e-3) / 1e9, "GB/s", ms_per_step,
-                         "int8-kv/bf16" if int8 else "bf16", {
-        "workload": f"long-context GQA decode, {'int8 KV with per-block fp32 scales' if int8 else 'bf16 KV'}: "
+                         "bf16" if kv == "bf16" else f"{kv}-kv/bf16", {
+        "workload": f"long-context GQA decode, {kv_text}: "
                     "16 sequences, 64 query heads over 8 KV heads, head_dim 128, "
                     "contexts U[8192, 32768]; step = cache write of each sequence's current "
                     "token + split-K decode + reduce",
         "context_tokens": tokens, "partition_tokens": part, "algo": a.algo})
     result.update({
         "tokens_per_s": S / (ms_per_step * 1e-3),
-        "kernel_ms": {"cache_write" + ("_int8" if int8 else ""): float(np.mean(wr_ms)),
+        "kernel_ms": {"cache_write" + ("" if kv == "bf16" else "_" + kv): float(np.mean(wr_ms)),
                       "decode_main": main_avg, "reduce": float(np.mean(red_ms))},
-        "bytes": {"step": step_bytes, "decode_main": main_bytes, "kv": kv},
+        "bytes": {"step": step_bytes, "decode_main": main_bytes, "kv": kvb},
         "roofline": roofline("decode_mfma_kernel (split-K main)" if algo != pkv.PKV_ALGO_WAVE
                              else "decode_wave_kernel (split-K main)", "hbm", achieved,
                              HBM_PEAK_GBS, "GB/s"),
@@ -640,19 +683,23 @@ def bench_beam(a, torch, pkv, algo):
 # ---------------------------------------------------------------------------
 # int8 storage of a long-context pool (whole blocks)
 # ---------------------------------------------------------------------------
-def bench_quantize(a, torch, pkv):
+def bench_quantize(a, torch, pkv, bits: int = 8):
     from synth import workloads as W
     print("[bench] building the long-context pool on the host", file=sys.stderr, flush=True)
     c = W.gqa_long_decode(seed=4)
     dev = "cuda"
     nb, hkv, D = c.num_blocks, c.kv_heads, c.head_dim
-    owned = [(int(c.block_tables[s_, j]), int(min(BLOCK, n - BLOCK * j)))
-             for s_, n in enumerate(c.context_lens) for j in range(W.blocks_for(n))]
+    owned = owned_blocks(c, W)
     blocks = torch.from_numpy(np.array([b for b, _ in owned], np.int32)).to(dev)
     filled_h = np.array([f for _, f in owned], np.int32)
     filled = torch.from_numpy(filled_h).to(dev)
     sk, sv = to_dev_bf16(c.k_cache, torch), to_dev_bf16(c.v_cache, torch)
-    dk = torch.zeros((nb, hkv, BLOCK, D), dtype=torch.int8, device=dev)
+    if bits == 8:
+        dk = torch.zeros((nb, hkv, BLOCK, D), dtype=torch.int8, device=dev)
+        encode = pkv.pkv_quantize_blocks
+    else:
+        dk = torch.zeros((nb, hkv, BLOCK, D // 2), dtype=torch.uint8, device=dev)
+        encode = pkv.pkv_quantize_blocks_int4
     dv = torch.zeros_like(dk)
     ks = torch.zeros((nb, hkv), dtype=torch.float32, device=dev)
     vs = torch.zeros_like(ks)
@@ -662,25 +709,27 @@ def bench_quantize(a, torch, pkv):
     def step(ev):
         if ev is not None:
             ev[0].record(stream)
-        pkv.pkv_quantize_blocks(sk, sv, dk, dv, ks, vs, blocks, filled)
+        encode(sk, sv, dk, dv, ks, vs, blocks, filled)
         if ev is not None:
             ev[1].record(stream)
 
     ms_per_step, (q_ms,) = run_timed(torch, step, a.steps, a.warmup, 1)
     rows = int(filled_h.sum())
     nlisted = len(owned)
-    # read the filled rows of K and V once (bf16), write every row's int8 code
+    # read the filled rows of K and V once (bf16), write every row's codes
     # and one fp32 scale per (block, head), K and V
-    nbytes = rows * hkv * D * 2 * 2 + nlisted * hkv * BLOCK * D * 2 + nlisted * hkv * 4 * 2
+    nbytes = (rows * hkv * D * 2 * 2 + nlisted * hkv * BLOCK * D * bits // 8 * 2
+              + nlisted * hkv * 4 * 2)
     avg = float(np.mean(q_ms))
+    name = "int8" if bits == 8 else "4-bit"
     result = base_result(a, METRIC, nbytes / (ms_per_step * 1e-3) / 1e9, "GB/s", ms_per_step,
-                         "bf16->int8", {
-        "workload": "int8 storage of a long-context pool: every owned block of 16 sequences x "
-                    "8 KV heads x 128, contexts U[8192, 32768], bf16 -> int8 codes + per-(block, "
-                    "head) fp32 scales",
+                         "bf16->int8" if bits == 8 else "bf16->int4", {
+        "workload": f"{name} storage of a long-context pool: every owned block of 16 sequences x "
+                    f"8 KV heads x 128, contexts U[8192, 32768], bf16 -> {name} codes + "
+                    "per-(block, head) fp32 scales",
         "blocks": nlisted})
     result.update({
-        "kernel_ms": {"quantize_blocks": avg},
+        "kernel_ms": {"quantize_blocks" + ("" if bits == 8 else "_int4"): avg},
         "bytes": {"per_call": nbytes},
         "roofline": roofline("quantize_blocks_kernel", "hbm", nbytes / (avg * 1e-3) / 1e9,
                              HBM_PEAK_GBS, "GB/s"),
@@ -958,7 +1007,8 @@ def bench_prefill_long(a, torch, pkv, algo):
     return result
 
 
-WORKLOADS = ("decode7b", "mixed", "beam", "gqa", "gqa-int8", "quantize", "swap", "prefix",
+WORKLOADS = ("decode7b", "mixed", "beam", "gqa", "gqa-int8", "gqa-int4", "quantize",
+             "quantize-int4", "swap", "prefix",
              "prefill-long")
 
 
@@ -1005,8 +1055,8 @@ def main(argv=None) -> int:
         result = bench_mixed(a, torch, pkv, algo)
     elif a.workload == "beam":
         result = bench_beam(a, torch, pkv, algo)
-    elif a.workload == "quantize":
-        result = bench_quantize(a, torch, pkv)
+    elif a.workload in ("quantize", "quantize-int4"):
+        result = bench_quantize(a, torch, pkv, 8 if a.workload == "quantize" else 4)
     elif a.workload == "swap":
         result = bench_swap(a, torch, pkv)
     elif a.workload == "prefix":
@@ -1014,7 +1064,8 @@ def main(argv=None) -> int:
     elif a.workload == "prefill-long":
         result = bench_prefill_long(a, torch, pkv, algo)
     else:
-        result = bench_gqa(a, torch, pkv, algo, int8=(a.workload == "gqa-int8"))
+        result = bench_gqa(a, torch, pkv, algo, {"gqa": "bf16", "gqa-int8": "int8",
+                                                 "gqa-int4": "int4"}[a.workload])
     print(json.dumps(result), flush=True)
     return 0
 

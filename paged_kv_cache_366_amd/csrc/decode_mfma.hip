@@ -29,8 +29,19 @@
 //   4-bit keys: the contraction order over head_dim is free, so lane
 //   (t, kg) reads elements kg*D/4 .. +D/4-1 of key row t in one load (16
 //   bytes at head_dim 128) and Q^T takes the same elements; 4-bit values
-//   are read 4 (or 2) bytes per row.  Codes widen exactly to 16-bit
-//   operands (a signed bit-field extract and a convert each).
+//   are read 4 (or 2) bytes per row.  Codes become 16-bit operands without
+//   a convert: each nibble, XORed to c + 8 (or 7 - c), is byte-permuted
+//   under a constant high byte, which spells the exact bf16 value 136 + c
+//   in the low half of an operand pair and c - 135 in the high half (f16:
+//   1032 + c and c - 1031, removed exactly by one packed add).  Key pairs
+//   come out as elements (0,2), (4,6), (1,3), (5,7) of each 8, and q is
+//   permuted to match once at load.  In bf16 the offsets stay in the
+//   products: scores carry 136 x (sum of the head's q in low halves) - 135
+//   x (sum in high halves), taken out with the score scale, and the value
+//   accumulators 136 x (weights of even tokens) - 135 x (weights of odd
+//   tokens), accumulated by one more product per tile against a constant
+//   operand and subtracted at the end.  The opposite signs keep a common
+//   component of q or of the weights from inflating the accumulators.
 //   Weights enter the product as a bf16 (or f16) pair hi + lo, hi = p rounded
 //   and lo = p - hi rounded, which keeps about 16 mantissa bits at the cost
 //   of a second MFMA per product; decode is HBM-bound, so it is free.
@@ -85,15 +96,41 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttnArgs a, int group)
   // Q^T operand: head r16, elements 32kk + 8kg .. +7 (4-bit keys:
   // kg*D/4 + 8kk .. +7, the elements that lane's key load holds).
   u32x4 qop[NK];
+  constexpr bool kOffset = kInt4 && M::kOffset4;   // bf16 4-bit: offsets removed later
+  float kcorr = 0.f;                                // the offsets' share of every score
   {
     const uint16_t* qp = static_cast<const uint16_t*>(a.q);
     const bool live = r16 < group;
     const int64_t qrow = (static_cast<int64_t>(row) * a.hq + hbase + (live ? r16 : 0)) * D;
+    float qlo = 0.f, qhi = 0.f;   // q in low / high halves of the operand pairs
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
       const int e0 = kInt4 ? kg * (D / 4) + 8 * kk : 32 * kk + 8 * kg;
       u32x4 v = *reinterpret_cast<const u32x4*>(qp + qrow + e0);
-      qop[kk] = live ? v : u32x4{0u, 0u, 0u, 0u};
+      v = live ? v : u32x4{0u, 0u, 0u, 0u};
+      if constexpr (kInt4) {
+        // the element order of the unpacked 4-bit keys: (0,2), (4,6), (1,3), (5,7)
+        qop[kk] = u32x4{__builtin_amdgcn_perm(v.y, v.x, 0x05040100u),
+                        __builtin_amdgcn_perm(v.w, v.z, 0x05040100u),
+                        __builtin_amdgcn_perm(v.y, v.x, 0x07060302u),
+                        __builtin_amdgcn_perm(v.w, v.z, 0x07060302u)};
+        if constexpr (kOffset) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            qlo += M::lo(dw(qop[kk], i));
+            qhi += M::hi(dw(qop[kk], i));
+          }
+        }
+      } else {
+        qop[kk] = v;
+      }
+    }
+    if constexpr (kOffset) {
+      qlo += __shfl_xor(qlo, 16);
+      qlo += __shfl_xor(qlo, 32);
+      qhi += __shfl_xor(qhi, 16);
+      qhi += __shfl_xor(qhi, 32);
+      kcorr = M::kOffsetLo4 * qlo + M::kOffsetHi4 * qhi;
     }
   }
 
@@ -107,6 +144,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttnArgs a, int group)
 
   float m = kNegInf, l = 0.f;
   f32x4 acc[NV];
+  f32x4 wacc = {0.f, 0.f, 0.f, 0.f};   // bf16 4-bit: the offsets' share of acc
 #pragma unroll
   for (int j = 0; j < NV; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -154,8 +192,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttnArgs a, int group)
         u32x4 kop;
         if constexpr (kInt4) {
           const uint32_t w = dw(kr[u][0], kk);
-          kop = u32x4{M::int_pair(i4_at(w, 0), i4_at(w, 1)), M::int_pair(i4_at(w, 2), i4_at(w, 3)),
-                      M::int_pair(i4_at(w, 4), i4_at(w, 5)), M::int_pair(i4_at(w, 6), i4_at(w, 7))};
+          const uint32_t lo = nib_lo(w, kFlipPairs), hi = nib_hi(w, kFlipPairs);
+          kop = u32x4{M::fix4(magic_pair(M::kMagic4, lo, 0)), M::fix4(magic_pair(M::kMagic4, lo, 1)),
+                      M::fix4(magic_pair(M::kMagic4, hi, 0)), M::fix4(magic_pair(M::kMagic4, hi, 1))};
         } else if constexpr (kInt8) {
           const uint32_t w0 = kr[u][kk].x ^ 0x80808080u, w1 = kr[u][kk].y ^ 0x80808080u;
           kop = u32x4{M::int_pair(i8_exact(w0, 0), i8_exact(w0, 1)),
@@ -168,12 +207,13 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttnArgs a, int group)
         s = M::k32(kop, qop[kk], s);
       }
       const float sc = kscale * a.scale_log2;
+      const float nc = -kcorr * sc;   // 0 unless the offset is in the scores
       float sv[4];
       float tmax = kNegInf;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bool valid = (p >= 0) && (tpos + 4 * kg + i < t1);
-        sv[i] = valid ? s[i] * sc : kNegInf;
+        sv[i] = valid ? (kOffset ? fmaf(s[i], sc, nc) : s[i] * sc) : kNegInf;
         tmax = fmaxf(tmax, sv[i]);
       }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
@@ -186,6 +226,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttnArgs a, int group)
         l *= alpha;
 #pragma unroll
         for (int j = 0; j < NV; ++j) acc[j] *= alpha;
+        if constexpr (kOffset) wacc *= alpha;
       }
       const float ms = (m == kNegInf) ? 0.f : m;
       float pv[4];
@@ -205,11 +246,13 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttnArgs a, int group)
       // the same 4 keys with the lo weights (the A operand repeats them)
       const u32x4 pcat = {phi.x, phi.y, plo.x, plo.y};
       // ---- out^T += V^T . P^T.  Value rows past the context (only in the
-      // partly filled last block) may hold anything: they are zeroed.
+      // partly filled last block) may hold anything: they are zeroed (4-bit
+      // codes always form finite operands and meet zero weights, so they
+      // need no masking).
       u32x4 vrow[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) vrow[e] = vr[u][e];
-      if (!(p >= 0 && tpos + 16 <= t1)) {
+      if (!kInt4 && !(p >= 0 && tpos + 16 <= t1)) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const bool valid = (p >= 0) && (tpos + 4 * kg + e < t1);
@@ -217,11 +260,36 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttnArgs a, int group)
         }
       }
       if constexpr (kInt4) {
+        // rows 4kg..4kg+3 hold NV codes each (one dword, or its low half);
+        // even rows take the low halves of the operand pairs, odd rows the
+        // high halves.  x01[h][w] interleaves rows 0 and 1 byte by byte:
+        // elements 4w + h and 4w + 2 + h (x23 the same for rows 2 and 3)
+        constexpr int NW = NV / 4;
+        uint32_t x01[2][NW], x23[2][NW];
+        {
+          const uint32_t l0 = nib_lo(vrow[0].x, kFlipLow), l1 = nib_lo(vrow[1].x, kFlipHigh);
+          const uint32_t l2 = nib_lo(vrow[2].x, kFlipLow), l3 = nib_lo(vrow[3].x, kFlipHigh);
+          const uint32_t h0 = nib_hi(vrow[0].x, kFlipLow), h1 = nib_hi(vrow[1].x, kFlipHigh);
+          const uint32_t h2 = nib_hi(vrow[2].x, kFlipLow), h3 = nib_hi(vrow[3].x, kFlipHigh);
+#pragma unroll
+          for (int w = 0; w < NW; ++w) {
+            const uint32_t sel = w ? 0x07030602u : 0x05010400u;
+            x01[0][w] = __builtin_amdgcn_perm(l1, l0, sel);
+            x01[1][w] = __builtin_amdgcn_perm(h1, h0, sel);
+            x23[0][w] = __builtin_amdgcn_perm(l3, l2, sel);
+            x23[1][w] = __builtin_amdgcn_perm(h3, h2, sel);
+          }
+        }
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
-          const uint32_t v01 = M::int_pair(i4_at(vrow[0].x, j), i4_at(vrow[1].x, j));
-          const uint32_t v23 = M::int_pair(i4_at(vrow[2].x, j), i4_at(vrow[3].x, j));
+          const int h = j & 1, w = j >> 2, pp = (j >> 1) & 1;
+          const uint32_t v01 = M::fix4(magic_pair(M::kMagic4, x01[h][w], pp));
+          const uint32_t v23 = M::fix4(magic_pair(M::kMagic4, x23[h][w], pp));
           acc[j] = M::k32(u32x4{v01, v23, v01, v23}, pcat, acc[j]);
+        }
+        if constexpr (kOffset) {
+          constexpr uint32_t o = M::kOffsetPair4;
+          wacc = M::k32(u32x4{o, o, o, o}, pcat, wacc);
         }
       } else if constexpr (kInt8) {
         // sign-flipped codes: each widens with one byte-select add and one convert
@@ -254,6 +322,10 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttnArgs a, int group)
   __shared__ float sm_m[kWaves][16];
   __shared__ float sm_l[kWaves][16];
   // acc[j][i] of lane (h, kg) is element NV*(4kg + i) + j of head h's row.
+  if constexpr (kOffset) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) acc[j] -= wacc;
+  }
 #pragma unroll
   for (int j = 0; j < NV; ++j)
 #pragma unroll

@@ -40,6 +40,18 @@ template <> struct Mx<BF16> {
   __device__ __forceinline__ static uint32_t int_pair(float lo, float hi) {
     return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
   }
+  // 4-bit codes c as operands without a convert (see nib_split): the low
+  // half of an operand pair is u = c + 8 under the high byte 0x43, the bf16
+  // value 136 + c; the high half is 7 - c under 0xC3, the value c - 135.
+  // Both exact; the offsets stay in the products and are taken out
+  // afterwards (kOffsetLo4, kOffsetHi4; kOffsetPair4 is the pair
+  // (136, -135)).  Opposite signs keep a common component of the other
+  // operand from building up in the accumulators.
+  static constexpr uint32_t kMagic4 = 0xC3C34343u;
+  static constexpr bool kOffset4 = true;
+  static constexpr float kOffsetLo4 = 136.f, kOffsetHi4 = -135.f;
+  static constexpr uint32_t kOffsetPair4 = 0xC3074308u;
+  __device__ __forceinline__ static uint32_t fix4(uint32_t x) { return x; }
 };
 template <> struct Mx<F16> {
   __device__ __forceinline__ static f32x4 k32(const u32x4& a, const u32x4& b, const f32x4& c) {
@@ -64,6 +76,18 @@ template <> struct Mx<F16> {
   }
   __device__ __forceinline__ static uint32_t int_pair(float lo, float hi) {
     return pack(lo, hi);   // exact: |x| <= 128 is an f16 value
+  }
+  // 4-bit codes: c + 8 under the high byte 0x64 is the f16 value 1032 + c
+  // (low half), 7 - c under 0xE4 is c - 1031 (high half); one packed f16 add
+  // of (-1032, 1031) leaves c exactly, so no offset remains.
+  static constexpr uint32_t kMagic4 = 0xE4E46464u;
+  static constexpr bool kOffset4 = false;
+  static constexpr float kOffsetLo4 = 0.f, kOffsetHi4 = 0.f;
+  static constexpr uint32_t kOffsetPair4 = 0u;
+  __device__ __forceinline__ static uint32_t fix4(uint32_t x) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const f16x2 v = __builtin_bit_cast(f16x2, x) + f16x2{-1032.f16, 1031.f16};
+    return __builtin_bit_cast(uint32_t, v);
   }
 };
 
@@ -100,6 +124,25 @@ __device__ __forceinline__ uint32_t pair_of(const u32x4& x, const u32x4& y, int 
 // flipped is an unsigned value (v_cvt_f32_ubyte), less 128.
 __device__ __forceinline__ float i8_exact(uint32_t flipped, int k) {
   return static_cast<float>((flipped >> (8 * k)) & 0xffu) - 128.f;
+}
+
+// 4-bit codes of one dword (element 2i in the low nibble of byte i), one
+// per byte: nib_lo takes elements 0, 2, 4, 6 and nib_hi elements 1, 3, 5, 7.
+// A byte bound for the low half of an operand pair is XORed with 8 (c + 8),
+// one for the high half with 7 (7 - c): `flip` gives the choice per byte.
+constexpr uint32_t kFlipPairs = 0x07080708u;   // bytes 0, 2 low halves; 1, 3 high
+constexpr uint32_t kFlipLow = 0x08080808u;
+constexpr uint32_t kFlipHigh = 0x07070707u;
+__device__ __forceinline__ uint32_t nib_lo(uint32_t w, uint32_t flip) {
+  return (w & 0x0F0F0F0Fu) ^ flip;
+}
+__device__ __forceinline__ uint32_t nib_hi(uint32_t w, uint32_t flip) {
+  return ((w >> 4) & 0x0F0F0F0Fu) ^ flip;
+}
+// Bytes 2p and 2p + 1 of x under the high bytes 0 and 2 of `magic`, as the
+// two 16-bit halves of one operand dword.
+__device__ __forceinline__ uint32_t magic_pair(uint32_t magic, uint32_t x, int p) {
+  return __builtin_amdgcn_perm(magic, x, p ? 0x06030402u : 0x06010400u);
 }
 
 // Lazy rescaling of an online softmax: the running reference max moves only

@@ -158,8 +158,8 @@ def test_int4_write_validation(monkeypatch):
 
 
 # ------------------------------------------------------------ decode
-def decode_int4(c, q_dtype, algo, parts, out_dtype=torch.float32):
-    q = to_dev(c.q, q_dtype)
+def decode_int4(c, q_dtype, algo, parts, out_dtype=torch.float32, q=None):
+    q = to_dev(c.q if q is None else q, q_dtype)
     out = torch.empty(q.shape, dtype=out_dtype, device=DEV)
     pkv.pkv_paged_attention_decode(out, q, torch.from_numpy(c.k_i4).to(DEV),
                                    torch.from_numpy(c.v_i4).to(DEV), i32(c.block_tables),
@@ -210,6 +210,18 @@ def test_int4_decode_is_the_same_for_both_kernels_and_outputs():
     f32 = decode_int4(c, "bf16", MFMA, 0)
     b16 = decode_int4(c, "bf16", MFMA, 0, torch.bfloat16)
     assert np.array_equal(b16, W.round_bf16(f32.astype(np.float32)).astype(np.float64))
+
+
+@pytest.mark.parametrize("qdt", ["bf16", "f16"])
+@pytest.mark.parametrize("parts", [0, 512])
+def test_int4_decode_with_a_common_query_component_and_long_contexts(qdt, parts):
+    """Queries shifted by a constant in every element (their sum is in the
+    hundreds) and contexts up to 9000 tokens in one partition: the 16-bit
+    operands of 4-bit codes carry constant offsets that must cancel."""
+    c = W.decode_case(99, 3, 16, 2, 128, lens=[4000, 777, 9000], dtype=qdt, int4=True)
+    q = W.round_to(c.q + np.float32(6.0), qdt)
+    got = decode_int4(c, qdt, AUTO, parts, q=q)
+    assert np.abs(got - oracle_int4(c, q)).max() <= TOL
 
 
 def test_decode_over_a_gpu_encoded_int4_pool():
