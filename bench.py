@@ -50,8 +50,8 @@ BLOCK = 16
 # 1.0) on this workload (seed 1, partition 256).  Valid only for the kernel
 # sources whose hash is recorded; a changed kernel reports null.
 TRAFFIC = {
-    "sources_sha1": "50f840a265e5b415e9cd94961ad55fc276e87b1a",
-    "bytes_per_launch": 1092189 * 1024 + 4861 * 1024,
+    "sources_sha1": "8a117e7a57b634f2f1c31559d8b352ddc1257470",
+    "bytes_per_launch": 1092219 * 1024 + 4860 * 1024,
 }
 KERNEL_SOURCES = ("decode_wave.hip", "attention_common.h", "device_common.h")
 
