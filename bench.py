@@ -45,13 +45,13 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BLOCK = 16
 
 # HBM traffic of the main decode kernel per launch, from rocprofv3 --pmc
-# FETCH_SIZE (546,139 KiB, scaled by 1 / 0.500041: the factor an elementwise
-# kernel that reads exactly 1 GiB shows) plus WRITE_SIZE (4,861 KiB, factor
-# 1.0) on this workload (seed 1, partition 256).  Valid only for the kernel
-# sources whose hash is recorded; a changed kernel reports null.
+# FETCH_SIZE (scaled by 1 / the factor an elementwise kernel that reads
+# exactly 1 GiB shows) plus WRITE_SIZE (factor 1.0) on this workload (seed 1,
+# partition 384).  Valid only for the kernel sources whose hash is recorded;
+# a changed kernel reports null.
 TRAFFIC = {
-    "sources_sha1": "8a117e7a57b634f2f1c31559d8b352ddc1257470",
-    "bytes_per_launch": 1092219 * 1024 + 4860 * 1024,
+    "sources_sha1": "581018606e31c322d6f2b263873419f6fc2ff846",
+    "bytes_per_launch": 1092160 * 1024 + 3417 * 1024,
 }
 KERNEL_SOURCES = ("decode_wave.hip", "attention_common.h", "device_common.h")
 
@@ -1020,7 +1020,7 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", choices=WORKLOADS, default="decode7b",
                     help="decode7b is the headline line; the others measure the other kernels")
     ap.add_argument("--partition", type=int, default=None,
-                    help="split-K partition size in tokens (0 = no split); default 256, or 512 "
+                    help="split-K partition size in tokens (0 = no split); default 384, or 512 "
                          "for the long-context GQA workloads")
     ap.add_argument("--algo", choices=("auto", "wave", "mfma"), default="auto")
     ap.add_argument("--prefill-partition", type=int, default=0,
@@ -1039,7 +1039,7 @@ def main(argv=None) -> int:
         return 2
     a.partition_set = a.partition is not None
     if a.partition is None:
-        a.partition = 256
+        a.partition = 384
 
     import torch
     import paged_kv_cache_366_amd as pkv

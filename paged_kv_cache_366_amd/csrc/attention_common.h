@@ -83,7 +83,6 @@ __device__ __forceinline__ void row_context(const AttnArgs& a, int row, int& seq
 // as the slow index, concurrent reads all sit at one offset modulo the
 // block stride and crowd a few channels: on MI355X that costs about a
 // quarter of the bandwidth.)
-constexpr int kDecodeWaves = 4;
 
 struct WgCoord {
   int row, part, hg;
@@ -99,17 +98,17 @@ __device__ __forceinline__ WgCoord wg_coord(int ngroups, int num_parts) {
 }
 
 // Block-table entries of one wavefront's share of a partition.  Wave w of
-// the workgroup takes the partition's 16-row tiles w, w + 4, w + 8, ...; its
-// k-th tile is tile `b0 + w + 4k` of the sequence, in table entry
-// (b0 + w + 4k) >> bs_shift.  Lane i holds the entry for k = k0 + i, so one
-// vector load covers 64 of the wave's tiles and each step reads its block id
-// with a lane read, off the load path.  Tiles at or past `bmax` (the end of
-// the partition or of the table row) read no entry.
+// a workgroup of nw waves takes the partition's 16-row tiles w, w + nw,
+// w + 2nw, ...; its k-th tile is tile `b0 + w + nw k` of the sequence, in
+// table entry (b0 + w + nw k) >> bs_shift.  Lane i holds the entry for
+// k = k0 + i, so one vector load covers 64 of the wave's tiles and each step
+// reads its block id with a lane read, off the load path.  Tiles at or past
+// `bmax` (the end of the partition or of the table row) read no entry.
 struct TableChunk {
   int entry = -1;
-  __device__ __forceinline__ void fetch(const int32_t* trow, int b0, int wave, int k0, int bmax,
-                                        int bs_shift) {
-    const int bi = wave + kDecodeWaves * (k0 + static_cast<int>(threadIdx.x & 63));
+  __device__ __forceinline__ void fetch(const int32_t* trow, int b0, int wave, int nw, int k0,
+                                        int bmax, int bs_shift) {
+    const int bi = wave + nw * (k0 + static_cast<int>(threadIdx.x & 63));
     entry = bi < bmax ? trow[(b0 + bi) >> bs_shift] : -1;
   }
   // Entry of the wave's tile k (k0 <= k < k0 + 64); k is wave-uniform.

@@ -45,15 +45,28 @@
 //   Weights enter the product as a bf16 (or f16) pair hi + lo, hi = p rounded
 //   and lo = p - hi rounded, which keeps about 16 mantissa bits at the cost
 //   of a second MFMA per product; decode is HBM-bound, so it is free.
-// Four wavefronts take the partition's tiles round-robin, two tiles in flight
-// each, and merge through LDS at the end.
+// The workgroup's wavefronts take the partition's tiles round-robin, two
+// tiles in flight each, and merge through LDS at the end.
 #include "attention_common.h"
 #include "mfma_common.h"
 
 namespace pkv {
 namespace {
 
-constexpr int kWaves = kDecodeWaves;
+// Wavefronts per workgroup, by storage width: four for 16-bit KV; two for
+// int8 and 4-bit codes, whose small tiles leave each wave's loads
+// latency-bound, so fewer waves per partition (more tiles each) measured
+// faster (4-bit about 8%, int8 about 1.5%).
+#ifndef PKV_MFMA_WAVES
+#define PKV_MFMA_WAVES 4
+#endif
+#ifndef PKV_MFMA_WAVES_CODES
+#define PKV_MFMA_WAVES_CODES 2
+#endif
+template <typename KT>
+constexpr int mfma_waves() {
+  return KT::bits == 16 ? PKV_MFMA_WAVES : PKV_MFMA_WAVES_CODES;
+}
 #ifndef PKV_MFMA_UNROLL
 #define PKV_MFMA_UNROLL 2
 #endif
@@ -61,7 +74,9 @@ constexpr int kUnroll = PKV_MFMA_UNROLL;   // tiles of K and V in flight per wav
 static_assert(64 % kUnroll == 0, "the unroll must divide the table chunk");
 
 template <typename QT, typename KT, int D>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(AttnArgs a, int group) {
+__global__ __launch_bounds__(64 * mfma_waves<KT>()) void decode_mfma_kernel(AttnArgs a,
+                                                                              int group) {
+  constexpr int kWaves = mfma_waves<KT>();
   constexpr bool kInt4 = (KT::bits == 4);
   constexpr bool kInt8 = (KT::bits == 8);
   constexpr bool kScaled = kInt4 || kInt8;    // codes with per-tile scales
@@ -91,7 +106,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttnArgs a, int group)
   const int bmax = min(a.part_tokens >> 4, (a.max_blocks << a.bs_shift) - b0);
   const int32_t* trow = a.tables + static_cast<int64_t>(seq) * a.max_blocks;
   TableChunk tc;
-  tc.fetch(trow, b0, wave, 0, bmax, a.bs_shift);
+  tc.fetch(trow, b0, wave, kWaves, 0, bmax, a.bs_shift);
 
   // Q^T operand: head r16, elements 32kk + 8kg .. +7 (4-bit keys:
   // kg*D/4 + 8kk .. +7, the elements that lane's key load holds).
@@ -155,7 +170,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttnArgs a, int group)
   const int voff = (4 * kg) * ROW + r16 * VB;                           // + e * ROW
 
   for (int k = 0; k < nbw; k += kUnroll) {
-    if (k > 0 && (k & 63) == 0) tc.fetch(trow, b0, wave, k, bmax, a.bs_shift);
+    if (k > 0 && (k & 63) == 0) tc.fetch(trow, b0, wave, kWaves, k, bmax, a.bs_shift);
     u32x4 kr[kUnroll][NKL], vr[kUnroll][4];
     int phys[kUnroll];
 #pragma unroll
@@ -343,9 +358,9 @@ template <typename QT, typename KT>
 pkv_status launch_qk(const AttnArgs& a, int D, int group, hipStream_t st) {
   dim3 grid(a.num_parts * a.num_rows * a.hkv);
   if (D == 64)
-    hipLaunchKernelGGL((decode_mfma_kernel<QT, KT, 64>), grid, dim3(256), 0, st, a, group);
+    hipLaunchKernelGGL((decode_mfma_kernel<QT, KT, 64>), grid, dim3(64 * mfma_waves<KT>()), 0, st, a, group);
   else
-    hipLaunchKernelGGL((decode_mfma_kernel<QT, KT, 128>), grid, dim3(256), 0, st, a, group);
+    hipLaunchKernelGGL((decode_mfma_kernel<QT, KT, 128>), grid, dim3(64 * mfma_waves<KT>()), 0, st, a, group);
   PKV_LAUNCH_CHECK("paged attention (MFMA)");
   return PKV_OK;
 }

@@ -10,7 +10,7 @@
 // (running max and sum rescaled as the max grows), which gives the same
 // result up to rounding without materialising the scores.
 //
-// Layout on gfx950.  A workgroup of 4 wavefronts owns one (query row, KV
+// Layout on gfx950.  A workgroup of 8 wavefronts owns one (query row, KV
 // head, context partition) and the G query heads that share that KV head.
 // One (block, KV head) tile of K is 16 rows x head_dim contiguous elements:
 // 4 KiB at bf16 / head_dim 128, read as 16-byte chunks so one wavefront load
@@ -22,7 +22,10 @@
 // its V chunk, so the softmax weight never leaves its lanes: the PV product
 // accumulates per lane, and rows, then wavefronts, are merged once at the
 // end.  Wavefronts take blocks round-robin, one block of K and V in flight
-// each; the kernel stays at 63 VGPRs so eight wavefronts share a SIMD.
+// each.  At bf16 / head_dim 128 the kernel takes 104 VGPRs (four waves per
+// SIMD): the compiler widens each value tile right after its load, ahead of
+// the softmax.  Pinning the widening next to the products (79 VGPRs, six
+// waves per SIMD) measured slower.
 // For 16-bit keys the score uses packed dot2 instructions on the raw pairs,
 // and only the partly filled last block of a context pays for per-row
 // masking.
@@ -37,7 +40,13 @@
 namespace pkv {
 namespace {
 
-constexpr int kWaves = kDecodeWaves;
+// Wavefronts per workgroup.  Eight, with 384-token partitions, measured
+// about 2% faster than four (at their best partition, 256) at the 7B
+// shape: the prologue and the merge amortise over more tiles per workgroup.
+#ifndef PKV_WAVE_WAVES
+#define PKV_WAVE_WAVES 8
+#endif
+constexpr int kWaves = PKV_WAVE_WAVES;
 
 // Dot product of one 16-byte chunk of 16-bit keys with the matching q
 // chunk, both as packed pairs: v_dot2 forms the two exact products and adds
@@ -101,7 +110,7 @@ __device__ __forceinline__ uint32_t dword(const u32x4& v, int i) {
 }
 
 template <typename QT, typename KT, int D, int G>
-__global__ __launch_bounds__(256) void decode_wave_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(AttnArgs a) {
   // 4-bit codes are read as 8-byte chunks (16 codes, the register shape of
   // an int8 chunk); everything else as 16-byte chunks.
   constexpr int CB = KT::bits == 4 ? 8 : 16;    // bytes of one lane chunk
@@ -131,7 +140,7 @@ __global__ __launch_bounds__(256) void decode_wave_kernel(AttnArgs a) {
   const int bmax = min(a.part_tokens >> 4, (a.max_blocks << a.bs_shift) - b0);
   const int32_t* trow = a.tables + static_cast<int64_t>(seq) * a.max_blocks;
   TableChunk tc;
-  tc.fetch(trow, b0, wave, 0, bmax, a.bs_shift);
+  tc.fetch(trow, b0, wave, kWaves, 0, bmax, a.bs_shift);
 
   // q slice of every head of the group: elements [c*E, c*E + E), as
   // floats, or as the raw 16-byte chunk when keys and q share a 16-bit type.
@@ -249,7 +258,7 @@ __global__ __launch_bounds__(256) void decode_wave_kernel(AttnArgs a) {
   // Loads of one block's K and V tiles; false for a table entry outside the
   // pool, which is skipped as if masked.
   auto load_block = [&](int k, u32x4 (&kr)[NL], u32x4 (&vr)[NL], float& ksc, float& vsc) {
-    if (k > 0 && (k & 63) == 0) tc.fetch(trow, b0, wave, k, bmax, a.bs_shift);
+    if (k > 0 && (k & 63) == 0) tc.fetch(trow, b0, wave, kWaves, k, bmax, a.bs_shift);
     const int p = tc.get(k);
     if (p < 0 || p >= a.num_blocks) return false;
     const int64_t toff = tile_index(a, p, kvh, b0 + wave + kWaves * k) * TILE;
@@ -350,10 +359,10 @@ pkv_status launch_d(const AttnArgs& a, int group, hipStream_t st) {
   for (int c : {8, 4, 2}) if (group % c == 0) { gw = c; break; }
   dim3 grid(a.num_parts * a.num_rows * (a.hq / gw));
   switch (gw) {
-    case 1: hipLaunchKernelGGL((decode_wave_kernel<QT, KT, D, 1>), grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((decode_wave_kernel<QT, KT, D, 2>), grid, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((decode_wave_kernel<QT, KT, D, 4>), grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL((decode_wave_kernel<QT, KT, D, 8>), grid, dim3(256), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((decode_wave_kernel<QT, KT, D, 1>), grid, dim3(64 * kWaves), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((decode_wave_kernel<QT, KT, D, 2>), grid, dim3(64 * kWaves), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((decode_wave_kernel<QT, KT, D, 4>), grid, dim3(64 * kWaves), 0, st, a); break;
+    default: hipLaunchKernelGGL((decode_wave_kernel<QT, KT, D, 8>), grid, dim3(64 * kWaves), 0, st, a); break;
   }
   PKV_LAUNCH_CHECK("paged attention (wavefront)");
   return PKV_OK;
