@@ -16,8 +16,10 @@ held back and handed to reshape_and_cache inside the step.
 
 One step (timed, inputs resident in HBM): reshape_and_cache of the 64 new
 K/V rows through the slot mapping -> split-K paged decode attention (main
-kernel) -> partition reduce.  HIP events on the launch stream bracket each
-kernel; the main kernel's average duration gives the roofline figure.
+kernel) -> partition reduce.  The timed steps run back to back with
+nothing between their launches; a second, instrumented pass of as many
+steps brackets each kernel with HIP events on the launch stream, and the
+main kernel's average duration there gives the roofline figure.
 
 The printed JSON line carries the step throughput in KV GB/s (algorithmic
 bytes: K/V rows every sequence attends to, q, out, the table entries and
@@ -160,19 +162,26 @@ def cpu_baseline(wl: Workload, min_seconds: float = 10.0, max_reps: int = 8):
 # timing
 # ---------------------------------------------------------------------------
 def run_timed(torch, step, steps: int, warmup: int, nseg: int):
-    """Warm up, then time `steps` calls of step(events) between two device
-    synchronisations.  step records nseg + 1 events on the launch stream
-    around its kernels; returns (ms per step, [per-segment ms lists])."""
+    """Warm up, then time `steps` calls of step(None) between two device
+    synchronisations: the step's own launches only, nothing recorded between
+    them.  A second pass of `steps` calls then has step record nseg + 1
+    events on the launch stream around its kernels (an event between two
+    kernels adds a few microseconds of its own, so that pass gives the
+    per-kernel durations but not the step time).  Returns (ms per step of
+    the first pass, [per-segment ms lists of the second])."""
     for _ in range(warmup):
         step(None)
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(None)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nseg + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     segs = [[e[j].elapsed_time(e[j + 1]) for e in evs] for j in range(nseg)]
     return wall * 1e3 / steps, segs
 
