@@ -458,7 +458,10 @@ pkv_status pkv_paged_attention_reduce(void* out, pkv_dtype out_dtype, const int3
  *                  bytes (may be NULL when that is 0), 256-byte aligned.
  * q_dtype F16/BF16 with kv_dtype equal to it (MFMA path), or F32 throughout
  * (wavefront path, one query row at a time).  Supported head_dim 64/128,
- * block_size 16/32/64/128, group (num_q_heads / num_kv_heads) of any size. */
+ * block_size 16/32/64/128, group (num_q_heads / num_kv_heads) of any size.
+ * With num_query_tokens = 0 (no sequences, or only empty chunks) the call
+ * checks its sizes and returns PKV_OK without launching; out and q may then
+ * be NULL. */
 size_t pkv_prefill_workspace_bytes(int32_t num_query_tokens, int32_t num_q_heads,
                                    int32_t head_dim, int32_t max_context_len,
                                    int32_t partition_tokens);

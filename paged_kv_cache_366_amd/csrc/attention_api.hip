@@ -64,8 +64,8 @@ int block_shift(int32_t bs) {
 pkv_status check_common(const char* who, void* out, pkv_dtype out_dt, const void* q,
                         pkv_dtype q_dt, const void* kc, const void* vc, pkv_dtype kv_dt,
                         const float* ks, const float* vs, const int32_t* tables, int32_t mb,
-                        const int32_t* lens, int32_t max_ctx, int32_t S, int32_t hq, int32_t hkv,
-                        int32_t D, int32_t bs, int32_t nb, float scale) {
+                        const int32_t* lens, int32_t max_ctx, int32_t S, int32_t rows,
+                        int32_t hq, int32_t hkv, int32_t D, int32_t bs, int32_t nb, float scale) {
   if (S < 0 || hq <= 0 || hkv <= 0 || nb <= 0 || mb < 0 || max_ctx < 0)
     return fail(PKV_ERR_INVALID, "%s: bad sizes (S=%d Hq=%d Hkv=%d NB=%d MB=%d max_ctx=%d)", who,
                 S, hq, hkv, nb, mb, max_ctx);
@@ -88,7 +88,9 @@ pkv_status check_common(const char* who, void* out, pkv_dtype out_dt, const void
   if (has_scales(kv_dt) && (!ks || !vs))
     return fail(PKV_ERR_INVALID, "%s: %s KV needs k_scale and v_scale", who, dtype_name(kv_dt));
   if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID, "%s: scale is not finite", who);
-  if (S > 0 && (!out || !q || !kc || !vc || !tables || !lens))
+  // q and out are read only when there are query rows (a prefill batch may
+  // hold sequences whose chunks are all empty)
+  if ((rows > 0 && (!out || !q)) || (S > 0 && (!kc || !vc || !tables || !lens)))
     return fail(PKV_ERR_INVALID, "%s: NULL pointer", who);
   if (!aligned(kc, 16) || !aligned(vc, 16) || !aligned(q, 16) || !aligned(out, 4))
     return fail(PKV_ERR_INVALID, "%s: q, k_cache and v_cache must be 16-byte aligned", who);
@@ -137,7 +139,7 @@ pkv_status decode_impl(DecodePart which, void* out, pkv_dtype out_dt, const void
                        int32_t algo, void* ws, size_t ws_bytes, void* stream) {
   const char* who = "paged_attention_decode";
   pkv_status st = check_common(who, out, out_dt, q, q_dt, kc, vc, kv_dt, ks, vs, tables, mb, lens,
-                               max_ctx, S, hq, hkv, D, bs, nb, scale);
+                               max_ctx, S, S, hq, hkv, D, bs, nb, scale);
   if (st) return st;
   if (part_tokens < 0 || part_tokens % 16 != 0)
     return fail(PKV_ERR_INVALID, "%s: partition_tokens %d must be 0 or a multiple of 16", who,
@@ -300,8 +302,8 @@ pkv_status pkv_paged_attention_prefill(
     const char* who = "paged_attention_prefill";
     pkv_status st = check_common(who, out, out_dtype, q, q_dtype, k_cache, v_cache, kv_dtype,
                                  k_scale, v_scale, block_tables, max_blocks_per_seq, context_lens,
-                                 max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                 block_size, num_blocks, scale);
+                                 max_context_len, num_seqs, num_query_tokens, num_q_heads,
+                                 num_kv_heads, head_dim, block_size, num_blocks, scale);
     if (st) return st;
     if (num_query_tokens < 0 || max_query_len < 0 || max_query_len > max_context_len)
       return fail(PKV_ERR_INVALID, "%s: bad query sizes", who);
