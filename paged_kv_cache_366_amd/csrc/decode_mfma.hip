@@ -141,10 +141,8 @@ __global__ __launch_bounds__(64 * mfma_waves<KT>()) void decode_mfma_kernel(Attn
       }
     }
     if constexpr (kOffset) {
-      qlo += __shfl_xor(qlo, 16);
-      qlo += __shfl_xor(qlo, 32);
-      qhi += __shfl_xor(qhi, 16);
-      qhi += __shfl_xor(qhi, 32);
+      qlo = sum_xor32(sum_xor16(qlo));
+      qhi = sum_xor32(sum_xor16(qhi));
       kcorr = M::kOffsetLo4 * qlo + M::kOffsetHi4 * qhi;
     }
   }
@@ -231,8 +229,7 @@ __global__ __launch_bounds__(64 * mfma_waves<KT>()) void decode_mfma_kernel(Attn
         sv[i] = valid ? (kOffset ? fmaf(s[i], sc, nc) : s[i] * sc) : kNegInf;
         tmax = fmaxf(tmax, sv[i]);
       }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      tmax = max_xor32(max_xor16(tmax));
       const bool grow = tmax > m + kRescaleSlack;
       if (__any(grow)) {   // rare after the first tiles: skips the accumulator rescale
         const float mn = grow ? tmax : m;
@@ -330,8 +327,7 @@ __global__ __launch_bounds__(64 * mfma_waves<KT>()) void decode_mfma_kernel(Attn
   }
 
   // Sum of each head's weights over its four lanes.
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  l = sum_xor32(sum_xor16(l));
 
   __shared__ float sm_o[kWaves][16][D];
   __shared__ float sm_m[kWaves][16];

@@ -138,6 +138,31 @@ __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
+// Combination of lane l with lane l ^ 16 (or l ^ 32), the same in every lane.
+// v_permlane16_swap exchanges the odd 16-lane rows of its first operand with
+// the even rows of its second (v_permlane32_swap: the upper 32 lanes of the
+// first with the lower 32 of the second); with x in both operands, the two
+// results hold x's even and odd rows (lower and upper halves), so a
+// commutative op of the two results is op(x[l], x[l ^ 16]) in every lane.
+// Both run in the VALU; a lane shuffle by 16 or 32 is an LDS permute that
+// the wavefront then waits on.
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Sum over aligned groups of N consecutive lanes (N = 8, 16, 32 or 64); every
 // lane of a group receives the group's sum.
 template <int N>
@@ -147,8 +172,8 @@ __device__ __forceinline__ float group_sum(float v) {
   v += dpp<PKV_DPP_QUAD_XOR2>(v);
   if (N >= 8) v += dpp<PKV_DPP_ROW_HALF_MIRROR>(v);
   if (N >= 16) v += dpp<PKV_DPP_ROW_MIRROR>(v);
-  if (N >= 32) v += __shfl_xor(v, 16);
-  if (N >= 64) v += __shfl_xor(v, 32);
+  if (N >= 32) v = sum_xor16(v);
+  if (N >= 64) v = sum_xor32(v);
   return v;
 }
 

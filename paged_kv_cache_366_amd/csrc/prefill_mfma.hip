@@ -258,8 +258,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
       // some lane of the wave exceeds it are the row maxima taken across
       // the lane groups (the same value in all four) and the row rescaled.
       if (__any(tmax > m[r] + kRescaleSlack)) {   // rare after the first blocks
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        tmax = max_xor32(max_xor16(tmax));
         const bool grow = tmax > m[r] + kRescaleSlack;
         const float mn = grow ? tmax : m[r];
         const float alpha = grow ? fast_exp2(m[r] - mn) : 1.f;
@@ -327,8 +326,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
   for (int r = 0; r < R; ++r) {
     // Each lane summed the weights of its 4 keys per block; add the 4 groups.
     float lr = l[r];
-    lr += __shfl_xor(lr, 16);
-    lr += __shfl_xor(lr, 32);
+    lr = sum_xor32(sum_xor16(lr));
     if (!qlive[r]) continue;
     // Partitions the row's own keys span (as the reduce counts them): one
     // means this workgroup (partition 0) writes the final row; more mean
