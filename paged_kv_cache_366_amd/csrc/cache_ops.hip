@@ -90,11 +90,7 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
 // stored two per byte, element 2i in the low nibble.
 constexpr float kSmallestNormal = 1.17549435e-38f;
 
-__device__ __forceinline__ float wave_absmax(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
-}
+__device__ __forceinline__ float wave_absmax(float v) { return group_max<64>(v); }
 
 template <int BITS> constexpr float kCodeMax = BITS == 8 ? 127.f : 7.f;
 

@@ -177,6 +177,21 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Maximum over aligned groups of N consecutive lanes, the same steps as
+// group_sum; every lane of a group receives the group's maximum.  All lanes
+// of the wavefront must be active.
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+  static_assert(N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group size");
+  v = fmaxf(v, dpp<PKV_DPP_QUAD_XOR1>(v));
+  v = fmaxf(v, dpp<PKV_DPP_QUAD_XOR2>(v));
+  if (N >= 8) v = fmaxf(v, dpp<PKV_DPP_ROW_HALF_MIRROR>(v));
+  if (N >= 16) v = fmaxf(v, dpp<PKV_DPP_ROW_MIRROR>(v));
+  if (N >= 32) v = max_xor16(v);
+  if (N >= 64) v = max_xor32(v);
+  return v;
+}
+
 __device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

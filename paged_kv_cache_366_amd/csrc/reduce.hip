@@ -23,16 +23,8 @@ namespace {
 constexpr int kReduceThreads = 256;
 constexpr int kReduceWeights = 1024;   // partitions whose weights are cached in LDS
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
-}
+__device__ __forceinline__ float wave_max(float v) { return group_max<64>(v); }
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 
 __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(AttnArgs a, int D) {
   const int h = blockIdx.x % a.hq;
