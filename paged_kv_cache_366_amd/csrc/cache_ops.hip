@@ -94,10 +94,20 @@ __device__ __forceinline__ float wave_absmax(float v) { return group_max<64>(v);
 
 template <int BITS> constexpr float kCodeMax = BITS == 8 ? 127.f : 7.f;
 
-// The code of x under scale s > 0 (float32 division, ties to even).
+// The code of x under scale s > 0: rint(x / s) of the float32 quotient
+// (ties to even), clamped to [-Q, Q]; r is float32(1 / s).  Every caller has
+// |x / s| <= Q (1 + 2^-23) with Q <= 127, so x * r lies within
+// 2^-23 |x / s| < 1.6e-5 of x / s and the float32 quotient within half an
+// ulp (< 3.9e-6); their rint can differ only if x * r is within 2e-5 of a
+// half-integer.  Values within 2^-14 of one (about 1 in 8,000) take the
+// division; the others round x * r.
+constexpr float kHalfSlack = 6.103515625e-05f;   // 2^-14
 template <int BITS>
-__device__ __forceinline__ int encode_one(float x, float s) {
-  return static_cast<int>(fminf(fmaxf(rintf(x / s), -kCodeMax<BITS>), kCodeMax<BITS>));
+__device__ __forceinline__ int encode_one(float x, float s, float r) {
+  const float qf = x * r;
+  float q = rintf(qf);
+  if (!(fabsf(qf - q) < 0.5f - kHalfSlack)) q = rintf(x / s);
+  return static_cast<int>(fminf(fmaxf(q, -kCodeMax<BITS>), kCodeMax<BITS>));
 }
 
 // Stores E codes at d: one byte each, or two per byte (4-bit).
@@ -198,6 +208,7 @@ __global__ __launch_bounds__(kThreads) void quantize_blocks_kernel(
   amax = wave_absmax(amax);
   float sc = amax / kCodeMax<BITS>;
   if (!(sc >= kSmallestNormal)) sc = 0.f;
+  const float rsc = sc > 0.f ? 1.f / sc : 0.f;
 
   auto encode = [&](int c, const u32x4& w) {
     int q[E];
@@ -205,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void quantize_blocks_kernel(
       float x[E];
       Unpack<T>::run(w, x);
 #pragma unroll
-      for (int e = 0; e < E; ++e) q[e] = encode_one<BITS>(x[e], sc);
+      for (int e = 0; e < E; ++e) q[e] = encode_one<BITS>(x[e], sc, rsc);
     } else {
 #pragma unroll
       for (int e = 0; e < E; ++e) q[e] = 0;
@@ -305,6 +316,7 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_quant_kernel(
   const float s_old = r0 > 0 ? scale[tix] : 0.f;
   float s_new = fmaxf(s_old, amax / kCodeMax<BITS>);
   if (!(s_new >= kSmallestNormal)) s_new = 0.f;
+  const float r_new = s_new > 0.f ? 1.f / s_new : 0.f;
 
   if (s_new > s_old && r0 > 0) {
     // existing rows: 16 bytes (128 / BITS codes) per lane step
@@ -314,7 +326,7 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_quant_kernel(
       load_codes<BITS>(*reinterpret_cast<const u32x4*>(dst + o), old);
       int q[N];
 #pragma unroll
-      for (int e = 0; e < N; ++e) q[e] = encode_one<BITS>(old[e] * s_old, s_new);
+      for (int e = 0; e < N; ++e) q[e] = encode_one<BITS>(old[e] * s_old, s_new, r_new);
       store_codes<BITS, N>(dst + o, q);
     }
   }
@@ -325,7 +337,7 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_quant_kernel(
       float x[E];
       Unpack<T>::run(*reinterpret_cast<const u32x4*>(src + (t + i) * stride + (c % ch) * 16), x);
 #pragma unroll
-      for (int e = 0; e < E; ++e) q[e] = encode_one<BITS>(x[e], s_new);
+      for (int e = 0; e < E; ++e) q[e] = encode_one<BITS>(x[e], s_new, r_new);
     } else {
 #pragma unroll
       for (int e = 0; e < E; ++e) q[e] = 0;
