@@ -52,8 +52,8 @@ BLOCK = 16
 # partition 384).  Valid only for the kernel sources whose hash is recorded;
 # a changed kernel reports null.
 TRAFFIC = {
-    "sources_sha1": "8aa2619a05324275d05a0e0595a9489b4d31c5c3",
-    "bytes_per_launch": 1092157 * 1024 + 3417 * 1024,
+    "sources_sha1": "e288b4f2213faef80f062da20e213c2b4fc53cea",
+    "bytes_per_launch": 1091072 * 1024 + 3379 * 1024,
 }
 KERNEL_SOURCES = ("decode_wave.hip", "attention_common.h", "device_common.h")
 
@@ -623,6 +623,9 @@ def bench_beam(a, torch, pkv, algo):
     tables, lens = pkv.pkv_seq_export(bm, beams, mb)
     host_us = (time.perf_counter() - t0) * 1e6
     stats = pkv.pkv_bm_stats_get(bm)
+    # beams share the prompt's blocks (the block manager counts them): K/V
+    # loads stay cached, so a block read by one beam serves the others
+    load_policy = pkv.PKV_KV_CACHED if stats["shared_blocks"] > 0 else 0
     pairs_d = torch.from_numpy(np.ascontiguousarray(pairs, np.int32).reshape(-1, 2)).to(dev)
     slots_d = torch.from_numpy(slots.astype(np.int32)).to(dev)
     bk, bv = to_dev_bf16(bc.beam_k, torch), to_dev_bf16(bc.beam_v, torch)
@@ -630,7 +633,9 @@ def bench_beam(a, torch, pkv, algo):
     t_d, l_d = torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev)
     S = len(beams)
     mc = int(lens.max())
-    part = a.partition
+    # the 64 beams' contexts are nearly equal (1,025-1,225 tokens) and fill
+    # the GPU unsplit, so one partition per context is the default here
+    part = a.partition if a.partition_set else 0
     out = torch.empty((S, hq, D), dtype=torch.float32, device=dev)
     ws = torch.empty(max(pkv.pkv_decode_workspace_bytes(S, hq, D, mc, part), 1),
                      dtype=torch.uint8, device=dev)
@@ -645,7 +650,7 @@ def bench_beam(a, torch, pkv, algo):
         if ev is not None:
             ev[1].record(stream)
         pkv.pkv_paged_attention_decode_partials(out, q, kc, vc, t_d, l_d, mc, float(bc.scale),
-                                                part, algo, workspace=ws)
+                                                part, algo | load_policy, workspace=ws)
         pkv.pkv_paged_attention_reduce(out, l_d, mc, part, ws)
         if ev is not None:
             ev[2].record(stream)
@@ -672,7 +677,8 @@ def bench_beam(a, torch, pkv, algo):
         "workload": "shared-prefix beam search with copy-on-write, bf16: 16 requests sharing a "
                     "1024-token prefix, 1-200 own tokens, beam width 4; step = copy_blocks of the "
                     "shared partial tails + reshape_and_cache of 64 tokens + decode + reduce",
-        "partition_tokens": part, "algo": a.algo, "cow_pairs": int(len(pairs))})
+        "partition_tokens": part, "algo": a.algo, "cow_pairs": int(len(pairs)),
+        "kv_loads": "cached" if load_policy else "pool-size rule"})
     result.update({
         "tokens_per_s": S / (ms_per_step * 1e-3),
         "kernel_ms": {"copy_blocks_and_reshape": float(np.mean(cow_ms)),
@@ -1029,8 +1035,8 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", choices=WORKLOADS, default="decode7b",
                     help="decode7b is the headline line; the others measure the other kernels")
     ap.add_argument("--partition", type=int, default=None,
-                    help="split-K partition size in tokens (0 = no split); default 384, or 512 "
-                         "for the long-context GQA workloads")
+                    help="split-K partition size in tokens (0 = no split); default 384, 512 "
+                         "for the long-context GQA workloads, 0 for the beam workload")
     ap.add_argument("--algo", choices=("auto", "wave", "mfma"), default="auto")
     ap.add_argument("--prefill-partition", type=int, default=0,
                     help="key partition size of chunked prefill in tokens (0 = no split)")

@@ -15,8 +15,8 @@ import numpy as np
 
 from ._lib import (PKV_ALGO_AUTO, PKV_ALGO_MFMA, PKV_ALGO_WAVE, PKV_BF16, PKV_ERR_DEVICE,  # noqa
                    PKV_ERR_INTERNAL, PKV_ERR_INVALID, PKV_ERR_OUT_OF_BLOCKS, PKV_ERR_UNSUPPORTED,
-                   PKV_F16, PKV_F32, PKV_I4, PKV_I8, PKV_OK, LIB_PATH, PkvBmStats, PkvError, PkvSwapStats,
-                   PkvOutOfBlocks, check, load)
+                   PKV_F16, PKV_F32, PKV_I4, PKV_I8, PKV_KV_CACHED, PKV_KV_STREAM, PKV_OK, LIB_PATH,
+                   PkvBmStats, PkvError, PkvSwapStats, PkvOutOfBlocks, check, load)
 
 __all__ = [n for n in dir() if n.startswith("pkv_") or n.startswith("PKV_")]
 

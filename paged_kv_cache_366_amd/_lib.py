@@ -14,6 +14,7 @@ PKV_OK, PKV_ERR_INVALID, PKV_ERR_OUT_OF_BLOCKS, PKV_ERR_UNSUPPORTED, PKV_ERR_DEV
     PKV_ERR_INTERNAL = range(6)
 PKV_F32, PKV_F16, PKV_BF16, PKV_I8, PKV_I4 = range(5)
 PKV_ALGO_AUTO, PKV_ALGO_WAVE, PKV_ALGO_MFMA = range(3)
+PKV_KV_STREAM, PKV_KV_CACHED = 0x10, 0x20   # K/V load policy, OR-ed into algo
 
 _i32, _i64, _f32, _sz, _vp = C.c_int32, C.c_int64, C.c_float, C.c_size_t, C.c_void_p
 _pi32 = C.POINTER(C.c_int32)

@@ -144,8 +144,10 @@ pkv_status decode_impl(DecodePart which, void* out, pkv_dtype out_dt, const void
   if (part_tokens < 0 || part_tokens % 16 != 0)
     return fail(PKV_ERR_INVALID, "%s: partition_tokens %d must be 0 or a multiple of 16", who,
                 part_tokens);
-  if (algo < PKV_ALGO_AUTO || algo > PKV_ALGO_MFMA)
-    return fail(PKV_ERR_INVALID, "%s: unknown algo %d", who, algo);
+  const int32_t policy = algo & (PKV_KV_STREAM | PKV_KV_CACHED);
+  algo &= ~(PKV_KV_STREAM | PKV_KV_CACHED);
+  if (algo < PKV_ALGO_AUTO || algo > PKV_ALGO_MFMA || policy == (PKV_KV_STREAM | PKV_KV_CACHED))
+    return fail(PKV_ERR_INVALID, "%s: unknown algo %d", who, algo | policy);
   const int group = hq / hkv;
   if (algo == PKV_ALGO_MFMA && !use_mfma(algo, q_dt, group))
     return fail(PKV_ERR_UNSUPPORTED, "%s: MFMA path needs 16-bit q and a group of at most 16",
@@ -185,6 +187,11 @@ pkv_status decode_impl(DecodePart which, void* out, pkv_dtype out_dt, const void
   a.part_tokens = parts > 1 ? part_tokens : std::max(16, (max_ctx + 15) / 16 * 16);
   a.out_kind = out_kind_of(out_dt);
   a.scale_log2 = scale * kLog2e;
+  // Stream the K/V loads unless the pool fits in the memory-side cache
+  // (then blocks shared by several sequences can be served from it).
+  const double pool_bytes = 2.0 * nb * hkv * bs * static_cast<double>(row_bytes(kv_dt, D));
+  a.stream_kv = policy == PKV_KV_STREAM ||
+                (policy == 0 && pool_bytes > static_cast<double>(PKV_KV_CACHE_BYTES));
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (which != DecodePart::kReduce) {
     st = use_mfma(algo, q_dt, group) ? launch_decode_mfma(a, q_dt, kv_dt, D, group, hs)

@@ -30,6 +30,7 @@ struct AttnArgs {
   int part_tokens;           // tokens per partition (multiple of 16)
   int out_kind;
   float scale_log2;          // scale * log2(e): scores are kept in the log2 domain
+  bool stream_kv;            // decode K/V loads carry the non-temporal hint
 };
 
 // Which sequence a query row belongs to.  Decode: row s is sequence s.

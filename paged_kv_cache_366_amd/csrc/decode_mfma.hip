@@ -73,7 +73,7 @@ constexpr int mfma_waves() {
 constexpr int kUnroll = PKV_MFMA_UNROLL;   // tiles of K and V in flight per wavefront
 static_assert(64 % kUnroll == 0, "the unroll must divide the table chunk");
 
-template <typename QT, typename KT, int D>
+template <typename QT, typename KT, int D, bool NTV>
 __global__ __launch_bounds__(64 * mfma_waves<KT>()) void decode_mfma_kernel(AttnArgs a,
                                                                               int group) {
   constexpr int kWaves = mfma_waves<KT>();
@@ -181,11 +181,16 @@ __global__ __launch_bounds__(64 * mfma_waves<KT>()) void decode_mfma_kernel(Attn
       phys[u] = p;
       if (p >= 0) {
         const int64_t toff = tile_index(a, p, kvh, b0 + wave + kWaves * (k + u)) * TILE;
+        // Value loads cover whole rows; with NTV (the streaming load
+        // policy) they carry the non-temporal hint, so tiles read once pass
+        // through the caches without evicting what is reused.  Key loads
+        // take parts of each row over several instructions and stay cached
+        // (streaming them measured slower for every storage type).
 #pragma unroll
         for (int kk = 0; kk < NKL; ++kk)
-          kr[u][kk] = load_bytes<KB>(kc + toff + koff + kk * 32 * KT::bytes);
+          kr[u][kk] = load_kv_bytes<KB, false>(kc + toff + koff + kk * 32 * KT::bytes);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vr[u][e] = load_bytes<VB>(vc + toff + voff + e * ROW);
+        for (int e = 0; e < 4; ++e) vr[u][e] = load_kv_bytes<VB, NTV>(vc + toff + voff + e * ROW);
       }
     }
 #pragma unroll
@@ -350,13 +355,21 @@ __global__ __launch_bounds__(64 * mfma_waves<KT>()) void decode_mfma_kernel(Attn
                              threadIdx.x, blockDim.x);
 }
 
-template <typename QT, typename KT>
-pkv_status launch_qk(const AttnArgs& a, int D, int group, hipStream_t st) {
+template <typename QT, typename KT, bool NTV>
+void launch_nt(const AttnArgs& a, int D, int group, hipStream_t st) {
   dim3 grid(a.num_parts * a.num_rows * a.hkv);
   if (D == 64)
-    hipLaunchKernelGGL((decode_mfma_kernel<QT, KT, 64>), grid, dim3(64 * mfma_waves<KT>()), 0, st, a, group);
+    hipLaunchKernelGGL((decode_mfma_kernel<QT, KT, 64, NTV>), grid, dim3(64 * mfma_waves<KT>()), 0, st, a, group);
   else
-    hipLaunchKernelGGL((decode_mfma_kernel<QT, KT, 128>), grid, dim3(64 * mfma_waves<KT>()), 0, st, a, group);
+    hipLaunchKernelGGL((decode_mfma_kernel<QT, KT, 128, NTV>), grid, dim3(64 * mfma_waves<KT>()), 0, st, a, group);
+}
+
+template <typename QT, typename KT>
+pkv_status launch_qk(const AttnArgs& a, int D, int group, hipStream_t st) {
+  if (a.stream_kv)
+    launch_nt<QT, KT, true>(a, D, group, st);
+  else
+    launch_nt<QT, KT, false>(a, D, group, st);
   PKV_LAUNCH_CHECK("paged attention (MFMA)");
   return PKV_OK;
 }

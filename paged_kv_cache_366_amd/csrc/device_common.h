@@ -192,6 +192,14 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// Loads of K/V tiles, which a kernel reads once; NT adds the non-temporal
+// hint.
+template <typename V, bool NT>
+__device__ __forceinline__ V load_kv(const void* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(static_cast<const V*>(p));
+  else return *static_cast<const V*>(p);
+}
+
 __device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -110,6 +110,25 @@ __device__ __forceinline__ u32x4 load_bytes(const uint8_t* p) {
   return r;
 }
 
+// load_bytes for K/V tiles in global memory (see load_kv).
+template <int B, bool NT>
+__device__ __forceinline__ u32x4 load_kv_bytes(const uint8_t* p) {
+  u32x4 r = {0u, 0u, 0u, 0u};
+  if constexpr (B == 16) {
+    r = load_kv<u32x4, NT>(p);
+  } else if constexpr (B == 8) {
+    const u32x2 v = load_kv<u32x2, NT>(p);
+    r.x = v.x;
+    r.y = v.y;
+  } else if constexpr (B == 4) {
+    r.x = load_kv<uint32_t, NT>(p);
+  } else {
+    static_assert(B == 2, "load width");
+    r.x = load_kv<uint16_t, NT>(p);
+  }
+  return r;
+}
+
 __device__ __forceinline__ uint32_t dw(const u32x4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }

@@ -232,3 +232,40 @@ def test_gqa_long_full_size_sampled(int8):
     assert err <= TOL16, err
     del d
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("kind", ["mha-bf16", "mha-int8", "gqa-bf16", "gqa-int8", "gqa-int4"])
+def test_load_policy_changes_no_bit(kind):
+    """Streaming (non-temporal) and cached K/V loads, forced either way or
+    left to the pool-size rule, give the same bits on both kernels; both
+    flags together are rejected."""
+    mha = kind.startswith("mha")
+    hq, hkv = (8, 8) if mha else (16, 2)
+    c = W.decode_case(80, 5, hq, hkv, 128, lens=[1, 37, 300, 777, 1500], dtype="bf16",
+                      int8=kind.endswith("int8"), int4=kind.endswith("int4"))
+    q = to_dev(c.q, "bf16")
+    if kind.endswith("int8"):
+        k, v = torch.from_numpy(c.k_i8).to(DEV), torch.from_numpy(c.v_i8).to(DEV)
+        ks, vs = torch.from_numpy(c.k_scale).to(DEV), torch.from_numpy(c.v_scale).to(DEV)
+    elif kind.endswith("int4"):
+        k, v = torch.from_numpy(c.k_i4).to(DEV), torch.from_numpy(c.v_i4).to(DEV)
+        ks, vs = torch.from_numpy(c.k_scale4).to(DEV), torch.from_numpy(c.v_scale4).to(DEV)
+    else:
+        k, v = to_dev(c.k_cache, "bf16"), to_dev(c.v_cache, "bf16")
+        ks = vs = None
+    tables, lens = i32(c.block_tables), i32(c.context_lens)
+    algos = [pkv.PKV_ALGO_WAVE] + ([] if mha else [pkv.PKV_ALGO_MFMA])
+    for algo in algos:
+        for parts in (0, 256):
+            outs = []
+            for policy in (0, pkv.PKV_KV_STREAM, pkv.PKV_KV_CACHED):
+                out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+                pkv.pkv_paged_attention_decode(out, q, k, v, tables, lens, 1500, float(c.scale),
+                                               parts, algo | policy, ks, vs)
+                torch.cuda.synchronize()
+                outs.append(out.cpu())
+            assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_paged_attention_decode(out, q, k, v, tables, lens, 1500, float(c.scale), 0,
+                                       pkv.PKV_KV_STREAM | pkv.PKV_KV_CACHED, ks, vs)
