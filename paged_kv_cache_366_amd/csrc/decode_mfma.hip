@@ -26,6 +26,11 @@
 //       product j sees elements m*D/16 + j of those four rows.  The
 //       accumulator of head h stays in lanes h, so the rescale by the softmax
 //       correction is lane-local.
+//   int8 keys: the contraction order over head_dim is free, so lane
+//   (t, kg) reads 16 consecutive codes of key row t at byte 16kg + 64j
+//   (j < D / 64) and product kk takes the half kk % 2 of load kk / 2; Q^T
+//   takes the same elements.  Half as many key loads as one per product,
+//   each covering half of every row it touches (about 6% faster).
 //   4-bit keys: the contraction order over head_dim is free, so lane
 //   (t, kg) reads elements kg*D/4 .. +D/4-1 of key row t in one load (16
 //   bytes at head_dim 128) and Q^T takes the same elements; 4-bit values
@@ -82,8 +87,9 @@ __global__ __launch_bounds__(64 * mfma_waves<KT>()) void decode_mfma_kernel(Attn
   constexpr bool kScaled = kInt4 || kInt8;    // codes with per-tile scales
   constexpr int NK = D / 32;                  // QK products per tile
   constexpr int NV = D / 16;                  // PV products per tile (= elements per lane row)
-  constexpr int NKL = kInt4 ? 1 : NK;         // K loads per lane and tile
-  constexpr int KB = kInt4 ? D / 8 : 8 * KT::bytes;   // bytes of one lane's K load
+  constexpr bool kWideK8 = kInt8;              // int8 keys: 16 codes per lane load
+  constexpr int NKL = kInt4 ? 1 : kWideK8 ? NK / 2 : NK;   // K loads per lane and tile
+  constexpr int KB = kInt4 ? D / 8 : kWideK8 ? 16 : 8 * KT::bytes;   // bytes of one lane's K load
   constexpr int VB = NV * KT::bits / 8;       // bytes of one lane's V chunk
   constexpr int ROW = D * KT::bits / 8;       // bytes of one token row
   constexpr int TILE = 16 * ROW;
@@ -120,7 +126,9 @@ __global__ __launch_bounds__(64 * mfma_waves<KT>()) void decode_mfma_kernel(Attn
     float qlo = 0.f, qhi = 0.f;   // q in low / high halves of the operand pairs
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
-      const int e0 = kInt4 ? kg * (D / 4) + 8 * kk : 32 * kk + 8 * kg;
+      const int e0 = kInt4     ? kg * (D / 4) + 8 * kk
+                     : kWideK8 ? 64 * (kk / 2) + 16 * kg + 8 * (kk % 2)
+                               : 32 * kk + 8 * kg;
       u32x4 v = *reinterpret_cast<const u32x4*>(qp + qrow + e0);
       v = live ? v : u32x4{0u, 0u, 0u, 0u};
       if constexpr (kInt4) {
@@ -164,7 +172,8 @@ __global__ __launch_bounds__(64 * mfma_waves<KT>()) void decode_mfma_kernel(Attn
   const uint8_t* kc = static_cast<const uint8_t*>(a.kc);
   const uint8_t* vc = static_cast<const uint8_t*>(a.vc);
   // lane offsets inside a tile
-  const int koff = r16 * ROW + (kInt4 ? kg * KB : 8 * kg * KT::bytes);   // + kk * 32 elements
+  const int koff = r16 * ROW + (kInt4 || kWideK8 ? kg * KB : 8 * kg * KT::bytes);
+  constexpr int KSTEP = kWideK8 ? 64 : 32 * KT::bytes;   // bytes between a lane's K loads
   const int voff = (4 * kg) * ROW + r16 * VB;                           // + e * ROW
 
   for (int k = 0; k < nbw; k += kUnroll) {
@@ -188,7 +197,7 @@ __global__ __launch_bounds__(64 * mfma_waves<KT>()) void decode_mfma_kernel(Attn
         // (streaming them measured slower for every storage type).
 #pragma unroll
         for (int kk = 0; kk < NKL; ++kk)
-          kr[u][kk] = load_kv_bytes<KB, false>(kc + toff + koff + kk * 32 * KT::bytes);
+          kr[u][kk] = load_kv_bytes<KB, false>(kc + toff + koff + kk * KSTEP);
 #pragma unroll
         for (int e = 0; e < 4; ++e) vr[u][e] = load_kv_bytes<VB, NTV>(vc + toff + voff + e * ROW);
       }
@@ -214,7 +223,9 @@ __global__ __launch_bounds__(64 * mfma_waves<KT>()) void decode_mfma_kernel(Attn
           kop = u32x4{M::fix4(magic_pair(M::kMagic4, lo, 0)), M::fix4(magic_pair(M::kMagic4, lo, 1)),
                       M::fix4(magic_pair(M::kMagic4, hi, 0)), M::fix4(magic_pair(M::kMagic4, hi, 1))};
         } else if constexpr (kInt8) {
-          const uint32_t w0 = kr[u][kk].x ^ 0x80808080u, w1 = kr[u][kk].y ^ 0x80808080u;
+          const u32x4& kw = kr[u][kWideK8 ? kk / 2 : kk];
+          const int h2 = kWideK8 ? 2 * (kk % 2) : 0;
+          const uint32_t w0 = dw(kw, h2) ^ 0x80808080u, w1 = dw(kw, h2 + 1) ^ 0x80808080u;
           kop = u32x4{M::int_pair(i8_exact(w0, 0), i8_exact(w0, 1)),
                       M::int_pair(i8_exact(w0, 2), i8_exact(w0, 3)),
                       M::int_pair(i8_exact(w1, 0), i8_exact(w1, 1)),
