@@ -125,7 +125,7 @@ def to_dev_bf16(x, torch):
     return torch.from_numpy(bits).to("cuda").view(torch.bfloat16)
 
 
-def cpu_baseline(wl: Workload, min_seconds: float = 10.0, max_reps: int = 8):
+def cpu_baseline(wl: Workload, min_seconds: float = 10.0, max_reps: int = 40):
     """The oracle over the whole batch, repeated until at least min_seconds."""
     from oracle import attention as A
 
