@@ -18,8 +18,9 @@ One step (timed, inputs resident in HBM): reshape_and_cache of the 64 new
 K/V rows through the slot mapping -> split-K paged decode attention (main
 kernel) -> partition reduce.  The timed steps run back to back with
 nothing between their launches; a second, instrumented pass of as many
-steps brackets each kernel with HIP events on the launch stream, and the
-main kernel's average duration there gives the roofline figure.
+steps, each after a 512 MB read that flushes the caches, brackets each
+kernel with HIP events on the launch stream, and the main kernel's average
+duration there gives the roofline figure.
 
 The printed JSON line carries the step throughput in KV GB/s (algorithmic
 bytes: K/V rows every sequence attends to, q, out, the table entries and
@@ -53,7 +54,7 @@ BLOCK = 16
 # a changed kernel reports null.
 TRAFFIC = {
     "sources_sha1": "e288b4f2213faef80f062da20e213c2b4fc53cea",
-    "bytes_per_launch": 1091072 * 1024 + 3379 * 1024,
+    "bytes_per_launch": 1092107 * 1024 + 3379 * 1024,
 }
 KERNEL_SOURCES = ("decode_wave.hip", "attention_common.h", "device_common.h")
 
@@ -161,14 +162,31 @@ def cpu_baseline(wl: Workload, min_seconds: float = 10.0, max_reps: int = 40):
 # ---------------------------------------------------------------------------
 # timing
 # ---------------------------------------------------------------------------
+FLUSH_BYTES = 512 << 20   # twice the 256 MB memory-side cache of an MI355X
+_flush_buf = None
+
+
+def flush_caches(torch) -> None:
+    """Reads FLUSH_BYTES of device memory, which evicts from the L2 caches and
+    the memory-side cache whatever a previous kernel left there.  A read, not
+    a write: a write would leave the caches full of dirty lines, and the next
+    kernel's reads would pay for writing them back."""
+    global _flush_buf
+    if _flush_buf is None:
+        _flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    _flush_buf.amax()
+
+
 def run_timed(torch, step, steps: int, warmup: int, nseg: int):
     """Warm up, then time `steps` calls of step(None) between two device
     synchronisations: the step's own launches only, nothing recorded between
     them.  A second pass of `steps` calls then has step record nseg + 1
-    events on the launch stream around its kernels (an event between two
-    kernels adds a few microseconds of its own, so that pass gives the
-    per-kernel durations but not the step time).  Returns (ms per step of
-    the first pass, [per-segment ms lists of the second])."""
+    events on the launch stream around its kernels, with a 512 MB read
+    before each call (outside the events) so that every call starts with
+    cold caches; an event between two kernels adds a few microseconds of its
+    own, so that pass gives the per-kernel durations but not the step time.
+    Returns (ms per step of the first pass, [per-segment ms lists of the
+    second])."""
     for _ in range(warmup):
         step(None)
     torch.cuda.synchronize()
@@ -180,6 +198,7 @@ def run_timed(torch, step, steps: int, warmup: int, nseg: int):
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nseg + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
+        flush_caches(torch)
         step(evs[i])
     torch.cuda.synchronize()
     segs = [[e[j].elapsed_time(e[j + 1]) for e in evs] for j in range(nseg)]
