@@ -370,6 +370,14 @@ pkv_status pkv_paged_attention_prefill(
     a.scale_log2 = scale * kLog2e;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const int group = num_q_heads / num_kv_heads;
+    // The matrix-core prefill streams K/V under the pool-size rule of decode
+    // when each tile has a single reader (see launch_prefill_mfma); the fp32
+    // wavefront rows of one chunk share their keys and keep cached loads.
+    if (q_dtype != PKV_F32) {
+      const double pool_bytes =
+          2.0 * num_blocks * num_kv_heads * block_size * static_cast<double>(row_bytes(kv_dtype, head_dim));
+      a.stream_kv = pool_bytes > static_cast<double>(PKV_KV_CACHE_BYTES);
+    }
     pkv_status ls = q_dtype == PKV_F32
                         ? launch_decode_wave(a, q_dtype, kv_dtype, head_dim, group, hs)
                         : launch_prefill_mfma(a, q_dtype, head_dim, group, max_query_len, hs);

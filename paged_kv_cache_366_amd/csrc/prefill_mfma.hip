@@ -73,7 +73,7 @@ constexpr int kGroup = PKV_PREFILL_GROUP;     // 16-key tiles per LDS step (one 
 constexpr int kRowTiles = PKV_PREFILL_RTILES; // 16-row tiles per wavefront
 constexpr int kTileRows = kPrefillWaves * 16 * kRowTiles;   // query rows per workgroup
 
-template <typename T, int D, int P, int R, int G0>
+template <typename T, int D, int P, int R, int G0, bool STREAM>
 __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs a, int max_tiles) {
   constexpr int NK = D / 32;              // QK products per block and row tile
   constexpr int NV = D / 16;              // PV products per block and row tile
@@ -185,8 +185,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
       int64_t off = toff[0];
 #pragma unroll
       for (int k = 1; k < G; ++k) off = g == k ? toff[k] : off;
-      rg[i] = *reinterpret_cast<const u32x4*>((rem < TILE_CHUNKS ? kc : vc) + off +
-                                              (rem % TILE_CHUNKS) * 16);
+      rg[i] = load_kv<u32x4, STREAM>((rem < TILE_CHUNKS ? kc : vc) + off + (rem % TILE_CHUNKS) * 16);
     }
   };
   auto sstore = [&](int buf, const u32x4 (&rg)[LPS], int st, const bool (&ok)[G]) {
@@ -357,17 +356,17 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
   }
 }
 
-template <typename T>
+template <typename T, bool NT>
 pkv_status launch_t(const AttnArgs& a, int D, int max_tiles, hipStream_t st) {
   const int64_t wgs = static_cast<int64_t>(a.num_seqs) * max_tiles * a.num_parts * a.hq;
   if (wgs > 0x7fffffff / kPrefillThreads)
     return fail(PKV_ERR_UNSUPPORTED, "prefill: launch too large");
   dim3 grid(static_cast<unsigned>(wgs));
   if (D == 64)
-    hipLaunchKernelGGL((prefill_mfma_kernel<T, 64, kDepth, kRowTiles, kGroup>), grid, dim3(kPrefillThreads), 0, st, a,
-                       max_tiles);
+    hipLaunchKernelGGL((prefill_mfma_kernel<T, 64, kDepth, kRowTiles, kGroup, NT>), grid, dim3(kPrefillThreads), 0, st,
+                       a, max_tiles);
   else
-    hipLaunchKernelGGL((prefill_mfma_kernel<T, 128, kDepth, kRowTiles, kGroup>), grid, dim3(kPrefillThreads), 0, st,
+    hipLaunchKernelGGL((prefill_mfma_kernel<T, 128, kDepth, kRowTiles, kGroup, NT>), grid, dim3(kPrefillThreads), 0, st,
                        a, max_tiles);
   PKV_LAUNCH_CHECK("chunked prefill (MFMA)");
   return PKV_OK;
@@ -377,11 +376,18 @@ pkv_status launch_t(const AttnArgs& a, int D, int max_tiles, hipStream_t st) {
 
 pkv_status launch_prefill_mfma(const AttnArgs& a, pkv_dtype q_dt, int D, int group,
                                int max_query_len, hipStream_t st) {
-  (void)group;
   if (max_query_len <= 0 || a.num_seqs <= 0) return PKV_OK;
   const int max_tiles = (max_query_len + kTileRows - 1) / kTileRows;
-  if (q_dt == PKV_BF16) return launch_t<BF16>(a, D, max_tiles, st);
-  if (q_dt == PKV_F16) return launch_t<F16>(a, D, max_tiles, st);
+  // A workgroup serves one query head and one row tile: when every chunk
+  // fits one row tile and no KV head serves several query heads, each K/V
+  // tile is read by one workgroup only, so (under the streaming policy) its
+  // loads carry the non-temporal hint; otherwise the other row tiles and
+  // heads reuse it from L2.
+  const bool stream = a.stream_kv && max_tiles == 1 && group == 1;
+  if (q_dt == PKV_BF16)
+    return stream ? launch_t<BF16, true>(a, D, max_tiles, st) : launch_t<BF16, false>(a, D, max_tiles, st);
+  if (q_dt == PKV_F16)
+    return stream ? launch_t<F16, true>(a, D, max_tiles, st) : launch_t<F16, false>(a, D, max_tiles, st);
   return fail(PKV_ERR_UNSUPPORTED, "MFMA prefill needs 16-bit q");
 }
 
