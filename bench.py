@@ -50,11 +50,11 @@ BLOCK = 16
 # HBM traffic of the main decode kernel per launch, from rocprofv3 --pmc
 # FETCH_SIZE (scaled by 1 / the factor an elementwise kernel that reads
 # exactly 1 GiB shows) plus WRITE_SIZE (factor 1.0) on this workload (seed 1,
-# partition 384).  Valid only for the kernel sources whose hash is recorded;
+# partition 1536).  Valid only for the kernel sources whose hash is recorded;
 # a changed kernel reports null.
 TRAFFIC = {
-    "sources_sha1": "e288b4f2213faef80f062da20e213c2b4fc53cea",
-    "bytes_per_launch": 1092107 * 1024 + 3379 * 1024,
+    "sources_sha1": "feded023f4481739d2e3582278df693e36948521",
+    "bytes_per_launch": 1092136 * 1024 + 1348 * 1024,
 }
 KERNEL_SOURCES = ("decode_wave.hip", "attention_common.h", "device_common.h")
 
@@ -1054,8 +1054,9 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", choices=WORKLOADS, default="decode7b",
                     help="decode7b is the headline line; the others measure the other kernels")
     ap.add_argument("--partition", type=int, default=None,
-                    help="split-K partition size in tokens (0 = no split); default 384, 512 "
-                         "for the long-context GQA workloads, 0 for the beam workload")
+                    help="split-K partition size in tokens (0 = no split); default 1536 for "
+                         "the 7B step, 1024 for the mixed step, 512 for the long-context GQA "
+                         "workloads, 0 for the beam workload")
     ap.add_argument("--algo", choices=("auto", "wave", "mfma"), default="auto")
     ap.add_argument("--prefill-partition", type=int, default=0,
                     help="key partition size of chunked prefill in tokens (0 = no split)")
@@ -1073,7 +1074,10 @@ def main(argv=None) -> int:
         return 2
     a.partition_set = a.partition is not None
     if a.partition is None:
-        a.partition = 384
+        # split-K partition per workload (the GQA and beam workloads choose
+        # their own): 1,536 tokens for the 7B step, whose streaming MHA decode
+        # then runs 16-wave workgroups, 1,024 for the mixed step's longer tail
+        a.partition = 1024 if a.workload == "mixed" else 1536
 
     import torch
     import paged_kv_cache_366_amd as pkv

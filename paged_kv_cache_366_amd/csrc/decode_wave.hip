@@ -47,13 +47,21 @@
 namespace pkv {
 namespace {
 
-// Wavefronts per workgroup.  Eight, with 384-token partitions, measured
-// about 2% faster than four (at their best partition, 256) at the 7B
-// shape: the prologue and the merge amortise over more tiles per workgroup.
+// Wavefronts per workgroup: 8, or 16 for a call that streams one head of
+// 16-bit K/V (MHA decode over a pool larger than the caches) with partitions
+// of at least kWideMinTokens.  Eight waves with 384-token partitions
+// measured about 2% faster than four at the 7B shape; sixteen waves with
+// 1,536-token partitions another 3% (the prologue and the merge amortise
+// over more tiles, and most contexts fit one partition and write no partial
+// state).  Sixteen waves lose with short partitions (1.5 tiles per wave at
+// 384 tokens) and on cache-resident shared blocks, and would not fit the
+// registers of a multi-head group.
 #ifndef PKV_WAVE_WAVES
 #define PKV_WAVE_WAVES 8
 #endif
-constexpr int kWaves = PKV_WAVE_WAVES;
+constexpr int kWavesDefault = PKV_WAVE_WAVES;
+constexpr int kWavesWide = 16;
+constexpr int kWideMinTokens = 1024;
 
 // Dot product of one 16-byte chunk of 16-bit keys with the matching q
 // chunk, both as packed pairs: v_dot2 forms the two exact products and adds
@@ -116,8 +124,9 @@ __device__ __forceinline__ uint32_t dword(const u32x4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-template <typename QT, typename KT, int D, int G, bool NT>
-__global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(AttnArgs a) {
+template <typename QT, typename KT, int D, int G, bool NT, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_wave_kernel(AttnArgs a) {
+  constexpr int kWaves = NW;
   // 4-bit codes are read as 8-byte chunks (16 codes, the register shape of
   // an int8 chunk); everything else as 16-byte chunks.
   constexpr int CB = KT::bits == 4 ? 8 : 16;    // bytes of one lane chunk
@@ -365,11 +374,21 @@ pkv_status launch_d(const AttnArgs& a, int group, hipStream_t st) {
   int gw = 1;
   for (int c : {8, 4, 2}) if (group % c == 0) { gw = c; break; }
   dim3 grid(a.num_parts * a.num_rows * (a.hq / gw));
+  const dim3 wg(64 * kWavesDefault);
   switch (gw) {
-    case 1: hipLaunchKernelGGL((decode_wave_kernel<QT, KT, D, 1, NT>), grid, dim3(64 * kWaves), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((decode_wave_kernel<QT, KT, D, 2, NT>), grid, dim3(64 * kWaves), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((decode_wave_kernel<QT, KT, D, 4, NT>), grid, dim3(64 * kWaves), 0, st, a); break;
-    default: hipLaunchKernelGGL((decode_wave_kernel<QT, KT, D, 8, NT>), grid, dim3(64 * kWaves), 0, st, a); break;
+    case 1:
+      if constexpr (KT::bits == 16 && NT) {
+        if (a.part_tokens >= kWideMinTokens) {
+          hipLaunchKernelGGL((decode_wave_kernel<QT, KT, D, 1, NT, kWavesWide>), grid,
+                             dim3(64 * kWavesWide), 0, st, a);
+          break;
+        }
+      }
+      hipLaunchKernelGGL((decode_wave_kernel<QT, KT, D, 1, NT, kWavesDefault>), grid, wg, 0, st, a);
+      break;
+    case 2: hipLaunchKernelGGL((decode_wave_kernel<QT, KT, D, 2, NT, kWavesDefault>), grid, wg, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((decode_wave_kernel<QT, KT, D, 4, NT, kWavesDefault>), grid, wg, 0, st, a); break;
+    default: hipLaunchKernelGGL((decode_wave_kernel<QT, KT, D, 8, NT, kWavesDefault>), grid, wg, 0, st, a); break;
   }
   PKV_LAUNCH_CHECK("paged attention (wavefront)");
   return PKV_OK;
