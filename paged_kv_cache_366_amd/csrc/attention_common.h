@@ -10,8 +10,8 @@ enum OutKind : int { kOutF32 = 0, kOutBF16 = 1, kOutF16 = 2 };
 
 struct AttnArgs {
   void* out;                 // [rows][Hq][D] final output
-  float* part_o;             // [rows][Hq][num_parts][D] partial outputs (NULL: no split)
-  float* part_ml;            // [rows][Hq][num_parts][2] partial (max, sum), log2 domain
+  float* part_o;             // [rows][num_parts][Hq][D] partial outputs (NULL: no split)
+  float* part_ml;            // [rows][num_parts][Hq][2] partial (max, sum), log2 domain
   const void* q;             // [rows][Hq][D]
   const void* kc;            // [NB][Hkv][16 << bs_shift][D]
   const void* vc;
@@ -135,6 +135,15 @@ __device__ __forceinline__ void merge_factors(float m1, float m2, float& m, floa
   f2 = fast_exp2(m2 - ms);
 }
 
+// Index of the partial state of (query row, head, partition) in part_o (in
+// units of D floats) and part_ml (pairs).  Partitions sit outside heads, so
+// the heads a workgroup merges for one partition are adjacent: a
+// grouped-query workgroup writes one contiguous run (8 heads x 128 floats)
+// and one run of (max, sum) pairs, not one per head.
+__device__ __forceinline__ int64_t part_slot(const AttnArgs& a, int64_t row, int h, int part) {
+  return (row * a.num_parts + part) * a.hq + h;
+}
+
 // Final merge of a workgroup: NW wavefronts each left, per head row g, a
 // softmax state (max m, sum l) and an unnormalised output row o[D] in LDS.
 // Rescales them to the common max and either writes the normalised output
@@ -164,7 +173,7 @@ __device__ __forceinline__ void finish_rows(const AttnArgs& a, const float (&sm_
     if (nparts <= 1) {
       store_out(a, orow * D + d, L > 0.f ? O / L : 0.f);
     } else {
-      const int64_t pi = orow * a.num_parts + part;
+      const int64_t pi = part_slot(a, row, hbase + g, part);
       a.part_o[pi * D + d] = O;
       if (d == 0) {
         a.part_ml[pi * 2] = M;

@@ -332,7 +332,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
     // each partition leaves its unnormalised output and (max, sum).
     const int rparts = a.num_parts > 1 ? (qlast[r] + a.part_tokens) / a.part_tokens : 1;
     if (part >= max(rparts, 1)) continue;
-    const int64_t grow = static_cast<int64_t>(qs + q0 + 16 * r + r16) * hq + h;
+    const int64_t qrow = qs + q0 + 16 * r + r16;
+    const int64_t grow = qrow * hq + h;
     if (rparts <= 1) {
       const float inv = lr > 0.f ? 1.f / lr : 0.f;
       // acc[r][j][i] is element NV*(4kg + i) + j of the row.
@@ -342,7 +343,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
         for (int j = 0; j < NV; ++j)
           store_out(a, grow * D + NV * (4 * kg + i) + j, acc[r][j][i] * inv);
     } else {
-      const int64_t slot = grow * a.num_parts + part;
+      const int64_t slot = part_slot(a, qrow, h, part);
       float* po = a.part_o + slot * D;
 #pragma unroll
       for (int i = 0; i < 4; ++i)

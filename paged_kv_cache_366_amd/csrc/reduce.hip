@@ -34,8 +34,12 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(AttnArgs a, int 
   const int nparts = (ctx + a.part_tokens - 1) / a.part_tokens;
   if (nparts <= 1) return;  // written by the main kernel
   const int64_t orow = static_cast<int64_t>(row) * a.hq + h;
-  const float* ml = a.part_ml + orow * a.num_parts * 2;
-  const float* po = a.part_o + orow * a.num_parts * D;
+  // partition p of this (row, head) is slot part_slot(a, row, h, p): the
+  // slots of consecutive partitions are hq apart
+  const float* ml = a.part_ml + part_slot(a, row, h, 0) * 2;
+  const float* po = a.part_o + part_slot(a, row, h, 0) * D;
+  const int64_t mls = 2 * static_cast<int64_t>(a.hq);   // floats between partitions' pairs
+  const int64_t pos = static_cast<int64_t>(a.hq) * D;   // floats between partitions' rows
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -44,7 +48,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(AttnArgs a, int 
   __shared__ float sacc[kReduceThreads];
 
   float mx = kNegInf;
-  for (int p = tid; p < nparts; p += kReduceThreads) mx = fmaxf(mx, ml[2 * p]);
+  for (int p = tid; p < nparts; p += kReduceThreads) mx = fmaxf(mx, ml[p * mls]);
   mx = wave_max(mx);
   if (lane == 0) red[0][wave] = mx;
   __syncthreads();
@@ -54,9 +58,9 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(AttnArgs a, int 
   const float ms = (M == kNegInf) ? 0.f : M;
   float ls = 0.f;
   for (int p = tid; p < nparts; p += kReduceThreads) {
-    const float w = fast_exp2(ml[2 * p] - ms);
+    const float w = fast_exp2(ml[p * mls] - ms);
     if (p < kReduceWeights) sw[p] = w;
-    ls += ml[2 * p + 1] * w;
+    ls += ml[p * mls + 1] * w;
   }
   ls = wave_sum(ls);
   if (lane == 0) red[1][wave] = ls;
@@ -71,8 +75,8 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(AttnArgs a, int 
   float O = 0.f;
 #pragma unroll 4
   for (int p = g; p < nparts; p += groups) {
-    const float w = p < kReduceWeights ? sw[p] : fast_exp2(ml[2 * p] - ms);
-    O += po[static_cast<int64_t>(p) * D + d] * w;
+    const float w = p < kReduceWeights ? sw[p] : fast_exp2(ml[p * mls] - ms);
+    O += po[p * pos + d] * w;
   }
   sacc[tid] = O;
   __syncthreads();
