@@ -124,10 +124,11 @@ def test_validation_rejects_a_chunk_longer_than_its_context(monkeypatch):
 
 
 # ---------------------------------------------------------------- mixed step
-def run_mixed_step(ms, sample_rows=None):
+def run_mixed_step(ms, sample_rows=None, decode_parts=(256,)):
     """Allocate through the block manager, write every new row through
-    reshape_and_cache, then run decode on the decode sequences and prefill
-    on the chunks.  The oracle side follows the same steps on host arrays."""
+    reshape_and_cache, then run decode on the decode sequences (once per
+    split-K partition size in `decode_parts`) and prefill on the chunks.
+    The oracle side follows the same steps on host arrays."""
     nb, hkv, d = ms.num_blocks, ms.kv_heads, ms.head_dim
     bm = pkv.pkv_bm_create(nb, 16, ms.perm)
     try:
@@ -163,10 +164,14 @@ def run_mixed_step(ms, sample_rows=None):
         starts = np.concatenate([[0], np.cumsum(ms.new)])
         qd_rows = starts[dec]
         qdev = to_dev(ms.q, ms.dtype)
-        out_d = torch.empty((len(dec),) + ms.q.shape[1:], dtype=torch.float32, device=DEV)
-        pkv.pkv_paged_attention_decode(out_d, qdev[torch.from_numpy(qd_rows).to(DEV)].contiguous(),
-                                       dk, dv, i32(tables[dec]), i32(lens[dec]),
-                                       int(lens[dec].max()), float(ms.scale), 256)
+        outs_d = []
+        for part in decode_parts:
+            out_d = torch.empty((len(dec),) + ms.q.shape[1:], dtype=torch.float32, device=DEV)
+            pkv.pkv_paged_attention_decode(out_d,
+                                           qdev[torch.from_numpy(qd_rows).to(DEV)].contiguous(),
+                                           dk, dv, i32(tables[dec]), i32(lens[dec]),
+                                           int(lens[dec].max()), float(ms.scale), part)
+            outs_d.append(out_d)
         qsl = np.concatenate([[0], np.cumsum(ms.new[pre])]).astype(np.int32)
         rows = np.concatenate([np.arange(starts[s], starts[s + 1]) for s in pre])
         qp = qdev[torch.from_numpy(rows).to(DEV)].contiguous()
@@ -177,7 +182,8 @@ def run_mixed_step(ms, sample_rows=None):
         torch.cuda.synchronize()
         # oracle
         ref_d = A.decode(ms.q[qd_rows], kc, vc, tables[dec], lens[dec], ms.scale)
-        assert np.abs(out_f64(out_d) - ref_d).max() <= TOL16
+        for part, out_d in zip(decode_parts, outs_d):
+            assert np.abs(out_f64(out_d) - ref_d).max() <= TOL16, part
         got = out_f64(out_p)
         if sample_rows is None:
             ref_p = A.prefill(ms.q[rows], kc, vc, tables[pre], qsl, lens[pre], ms.scale)
@@ -213,7 +219,9 @@ def test_mixed_step_full_size_sampled():
     # 48 decode sequences (contexts U[64, 4096]) and four 512-row chunks over
     # 0/512/1024/1536 cached tokens, 32 heads x 128, bf16
     ms = W.mixed_step(seed=2)
-    run_mixed_step(ms, sample_rows=6)
+    # 1,024-token partitions are the step's timed launch shape (its 1.6 GB
+    # pool streams, so the wavefront kernel runs 16-wave workgroups)
+    run_mixed_step(ms, sample_rows=6, decode_parts=(256, 1024))
 
 
 # ------------------------------------------------------------ split-K prefill

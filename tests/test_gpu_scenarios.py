@@ -82,12 +82,12 @@ class Both:
         pkv.pkv_bm_destroy(self.bm)
 
 
-def gpu_decode(both, q, tables, lens, scale, parts=256, dtype="bf16"):
+def gpu_decode(both, q, tables, lens, scale, parts=256, dtype="bf16", algo=pkv.PKV_ALGO_AUTO):
     qd = to_dev(q, dtype)
     out = torch.empty(qd.shape, dtype=torch.float32, device=DEV)
     mc = int(max(int(lens.max()), 1))
     pkv.pkv_paged_attention_decode(out, qd, both.dk, both.dv, i32(tables), i32(lens), mc,
-                                   float(scale), parts)
+                                   float(scale), parts, algo)
     torch.cuda.synchronize()
     return out_f64(out)
 
@@ -121,13 +121,17 @@ def run_beam_case(bc: W.BeamCase, check_every_beam=True):
         out = gpu_decode(both, bc.q, bt, bl, bc.scale)
         stats = pkv.pkv_bm_stats_get(both.bm)
         assert stats["shared_blocks"] > 0
+        # shared blocks: no split and cached K/V loads, as a serving step
+        # over beams would launch it
+        whole = gpu_decode(both, bc.q, bt, bl, bc.scale, parts=0,
+                           algo=pkv.PKV_ALGO_AUTO | pkv.PKV_KV_CACHED)
         if check_every_beam:
-            ref = A.decode(bc.q, both.kc, both.vc, bt, bl, bc.scale)
-            assert np.abs(out - ref).max() <= TOL16
+            idx = np.arange(len(beams))
         else:
             idx = np.random.default_rng(0).choice(len(beams), 6, replace=False)
-            ref = A.decode(bc.q[idx], both.kc, both.vc, bt[idx], bl[idx], bc.scale)
-            assert np.abs(out[idx] - ref).max() <= TOL16
+        ref = A.decode(bc.q[idx], both.kc, both.vc, bt[idx], bl[idx], bc.scale)
+        assert np.abs(out[idx] - ref).max() <= TOL16
+        assert np.abs(whole[idx] - ref).max() <= TOL16
         return pairs
     finally:
         both.close()
