@@ -30,7 +30,12 @@
 //   (t, kg) reads 16 consecutive codes of key row t at byte 16kg + 64j
 //   (j < D / 64) and product kk takes the half kk % 2 of load kk / 2; Q^T
 //   takes the same elements.  Half as many key loads as one per product,
-//   each covering half of every row it touches (about 6% faster).
+//   each covering half of every row it touches (about 6% faster).  Int8
+//   codes, sign-flipped to u = k + 128, enter both products as u (exact in
+//   bf16 and f16) after one byte convert each: scores carry 128 x (sum of
+//   the head's q), taken out with the score scale, and the value
+//   accumulators 128 x (sum of the weights), accumulated by one more product
+//   per tile against a constant operand and subtracted at the end.
 //   4-bit keys: the contraction order over head_dim is free, so lane
 //   (t, kg) reads elements kg*D/4 .. +D/4-1 of key row t in one load (16
 //   bytes at head_dim 128) and Q^T takes the same elements; 4-bit values
@@ -117,7 +122,11 @@ __global__ __launch_bounds__(64 * mfma_waves<KT>()) void decode_mfma_kernel(Attn
   // Q^T operand: head r16, elements 32kk + 8kg .. +7 (4-bit keys:
   // kg*D/4 + 8kk .. +7, the elements that lane's key load holds).
   u32x4 qop[NK];
-  constexpr bool kOffset = kInt4 && M::kOffset4;   // bf16 4-bit: offsets removed later
+  // Offsets left in the operands and removed from the sums later: bf16
+  // 4-bit codes, and int8 codes, which enter as u = k + 128 (0..255, exact
+  // in bf16 and f16) straight from a byte convert.
+  constexpr bool kOffset = (kInt4 && M::kOffset4) || kInt8;
+  constexpr float kOffset8 = 128.f;
   float kcorr = 0.f;                                // the offsets' share of every score
   {
     const uint16_t* qp = static_cast<const uint16_t*>(a.q);
@@ -146,12 +155,19 @@ __global__ __launch_bounds__(64 * mfma_waves<KT>()) void decode_mfma_kernel(Attn
         }
       } else {
         qop[kk] = v;
+        if constexpr (kInt8) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            qlo += M::lo(dw(v, i));
+            qhi += M::hi(dw(v, i));
+          }
+        }
       }
     }
     if constexpr (kOffset) {
       qlo = sum_xor32(sum_xor16(qlo));
       qhi = sum_xor32(sum_xor16(qhi));
-      kcorr = M::kOffsetLo4 * qlo + M::kOffsetHi4 * qhi;
+      kcorr = kInt8 ? kOffset8 * (qlo + qhi) : M::kOffsetLo4 * qlo + M::kOffsetHi4 * qhi;
     }
   }
 
@@ -226,10 +242,10 @@ __global__ __launch_bounds__(64 * mfma_waves<KT>()) void decode_mfma_kernel(Attn
           const u32x4& kw = kr[u][kWideK8 ? kk / 2 : kk];
           const int h2 = kWideK8 ? 2 * (kk % 2) : 0;
           const uint32_t w0 = dw(kw, h2) ^ 0x80808080u, w1 = dw(kw, h2 + 1) ^ 0x80808080u;
-          kop = u32x4{M::int_pair(i8_exact(w0, 0), i8_exact(w0, 1)),
-                      M::int_pair(i8_exact(w0, 2), i8_exact(w0, 3)),
-                      M::int_pair(i8_exact(w1, 0), i8_exact(w1, 1)),
-                      M::int_pair(i8_exact(w1, 2), i8_exact(w1, 3))};
+          kop = u32x4{M::int_pair(u8_value(w0, 0), u8_value(w0, 1)),
+                      M::int_pair(u8_value(w0, 2), u8_value(w0, 3)),
+                      M::int_pair(u8_value(w1, 0), u8_value(w1, 1)),
+                      M::int_pair(u8_value(w1, 2), u8_value(w1, 3))};
         } else {
           kop = kr[u][kk];
         }
@@ -320,17 +336,20 @@ __global__ __launch_bounds__(64 * mfma_waves<KT>()) void decode_mfma_kernel(Attn
           wacc = M::k32(u32x4{o, o, o, o}, pcat, wacc);
         }
       } else if constexpr (kInt8) {
-        // sign-flipped codes: each widens with one byte-select add and one convert
+        // sign-flipped codes u = k + 128, one byte convert each; the
+        // offset's share, 128 x the weights, is collected in wacc
 #pragma unroll
         for (int e = 0; e < 4; ++e) vrow[e] ^= u32x4{0x80808080u, 0x80808080u, 0x80808080u, 0x80808080u};
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
-          const uint32_t v01 = M::int_pair(i8_exact(dw(vrow[0], j >> 2), j & 3),
-                                           i8_exact(dw(vrow[1], j >> 2), j & 3));
-          const uint32_t v23 = M::int_pair(i8_exact(dw(vrow[2], j >> 2), j & 3),
-                                           i8_exact(dw(vrow[3], j >> 2), j & 3));
+          const uint32_t v01 = M::int_pair(u8_value(dw(vrow[0], j >> 2), j & 3),
+                                           u8_value(dw(vrow[1], j >> 2), j & 3));
+          const uint32_t v23 = M::int_pair(u8_value(dw(vrow[2], j >> 2), j & 3),
+                                           u8_value(dw(vrow[3], j >> 2), j & 3));
           acc[j] = M::k32(u32x4{v01, v23, v01, v23}, pcat, acc[j]);
         }
+        const uint32_t o = M::int_pair(kOffset8, kOffset8);
+        wacc = M::k32(u32x4{o, o, o, o}, pcat, wacc);
       } else {
 #pragma unroll
         for (int j = 0; j < NV; ++j) {

@@ -139,10 +139,10 @@ __device__ __forceinline__ uint32_t pair_of(const u32x4& x, const u32x4& y, int 
   return __builtin_amdgcn_perm(dw(y, j >> 1), dw(x, j >> 1), (j & 1) ? 0x07060302u : 0x05040100u);
 }
 
-// Signed byte k of a dword, exactly, as float: the byte with its sign bit
-// flipped is an unsigned value (v_cvt_f32_ubyte), less 128.
-__device__ __forceinline__ float i8_exact(uint32_t flipped, int k) {
-  return static_cast<float>((flipped >> (8 * k)) & 0xffu) - 128.f;
+// byte k of a dword as a float (one byte convert): a sign-flipped int8 code
+// read as u = code + 128
+__device__ __forceinline__ float u8_value(uint32_t flipped, int k) {
+  return static_cast<float>((flipped >> (8 * k)) & 0xffu);
 }
 
 // 4-bit codes of one dword (element 2i in the low nibble of byte i), one
