@@ -181,7 +181,7 @@ __global__ __launch_bounds__(64 * mfma_waves<KT>()) void decode_mfma_kernel(Attn
 
   float m = kNegInf, l = 0.f;
   f32x4 acc[NV];
-  f32x4 wacc = {0.f, 0.f, 0.f, 0.f};   // bf16 4-bit: the offsets' share of acc
+  f32x4 wacc = {0.f, 0.f, 0.f, 0.f};   // int8, and bf16 4-bit: the offsets' share of acc
 #pragma unroll
   for (int j = 0; j < NV; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 

@@ -10,8 +10,8 @@
 // (running max and sum rescaled as the max grows), which gives the same
 // result up to rounding without materialising the scores.
 //
-// Layout on gfx950.  A workgroup of 8 wavefronts owns one (query row, KV
-// head, context partition) and the G query heads that share that KV head.
+// Layout on gfx950.  A workgroup of 8 (or 16) wavefronts owns one (query
+// row, context partition) and G query heads that share one KV head.
 // One (block, KV head) tile of K is 16 rows x head_dim contiguous elements:
 // 4 KiB at bf16 / head_dim 128, read as 16-byte chunks so one wavefront load
 // instruction covers 1 KiB of consecutive bytes.  C = row_bytes / 16 lanes
@@ -188,7 +188,6 @@ __global__ __launch_bounds__(64 * NW) void decode_wave_kernel(AttnArgs a) {
   const int t0 = part * a.part_tokens;
   const int t1 = min(ctx, t0 + a.part_tokens);
   const int nb = ((t1 + 15) >> 4) - b0;
-  const int nbw = nb > wave ? (nb - wave + kWaves - 1) / kWaves : 0;   // this wave's blocks
 
   float m[G], l[G], o[G][E];
 #pragma unroll
@@ -298,11 +297,11 @@ __global__ __launch_bounds__(64 * NW) void decode_wave_kernel(AttnArgs a) {
     return true;
   };
 
-  // The wave's blocks are partition blocks wave, wave + 4, ...; all are
-  // whole except possibly the partition's last block, which is then the
-  // wave's last.  One block's K and V (8 KiB at bf16 / head_dim 128) are in
-  // flight per wave; at 63 VGPRs eight waves share a SIMD, so a CU keeps
-  // about 256 KiB of loads outstanding.
+  // The wave's blocks are partition blocks wave, wave + NW, wave + 2 NW,
+  // ...; all are whole except possibly the partition's last block, which is
+  // then the wave's last.  One block's K and V (8 KiB at bf16 / head_dim
+  // 128) are in flight per wave; at 104 VGPRs four waves share a SIMD, so a
+  // CU keeps about 128 KiB of loads outstanding.
   const bool partial_tail = (t1 & 15) != 0;
   const int nwhole = nb - (partial_tail ? 1 : 0);
   const int kwhole = nwhole > wave ? (nwhole - wave + kWaves - 1) / kWaves : 0;
@@ -341,8 +340,8 @@ __global__ __launch_bounds__(64 * NW) void decode_wave_kernel(AttnArgs a) {
   }
 
   // Merge the wavefronts through LDS.  Each wave leaves its state there and
-  // counts itself in; the last to arrive merges all four and writes, the
-  // others end at once (no barrier: a wave with fewer blocks does not wait
+  // counts itself in; the last to arrive merges all NW of them and writes,
+  // the others end at once (no barrier: a wave with fewer blocks does not wait
   // for the slowest, and its slot frees for the next workgroup).
   __shared__ float sm_o[kWaves][G][D];
   __shared__ float sm_m[kWaves][G];
@@ -367,12 +366,23 @@ __global__ __launch_bounds__(64 * NW) void decode_wave_kernel(AttnArgs a) {
   finish_rows<kWaves, G, D>(a, sm_o, sm_m, sm_l, G, row, hbase, part, nparts, lane, 64);
 }
 
+// Most query heads one workgroup serves.  Each head holds its q slice and an
+// output chunk of E floats per lane, so the register file bounds the group:
+// four heads of 16-bit or fp32 K/V, two of int8 or 4-bit codes (16 elements
+// per lane) fit in 256 VGPRs without spilling to scratch; larger groups are
+// split over several workgroups of the grid, which read the same K/V tiles
+// at about the same time (the head group is the fastest grid index).
+template <typename KT>
+constexpr int max_wave_heads() {
+  return KT::bits <= 8 ? 2 : 4;
+}
+
 template <typename QT, typename KT, int D, bool NT>
 pkv_status launch_d(const AttnArgs& a, int group, hipStream_t st) {
-  // Heads per workgroup: the whole group when it is 1, 2, 4 or 8, otherwise
-  // the largest of those dividing it (each workgroup then re-reads the KV).
+  // Heads per workgroup: the largest of 4, 2 and 1 that divides the group,
+  // capped by max_wave_heads.
   int gw = 1;
-  for (int c : {8, 4, 2}) if (group % c == 0) { gw = c; break; }
+  for (int c : {4, 2}) if (c <= max_wave_heads<KT>() && group % c == 0) { gw = c; break; }
   dim3 grid(a.num_parts * a.num_rows * (a.hq / gw));
   const dim3 wg(64 * kWavesDefault);
   switch (gw) {
@@ -387,8 +397,10 @@ pkv_status launch_d(const AttnArgs& a, int group, hipStream_t st) {
       hipLaunchKernelGGL((decode_wave_kernel<QT, KT, D, 1, NT, kWavesDefault>), grid, wg, 0, st, a);
       break;
     case 2: hipLaunchKernelGGL((decode_wave_kernel<QT, KT, D, 2, NT, kWavesDefault>), grid, wg, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((decode_wave_kernel<QT, KT, D, 4, NT, kWavesDefault>), grid, wg, 0, st, a); break;
-    default: hipLaunchKernelGGL((decode_wave_kernel<QT, KT, D, 8, NT, kWavesDefault>), grid, wg, 0, st, a); break;
+    default:
+      if constexpr (max_wave_heads<KT>() >= 4)
+        hipLaunchKernelGGL((decode_wave_kernel<QT, KT, D, 4, NT, kWavesDefault>), grid, wg, 0, st, a);
+      break;
   }
   PKV_LAUNCH_CHECK("paged attention (wavefront)");
   return PKV_OK;

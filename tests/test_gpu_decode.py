@@ -139,6 +139,78 @@ def test_gqa_matches_oracle(gqa, algo, int8):
         assert err <= TOL16, (parts, err)
 
 
+def bf16_out_ok(ob, of, ref):
+    """A bf16 output run: bit for bit the round-to-nearest-even of the fp32
+    run, and within the oracle bar plus half a bf16 ulp of the reference."""
+    assert torch.equal(ob.view(torch.int16), of.to(torch.bfloat16).view(torch.int16))
+    err = np.abs(out_f64(ob) - ref) - np.abs(ref) * 2.0 ** -8
+    assert err.max() <= TOL16, err.max()
+
+
+@pytest.mark.parametrize("int8", [False, True], ids=["bf16", "int8"])
+def test_gqa_mfma_bf16_output_is_rne_of_f32(gqa, int8):
+    """The matrix-core kernel's 16-bit output path (merge and store) on
+    non-zero data, with and without a split."""
+    c, d16, d8 = gqa
+    d = d8 if int8 else d16
+    ref = oracle_decode(c, int8=int8)
+    for parts in (0, 512):
+        of = d.decode(parts=parts, algo=MFMA)
+        assert np.abs(out_f64(of) - ref).max() <= TOL16
+        ob = d.decode(parts=parts, algo=MFMA, out_dtype=torch.bfloat16)
+        bf16_out_ok(ob, of, ref)
+
+
+@pytest.mark.parametrize("qdt", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_int8_kv_every_q_dtype_and_head_dim(qdt, D):
+    """int8 KV under every q type and head_dim: the wavefront kernel for all
+    of them, the matrix-core kernel for 16-bit q (f16 q builds its operands
+    through its own integer-pair path); group 8, so AUTO takes the
+    matrix-core kernel for 16-bit q."""
+    c = W.decode_case(500 + D, 4, 16, 2, D, lens=[1, 33, 700, 2100], dtype=qdt, int8=True)
+    d = DevCase(c, int8=True)
+    ref = oracle_decode(c, int8=True)
+    algos = [WAVE, pkv.PKV_ALGO_AUTO] + ([MFMA] if qdt != "f32" else [])
+    for algo in algos:
+        for parts in (0, 256):
+            out = d.decode(parts=parts, algo=algo)
+            err = np.abs(out_f64(out) - ref).max()
+            assert err <= TOL16, (algo, parts, err)
+            assert err <= 1e-4, f"unexpectedly large error {err} ({algo}, {parts})"
+    if qdt == "f16":
+        of = d.decode(parts=256, algo=MFMA)
+        ob = d.decode(parts=256, algo=MFMA, out_dtype=torch.float16)
+        assert torch.equal(ob, of.to(torch.float16))
+
+
+def test_int8_mfma_biased_q_and_value_outliers():
+    """int8 codes enter the matrix-core products with an offset that is taken
+    out after the sums; a query with a large common component (every element
+    shifted by +4) and value tiles whose scale is set by one large outlier
+    (small codes elsewhere) over one 9,000-token partition are the worst case
+    of that cancellation.  Error against the oracle stays within the bar."""
+    c = W.decode_case(610, 2, 16, 2, 128, lens=[9000, 4100], dtype="bf16")
+    rng = np.random.default_rng(611)
+    c.q = W.round_bf16(c.q + np.float32(4.0))
+    # one outlier of 200 in every third owned value tile
+    for s, n in enumerate(c.context_lens):
+        for j in range(0, W.blocks_for(int(n)), 3):
+            b = int(c.block_tables[s, j])
+            rows = min(16, int(n) - 16 * j)
+            h = int(rng.integers(0, 2))
+            c.v_cache[b, h, int(rng.integers(0, rows)), int(rng.integers(0, 128))] = 200.0
+    c.k_i8, c.k_scale = W.int8_pool(c.k_cache, c.block_tables, c.context_lens)
+    c.v_i8, c.v_scale = W.int8_pool(c.v_cache, c.block_tables, c.context_lens)
+    d = DevCase(c, int8=True)
+    ref = oracle_decode(c, int8=True)
+    for algo in (MFMA, WAVE):
+        out = d.decode(parts=0, algo=algo)
+        err = np.abs(out_f64(out) - ref).max()
+        print(f"biased q, value outliers, algo {algo}: max abs err {err:.3e}")
+        assert err <= TOL16, (algo, err)
+
+
 @pytest.mark.parametrize("group", [2, 4, 8, 16])
 def test_group_sizes_mfma(group):
     hkv = 2
@@ -233,9 +305,14 @@ def test_gqa_long_full_size_sampled(int8):
     rng = np.random.default_rng(1)
     pairs = [(int(s), int(h)) for s, h in zip(rng.integers(0, 16, 12), rng.integers(0, 64, 12))]
     ref = sampled_oracle(c, pairs, int8=int8)
-    out = d.decode(parts=512).float().cpu().numpy()
+    of = d.decode(parts=512)
+    out = of.float().cpu().numpy()
     err = max(np.abs(out[s, h] - ref[(s, h)]).max() for s, h in pairs)
     assert err <= TOL16, err
+    # the bf16 output of the same launch shape: the round-to-nearest-even of
+    # the fp32 output, bit for bit
+    ob = d.decode(parts=512, out_dtype=torch.bfloat16)
+    assert torch.equal(ob.view(torch.int16), of.to(torch.bfloat16).view(torch.int16))
     del d
     torch.cuda.empty_cache()
 

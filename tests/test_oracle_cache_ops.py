@@ -100,3 +100,28 @@ def test_swap_blocks_round_trip_and_untouched_blocks():
         assert h == h2
         assert np.array_equal(k2[d_new], dev_k[s_dev]) and np.array_equal(v2[d_new], dev_v[s_dev])
     assert not k2[[0, 1, 2, 4, 6, 7, 8, 10, 11]].any()
+
+
+def test_swap_blocks_scales_hand_worked():
+    """The scale branch of swap_blocks, worked by hand: each (src, dst) pair
+    moves src's K scales into dst's K scales and src's V scales into dst's V
+    scales (never crossed), and destination blocks no pair names keep
+    theirs.  Source pools: 3 blocks x 2 KV heads; destination: 4 blocks."""
+    src_k = np.arange(3 * 2 * 16 * 2, dtype=np.float32).reshape(3, 2, 16, 2)
+    src_v = -src_k
+    src_ks = np.array([[1.0, 2.0], [3.0, 4.0], [5.0, 6.0]], np.float32)
+    src_vs = np.array([[10.0, 20.0], [30.0, 40.0], [50.0, 60.0]], np.float32)
+    dst_k = np.zeros((4, 2, 16, 2), np.float32)
+    dst_v = np.zeros_like(dst_k)
+    dst_ks = np.full((4, 2), -1.0, np.float32)
+    dst_vs = np.full((4, 2), -2.0, np.float32)
+    dk, dv, dks, dvs = C.swap_blocks(dst_k, dst_v, src_k, src_v, [(2, 0), (0, 3)],
+                                     dst_ks, dst_vs, src_ks, src_vs)
+    assert np.array_equal(dks, np.array([[5.0, 6.0], [-1.0, -1.0], [-1.0, -1.0], [1.0, 2.0]],
+                                        np.float32))
+    assert np.array_equal(dvs, np.array([[50.0, 60.0], [-2.0, -2.0], [-2.0, -2.0],
+                                         [10.0, 20.0]], np.float32))
+    assert np.array_equal(dk[0], src_k[2]) and np.array_equal(dv[3], src_v[0])
+    assert not dk[[1, 2]].any() and not dv[[1, 2]].any()
+    # the inputs are not modified
+    assert (dst_ks == -1.0).all() and (dst_vs == -2.0).all()
