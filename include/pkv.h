@@ -444,6 +444,31 @@ pkv_status pkv_paged_attention_decode_partials(
     int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
     int32_t partition_tokens, int32_t algo, void* workspace, size_t workspace_bytes, void* stream);
 
+/* pkv_paged_attention_decode without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The split-K partial results go
+ * to a scratch array of PKV_NOALLOC_SCRATCH_BYTES that the library holds in
+ * device memory, one per GPU, from the first call on that GPU until the
+ * process ends.  The call itself allocates nothing.
+ *   Same arguments, kernels and results as pkv_paged_attention_decode (bit
+ *   for bit, for the same partition_tokens and algo); the thread's current
+ *   device must be the one `stream` runs on.
+ *   A call whose partial results would need more than the scratch holds
+ *   (pkv_decode_workspace_bytes(...) > PKV_NOALLOC_SCRATCH_BYTES) returns
+ *   PKV_ERR_INVALID before any launch; larger partitions shrink the need.
+ *   Nothing in the scratch must start at zero: every partial state a reduce
+ *   reads is written earlier in the same call.
+ *   Calls that overlap on one GPU (several streams, several threads) share
+ *   its scratch and race: the caller serialises them. */
+#define PKV_NOALLOC_SCRATCH_BYTES (64ull << 20)
+pkv_status pkv_paged_attention_decode_noalloc(
+    void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype, const void* k_cache,
+    const void* v_cache, pkv_dtype kv_dtype, const float* k_scale, const float* v_scale,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+    int32_t partition_tokens, int32_t algo, void* stream);
+
 pkv_status pkv_paged_attention_reduce(void* out, pkv_dtype out_dtype, const int32_t* context_lens,
                                       int32_t max_context_len, int32_t num_seqs,
                                       int32_t num_q_heads, int32_t head_dim,

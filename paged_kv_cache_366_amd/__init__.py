@@ -15,7 +15,8 @@ import numpy as np
 
 from ._lib import (PKV_ALGO_AUTO, PKV_ALGO_MFMA, PKV_ALGO_WAVE, PKV_BF16, PKV_ERR_DEVICE,  # noqa
                    PKV_ERR_INTERNAL, PKV_ERR_INVALID, PKV_ERR_OUT_OF_BLOCKS, PKV_ERR_UNSUPPORTED,
-                   PKV_F16, PKV_F32, PKV_I4, PKV_I8, PKV_KV_CACHED, PKV_KV_STREAM, PKV_OK, LIB_PATH,
+                   PKV_F16, PKV_F32, PKV_I4, PKV_I8, PKV_KV_CACHED, PKV_KV_STREAM,
+                   PKV_NOALLOC_SCRATCH_BYTES, PKV_OK, LIB_PATH,
                    PkvBmStats, PkvError, PkvSwapStats, PkvOutOfBlocks, check, load)
 
 __all__ = [n for n in dir() if n.startswith("pkv_") or n.startswith("PKV_")]
@@ -371,7 +372,7 @@ def pkv_decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
 
 
 def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
-                 partition_tokens, algo, k_scale, v_scale, workspace, stream):
+                 partition_tokens, algo, k_scale, v_scale, workspace, stream, allocate=True):
     torch = _torch()
     S, hq, d = q.shape
     nb, hkv, bs, _ = k_cache.shape
@@ -381,7 +382,7 @@ def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, max_conte
     if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
         raise ValueError("block_tables must be [S, MB] and context_lens [S]")
     need = pkv_decode_workspace_bytes(S, hq, d, max_context_len, partition_tokens)
-    if need and workspace is None:
+    if need and workspace is None and allocate:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = C.c_void_p(workspace.data_ptr()) if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -418,6 +419,19 @@ def pkv_paged_attention_decode_partials(out, q, k_cache, v_cache, block_tables, 
                             workspace, stream)
     check(load().pkv_paged_attention_decode_partials(*args))
     return ws
+
+
+def pkv_paged_attention_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens,
+                                       max_context_len: int, scale: float,
+                                       partition_tokens: int = 0, algo: int = PKV_ALGO_AUTO,
+                                       k_scale=None, v_scale=None, stream=None) -> None:
+    """pkv_paged_attention_decode with the split-K partial results in the
+    library's fixed per-GPU scratch (PKV_NOALLOC_SCRATCH_BYTES): no workspace
+    argument and nothing allocated, here or in the library."""
+    args, _ = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens,
+                           max_context_len, scale, partition_tokens, algo, k_scale, v_scale,
+                           None, stream, allocate=False)
+    check(load().pkv_paged_attention_decode_noalloc(*args[:-3], args[-1]))
 
 
 def pkv_paged_attention_reduce(out, context_lens, max_context_len: int, partition_tokens: int,

@@ -15,6 +15,7 @@ PKV_OK, PKV_ERR_INVALID, PKV_ERR_OUT_OF_BLOCKS, PKV_ERR_UNSUPPORTED, PKV_ERR_DEV
 PKV_F32, PKV_F16, PKV_BF16, PKV_I8, PKV_I4 = range(5)
 PKV_ALGO_AUTO, PKV_ALGO_WAVE, PKV_ALGO_MFMA = range(3)
 PKV_KV_STREAM, PKV_KV_CACHED = 0x10, 0x20   # K/V load policy, OR-ed into algo
+PKV_NOALLOC_SCRATCH_BYTES = 64 << 20        # scratch of the allocation-free decode
 
 _i32, _i64, _f32, _sz, _vp = C.c_int32, C.c_int64, C.c_float, C.c_size_t, C.c_void_p
 _pi32 = C.POINTER(C.c_int32)
@@ -79,6 +80,9 @@ SIGNATURES = {
     "pkv_paged_attention_decode_partials": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _i32, _vp, _vp,
                                                    _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                                                    _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp]),
+    "pkv_paged_attention_decode_noalloc": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _i32, _vp, _vp,
+                                                  _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
+                                                  _i32, _i32, _f32, _i32, _i32, _vp]),
     "pkv_paged_attention_reduce": (_i32, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _sz,
                                           _vp]),
     "pkv_paged_attention_prefill": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp,

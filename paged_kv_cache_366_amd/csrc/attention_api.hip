@@ -1,5 +1,6 @@
 // C entry points of paged attention: argument checks, workspace layout and
 // the choice between the wavefront and matrix-core kernels.
+#include <atomic>
 #include <cmath>
 #include <vector>
 
@@ -202,6 +203,40 @@ pkv_status decode_impl(DecodePart which, void* out, pkv_dtype out_dt, const void
   return PKV_OK;
 }
 
+// Scratch of the allocation-free decode entry point: split-K partial states
+// in a file-scope device array, one instance per GPU the library runs on.
+// In host code `scratch` names a host-side stand-in, not device memory, so
+// its device address is looked up once per device (hipGetSymbolAddress,
+// with that device current) and only that address is handed to kernels.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+pkv_status scratch_address(const char* who, void** addr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return fail(PKV_ERR_DEVICE, "%s: hipGetDevice failed: %s", who, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: device %d beyond the %d the library tracks", who, dev,
+                kMaxDevices);
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(PKV_ERR_DEVICE, "%s: scratch address of device %d: %s", who, dev,
+                  hipGetErrorString(e));
+    g_scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  *addr = p;
+  return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -256,6 +291,39 @@ pkv_status pkv_paged_attention_decode_partials(
                        max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                        num_blocks, scale, partition_tokens, algo, workspace, workspace_bytes,
                        stream);
+  })
+}
+
+pkv_status pkv_paged_attention_decode_noalloc(
+    void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype, const void* k_cache,
+    const void* v_cache, pkv_dtype kv_dtype, const float* k_scale, const float* v_scale,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+    int32_t partition_tokens, int32_t algo, void* stream) {
+  PKV_GUARD({
+    const char* who = "paged_attention_decode_noalloc";
+    if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0 ||
+        partition_tokens < 0)
+      return fail(PKV_ERR_INVALID, "%s: bad sizes", who);
+    const size_t need = workspace_layout(num_seqs, num_q_heads, head_dim,
+                                         num_partitions(max_context_len, partition_tokens))
+                            .total;
+    if (need > PKV_NOALLOC_SCRATCH_BYTES)
+      return fail(PKV_ERR_INVALID,
+                  "%s: split-K partial results need %zu bytes, more than the %llu-byte scratch "
+                  "(use larger partitions, or the workspace entry point)",
+                  who, need, static_cast<unsigned long long>(PKV_NOALLOC_SCRATCH_BYTES));
+    void* ws = nullptr;
+    if (need > 0) {
+      pkv_status st = scratch_address(who, &ws);
+      if (st) return st;
+    }
+    return decode_impl(DecodePart::kAll, out, out_dtype, q, q_dtype, k_cache, v_cache, kv_dtype,
+                       k_scale, v_scale, block_tables, max_blocks_per_seq, context_lens,
+                       max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                       num_blocks, scale, partition_tokens, algo, ws,
+                       need > 0 ? PKV_NOALLOC_SCRATCH_BYTES : 0, stream);
   })
 }
 

@@ -233,3 +233,22 @@ def test_load_policy_flags_are_checked_on_the_host():
         assert decode(kernel | pkv.PKV_KV_STREAM | pkv.PKV_KV_CACHED) == PKV_ERR_INVALID
     assert decode(3) == PKV_ERR_INVALID
     assert decode(0x40) == PKV_ERR_INVALID
+
+
+def test_noalloc_decode_refuses_oversize_and_accepts_empty_without_a_gpu():
+    """The allocation-free decode checks its split-K need against the fixed
+    scratch before any HIP call: too large is INVALID, an empty batch is OK."""
+    import paged_kv_cache_366_amd as pkv
+    from paged_kv_cache_366_amd._lib import PKV_BF16, PKV_ERR_INVALID, PKV_OK
+    lib = pkv.load()
+    # 64 sequences x 64 heads, 16-token partitions of 32,768 tokens: 4 GiB
+    assert pkv.pkv_decode_workspace_bytes(64, 64, 128, 32768, 16) > pkv.PKV_NOALLOC_SCRATCH_BYTES
+    st = lib.pkv_paged_attention_decode_noalloc(None, PKV_BF16, None, PKV_BF16, None, None,
+                                                PKV_BF16, None, None, None, 2048, None, 32768, 64,
+                                                64, 8, 128, 16, 10, 0.1, 16, 0, None)
+    assert st == PKV_ERR_INVALID
+    assert b"scratch" in lib.pkv_last_error()
+    st = lib.pkv_paged_attention_decode_noalloc(None, PKV_BF16, None, PKV_BF16, None, None,
+                                                PKV_BF16, None, None, None, 8, None, 128, 0, 8, 2,
+                                                128, 16, 10, 0.1, 0, 0, None)
+    assert st == PKV_OK
