@@ -132,6 +132,21 @@ typedef struct pkv_bm_stats {
  * share ratio; [kongchang] section "显存浪费的三种形式" names the waste). */
 pkv_status pkv_bm_stats_get(const pkv_bm* bm, pkv_bm_stats* out);
 
+/* Latency of page allocation, the health bar of [cnnetsun] §4.2 (P99 of
+ * page allocation under 1 ms).  Every call that takes blocks from the pool
+ * (pkv_bm_alloc, pkv_seq_create, pkv_seq_create_cached, pkv_seq_append,
+ * pkv_seq_append_batch), failed ones included, times itself on the host's
+ * steady clock; the percentiles cover the latest min(calls, 65536) of them
+ * (nearest rank).  reset != 0 starts a new count after reading. */
+typedef struct pkv_bm_latency {
+  int64_t calls;     /* allocating calls since creation or the last reset */
+  int32_t window;    /* calls the percentiles cover */
+  double p50_us;
+  double p99_us;
+  double max_us;
+} pkv_bm_latency;
+pkv_status pkv_bm_latency_get(pkv_bm* bm, pkv_bm_latency* out, int32_t reset);
+
 /* ------------------------------------------------------------------------
  * Sequences (host).  Sequence ids count up from 0 and are never reused.
  * ---------------------------------------------------------------------- */

@@ -17,7 +17,7 @@ from ._lib import (PKV_ALGO_AUTO, PKV_ALGO_MFMA, PKV_ALGO_WAVE, PKV_BF16, PKV_ER
                    PKV_ERR_INTERNAL, PKV_ERR_INVALID, PKV_ERR_OUT_OF_BLOCKS, PKV_ERR_UNSUPPORTED,
                    PKV_F16, PKV_F32, PKV_I4, PKV_I8, PKV_KV_CACHED, PKV_KV_STREAM,
                    PKV_NOALLOC_SCRATCH_BYTES, PKV_OK, LIB_PATH,
-                   PkvBmStats, PkvError, PkvSwapStats, PkvOutOfBlocks, check, load)
+                   PkvBmLatency, PkvBmStats, PkvError, PkvSwapStats, PkvOutOfBlocks, check, load)
 
 __all__ = [n for n in dir() if n.startswith("pkv_") or n.startswith("PKV_")]
 
@@ -84,6 +84,14 @@ def pkv_bm_stats_get(bm) -> dict:
     s = PkvBmStats()
     check(load().pkv_bm_stats_get(bm, C.byref(s)))
     return {f: getattr(s, f) for f, _ in PkvBmStats._fields_}
+
+
+def pkv_bm_latency_get(bm, reset: bool = False) -> dict:
+    """Host latency of the block manager's allocating calls: count, window,
+    p50 / p99 / max in microseconds."""
+    st = PkvBmLatency()
+    check(load().pkv_bm_latency_get(bm, C.byref(st), int(bool(reset))))
+    return {name: getattr(st, name) for name, _ in st._fields_}
 
 
 def pkv_seq_create(bm, num_tokens: int) -> int:

@@ -34,6 +34,11 @@ class PkvBmStats(C.Structure):
                 ("logical_blocks", _i64), ("tokens", _i64), ("waste_slots", _i64)]
 
 
+class PkvBmLatency(C.Structure):
+    _fields_ = [("calls", _i64), ("window", _i32), ("p50_us", C.c_double),
+                ("p99_us", C.c_double), ("max_us", C.c_double)]
+
+
 # name -> (restype, argtypes)
 SIGNATURES = {
     "pkv_last_error": (C.c_char_p, []),
@@ -46,6 +51,7 @@ SIGNATURES = {
     "pkv_bm_num_free": (_i32, [_vp]),
     "pkv_bm_get_state": (_i32, [_vp, _pi32, _pi32, _pi32]),
     "pkv_bm_stats_get": (_i32, [_vp, C.POINTER(PkvBmStats)]),
+    "pkv_bm_latency_get": (_i32, [_vp, C.POINTER(PkvBmLatency), _i32]),
     "pkv_seq_create": (_i32, [_vp, _i32, _pi64]),
     "pkv_seq_fork": (_i32, [_vp, _i64, _pi64]),
     "pkv_seq_append": (_i32, [_vp, _i64, _i32, _pi32, _pi32, _pi32]),

@@ -24,6 +24,7 @@
 // is allocated: freeing the block (count 0) drops it, and the cache holds no
 // reference of its own.
 #include <algorithm>
+#include <chrono>
 #include <cstdlib>
 #include <cstring>
 #include <new>
@@ -101,6 +102,20 @@ struct pkv_bm {
   int32_t prefix_count = 0;
   int64_t prefix_lookups = 0;
   int64_t prefix_hits = 0;
+  // Durations of the latest calls that take blocks from the pool (alloc,
+  // create, append), in nanoseconds: a ring of the last kLatencyWindow.
+  static constexpr int32_t kLatencyWindow = 1 << 16;
+  std::vector<uint32_t> latency_ns;
+  int64_t latency_calls = 0;
+  void record_latency(std::chrono::steady_clock::time_point t0) {
+    const auto ns = std::chrono::duration_cast<std::chrono::nanoseconds>(
+                        std::chrono::steady_clock::now() - t0)
+                        .count();
+    if (latency_ns.empty()) latency_ns.resize(kLatencyWindow);
+    latency_ns[latency_calls % kLatencyWindow] =
+        static_cast<uint32_t>(std::min<int64_t>(ns, UINT32_MAX));
+    ++latency_calls;
+  }
 
   int32_t blocks_for(int64_t tokens) const {
     return static_cast<int32_t>((tokens + block_size - 1) / block_size);
@@ -177,6 +192,20 @@ struct pkv_bm {
   }
 };
 
+namespace {
+
+// Times one allocating call of the block manager, success or failure.
+struct AllocTimer {
+  pkv_bm* bm;
+  std::chrono::steady_clock::time_point t0 = std::chrono::steady_clock::now();
+  explicit AllocTimer(pkv_bm* b) : bm(b) {}
+  ~AllocTimer() {
+    if (bm) bm->record_latency(t0);
+  }
+};
+
+}  // namespace
+
 extern "C" {
 
 const char* pkv_last_error(void) { return g_last_error.c_str(); }
@@ -220,6 +249,7 @@ void pkv_bm_destroy(pkv_bm* bm) { delete bm; }
 
 pkv_status pkv_bm_alloc(pkv_bm* bm, int32_t n, int32_t* ids_out) {
   PKV_GUARD({
+    AllocTimer timer(bm);
     if (!bm) return pkv::fail(PKV_ERR_INVALID, "bm is NULL");
     if (n < 0 || (n > 0 && !ids_out)) return pkv::fail(PKV_ERR_INVALID, "bad count or output");
     if (static_cast<size_t>(n) > bm->free_list.size())
@@ -280,8 +310,35 @@ pkv_status pkv_bm_stats_get(const pkv_bm* bm, pkv_bm_stats* out) {
   return PKV_OK;
 }
 
+pkv_status pkv_bm_latency_get(pkv_bm* bm, pkv_bm_latency* out, int32_t reset) {
+  PKV_GUARD({
+    if (!bm || !out) return pkv::fail(PKV_ERR_INVALID, "NULL argument");
+    pkv_bm_latency r{};
+    r.calls = bm->latency_calls;
+    const int64_t w = std::min<int64_t>(bm->latency_calls, pkv_bm::kLatencyWindow);
+    r.window = static_cast<int32_t>(w);
+    if (w > 0) {
+      std::vector<uint32_t> v(bm->latency_ns.begin(), bm->latency_ns.begin() + w);
+      // nearest-rank percentiles: the ceil(p * w)-th smallest duration
+      auto rank = [&](double p) {
+        int64_t k = static_cast<int64_t>(p * static_cast<double>(w) + 0.999999999);
+        k = std::max<int64_t>(1, std::min<int64_t>(k, w)) - 1;
+        std::nth_element(v.begin(), v.begin() + k, v.end());
+        return v[k] * 1e-3;
+      };
+      r.p50_us = rank(0.50);
+      r.p99_us = rank(0.99);
+      r.max_us = *std::max_element(v.begin(), v.end()) * 1e-3;
+    }
+    if (reset) bm->latency_calls = 0;
+    *out = r;
+    return PKV_OK;
+  })
+}
+
 pkv_status pkv_seq_create(pkv_bm* bm, int32_t num_tokens, int64_t* seq_out) {
   PKV_GUARD({
+    AllocTimer timer(bm);
     if (!bm || !seq_out) return pkv::fail(PKV_ERR_INVALID, "NULL argument");
     if (num_tokens < 0) return pkv::fail(PKV_ERR_INVALID, "negative length %d", num_tokens);
     int32_t nb = bm->blocks_for(num_tokens);
@@ -307,6 +364,7 @@ int32_t pkv_adaptive_block_size(double avg_context_len) {
 pkv_status pkv_seq_create_cached(pkv_bm* bm, const int32_t* tokens, int32_t num_tokens,
                                  int64_t* seq_out, int32_t* cached_out) {
   PKV_GUARD({
+    AllocTimer timer(bm);
     if (!bm || !seq_out || (num_tokens > 0 && !tokens))
       return pkv::fail(PKV_ERR_INVALID, "NULL argument");
     if (num_tokens < 0) return pkv::fail(PKV_ERR_INVALID, "negative length %d", num_tokens);
@@ -399,6 +457,7 @@ pkv_status pkv_seq_fork(pkv_bm* bm, int64_t parent, int64_t* child_out) {
 pkv_status pkv_seq_append(pkv_bm* bm, int64_t seq, int32_t num_tokens, int32_t* slots_out,
                           int32_t* cow_src, int32_t* cow_dst) {
   PKV_GUARD({
+    AllocTimer timer(bm);
     if (!bm) return pkv::fail(PKV_ERR_INVALID, "bm is NULL");
     Sequence* s = bm->find(seq);
     if (!s) return pkv::fail(PKV_ERR_INVALID, "unknown sequence %lld", (long long)seq);
@@ -422,6 +481,7 @@ pkv_status pkv_seq_append(pkv_bm* bm, int64_t seq, int32_t num_tokens, int32_t* 
 pkv_status pkv_seq_append_batch(pkv_bm* bm, const int64_t* seqs, int32_t n, int32_t* slots_out,
                                 int32_t* cow_pairs_out, int32_t* num_cow_out) {
   PKV_GUARD({
+    AllocTimer timer(bm);
     if (!bm) return pkv::fail(PKV_ERR_INVALID, "bm is NULL");
     if (n < 0 || (n > 0 && (!seqs || !slots_out || !cow_pairs_out)))
       return pkv::fail(PKV_ERR_INVALID, "bad count or NULL array");

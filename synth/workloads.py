@@ -41,10 +41,14 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     NaN stays NaN; finite inputs never overflow for the N(0,1) draws used here.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    bits = x.view(np.uint32).astype(np.uint64)
-    lsb = (bits >> 16) & 1
-    rounded = ((bits + 0x7FFF + lsb) & 0xFFFF0000).astype(np.uint32)
-    out = rounded.view(np.float32).copy()
+    bits = x.view(np.uint32)
+    # uint32 arithmetic: a finite pattern plus 0x8000 stays below 2^32; NaN
+    # patterns may wrap and are restored below
+    rounded = (bits >> np.uint32(16)) & np.uint32(1)
+    rounded += bits
+    rounded += np.uint32(0x7FFF)
+    rounded &= np.uint32(0xFFFF0000)
+    out = rounded.view(np.float32)
     nan = np.isnan(x)
     if nan.any():
         out[nan] = np.float32(np.nan)
@@ -224,20 +228,31 @@ def int8_pool(cache: np.ndarray, tables: np.ndarray, lens,
     nb, hkv, bs, d = cache.shape
     codes = np.full(cache.shape, I8_NEVER, np.int8)
     scales = np.full((nb, hkv), np.float32(np.nan), np.float32)
-    done = set()
+    filled = {}
     for s, n in enumerate(lens):
         n = int(n)
         for j in range(blocks_for(n, block_size)):
             b = int(tables[s, j])
-            filled = min(block_size, n - j * block_size)
-            if b in done:
-                continue
-            done.add(b)
-            codes[b] = I8_UNUSED
-            for h in range(hkv):
-                q, sc = quantize_int8(cache[b, h, :filled, :])
-                codes[b, h, :filled, :] = q
-                scales[b, h] = sc
+            if b not in filled:
+                filled[b] = min(block_size, n - j * block_size)
+    if not filled:
+        return codes, scales
+    # every owned (block, kv head) tile at once: the same float32 steps as
+    # quantize_int8, with rows past a block's filled count left out of the
+    # maximum (held as 0) and stored as I8_UNUSED
+    blk = np.fromiter(filled.keys(), np.int64, len(filled))
+    nfill = np.fromiter(filled.values(), np.int64, len(filled))
+    live = np.arange(bs)[None, :] < nfill[:, None]                       # [nblk, bs]
+    for lo in range(0, len(blk), 4096):
+        b, lv = blk[lo:lo + 4096], live[lo:lo + 4096]
+        x = np.where(lv[:, None, :, None], cache[b], np.float32(0))         # [n, hkv, bs, d]
+        a = np.abs(x).max(axis=(2, 3))                                       # [n, hkv]
+        sc = (a / np.float32(127.0)).astype(np.float32)
+        safe = np.where(sc == 0, np.float32(1), sc)
+        q = np.clip(np.rint(x / safe[:, :, None, None]), -127, 127).astype(np.int8)
+        q[sc == 0] = 0
+        codes[b] = np.where(lv[:, None, :, None], q, I8_UNUSED)
+        scales[b] = sc
     return codes, scales
 
 

@@ -265,3 +265,24 @@ def test_prefix_cache_collision_does_not_share():
         assert pkv.pkv_bm_prefix_stats(bm)["cached_blocks"] == 3600
     finally:
         pkv.pkv_bm_destroy(bm)
+
+
+def test_allocation_latency_is_recorded():
+    """Every call that takes blocks from the pool times itself (failed ones
+    too); the percentiles are ordered and a reset starts a new count."""
+    bm = pkv.pkv_bm_create(4096, 16, None)
+    try:
+        lat0 = pkv.pkv_bm_latency_get(bm)
+        assert lat0["calls"] == 0 and lat0["window"] == 0 and lat0["p99_us"] == 0
+        ids = [pkv.pkv_seq_create(bm, 100) for _ in range(50)]
+        pkv.pkv_bm_alloc(bm, 3)
+        pkv.pkv_seq_append_batch(bm, ids)
+        with pytest.raises(pkv.PkvOutOfBlocks):
+            pkv.pkv_bm_alloc(bm, 10 ** 6)
+        pkv.pkv_seq_free(bm, ids[0])          # frees are not allocations
+        lat = pkv.pkv_bm_latency_get(bm, reset=True)
+        assert lat["calls"] == 53 and lat["window"] == 53
+        assert 0 <= lat["p50_us"] <= lat["p99_us"] <= lat["max_us"] < 1e5
+        assert pkv.pkv_bm_latency_get(bm)["calls"] == 0
+    finally:
+        pkv.pkv_bm_destroy(bm)
