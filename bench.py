@@ -1,32 +1,50 @@
-"""Benchmark of one paged decode step at the LLaMA-7B attention shape on one GPU.
+"""Benchmark of paged decode attention on one MI355X: the five workloads.
 
-    python bench.py [--steps K] [--warmup W] [--partition P] [--algo auto|wave|mfma]
-                    [--no-cpu-baseline] [--calib-copy-mib M]
+    python bench.py [--steps K] [--warmup W] [--workload all|decode7b|mixed|beam|gqa|...]
+                    [--partition P] [--algo auto|wave|mfma] [--no-cpu-baseline]
+                    [--calib-copy-mib M]
 
-Workload (7B-shape decode, bf16): 64 sequences, 32 query heads = 32 KV heads,
-head_dim 128, 16-token blocks, context lengths uniform on [128, 2048] (each
-includes the token being decoded), a pool of ceil(1.25 x the blocks needed)
-blocks whose free list starts as a seeded random permutation, q/K/V drawn
-N(0, 1) in fp32 and rounded to bf16.
+The default (--workload all) prints ONE JSON line.  Its `value` is the
+headline: the 7B-shape decode step (64 sequences, 32 query heads = 32 KV
+heads, head_dim 128, 16-token blocks, contexts uniform on [128, 2048], each
+including the token being decoded; a pool of ceil(1.25 x the blocks needed)
+whose free list starts as a seeded permutation; q/K/V drawn N(0, 1) in fp32
+and rounded to bf16).  One step (timed, inputs resident in HBM):
+reshape_and_cache of the 64 new K/V rows through the slot mapping -> split-K
+paged decode attention (main kernel) -> partition reduce.  `value` is step
+algorithmic bytes (K/V rows every sequence attends to, q, out, the table
+entries and lengths read, the new rows moved by reshape_and_cache) per
+second.  `roofline` is the main kernel's, from HIP events on its stream.
 
-Set-up (untimed): the C++ block manager creates each sequence with its
-n - 1 cached tokens and appends the current token (slot mapping); the pool
-is filled along the exported block tables; the current token's K/V rows are
-held back and handed to reshape_and_cache inside the step.
+The same line carries the other four workloads as keys of their own, each
+with its step time, per-kernel times (mean, median, p10, p90), its own
+roofline, the sampled error against the CPU oracle and the oracle timed on a
+bounded sample:
+  c3_mixed     continuous-batching step: 48 decode sequences (contexts
+               U[64, 4096]) + 4 chunked-prefill sequences of 512 causal rows
+               over 0/512/1024/1536 cached tokens, with reshape_and_cache of
+               the 2,096 new rows; prefill reported in TFLOP/s against the
+               bf16 matrix peak;
+  c4_beam      16 requests sharing a 1,024-token prefix, 1-200 own tokens,
+               beam width 4: copy_blocks of the shared partial tails +
+               reshape_and_cache + decode; its K/V working set is cache
+               resident, so the HBM roofline uses unique bytes and the
+               logical bytes (shared blocks once per beam) are reported
+               separately against no HBM bound;
+  c5_gqa_bf16  16 sequences, 64 query heads over 8 KV heads (group 8,
+               matrix cores), head_dim 128, contexts U[8192, 32768], split-K
+               partitions of 512 tokens + reduce, bf16 KV;
+  c5_gqa_int8  the same with int8 KV and per-block fp32 scales (the pool is
+               the library's block encoder output over the bf16 pool).
 
-One step (timed, inputs resident in HBM): reshape_and_cache of the 64 new
-K/V rows through the slot mapping -> split-K paged decode attention (main
-kernel) -> partition reduce.  The timed steps run back to back with
-nothing between their launches; a second, instrumented pass of as many
-steps, each after a 512 MB read that flushes the caches, brackets each
-kernel with HIP events on the launch stream, and the main kernel's average
-duration there gives the roofline figure.
+Timing: W untimed warm-up steps, then K steps back to back between two
+device synchronisations (the step time), then a second pass of K steps, each
+after a 512 MB read that flushes the caches, with HIP events on the launch
+stream around every kernel (the per-kernel times).
 
-The printed JSON line carries the step throughput in KV GB/s (algorithmic
-bytes: K/V rows every sequence attends to, q, out, the table entries and
-lengths read, and the new rows moved by reshape_and_cache), the roofline of
-the main decode kernel, and the CPU oracle timed on the host over the same
-batch as a reported baseline.
+Other --workload values print the line of one workload on its own (and the
+kernels that no default line covers: int8/4-bit storage, swapping, prefix
+caching, long-document prefill).
 """
 from __future__ import annotations
 
@@ -45,18 +63,19 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16/f16 matrix peak, published
 BLOCK = 16
+METRIC = "paged decode attention: KV GB/s (% of HBM peak) + tokens/s at 7B shape"
+PAGE_ALLOC_P99_BAR_US = 1000.0   # cnnetsun.cn section 4.2: page allocation P99 < 1 ms
 
-# HBM traffic of the main decode kernel per launch, from rocprofv3 --pmc
-# FETCH_SIZE (scaled by 1 / the factor an elementwise kernel that reads
-# exactly 1 GiB shows) plus WRITE_SIZE (factor 1.0) on this workload (seed 1,
-# partition 1536).  Valid only for the kernel sources whose hash is recorded;
-# a changed kernel reports null.
-TRAFFIC = {
-    "sources_sha1": "c284bdf5b02775aeaf95799b42bca1b064853e5d",
-    "bytes_per_launch": 1092141 * 1024 + 1366 * 1024,
-}
-KERNEL_SOURCES = ("decode_wave.hip", "attention_common.h", "device_common.h")
+# HBM traffic of a workload's main kernel per launch, from two rocprofv3
+# --pmc passes over the bench (FETCH_SIZE scaled by 1 / the factor that a
+# known-size copy kernel shows in the same run, WRITE_SIZE as read), with the
+# profile that records the counts.  Valid only while the kernel sources hash
+# to the measured value; a changed kernel reports null.
+TRAFFIC = {}
+KERNEL_SOURCES = ("decode_wave.hip", "decode_mfma.hip", "attention_common.h", "device_common.h",
+                  "mfma_common.h")
 
 
 def kernel_sources_sha1() -> str:
@@ -67,55 +86,20 @@ def kernel_sources_sha1() -> str:
     return h.hexdigest()
 
 
-class Workload:
-    """7B-shape decode batch, built through the library's block manager."""
-
-    def __init__(self, seed: int = 1, num_seqs: int = 64, heads: int = 32, head_dim: int = 128,
-                 len_range=(128, 2048), block_size: int = BLOCK):
-        import paged_kv_cache_366_amd as pkv
-        from synth import workloads as W
-
-        rng = np.random.default_rng(seed)
-        self.S, self.H, self.D, self.bs = num_seqs, heads, head_dim, block_size
-        bs = block_size
-        lens = W.draw_lengths(rng, num_seqs, *len_range)
-        nb = W.pool_size(lens, 1.25, bs)
-        perm = W.draw_permutation(rng, nb)
-        t0 = time.perf_counter()
-        bm = pkv.pkv_bm_create(nb, bs, perm)
-        seqs = [pkv.pkv_seq_create(bm, int(n) - 1) for n in lens]
-        t1 = time.perf_counter()
-        slots, cow = pkv.pkv_seq_append_batch(bm, seqs)
-        self.max_blocks = int(max(W.blocks_for(n, bs) for n in lens))
-        tables, lens_bm = pkv.pkv_seq_export(bm, seqs, self.max_blocks)
-        t2 = time.perf_counter()
-        assert len(cow) == 0 and np.array_equal(lens_bm, lens)
-        self.host_bm = {"create_us": (t1 - t0) * 1e6, "append_export_us": (t2 - t1) * 1e6}
-        self.bm, self.seqs = bm, seqs
-        q = W.draw_normal(rng, (num_seqs, heads, head_dim), "bf16")
-        kc, vc, _, _ = W.draw_paged_kv(rng, tables, lens, nb, heads, head_dim, "bf16", bs)
-        self.lens, self.tables, self.slots, self.q = lens, tables, slots, q
-        self.kc_full, self.vc_full = kc, vc          # with the current token (oracle side)
-        blk, row = slots // bs, slots % bs
-        self.new_k = kc[blk, :, row, :].copy()       # [S, H, D]
-        self.new_v = vc[blk, :, row, :].copy()
-        self.num_blocks = nb
-        self.scale = np.float32(1.0 / math.sqrt(head_dim))
-
-    # algorithmic bytes (bf16 everywhere, fp32 output)
-    def kv_bytes(self) -> int:
-        return int(self.lens.astype(np.int64).sum()) * self.H * self.D * 2 * 2
-
-    def main_kernel_bytes(self) -> int:
-        tbl = int(sum(W_blocks(n, self.bs) for n in self.lens)) * 4
-        return self.kv_bytes() + self.S * self.H * self.D * 2 + tbl + self.S * 4
-
-    def step_bytes(self) -> int:
-        out = self.S * self.H * self.D * 4
-        rc = self.S * self.H * self.D * 2 * 2 * 2 + self.S * 4   # read new K,V + write them
-        return self.main_kernel_bytes() + out + rc
+def traffic_of(name: str):
+    """(bytes per launch or None, where the figure comes from)."""
+    t = TRAFFIC.get(name)
+    if t is None:
+        return None, "not measured for this workload"
+    if t["sources_sha1"] != kernel_sources_sha1():
+        return None, (f"stale: kernel sources changed since the counter run in {t['profile']}")
+    return t["bytes_per_launch"], (f"rocprofv3 --pmc FETCH_SIZE (scaled by the calibration copy) "
+                                   f"+ WRITE_SIZE, {t['profile']}")
 
 
+# ---------------------------------------------------------------------------
+# host-side helpers
+# ---------------------------------------------------------------------------
 def W_blocks(n, block_size: int = BLOCK) -> int:
     return -(-int(n) // block_size)
 
@@ -126,37 +110,52 @@ def to_dev_bf16(x, torch):
     return torch.from_numpy(bits).to("cuda").view(torch.bfloat16)
 
 
-def cpu_baseline(wl: Workload, min_seconds: float = 10.0, max_reps: int = 40):
-    """The oracle over the whole batch, repeated until at least min_seconds."""
-    from oracle import attention as A
+def stats_ms(xs):
+    a = np.asarray(xs, np.float64)
+    return {"mean": float(a.mean()), "median": float(np.median(a)),
+            "p10": float(np.percentile(a, 10)), "p90": float(np.percentile(a, 90))}
 
-    reps, wall, cpu = 0, 0.0, 0.0
-    out = None
-    while reps < max_reps and (wall < min_seconds or reps == 0):
-        c0, t0 = time.process_time(), time.perf_counter()
-        out = A.decode(wl.q, wl.kc_full, wl.vc_full, wl.tables, wl.lens, wl.scale,
-                       block_size=wl.bs)
-        wall += time.perf_counter() - t0
-        cpu += time.process_time() - c0
-        reps += 1
-    per_call = wall / reps
+
+def host_info():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover - informational only
+        pass
     try:
         from threadpoolctl import threadpool_info
         blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover - informational only
         blas = None
-    res = {
-        "value": wl.kv_bytes() / per_call / 1e9,
-        "unit": "GB/s",
-        "cores": max(1, int(math.ceil(cpu / wall - 0.05))),
-        "kind": "oracle",
-        "sample": f"full batch ({wl.S} sequences, {int(wl.lens.sum())} context tokens) x {reps} "
-                  f"passes of the float64 oracle, {per_call:.2f} s per pass",
-        "tokens_per_s": wl.S / per_call,
-        "host_cores_visible": len(os.sched_getaffinity(0)),
-        "blas_threads": blas,
-    }
-    return res, out
+    return {"cpu_model": model, "host_cores_visible": len(os.sched_getaffinity(0)),
+            "numpy": np.__version__, "blas_threads": blas}
+
+
+class OracleClock:
+    """Wall and CPU time of the oracle calls made through it."""
+
+    def __init__(self):
+        self.wall = 0.0
+        self.cpu = 0.0
+
+    def __call__(self, fn, *args, **kw):
+        c0, t0 = time.process_time(), time.perf_counter()
+        r = fn(*args, **kw)
+        self.wall += time.perf_counter() - t0
+        self.cpu += time.process_time() - c0
+        return r
+
+    def baseline(self, nbytes: float, sample: str, **extra):
+        """The oracle's rate over its sample, as KV GB/s on the workload's own
+        byte rule (the K/V rows the sampled sequences attend to)."""
+        wall = max(self.wall, 1e-9)
+        return {"value": nbytes / wall / 1e9, "unit": "GB/s",
+                "cores": max(1, int(math.ceil(self.cpu / wall - 0.05))), "kind": "oracle",
+                "sample": sample, "seconds": self.wall, **extra, **host_info()}
 
 
 # ---------------------------------------------------------------------------
@@ -224,18 +223,115 @@ def base_result(a, metric, value, unit, ms_per_step, dtype, config):
     }
 
 
-def roofline(kernel, bound, achieved, peak, unit, traffic=None):
-    return {"kernel": kernel, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
-            "frac": achieved / peak, "traffic": traffic}
+def roofline(kernel, bound, achieved, peak, unit, traffic=None, traffic_source=None):
+    r = {"kernel": kernel, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+         "frac": achieved / peak, "traffic": traffic}
+    if traffic_source is not None:
+        r["traffic_source"] = traffic_source
+    return r
 
 
-METRIC = "paged decode attention: KV GB/s (% of HBM peak) + tokens/s at 7B shape"
-BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16/f16 matrix peak, published
+def free_device(torch):
+    import gc
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
 
 # ---------------------------------------------------------------------------
 # 7B-shape decode (the headline line)
 # ---------------------------------------------------------------------------
+class Workload:
+    """7B-shape decode batch, built through the library's block manager."""
+
+    def __init__(self, seed: int = 1, num_seqs: int = 64, heads: int = 32, head_dim: int = 128,
+                 len_range=(128, 2048), block_size: int = BLOCK):
+        import paged_kv_cache_366_amd as pkv
+        from synth import workloads as W
+
+        rng = np.random.default_rng(seed)
+        self.S, self.H, self.D, self.bs = num_seqs, heads, head_dim, block_size
+        bs = block_size
+        lens = W.draw_lengths(rng, num_seqs, *len_range)
+        nb = W.pool_size(lens, 1.25, bs)
+        perm = W.draw_permutation(rng, nb)
+        t0 = time.perf_counter()
+        bm = pkv.pkv_bm_create(nb, bs, perm)
+        seqs = [pkv.pkv_seq_create(bm, int(n) - 1) for n in lens]
+        t1 = time.perf_counter()
+        slots, cow = pkv.pkv_seq_append_batch(bm, seqs)
+        self.max_blocks = int(max(W.blocks_for(n, bs) for n in lens))
+        tables, lens_bm = pkv.pkv_seq_export(bm, seqs, self.max_blocks)
+        t2 = time.perf_counter()
+        assert len(cow) == 0 and np.array_equal(lens_bm, lens)
+        self.host_bm = {"create_us": (t1 - t0) * 1e6, "append_export_us": (t2 - t1) * 1e6}
+        self.bm, self.seqs, self.perm = bm, seqs, perm
+        q = W.draw_normal(rng, (num_seqs, heads, head_dim), "bf16")
+        kc, vc, _, _ = W.draw_paged_kv(rng, tables, lens, nb, heads, head_dim, "bf16", bs)
+        self.lens, self.tables, self.slots, self.q = lens, tables, slots, q
+        self.kc_full, self.vc_full = kc, vc          # with the current token (oracle side)
+        blk, row = slots // bs, slots % bs
+        self.new_k = kc[blk, :, row, :].copy()       # [S, H, D]
+        self.new_v = vc[blk, :, row, :].copy()
+        self.num_blocks = nb
+        self.scale = np.float32(1.0 / math.sqrt(head_dim))
+
+    # algorithmic bytes (bf16 everywhere, fp32 output)
+    def kv_bytes(self) -> int:
+        return int(self.lens.astype(np.int64).sum()) * self.H * self.D * 2 * 2
+
+    def main_kernel_bytes(self) -> int:
+        tbl = int(sum(W_blocks(n, self.bs) for n in self.lens)) * 4
+        return self.kv_bytes() + self.S * self.H * self.D * 2 + tbl + self.S * 4
+
+    def step_bytes(self) -> int:
+        out = self.S * self.H * self.D * 4
+        rc = self.S * self.H * self.D * 2 * 2 * 2 + self.S * 4   # read new K,V + write them
+        return self.main_kernel_bytes() + out + rc
+
+
+def cpu_baseline(wl: Workload, min_seconds: float = 10.0, max_reps: int = 40):
+    """The oracle over the whole batch, repeated until at least min_seconds."""
+    from oracle import attention as A
+
+    clock = OracleClock()
+    reps = 0
+    out = None
+    while reps < max_reps and (clock.wall < min_seconds or reps == 0):
+        out = clock(A.decode, wl.q, wl.kc_full, wl.vc_full, wl.tables, wl.lens, wl.scale,
+                    block_size=wl.bs)
+        reps += 1
+    per_call = clock.wall / reps
+    res = clock.baseline(
+        wl.kv_bytes() * reps,
+        f"full batch ({wl.S} sequences, {int(wl.lens.sum())} context tokens) x {reps} passes of "
+        f"the float64 oracle, {per_call:.2f} s per pass",
+        tokens_per_s=wl.S / per_call)
+    return res, out
+
+
+def allocation_latency(pkv, wl: Workload, rounds: int = 40):
+    """Page-allocation latency inside the library on the 7B-shape pool: each
+    round creates the batch's 64 sequences at their cached lengths, appends
+    their current token, and frees them; the library times every call that
+    takes blocks (64 creates and one batch append per round)."""
+    bm = pkv.pkv_bm_create(wl.num_blocks, wl.bs, wl.perm)
+    try:
+        for _ in range(rounds):
+            seqs = [pkv.pkv_seq_create(bm, int(n) - 1) for n in wl.lens]
+            pkv.pkv_seq_append_batch(bm, seqs)
+            for s_ in seqs:
+                pkv.pkv_seq_free(bm, s_)
+        lat = pkv.pkv_bm_latency_get(bm)
+    finally:
+        pkv.pkv_bm_destroy(bm)
+    lat["bar_p99_us"] = PAGE_ALLOC_P99_BAR_US
+    lat["meets_bar"] = bool(lat["p99_us"] < PAGE_ALLOC_P99_BAR_US)
+    lat["workload"] = (f"{rounds} rounds of: create the 64 sequences of the 7B-shape batch "
+                       f"({wl.num_blocks}-block pool), append one token each, free them")
+    return lat
+
+
 def bench_decode7b(a, torch, pkv, algo):
     print("[bench] building the 7B-shape decode workload on the host", file=sys.stderr, flush=True)
     wl = Workload(seed=a.seed, block_size=a.block_size)
@@ -283,10 +379,7 @@ def bench_decode7b(a, torch, pkv, algo):
     step_bytes = wl.step_bytes()
     main_bytes = wl.main_kernel_bytes()
     achieved = main_bytes / (main_avg * 1e-3) / 1e9
-    traffic = None
-    if (TRAFFIC["sources_sha1"] == kernel_sources_sha1() and TRAFFIC["bytes_per_launch"]
-            and wl.bs == BLOCK):
-        traffic = TRAFFIC["bytes_per_launch"]
+    traffic, tsrc = traffic_of("decode7b") if wl.bs == BLOCK else (None, "not measured")
     result = base_result(a, METRIC, step_bytes / (ms_per_step * 1e-3) / 1e9, "GB/s", ms_per_step,
                          "bf16", {
         "workload": "7B-shape paged decode, bf16 KV and q, fp32 accumulate: 64 sequences, "
@@ -298,23 +391,26 @@ def bench_decode7b(a, torch, pkv, algo):
     result.update({
         "tokens_per_s": wl.S / (ms_per_step * 1e-3),
         "hbm_frac_step": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "kernel_ms": {"reshape_and_cache": float(np.mean(rc_ms)), "decode_main": main_avg,
-                      "decode_main_median": float(np.median(main_ms)),
-                      "reduce": float(np.mean(red_ms))},
+        "kernel_ms": {"reshape_and_cache": stats_ms(rc_ms), "decode_main": stats_ms(main_ms),
+                      "reduce": stats_ms(red_ms)},
         "bytes": {"step": step_bytes, "decode_main": main_bytes, "kv": wl.kv_bytes()},
         "roofline": roofline("decode_wave_kernel (split-K main)", "hbm", achieved, HBM_PEAK_GBS,
-                             "GB/s", traffic),
+                             "GB/s", traffic, tsrc),
         "host_block_manager_us": wl.host_bm,
+        "page_allocation_latency": allocation_latency(pkv, wl),
         "block_manager": {k: v for k, v in pkv.pkv_bm_stats_get(wl.bm).items()
                           if k in ("num_blocks", "used_blocks", "logical_blocks", "waste_slots")},
         "cpu_baseline": None,
     })
+    got = out.cpu().numpy().astype(np.float64)
+    del kc, vc, ws
+    free_device(torch)
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle on the same batch", file=sys.stderr, flush=True)
-        cb, ref = cpu_baseline(wl)
+        cb, ref = cpu_baseline(wl, min_seconds=a.oracle_seconds)
         result["cpu_baseline"] = cb
-        got = out.cpu().numpy().astype(np.float64)
         result["max_abs_err_vs_oracle"] = float(np.abs(got - ref).max())
+    pkv.pkv_bm_destroy(wl.bm)
     return result
 
 
@@ -327,31 +423,53 @@ def owned_blocks(c, W):
             for s_, n in enumerate(c.context_lens) for j in range(W.blocks_for(n))]
 
 
-def bench_gqa(a, torch, pkv, algo, kv: str):
+def coded_rows(c, cache, s_, qmax):
+    """Rows [0, n) of sequence s_ for every KV head as the oracle's block
+    encoder codes them (codes x scale, float64), from the host pool."""
+    from oracle import quantize as Q
+    from synth import workloads as W
+    n = int(c.context_lens[s_])
+    out = np.empty((n, cache.shape[1], cache.shape[3]), np.float64)
+    for j in range(W.blocks_for(n)):
+        f = min(BLOCK, n - BLOCK * j)
+        b = c.block_tables[s_, j]
+        for g in range(cache.shape[1]):
+            codes, sc = Q.quantize_tile(cache[b, g], f, qmax)
+            out[BLOCK * j:BLOCK * j + f, g] = codes[:f].astype(np.float64) * np.float64(sc)
+    return out
+
+
+def gqa_case():
     from synth import workloads as W
     print("[bench] building the long-context GQA workload on the host", file=sys.stderr,
           flush=True)
+    return W.gqa_long_decode(seed=4)
+
+
+def bench_gqa(a, torch, pkv, algo, kv: str, c=None, sample_seqs: int = 6):
+    from oracle import attention as A
+    from oracle import quantize as Q
+    from synth import workloads as W
+    if c is None:
+        c = gqa_case()
     int8, int4 = kv == "int8", kv == "int4"
-    c = W.gqa_long_decode(seed=4, int8=int8)
     dev = "cuda"
-    if int8:
-        kc = torch.from_numpy(c.k_i8).to(dev)
-        vc = torch.from_numpy(c.v_i8).to(dev)
-        ks = torch.from_numpy(c.k_scale).to(dev)
-        vs = torch.from_numpy(c.v_scale).to(dev)
-    elif int4:
-        # the 4-bit pool is the block encoder's output over the bf16 pool
-        # (built before the timed region)
+    if int8 or int4:
+        # the int8 / 4-bit pool is the library's block encoder output over
+        # the bf16 pool (built before the timed region)
         sk, sv = to_dev_bf16(c.k_cache, torch), to_dev_bf16(c.v_cache, torch)
         nb_, hkv_, D_ = c.num_blocks, c.kv_heads, c.head_dim
-        kc = torch.zeros((nb_, hkv_, BLOCK, D_ // 2), dtype=torch.uint8, device=dev)
+        width = D_ if int8 else D_ // 2
+        kc = torch.zeros((nb_, hkv_, BLOCK, width), dtype=torch.int8 if int8 else torch.uint8,
+                         device=dev)
         vc = torch.zeros_like(kc)
         ks = torch.zeros((nb_, hkv_), dtype=torch.float32, device=dev)
         vs = torch.zeros_like(ks)
         own = owned_blocks(c, W)
-        pkv.pkv_quantize_blocks_int4(
-            sk, sv, kc, vc, ks, vs, torch.from_numpy(np.array([b for b, _ in own], np.int32)).to(dev),
-            torch.from_numpy(np.array([f for _, f in own], np.int32)).to(dev))
+        encode = pkv.pkv_quantize_blocks if int8 else pkv.pkv_quantize_blocks_int4
+        encode(sk, sv, kc, vc, ks, vs,
+               torch.from_numpy(np.array([b for b, _ in own], np.int32)).to(dev),
+               torch.from_numpy(np.array([f for _, f in own], np.int32)).to(dev))
         torch.cuda.synchronize()
         del sk, sv
     else:
@@ -400,6 +518,8 @@ def bench_gqa(a, torch, pkv, algo, kv: str):
         if ev is not None:
             ev[3].record(stream)
 
+    print(f"[bench] GQA {kv}: warmup {a.warmup}, timing {a.steps} steps", file=sys.stderr,
+          flush=True)
     ms_per_step, (wr_ms, main_ms, red_ms) = run_timed(torch, step, a.steps, a.warmup, 3)
     tokens = int(c.context_lens.astype(np.int64).sum())
     bits = 8 if int8 else 4 if int4 else 16
@@ -412,37 +532,34 @@ def bench_gqa(a, torch, pkv, algo, kv: str):
     step_bytes = main_bytes + S * hq * D * 4 + wr_bytes
     main_avg = float(np.mean(main_ms))
     achieved = main_bytes / (main_avg * 1e-3) / 1e9
-    # sampled parity of this run's output against the oracle, one row at a time
-    from oracle import attention as A
+    got = out.cpu().numpy()
+    del kc, vc, ws, ks, vs
+    free_device(torch)
+    # sampled parity of this run's output against the oracle, whole sequences
+    # (every query head), from the host pool; the oracle encodes int8 / 4-bit
+    # tiles itself.  The same calls are the CPU baseline's sample.
     rng = np.random.default_rng(1)
     G = hq // hkv
-    got = out.cpu().numpy()
+    clock = OracleClock()
     err = 0.0
-    src_k, src_v = (c.k_i8, c.v_i8) if int8 else (c.k_cache, c.v_cache)
-    sk, sv = (c.k_scale, c.v_scale) if int8 else (None, None)
-    if int4:
-        from oracle import quantize as Q
-
-        def rows4(cache, s_, g):
-            # the oracle's 4-bit encoding of this sequence's tiles, decoded
-            n = int(c.context_lens[s_])
-            out_rows = []
-            for j in range(W.blocks_for(n)):
-                f = min(BLOCK, n - BLOCK * j)
-                codes, sc = Q.quantize_tile(cache[c.block_tables[s_, j], g], f, Q.INT4_MAX)
-                out_rows.append(codes[:f].astype(np.float64) * np.float64(sc))
-            return np.concatenate(out_rows)
-    for s_, h_ in zip(rng.integers(0, S, 6), rng.integers(0, hq, 6)):
+    pick = rng.choice(S, min(sample_seqs, S), replace=False)
+    for s_ in pick:
         n = int(c.context_lens[s_])
-        if int4:
-            K, V = rows4(c.k_cache, s_, h_ // G), rows4(c.v_cache, s_, h_ // G)
+        if scaled:
+            qmax = Q.INT8_MAX if int8 else Q.INT4_MAX
+            K = clock(coded_rows, c, c.k_cache, s_, qmax)
+            V = clock(coded_rows, c, c.v_cache, s_, qmax)
         else:
-            K = A.gather(src_k, c.block_tables[s_], n, BLOCK, sk)[:, h_ // G]
-            V = A.gather(src_v, c.block_tables[s_], n, BLOCK, sv)[:, h_ // G]
-        err = max(err, float(np.abs(got[s_, h_] - A.attend(c.q[s_, h_], K, V, c.scale)).max()))
-    kv_text = {"int8": "int8 KV with per-block fp32 scales",
+            K = clock(A.gather, c.k_cache, c.block_tables[s_], n, BLOCK)
+            V = clock(A.gather, c.v_cache, c.block_tables[s_], n, BLOCK)
+        for h_ in range(hq):
+            ref = clock(A.attend, c.q[s_, h_], K[:, h_ // G], V[:, h_ // G], c.scale)
+            err = max(err, float(np.abs(got[s_, h_] - ref).max()))
+    sample_tokens = int(sum(int(c.context_lens[s_]) for s_ in pick))
+    kv_text = {"int8": "int8 KV (block encoder output) with per-block fp32 scales",
                "int4": "4-bit KV (block encoder output) with per-block fp32 scales",
                "bf16": "bf16 KV"}[kv]
+    traffic, tsrc = traffic_of(f"gqa-{kv}")
     result = base_result(a, METRIC, step_bytes / (ms_per_step * 1e-3) / 1e9, "GB/s", ms_per_step,
                          "bf16" if kv == "bf16" else f"{kv}-kv/bf16", {
         "workload": f"long-context GQA decode, {kv_text}: "
@@ -452,14 +569,19 @@ def bench_gqa(a, torch, pkv, algo, kv: str):
         "context_tokens": tokens, "partition_tokens": part, "algo": a.algo})
     result.update({
         "tokens_per_s": S / (ms_per_step * 1e-3),
-        "kernel_ms": {"cache_write" + ("" if kv == "bf16" else "_" + kv): float(np.mean(wr_ms)),
-                      "decode_main": main_avg, "reduce": float(np.mean(red_ms))},
+        "kernel_ms": {"cache_write" + ("" if kv == "bf16" else "_" + kv): stats_ms(wr_ms),
+                      "decode_main": stats_ms(main_ms), "reduce": stats_ms(red_ms)},
         "bytes": {"step": step_bytes, "decode_main": main_bytes, "kv": kvb},
+        "kv_gbs_step": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "roofline": roofline("decode_mfma_kernel (split-K main)" if algo != pkv.PKV_ALGO_WAVE
                              else "decode_wave_kernel (split-K main)", "hbm", achieved,
-                             HBM_PEAK_GBS, "GB/s"),
+                             HBM_PEAK_GBS, "GB/s", traffic, tsrc),
         "max_abs_err_vs_oracle_sampled": err,
-        "cpu_baseline": None,
+        "cpu_baseline": None if a.no_cpu_baseline else clock.baseline(
+            sample_tokens * hkv * D * bits // 8 * 2,
+            f"{len(pick)} whole sequences ({sample_tokens} tokens, all {hq} query heads) of the "
+            "batch through the float64 oracle" + (" (with its own block encoder)" if scaled
+                                                 else "")),
     })
     return result
 
@@ -468,6 +590,7 @@ def bench_gqa(a, torch, pkv, algo, kv: str):
 # continuous-batching mixed step: decode sequences + prefill chunks
 # ---------------------------------------------------------------------------
 def bench_mixed(a, torch, pkv, algo):
+    from oracle import attention as A
     from synth import workloads as W
     print("[bench] building the mixed-step workload on the host", file=sys.stderr, flush=True)
     ms = W.mixed_step(seed=2)
@@ -507,7 +630,7 @@ def bench_mixed(a, torch, pkv, algo):
     qsl = np.concatenate([[0], np.cumsum(ms.new[pre])]).astype(np.int32)
     qsl_d = torch.from_numpy(qsl).to(dev)
     mc_d, mc_p, mq = int(lens[dec].max()), int(lens[pre].max()), int(ms.new[pre].max())
-    part = a.partition
+    part = a.partition if a.partition_set else 1024
     out_d = torch.empty(q_d.shape, dtype=torch.float32, device=dev)
     out_p = torch.empty(q_p.shape, dtype=torch.float32, device=dev)
     ws = torch.empty(max(pkv.pkv_decode_workspace_bytes(len(dec), hq, D, mc_d, part), 1),
@@ -534,6 +657,8 @@ def bench_mixed(a, torch, pkv, algo):
         if ev is not None:
             ev[3].record(stream)
 
+    print(f"[bench] mixed step: warmup {a.warmup}, timing {a.steps} steps", file=sys.stderr,
+          flush=True)
     ms_per_step, (rc_ms, dec_ms, pre_ms) = run_timed(torch, step, a.steps, a.warmup, 3)
     T = int(ms.new.sum())
     kv_dec = int(lens[dec].astype(np.int64).sum()) * hkv * D * 4
@@ -548,29 +673,43 @@ def bench_mixed(a, torch, pkv, algo):
         flops += sum(n - ql + i + 1 for i in range(ql)) * hq * D * 4
     pre_avg = float(np.mean(pre_ms))
     dec_avg = float(np.mean(dec_ms))
-    # sampled parity: a few prefill rows and decode rows against the oracle
-    from oracle import attention as A
-    rng = np.random.default_rng(0)
     got_p, got_d = out_p.cpu().numpy(), out_d.cpu().numpy()
-    err = 0.0
+    pkv.pkv_bm_destroy(bm)
+    del kc, vc, ws, ws_p
+    free_device(torch)
+
+    # sampled parity against the oracle over each sequence's logical rows
+    # (the cached prior rows, then the step's new rows), from the host draws.
+    # The same calls are the CPU baseline's sample.
+    def logical(s_):
+        K = np.concatenate([ms.prior_k[s_], ms.new_k[starts[s_]:starts[s_ + 1]]])
+        V = np.concatenate([ms.prior_v[s_], ms.new_v[starts[s_]:starts[s_ + 1]]])
+        return K.astype(np.float64), V.astype(np.float64)
+
+    rng = np.random.default_rng(0)
+    G = hq // hkv
+    clock, clock_p = OracleClock(), OracleClock()
+    err_d = err_p = 0.0
+    dec_pick = rng.choice(len(dec), 24, replace=False)
+    for j in dec_pick:
+        s_ = dec[j]
+        K, V = clock(logical, s_)
+        for h_ in range(hq):
+            ref = clock(A.attend, ms.q[starts[s_], h_], K[:, h_ // G], V[:, h_ // G], ms.scale)
+            err_d = max(err_d, float(np.abs(got_d[j, h_] - ref).max()))
+    dec_tokens = int(sum(int(lens[dec[j]]) for j in dec_pick))
+    pre_flops = 0
     for j, s_ in enumerate(pre):
         n, ql = int(lens[s_]), int(ms.new[s_])
-        K = gather_dev_all(kc, tables[s_], n, torch)
-        V = gather_dev_all(vc, tables[s_], n, torch)
+        K, V = clock_p(logical, s_)
         for i in (0, ql // 2, ql - 1):
-            h_ = int(rng.integers(0, hq))
             P = n - ql + i
-            ref = A.attend(ms.q[rows_p[qsl[j] + i], h_], K[:P + 1, h_], V[:P + 1, h_], ms.scale)
-            err = max(err, float(np.abs(got_p[qsl[j] + i, h_] - ref).max()))
-    for j in rng.choice(len(dec), 4, replace=False):
-        s_ = dec[j]
-        n = int(lens[s_])
-        K = gather_dev_all(kc, tables[s_], n, torch)
-        V = gather_dev_all(vc, tables[s_], n, torch)
-        h_ = int(rng.integers(0, hq))
-        ref = A.attend(ms.q[starts[s_], h_], K[:, h_], V[:, h_], ms.scale)
-        err = max(err, float(np.abs(got_d[j, h_] - ref).max()))
-    pkv.pkv_bm_destroy(bm)
+            for h_ in range(hq):
+                ref = clock_p(A.attend, ms.q[rows_p[qsl[j] + i], h_], K[:P + 1, h_ // G],
+                              V[:P + 1, h_ // G], ms.scale)
+                err_p = max(err_p, float(np.abs(got_p[qsl[j] + i, h_] - ref).max()))
+                pre_flops += 4 * D * (P + 1)
+    traffic, tsrc = traffic_of("mixed-decode")
     result = base_result(a, METRIC, step_bytes / (ms_per_step * 1e-3) / 1e9, "GB/s", ms_per_step,
                          "bf16", {
         "workload": "continuous-batching mixed step, bf16: 48 decode sequences (contexts "
@@ -581,36 +720,37 @@ def bench_mixed(a, torch, pkv, algo):
         "algo": a.algo})
     result.update({
         "tokens_per_s": (len(dec) + len(rows_p)) / (ms_per_step * 1e-3),
-        "kernel_ms": {"reshape_and_cache": float(np.mean(rc_ms)), "decode_and_reduce": dec_avg,
-                      "prefill": pre_avg},
+        "kernel_ms": {"reshape_and_cache": stats_ms(rc_ms), "decode_and_reduce": stats_ms(dec_ms),
+                      "prefill": stats_ms(pre_ms)},
         "bytes": {"step": step_bytes, "decode": dec_bytes, "prefill_unique": pre_bytes,
                   "reshape_and_cache": rc_bytes},
+        "kv_gbs_decode": dec_bytes / (dec_avg * 1e-3) / 1e9,
         "prefill_gflop": flops / 1e9,
+        "prefill_tflops": flops / (pre_avg * 1e-3) / 1e12,
         "roofline": roofline("decode_wave_kernel + reduce (decode part)", "hbm",
-                             dec_bytes / (dec_avg * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
+                             dec_bytes / (dec_avg * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s", traffic,
+                             tsrc),
         "roofline_prefill": roofline("prefill_mfma_kernel", "mfma",
                                      flops / (pre_avg * 1e-3) / 1e12, BF16_MFMA_PEAK_TFLOPS,
                                      "TFLOP/s"),
         "host_block_manager_us": {"append_export_us": host_us},
-        "max_abs_err_vs_oracle_sampled": err,
-        "cpu_baseline": None,
+        "max_abs_err_vs_oracle_sampled": max(err_d, err_p),
+        "max_abs_err_vs_oracle_sampled_parts": {"decode": err_d, "prefill": err_p},
+        "cpu_baseline": None if a.no_cpu_baseline else clock.baseline(
+            dec_tokens * hkv * D * 4,
+            f"24 decode sequences ({dec_tokens} tokens, all {hq} heads) through the float64 "
+            f"oracle (value); 3 rows of each prefill chunk, all heads (prefill_tflops)",
+            prefill_seconds=clock_p.wall,
+            prefill_tflops=pre_flops / max(clock_p.wall, 1e-9) / 1e12),
     })
     return result
-
-
-def gather_dev_all(cache, table_row, n, torch):
-    """Rows [0, n) of every KV head of a bf16 device pool through one table
-    row, read back as float64 [n, heads, D] for the oracle's per-row check."""
-    nb = -(-n // BLOCK)
-    idx = torch.from_numpy(np.asarray(table_row[:nb], np.int64)).to(cache.device)
-    rows = cache[idx].float().permute(0, 2, 1, 3).reshape(nb * BLOCK, cache.shape[1], -1)[:n]
-    return rows.cpu().numpy().astype(np.float64)
 
 
 # ---------------------------------------------------------------------------
 # shared prefix + beam search with copy-on-write
 # ---------------------------------------------------------------------------
 def bench_beam(a, torch, pkv, algo):
+    from oracle import attention as A
     from synth import workloads as W
     print("[bench] building the shared-prefix beam workload on the host", file=sys.stderr,
           flush=True)
@@ -674,24 +814,38 @@ def bench_beam(a, torch, pkv, algo):
         if ev is not None:
             ev[2].record(stream)
 
+    print(f"[bench] beams: warmup {a.warmup}, timing {a.steps} steps", file=sys.stderr,
+          flush=True)
     ms_per_step, (cow_ms, dec_ms) = run_timed(torch, step, a.steps, a.warmup, 2)
     logical = int(lens.astype(np.int64).sum()) * hkv * D * 4
     unique_blocks = len(set(int(b) for s_ in range(S) for b in tables[s_, :W.blocks_for(lens[s_])]))
     unique = unique_blocks * hkv * BLOCK * D * 4
     dec_avg = float(np.mean(dec_ms))
-    from oracle import attention as A
     got = out.cpu().numpy()
-    rng = np.random.default_rng(0)
-    err = 0.0
-    for s_ in rng.choice(S, 6, replace=False):
-        n = int(lens[s_])
-        K = gather_dev_all(kc, tables[s_], n, torch)
-        V = gather_dev_all(vc, tables[s_], n, torch)
-        h_ = int(rng.integers(0, hq))
-        ref = A.attend(bc.q[s_, h_], K[:, h_], V[:, h_], bc.scale)
-        err = max(err, float(np.abs(got[s_, h_] - ref).max()))
     pkv.pkv_bm_destroy(bm)
-    result = base_result(a, METRIC, logical / (dec_avg * 1e-3) / 1e9, "GB/s (logical)",
+    del kc, vc, ws
+    free_device(torch)
+    # sampled parity over each beam's logical rows (prefix, the request's own
+    # tokens, the beam's token) from the host draws; the CPU baseline's sample
+    rng = np.random.default_rng(0)
+    clock = OracleClock()
+    err = 0.0
+    pick = rng.choice(S, 32, replace=False)
+
+    def logical_rows(b):
+        r = b // bc.beam_width
+        K = np.concatenate([bc.prefix_k, bc.req_k[r], bc.beam_k[b:b + 1]]).astype(np.float64)
+        V = np.concatenate([bc.prefix_v, bc.req_v[r], bc.beam_v[b:b + 1]]).astype(np.float64)
+        return K, V
+
+    for b in pick:
+        K, V = clock(logical_rows, int(b))
+        assert K.shape[0] == lens[b]
+        for h_ in range(hq):
+            ref = clock(A.attend, bc.q[b, h_], K[:, h_], V[:, h_], bc.scale)
+            err = max(err, float(np.abs(got[b, h_] - ref).max()))
+    sample_tokens = int(sum(int(lens[b]) for b in pick))
+    result = base_result(a, METRIC, unique / (dec_avg * 1e-3) / 1e9, "GB/s (unique K/V)",
                          ms_per_step, "bf16", {
         "workload": "shared-prefix beam search with copy-on-write, bf16: 16 requests sharing a "
                     "1024-token prefix, 1-200 own tokens, beam width 4; step = copy_blocks of the "
@@ -700,16 +854,22 @@ def bench_beam(a, torch, pkv, algo):
         "kv_loads": "cached" if load_policy else "pool-size rule"})
     result.update({
         "tokens_per_s": S / (ms_per_step * 1e-3),
-        "kernel_ms": {"copy_blocks_and_reshape": float(np.mean(cow_ms)),
-                      "decode_and_reduce": dec_avg},
+        "kernel_ms": {"copy_blocks_and_reshape": stats_ms(cow_ms),
+                      "decode_and_reduce": stats_ms(dec_ms)},
         "bytes": {"logical_kv": logical, "unique_kv": unique},
-        "note": "logical bytes count shared blocks once per beam; the unique working set "
-                "fits the 256 MB MALL, so logical GB/s may exceed the HBM peak",
-        "roofline": roofline("decode_wave_kernel + reduce (logical bytes)", "hbm",
-                             logical / (dec_avg * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
+        "note": "the unique K/V working set (each shared block once) fits the 256 MB "
+                "memory-side cache; roofline is unique bytes against HBM, logical bytes (shared "
+                "blocks once per beam) are the cache-served rate",
+        "roofline": roofline("decode_wave_kernel + reduce (unique K/V bytes)", "hbm",
+                             unique / (dec_avg * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
+        "logical_kv_gbs": {"bound": "cache", "achieved": logical / (dec_avg * 1e-3) / 1e9,
+                           "unit": "GB/s"},
         "block_manager": {"append_export_us": host_us, **stats},
         "max_abs_err_vs_oracle_sampled": err,
-        "cpu_baseline": None,
+        "cpu_baseline": None if a.no_cpu_baseline else clock.baseline(
+            sample_tokens * hkv * D * 4,
+            f"32 beams ({sample_tokens} logical tokens, all {hq} heads) through the float64 "
+            "oracle; value in logical K/V bytes"),
     })
     return result
 
@@ -935,8 +1095,8 @@ def bench_prefix(a, torch, pkv, algo):
     err = 0.0
     for j in rng.choice(len(rest), 4, replace=False):
         r, n = rest[j], int(lens[rest[j]])
-        K = gather_dev_all(kc, hit["tables_h"][j], n, torch)
-        V = gather_dev_all(vc, hit["tables_h"][j], n, torch)
+        K = c.k[r].astype(np.float64)     # the request's rows, as written
+        V = c.v[r].astype(np.float64)
         for i in (0, hit["rows"][j] - 1):
             P = cached[j] + i
             h_ = int(rng.integers(0, hq))
@@ -1015,8 +1175,8 @@ def bench_prefill_long(a, torch, pkv, algo):
     rng = np.random.default_rng(0)
     err = 0.0
     for s_ in range(4):
-        K = gather_dev_all(kc, c.block_tables[s_], 16384, torch)
-        V = gather_dev_all(vc, c.block_tables[s_], 16384, torch)
+        K = A.gather(c.k_cache, c.block_tables[s_], 16384, BLOCK)
+        V = A.gather(c.v_cache, c.block_tables[s_], 16384, BLOCK)
         for i in (0, 63):
             h_ = int(rng.integers(0, hq))
             P = 16384 - 64 + i
@@ -1041,9 +1201,37 @@ def bench_prefill_long(a, torch, pkv, algo):
     return result
 
 
-WORKLOADS = ("decode7b", "mixed", "beam", "gqa", "gqa-int8", "gqa-int4", "quantize",
-             "quantize-int4", "swap", "prefix",
-             "prefill-long")
+WORKLOADS = ("all", "decode7b", "mixed", "beam", "gqa", "gqa-int8", "gqa-int4", "quantize",
+             "quantize-int4", "swap", "prefix", "prefill-long")
+
+# keys of a workload line kept when it is nested in the default line
+SUB_KEYS = ("value", "unit", "ms_per_step", "dtype", "config", "tokens_per_s", "kernel_ms",
+            "bytes", "kv_gbs_step", "kv_gbs_decode", "prefill_gflop", "prefill_tflops",
+            "roofline", "roofline_prefill", "logical_kv_gbs", "note", "block_manager",
+            "max_abs_err_vs_oracle_sampled", "max_abs_err_vs_oracle_sampled_parts",
+            "cpu_baseline")
+
+
+def nested(line: dict) -> dict:
+    return {k: line[k] for k in SUB_KEYS if k in line}
+
+
+def bench_all(a, torch, pkv, algo):
+    """The headline line with the other four workloads nested in it."""
+    t0 = time.perf_counter()
+    result = bench_decode7b(a, torch, pkv, algo)
+    free_device(torch)
+    result["c3_mixed"] = nested(bench_mixed(a, torch, pkv, algo))
+    free_device(torch)
+    result["c4_beam"] = nested(bench_beam(a, torch, pkv, algo))
+    free_device(torch)
+    c = gqa_case()
+    result["c5_gqa_bf16"] = nested(bench_gqa(a, torch, pkv, algo, "bf16", c))
+    free_device(torch)
+    result["c5_gqa_int8"] = nested(bench_gqa(a, torch, pkv, algo, "int8", c))
+    free_device(torch)
+    result["bench_wall_s"] = time.perf_counter() - t0
+    return result
 
 
 def main(argv=None) -> int:
@@ -1051,12 +1239,14 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", choices=WORKLOADS, default="decode7b",
-                    help="decode7b is the headline line; the others measure the other kernels")
+    ap.add_argument("--workload", choices=WORKLOADS, default="all",
+                    help="all: the headline 7B decode line with the mixed-step, beam and "
+                         "long-context GQA (bf16, int8) workloads nested in it; the others "
+                         "print one workload's line")
     ap.add_argument("--partition", type=int, default=None,
-                    help="split-K partition size in tokens (0 = no split); default 1536 for "
-                         "the 7B step, 1024 for the mixed step, 512 for the long-context GQA "
-                         "workloads, 0 for the beam workload")
+                    help="split-K partition size in tokens (0 = no split) for every workload "
+                         "run; default 1536 for the 7B step, 1024 for the mixed step, 512 for "
+                         "the long-context GQA workloads, 0 for the beam workload")
     ap.add_argument("--algo", choices=("auto", "wave", "mfma"), default="auto")
     ap.add_argument("--prefill-partition", type=int, default=0,
                     help="key partition size of chunked prefill in tokens (0 = no split)")
@@ -1064,6 +1254,8 @@ def main(argv=None) -> int:
                     help="KV block size of the decode7b workload (16 is the headline line)")
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--oracle-seconds", type=float, default=8.0,
+                    help="least CPU time of the headline's oracle baseline (whole-batch passes)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one elementwise kernel that reads and writes this many MiB "
                          "(a known-size kernel for scaling rocprofv3 byte counters)")
@@ -1074,10 +1266,10 @@ def main(argv=None) -> int:
         return 2
     a.partition_set = a.partition is not None
     if a.partition is None:
-        # split-K partition per workload (the GQA and beam workloads choose
-        # their own): 1,536 tokens for the 7B step, whose streaming MHA decode
-        # then runs 16-wave workgroups, 1,024 for the mixed step's longer tail
-        a.partition = 1024 if a.workload == "mixed" else 1536
+        # the 7B step's split-K partition (the other workloads choose their
+        # own unless --partition is given): 1,536 tokens, whose streaming MHA
+        # decode then runs 16-wave workgroups
+        a.partition = 1536
 
     import torch
     import paged_kv_cache_366_amd as pkv
@@ -1087,7 +1279,9 @@ def main(argv=None) -> int:
         return 2
     pkv.load()
     algo = {"auto": pkv.PKV_ALGO_AUTO, "wave": pkv.PKV_ALGO_WAVE, "mfma": pkv.PKV_ALGO_MFMA}[a.algo]
-    if a.workload == "decode7b":
+    if a.workload == "all":
+        result = bench_all(a, torch, pkv, algo)
+    elif a.workload == "decode7b":
         result = bench_decode7b(a, torch, pkv, algo)
     elif a.workload == "mixed":
         result = bench_mixed(a, torch, pkv, algo)
