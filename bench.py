@@ -285,9 +285,12 @@ class Workload:
         return self.kv_bytes() + self.S * self.H * self.D * 2 + tbl + self.S * 4
 
     def step_bytes(self) -> int:
+        """The step's algorithmic bytes: every K/V row the sequences attend
+        (the new token's read once, from its input rows), q, tables and
+        lengths, the fp32 output, and the new rows written to their slots."""
         out = self.S * self.H * self.D * 4
-        rc = self.S * self.H * self.D * 2 * 2 * 2 + self.S * 4   # read new K,V + write them
-        return self.main_kernel_bytes() + out + rc
+        new_rows = self.S * self.H * self.D * 2 * 2
+        return self.main_kernel_bytes() + out + new_rows
 
 
 def cpu_baseline(wl: Workload, min_seconds: float = 10.0, max_reps: int = 40):
@@ -349,61 +352,87 @@ def bench_decode7b(a, torch, pkv, algo):
     tables = torch.from_numpy(wl.tables).to(dev)
     lens = torch.from_numpy(wl.lens).to(dev)
     max_ctx = int(wl.lens.max())
+    part = a.partition if a.partition_set else 2048
     out = torch.empty((wl.S, wl.H, wl.D), dtype=torch.float32, device=dev)
-    ws_bytes = pkv.pkv_decode_workspace_bytes(wl.S, wl.H, wl.D, max_ctx, a.partition)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(pkv.pkv_decode_step_workspace_bytes(wl.S, wl.H, wl.D, max_ctx, part), 1),
+                     dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
 
+    # One launch per step: the attention kernel appends each sequence's new
+    # K/V rows at its last position and attends with them (2,048-token
+    # partitions cover every context, so no split and no reduce).
     def step(ev):
+        if ev is not None:
+            ev[0].record(stream)
+        pkv.pkv_paged_attention_decode_step(out, q, new_k, new_v, kc, vc, tables, lens, max_ctx,
+                                            float(wl.scale), part, algo, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+
+    print(f"[bench] warmup {a.warmup}, timing {a.steps} steps", file=sys.stderr, flush=True)
+    ms_per_step, (main_ms,) = run_timed(torch, step, a.steps, a.warmup, 1)
+    if a.calib_copy_mib:
+        calibration_kernel(torch, a.calib_copy_mib)
+    got = out.cpu().numpy().astype(np.float64)
+
+    # the same step as three launches (reshape_and_cache, split-K decode with
+    # 1,536-token partitions, reduce), for comparison
+    sep_part = 1536
+    ws3 = torch.empty(max(pkv.pkv_decode_workspace_bytes(wl.S, wl.H, wl.D, max_ctx, sep_part), 1),
+                      dtype=torch.uint8, device=dev)
+    out3 = torch.empty_like(out)
+
+    def step3(ev):
         if ev is not None:
             ev[0].record(stream)
         pkv.pkv_reshape_and_cache(new_k, new_v, kc, vc, slots)
         if ev is not None:
             ev[1].record(stream)
-        pkv.pkv_paged_attention_decode_partials(out, q, kc, vc, tables, lens, max_ctx,
-                                                float(wl.scale), a.partition, algo,
-                                                workspace=ws)
+        pkv.pkv_paged_attention_decode_partials(out3, q, kc, vc, tables, lens, max_ctx,
+                                                float(wl.scale), sep_part, algo, workspace=ws3)
         if ev is not None:
             ev[2].record(stream)
-        pkv.pkv_paged_attention_reduce(out, lens, max_ctx, a.partition, ws)
+        pkv.pkv_paged_attention_reduce(out3, lens, max_ctx, sep_part, ws3)
         if ev is not None:
             ev[3].record(stream)
 
-    print(f"[bench] warmup {a.warmup}, timing {a.steps} steps", file=sys.stderr, flush=True)
-    ms_per_step, (rc_ms, main_ms, red_ms) = run_timed(torch, step, a.steps, a.warmup, 3)
-    if a.calib_copy_mib:
-        calibration_kernel(torch, a.calib_copy_mib)
+    ms3, (rc_ms, main3_ms, red_ms) = run_timed(torch, step3, a.steps, a.warmup, 3)
+    sep_diff = float((out3 - out).abs().max())
 
     main_avg = float(np.mean(main_ms))
     step_bytes = wl.step_bytes()
-    main_bytes = wl.main_kernel_bytes()
-    achieved = main_bytes / (main_avg * 1e-3) / 1e9
+    achieved = step_bytes / (main_avg * 1e-3) / 1e9
     traffic, tsrc = traffic_of("decode7b") if wl.bs == BLOCK else (None, "not measured")
     result = base_result(a, METRIC, step_bytes / (ms_per_step * 1e-3) / 1e9, "GB/s", ms_per_step,
                          "bf16", {
         "workload": "7B-shape paged decode, bf16 KV and q, fp32 accumulate: 64 sequences, "
                     f"32 heads MHA, head_dim 128, block_size {wl.bs}, contexts U[128, 2048], "
-                    "pool 1.25x, random placement; step = reshape_and_cache + decode + reduce",
+                    "pool 1.25x, random placement; step = append of each sequence's new K/V "
+                    "rows + decode attention, one launch",
         "num_seqs": wl.S, "heads": wl.H, "head_dim": wl.D, "block_size": wl.bs,
         "context_tokens": int(wl.lens.sum()), "num_blocks": wl.num_blocks,
-        "partition_tokens": a.partition, "algo": a.algo, "seed": a.seed})
+        "partition_tokens": part, "algo": a.algo, "seed": a.seed})
     result.update({
         "tokens_per_s": wl.S / (ms_per_step * 1e-3),
         "hbm_frac_step": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "kernel_ms": {"reshape_and_cache": stats_ms(rc_ms), "decode_main": stats_ms(main_ms),
-                      "reduce": stats_ms(red_ms)},
-        "bytes": {"step": step_bytes, "decode_main": main_bytes, "kv": wl.kv_bytes()},
-        "roofline": roofline("decode_wave_kernel (split-K main)", "hbm", achieved, HBM_PEAK_GBS,
-                             "GB/s", traffic, tsrc),
+        "kernel_ms": {"decode_step": stats_ms(main_ms)},
+        "bytes": {"step": step_bytes, "kv": wl.kv_bytes(),
+                  "new_rows_written": wl.S * wl.H * wl.D * 2 * 2},
+        "roofline": roofline("decode_wave_kernel (append + attention, one launch per step)",
+                             "hbm", achieved, HBM_PEAK_GBS, "GB/s", traffic, tsrc),
+        "three_launch_step": {
+            "ms_per_step": ms3, "partition_tokens": sep_part,
+            "kernel_ms": {"reshape_and_cache": stats_ms(rc_ms), "decode_main": stats_ms(main3_ms),
+                          "reduce": stats_ms(red_ms)},
+            "max_abs_diff_vs_one_launch": sep_diff},
         "host_block_manager_us": wl.host_bm,
         "page_allocation_latency": allocation_latency(pkv, wl),
         "block_manager": {k: v for k, v in pkv.pkv_bm_stats_get(wl.bm).items()
                           if k in ("num_blocks", "used_blocks", "logical_blocks", "waste_slots")},
         "cpu_baseline": None,
     })
-    got = out.cpu().numpy().astype(np.float64)
-    del kc, vc, ws
+    del kc, vc, ws, ws3
     free_device(torch)
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle on the same batch", file=sys.stderr, flush=True)
@@ -483,8 +512,9 @@ def bench_gqa(a, torch, pkv, algo, kv: str, c=None, sample_seqs: int = 6):
     max_ctx = int(c.context_lens.max())
     part = a.partition if a.partition_set else 512
     out = torch.empty((S, hq, D), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(pkv.pkv_decode_workspace_bytes(S, hq, D, max_ctx, part), 1),
+    ws = torch.zeros(max(pkv.pkv_decode_step_workspace_bytes(S, hq, D, max_ctx, part), 1),
                      dtype=torch.uint8, device=dev)
+    scaled = int8 or int4
     # the step's cache write: each sequence's current token (the last
     # position) goes to its slot, into the int8 or 4-bit pool through
     # quantise-on-write (its block's scale already covers it, so the write is
@@ -498,6 +528,10 @@ def bench_gqa(a, torch, pkv, algo, kv: str, c=None, sample_seqs: int = 6):
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
 
+    # bf16: the attention launch appends the current token's rows itself
+    # (pkv_paged_attention_decode_step), then the reduce kernel merges the
+    # 512-token partitions: two launches.  int8 / 4-bit: quantise-on-write of
+    # the current token, the attention launch, the reduce: three.
     def step(ev):
         if ev is not None:
             ev[0].record(stream)
@@ -505,33 +539,37 @@ def bench_gqa(a, torch, pkv, algo, kv: str, c=None, sample_seqs: int = 6):
             pkv.pkv_reshape_and_cache_int8(new_k, new_v, kc, vc, ks, vs, slots_d)
         elif int4:
             pkv.pkv_reshape_and_cache_int4(new_k, new_v, kc, vc, ks, vs, slots_d)
-        else:
-            pkv.pkv_reshape_and_cache(new_k, new_v, kc, vc, slots_d)
         if ev is not None:
             ev[1].record(stream)
-        pkv.pkv_paged_attention_decode_partials(out, q, kc, vc, tables, lens, max_ctx,
-                                                float(c.scale), part, algo, k_scale=ks,
-                                                v_scale=vs, workspace=ws)
+        if scaled:
+            pkv.pkv_paged_attention_decode(out, q, kc, vc, tables, lens, max_ctx, float(c.scale),
+                                           part, algo, k_scale=ks, v_scale=vs, workspace=ws)
+        else:
+            pkv.pkv_paged_attention_decode_step(out, q, new_k, new_v, kc, vc, tables, lens,
+                                                max_ctx, float(c.scale), part, algo,
+                                                workspace=ws)
         if ev is not None:
             ev[2].record(stream)
-        pkv.pkv_paged_attention_reduce(out, lens, max_ctx, part, ws)
-        if ev is not None:
-            ev[3].record(stream)
 
     print(f"[bench] GQA {kv}: warmup {a.warmup}, timing {a.steps} steps", file=sys.stderr,
           flush=True)
-    ms_per_step, (wr_ms, main_ms, red_ms) = run_timed(torch, step, a.steps, a.warmup, 3)
+    ms_per_step, (wr_ms, main_ms) = run_timed(torch, step, a.steps, a.warmup, 2)
     tokens = int(c.context_lens.astype(np.int64).sum())
     bits = 8 if int8 else 4 if int4 else 16
-    scaled = int8 or int4
     kvb = tokens * hkv * D * bits // 8 * 2
     nblk = sum(W.blocks_for(n) for n in c.context_lens)
-    main_bytes = kvb + S * hq * D * 2 + nblk * 4 + S * 4 + (nblk * hkv * 8 if scaled else 0)
-    # + the cache write: bf16 rows read, rows written in the pool's type (and scales)
-    wr_bytes = S * hkv * D * 2 * 2 + S * hkv * D * bits // 8 * 2 + (S * hkv * 8 if scaled else 0)
-    step_bytes = main_bytes + S * hq * D * 4 + wr_bytes
+    # attention: every K/V row attended (the current token's once), q, table
+    # entries, lengths, scales, and the fp32 output
+    main_bytes = (kvb + S * hq * D * 2 + nblk * 4 + S * 4 + (nblk * hkv * 8 if scaled else 0)
+                  + S * hq * D * 4)
+    # + the cache write: the current token's rows written in the pool's type
+    # (and scales); quantise-on-write also reads its bf16 rows
+    wr_bytes = (S * hkv * D * bits // 8 * 2 + (S * hkv * 8 if scaled else 0)
+                + (S * hkv * D * 2 * 2 if scaled else 0))
+    step_bytes = main_bytes + wr_bytes
     main_avg = float(np.mean(main_ms))
-    achieved = main_bytes / (main_avg * 1e-3) / 1e9
+    # the attention launch(es): main kernel + reduce (the append included for bf16)
+    achieved = (main_bytes + (0 if scaled else wr_bytes)) / (main_avg * 1e-3) / 1e9
     got = out.cpu().numpy()
     del kc, vc, ws, ks, vs
     free_device(torch)
@@ -565,17 +603,19 @@ def bench_gqa(a, torch, pkv, algo, kv: str, c=None, sample_seqs: int = 6):
         "workload": f"long-context GQA decode, {kv_text}: "
                     "16 sequences, 64 query heads over 8 KV heads, head_dim 128, "
                     "contexts U[8192, 32768]; step = cache write of each sequence's current "
-                    "token + split-K decode + reduce",
+                    "token (bf16: inside the attention launch; codes: quantise-on-write) + "
+                    "split-K decode with 512-token partitions + reduce kernel",
         "context_tokens": tokens, "partition_tokens": part, "algo": a.algo})
     result.update({
         "tokens_per_s": S / (ms_per_step * 1e-3),
-        "kernel_ms": {"cache_write" + ("" if kv == "bf16" else "_" + kv): stats_ms(wr_ms),
-                      "decode_main": stats_ms(main_ms), "reduce": stats_ms(red_ms)},
+        "kernel_ms": ({"cache_write_" + kv: stats_ms(wr_ms), "decode_and_reduce": stats_ms(main_ms)}
+                      if scaled else {"append_decode_and_reduce": stats_ms(main_ms)}),
         "bytes": {"step": step_bytes, "decode_main": main_bytes, "kv": kvb},
         "kv_gbs_step": step_bytes / (ms_per_step * 1e-3) / 1e9,
-        "roofline": roofline("decode_mfma_kernel (split-K main)" if algo != pkv.PKV_ALGO_WAVE
-                             else "decode_wave_kernel (split-K main)", "hbm", achieved,
-                             HBM_PEAK_GBS, "GB/s", traffic, tsrc),
+        "roofline": roofline(("decode_mfma_kernel" if algo != pkv.PKV_ALGO_WAVE
+                              else "decode_wave_kernel") + " + reduce_kernel"
+                             + ("" if scaled else " (append in the main kernel)"), "hbm",
+                             achieved, HBM_PEAK_GBS, "GB/s", traffic, tsrc),
         "max_abs_err_vs_oracle_sampled": err,
         "cpu_baseline": None if a.no_cpu_baseline else clock.baseline(
             sample_tokens * hkv * D * bits // 8 * 2,
@@ -1245,7 +1285,7 @@ def main(argv=None) -> int:
                          "print one workload's line")
     ap.add_argument("--partition", type=int, default=None,
                     help="split-K partition size in tokens (0 = no split) for every workload "
-                         "run; default 1536 for the 7B step, 1024 for the mixed step, 512 for "
+                         "run; default 2048 for the 7B step, 1024 for the mixed step, 512 for "
                          "the long-context GQA workloads, 0 for the beam workload")
     ap.add_argument("--algo", choices=("auto", "wave", "mfma"), default="auto")
     ap.add_argument("--prefill-partition", type=int, default=0,
@@ -1266,10 +1306,10 @@ def main(argv=None) -> int:
         return 2
     a.partition_set = a.partition is not None
     if a.partition is None:
-        # the 7B step's split-K partition (the other workloads choose their
-        # own unless --partition is given): 1,536 tokens, whose streaming MHA
-        # decode then runs 16-wave workgroups
-        a.partition = 1536
+        # each workload chooses its own split-K partition unless --partition
+        # is given: 2,048 tokens (no split) for the 7B step, 1,024 for the
+        # mixed step's decode part, 512 for long-context GQA, none for beams
+        a.partition = 0
 
     import torch
     import paged_kv_cache_366_amd as pkv

@@ -80,6 +80,10 @@ typedef int32_t pkv_dtype;
 #define PKV_KV_STREAM 0x10
 #define PKV_KV_CACHED 0x20
 #define PKV_KV_CACHE_BYTES (256ull << 20)
+/* pkv_paged_attention_decode_step only, OR-ed into algo: split rows are
+ * merged inside the attention launch by the last of their partitions to
+ * finish, instead of by the reduce kernel after it (see that call). */
+#define PKV_MERGE_IN_KERNEL 0x40
 
 /* Thread-local description of the last failure of this thread. */
 const char* pkv_last_error(void);
@@ -442,6 +446,47 @@ pkv_status pkv_paged_attention_decode(
     const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
     int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
     int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+    int32_t partition_tokens, int32_t algo, void* workspace, size_t workspace_bytes, void* stream);
+
+/* One decode step: append the step's new token of every sequence, then
+ * attend, in the attention kernel's launch ([nxbn] §1: only the new token's
+ * K/V is computed and appended to the cache each step, then the query
+ * attends over all of it; [nxbn] §2.2: its address comes from the block
+ * table).
+ *   new_k, new_v   device [num_seqs][num_kv_heads][head_dim] in kv_dtype
+ *                  (F32/F16/BF16), or both NULL (no append).  Row s is the
+ *                  K/V of sequence s's position context_lens[s] - 1: the
+ *                  kernel writes it to that position's slot
+ *                  (block_tables[s][p / block_size], row p % block_size) and
+ *                  attends with it; a context of 0 appends nothing.  The
+ *                  result is that of pkv_reshape_and_cache with those slots
+ *                  followed by pkv_paged_attention_decode.  I8/I4 pools
+ *                  append through quantise-on-write instead (UNSUPPORTED
+ *                  here); pass NULL rows to decode them in one launch.
+ *   Rows whose context spans several partitions are merged by the reduce
+ *   kernel in a second launch, or, with PKV_MERGE_IN_KERNEL in algo, inside
+ *   the attention launch by the last partition of the row to finish (a
+ *   device-scope counter per row and head group; no workgroup waits).  Both
+ *   merge in the same order, so the output has the same bits either way and
+ *   as pkv_paged_attention_decode's.  On MI355X the separate reduce
+ *   measured faster (the in-launch merge puts a row's whole merge, with
+ *   reads that bypass the caches, in one workgroup at the launch's tail).
+ *   workspace      device memory of pkv_decode_step_workspace_bytes(...)
+ *                  bytes, 256-byte aligned: the partial results, then one
+ *                  int32 arrival counter per (sequence, query head).  With
+ *                  PKV_MERGE_IN_KERNEL the counters must be zero before the
+ *                  first call that uses the workspace (allocate it
+ *                  zero-filled); every call leaves them zero.  Calls that
+ *                  share a workspace must not overlap.
+ * Other arguments and rules: as pkv_paged_attention_decode. */
+size_t pkv_decode_step_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                       int32_t max_context_len, int32_t partition_tokens);
+pkv_status pkv_paged_attention_decode_step(
+    void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype, const void* new_k,
+    const void* new_v, void* k_cache, void* v_cache, pkv_dtype kv_dtype, const float* k_scale,
+    const float* v_scale, const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
     int32_t partition_tokens, int32_t algo, void* workspace, size_t workspace_bytes, void* stream);
 
 /* The two halves of pkv_paged_attention_decode, for callers that schedule

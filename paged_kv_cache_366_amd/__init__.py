@@ -16,7 +16,7 @@ import numpy as np
 from ._lib import (PKV_ALGO_AUTO, PKV_ALGO_MFMA, PKV_ALGO_WAVE, PKV_BF16, PKV_ERR_DEVICE,  # noqa
                    PKV_ERR_INTERNAL, PKV_ERR_INVALID, PKV_ERR_OUT_OF_BLOCKS, PKV_ERR_UNSUPPORTED,
                    PKV_F16, PKV_F32, PKV_I4, PKV_I8, PKV_KV_CACHED, PKV_KV_STREAM,
-                   PKV_NOALLOC_SCRATCH_BYTES, PKV_OK, LIB_PATH,
+                   PKV_MERGE_IN_KERNEL, PKV_NOALLOC_SCRATCH_BYTES, PKV_OK, LIB_PATH,
                    PkvBmLatency, PkvBmStats, PkvError, PkvSwapStats, PkvOutOfBlocks, check, load)
 
 __all__ = [n for n in dir() if n.startswith("pkv_") or n.startswith("PKV_")]
@@ -416,6 +416,51 @@ def pkv_paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_l
                             workspace, stream)
     check(load().pkv_paged_attention_decode(*args))
     return ws
+
+
+def pkv_decode_step_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
+                                    max_context_len: int, partition_tokens: int) -> int:
+    return load().pkv_decode_step_workspace_bytes(num_seqs, num_q_heads, head_dim,
+                                                  max_context_len, partition_tokens)
+
+
+def pkv_paged_attention_decode_step(out, q, new_k, new_v, k_cache, v_cache, block_tables,
+                                    context_lens, max_context_len: int, scale: float,
+                                    partition_tokens: int = 0, algo: int = PKV_ALGO_AUTO,
+                                    k_scale=None, v_scale=None, workspace=None, stream=None):
+    """Append new_k / new_v [S, Hkv, D] (or None) at each sequence's last
+    position and decode in the same launch; split rows are merged by the
+    reduce kernel, or in the launch with PKV_MERGE_IN_KERNEL in algo (then
+    the workspace, allocated zero-filled here when not given, must start
+    with zero counters; calls leave them zero).  Returns the workspace."""
+    torch = _torch()
+    S, hq, d = q.shape
+    nb, hkv, bs, _ = k_cache.shape
+    if out.shape != q.shape or _pool_head_dim(k_cache) != d or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables must be [S, MB] and context_lens [S]")
+    if (new_k is None) != (new_v is None):
+        raise ValueError("new_k and new_v are both given or both None")
+    if new_k is not None:
+        coded = k_cache.dtype in (torch.int8, torch.uint8)   # refused by the library
+        for t in (new_k, new_v):
+            if t.shape != (S, hkv, d) or (t.dtype != k_cache.dtype and not coded):
+                raise ValueError("new rows must be [S, Hkv, D] in the pool's dtype")
+    need = pkv_decode_step_workspace_bytes(S, hq, d, max_context_len, partition_tokens)
+    if need and workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    check(load().pkv_paged_attention_decode_step(
+        _dev(out, "out"), _dtype_code(out), _dev(q, "q"), _dtype_code(q),
+        _dev(new_k, "new_k"), _dev(new_v, "new_v"), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), _dtype_code(k_cache), _dev(k_scale, "k_scale", torch.float32),
+        _dev(v_scale, "v_scale", torch.float32), _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32),
+        int(max_context_len), S, hq, hkv, d, bs, nb, float(scale), int(partition_tokens),
+        int(algo), C.c_void_p(workspace.data_ptr()) if workspace is not None else None, ws_len,
+        _stream(q, stream)))
+    return workspace
 
 
 def pkv_paged_attention_decode_partials(out, q, k_cache, v_cache, block_tables, context_lens,

@@ -16,6 +16,7 @@ PKV_F32, PKV_F16, PKV_BF16, PKV_I8, PKV_I4 = range(5)
 PKV_ALGO_AUTO, PKV_ALGO_WAVE, PKV_ALGO_MFMA = range(3)
 PKV_KV_STREAM, PKV_KV_CACHED = 0x10, 0x20   # K/V load policy, OR-ed into algo
 PKV_NOALLOC_SCRATCH_BYTES = 64 << 20        # scratch of the allocation-free decode
+PKV_MERGE_IN_KERNEL = 0x40                  # decode step: merge split rows in the launch
 
 _i32, _i64, _f32, _sz, _vp = C.c_int32, C.c_int64, C.c_float, C.c_size_t, C.c_void_p
 _pi32 = C.POINTER(C.c_int32)
@@ -83,6 +84,11 @@ SIGNATURES = {
     "pkv_paged_attention_decode": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp,
                                           _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                           _f32, _i32, _i32, _vp, _sz, _vp]),
+    "pkv_decode_step_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pkv_paged_attention_decode_step": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _i32,
+                                               _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
+                                               _i32, _i32, _i32, _f32, _i32, _i32, _vp, _sz,
+                                               _vp]),
     "pkv_paged_attention_decode_partials": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _i32, _vp, _vp,
                                                    _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                                                    _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp]),

@@ -44,6 +44,12 @@ WsLayout workspace_layout(int64_t rows, int64_t hq, int64_t D, int parts) {
   return w;
 }
 
+// Decode-step workspace: the split-K layout above, then one int32 arrival
+// counter per (row, query head) for the in-kernel merge.
+size_t counter_bytes(int64_t rows, int64_t hq, int parts) {
+  return parts > 1 ? align_up(static_cast<size_t>(rows * hq) * sizeof(int32_t)) : 0;
+}
+
 int out_kind_of(pkv_dtype out_dt) {
   return out_dt == PKV_F32 ? kOutF32 : out_dt == PKV_BF16 ? kOutBF16 : kOutF16;
 }
@@ -130,14 +136,17 @@ bool use_mfma(int32_t algo, pkv_dtype q_dt, int group) {
   return able && group >= 4;
 }
 
-enum class DecodePart { kAll, kMain, kReduce };
+// kStep: one launch of the main kernel that also appends the step's new K/V
+// rows (when given) and merges split rows itself (counters in the workspace).
+enum class DecodePart { kAll, kMain, kReduce, kStep };
 
 pkv_status decode_impl(DecodePart which, void* out, pkv_dtype out_dt, const void* q,
                        pkv_dtype q_dt, const void* kc, const void* vc, pkv_dtype kv_dt,
                        const float* ks, const float* vs, const int32_t* tables, int32_t mb,
                        const int32_t* lens, int32_t max_ctx, int32_t S, int32_t hq, int32_t hkv,
                        int32_t D, int32_t bs, int32_t nb, float scale, int32_t part_tokens,
-                       int32_t algo, void* ws, size_t ws_bytes, void* stream) {
+                       int32_t algo, void* ws, size_t ws_bytes, void* stream,
+                       const void* new_k = nullptr, const void* new_v = nullptr) {
   const char* who = "paged_attention_decode";
   pkv_status st = check_common(who, out, out_dt, q, q_dt, kc, vc, kv_dt, ks, vs, tables, mb, lens,
                                max_ctx, S, S, hq, hkv, D, bs, nb, scale);
@@ -146,19 +155,31 @@ pkv_status decode_impl(DecodePart which, void* out, pkv_dtype out_dt, const void
     return fail(PKV_ERR_INVALID, "%s: partition_tokens %d must be 0 or a multiple of 16", who,
                 part_tokens);
   const int32_t policy = algo & (PKV_KV_STREAM | PKV_KV_CACHED);
-  algo &= ~(PKV_KV_STREAM | PKV_KV_CACHED);
+  const bool merge_in_kernel = (algo & PKV_MERGE_IN_KERNEL) != 0;
+  algo &= ~(PKV_KV_STREAM | PKV_KV_CACHED | PKV_MERGE_IN_KERNEL);
   if (algo < PKV_ALGO_AUTO || algo > PKV_ALGO_MFMA || policy == (PKV_KV_STREAM | PKV_KV_CACHED))
     return fail(PKV_ERR_INVALID, "%s: unknown algo %d", who, algo | policy);
+  if (merge_in_kernel && which != DecodePart::kStep)
+    return fail(PKV_ERR_INVALID, "%s: PKV_MERGE_IN_KERNEL applies to the decode step only", who);
   const int group = hq / hkv;
   if (algo == PKV_ALGO_MFMA && !use_mfma(algo, q_dt, group))
     return fail(PKV_ERR_UNSUPPORTED, "%s: MFMA path needs 16-bit q and a group of at most 16",
                 who);
+  if (which == DecodePart::kStep && (new_k != nullptr) != (new_v != nullptr))
+    return fail(PKV_ERR_INVALID, "%s: new_k and new_v are both given or both NULL", who);
+  if (new_k != nullptr && has_scales(kv_dt))
+    return fail(PKV_ERR_UNSUPPORTED,
+                "%s: appending rows to %s KV takes quantise-on-write (pkv_reshape_and_cache_%s)",
+                who, dtype_name(kv_dt), kv_dt == PKV_I8 ? "int8" : "int4");
+  if (new_k != nullptr && (!aligned(new_k, 16) || !aligned(new_v, 16)))
+    return fail(PKV_ERR_INVALID, "%s: new_k and new_v must be 16-byte aligned", who);
   if (S == 0) return PKV_OK;
   const int parts = num_partitions(max_ctx, part_tokens);
   const WsLayout w = workspace_layout(S, hq, D, parts);
-  if (w.total > 0 && (!ws || ws_bytes < w.total || !aligned(ws, kAlign)))
+  const size_t need = w.total + (which == DecodePart::kStep ? counter_bytes(S, hq, parts) : 0);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, kAlign)))
     return fail(PKV_ERR_INVALID, "%s: workspace needs %zu bytes, 256-byte aligned (got %zu)", who,
-                w.total, ws_bytes);
+                need, ws_bytes);
   if (deep_validation() && which != DecodePart::kReduce) {
     st = deep_check_tables(who, tables, mb, lens, max_ctx, S, nb, bs, stream);
     if (st) return st;
@@ -193,13 +214,22 @@ pkv_status decode_impl(DecodePart which, void* out, pkv_dtype out_dt, const void
   const double pool_bytes = 2.0 * nb * hkv * bs * static_cast<double>(row_bytes(kv_dt, D));
   a.stream_kv = policy == PKV_KV_STREAM ||
                 (policy == 0 && pool_bytes > static_cast<double>(PKV_KV_CACHE_BYTES));
+  if (which == DecodePart::kStep) {
+    a.new_k = new_k;
+    a.new_v = new_v;
+    a.counters = (merge_in_kernel && parts > 1)
+                     ? reinterpret_cast<int32_t*>(static_cast<char*>(ws) + w.total)
+                     : nullptr;
+  }
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (which != DecodePart::kReduce) {
     st = use_mfma(algo, q_dt, group) ? launch_decode_mfma(a, q_dt, kv_dt, D, group, hs)
                                      : launch_decode_wave(a, q_dt, kv_dt, D, group, hs);
     if (st) return st;
   }
-  if (which != DecodePart::kMain && parts > 1) return launch_reduce(a, D, hs);
+  const bool reduce = which == DecodePart::kAll || which == DecodePart::kReduce ||
+                      (which == DecodePart::kStep && a.counters == nullptr);
+  if (reduce && parts > 1) return launch_reduce(a, D, hs);
   return PKV_OK;
 }
 
@@ -249,6 +279,14 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
       .total;
 }
 
+size_t pkv_decode_step_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                       int32_t max_context_len, int32_t partition_tokens) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
+  const int parts = num_partitions(max_context_len, partition_tokens);
+  return workspace_layout(num_seqs, num_q_heads, head_dim, parts).total +
+         counter_bytes(num_seqs, num_q_heads, parts);
+}
+
 size_t pkv_prefill_workspace_bytes(int32_t num_query_tokens, int32_t num_q_heads,
                                    int32_t head_dim, int32_t max_context_len,
                                    int32_t partition_tokens) {
@@ -274,6 +312,23 @@ pkv_status pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void
                        max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                        num_blocks, scale, partition_tokens, algo, workspace, workspace_bytes,
                        stream);
+  })
+}
+
+pkv_status pkv_paged_attention_decode_step(
+    void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype, const void* new_k,
+    const void* new_v, void* k_cache, void* v_cache, pkv_dtype kv_dtype, const float* k_scale,
+    const float* v_scale, const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+    int32_t partition_tokens, int32_t algo, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  PKV_GUARD({
+    return decode_impl(DecodePart::kStep, out, out_dtype, q, q_dtype, k_cache, v_cache, kv_dtype,
+                       k_scale, v_scale, block_tables, max_blocks_per_seq, context_lens,
+                       max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                       num_blocks, scale, partition_tokens, algo, workspace, workspace_bytes,
+                       stream, new_k, new_v);
   })
 }
 

@@ -31,6 +31,11 @@ struct AttnArgs {
   int out_kind;
   float scale_log2;          // scale * log2(e): scores are kept in the log2 domain
   bool stream_kv;            // decode K/V loads carry the non-temporal hint
+  // Decode step extras (NULL when unused):
+  const void* new_k;         // [S][Hkv][D] the step's K row of each sequence, written to
+  const void* new_v;         //   position lens[s] - 1 and attended from these buffers
+  int32_t* counters;         // [rows][Hq] arrivals per (row, first head of the group);
+                             //   non-NULL: the last partition to finish merges the row
 };
 
 // Which sequence a query row belongs to.  Decode: row s is sequence s.
@@ -144,6 +149,95 @@ __device__ __forceinline__ int64_t part_slot(const AttnArgs& a, int64_t row, int
   return (row * a.num_parts + part) * a.hq + h;
 }
 
+// Canonical merge of the split-K partial states of one (row, head): with
+// M = max_p m_p and f_p = 2^(m_p - M), L = sum_p l_p f_p and
+// O[d] = sum_p o_p[d] f_p, each sum taken in partition order p = 0, 1, ...
+// with one fused multiply-add per term, and the row is O / L (0 when L = 0).
+// Every merger (the reduce kernel, the last workgroup of a row) runs these
+// same steps, so all give the same bits for a fixed partition size.
+struct PartMerge {
+  float ms;   // M, or 0 when no partition saw a key
+  float L;
+};
+// Loads of partial states.  Coherent: device-scope atomic loads, which read
+// past the caches of this XCD (another workgroup of the same launch wrote
+// them); otherwise plain loads (a later launch).  The value is the same.
+template <bool Coherent>
+__device__ __forceinline__ float load_part(const float* p) {
+  if constexpr (Coherent)
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    return *p;
+}
+template <bool Coherent = false>
+__device__ __forceinline__ PartMerge merge_ml(const AttnArgs& a, int64_t row, int h, int nparts) {
+  const float* ml = a.part_ml + part_slot(a, row, h, 0) * 2;
+  const int64_t st = 2 * static_cast<int64_t>(a.hq);   // floats between partitions' pairs
+  float M = kNegInf;
+  for (int p = 0; p < nparts; ++p) M = fmaxf(M, load_part<Coherent>(ml + p * st));
+  PartMerge r;
+  r.ms = (M == kNegInf) ? 0.f : M;
+  r.L = 0.f;
+  for (int p = 0; p < nparts; ++p)
+    r.L = fmaf(load_part<Coherent>(ml + p * st + 1),
+               fast_exp2(load_part<Coherent>(ml + p * st) - r.ms), r.L);
+  return r;
+}
+template <bool Coherent = false>
+__device__ __forceinline__ float merge_elem(const AttnArgs& a, int64_t row, int h, int nparts,
+                                            const PartMerge& pm, int d, int D) {
+  const float* ml = a.part_ml + part_slot(a, row, h, 0) * 2;
+  const float* po = a.part_o + part_slot(a, row, h, 0) * D + d;
+  const int64_t st = 2 * static_cast<int64_t>(a.hq);
+  const int64_t so = static_cast<int64_t>(a.hq) * D;   // floats between partitions' rows
+  float O = 0.f;
+#pragma unroll 4
+  for (int p = 0; p < nparts; ++p)
+    O = fmaf(load_part<Coherent>(po + p * so),
+             fast_exp2(load_part<Coherent>(ml + p * st) - pm.ms), O);
+  return pm.L > 0.f ? O / pm.L : 0.f;
+}
+
+// Last-arriver merge inside a decode kernel.  Each workgroup of a row whose
+// context spans several partitions has written its partial state with
+// device-scope atomic stores (finish_rows, when counters are set), which
+// write through the caches of its XCD; the `stride` threads of the
+// workgroup that wrote it (tid = 0 .. stride - 1) call this.  Each waits
+// until its own stores are complete, `sync` (a barrier of those threads)
+// puts every store before thread 0's device-scope count of the workgroup on
+// the row's counter, and `bcast` hands thread 0's verdict to the others.
+// The workgroup that brings the count to nparts resets the counter to 0 and
+// merges the row's partitions (the canonical order above) for its heads
+// [hbase, hbase + nheads), reading them with device-scope atomic loads that
+// issue only once the count has returned.  Only the partial states cross
+// workgroups, and only through such loads and stores, so no cache-wide
+// write-back or invalidation is needed.  No workgroup waits for another.
+// The counters must be zero when the launch starts; every launch leaves
+// them zero.
+template <typename Sync, typename Bcast>
+__device__ __forceinline__ void merge_if_last(const AttnArgs& a, int row, int hbase, int nheads,
+                                              int nparts, int D, int tid, int stride, Sync sync,
+                                              Bcast bcast) {
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's partial-state stores are complete
+  sync();
+  int last = 0;
+  if (tid == 0) {
+    int32_t* ctr = a.counters + static_cast<int64_t>(row) * a.hq + hbase;
+    const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = old == nparts - 1;
+    if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (!bcast(last)) return;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  for (int idx = tid; idx < nheads * D; idx += stride) {
+    const int g = idx / D;
+    const int d = idx % D;
+    const PartMerge pm = merge_ml<true>(a, row, hbase + g, nparts);
+    store_out(a, (static_cast<int64_t>(row) * a.hq + hbase + g) * D + d,
+              merge_elem<true>(a, row, hbase + g, nparts, pm, d, D));
+  }
+}
+
 // Final merge of a workgroup: NW wavefronts each left, per head row g, a
 // softmax state (max m, sum l) and an unnormalised output row o[D] in LDS.
 // Rescales them to the common max and either writes the normalised output
@@ -172,6 +266,15 @@ __device__ __forceinline__ void finish_rows(const AttnArgs& a, const float (&sm_
     const int64_t orow = static_cast<int64_t>(row) * a.hq + hbase + g;
     if (nparts <= 1) {
       store_out(a, orow * D + d, L > 0.f ? O / L : 0.f);
+    } else if (a.counters != nullptr) {
+      // merged in this launch by another workgroup: write through
+      const int64_t pi = part_slot(a, row, hbase + g, part);
+      __hip_atomic_store(a.part_o + pi * D + d, O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (d == 0) {
+        __hip_atomic_store(a.part_ml + pi * 2, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.part_ml + pi * 2 + 1, L, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
     } else {
       const int64_t pi = part_slot(a, row, hbase + g, part);
       a.part_o[pi * D + d] = O;

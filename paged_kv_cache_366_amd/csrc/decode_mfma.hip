@@ -31,11 +31,17 @@
 //   (j < D / 64) and product kk takes the half kk % 2 of load kk / 2; Q^T
 //   takes the same elements.  Half as many key loads as one per product,
 //   each covering half of every row it touches (about 6% faster).  Int8
-//   codes, sign-flipped to u = k + 128, enter both products as u (exact in
-//   bf16 and f16) after one byte convert each: scores carry 128 x (sum of
-//   the head's q), taken out with the score scale, and the value
-//   accumulators 128 x (sum of the weights), accumulated by one more product
-//   per tile against a constant operand and subtracted at the end.
+//   products run in f16 whatever the q type: a code k, flipped to the byte
+//   k + 128 and put under the high byte 0x64 by a byte permute, is the f16
+//   value 1152 + k, and one packed f16 add per pair leaves k exactly (about
+//   1.25 instructions per code, against 1.5 for a byte convert per code and
+//   a pack into bf16, whose 7-bit mantissa cannot hold a code).  q enters
+//   as f16 scaled by a power of two per head (its largest element to
+//   [2^14, 2^15)), undone in the score scale.  The weights enter as f16
+//   hi + lo pairs: the tile's value scale joins their exponent (log2 of it
+//   added to the scores, so the running maximum covers it and a row's
+//   largest weight sits at 2^7, far from f16's limits), and the sum of
+//   weights takes each one times 1 / scale.
 //   4-bit keys: the contraction order over head_dim is free, so lane
 //   (t, kg) reads elements kg*D/4 .. +D/4-1 of key row t in one load (16
 //   bytes at head_dim 128) and Q^T takes the same elements; 4-bit values
@@ -57,6 +63,8 @@
 //   of a second MFMA per product; decode is HBM-bound, so it is free.
 // The workgroup's wavefronts take the partition's tiles round-robin, two
 // tiles in flight each, and merge through LDS at the end.
+#include <type_traits>
+
 #include "attention_common.h"
 #include "mfma_common.h"
 
@@ -99,6 +107,10 @@ __global__ __launch_bounds__(64 * mfma_waves<KT>()) void decode_mfma_kernel(Attn
   constexpr int ROW = D * KT::bits / 8;       // bytes of one token row
   constexpr int TILE = 16 * ROW;
   using M = Mx<QT>;
+  // int8 codes run both products in f16 whatever the q type: a code byte
+  // under the high byte 0x64 (or 0xE4) is an exact f16 value, so one byte
+  // permute forms two operands (bf16's 7-bit mantissa cannot hold 8 bits)
+  using MK = typename std::conditional<KT::bits == 8, Mx<F16>, Mx<QT>>::type;
 
   const int wave = wave_uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -123,21 +135,53 @@ __global__ __launch_bounds__(64 * mfma_waves<KT>()) void decode_mfma_kernel(Attn
   // kg*D/4 + 8kk .. +7, the elements that lane's key load holds).
   u32x4 qop[NK];
   // Offsets left in the operands and removed from the sums later: bf16
-  // 4-bit codes, and int8 codes, which enter as u = k + 128 (0..255, exact
-  // in bf16 and f16) straight from a byte convert.
-  constexpr bool kOffset = (kInt4 && M::kOffset4) || kInt8;
-  constexpr float kOffset8 = 128.f;
+  // 4-bit codes, and int8 codes (below).
+  constexpr bool kOffset = kInt4 && M::kOffset4;
   float kcorr = 0.f;                                // the offsets' share of every score
-  {
+  float qinv = 1.f;                                 // int8: 2^-e, undoing q's f16 scaling
+  if constexpr (kInt8) {
+    // q as f16 operands: each head's row scaled by 2^e so that its largest
+    // |element| lies in [2^14, 2^15) (exact: bf16 and f16 values have at
+    // most 11 significant bits; only elements 2^28 or more below the row's
+    // largest fall to f16 subnormals).  Scores are divided by 2^e again
+    // through the score scale.
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q);
+    const bool live = r16 < group;
+    const int64_t qrow = (static_cast<int64_t>(row) * a.hq + hbase + (live ? r16 : 0)) * D;
+    float qf[NK][8];
+    float amax = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      const int e0 = 64 * (kk / 2) + 16 * kg + 8 * (kk % 2);   // the lane's 16-code key load
+      u32x4 v = *reinterpret_cast<const u32x4*>(qp + qrow + e0);
+      v = live ? v : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        qf[kk][2 * i] = M::lo(dw(v, i));
+        qf[kk][2 * i + 1] = M::hi(dw(v, i));
+        amax = fmaxf(amax, fmaxf(fabsf(qf[kk][2 * i]), fabsf(qf[kk][2 * i + 1])));
+      }
+    }
+    amax = max_xor32(max_xor16(amax));   // the head's four lane groups
+    const int e = amax > 0.f ? min(max(15 - __builtin_amdgcn_frexp_expf(amax), -126), 100) : 0;
+    qinv = __builtin_amdgcn_ldexpf(1.f, -e);
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = MK::pack(__builtin_amdgcn_ldexpf(qf[kk][2 * i], e),
+                        __builtin_amdgcn_ldexpf(qf[kk][2 * i + 1], e));
+      qop[kk] = u32x4{w[0], w[1], w[2], w[3]};
+    }
+  } else {
     const uint16_t* qp = static_cast<const uint16_t*>(a.q);
     const bool live = r16 < group;
     const int64_t qrow = (static_cast<int64_t>(row) * a.hq + hbase + (live ? r16 : 0)) * D;
     float qlo = 0.f, qhi = 0.f;   // q in low / high halves of the operand pairs
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
-      const int e0 = kInt4     ? kg * (D / 4) + 8 * kk
-                     : kWideK8 ? 64 * (kk / 2) + 16 * kg + 8 * (kk % 2)
-                               : 32 * kk + 8 * kg;
+      const int e0 = kInt4 ? kg * (D / 4) + 8 * kk : 32 * kk + 8 * kg;
       u32x4 v = *reinterpret_cast<const u32x4*>(qp + qrow + e0);
       v = live ? v : u32x4{0u, 0u, 0u, 0u};
       if constexpr (kInt4) {
@@ -155,19 +199,12 @@ __global__ __launch_bounds__(64 * mfma_waves<KT>()) void decode_mfma_kernel(Attn
         }
       } else {
         qop[kk] = v;
-        if constexpr (kInt8) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            qlo += M::lo(dw(v, i));
-            qhi += M::hi(dw(v, i));
-          }
-        }
       }
     }
     if constexpr (kOffset) {
       qlo = sum_xor32(sum_xor16(qlo));
       qhi = sum_xor32(sum_xor16(qhi));
-      kcorr = kInt8 ? kOffset8 * (qlo + qhi) : M::kOffsetLo4 * qlo + M::kOffsetHi4 * qhi;
+      kcorr = M::kOffsetLo4 * qlo + M::kOffsetHi4 * qhi;
     }
   }
 
@@ -181,7 +218,7 @@ __global__ __launch_bounds__(64 * mfma_waves<KT>()) void decode_mfma_kernel(Attn
 
   float m = kNegInf, l = 0.f;
   f32x4 acc[NV];
-  f32x4 wacc = {0.f, 0.f, 0.f, 0.f};   // int8, and bf16 4-bit: the offsets' share of acc
+  f32x4 wacc = {0.f, 0.f, 0.f, 0.f};   // bf16 4-bit: the offsets' share of acc
 #pragma unroll
   for (int j = 0; j < NV; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -191,31 +228,58 @@ __global__ __launch_bounds__(64 * mfma_waves<KT>()) void decode_mfma_kernel(Attn
   const int koff = r16 * ROW + (kInt4 || kWideK8 ? kg * KB : 8 * kg * KT::bytes);
   constexpr int KSTEP = kWideK8 ? 64 : 32 * KT::bytes;   // bytes between a lane's K loads
   const int voff = (4 * kg) * ROW + r16 * VB;                           // + e * ROW
+  // A decode step that appends (new_k set, 16-bit K/V): position ctx - 1 is
+  // the step's new token, whose K and V rows come from new_k and new_v; the
+  // lanes that hold parts of that row read them there and, once the tile is
+  // processed, write them to the token's slot in the cache.
+  constexpr bool kCanAppend = KT::bits == 16;
+  const bool append = kCanAppend && a.new_k != nullptr;
+  const int64_t new_row = (static_cast<int64_t>(seq) * a.hkv + kvh) * ROW;
 
   for (int k = 0; k < nbw; k += kUnroll) {
     if (k > 0 && (k & 63) == 0) tc.fetch(trow, b0, wave, kWaves, k, bmax, a.bs_shift);
     u32x4 kr[kUnroll][NKL], vr[kUnroll][4];
     int phys[kUnroll];
+    int nrow[kUnroll];          // row of the step's new token in the tile, or -1
+    int64_t tofs[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       int p = -1;
+      nrow[u] = -1;
+      tofs[u] = 0;
       if (k + u < nbw) {
         p = tc.get(k + u);
         if (p < 0 || p >= a.num_blocks) p = -1;
       }
       phys[u] = p;
       if (p >= 0) {
-        const int64_t toff = tile_index(a, p, kvh, b0 + wave + kWaves * (k + u)) * TILE;
+        const int tt = b0 + wave + kWaves * (k + u);
+        const int64_t toff = tile_index(a, p, kvh, tt) * TILE;
+        tofs[u] = toff;
+        if (append) {
+          const int r = ctx - 1 - tt * 16;   // wave-uniform
+          nrow[u] = (r >= 0 && r < 16) ? r : -1;
+        }
         // Value loads cover whole rows; with NTV (the streaming load
         // policy) they carry the non-temporal hint, so tiles read once pass
         // through the caches without evicting what is reused.  Key loads
         // take parts of each row over several instructions and stay cached
         // (streaming them measured slower for every storage type).
+        const bool knew = kCanAppend && nrow[u] == r16;
 #pragma unroll
-        for (int kk = 0; kk < NKL; ++kk)
-          kr[u][kk] = load_kv_bytes<KB, false>(kc + toff + koff + kk * KSTEP);
+        for (int kk = 0; kk < NKL; ++kk) {
+          const uint8_t* kp = knew ? static_cast<const uint8_t*>(a.new_k) + new_row +
+                                         (koff - r16 * ROW) + kk * KSTEP
+                                   : kc + toff + koff + kk * KSTEP;
+          kr[u][kk] = load_kv_bytes<KB, false>(kp);
+        }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vr[u][e] = load_kv_bytes<VB, NTV>(vc + toff + voff + e * ROW);
+        for (int e = 0; e < 4; ++e) {
+          const bool vnew = kCanAppend && nrow[u] == 4 * kg + e;
+          const uint8_t* vp = vnew ? static_cast<const uint8_t*>(a.new_v) + new_row + r16 * VB
+                                   : vc + toff + voff + e * ROW;
+          vr[u][e] = load_kv_bytes<VB, NTV>(vp);
+        }
       }
     }
 #pragma unroll
@@ -239,26 +303,33 @@ __global__ __launch_bounds__(64 * mfma_waves<KT>()) void decode_mfma_kernel(Attn
           kop = u32x4{M::fix4(magic_pair(M::kMagic4, lo, 0)), M::fix4(magic_pair(M::kMagic4, lo, 1)),
                       M::fix4(magic_pair(M::kMagic4, hi, 0)), M::fix4(magic_pair(M::kMagic4, hi, 1))};
         } else if constexpr (kInt8) {
-          const u32x4& kw = kr[u][kWideK8 ? kk / 2 : kk];
-          const int h2 = kWideK8 ? 2 * (kk % 2) : 0;
+          // exact f16 codes, two per permute and add (i8_pair)
+          const u32x4& kw = kr[u][kk / 2];
+          const int h2 = 2 * (kk % 2);
           const uint32_t w0 = dw(kw, h2) ^ 0x80808080u, w1 = dw(kw, h2 + 1) ^ 0x80808080u;
-          kop = u32x4{M::int_pair(u8_value(w0, 0), u8_value(w0, 1)),
-                      M::int_pair(u8_value(w0, 2), u8_value(w0, 3)),
-                      M::int_pair(u8_value(w1, 0), u8_value(w1, 1)),
-                      M::int_pair(u8_value(w1, 2), u8_value(w1, 3))};
+          kop = u32x4{i8_pair(w0, 0), i8_pair(w0, 1), i8_pair(w1, 0), i8_pair(w1, 1)};
         } else {
           kop = kr[u][kk];
         }
-        s = M::k32(kop, qop[kk], s);
+        s = MK::k32(kop, qop[kk], s);
       }
-      const float sc = kscale * a.scale_log2;
-      const float nc = -kcorr * sc;   // 0 unless the offset is in the scores
+      // int8: the tile's value scale enters the weights through the exponent
+      // (lv = log2 of the scale), so the running maximum covers it and the
+      // largest weight of a row sits at 2^7, well inside f16's range; the
+      // sum l takes each weight times 1 / scale.  A tile whose scale is 0
+      // (or below the smallest normal float) holds zero values: its weights
+      // count in l and its products get zero weights.
+      const bool vok = !kInt8 || vscale >= 1.17549435e-38f;
+      const float lv = (kInt8 && vok) ? __log2f(vscale) : 0.f;
+      const float rv = (kInt8 && vok) ? __builtin_amdgcn_rcpf(vscale) : 1.f;
+      const float sc = kscale * a.scale_log2 * qinv;
+      const float nc = -kcorr * sc + lv;   // the offsets' share (4-bit) and log2 of the value scale (int8)
       float sv[4];
       float tmax = kNegInf;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bool valid = (p >= 0) && (tpos + 4 * kg + i < t1);
-        sv[i] = valid ? (kOffset ? fmaf(s[i], sc, nc) : s[i] * sc) : kNegInf;
+        sv[i] = valid ? ((kOffset || kInt8) ? fmaf(s[i], sc, nc) : s[i] * sc) : kNegInf;
         tmax = fmaxf(tmax, sv[i]);
       }
       tmax = max_xor32(max_xor16(tmax));
@@ -274,29 +345,39 @@ __global__ __launch_bounds__(64 * mfma_waves<KT>()) void decode_mfma_kernel(Attn
       }
       const float ms = (m == kNegInf) ? 0.f : m;
       float pv[4];
+      if constexpr (kInt8) {
+        const float ms7 = ms - 7.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pw = fast_exp2(sv[i] - ms);
-        l += pw;
-        pv[i] = pw * vscale;
+        for (int i = 0; i < 4; ++i) {
+          const float pw = fast_exp2(sv[i] - ms7);
+          l = fmaf(pw, rv, l);
+          pv[i] = vok ? pw : 0.f;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pw = fast_exp2(sv[i] - ms);
+          l += pw;
+          pv[i] = pw * vscale;
+        }
       }
       // ---- P^T operand as hi + lo pairs
-      const uint32_t h01 = M::pack(pv[0], pv[1]);
-      const uint32_t h23 = M::pack(pv[2], pv[3]);
+      const uint32_t h01 = MK::pack(pv[0], pv[1]);
+      const uint32_t h23 = MK::pack(pv[2], pv[3]);
       const u32x2 phi = {h01, h23};
-      const u32x2 plo = {M::pack(pv[0] - M::lo(h01), pv[1] - M::hi(h01)),
-                         M::pack(pv[2] - M::lo(h23), pv[3] - M::hi(h23))};
+      const u32x2 plo = {MK::pack(pv[0] - MK::lo(h01), pv[1] - MK::hi(h01)),
+                         MK::pack(pv[2] - MK::lo(h23), pv[3] - MK::hi(h23))};
       // K = 32 of one product: the lane's 4 keys with the hi weights, then
       // the same 4 keys with the lo weights (the A operand repeats them)
       const u32x4 pcat = {phi.x, phi.y, plo.x, plo.y};
       // ---- out^T += V^T . P^T.  Value rows past the context (only in the
       // partly filled last block) may hold anything: they are zeroed (4-bit
-      // codes always form finite operands and meet zero weights, so they
-      // need no masking).
+      // and int8 codes always form finite operands and meet zero weights, so
+      // they need no masking).
       u32x4 vrow[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) vrow[e] = vr[u][e];
-      if (!kInt4 && !(p >= 0 && tpos + 16 <= t1)) {
+      if (!kInt4 && !kInt8 && !(p >= 0 && tpos + 16 <= t1)) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const bool valid = (p >= 0) && (tpos + 4 * kg + e < t1);
@@ -336,26 +417,48 @@ __global__ __launch_bounds__(64 * mfma_waves<KT>()) void decode_mfma_kernel(Attn
           wacc = M::k32(u32x4{o, o, o, o}, pcat, wacc);
         }
       } else if constexpr (kInt8) {
-        // sign-flipped codes u = k + 128, one byte convert each; the
-        // offset's share, 128 x the weights, is collected in wacc
+        // rows 4kg..4kg+3 hold NV codes each (NV / 4 dwords): a flip per
+        // row dword, one permute interleaving two rows byte by byte, then
+        // each operand pair (row 0's element j low, row 1's high) exact in
+        // f16 by one permute and one packed add (i8_pair)
+        constexpr int NW = NV / 4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vrow[e] ^= u32x4{0x80808080u, 0x80808080u, 0x80808080u, 0x80808080u};
+        for (int w = 0; w < NW; ++w) {
+          const uint32_t r0 = dw(vrow[0], w) ^ 0x80808080u, r1 = dw(vrow[1], w) ^ 0x80808080u;
+          const uint32_t r2 = dw(vrow[2], w) ^ 0x80808080u, r3 = dw(vrow[3], w) ^ 0x80808080u;
 #pragma unroll
-        for (int j = 0; j < NV; ++j) {
-          const uint32_t v01 = M::int_pair(u8_value(dw(vrow[0], j >> 2), j & 3),
-                                           u8_value(dw(vrow[1], j >> 2), j & 3));
-          const uint32_t v23 = M::int_pair(u8_value(dw(vrow[2], j >> 2), j & 3),
-                                           u8_value(dw(vrow[3], j >> 2), j & 3));
-          acc[j] = M::k32(u32x4{v01, v23, v01, v23}, pcat, acc[j]);
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t sel = h ? 0x07030602u : 0x05010400u;
+            const uint32_t x01 = __builtin_amdgcn_perm(r1, r0, sel);
+            const uint32_t x23 = __builtin_amdgcn_perm(r3, r2, sel);
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+              const int j = 4 * w + 2 * h + pp;
+              const uint32_t v01 = i8_pair(x01, pp);
+              const uint32_t v23 = i8_pair(x23, pp);
+              acc[j] = MK::k32(u32x4{v01, v23, v01, v23}, pcat, acc[j]);
+            }
+          }
         }
-        const uint32_t o = M::int_pair(kOffset8, kOffset8);
-        wacc = M::k32(u32x4{o, o, o, o}, pcat, wacc);
       } else {
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
           const uint32_t v01 = pair_of(vrow[0], vrow[1], j);
           const uint32_t v23 = pair_of(vrow[2], vrow[3], j);
           acc[j] = M::k32(u32x4{v01, v23, v01, v23}, pcat, acc[j]);
+        }
+      }
+      if constexpr (kCanAppend) {
+        if (nrow[u] >= 0) {   // the new token's rows to their slot (vector stores)
+          uint8_t* kw = static_cast<uint8_t*>(const_cast<void*>(a.kc)) + tofs[u] + koff;
+          uint8_t* vw = static_cast<uint8_t*>(const_cast<void*>(a.vc)) + tofs[u] + voff;
+          if (nrow[u] == r16) {
+#pragma unroll
+            for (int kk = 0; kk < NKL; ++kk) store_bytes<KB>(kw + kk * KSTEP, kr[u][kk]);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (nrow[u] == 4 * kg + e) store_bytes<VB>(vw + e * ROW, vr[u][e]);
         }
       }
     }
@@ -383,6 +486,17 @@ __global__ __launch_bounds__(64 * mfma_waves<KT>()) void decode_mfma_kernel(Attn
   __syncthreads();
   finish_rows<kWaves, 16, D>(a, sm_o, sm_m, sm_l, group, row, hbase, part, nparts,
                              threadIdx.x, blockDim.x);
+  // With counters, the last partition of a split row to finish merges it.
+  if (a.counters != nullptr && nparts > 1) {
+    __shared__ int sm_last;
+    merge_if_last(a, row, hbase, group, nparts, D, threadIdx.x, blockDim.x,
+                  [] { __syncthreads(); },
+                  [&](int v) {
+                    if (threadIdx.x == 0) sm_last = v;
+                    __syncthreads();
+                    return sm_last;
+                  });
+  }
 }
 
 template <typename QT, typename KT, bool NTV>

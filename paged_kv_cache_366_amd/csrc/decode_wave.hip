@@ -270,18 +270,40 @@ __global__ __launch_bounds__(64 * NW) void decode_wave_kernel(AttnArgs a) {
     }
   };
 
+  // A decode step that appends (new_k set, 16-bit or fp32 K/V): position
+  // ctx - 1 is the step's new token, whose K and V rows come from new_k and
+  // new_v; the lanes that hold that row read it there and, after the block
+  // is processed, write it to its slot in the cache.
+  constexpr bool kCanAppend = KT::bits >= 16;
+  const bool append = kCanAppend && a.new_k != nullptr;
+  const int64_t new_off = (static_cast<int64_t>(seq) * a.hkv + kvh) * D * KT::bytes + c * CB;
+
   // Loads of one block's K and V tiles; false for a table entry outside the
-  // pool, which is skipped as if masked.
-  auto load_block = [&](int k, u32x4 (&kr)[NL], u32x4 (&vr)[NL], float& ksc, float& vsc) {
+  // pool, which is skipped as if masked.  `toff` receives the tile's byte
+  // offset and `nrow` the row of the step's new token in it (or -1).
+  auto load_block = [&](int k, u32x4 (&kr)[NL], u32x4 (&vr)[NL], float& ksc, float& vsc,
+                        int64_t& toff, int& nrow) {
     if (k > 0 && (k & 63) == 0) tc.fetch(trow, b0, wave, kWaves, k, bmax, a.bs_shift);
     const int p = tc.get(k);
+    nrow = -1;
     if (p < 0 || p >= a.num_blocks) return false;
-    const int64_t toff = tile_index(a, p, kvh, b0 + wave + kWaves * k) * TILE;
+    const int tt = b0 + wave + kWaves * k;
+    toff = tile_index(a, p, kvh, tt) * TILE;
+    if (append) {
+      const int r = ctx - 1 - tt * 16;   // wave-uniform
+      nrow = (r >= 0 && r < 16) ? r : -1;
+    }
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
       if constexpr (CB == 16) {
-        kr[j] = load_kv<u32x4, NT>(kbase + toff + j * 64 * CB);
-        vr[j] = load_kv<u32x4, NT>(vbase + toff + j * 64 * CB);
+        const uint8_t* kp = kbase + toff + j * 64 * CB;
+        const uint8_t* vp = vbase + toff + j * 64 * CB;
+        if (kCanAppend && nrow >= 0 && j * TPL + u == nrow) {
+          kp = static_cast<const uint8_t*>(a.new_k) + new_off;
+          vp = static_cast<const uint8_t*>(a.new_v) + new_off;
+        }
+        kr[j] = load_kv<u32x4, NT>(kp);
+        vr[j] = load_kv<u32x4, NT>(vp);
       } else {
         const u32x2 k2 = load_kv<u32x2, NT>(kbase + toff + j * 64 * CB);
         const u32x2 v2 = load_kv<u32x2, NT>(vbase + toff + j * 64 * CB);
@@ -319,8 +341,23 @@ __global__ __launch_bounds__(64 * NW) void decode_wave_kernel(AttnArgs a) {
   for (int k = 0; k < kall; ++k) {
     u32x4 kr[NL], vr[NL];
     float ksc = 1.f, vsc = 1.f;
-    const bool ok = load_block(k, kr, vr, ksc, vsc);
+    int64_t toff = 0;
+    int nrow = -1;
+    const bool ok = load_block(k, kr, vr, ksc, vsc, toff, nrow);
     step(k, ok, kr, vr, ksc, vsc);
+    if constexpr (kCanAppend) {
+      if (nrow >= 0) {   // the new token's rows to their slot (vector stores)
+        uint8_t* kw = static_cast<uint8_t*>(const_cast<void*>(a.kc)) + lane * CB + toff;
+        uint8_t* vw = static_cast<uint8_t*>(const_cast<void*>(a.vc)) + lane * CB + toff;
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+          if (j * TPL + u == nrow) {
+            *reinterpret_cast<u32x4*>(kw + j * 64 * CB) = kr[j];
+            *reinterpret_cast<u32x4*>(vw + j * 64 * CB) = vr[j];
+          }
+        }
+      }
+    }
   }
 
   // Merge the token-row groups of the wavefront (lanes c, c+C, c+2C, ...).
@@ -364,6 +401,10 @@ __global__ __launch_bounds__(64 * NW) void decode_wave_kernel(AttnArgs a) {
   if (arrived != kWaves - 1) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   finish_rows<kWaves, G, D>(a, sm_o, sm_m, sm_l, G, row, hbase, part, nparts, lane, 64);
+  // With counters, the last partition of a split row to finish merges it.
+  if (a.counters != nullptr && nparts > 1)
+    merge_if_last(a, row, hbase, G, nparts, D, lane, 64, [] {},
+                  [](int v) { return __shfl(v, 0); });
 }
 
 // Most query heads one workgroup serves.  Each head holds its q slice and an

@@ -129,6 +129,21 @@ __device__ __forceinline__ u32x4 load_kv_bytes(const uint8_t* p) {
   return r;
 }
 
+// Stores of the low 2, 4, 8 or 16 bytes of a u32x4 (vector stores).
+template <int B>
+__device__ __forceinline__ void store_bytes(uint8_t* p, const u32x4& v) {
+  if constexpr (B == 16) {
+    *reinterpret_cast<u32x4*>(p) = v;
+  } else if constexpr (B == 8) {
+    *reinterpret_cast<u32x2*>(p) = u32x2{v.x, v.y};
+  } else if constexpr (B == 4) {
+    *reinterpret_cast<uint32_t*>(p) = v.x;
+  } else {
+    static_assert(B == 2, "store width");
+    *reinterpret_cast<uint16_t*>(p) = static_cast<uint16_t>(v.x);
+  }
+}
+
 __device__ __forceinline__ uint32_t dw(const u32x4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
@@ -162,6 +177,19 @@ __device__ __forceinline__ uint32_t nib_hi(uint32_t w, uint32_t flip) {
 // two 16-bit halves of one operand dword.
 __device__ __forceinline__ uint32_t magic_pair(uint32_t magic, uint32_t x, int p) {
   return __builtin_amdgcn_perm(magic, x, p ? 0x06030402u : 0x06010400u);
+}
+
+// int8 codes as exact f16 operands.  A code k XORed with 0x80 is the byte
+// u = k + 128; under the high byte 0x64 a byte u is the f16 value 1024 + u,
+// so one byte permute forms a pair (1024 + u0, 1024 + u1) and one packed f16
+// add of (-1152, -1152) leaves (k0, k1) exactly (integers below 2048 are f16
+// values).  i8_pair takes bytes 2p and 2p + 1 of a dword of flipped codes.
+constexpr uint32_t kI8Magic = 0x64646464u;
+__device__ __forceinline__ uint32_t i8_pair(uint32_t flipped, int p) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const uint32_t x = magic_pair(kI8Magic, flipped, p);
+  const f16x2 v = __builtin_bit_cast(f16x2, x) + f16x2{-1152.f16, -1152.f16};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Lazy rescaling of an online softmax: the running reference max moves only

@@ -185,21 +185,29 @@ def test_int8_kv_every_q_dtype_and_head_dim(qdt, D):
 
 
 def test_int8_mfma_biased_q_and_value_outliers():
-    """int8 codes enter the matrix-core products with an offset that is taken
-    out after the sums; a query with a large common component (every element
-    shifted by +4) and value tiles whose scale is set by one large outlier
-    (small codes elsewhere) over one 9,000-token partition are the worst case
-    of that cancellation.  Error against the oracle stays within the bar."""
+    """A query with a large common component (every element shifted by +4),
+    value tiles whose scale is set by one large outlier (small codes
+    elsewhere) and key tiles with outliers, over one 9,000-token partition:
+    the case where offsets kept in the products would cancel worst, and
+    where a tile's value scale differs most from its neighbours' (the int8
+    matrix-core path folds it into the weights' exponent).  Error against
+    the oracle stays within the bar."""
     c = W.decode_case(610, 2, 16, 2, 128, lens=[9000, 4100], dtype="bf16")
     rng = np.random.default_rng(611)
     c.q = W.round_bf16(c.q + np.float32(4.0))
-    # one outlier of 200 in every third owned value tile
+    # one outlier of 200 in every third owned value tile, and of 60 in every
+    # fifth key tile
     for s, n in enumerate(c.context_lens):
         for j in range(0, W.blocks_for(int(n)), 3):
             b = int(c.block_tables[s, j])
             rows = min(16, int(n) - 16 * j)
             h = int(rng.integers(0, 2))
             c.v_cache[b, h, int(rng.integers(0, rows)), int(rng.integers(0, 128))] = 200.0
+        for j in range(1, W.blocks_for(int(n)), 5):
+            b = int(c.block_tables[s, j])
+            rows = min(16, int(n) - 16 * j)
+            h = int(rng.integers(0, 2))
+            c.k_cache[b, h, int(rng.integers(0, rows)), int(rng.integers(0, 128))] = 60.0
     c.k_i8, c.k_scale = W.int8_pool(c.k_cache, c.block_tables, c.context_lens)
     c.v_i8, c.v_scale = W.int8_pool(c.v_cache, c.block_tables, c.context_lens)
     d = DevCase(c, int8=True)

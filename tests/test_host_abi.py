@@ -209,7 +209,8 @@ def test_header_constants_match_the_binding():
     text = open(HEADER).read()
     defines = dict(re.findall(r"#define\s+(PKV_[A-Z0-9_]+)\s+(0x[0-9a-fA-F]+|\d+)\b", text))
     for name in ("PKV_F32", "PKV_F16", "PKV_BF16", "PKV_I8", "PKV_I4", "PKV_ALGO_AUTO",
-                 "PKV_ALGO_WAVE", "PKV_ALGO_MFMA", "PKV_KV_STREAM", "PKV_KV_CACHED"):
+                 "PKV_ALGO_WAVE", "PKV_ALGO_MFMA", "PKV_KV_STREAM", "PKV_KV_CACHED",
+                 "PKV_MERGE_IN_KERNEL"):
         assert int(defines[name], 0) == getattr(pkv, name), name
     flags = pkv.PKV_KV_STREAM | pkv.PKV_KV_CACHED
     assert flags & (pkv.PKV_ALGO_AUTO | pkv.PKV_ALGO_WAVE | pkv.PKV_ALGO_MFMA) == 0
@@ -252,3 +253,24 @@ def test_noalloc_decode_refuses_oversize_and_accepts_empty_without_a_gpu():
                                                 PKV_BF16, None, None, None, 8, None, 128, 0, 8, 2,
                                                 128, 16, 10, 0.1, 0, 0, None)
     assert st == PKV_OK
+
+
+def test_in_kernel_merge_flag_only_for_the_decode_step():
+    """PKV_MERGE_IN_KERNEL is accepted by the decode step and refused by the
+    other decode calls, on the host (empty batches: no device call)."""
+    import paged_kv_cache_366_amd as pkv
+    from paged_kv_cache_366_amd._lib import PKV_BF16, PKV_ERR_INVALID, PKV_OK
+    lib = pkv.load()
+    flag = pkv.PKV_MERGE_IN_KERNEL
+    st = lib.pkv_paged_attention_decode(None, PKV_BF16, None, PKV_BF16, None, None, PKV_BF16,
+                                        None, None, None, 8, None, 128, 0, 8, 2, 128, 16, 10,
+                                        0.1, 256, flag, None, 0, None)
+    assert st == PKV_ERR_INVALID
+    st = lib.pkv_paged_attention_decode_step(None, PKV_BF16, None, PKV_BF16, None, None, None,
+                                             None, PKV_BF16, None, None, None, 8, None, 128, 0, 8,
+                                             2, 128, 16, 10, 0.1, 256, flag, None, 0, None)
+    assert st == PKV_OK
+    # the step's workspace holds the partial results, then the counters
+    assert (pkv.pkv_decode_step_workspace_bytes(4, 8, 128, 1024, 256)
+            > pkv.pkv_decode_workspace_bytes(4, 8, 128, 1024, 256))
+    assert pkv.pkv_decode_step_workspace_bytes(4, 8, 128, 1024, 0) == 0
