@@ -26,10 +26,11 @@
 // LDS, so product j sees element m*D/16 + j; at the end the lane holds 32
 // contiguous output elements of its row.
 //
-// Loads: the next step's global loads are issued right after the barrier
-// and land in registers while the wavefronts compute; no branch guards them
-// (a block outside the pool reads a fixed in-pool address), so the wait
-// before the LDS store covers only that step's loads.
+// Loads: the global loads of the steps two ahead are issued right after
+// the barrier and land in registers while the wavefronts compute (two steps
+// in flight measured 6% faster than one; three or four, slower); no branch
+// guards them (a block outside the pool reads a fixed in-pool address), so
+// the wait before the LDS store covers only that step's loads.
 //
 // Causality: a key t is used by row i when t <= P_i; rows past the chunk are
 // idle, and a wavefront skips tiles past its last row's position; tiles
@@ -44,9 +45,12 @@
 //
 // Measured on MI355X (mixed step, four 512-row chunks): the loads, LDS
 // stores and barriers alone take about 60% of the kernel's time, at about
-// 6.6 TB/s of K/V delivered to the compute units, close to what streaming
-// reads reach; deeper prefetch, wider workgroups and wider steps move the
-// total by a few percent at most.
+// 6.6 TB/s of K/V delivered to the compute units; counters put the VALU at
+// 43% and the matrix cores at 17% of their issue capacity, with on average
+// half of the wave slots occupied as short row tiles finish first.  Wider
+// workgroups, 32 rows per wavefront, wider steps, key partitions for the
+// long row tiles and operand pairs formed without permutes each measured
+// slower or within a few percent.
 #include "attention_common.h"
 #include "mfma_common.h"
 
@@ -59,7 +63,7 @@ namespace {
 constexpr int kPrefillWaves = PKV_PREFILL_WAVES;   // wavefronts (16 rows each) per workgroup
 constexpr int kPrefillThreads = 64 * kPrefillWaves;
 #ifndef PKV_PREFILL_DEPTH
-#define PKV_PREFILL_DEPTH 1
+#define PKV_PREFILL_DEPTH 2
 #endif
 #ifndef PKV_PREFILL_RTILES
 #define PKV_PREFILL_RTILES 1
