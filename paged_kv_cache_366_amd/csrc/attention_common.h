@@ -150,9 +150,10 @@ __device__ __forceinline__ int64_t part_slot(const AttnArgs& a, int64_t row, int
 }
 
 // Canonical merge of the split-K partial states of one (row, head): with
-// M = max_p m_p and f_p = 2^(m_p - M), L = sum_p l_p f_p and
-// O[d] = sum_p o_p[d] f_p, each sum taken in partition order p = 0, 1, ...
-// with one fused multiply-add per term, and the row is O / L (0 when L = 0).
+// M = max_p m_p and f_p = 2^(m_p - M), L = sum_p l_p f_p taken in partition
+// order p = 0, 1, ..., and O[d] = (sum over the first ceil(P / 2)
+// partitions) + (sum over the rest), each half in partition order, with one
+// fused multiply-add per term; the row is O / L (0 when L = 0).
 // Every merger (the reduce kernel, the last workgroup of a row) runs these
 // same steps, so all give the same bits for a fixed partition size.
 struct PartMerge {
@@ -190,12 +191,15 @@ __device__ __forceinline__ float merge_elem(const AttnArgs& a, int64_t row, int 
   const float* po = a.part_o + part_slot(a, row, h, 0) * D + d;
   const int64_t st = 2 * static_cast<int64_t>(a.hq);
   const int64_t so = static_cast<int64_t>(a.hq) * D;   // floats between partitions' rows
-  float O = 0.f;
-#pragma unroll 4
-  for (int p = 0; p < nparts; ++p)
-    O = fmaf(load_part<Coherent>(po + p * so),
-             fast_exp2(load_part<Coherent>(ml + p * st) - pm.ms), O);
-  return pm.L > 0.f ? O / pm.L : 0.f;
+  // two halves of the partitions, each summed in order, then added
+  const int half = (nparts + 1) >> 1;
+  float O[2] = {0.f, 0.f};
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+    for (int p = g * half; p < min(nparts, (g + 1) * half); ++p)
+      O[g] = fmaf(load_part<Coherent>(po + p * so),
+                  fast_exp2(load_part<Coherent>(ml + p * st) - pm.ms), O[g]);
+  return pm.L > 0.f ? (O[0] + O[1]) / pm.L : 0.f;
 }
 
 // Last-arriver merge inside a decode kernel.  Each workgroup of a row whose

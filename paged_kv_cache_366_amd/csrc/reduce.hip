@@ -10,29 +10,33 @@
 namespace pkv {
 namespace {
 
-// One workgroup of head_dim threads per (row, head), head fastest.  The
+// One workgroup of 2 x head_dim threads per (row, head), head fastest.  The
 // partitions' (max, sum) pairs are loaded once, in parallel, into LDS, where
 // each partition's rescale factor f_p = 2^(m_p - M) is computed once; then
-// every thread forms L and its element's O in the canonical partition order
-// (merge_ml, merge_elem: the same steps, hence the same bits, as the
-// last-arriver merge inside the decode kernels), its loads of the
-// partitions' outputs independent of each other.
+// thread (g, d) sums element d over half g of the partitions in order, and
+// the two halves are added: the canonical order of merge_ml / merge_elem,
+// so the same bits as the last-arriver merge inside the decode kernels.
+// Each thread's loads of the partitions' outputs are independent.
 constexpr int kMaxCachedParts = 1024;   // partitions whose (max, sum, factor) sit in LDS
 
-__global__ __launch_bounds__(128) void reduce_kernel(AttnArgs a, int D) {
+__global__ __launch_bounds__(256) void reduce_kernel(AttnArgs a, int D) {
   const int h = blockIdx.x % a.hq;
   const int row = blockIdx.x / a.hq;
   int seq, ctx;
   row_context(a, row, seq, ctx);
   const int nparts = (ctx + a.part_tokens - 1) / a.part_tokens;
   if (nparts <= 1) return;  // written by the main kernel
-  const int d = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int nt = 2 * D;
+  const int g = tid / D;
+  const int d = tid % D;
   const float* ml = a.part_ml + part_slot(a, row, h, 0) * 2;
   const int64_t st = 2 * static_cast<int64_t>(a.hq);   // floats between partitions' pairs
   __shared__ float s_m[kMaxCachedParts], s_l[kMaxCachedParts];
-  __shared__ float s_red[2];
+  __shared__ float s_red[4];
+  __shared__ float s_o[128];
   float mx = kNegInf;
-  for (int p = d; p < nparts; p += D) {
+  for (int p = tid; p < nparts; p += nt) {
     const float mp = ml[p * st], lp = ml[p * st + 1];
     if (p < kMaxCachedParts) {
       s_m[p] = mp;
@@ -41,32 +45,39 @@ __global__ __launch_bounds__(128) void reduce_kernel(AttnArgs a, int D) {
     mx = fmaxf(mx, mp);
   }
   mx = group_max<64>(mx);
-  if ((d & 63) == 0) s_red[d >> 6] = mx;
+  if ((tid & 63) == 0) s_red[tid >> 6] = mx;
   __syncthreads();
   float M = s_red[0];
-  if (D > 64) M = fmaxf(M, s_red[1]);
+  for (int w = 1; w < nt / 64; ++w) M = fmaxf(M, s_red[w]);
   const float ms = (M == kNegInf) ? 0.f : M;
-  for (int p = d; p < min(nparts, kMaxCachedParts); p += D) s_m[p] = fast_exp2(s_m[p] - ms);
+  for (int p = tid; p < min(nparts, kMaxCachedParts); p += nt) s_m[p] = fast_exp2(s_m[p] - ms);
   __syncthreads();
-  // L and O in partition order; f_p from LDS (or recomputed past the cache)
+  // f_p from LDS (or recomputed past the cache)
   auto factor = [&](int p) {
     return p < kMaxCachedParts ? s_m[p] : fast_exp2(ml[p * st] - ms);
   };
   auto lsum = [&](int p) { return p < kMaxCachedParts ? s_l[p] : ml[p * st + 1]; };
-  float L = 0.f;
-  for (int p = 0; p < nparts; ++p) L = fmaf(lsum(p), factor(p), L);
+  const int half = (nparts + 1) >> 1;
   const float* po = a.part_o + part_slot(a, row, h, 0) * D + d;
   const int64_t so = static_cast<int64_t>(a.hq) * D;   // floats between partitions' rows
   float O = 0.f;
+  const int p_end = min(nparts, (g + 1) * half);
 #pragma unroll 8
-  for (int p = 0; p < nparts; ++p) O = fmaf(po[p * so], factor(p), O);
-  store_out(a, (static_cast<int64_t>(row) * a.hq + h) * D + d, L > 0.f ? O / L : 0.f);
+  for (int p = g * half; p < p_end; ++p) O = fmaf(po[p * so], factor(p), O);
+  if (g == 1) s_o[d] = O;
+  __syncthreads();
+  if (g == 0) {
+    float L = 0.f;
+    for (int p = 0; p < nparts; ++p) L = fmaf(lsum(p), factor(p), L);
+    store_out(a, (static_cast<int64_t>(row) * a.hq + h) * D + d,
+              L > 0.f ? (O + s_o[d]) / L : 0.f);
+  }
 }
 
 }  // namespace
 
 pkv_status launch_reduce(const AttnArgs& a, int D, hipStream_t st) {
-  hipLaunchKernelGGL(reduce_kernel, dim3(a.hq * a.num_rows), dim3(D), 0, st, a, D);
+  hipLaunchKernelGGL(reduce_kernel, dim3(a.hq * a.num_rows), dim3(2 * D), 0, st, a, D);
   PKV_LAUNCH_CHECK("partition reduce");
   return PKV_OK;
 }
