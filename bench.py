@@ -73,7 +73,19 @@ PAGE_ALLOC_P99_BAR_US = 1000.0   # cnnetsun.cn section 4.2: page allocation P99 
 # known-size copy kernel shows in the same run, WRITE_SIZE as read), with the
 # profile that records the counts.  Valid only while the kernel sources hash
 # to the measured value; a changed kernel reports null.
-TRAFFIC = {}
+# HBM bytes per step of the dominant kernel(s), from rocprofv3 counter runs:
+# FETCH_SIZE scaled by 1 / 0.500040 (a 1 GiB torch.bitwise_not in the same
+# process reads as 524,330 KiB) plus WRITE_SIZE (exact for the same copy).
+# Reported only while the kernel sources hash to the value they were taken on.
+_SHA = "3cdc8de583e409dccab92677284d1e30b27d151b"
+TRAFFIC = {
+    "decode7b": {"bytes_per_launch": 1120438917, "sources_sha1": _SHA, "partition_tokens": 2048,
+                 "profile": "profiles/decode_wave_7b_bf16_p2048_step_kernel_trace.md"},
+    "gqa-bf16": {"bytes_per_launch": 1591541385, "sources_sha1": _SHA, "partition_tokens": 512,
+                 "profile": "profiles/decode_mfma_gqa_long_bf16_p512_kernel_trace.md"},
+    "gqa-int8": {"bytes_per_launch": 868236428, "sources_sha1": _SHA, "partition_tokens": 512,
+                 "profile": "profiles/decode_mfma_gqa_long_int8_p512_kernel_trace.md"},
+}
 KERNEL_SOURCES = ("decode_wave.hip", "decode_mfma.hip", "attention_common.h", "device_common.h",
                   "mfma_common.h")
 
@@ -86,11 +98,14 @@ def kernel_sources_sha1() -> str:
     return h.hexdigest()
 
 
-def traffic_of(name: str):
-    """(bytes per launch or None, where the figure comes from)."""
+def traffic_of(name: str, part: int):
+    """(bytes per step of the roofline's kernels or None, where the figure
+    comes from)."""
     t = TRAFFIC.get(name)
     if t is None:
         return None, "not measured for this workload"
+    if t["partition_tokens"] != part:
+        return None, f"measured at {t['partition_tokens']}-token partitions, not {part}"
     if t["sources_sha1"] != kernel_sources_sha1():
         return None, (f"stale: kernel sources changed since the counter run in {t['profile']}")
     return t["bytes_per_launch"], (f"rocprofv3 --pmc FETCH_SIZE (scaled by the calibration copy) "
@@ -378,6 +393,9 @@ def bench_decode7b(a, torch, pkv, algo):
 
     # the same step as three launches (reshape_and_cache, split-K decode with
     # 1,536-token partitions, reduce), for comparison
+    if a.no_compare:
+        return finish_decode7b(a, torch, pkv, wl, kc, vc, ws, got, ms_per_step, main_ms, part,
+                               None)
     sep_part = 1536
     ws3 = torch.empty(max(pkv.pkv_decode_workspace_bytes(wl.S, wl.H, wl.D, max_ctx, sep_part), 1),
                       dtype=torch.uint8, device=dev)
@@ -398,12 +416,20 @@ def bench_decode7b(a, torch, pkv, algo):
             ev[3].record(stream)
 
     ms3, (rc_ms, main3_ms, red_ms) = run_timed(torch, step3, a.steps, a.warmup, 3)
-    sep_diff = float((out3 - out).abs().max())
+    three = {
+        "ms_per_step": ms3, "partition_tokens": sep_part,
+        "kernel_ms": {"reshape_and_cache": stats_ms(rc_ms), "decode_main": stats_ms(main3_ms),
+                      "reduce": stats_ms(red_ms)},
+        "max_abs_diff_vs_one_launch": float((out3 - out).abs().max())}
+    del ws3
+    return finish_decode7b(a, torch, pkv, wl, kc, vc, ws, got, ms_per_step, main_ms, part, three)
 
+
+def finish_decode7b(a, torch, pkv, wl, kc, vc, ws, got, ms_per_step, main_ms, part, three):
     main_avg = float(np.mean(main_ms))
     step_bytes = wl.step_bytes()
     achieved = step_bytes / (main_avg * 1e-3) / 1e9
-    traffic, tsrc = traffic_of("decode7b") if wl.bs == BLOCK else (None, "not measured")
+    traffic, tsrc = traffic_of("decode7b", part) if wl.bs == BLOCK else (None, "not measured")
     result = base_result(a, METRIC, step_bytes / (ms_per_step * 1e-3) / 1e9, "GB/s", ms_per_step,
                          "bf16", {
         "workload": "7B-shape paged decode, bf16 KV and q, fp32 accumulate: 64 sequences, "
@@ -421,18 +447,14 @@ def bench_decode7b(a, torch, pkv, algo):
                   "new_rows_written": wl.S * wl.H * wl.D * 2 * 2},
         "roofline": roofline("decode_wave_kernel (append + attention, one launch per step)",
                              "hbm", achieved, HBM_PEAK_GBS, "GB/s", traffic, tsrc),
-        "three_launch_step": {
-            "ms_per_step": ms3, "partition_tokens": sep_part,
-            "kernel_ms": {"reshape_and_cache": stats_ms(rc_ms), "decode_main": stats_ms(main3_ms),
-                          "reduce": stats_ms(red_ms)},
-            "max_abs_diff_vs_one_launch": sep_diff},
+        "three_launch_step": three,
         "host_block_manager_us": wl.host_bm,
         "page_allocation_latency": allocation_latency(pkv, wl),
         "block_manager": {k: v for k, v in pkv.pkv_bm_stats_get(wl.bm).items()
                           if k in ("num_blocks", "used_blocks", "logical_blocks", "waste_slots")},
         "cpu_baseline": None,
     })
-    del kc, vc, ws, ws3
+    del kc, vc, ws
     free_device(torch)
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle on the same batch", file=sys.stderr, flush=True)
@@ -597,7 +619,7 @@ def bench_gqa(a, torch, pkv, algo, kv: str, c=None, sample_seqs: int = 6):
     kv_text = {"int8": "int8 KV (block encoder output) with per-block fp32 scales",
                "int4": "4-bit KV (block encoder output) with per-block fp32 scales",
                "bf16": "bf16 KV"}[kv]
-    traffic, tsrc = traffic_of(f"gqa-{kv}")
+    traffic, tsrc = traffic_of(f"gqa-{kv}", part)
     result = base_result(a, METRIC, step_bytes / (ms_per_step * 1e-3) / 1e9, "GB/s", ms_per_step,
                          "bf16" if kv == "bf16" else f"{kv}-kv/bf16", {
         "workload": f"long-context GQA decode, {kv_text}: "
@@ -749,7 +771,7 @@ def bench_mixed(a, torch, pkv, algo):
                               V[:P + 1, h_ // G], ms.scale)
                 err_p = max(err_p, float(np.abs(got_p[qsl[j] + i, h_] - ref).max()))
                 pre_flops += 4 * D * (P + 1)
-    traffic, tsrc = traffic_of("mixed-decode")
+    traffic, tsrc = traffic_of("mixed-decode", part)
     result = base_result(a, METRIC, step_bytes / (ms_per_step * 1e-3) / 1e9, "GB/s", ms_per_step,
                          "bf16", {
         "workload": "continuous-batching mixed step, bf16: 48 decode sequences (contexts "
@@ -1294,6 +1316,8 @@ def main(argv=None) -> int:
                     help="KV block size of the decode7b workload (16 is the headline line)")
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="7B step: skip the three-launch comparison (for profiling one kernel)")
     ap.add_argument("--oracle-seconds", type=float, default=8.0,
                     help="least CPU time of the headline's oracle baseline (whole-batch passes)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
