@@ -144,6 +144,21 @@ __device__ __forceinline__ void store_bytes(uint8_t* p, const u32x4& v) {
   }
 }
 
+// gfx950 LDS transpose read of 16-bit elements (8 bytes per lane).  Within
+// each group of 16 lanes, lane j receives element j % 4 of the 4-element
+// runs that lanes j / 4, 4 + j / 4, 8 + j / 4 and 12 + j / 4 of the group
+// point at (in that order).  So when lane 4k + q points at row k of a
+// row-major tile, columns c + 4q .. c + 4q + 3, lane j receives column c + j
+// of rows 0 .. 3: a 4 x 16 block transposed.  `p` is an 8-byte aligned
+// address in LDS.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
+  typedef short s16x4_t __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+  const s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)((__attribute__((address_space(3))) const uint8_t*)p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
 __device__ __forceinline__ uint32_t dw(const u32x4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }

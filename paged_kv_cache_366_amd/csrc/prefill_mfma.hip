@@ -11,29 +11,30 @@
 // Layout.  A workgroup of 4 wavefronts owns 64 consecutive rows of one
 // sequence's chunk for one query head; wavefront w takes rows 16w..16w+15.
 // Every row of the workgroup reads the same keys, so K and V go through LDS
-// in steps of two 16-row tiles (double-buffered, rows padded by 16 bytes so
-// the 16 key rows a wavefront reads at one column fall in different banks)
-// and all four wavefronts read them there.  Per tile and wavefront:
-//   S^T [16 keys x 16 rows] = K [16 x D] . Q^T [D x 16]      (D/32 MFMA 16x16x32)
+// in steps of two 16-key tiles (double-buffered, rows padded by 16 bytes)
+// and all four wavefronts read them there.  Per step and wavefront:
+//   S^T [16 keys x 16 rows] = K [16 x D] . Q^T [D x 16], per tile
+//       (D/32 MFMA 16x16x32; lane (r16, kg) holds keys 4kg..4kg+3 of row r16)
 //   online softmax per row (column), lazily rescaled: the row maximum across
 //   the four lane groups is taken only when some score outgrows the running
-//   one by the slack; the row's weights stay in the lanes that hold them,
-//   which is exactly the B operand of the next product;
-//   O^T [D x 16 rows] += V^T [D x 16 keys] . P^T [16 keys x 16 rows]
-//       (D/16 MFMA 16x16x32, weights as a 16-bit hi + lo pair: K = 32 is the
-//       lane's 4 keys with the hi weights, then the same keys with the lo)
-// Lane (m, g) reads the D/16 elements m*D/16.. of key rows 4g..4g+3 from
-// LDS, so product j sees element m*D/16 + j; at the end the lane holds 32
-// contiguous output elements of its row.
+//   one by the slack; the lane's 8 weights (4 keys of each tile) are exactly
+//   its B operand of the value product, so they never move between lanes;
+//   O^T [D x 16 rows] += V^T [D x 32 keys] . P^T [32 keys x 16 rows]
+//       (D/16 output blocks, each one MFMA 16x16x32 with the weights' bf16
+//       (or f16) hi parts and one with the lo parts: an fp32-accurate sum)
+// V^T comes straight out of LDS with gfx950's transpose read: two 8-byte
+// reads per output block give the lane its 8 keys at one output element,
+// in the key order of its weights, with no register permutes.  Lane
+// (r16, kg) ends with elements 16j + 4kg .. +3 of its row for each block j.
 //
-// Loads: the global loads of the steps two ahead are issued right after
-// the barrier and land in registers while the wavefronts compute (two steps
-// in flight measured 6% faster than one; three or four, slower); no branch
+// Loads: the global loads of the next step are issued right after the
+// barrier and land in registers while the wavefronts compute; no branch
 // guards them (a block outside the pool reads a fixed in-pool address), so
-// the wait before the LDS store covers only that step's loads.
+// the wait before the LDS store covers only that step's loads.  Steps whose
+// rows all exist are stored as they are; otherwise missing rows become zeros.
 //
 // Causality: a key t is used by row i when t <= P_i; rows past the chunk are
-// idle, and a wavefront skips tiles past its last row's position; tiles
+// idle, and a wavefront skips steps past its last row's position; steps
 // wholly at or below the wavefront's first row position skip the test.  Key
 // rows past the workgroup's last position (the unwritten tail of the last
 // block) are stored to LDS as zeros, so no garbage enters the products; a
@@ -41,16 +42,17 @@
 //
 // Grid order: the query head is the fastest index, so (with a head count
 // that is a multiple of 8) all tiles of one (sequence, head) go to the same
-// XCD and share the K/V lines it caches in L2.
+// XCD and share the K/V lines it caches in L2.  Sequences go longest
+// context first and, within one, the last row tiles (the most keys) first:
+// all of a compute unit's workgroups are resident together and older waves
+// issue first, so the heaviest tiles lead instead of finishing alone.
 //
-// Measured on MI355X (mixed step, four 512-row chunks): the loads, LDS
-// stores and barriers alone take about 60% of the kernel's time, at about
-// 6.6 TB/s of K/V delivered to the compute units; counters put the VALU at
-// 43% and the matrix cores at 17% of their issue capacity, with on average
-// half of the wave slots occupied as short row tiles finish first.  Wider
-// workgroups, 32 rows per wavefront, wider steps, key partitions for the
-// long row tiles and operand pairs formed without permutes each measured
-// slower or within a few percent.
+// Measured on MI355X (mixed step, four 512-row chunks over 0..1536 cached
+// tokens): the transposed value reads took the kernel from 140 to 109 us,
+// the order by context length and one register stage (128 VGPRs, four
+// waves per SIMD) to 95 us.  Counters then show the matrix cores 24% busy,
+// the VALU about 40%, waves waiting on dependencies a third of their time
+// and LDS bank conflicts in about 16% of the cycles.
 #include "attention_common.h"
 #include "mfma_common.h"
 
@@ -63,7 +65,7 @@ namespace {
 constexpr int kPrefillWaves = PKV_PREFILL_WAVES;   // wavefronts (16 rows each) per workgroup
 constexpr int kPrefillThreads = 64 * kPrefillWaves;
 #ifndef PKV_PREFILL_DEPTH
-#define PKV_PREFILL_DEPTH 2
+#define PKV_PREFILL_DEPTH 1
 #endif
 #ifndef PKV_PREFILL_RTILES
 #define PKV_PREFILL_RTILES 1
@@ -72,16 +74,20 @@ constexpr int kPrefillThreads = 64 * kPrefillWaves;
 #define PKV_PREFILL_GROUP 2
 #endif
 // Tuning constants (the defaults measured best on MI355X):
-constexpr int kDepth = PKV_PREFILL_DEPTH;     // steps whose global loads are in flight
+constexpr int kDepth = PKV_PREFILL_DEPTH;     // steps whose global loads are in flight (one measured best)
 constexpr int kGroup = PKV_PREFILL_GROUP;     // 16-key tiles per LDS step (one barrier)
 constexpr int kRowTiles = PKV_PREFILL_RTILES; // 16-row tiles per wavefront
 constexpr int kTileRows = kPrefillWaves * 16 * kRowTiles;   // query rows per workgroup
 
+#ifdef PKV_PREFILL_WPE
+#define PKV_PREFILL_ATTR __attribute__((amdgpu_waves_per_eu(PKV_PREFILL_WPE)))
+#else
+#define PKV_PREFILL_ATTR
+#endif
 template <typename T, int D, int P, int R, int G0, bool STREAM>
-__global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs a, int max_tiles) {
+__global__ __launch_bounds__(kPrefillThreads) PKV_PREFILL_ATTR void prefill_mfma_kernel(AttnArgs a, int max_tiles) {
   constexpr int NK = D / 32;              // QK products per block and row tile
   constexpr int NV = D / 16;              // PV products per block and row tile
-  constexpr int VB = NV * 2;              // bytes of a lane's V chunk
   constexpr int ROWB = D * 2;             // bytes of a K/V row
   constexpr int LROW = ROWB + 16;         // LDS row stride
   constexpr int CHUNKS = ROWB / 16;       // 16-byte chunks per row
@@ -91,6 +97,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
   constexpr int G = (G0 * 2 * TILE_CHUNKS >= NT) ? G0 : NT / (2 * TILE_CHUNKS);
   constexpr int LPS = G * 2 * TILE_CHUNKS / NT;   // K+V chunks per thread per step
   static_assert(G * 2 * TILE_CHUNKS == NT * LPS, "a step's K and V split evenly over the threads");
+  static_assert(G == 2, "a step is two 16-key tiles: the K = 32 of one value product");
   constexpr int WROWS = 16 * R;           // rows per wavefront
   constexpr int TROWS = kPrefillWaves * WROWS;
   using M = Mx<T>;
@@ -103,7 +110,27 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
   const int part = rest % a.num_parts;   // key partition (split-K)
   const int rest2 = rest / a.num_parts;
   const int tile = max_tiles - 1 - rest2 % max_tiles;
-  const int seq = rest2 / max_tiles;
+  // Sequences are taken in order of context length, longest first (ties in
+  // index order), so the row tiles with the most keys start first and their
+  // waves are the oldest on their compute units (older waves issue first).
+  // The rank is computed here by the workgroup, for up to kPrefillThreads
+  // sequences; a larger batch keeps index order.
+  int seq = rest2 / max_tiles;
+  if (a.num_seqs <= kPrefillThreads) {
+    __shared__ int s_seq;
+    const int t = threadIdx.x;
+    if (t < a.num_seqs) {
+      const int lt = a.lens[t];
+      int rank = 0;
+      for (int u = 0; u < a.num_seqs; ++u) {
+        const int lu = a.lens[u];
+        rank += (lu > lt || (lu == lt && u < t)) ? 1 : 0;
+      }
+      if (rank == seq) s_seq = t;
+    }
+    __syncthreads();
+    seq = wave_uniform(s_seq);
+  }
   const int qs = a.qsl[seq];
   const int qlen = a.qsl[seq + 1] - qs;
   if (tile * TROWS >= qlen) return;
@@ -172,6 +199,10 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
   // past the table) reads the same bytes of the pool's first tile instead;
   // the store turns it, and every row past the workgroup's last key, into
   // zeros.
+  // Chunk i of a thread is chunk NT * i + threadIdx.x of the step; with
+  // NT and 2 TILE_CHUNKS powers of two, its block (gi) is the same for the
+  // whole workgroup and known at compile time.
+  static_assert(NT % (2 * TILE_CHUNKS) == 0 || (2 * TILE_CHUNKS) % NT == 0, "chunk split");
   auto gload = [&](int st, u32x4 (&rg)[LPS], bool (&ok)[G]) {
     int64_t toff[G];
 #pragma unroll
@@ -183,30 +214,38 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
     }
 #pragma unroll
     for (int i = 0; i < LPS; ++i) {
-      const int c = threadIdx.x + NT * i;
-      const int g = c / (2 * TILE_CHUNKS);
-      const int rem = c % (2 * TILE_CHUNKS);
-      int64_t off = toff[0];
-#pragma unroll
-      for (int k = 1; k < G; ++k) off = g == k ? toff[k] : off;
-      rg[i] = load_kv<u32x4, STREAM>((rem < TILE_CHUNKS ? kc : vc) + off + (rem % TILE_CHUNKS) * 16);
+      constexpr int kStep = 2 * TILE_CHUNKS;
+      const int gi = (NT * i) / kStep;
+      const int rem = (NT * i) % kStep + static_cast<int>(threadIdx.x);
+      rg[i] = load_kv<u32x4, STREAM>((rem < TILE_CHUNKS ? kc : vc) + toff[gi] +
+                                     (rem % TILE_CHUNKS) * 16);
     }
   };
   auto sstore = [&](int buf, const u32x4 (&rg)[LPS], int st, const bool (&ok)[G]) {
-#pragma unroll
-    for (int i = 0; i < LPS; ++i) {
-      const int c = threadIdx.x + NT * i;
-      const int g = c / (2 * TILE_CHUNKS);
-      const int rem = c % (2 * TILE_CHUNKS);
-      const int which = rem / TILE_CHUNKS;
+    auto dst_of = [&](int i) {
+      constexpr int kStep = 2 * TILE_CHUNKS;
+      const int gi = (NT * i) / kStep;
+      const int rem = (NT * i) % kStep + static_cast<int>(threadIdx.x);
       const int rc = rem % TILE_CHUNKS;
-      const int row = rc / CHUNKS;
-      bool okg = ok[0];
+      return (rem / TILE_CHUNKS == 0 ? sk[buf] : sv[buf]) + (gi * 16 + rc / CHUNKS) * LROW +
+             (rc % CHUNKS) * 16;
+    };
+    // Every row of both blocks in the pool and at or below the workgroup's
+    // last key (wave-uniform): plain stores; otherwise zeros where not.
+    if (ok[0] && ok[1] && (b_begin + st * G + G) * 16 - 1 <= tlast) {
 #pragma unroll
-      for (int k = 1; k < G; ++k) okg = g == k ? ok[k] : okg;
-      const bool use = okg && (b_begin + st * G + g) * 16 + row <= tlast;
-      uint8_t* dst = (which == 0 ? sk[buf] : sv[buf]) + (g * 16 + row) * LROW + (rc % CHUNKS) * 16;
-      *reinterpret_cast<u32x4*>(dst) = use ? rg[i] : u32x4{0u, 0u, 0u, 0u};
+      for (int i = 0; i < LPS; ++i) *reinterpret_cast<u32x4*>(dst_of(i)) = rg[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < LPS; ++i) {
+        constexpr int kStep = 2 * TILE_CHUNKS;
+        const int gi = (NT * i) / kStep;
+        const int rem = (NT * i) % kStep + static_cast<int>(threadIdx.x);
+        const int row = (rem % TILE_CHUNKS) / CHUNKS;
+        const bool use = ok[gi] && (b_begin + st * G + gi) * 16 + row <= tlast;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(dst_of(i)) = use ? rg[i] : z;
+      }
     }
   };
 
@@ -220,47 +259,70 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
     for (int j = 0; j < NV; ++j) acc[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // One block: its tile from LDS buffer `buf`, for each of the wave's row
-  // tiles.  The K operands and the V operand are read and built once and
-  // serve every row tile.
-  // `ok`: the block is in the pool (and in this workgroup's range); it sits
-  // in slot g of the LDS step.
-  auto compute = [&](int b, int buf, bool ok, int g) {
-    const int kb = b * 16;
-    if (!ok || kb > wlast) return;   // wave-uniform
-    const int lrow0 = g * 16;   // the block's first row in the LDS step
-    // ---- S^T = K . Q^T
-    f32x4 s[R];
+  // Lane (r16, kg) of the transposed V reads: source lane 4k + q of its
+  // 16-lane group points at key row 4kg + k, columns 16j + 4q .. +3, so that
+  // (by the transpose read's layout) it receives element 16j + r16 of key
+  // rows 4kg .. 4kg + 3.
+  const int tr_off = (4 * kg + (r16 >> 2)) * LROW + (r16 & 3) * 8;
+
+  // One LDS step: its two 16-key tiles from LDS buffer `buf`, for each of the
+  // wave's row tiles.  `ok[g]`: tile g's block is in the pool and in range.
+  auto compute = [&](int st, int buf, const bool (&ok)[G]) {
+    const int kb = (b_begin + st * G) * 16;   // first key of the step
+    bool use[G];
 #pragma unroll
-    for (int r = 0; r < R; ++r) s[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < G; ++g) use[g] = ok[g] && kb + 16 * g <= wlast;   // wave-uniform
+    if (!use[0] && !use[1]) return;
+    // ---- S^T = K . Q^T for each tile (a tile out of range has no scores)
+    f32x4 s[G][R];
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      const u32x4 kop =
-          *reinterpret_cast<const u32x4*>(sk[buf] + (lrow0 + r16) * LROW + (32 * kk + 8 * kg) * 2);
+    for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int r = 0; r < R; ++r) s[r] = M::k32(kop, qop[r][kk], s[r]);
+      for (int r = 0; r < R; ++r) s[g][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (!use[g]) continue;
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        const u32x4 kop = *reinterpret_cast<const u32x4*>(
+            sk[buf] + (16 * g + r16) * LROW + (32 * kk + 8 * kg) * 2);
+#pragma unroll
+        for (int r = 0; r < R; ++r) s[g][r] = M::k32(kop, qop[r][kk], s[g][r]);
+      }
     }
-    // ---- online softmax per row, lazily rescaled; P^T as hi + lo pairs.
-    // Tiles wholly at or below the wave's first row position need no causal
-    // mask (the key rows past the workgroup's last key, zeros in LDS, only
-    // occur in tiles that reach past it).
-    const bool whole = kb + 15 <= wfirst;
-    u32x4 pcat[R];
+    // ---- online softmax per row over the step's 8 keys of this lane, lazily
+    // rescaled; P^T as a hi and a lo operand.  When both tiles are in range
+    // and wholly at or below the wave's first row position, no key needs the
+    // causal test (wave-uniform).
+    const bool all_whole = use[0] && use[1] && kb + 16 * G - 1 <= wfirst;
+    u32x4 phi[R], plo[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      float sc[4];
+      float sc[G][4];
+      if (all_whole) {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sc[g][i] = s[g][r][i] * a.scale_log2;
+      } else {
+        // keys past the row's position, or of a tile out of range, get no weight
+        const int lim = qlast[r] - kb - 4 * kg;   // key kb + 4kg + c is used when c <= lim
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            sc[g][i] = (use[g] && 16 * g + i <= lim) ? s[g][r][i] * a.scale_log2 : kNegInf;
+      }
       float tmax = kNegInf;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = kb + 4 * kg + i;
-        sc[i] = (whole || t <= qlast[r]) ? s[r][i] * a.scale_log2 : kNegInf;
-        tmax = fmaxf(tmax, sc[i]);
-      }
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sc[g][i]);
       // The running max of a row is shared by its four lane groups.  A lane
       // whose keys stay within the slack of it changes nothing; only when
       // some lane of the wave exceeds it are the row maxima taken across
       // the lane groups (the same value in all four) and the row rescaled.
-      if (__any(tmax > m[r] + kRescaleSlack)) {   // rare after the first blocks
+      if (__any(tmax > m[r] + kRescaleSlack)) {   // rare after the first steps
         tmax = max_xor32(max_xor16(tmax));
         const bool grow = tmax > m[r] + kRescaleSlack;
         const float mn = grow ? tmax : m[r];
@@ -271,31 +333,42 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
         for (int j = 0; j < NV; ++j) acc[r][j] *= alpha;
       }
       const float ms = (m[r] == kNegInf) ? 0.f : m[r];
-      float pw[4];
+      float pw[G][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pw[i] = fast_exp2(sc[i] - ms);
-        l[r] += pw[i];
-      }
-      const uint32_t h01 = M::pack(pw[0], pw[1]);
-      const uint32_t h23 = M::pack(pw[2], pw[3]);
-      // K = 32 of one product: the lane's 4 keys with the hi weights, then
-      // the same 4 keys with the lo weights (the A operand repeats them)
-      pcat[r] = u32x4{h01, h23, M::pack(pw[0] - M::lo(h01), pw[1] - M::hi(h01)),
-                      M::pack(pw[2] - M::lo(h23), pw[3] - M::hi(h23))};
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pw[g][i] = fast_exp2(sc[g][i] - ms);
+          l[r] += pw[g][i];
+        }
+      uint32_t h[4], lo[4];
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          h[2 * g + i] = M::pack(pw[g][2 * i], pw[g][2 * i + 1]);
+          lo[2 * g + i] = M::pack(pw[g][2 * i] - M::lo(h[2 * g + i]),
+                                  pw[g][2 * i + 1] - M::hi(h[2 * g + i]));
+        }
+      phi[r] = u32x4{h[0], h[1], h[2], h[3]};
+      plo[r] = u32x4{lo[0], lo[1], lo[2], lo[3]};
     }
-    // ---- O^T += V^T . P^T
-    u32x4 vrow[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      vrow[e] = load_bytes<VB>(sv[buf] + (lrow0 + 4 * kg + e) * LROW + r16 * VB);
+    // ---- O^T += V^T . P^T, 16 output elements per product: the K = 32
+    // slots of lane group kg are keys 4kg .. 4kg + 3 of the first tile, then
+    // the same keys of the second; one product with the hi weights, one with
+    // the lo.  Rows of a tile out of range hold finite values (zeros past
+    // the workgroup's last key) and meet zero weights.
+    const uint8_t* vb = sv[buf] + tr_off;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      const uint32_t v01 = pair_of(vrow[0], vrow[1], j);
-      const uint32_t v23 = pair_of(vrow[2], vrow[3], j);
-      const u32x4 vop = {v01, v23, v01, v23};
+      const u32x2 v0 = lds_read_tr16(vb + 32 * j);
+      const u32x2 v1 = lds_read_tr16(vb + 16 * LROW + 32 * j);
+      const u32x4 vop = {v0.x, v0.y, v1.x, v1.y};
 #pragma unroll
-      for (int r = 0; r < R; ++r) acc[r][j] = M::k32(vop, pcat[r], acc[r][j]);
+      for (int r = 0; r < R; ++r) {
+        acc[r][j] = M::k32(vop, phi[r], acc[r][j]);
+        acc[r][j] = M::k32(vop, plo[r], acc[r][j]);
+      }
     }
   };
 
@@ -320,8 +393,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
       sstore(st & 1, ld[u], st, ok);
       __syncthreads();
       gload(st + P, ld[u], ld_ok[u]);
-#pragma unroll
-      for (int g = 0; g < G; ++g) compute(b_begin + st * G + g, st & 1, ok[g], g);
+      compute(st, st & 1, ok);
     }
   }
 
@@ -340,19 +412,18 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
     const int64_t grow = qrow * hq + h;
     if (rparts <= 1) {
       const float inv = lr > 0.f ? 1.f / lr : 0.f;
-      // acc[r][j][i] is element NV*(4kg + i) + j of the row.
+      // acc[r][j][i] is element 16j + 4kg + i of the row.
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < NV; ++j)
 #pragma unroll
-        for (int j = 0; j < NV; ++j)
-          store_out(a, grow * D + NV * (4 * kg + i) + j, acc[r][j][i] * inv);
+        for (int i = 0; i < 4; ++i)
+          store_out(a, grow * D + 16 * j + 4 * kg + i, acc[r][j][i] * inv);
     } else {
       const int64_t slot = part_slot(a, qrow, h, part);
       float* po = a.part_o + slot * D;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < NV; ++j) po[NV * (4 * kg + i) + j] = acc[r][j][i];
+      for (int j = 0; j < NV; ++j)
+        *reinterpret_cast<f32x4*>(po + 16 * j + 4 * kg) = acc[r][j];
       if (kg == 0) {
         a.part_ml[slot * 2] = m[r];
         a.part_ml[slot * 2 + 1] = lr;
