@@ -79,7 +79,7 @@ def build(jobs: int = 0, debug: bool = False, verbose: bool = False) -> str:
             if rc:
                 raise RuntimeError(f"compile failed: {cmd}")
     tmp = LIB + ".tmp"
-    rc, cmd, out = _run([cc, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs])
+    rc, cmd, out = _run([cc, "-shared", f"--offload-arch={ARCH}", "-Wl,--no-undefined", "-o", tmp, *objs])
     if rc:
         print(cmd)
         print(out)

@@ -159,6 +159,14 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
+// gfx950 direct load of 16 bytes per lane from global memory into LDS: lane
+// l's bytes land at lds + 16 l (lds: wave-uniform, 16-byte aligned).  The
+// load counts in vmcnt like any vector load; its data is in LDS once that
+// count has passed it.
+__device__ __forceinline__ void load_to_lds16(const void* g, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
 __device__ __forceinline__ uint32_t dw(const u32x4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }

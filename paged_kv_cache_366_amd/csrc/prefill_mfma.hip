@@ -11,8 +11,8 @@
 // Layout.  A workgroup of 4 wavefronts owns 64 consecutive rows of one
 // sequence's chunk for one query head; wavefront w takes rows 16w..16w+15.
 // Every row of the workgroup reads the same keys, so K and V go through LDS
-// in steps of two 16-key tiles (double-buffered, rows padded by 16 bytes)
-// and all four wavefronts read them there.  Per step and wavefront:
+// in steps of two 16-key tiles and all four wavefronts read them there.
+// Per step and wavefront:
 //   S^T [16 keys x 16 rows] = K [16 x D] . Q^T [D x 16], per tile
 //       (D/32 MFMA 16x16x32; lane (r16, kg) holds keys 4kg..4kg+3 of row r16)
 //   online softmax per row (column), lazily rescaled: the row maximum across
@@ -27,11 +27,16 @@
 // in the key order of its weights, with no register permutes.  Lane
 // (r16, kg) ends with elements 16j + 4kg .. +3 of its row for each block j.
 //
-// Loads: the global loads of the next step are issued right after the
-// barrier and land in registers while the wavefronts compute; no branch
-// guards them (a block outside the pool reads a fixed in-pool address), so
-// the wait before the LDS store covers only that step's loads.  Steps whose
-// rows all exist are stored as they are; otherwise missing rows become zeros.
+// Loads: K and V move from global memory to LDS with gfx950's direct loads
+// (no registers in between) into three stages, so the loads of the next two
+// steps are in flight while a step computes.  Rows are unpadded and their
+// 16-byte chunks XOR-swizzled by row, which keeps the rows read at one
+// column in different banks.  Each wave waits for its own loads of a step,
+// then one barrier (without the memory fence of __syncthreads, which would
+// also wait for the steps still loading) makes every wave's loads visible.
+// Rows past the workgroup's last key and rows of blocks outside the pool
+// are zeroed by the wave that loaded them, after they land and before the
+// barrier.
 //
 // Causality: a key t is used by row i when t <= P_i; rows past the chunk are
 // idle, and a wavefront skips steps past its last row's position; steps
@@ -49,10 +54,12 @@
 //
 // Measured on MI355X (mixed step, four 512-row chunks over 0..1536 cached
 // tokens): the transposed value reads took the kernel from 140 to 109 us,
-// the order by context length and one register stage (128 VGPRs, four
-// waves per SIMD) to 95 us.  Counters then show the matrix cores 24% busy,
-// the VALU about 40%, waves waiting on dependencies a third of their time
-// and LDS bank conflicts in about 16% of the cycles.
+// the order by context length and four waves per SIMD to about 91 us, the
+// direct loads to 86 us.  What bounds it: without its arithmetic the same
+// kernel (loads, LDS, barriers) still takes about 62 us, and with its
+// arithmetic the longest row tiles (2,048 keys, 64 steps) finish last;
+// 8-wave workgroups (half the K/V traffic) and key partitions (fp32 partial
+// rows) both measured slower.
 #include "attention_common.h"
 #include "mfma_common.h"
 
@@ -64,9 +71,6 @@ namespace {
 #endif
 constexpr int kPrefillWaves = PKV_PREFILL_WAVES;   // wavefronts (16 rows each) per workgroup
 constexpr int kPrefillThreads = 64 * kPrefillWaves;
-#ifndef PKV_PREFILL_DEPTH
-#define PKV_PREFILL_DEPTH 1
-#endif
 #ifndef PKV_PREFILL_RTILES
 #define PKV_PREFILL_RTILES 1
 #endif
@@ -74,29 +78,24 @@ constexpr int kPrefillThreads = 64 * kPrefillWaves;
 #define PKV_PREFILL_GROUP 2
 #endif
 // Tuning constants (the defaults measured best on MI355X):
-constexpr int kDepth = PKV_PREFILL_DEPTH;     // steps whose global loads are in flight (one measured best)
 constexpr int kGroup = PKV_PREFILL_GROUP;     // 16-key tiles per LDS step (one barrier)
 constexpr int kRowTiles = PKV_PREFILL_RTILES; // 16-row tiles per wavefront
 constexpr int kTileRows = kPrefillWaves * 16 * kRowTiles;   // query rows per workgroup
 
-#ifdef PKV_PREFILL_WPE
-#define PKV_PREFILL_ATTR __attribute__((amdgpu_waves_per_eu(PKV_PREFILL_WPE)))
-#else
-#define PKV_PREFILL_ATTR
+// Registers for four waves per SIMD (at most 128 VGPRs): a compute unit
+// then holds four workgroups (LDS allows four too).  Left to itself the
+// compiler takes 130, which leaves room for three.
+#ifndef PKV_PREFILL_WPE
+#define PKV_PREFILL_WPE 4
 #endif
-template <typename T, int D, int P, int R, int G0, bool STREAM>
+#define PKV_PREFILL_ATTR __attribute__((amdgpu_waves_per_eu(PKV_PREFILL_WPE)))
+template <typename T, int D, int R, int G0>
 __global__ __launch_bounds__(kPrefillThreads) PKV_PREFILL_ATTR void prefill_mfma_kernel(AttnArgs a, int max_tiles) {
   constexpr int NK = D / 32;              // QK products per block and row tile
   constexpr int NV = D / 16;              // PV products per block and row tile
   constexpr int ROWB = D * 2;             // bytes of a K/V row
-  constexpr int LROW = ROWB + 16;         // LDS row stride
   constexpr int CHUNKS = ROWB / 16;       // 16-byte chunks per row
-  constexpr int TILE_CHUNKS = 16 * CHUNKS;
-  constexpr int NT = kPrefillThreads;
-  // Blocks per LDS step: at least enough that every thread has a chunk.
-  constexpr int G = (G0 * 2 * TILE_CHUNKS >= NT) ? G0 : NT / (2 * TILE_CHUNKS);
-  constexpr int LPS = G * 2 * TILE_CHUNKS / NT;   // K+V chunks per thread per step
-  static_assert(G * 2 * TILE_CHUNKS == NT * LPS, "a step's K and V split evenly over the threads");
+  constexpr int G = G0;                   // 16-key tiles per step
   static_assert(G == 2, "a step is two 16-key tiles: the K = 32 of one value product");
   constexpr int WROWS = 16 * R;           // rows per wavefront
   constexpr int TROWS = kPrefillWaves * WROWS;
@@ -179,72 +178,110 @@ __global__ __launch_bounds__(kPrefillThreads) PKV_PREFILL_ATTR void prefill_mfma
     }
   }
 
-  __shared__ __align__(16) uint8_t sk[2][G * 16 * LROW];
-  __shared__ __align__(16) uint8_t sv[2][G * 16 * LROW];
-
   const int32_t* trow = a.tables + static_cast<int64_t>(seq) * a.max_blocks;
   const uint8_t* kc = static_cast<const uint8_t*>(a.kc);
   const uint8_t* vc = static_cast<const uint8_t*>(a.vc);
 
-  // Tile b of the context into registers: K chunks first, then V.  Rows past
-  // the workgroup's last key, and every row of a block outside the pool,
-  // become zeros.  P blocks are in flight: slot u of the ring holds block
-  // b with b % P == u, so after unrolling every index is static.
-  u32x4 ld[P][LPS];
-  bool ld_ok[P][G];
-  // Loads of the G blocks of step st: chunk c of the step is block c / (2
-  // TILE_CHUNKS), K then V.  No branch around them and nothing consumes
-  // them before the LDS store, so the wait there covers only that step's
-  // loads and P steps really are in flight.  A block outside the pool (or
-  // past the table) reads the same bytes of the pool's first tile instead;
-  // the store turns it, and every row past the workgroup's last key, into
-  // zeros.
-  // Chunk i of a thread is chunk NT * i + threadIdx.x of the step; with
-  // NT and 2 TILE_CHUNKS powers of two, its block (gi) is the same for the
-  // whole workgroup and known at compile time.
-  static_assert(NT % (2 * TILE_CHUNKS) == 0 || (2 * TILE_CHUNKS) % NT == 0, "chunk split");
-  auto gload = [&](int st, u32x4 (&rg)[LPS], bool (&ok)[G]) {
+  // ---- K/V staging: direct global -> LDS loads into three stages --------
+  // A stage holds one step (two 16-key tiles) of K and of V: 32 rows of
+  // ROWB bytes each, unpadded.  One load instruction of a wave fills 1 KiB
+  // (lane l's 16 bytes land at byte 16 l), i.e. RPL whole rows.  The
+  // 16-byte chunk c of stage row r sits at chunk position c ^ (r % CHUNKS),
+  // so rows read at one column fall in different banks.  Loads of the step
+  // two ahead are in flight while a step computes, and they hold no
+  // registers.
+  constexpr int SROWS = G * 16;
+  constexpr int STAGE = SROWS * ROWB;
+  constexpr int RPL = 1024 / ROWB;                // rows per load instruction
+  constexpr int LPO = SROWS / RPL;                // load instructions per operand and step
+  // Per wave and operand: LDW instructions, by waves [0, LPO / LDW); with
+  // more waves than instructions the rest load nothing.
+  constexpr int LDW = LPO >= kPrefillWaves ? LPO / kPrefillWaves : 1;
+  static_assert(LPO % LDW == 0 && (LPO >= kPrefillWaves ? LPO % kPrefillWaves == 0 : true),
+                "loads split evenly over the waves");
+  const bool loader = wave * LDW < LPO;          // wave-uniform
+  constexpr int NLD = 2 * LDW;                    // vector memory instructions per loading wave and step
+  __shared__ __align__(1024) uint8_t sk0[STAGE], sk1[STAGE], sk2[STAGE];
+  __shared__ __align__(1024) uint8_t sv0[STAGE], sv1[STAGE], sv2[STAGE];
+
+  // Lane constants.  Load k of this wave (per operand) fills stage rows
+  // [RPL (wave LDW + k), +RPL); the lane's chunk comes from row
+  // rl = that + lane / CHUNKS of the step, chunk (lane % CHUNKS) ^ (rl % CHUNKS).
+  uint32_t loff[LDW];   // byte offset of the lane's chunk within its 16-row tile
+#pragma unroll
+  for (int k = 0; k < LDW; ++k) {
+    const int rl = RPL * (wave * LDW + k) + lane / CHUNKS;
+    loff[k] = (rl % 16) * ROWB + ((lane % CHUNKS) ^ (rl % CHUNKS)) * 16;
+  }
+  // K operand reads: row r16 (+16 for the second tile), chunk 4kk + kg.
+  uint32_t koff[NK];
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) koff[kk] = r16 * ROWB + ((4 * kk + kg) ^ (r16 % CHUNKS)) * 16;
+  // V transpose reads: source row 4kg + (r16 >> 2), elements 16j + 4 (r16 & 3)
+  // .. +3 = chunk 2j + ((r16 & 3) >> 1), half r16 & 1.
+  uint32_t voff[NV];
+  {
+    const int vr = 4 * kg + (r16 >> 2);
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+      voff[j] = vr * ROWB + ((2 * j + ((r16 & 3) >> 1)) ^ (vr % CHUNKS)) * 16 + (r16 & 1) * 8;
+  }
+
+  // Stage u's K and V bases (compile-time after unrolling).
+  auto kst = [&](int u) -> uint8_t* { return u == 0 ? sk0 : u == 1 ? sk1 : sk2; };
+  auto vst = [&](int u) -> uint8_t* { return u == 0 ? sv0 : u == 1 ? sv1 : sv2; };
+
+  // Issue the loads of step st into stage u: the step's table entries, then
+  // NLD instructions.  A block outside the pool or past the workgroup's range
+  // loads the pool's first tile instead, so every step issues the same
+  // count of loads (the waits below count them); such rows are zeroed after
+  // they land, by the wave that loaded them.
+  // Table entries come from a window of 64 in a vector register (lane i:
+  // entry tv_base + i), read with a lane read: a load per step would have
+  // to wait for every staging load issued before it.  The window moves (one
+  // load, which does wait) when a step needs an entry past it.
+  int tv_base = b_begin >> a.bs_shift;
+  int tv = tv_base + lane < a.max_blocks ? trow[tv_base + lane] : -1;
+  auto entry = [&](int e) {   // e: wave-uniform, not decreasing
+    if (e >= tv_base + 64) {
+      tv_base = e;
+      tv = e + lane < a.max_blocks ? trow[e + lane] : -1;
+    }
+    return __builtin_amdgcn_readlane(tv, e - tv_base);
+  };
+  bool okst[3][G];
+  auto issue = [&](int st, int u) {
     int64_t toff[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int b = b_begin + st * G + g;
-      const int p = trow[min(b, b_end - 1) >> a.bs_shift];
-      ok[g] = b < b_end && p >= 0 && p < a.num_blocks;
-      toff[g] = ok[g] ? tile_index(a, p, kvh, b) * (16 * ROWB) : 0;
+      const int p = entry(min(b, b_end - 1) >> a.bs_shift);
+      okst[u][g] = b < b_end && p >= 0 && p < a.num_blocks;
+      toff[g] = okst[u][g] ? tile_index(a, p, kvh, b) * (16 * ROWB) : 0;
     }
+    if (!loader) return;
 #pragma unroll
-    for (int i = 0; i < LPS; ++i) {
-      constexpr int kStep = 2 * TILE_CHUNKS;
-      const int gi = (NT * i) / kStep;
-      const int rem = (NT * i) % kStep + static_cast<int>(threadIdx.x);
-      rg[i] = load_kv<u32x4, STREAM>((rem < TILE_CHUNKS ? kc : vc) + toff[gi] +
-                                     (rem % TILE_CHUNKS) * 16);
+    for (int k = 0; k < LDW; ++k) {
+      const int g = (RPL * (wave * LDW + k)) / 16;   // wave-uniform
+      const int64_t t = g == 0 ? toff[0] : toff[1];
+      load_to_lds16(kc + t + loff[k], kst(u) + 1024 * (wave * LDW + k));
+      load_to_lds16(vc + t + loff[k], vst(u) + 1024 * (wave * LDW + k));
     }
   };
-  auto sstore = [&](int buf, const u32x4 (&rg)[LPS], int st, const bool (&ok)[G]) {
-    auto dst_of = [&](int i) {
-      constexpr int kStep = 2 * TILE_CHUNKS;
-      const int gi = (NT * i) / kStep;
-      const int rem = (NT * i) % kStep + static_cast<int>(threadIdx.x);
-      const int rc = rem % TILE_CHUNKS;
-      return (rem / TILE_CHUNKS == 0 ? sk[buf] : sv[buf]) + (gi * 16 + rc / CHUNKS) * LROW +
-             (rc % CHUNKS) * 16;
-    };
-    // Every row of both blocks in the pool and at or below the workgroup's
-    // last key (wave-uniform): plain stores; otherwise zeros where not.
-    if (ok[0] && ok[1] && (b_begin + st * G + G) * 16 - 1 <= tlast) {
+  // After this wave's loads of step st (stage u) have landed: zero the rows
+  // it loaded that are past the workgroup's last key or in a block outside
+  // the pool (wave-uniform test first).
+  auto fixup = [&](int st, int u) {
+    if (!loader || (okst[u][0] && okst[u][1] && (b_begin + st * G + G) * 16 - 1 <= tlast)) return;
 #pragma unroll
-      for (int i = 0; i < LPS; ++i) *reinterpret_cast<u32x4*>(dst_of(i)) = rg[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < LPS; ++i) {
-        constexpr int kStep = 2 * TILE_CHUNKS;
-        const int gi = (NT * i) / kStep;
-        const int rem = (NT * i) % kStep + static_cast<int>(threadIdx.x);
-        const int row = (rem % TILE_CHUNKS) / CHUNKS;
-        const bool use = ok[gi] && (b_begin + st * G + gi) * 16 + row <= tlast;
+    for (int k = 0; k < LDW; ++k) {
+      const int rl = RPL * (wave * LDW + k) + lane / CHUNKS;
+      const int g = rl / 16;
+      const bool ok = g == 0 ? okst[u][0] : okst[u][1];
+      if (!ok || (b_begin + st * G) * 16 + rl > tlast) {
         const u32x4 z = {0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(dst_of(i)) = use ? rg[i] : z;
+        *reinterpret_cast<u32x4*>(kst(u) + 1024 * (wave * LDW + k) + 16 * lane) = z;
+        *reinterpret_cast<u32x4*>(vst(u) + 1024 * (wave * LDW + k) + 16 * lane) = z;
       }
     }
   };
@@ -259,19 +296,13 @@ __global__ __launch_bounds__(kPrefillThreads) PKV_PREFILL_ATTR void prefill_mfma
     for (int j = 0; j < NV; ++j) acc[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Lane (r16, kg) of the transposed V reads: source lane 4k + q of its
-  // 16-lane group points at key row 4kg + k, columns 16j + 4q .. +3, so that
-  // (by the transpose read's layout) it receives element 16j + r16 of key
-  // rows 4kg .. 4kg + 3.
-  const int tr_off = (4 * kg + (r16 >> 2)) * LROW + (r16 & 3) * 8;
-
-  // One LDS step: its two 16-key tiles from LDS buffer `buf`, for each of the
-  // wave's row tiles.  `ok[g]`: tile g's block is in the pool and in range.
-  auto compute = [&](int st, int buf, const bool (&ok)[G]) {
+  // One step: its two 16-key tiles from stage u, for each of the wave's row
+  // tiles.
+  auto compute = [&](int st, int u) {
     const int kb = (b_begin + st * G) * 16;   // first key of the step
     bool use[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) use[g] = ok[g] && kb + 16 * g <= wlast;   // wave-uniform
+    for (int g = 0; g < G; ++g) use[g] = okst[u][g] && kb + 16 * g <= wlast;   // wave-uniform
     if (!use[0] && !use[1]) return;
     // ---- S^T = K . Q^T for each tile (a tile out of range has no scores)
     f32x4 s[G][R];
@@ -284,8 +315,7 @@ __global__ __launch_bounds__(kPrefillThreads) PKV_PREFILL_ATTR void prefill_mfma
       if (!use[g]) continue;
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
-        const u32x4 kop = *reinterpret_cast<const u32x4*>(
-            sk[buf] + (16 * g + r16) * LROW + (32 * kk + 8 * kg) * 2);
+        const u32x4 kop = *reinterpret_cast<const u32x4*>(kst(u) + 16 * g * ROWB + koff[kk]);
 #pragma unroll
         for (int r = 0; r < R; ++r) s[g][r] = M::k32(kop, qop[r][kk], s[g][r]);
       }
@@ -358,11 +388,10 @@ __global__ __launch_bounds__(kPrefillThreads) PKV_PREFILL_ATTR void prefill_mfma
     // the same keys of the second; one product with the hi weights, one with
     // the lo.  Rows of a tile out of range hold finite values (zeros past
     // the workgroup's last key) and meet zero weights.
-    const uint8_t* vb = sv[buf] + tr_off;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      const u32x2 v0 = lds_read_tr16(vb + 32 * j);
-      const u32x2 v1 = lds_read_tr16(vb + 16 * LROW + 32 * j);
+      const u32x2 v0 = lds_read_tr16(vst(u) + voff[j]);
+      const u32x2 v1 = lds_read_tr16(vst(u) + 16 * ROWB + voff[j]);
       const u32x4 vop = {v0.x, v0.y, v1.x, v1.y};
 #pragma unroll
       for (int r = 0; r < R; ++r) {
@@ -372,30 +401,42 @@ __global__ __launch_bounds__(kPrefillThreads) PKV_PREFILL_ATTR void prefill_mfma
     }
   };
 
+  // vmcnt(n) alone (expcnt and lgkmcnt left at their maxima).
+  constexpr int kWaitOneStep = (NLD & 15) | ((NLD >> 4) << 14) | (7 << 4) | (15 << 8);
+  static_assert(NLD < 64, "vmcnt range");
+  // Barrier without the memory fence __syncthreads adds: that fence waits for
+  // every load in flight, including the next steps' staging.  The empty asm
+  // statements keep the compiler from moving memory accesses across it.
+  auto barrier = [] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
   const int nstep = (b_end - b_begin + G - 1) / G;
-  {   // (the loads read table entries of blocks b_begin .. b_end - 1 only)
-#pragma unroll
-    for (int u = 0; u < P; ++u) gload(u, ld[u], ld_ok[u]);
-  }
-  // Step st: its registers go to LDS buffer st & 1 (the other buffer may
-  // still be read by slower waves for step st - 1), one barrier, then the
-  // freed registers start loading step st + P.  Whole groups of P steps, so
-  // no step is conditional (a step past the last block stores zeros and
-  // computes nothing).
+  // (the loads read table entries of blocks b_begin .. b_end - 1 only)
+  issue(0, 0);
+  issue(1, 1);
+  // Step st: wait for this wave's loads of step st (those of step st + 1
+  // stay in flight), zero its invalid rows, barrier (every wave's loads of
+  // step st have landed and every wave is done with step st - 1), start the
+  // loads of step st + 2 into the stage step st - 1 used, compute step st.
+  // Whole groups of three steps, so every stage index is static; steps past
+  // the last block load the first tile and compute nothing.
 #pragma unroll 1
-  for (int s0 = 0; s0 < nstep; s0 += P) {
+  for (int s0 = 0; s0 < nstep; s0 += 3) {
 #pragma unroll
-    for (int u = 0; u < P; ++u) {
+    for (int u = 0; u < 3; ++u) {
       const int st = s0 + u;
-      bool ok[G];
-#pragma unroll
-      for (int g = 0; g < G; ++g) ok[g] = ld_ok[u][g];
-      sstore(st & 1, ld[u], st, ok);
-      __syncthreads();
-      gload(st + P, ld[u], ld_ok[u]);
-      compute(st, st & 1, ok);
+      __builtin_amdgcn_s_waitcnt(kWaitOneStep);
+      fixup(st, u);
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the zeros are in LDS
+      barrier();
+      issue(st + 2, (u + 2) % 3);
+      compute(st, u);
     }
   }
+  __builtin_amdgcn_s_waitcnt(0);   // no load may land after the workgroup's LDS is released
 
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -432,17 +473,17 @@ __global__ __launch_bounds__(kPrefillThreads) PKV_PREFILL_ATTR void prefill_mfma
   }
 }
 
-template <typename T, bool NT>
+template <typename T>
 pkv_status launch_t(const AttnArgs& a, int D, int max_tiles, hipStream_t st) {
   const int64_t wgs = static_cast<int64_t>(a.num_seqs) * max_tiles * a.num_parts * a.hq;
   if (wgs > 0x7fffffff / kPrefillThreads)
     return fail(PKV_ERR_UNSUPPORTED, "prefill: launch too large");
   dim3 grid(static_cast<unsigned>(wgs));
   if (D == 64)
-    hipLaunchKernelGGL((prefill_mfma_kernel<T, 64, kDepth, kRowTiles, kGroup, NT>), grid, dim3(kPrefillThreads), 0, st,
+    hipLaunchKernelGGL((prefill_mfma_kernel<T, 64, kRowTiles, kGroup>), grid, dim3(kPrefillThreads), 0, st,
                        a, max_tiles);
   else
-    hipLaunchKernelGGL((prefill_mfma_kernel<T, 128, kDepth, kRowTiles, kGroup, NT>), grid, dim3(kPrefillThreads), 0, st,
+    hipLaunchKernelGGL((prefill_mfma_kernel<T, 128, kRowTiles, kGroup>), grid, dim3(kPrefillThreads), 0, st,
                        a, max_tiles);
   PKV_LAUNCH_CHECK("chunked prefill (MFMA)");
   return PKV_OK;
@@ -454,16 +495,12 @@ pkv_status launch_prefill_mfma(const AttnArgs& a, pkv_dtype q_dt, int D, int gro
                                int max_query_len, hipStream_t st) {
   if (max_query_len <= 0 || a.num_seqs <= 0) return PKV_OK;
   const int max_tiles = (max_query_len + kTileRows - 1) / kTileRows;
-  // A workgroup serves one query head and one row tile: when every chunk
-  // fits one row tile and no KV head serves several query heads, each K/V
-  // tile is read by one workgroup only, so (under the streaming policy) its
-  // loads carry the non-temporal hint; otherwise the other row tiles and
-  // heads reuse it from L2.
-  const bool stream = a.stream_kv && max_tiles == 1 && group == 1;
-  if (q_dt == PKV_BF16)
-    return stream ? launch_t<BF16, true>(a, D, max_tiles, st) : launch_t<BF16, false>(a, D, max_tiles, st);
-  if (q_dt == PKV_F16)
-    return stream ? launch_t<F16, true>(a, D, max_tiles, st) : launch_t<F16, false>(a, D, max_tiles, st);
+  // K/V go to LDS by direct loads with the default cache policy: the other
+  // row tiles of a chunk, and the other query heads of a KV head, read the
+  // same tiles, mostly at about the same time.
+  (void)group;
+  if (q_dt == PKV_BF16) return launch_t<BF16>(a, D, max_tiles, st);
+  if (q_dt == PKV_F16) return launch_t<F16>(a, D, max_tiles, st);
   return fail(PKV_ERR_UNSUPPORTED, "MFMA prefill needs 16-bit q");
 }
 
