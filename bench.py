@@ -33,7 +33,7 @@ bounded sample:
                separately against no HBM bound;
   c5_gqa_bf16  16 sequences, 64 query heads over 8 KV heads (group 8,
                matrix cores), head_dim 128, contexts U[8192, 32768], split-K
-               partitions of 512 tokens + reduce, bf16 KV;
+               partitions of 1,024 tokens + reduce, bf16 KV;
   c5_gqa_int8  the same with int8 KV and per-block fp32 scales (the pool is
                the library's block encoder output over the bf16 pool).
 
@@ -532,7 +532,7 @@ def bench_gqa(a, torch, pkv, algo, kv: str, c=None, sample_seqs: int = 6):
     S, hq, D = c.q.shape
     hkv = c.kv_heads
     max_ctx = int(c.context_lens.max())
-    part = a.partition if a.partition_set else 512
+    part = a.partition if a.partition_set else 1024
     out = torch.empty((S, hq, D), dtype=torch.float32, device=dev)
     ws = torch.zeros(max(pkv.pkv_decode_step_workspace_bytes(S, hq, D, max_ctx, part), 1),
                      dtype=torch.uint8, device=dev)
@@ -552,7 +552,7 @@ def bench_gqa(a, torch, pkv, algo, kv: str, c=None, sample_seqs: int = 6):
 
     # bf16: the attention launch appends the current token's rows itself
     # (pkv_paged_attention_decode_step), then the reduce kernel merges the
-    # 512-token partitions: two launches.  int8 / 4-bit: quantise-on-write of
+    # partitions: two launches.  int8 / 4-bit: quantise-on-write of
     # the current token, the attention launch, the reduce: three.
     def step(ev):
         if ev is not None:
@@ -626,7 +626,7 @@ def bench_gqa(a, torch, pkv, algo, kv: str, c=None, sample_seqs: int = 6):
                     "16 sequences, 64 query heads over 8 KV heads, head_dim 128, "
                     "contexts U[8192, 32768]; step = cache write of each sequence's current "
                     "token (bf16: inside the attention launch; codes: quantise-on-write) + "
-                    "split-K decode with 512-token partitions + reduce kernel",
+                    f"split-K decode with {part}-token partitions + reduce kernel",
         "context_tokens": tokens, "partition_tokens": part, "algo": a.algo})
     result.update({
         "tokens_per_s": S / (ms_per_step * 1e-3),

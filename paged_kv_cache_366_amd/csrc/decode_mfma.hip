@@ -61,8 +61,12 @@
 //   Weights enter the product as a bf16 (or f16) pair hi + lo, hi = p rounded
 //   and lo = p - hi rounded, which keeps about 16 mantissa bits at the cost
 //   of a second MFMA per product; decode is HBM-bound, so it is free.
-// The workgroup's wavefronts take the partition's tiles round-robin, two
-// tiles in flight each, and merge through LDS at the end.
+// The workgroup's wavefronts take the partition's tiles round-robin and
+// merge through LDS at the end.  16-bit KV: two tiles loaded, then both
+// computed.  Codes: each wave issues the loads of its next tile before it
+// computes the current one (two register buffers; about 1.5% faster for
+// int8 and 4-bit; for 16-bit KV the second buffer costs a wave per SIMD
+// and measured no faster).
 #include <type_traits>
 
 #include "attention_common.h"
@@ -85,16 +89,41 @@ template <typename KT>
 constexpr int mfma_waves() {
   return KT::bits == 16 ? PKV_MFMA_WAVES : PKV_MFMA_WAVES_CODES;
 }
-#ifndef PKV_MFMA_UNROLL
-#define PKV_MFMA_UNROLL 2
+// Tiles per load group (a wave computes one group while the next is in
+// flight), by storage width.
+#ifndef PKV_MFMA_UNROLL16
+#define PKV_MFMA_UNROLL16 2
 #endif
-constexpr int kUnroll = PKV_MFMA_UNROLL;   // tiles of K and V in flight per wavefront
-static_assert(64 % kUnroll == 0, "the unroll must divide the table chunk");
+#ifndef PKV_MFMA_UNROLL_CODES
+#define PKV_MFMA_UNROLL_CODES 1
+#endif
+template <typename KT>
+constexpr int mfma_unroll() {
+  return KT::bits == 16 ? PKV_MFMA_UNROLL16 : PKV_MFMA_UNROLL_CODES;
+}
+// Whether a wave issues the next group's loads before computing the current
+// one (two register buffers), by storage width.
+#ifndef PKV_MFMA_PIPE16
+#define PKV_MFMA_PIPE16 0
+#endif
+#ifndef PKV_MFMA_PIPE_CODES
+#define PKV_MFMA_PIPE_CODES 1
+#endif
+template <typename KT>
+constexpr bool mfma_pipe() {
+  return KT::bits == 16 ? PKV_MFMA_PIPE16 != 0 : PKV_MFMA_PIPE_CODES != 0;
+}
+#ifndef PKV_MFMA_WPE16
+#define PKV_MFMA_WPE16 1
+#endif
 
 template <typename QT, typename KT, int D, bool NTV>
-__global__ __launch_bounds__(64 * mfma_waves<KT>()) void decode_mfma_kernel(AttnArgs a,
-                                                                              int group) {
+__global__ __launch_bounds__(64 * mfma_waves<KT>())
+__attribute__((amdgpu_waves_per_eu(KT::bits == 16 ? PKV_MFMA_WPE16 : 1))) void decode_mfma_kernel(
+    AttnArgs a, int group) {
   constexpr int kWaves = mfma_waves<KT>();
+  constexpr int kUnroll = mfma_unroll<KT>();
+  static_assert(64 % kUnroll == 0, "the unroll must divide the table chunk");
   constexpr bool kInt4 = (KT::bits == 4);
   constexpr bool kInt8 = (KT::bits == 8);
   constexpr bool kScaled = kInt4 || kInt8;    // codes with per-tile scales
@@ -236,12 +265,22 @@ __global__ __launch_bounds__(64 * mfma_waves<KT>()) void decode_mfma_kernel(Attn
   const bool append = kCanAppend && a.new_k != nullptr;
   const int64_t new_row = (static_cast<int64_t>(seq) * a.hkv + kvh) * ROW;
 
-  for (int k = 0; k < nbw; k += kUnroll) {
-    if (k > 0 && (k & 63) == 0) tc.fetch(trow, b0, wave, kWaves, k, bmax, a.bs_shift);
+  // Tiles of K and V travel in groups of kUnroll through two register
+  // buffers: the loads of the next group are issued before the current one
+  // is computed, so each wave keeps a group in flight while it works.
+  struct TileBuf {
     u32x4 kr[kUnroll][NKL], vr[kUnroll][4];
     int phys[kUnroll];
     int nrow[kUnroll];          // row of the step's new token in the tile, or -1
     int64_t tofs[kUnroll];
+  };
+  auto issue = [&](int k, TileBuf& tb) {
+    if (k > 0 && (k & 63) == 0) tc.fetch(trow, b0, wave, kWaves, k, bmax, a.bs_shift);
+    auto& kr = tb.kr;
+    auto& vr = tb.vr;
+    auto& phys = tb.phys;
+    auto& nrow = tb.nrow;
+    auto& tofs = tb.tofs;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       int p = -1;
@@ -282,6 +321,13 @@ __global__ __launch_bounds__(64 * mfma_waves<KT>()) void decode_mfma_kernel(Attn
         }
       }
     }
+  };
+  auto compute = [&](int k, TileBuf& tb) {
+    auto& kr = tb.kr;
+    auto& vr = tb.vr;
+    auto& phys = tb.phys;
+    auto& nrow = tb.nrow;
+    auto& tofs = tb.tofs;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       if (k + u >= nbw) break;
@@ -461,6 +507,23 @@ __global__ __launch_bounds__(64 * mfma_waves<KT>()) void decode_mfma_kernel(Attn
             if (nrow[u] == 4 * kg + e) store_bytes<VB>(vw + e * ROW, vr[u][e]);
         }
       }
+    }
+  };
+  if constexpr (mfma_pipe<KT>()) {
+    TileBuf tb0, tb1;
+    issue(0, tb0);
+    for (int k = 0; k < nbw; k += 2 * kUnroll) {
+      issue(k + kUnroll, tb1);   // tiles past the wave's last are not loaded
+      compute(k, tb0);
+      if (k + kUnroll >= nbw) break;
+      issue(k + 2 * kUnroll, tb0);
+      compute(k + kUnroll, tb1);
+    }
+  } else {
+    for (int k = 0; k < nbw; k += kUnroll) {
+      TileBuf tb;
+      issue(k, tb);
+      compute(k, tb);
     }
   }
 
