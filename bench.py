@@ -74,17 +74,17 @@ PAGE_ALLOC_P99_BAR_US = 1000.0   # cnnetsun.cn section 4.2: page allocation P99 
 # profile that records the counts.  Valid only while the kernel sources hash
 # to the measured value; a changed kernel reports null.
 # HBM bytes per step of the dominant kernel(s), from rocprofv3 counter runs:
-# FETCH_SIZE scaled by 1 / 0.500040 (a 1 GiB torch.bitwise_not in the same
-# process reads as 524,330 KiB) plus WRITE_SIZE (exact for the same copy).
+# FETCH_SIZE scaled by 1 / 0.500041 (a 1 GiB torch.bitwise_not in the same
+# process reads as 524,331 KiB) plus WRITE_SIZE (exact for the same copy).
 # Reported only while the kernel sources hash to the value they were taken on.
-_SHA = "3cdc8de583e409dccab92677284d1e30b27d151b"
+_SHA = "2538eaff979f058f0b2f7addcf85db0c6153e93b"
 TRAFFIC = {
-    "decode7b": {"bytes_per_launch": 1120438917, "sources_sha1": _SHA, "partition_tokens": 2048,
+    "decode7b": {"bytes_per_launch": 1120437360, "sources_sha1": _SHA, "partition_tokens": 2048,
                  "profile": "profiles/decode_wave_7b_bf16_p2048_step_kernel_trace.md"},
-    "gqa-bf16": {"bytes_per_launch": 1591541385, "sources_sha1": _SHA, "partition_tokens": 512,
-                 "profile": "profiles/decode_mfma_gqa_long_bf16_p512_kernel_trace.md"},
-    "gqa-int8": {"bytes_per_launch": 868236428, "sources_sha1": _SHA, "partition_tokens": 512,
-                 "profile": "profiles/decode_mfma_gqa_long_int8_p512_kernel_trace.md"},
+    "gqa-bf16": {"bytes_per_launch": 1566064584, "sources_sha1": _SHA, "partition_tokens": 1024,
+                 "profile": "profiles/decode_mfma_gqa_long_bf16_p1024_kernel_trace.md"},
+    "gqa-int8": {"bytes_per_launch": 842335239, "sources_sha1": _SHA, "partition_tokens": 1024,
+                 "profile": "profiles/decode_mfma_gqa_long_int8_p1024_kernel_trace.md"},
 }
 KERNEL_SOURCES = ("decode_wave.hip", "decode_mfma.hip", "attention_common.h", "device_common.h",
                   "mfma_common.h")
@@ -532,7 +532,7 @@ def bench_gqa(a, torch, pkv, algo, kv: str, c=None, sample_seqs: int = 6):
     S, hq, D = c.q.shape
     hkv = c.kv_heads
     max_ctx = int(c.context_lens.max())
-    part = a.partition if a.partition_set else 1024
+    part = a.partition if a.partition_set else (512 if kv == "int4" else 1024)
     out = torch.empty((S, hq, D), dtype=torch.float32, device=dev)
     ws = torch.zeros(max(pkv.pkv_decode_step_workspace_bytes(S, hq, D, max_ctx, part), 1),
                      dtype=torch.uint8, device=dev)
