@@ -21,11 +21,14 @@
 // with the token's score.  The lanes that hold token t's K chunk also load
 // its V chunk, so the softmax weight never leaves its lanes: the PV product
 // accumulates per lane, and rows, then wavefronts, are merged once at the
-// end.  Wavefronts take blocks round-robin, one block of K and V in flight
-// each.  At bf16 / head_dim 128 the kernel takes 104 VGPRs (four waves per
-// SIMD): the compiler widens each value tile right after its load, ahead of
-// the softmax.  Pinning the widening next to the products (79 VGPRs, six
-// waves per SIMD) measured slower.
+// end.  Wavefronts take blocks round-robin.  A wave loads a block's K and
+// V into one set of registers and rotates them: the next block's K loads
+// go out once the scores are taken, its V loads once the values are
+// summed, so a tile stays in flight while the wave computes (2% faster at
+// the 7B shape than loading each block after the previous one).  At bf16 /
+// head_dim 128 the kernel takes 109 VGPRs (four waves per SIMD).  Pinning
+// the widening of the value tiles next to the products (fewer registers,
+// six waves per SIMD) measured slower.
 // For 16-bit keys the score uses packed dot2 instructions on the raw pairs,
 // and only the partly filled last block of a context pays for per-row
 // masking.
@@ -206,8 +209,12 @@ __global__ __launch_bounds__(64 * NW) void decode_wave_kernel(AttnArgs a) {
   // only for the partly filled last block of the context: its rows past the
   // context may hold anything (NaN included), so they are zeroed, not just
   // given zero weight.  Whole blocks run without any per-row test.
-  auto block_step = [&](auto masked_tag, const u32x4 (&kr)[NL], const u32x4 (&vr)[NL], int tpos,
-                        float ksc, float vsc) {
+  // One block in two halves: scores and the online softmax from the K tile
+  // (leaving the block's weights in pw), then the weighted sum of the V
+  // tile's rows.  The rotated loop below issues the next block's K loads
+  // between the two.
+  auto qk_softmax = [&](auto masked_tag, const u32x4 (&kr)[NL], int tpos, float ksc, float vsc,
+                        float (&pw)[G][NL]) {
     constexpr bool masked = decltype(masked_tag)::value;
     float s[G][NL];
 #pragma unroll
@@ -228,7 +235,6 @@ __global__ __launch_bounds__(64 * NW) void decode_wave_kernel(AttnArgs a) {
         s[g][j] = valid ? dot * (ksc * a.scale_log2) : kNegInf;
       }
     }
-    float pw[G][NL];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float tmax = s[g][0];
@@ -252,6 +258,9 @@ __global__ __launch_bounds__(64 * NW) void decode_wave_kernel(AttnArgs a) {
         for (int j = 0; j < NL; ++j) pw[g][j] *= vsc;   // per-block value scale
       }
     }
+  };
+  auto pv_sum = [&](auto masked_tag, const u32x4 (&vr)[NL], int tpos, const float (&pw)[G][NL]) {
+    constexpr bool masked = decltype(masked_tag)::value;
     constexpr int ND = UnpackDw<KT>::n;
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
@@ -268,6 +277,12 @@ __global__ __launch_bounds__(64 * NW) void decode_wave_kernel(AttnArgs a) {
         }
       }
     }
+  };
+  auto block_step = [&](auto masked_tag, const u32x4 (&kr)[NL], const u32x4 (&vr)[NL], int tpos,
+                        float ksc, float vsc) {
+    float pw[G][NL];
+    qk_softmax(masked_tag, kr, tpos, ksc, vsc, pw);
+    pv_sum(masked_tag, vr, tpos, pw);
   };
 
   // A decode step that appends (new_k set, 16-bit or fp32 K/V): position
@@ -319,11 +334,54 @@ __global__ __launch_bounds__(64 * NW) void decode_wave_kernel(AttnArgs a) {
     return true;
   };
 
+  // The same loads in two halves, for the rotated loop: the block's
+  // position, scales and K tile; then its V tile.
+  auto load_k = [&](int k, u32x4 (&kr)[NL], float& ksc, float& vsc, int64_t& toff, int& nrow) {
+    if (k > 0 && (k & 63) == 0) tc.fetch(trow, b0, wave, kWaves, k, bmax, a.bs_shift);
+    const int p = tc.get(k);
+    nrow = -1;
+    if (p < 0 || p >= a.num_blocks) return false;
+    const int tt = b0 + wave + kWaves * k;
+    toff = tile_index(a, p, kvh, tt) * TILE;
+    if (append) {
+      const int r = ctx - 1 - tt * 16;   // wave-uniform
+      nrow = (r >= 0 && r < 16) ? r : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      if constexpr (CB == 16) {
+        const uint8_t* kp = kbase + toff + j * 64 * CB;
+        if (kCanAppend && nrow >= 0 && j * TPL + u == nrow) kp = static_cast<const uint8_t*>(a.new_k) + new_off;
+        kr[j] = load_kv<u32x4, NT>(kp);
+      } else {
+        const u32x2 k2 = load_kv<u32x2, NT>(kbase + toff + j * 64 * CB);
+        kr[j] = u32x4{k2.x, k2.y, 0u, 0u};
+      }
+    }
+    ksc = vsc = 1.f;
+    if (kScaled) {
+      ksc = a.ks[static_cast<int64_t>(p) * a.hkv + kvh];
+      vsc = a.vs[static_cast<int64_t>(p) * a.hkv + kvh];
+    }
+    return true;
+  };
+  auto load_v = [&](u32x4 (&vr)[NL], int64_t toff, int nrow) {
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      if constexpr (CB == 16) {
+        const uint8_t* vp = vbase + toff + j * 64 * CB;
+        if (kCanAppend && nrow >= 0 && j * TPL + u == nrow) vp = static_cast<const uint8_t*>(a.new_v) + new_off;
+        vr[j] = load_kv<u32x4, NT>(vp);
+      } else {
+        const u32x2 v2 = load_kv<u32x2, NT>(vbase + toff + j * 64 * CB);
+        vr[j] = u32x4{v2.x, v2.y, 0u, 0u};
+      }
+    }
+  };
+
   // The wave's blocks are partition blocks wave, wave + NW, wave + 2 NW,
   // ...; all are whole except possibly the partition's last block, which is
-  // then the wave's last.  One block's K and V (8 KiB at bf16 / head_dim
-  // 128) are in flight per wave; at 104 VGPRs four waves share a SIMD, so a
-  // CU keeps about 128 KiB of loads outstanding.
+  // then the wave's last.
   const bool partial_tail = (t1 & 15) != 0;
   const int nwhole = nb - (partial_tail ? 1 : 0);
   const int kwhole = nwhole > wave ? (nwhole - wave + kWaves - 1) / kWaves : 0;
@@ -337,25 +395,75 @@ __global__ __launch_bounds__(64 * NW) void decode_wave_kernel(AttnArgs a) {
     else
       block_step(std::true_type{}, kr, vr, tpos, ksc, vsc);
   };
-#pragma unroll 1
-  for (int k = 0; k < kall; ++k) {
+  // The new token's K or V row to its slot (vector stores), from the
+  // registers that hold its tile.
+  auto store_new = [&](const u32x4 (&r)[NL], void* cache, int64_t toff, int nrow) {
+    if constexpr (kCanAppend) {
+      if (nrow >= 0) {
+        uint8_t* w = static_cast<uint8_t*>(cache) + lane * CB + toff;
+#pragma unroll
+        for (int j = 0; j < NL; ++j)
+          if (j * TPL + u == nrow) *reinterpret_cast<u32x4*>(w + j * 64 * CB) = r[j];
+      }
+    }
+  };
+#ifndef PKV_WAVE_ROTATE
+#define PKV_WAVE_ROTATE 1
+#endif
+  if constexpr (PKV_WAVE_ROTATE != 0) {
+    // Rotated: the next block's K loads go out once this block's scores are
+    // taken, its V loads once this block's values are summed, into the same
+    // registers, so a wave keeps one tile in flight while it computes.
     u32x4 kr[NL], vr[NL];
     float ksc = 1.f, vsc = 1.f;
     int64_t toff = 0;
     int nrow = -1;
-    const bool ok = load_block(k, kr, vr, ksc, vsc, toff, nrow);
-    step(k, ok, kr, vr, ksc, vsc);
-    if constexpr (kCanAppend) {
-      if (nrow >= 0) {   // the new token's rows to their slot (vector stores)
-        uint8_t* kw = static_cast<uint8_t*>(const_cast<void*>(a.kc)) + lane * CB + toff;
-        uint8_t* vw = static_cast<uint8_t*>(const_cast<void*>(a.vc)) + lane * CB + toff;
-#pragma unroll
-        for (int j = 0; j < NL; ++j) {
-          if (j * TPL + u == nrow) {
-            *reinterpret_cast<u32x4*>(kw + j * 64 * CB) = kr[j];
-            *reinterpret_cast<u32x4*>(vw + j * 64 * CB) = vr[j];
-          }
-        }
+    bool ok = false;
+    if (kall > 0) {
+      ok = load_k(0, kr, ksc, vsc, toff, nrow);
+      if (ok) load_v(vr, toff, nrow);
+    }
+#pragma unroll 1
+    for (int k = 0; k < kall; ++k) {
+      const int tpos = (b0 + wave + kWaves * k) * 16;
+      float pw[G][NL];
+      if (ok) {
+        if (k < kwhole)
+          qk_softmax(std::false_type{}, kr, tpos, ksc, vsc, pw);
+        else
+          qk_softmax(std::true_type{}, kr, tpos, ksc, vsc, pw);
+        store_new(kr, const_cast<void*>(a.kc), toff, nrow);
+      }
+      float ksc_n = 1.f, vsc_n = 1.f;
+      int64_t toff_n = 0;
+      int nrow_n = -1;
+      const bool ok_n = k + 1 < kall && load_k(k + 1, kr, ksc_n, vsc_n, toff_n, nrow_n);
+      if (ok) {
+        if (k < kwhole)
+          pv_sum(std::false_type{}, vr, tpos, pw);
+        else
+          pv_sum(std::true_type{}, vr, tpos, pw);
+        store_new(vr, const_cast<void*>(a.vc), toff, nrow);
+      }
+      if (ok_n) load_v(vr, toff_n, nrow_n);
+      ok = ok_n;
+      ksc = ksc_n;
+      vsc = vsc_n;
+      toff = toff_n;
+      nrow = nrow_n;
+    }
+  } else {
+#pragma unroll 1
+    for (int k = 0; k < kall; ++k) {
+      u32x4 kr[NL], vr[NL];
+      float ksc = 1.f, vsc = 1.f;
+      int64_t toff = 0;
+      int nrow = -1;
+      const bool ok = load_block(k, kr, vr, ksc, vsc, toff, nrow);
+      step(k, ok, kr, vr, ksc, vsc);
+      if (ok) {
+        store_new(kr, const_cast<void*>(a.kc), toff, nrow);
+        store_new(vr, const_cast<void*>(a.vc), toff, nrow);
       }
     }
   }
