@@ -21,8 +21,8 @@
 // with the token's score.  The lanes that hold token t's K chunk also load
 // its V chunk, so the softmax weight never leaves its lanes: the PV product
 // accumulates per lane, and rows, then wavefronts, are merged once at the
-// end.  Wavefronts take blocks round-robin.  A wave loads a block's K and
-// V into one set of registers and rotates them: the next block's K loads
+// end.  Wavefronts take blocks round-robin.  With streaming loads a wave
+// loads a block's K and V into one set of registers and rotates them: the next block's K loads
 // go out once the scores are taken, its V loads once the values are
 // summed, so a tile stays in flight while the wave computes (2% faster at
 // the 7B shape than loading each block after the previous one).  At bf16 /
@@ -410,10 +410,13 @@ __global__ __launch_bounds__(64 * NW) void decode_wave_kernel(AttnArgs a) {
 #ifndef PKV_WAVE_ROTATE
 #define PKV_WAVE_ROTATE 1
 #endif
-  if constexpr (PKV_WAVE_ROTATE != 0) {
-    // Rotated: the next block's K loads go out once this block's scores are
-    // taken, its V loads once this block's values are summed, into the same
-    // registers, so a wave keeps one tile in flight while it computes.
+  if constexpr (PKV_WAVE_ROTATE != 0 && NT) {
+    // Rotated (streaming loads): the next block's K loads go out once this
+    // block's scores are taken, its V loads once this block's values are
+    // summed, into the same registers, so a wave keeps one tile in flight
+    // while it computes.  With cached loads over cache-resident blocks (the
+    // shared-prefix beams) it measured 7% slower, so those load each block
+    // after the previous one.
     u32x4 kr[NL], vr[NL];
     float ksc = 1.f, vsc = 1.f;
     int64_t toff = 0;
