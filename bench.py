@@ -77,13 +77,13 @@ PAGE_ALLOC_P99_BAR_US = 1000.0   # cnnetsun.cn section 4.2: page allocation P99 
 # FETCH_SIZE scaled by 1 / 0.500041 (a 1 GiB torch.bitwise_not in the same
 # process reads as 524,331 KiB) plus WRITE_SIZE (exact for the same copy).
 # Reported only while the kernel sources hash to the value they were taken on.
-_SHA = "2538eaff979f058f0b2f7addcf85db0c6153e93b"
+_SHA = "66877b3eca513f2f7390e83b40beaef7ace1c3f1"
 TRAFFIC = {
-    "decode7b": {"bytes_per_launch": 1120437360, "sources_sha1": _SHA, "partition_tokens": 2048,
+    "decode7b": {"bytes_per_launch": 1120459873, "sources_sha1": _SHA, "partition_tokens": 2048,
                  "profile": "profiles/decode_wave_7b_bf16_p2048_step_kernel_trace.md"},
-    "gqa-bf16": {"bytes_per_launch": 1566064584, "sources_sha1": _SHA, "partition_tokens": 1024,
+    "gqa-bf16": {"bytes_per_launch": 1566085053, "sources_sha1": _SHA, "partition_tokens": 1024,
                  "profile": "profiles/decode_mfma_gqa_long_bf16_p1024_kernel_trace.md"},
-    "gqa-int8": {"bytes_per_launch": 842335239, "sources_sha1": _SHA, "partition_tokens": 1024,
+    "gqa-int8": {"bytes_per_launch": 842329110, "sources_sha1": _SHA, "partition_tokens": 1024,
                  "profile": "profiles/decode_mfma_gqa_long_int8_p1024_kernel_trace.md"},
 }
 KERNEL_SOURCES = ("decode_wave.hip", "decode_mfma.hip", "attention_common.h", "device_common.h",
