@@ -47,6 +47,11 @@
 
 #include "attention_common.h"
 
+// A multiply-add is fused only where the code says fmaf.  Left to the
+// compiler, the fusing depends on how the loop around it is laid out, and the
+// streaming and cached loop forms below would round differently.
+#pragma clang fp contract(off)
+
 namespace pkv {
 namespace {
 
@@ -249,7 +254,7 @@ __global__ __launch_bounds__(64 * NW) void decode_wave_kernel(AttnArgs a) {
         pw[g][j] = fast_exp2(s[g][j] - ms);
         psum += pw[g][j];
       }
-      l[g] = l[g] * alpha + psum;
+      l[g] = fmaf(l[g], alpha, psum);
       m[g] = mn;
 #pragma unroll
       for (int e = 0; e < E; ++e) o[g][e] *= alpha;
@@ -480,9 +485,9 @@ __global__ __launch_bounds__(64 * NW) void decode_wave_kernel(AttnArgs a) {
       const float l2 = __shfl_xor(l[g], off);
       float mn, f1, f2;
       merge_factors(m[g], m2, mn, f1, f2);
-      l[g] = l[g] * f1 + l2 * f2;
+      l[g] = fmaf(l[g], f1, l2 * f2);
 #pragma unroll
-      for (int e = 0; e < E; ++e) o[g][e] = o[g][e] * f1 + __shfl_xor(o[g][e], off) * f2;
+      for (int e = 0; e < E; ++e) o[g][e] = fmaf(o[g][e], f1, __shfl_xor(o[g][e], off) * f2);
       m[g] = mn;
     }
   }
