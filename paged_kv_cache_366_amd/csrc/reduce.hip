@@ -16,8 +16,12 @@ namespace {
 // thread (g, d) sums element d over half g of the partitions in order, and
 // the two halves are added: the canonical order of merge_ml / merge_elem,
 // so the same bits as the last-arriver merge inside the decode kernels.
-// Each thread's loads of the partitions' outputs are independent.
+// Each thread's loads of the partitions' outputs do not depend on the
+// factors: the first kChunk of them are issued before the (max, sum) pass,
+// and each later chunk before the previous one is summed, so a workgroup
+// waits on memory about twice rather than once per unrolled batch.
 constexpr int kMaxCachedParts = 1024;   // partitions whose (max, sum, factor) sit in LDS
+constexpr int kChunk = 16;              // partition outputs a thread holds in flight
 
 __global__ __launch_bounds__(256) void reduce_kernel(AttnArgs a, int D) {
   const int h = blockIdx.x % a.hq;
@@ -32,6 +36,17 @@ __global__ __launch_bounds__(256) void reduce_kernel(AttnArgs a, int D) {
   const int d = tid % D;
   const float* ml = a.part_ml + part_slot(a, row, h, 0) * 2;
   const int64_t st = 2 * static_cast<int64_t>(a.hq);   // floats between partitions' pairs
+  const int half = (nparts + 1) >> 1;
+  const float* po = a.part_o + part_slot(a, row, h, 0) * D + d;
+  const int64_t so = static_cast<int64_t>(a.hq) * D;   // floats between partitions' rows
+  const int p_begin = g * half;
+  const int p_end = min(nparts, (g + 1) * half);
+  float ov[kChunk];
+  auto load_chunk = [&](int p0) {
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) ov[i] = p0 + i < p_end ? po[(p0 + i) * so] : 0.f;
+  };
+  load_chunk(p_begin);
   __shared__ float s_m[kMaxCachedParts], s_l[kMaxCachedParts];
   __shared__ float s_red[4];
   __shared__ float s_o[128];
@@ -57,18 +72,25 @@ __global__ __launch_bounds__(256) void reduce_kernel(AttnArgs a, int D) {
     return p < kMaxCachedParts ? s_m[p] : fast_exp2(ml[p * st] - ms);
   };
   auto lsum = [&](int p) { return p < kMaxCachedParts ? s_l[p] : ml[p * st + 1]; };
-  const int half = (nparts + 1) >> 1;
-  const float* po = a.part_o + part_slot(a, row, h, 0) * D + d;
-  const int64_t so = static_cast<int64_t>(a.hq) * D;   // floats between partitions' rows
-  float O = 0.f;
-  const int p_end = min(nparts, (g + 1) * half);
+  // The sum L first (LDS only), while the output loads are in flight.
+  float L = 0.f;
+  if (g == 0) {
 #pragma unroll 8
-  for (int p = g * half; p < p_end; ++p) O = fmaf(po[p * so], factor(p), O);
+    for (int p = 0; p < nparts; ++p) L = fmaf(lsum(p), factor(p), L);
+  }
+  float O = 0.f;
+  for (int p0 = p_begin; p0 < p_end; p0 += kChunk) {
+    float cur[kChunk];
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) cur[i] = ov[i];
+    if (p0 + kChunk < p_end) load_chunk(p0 + kChunk);
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i)
+      if (p0 + i < p_end) O = fmaf(cur[i], factor(p0 + i), O);
+  }
   if (g == 1) s_o[d] = O;
   __syncthreads();
   if (g == 0) {
-    float L = 0.f;
-    for (int p = 0; p < nparts; ++p) L = fmaf(lsum(p), factor(p), L);
     store_out(a, (static_cast<int64_t>(row) * a.hq + h) * D + d,
               L > 0.f ? (O + s_o[d]) / L : 0.f);
   }
