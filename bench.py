@@ -33,7 +33,10 @@ bounded sample:
                separately against no HBM bound;
   c5_gqa_bf16  16 sequences, 64 query heads over 8 KV heads (group 8,
                matrix cores), head_dim 128, contexts U[8192, 32768], split-K
-               partitions of 1,024 tokens + reduce, bf16 KV;
+               decode + reduce, bf16 KV, with the partition the library
+               picks for these lengths (pkv_decode_partition_tokens: the
+               shortest whose workgroups fill one round of the resident
+               ones; --partition overrides it);
   c5_gqa_int8  the same with int8 KV and per-block fp32 scales (the pool is
                the library's block encoder output over the bf16 pool).
 
@@ -532,7 +535,11 @@ def bench_gqa(a, torch, pkv, algo, kv: str, c=None, sample_seqs: int = 6):
     S, hq, D = c.q.shape
     hkv = c.kv_heads
     max_ctx = int(c.context_lens.max())
-    part = a.partition if a.partition_set else (512 if kv == "int4" else 1024)
+    # the library's partition for these lengths and this kernel: the
+    # shortest whose workgroups fit one round of the resident ones
+    kv_code = pkv.PKV_I8 if int8 else pkv.PKV_I4 if int4 else pkv.PKV_BF16
+    part = a.partition if a.partition_set else pkv.pkv_decode_partition_tokens(
+        c.context_lens, pkv.PKV_BF16, kv_code, hq, hkv, D, BLOCK, c.num_blocks, algo)
     out = torch.empty((S, hq, D), dtype=torch.float32, device=dev)
     ws = torch.zeros(max(pkv.pkv_decode_step_workspace_bytes(S, hq, D, max_ctx, part), 1),
                      dtype=torch.uint8, device=dev)
@@ -626,7 +633,10 @@ def bench_gqa(a, torch, pkv, algo, kv: str, c=None, sample_seqs: int = 6):
                     "16 sequences, 64 query heads over 8 KV heads, head_dim 128, "
                     "contexts U[8192, 32768]; step = cache write of each sequence's current "
                     "token (bf16: inside the attention launch; codes: quantise-on-write) + "
-                    f"split-K decode with {part}-token partitions + reduce kernel",
+                    f"split-K decode with {part}-token partitions ("
+                    + ("set by --partition" if a.partition_set else
+                       "the library's choice for these lengths and this kernel")
+                    + ") + reduce kernel",
         "context_tokens": tokens, "partition_tokens": part, "algo": a.algo})
     result.update({
         "tokens_per_s": S / (ms_per_step * 1e-3),
@@ -692,7 +702,8 @@ def bench_mixed(a, torch, pkv, algo):
     qsl = np.concatenate([[0], np.cumsum(ms.new[pre])]).astype(np.int32)
     qsl_d = torch.from_numpy(qsl).to(dev)
     mc_d, mc_p, mq = int(lens[dec].max()), int(lens[pre].max()), int(ms.new[pre].max())
-    part = a.partition if a.partition_set else 1024
+    part = a.partition if a.partition_set else pkv.pkv_decode_partition_tokens(
+        lens[dec], pkv.PKV_BF16, pkv.PKV_BF16, hq, hkv, D, BLOCK, nb, algo)
     out_d = torch.empty(q_d.shape, dtype=torch.float32, device=dev)
     out_p = torch.empty(q_p.shape, dtype=torch.float32, device=dev)
     ws = torch.empty(max(pkv.pkv_decode_workspace_bytes(len(dec), hq, D, mc_d, part), 1),
@@ -1307,8 +1318,9 @@ def main(argv=None) -> int:
                          "print one workload's line")
     ap.add_argument("--partition", type=int, default=None,
                     help="split-K partition size in tokens (0 = no split) for every workload "
-                         "run; default 2048 for the 7B step, 1024 for the mixed step, 512 for "
-                         "the long-context GQA workloads, 0 for the beam workload")
+                         "run; default 2048 for the 7B step (no split), 0 for the beam "
+                         "workload, the library's choice (pkv_decode_partition_tokens) for the "
+                         "mixed step and the long-context GQA workloads")
     ap.add_argument("--algo", choices=("auto", "wave", "mfma"), default="auto")
     ap.add_argument("--prefill-partition", type=int, default=0,
                     help="key partition size of chunked prefill in tokens (0 = no split)")
@@ -1331,8 +1343,9 @@ def main(argv=None) -> int:
     a.partition_set = a.partition is not None
     if a.partition is None:
         # each workload chooses its own split-K partition unless --partition
-        # is given: 2,048 tokens (no split) for the 7B step, 1,024 for the
-        # mixed step's decode part, 512 for long-context GQA, none for beams
+        # is given: 2,048 tokens (no split) for the 7B step, none for beams,
+        # the library's choice for the mixed step's decode part and for
+        # long-context GQA
         a.partition = 0
 
     import torch

@@ -440,6 +440,49 @@ pkv_status pkv_quantize_blocks_int4(const void* src_k, const void* src_v, pkv_dt
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_context_len, int32_t partition_tokens);
 
+/* Partition size for a decode launch (host).  The keys of a context may be
+ * split into partitions whose partial results merge into one softmax
+ * ([cnnetsun] §3.1: a softmax over the scores of every page); how long the
+ * partitions are is a choice of the launch, not of the method, and changes
+ * results only by rounding.  A decode launch holds one workgroup per
+ * (partition, row, workgroup of heads); when the grid needs one round of the
+ * workgroups the GPU keeps resident plus a fraction of another, that
+ * fraction runs with the GPU mostly idle.  This picks the shortest
+ * partition (a multiple of 16 tokens, at least min_tokens) whose workgroups
+ * fit in the whole rounds the launch needs without a split, so each round
+ * is as full as it can be; 0 (no split) when no split fits in them.
+ *   context_lens   host int32[num_seqs], each >= 0 (the lengths the decode
+ *                  call will see on the device)
+ *   workgroups_per_partition  workgroups a (partition, row) takes
+ *   resident_workgroups       workgroups of the launch the GPU holds at once
+ *   min_tokens     shortest partition allowed
+ *   partition_tokens  out: the partition, or 0
+ * Reads only host memory; INVALID for NULL pointers, negative lengths or
+ * sizes, or non-positive workgroup counts. */
+pkv_status pkv_decode_partition_for_capacity(const int32_t* context_lens, int32_t num_seqs,
+                                             int32_t workgroups_per_partition,
+                                             int64_t resident_workgroups, int32_t min_tokens,
+                                             int32_t* partition_tokens);
+
+/* pkv_decode_partition_for_capacity for the kernel a decode call with these
+ * arguments launches on the current device: its resident workgroups come
+ * from the runtime's occupancy query times the device's compute units, its
+ * workgroups per (partition, row) from its heads per workgroup, and the
+ * shortest partition is 256 tokens (1,024 for the 16-wave kernel of one head
+ * of streamed 16-bit K/V, which runs only at partitions that long).  Pass
+ * the result as partition_tokens to pkv_paged_attention_decode (or _step,
+ * _partials), with pkv_decode_workspace_bytes for it.
+ *   context_lens   host int32[num_seqs]
+ *   q_dtype .. algo  as pkv_paged_attention_decode (num_blocks and
+ *                  block_size decide the load policy the launch takes)
+ *   partition_tokens  out
+ * Errors: INVALID / UNSUPPORTED as the decode call would report them for
+ * these types and sizes; DEVICE when the occupancy query fails. */
+pkv_status pkv_decode_partition_tokens(const int32_t* context_lens, int32_t num_seqs,
+                                       pkv_dtype q_dtype, pkv_dtype kv_dtype, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                       int32_t num_blocks, int32_t algo, int32_t* partition_tokens);
+
 pkv_status pkv_paged_attention_decode(
     void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype, const void* k_cache,
     const void* v_cache, pkv_dtype kv_dtype, const float* k_scale, const float* v_scale,

@@ -379,6 +379,30 @@ def pkv_decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
                                              partition_tokens)
 
 
+def pkv_decode_partition_for_capacity(context_lens, workgroups_per_partition: int,
+                                      resident_workgroups: int, min_tokens: int) -> int:
+    """Shortest partition whose workgroups fill the launch's whole rounds
+    (0: no split); context_lens is a host sequence of lengths."""
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    out = C.c_int32(0)
+    check(load().pkv_decode_partition_for_capacity(_i32p(lens), len(lens), workgroups_per_partition,
+                                                   resident_workgroups, min_tokens, C.byref(out)))
+    return out.value
+
+
+def pkv_decode_partition_tokens(context_lens, q_dtype: int, kv_dtype: int, num_q_heads: int,
+                                num_kv_heads: int, head_dim: int, block_size: int,
+                                num_blocks: int, algo: int = PKV_ALGO_AUTO) -> int:
+    """Partition for the decode kernel these arguments launch on the current
+    device (0: no split); context_lens is a host sequence of lengths."""
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    out = C.c_int32(0)
+    check(load().pkv_decode_partition_tokens(_i32p(lens), len(lens), q_dtype, kv_dtype, num_q_heads,
+                                             num_kv_heads, head_dim, block_size, num_blocks, algo,
+                                             C.byref(out)))
+    return out.value
+
+
 def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
                  partition_tokens, algo, k_scale, v_scale, workspace, stream, allocate=True):
     torch = _torch()

@@ -1,6 +1,8 @@
 // C entry points of paged attention: argument checks, workspace layout and
 // the choice between the wavefront and matrix-core kernels.
+#include <algorithm>
 #include <atomic>
+#include <climits>
 #include <cmath>
 #include <vector>
 
@@ -15,6 +17,10 @@ pkv_status launch_decode_mfma(const AttnArgs& a, pkv_dtype q_dt, pkv_dtype kv_dt
                               int group, hipStream_t st);
 pkv_status launch_prefill_mfma(const AttnArgs& a, pkv_dtype q_dt, int D, int group,
                                int max_query_len, hipStream_t st);
+pkv_status decode_wave_occupancy(pkv_dtype q_dt, pkv_dtype kv_dt, int D, int group,
+                                 int part_tokens, bool nt, int* wg_per_cu, int* heads_per_wg,
+                                 int* min_part_tokens);
+pkv_status decode_mfma_occupancy(pkv_dtype q_dt, pkv_dtype kv_dt, int D, bool nt, int* wg_per_cu);
 }  // namespace pkv
 
 using namespace pkv;
@@ -22,6 +28,9 @@ using namespace pkv;
 namespace {
 
 constexpr size_t kAlign = 256;
+// Shortest partition the automatic choice takes: below it each workgroup's
+// start (table entries, q) and partial-state write outweigh its keys.
+constexpr int32_t kMinAutoPartition = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -294,6 +303,104 @@ size_t pkv_prefill_workspace_bytes(int32_t num_query_tokens, int32_t num_q_heads
   return workspace_layout(num_query_tokens, num_q_heads, head_dim,
                           num_partitions(max_context_len, partition_tokens))
       .total;
+}
+
+pkv_status pkv_decode_partition_for_capacity(const int32_t* context_lens, int32_t num_seqs,
+                                             int32_t workgroups_per_partition,
+                                             int64_t resident_workgroups, int32_t min_tokens,
+                                             int32_t* partition_tokens) {
+  const char* who = "decode_partition_for_capacity";
+  if (!partition_tokens || (num_seqs > 0 && !context_lens))
+    return fail(PKV_ERR_INVALID, "%s: NULL pointer", who);
+  if (num_seqs < 0 || workgroups_per_partition <= 0 || resident_workgroups <= 0 || min_tokens < 0)
+    return fail(PKV_ERR_INVALID, "%s: bad sizes (S=%d per-partition %d resident %lld min %d)", who,
+                num_seqs, workgroups_per_partition, static_cast<long long>(resident_workgroups),
+                min_tokens);
+  int32_t max_len = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    if (context_lens[s] < 0)
+      return fail(PKV_ERR_INVALID, "%s: context_lens[%d] = %d", who, s, context_lens[s]);
+    max_len = std::max(max_len, context_lens[s]);
+  }
+  *partition_tokens = 0;
+  const int64_t cap = (static_cast<int64_t>(max_len) + 15) / 16 * 16;   // one partition per context
+  const int64_t lo = std::max<int64_t>(16, (static_cast<int64_t>(min_tokens) + 15) / 16 * 16);
+  if (max_len == 0 || lo >= cap) return PKV_OK;
+  // Workgroups holding keys at partitions of p tokens (those of partitions
+  // past a context's end exit at once and hold no slot).
+  auto wgs = [&](int64_t p) {
+    int64_t n = 0;
+    for (int32_t s = 0; s < num_seqs; ++s) n += (context_lens[s] + p - 1) / p;
+    return n * workgroups_per_partition;
+  };
+  // Whole rounds the launch needs without a split; the smallest partition
+  // that still fits in them fills them the most.
+  const int64_t rounds = (wgs(cap) + resident_workgroups - 1) / resident_workgroups;
+  const int64_t target = rounds * resident_workgroups;
+  int64_t a = lo / 16, b = cap / 16;   // wgs(16 b) <= target; find the least such
+  while (a < b) {
+    const int64_t m = (a + b) / 2;
+    if (wgs(16 * m) <= target) b = m; else a = m + 1;
+  }
+  if (16 * a < cap) *partition_tokens = static_cast<int32_t>(16 * a);
+  return PKV_OK;
+}
+
+pkv_status pkv_decode_partition_tokens(const int32_t* context_lens, int32_t num_seqs,
+                                       pkv_dtype q_dtype, pkv_dtype kv_dtype, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                       int32_t num_blocks, int32_t algo, int32_t* partition_tokens) {
+  const char* who = "decode_partition_tokens";
+  if (!partition_tokens) return fail(PKV_ERR_INVALID, "%s: NULL pointer", who);
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID, "%s: bad sizes (Hq=%d Hkv=%d NB=%d)", who, num_q_heads,
+                num_kv_heads, num_blocks);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: head_dim %d (64 or 128)", who, head_dim);
+  if (block_shift(block_size) < 0)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: block_size %d (16, 32, 64 or 128)", who, block_size);
+  if (q_dtype != PKV_F32 && q_dtype != PKV_F16 && q_dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: q dtype %s", who, dtype_name(q_dtype));
+  if (kv_dtype != q_dtype && !has_scales(kv_dtype))
+    return fail(PKV_ERR_UNSUPPORTED, "%s: kv dtype %s with q dtype %s", who,
+                dtype_name(kv_dtype), dtype_name(q_dtype));
+  const int32_t policy = algo & (PKV_KV_STREAM | PKV_KV_CACHED);
+  const int32_t base = algo & ~(PKV_KV_STREAM | PKV_KV_CACHED | PKV_MERGE_IN_KERNEL);
+  if (base < PKV_ALGO_AUTO || base > PKV_ALGO_MFMA || policy == (PKV_KV_STREAM | PKV_KV_CACHED))
+    return fail(PKV_ERR_INVALID, "%s: unknown algo %d", who, algo);
+  const int group = num_q_heads / num_kv_heads;
+  if (base == PKV_ALGO_MFMA && !use_mfma(base, q_dtype, group))
+    return fail(PKV_ERR_UNSUPPORTED, "%s: MFMA path needs 16-bit q and a group of at most 16",
+                who);
+  // the launch's choice of load policy and kernel
+  const double pool_bytes =
+      2.0 * num_blocks * num_kv_heads * block_size * static_cast<double>(row_bytes(kv_dtype, head_dim));
+  const bool nt = policy == PKV_KV_STREAM ||
+                  (policy == 0 && pool_bytes > static_cast<double>(PKV_KV_CACHE_BYTES));
+  int per_cu = 0, per_partition = 0, min_tokens = kMinAutoPartition;
+  pkv_status st;
+  if (use_mfma(base, q_dtype, group)) {
+    st = decode_mfma_occupancy(q_dtype, kv_dtype, head_dim, nt, &per_cu);
+    per_partition = num_kv_heads;
+  } else {
+    // the variant of the largest partitions (the 16-wave kernel where it
+    // applies, which runs only from its own minimum partition up)
+    int heads = 1, wide_min = 0;
+    st = decode_wave_occupancy(q_dtype, kv_dtype, head_dim, group, INT32_MAX, nt, &per_cu, &heads,
+                               &wide_min);
+    per_partition = num_q_heads / heads;
+    min_tokens = std::max(min_tokens, wide_min);
+  }
+  if (st) return st;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return fail(PKV_ERR_DEVICE, "%s: %s", who, hipGetErrorString(e));
+  if (per_cu <= 0 || cus <= 0)
+    return fail(PKV_ERR_DEVICE, "%s: the decode kernel does not fit a compute unit", who);
+  return pkv_decode_partition_for_capacity(context_lens, num_seqs, per_partition,
+                                           static_cast<int64_t>(per_cu) * cus, min_tokens,
+                                           partition_tokens);
 }
 
 pkv_status pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void* q,

@@ -89,17 +89,74 @@ __device__ __forceinline__ void row_context(const AttnArgs& a, int row, int& seq
 // as the slow index, concurrent reads all sit at one offset modulo the
 // block stride and crowd a few channels: on MI355X that costs about a
 // quarter of the bandwidth.)
+//
+// A split decode launch (one row per sequence, several partitions) sizes
+// its grid by the longest context, so shorter rows leave workgroups with no
+// keys.  Those exit, but only once their first loads return, which under
+// a full memory system takes microseconds: placed among the rows they
+// would hold slots that later partitions wait for.  So the grid lists the
+// used (row, partition) pairs first, row by row, and the empty workgroups
+// after all of them.  Each wave finds its pair from the partition counts of
+// all rows (a prefix sum over the context lengths, 256 rows per round of
+// loads); `row` is -1 for an empty workgroup.
 
 struct WgCoord {
   int row, part, hg;
 };
-__device__ __forceinline__ WgCoord wg_coord(int ngroups, int num_parts) {
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(v, d);
+    if (lane >= d) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ WgCoord wg_coord(const AttnArgs& a, int ngroups) {
   WgCoord c;
   const int bid = blockIdx.x;
   c.hg = bid % ngroups;
-  const int rest = bid / ngroups;
-  c.part = rest % num_parts;
-  c.row = rest / num_parts;
+  const int idx = bid / ngroups;
+  if (a.num_parts <= 1 || a.qsl != nullptr) {
+    c.part = idx % a.num_parts;
+    c.row = idx / a.num_parts;
+    return c;
+  }
+  const int lane = threadIdx.x & 63;
+  const int cap = min(a.max_ctx, a.max_blocks << (4 + a.bs_shift));   // as row_ctx
+  const int pt = a.part_tokens;
+  int base = 0;   // partitions of the rows before this round
+  for (int r0 = 0; r0 < a.num_rows; r0 += 256) {
+    int n[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = r0 + 64 * j + lane;
+      n[j] = r < a.num_rows ? a.lens[r] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // partitions of each row (a row with no keys still takes one, which
+      // writes its zero output)
+      const int cnt = n[j] < 0 ? 0 : max(1, (max(0, min(n[j], cap)) + pt - 1) / pt);
+      const int incl = wave_incl_scan(cnt);
+      // lane reads: the branch and the results are the same on every lane,
+      // so they stay in scalar registers, as do the addresses derived from
+      // them (read through a lane shuffle they would not)
+      const int total = __builtin_amdgcn_readlane(incl, 63);
+      if (idx < base + total) {
+        const unsigned long long hit = __ballot(base + incl > idx);
+        const int l = __ffsll(hit) - 1;
+        c.row = r0 + 64 * j + l;
+        c.part = idx - base - __builtin_amdgcn_readlane(incl - cnt, l);
+        return c;
+      }
+      base += total;
+    }
+  }
+  c.row = -1;
+  c.part = 0;
   return c;
 }
 

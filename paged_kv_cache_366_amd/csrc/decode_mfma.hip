@@ -146,7 +146,8 @@ __attribute__((amdgpu_waves_per_eu(KT::bits == 16 ? PKV_MFMA_WPE16 : 1))) void d
   const int r16 = lane & 15;   // head (B/D operand column) or token / dim row (A operand)
   const int kg = lane >> 4;
 
-  const WgCoord wc = wg_coord(a.hkv, a.num_parts);
+  const WgCoord wc = wg_coord(a, a.hkv);
+  if (wc.row < 0) return;   // past every row's partitions
   const int part = wc.part;
   const int row = wc.row;
   const int kvh = wc.hg;
@@ -562,23 +563,36 @@ __attribute__((amdgpu_waves_per_eu(KT::bits == 16 ? PKV_MFMA_WPE16 : 1))) void d
   }
 }
 
-template <typename QT, typename KT, bool NTV>
-void launch_nt(const AttnArgs& a, int D, int group, hipStream_t st) {
-  dim3 grid(a.num_parts * a.num_rows * a.hkv);
-  if (D == 64)
-    hipLaunchKernelGGL((decode_mfma_kernel<QT, KT, 64, NTV>), grid, dim3(64 * mfma_waves<KT>()), 0, st, a, group);
-  else
-    hipLaunchKernelGGL((decode_mfma_kernel<QT, KT, 128, NTV>), grid, dim3(64 * mfma_waves<KT>()), 0, st, a, group);
-}
+// The kernel one launch runs: one workgroup of mfma_waves<KT>() waves per
+// (partition, row, KV head).
+struct MfmaKernel {
+  const void* fn;
+  int threads;
+};
 
 template <typename QT, typename KT>
-pkv_status launch_qk(const AttnArgs& a, int D, int group, hipStream_t st) {
-  if (a.stream_kv)
-    launch_nt<QT, KT, true>(a, D, group, st);
-  else
-    launch_nt<QT, KT, false>(a, D, group, st);
-  PKV_LAUNCH_CHECK("paged attention (MFMA)");
-  return PKV_OK;
+MfmaKernel pick_qk(int D, bool nt) {
+  constexpr int threads = 64 * mfma_waves<KT>();
+  if (nt)
+    return {D == 64 ? reinterpret_cast<const void*>(&decode_mfma_kernel<QT, KT, 64, true>)
+                    : reinterpret_cast<const void*>(&decode_mfma_kernel<QT, KT, 128, true>),
+            threads};
+  return {D == 64 ? reinterpret_cast<const void*>(&decode_mfma_kernel<QT, KT, 64, false>)
+                  : reinterpret_cast<const void*>(&decode_mfma_kernel<QT, KT, 128, false>),
+          threads};
+}
+
+// Null fn for a q type the matrix-core path does not take.
+MfmaKernel pick_mfma(pkv_dtype q_dt, pkv_dtype kv_dt, int D, bool nt) {
+  if (q_dt == PKV_BF16)
+    return kv_dt == PKV_I8   ? pick_qk<BF16, I8>(D, nt)
+           : kv_dt == PKV_I4 ? pick_qk<BF16, I4>(D, nt)
+                             : pick_qk<BF16, BF16>(D, nt);
+  if (q_dt == PKV_F16)
+    return kv_dt == PKV_I8   ? pick_qk<F16, I8>(D, nt)
+           : kv_dt == PKV_I4 ? pick_qk<F16, I4>(D, nt)
+                             : pick_qk<F16, F16>(D, nt);
+  return {nullptr, 0};
 }
 
 }  // namespace
@@ -586,15 +600,29 @@ pkv_status launch_qk(const AttnArgs& a, int D, int group, hipStream_t st) {
 pkv_status launch_decode_mfma(const AttnArgs& a, pkv_dtype q_dt, pkv_dtype kv_dt, int D,
                               int group, hipStream_t st) {
   if (group > 16) return fail(PKV_ERR_UNSUPPORTED, "MFMA decode: group %d > 16", group);
-  if (q_dt == PKV_BF16)
-    return kv_dt == PKV_I8   ? launch_qk<BF16, I8>(a, D, group, st)
-           : kv_dt == PKV_I4 ? launch_qk<BF16, I4>(a, D, group, st)
-                             : launch_qk<BF16, BF16>(a, D, group, st);
-  if (q_dt == PKV_F16)
-    return kv_dt == PKV_I8   ? launch_qk<F16, I8>(a, D, group, st)
-           : kv_dt == PKV_I4 ? launch_qk<F16, I4>(a, D, group, st)
-                             : launch_qk<F16, F16>(a, D, group, st);
-  return fail(PKV_ERR_UNSUPPORTED, "MFMA decode needs 16-bit q");
+  const MfmaKernel k = pick_mfma(q_dt, kv_dt, D, a.stream_kv != 0);
+  if (k.fn == nullptr) return fail(PKV_ERR_UNSUPPORTED, "MFMA decode needs 16-bit q");
+  AttnArgs args = a;
+  int grp = group;
+  void* params[] = {&args, &grp};
+  const hipError_t e = hipLaunchKernel(k.fn, dim3(a.num_parts * a.num_rows * a.hkv),
+                                       dim3(k.threads), params, 0, st);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PKV_ERR_DEVICE, "paged attention (MFMA) launch failed: %s", hipGetErrorString(e));
+  }
+  PKV_LAUNCH_CHECK("paged attention (MFMA)");
+  return PKV_OK;
+}
+
+pkv_status decode_mfma_occupancy(pkv_dtype q_dt, pkv_dtype kv_dt, int D, bool nt, int* wg_per_cu) {
+  const MfmaKernel k = pick_mfma(q_dt, kv_dt, D, nt);
+  if (k.fn == nullptr) return fail(PKV_ERR_UNSUPPORTED, "MFMA decode needs 16-bit q");
+  int n = 0;
+  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k.fn, k.threads, 0);
+  if (e != hipSuccess) return fail(PKV_ERR_DEVICE, "MFMA decode occupancy: %s", hipGetErrorString(e));
+  *wg_per_cu = n;
+  return PKV_OK;
 }
 
 }  // namespace pkv

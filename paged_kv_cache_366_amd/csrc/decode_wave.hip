@@ -146,7 +146,8 @@ __global__ __launch_bounds__(64 * NW) void decode_wave_kernel(AttnArgs a) {
   static_assert(C >= 4 && C <= 64 && NL >= 1, "unsupported head_dim / dtype");
   constexpr bool kScaled = (KT::bits <= 8);     // codes with per-tile scales
 
-  const WgCoord wc = wg_coord(a.hq / G, a.num_parts);
+  const WgCoord wc = wg_coord(a, a.hq / G);
+  if (wc.row < 0) return;   // past every row's partitions
   const int part = wc.part;
   const int row = wc.row;
   const int hbase = wc.hg * G;                        // first query head
@@ -534,64 +535,93 @@ constexpr int max_wave_heads() {
   return KT::bits <= 8 ? 2 : 4;
 }
 
+// The kernel one launch runs: heads per workgroup are the largest of 4, 2
+// and 1 that divides the group, capped by max_wave_heads; one head of
+// streamed 16-bit K/V with partitions of at least kWideMinTokens runs the
+// 16-wave kernel.
+struct WaveKernel {
+  const void* fn;
+  int threads;
+  int heads;   // query heads per workgroup
+};
+
 template <typename QT, typename KT, int D, bool NT>
-pkv_status launch_d(const AttnArgs& a, int group, hipStream_t st) {
-  // Heads per workgroup: the largest of 4, 2 and 1 that divides the group,
-  // capped by max_wave_heads.
+WaveKernel pick_d(int group, int part_tokens) {
   int gw = 1;
   for (int c : {4, 2}) if (c <= max_wave_heads<KT>() && group % c == 0) { gw = c; break; }
-  dim3 grid(a.num_parts * a.num_rows * (a.hq / gw));
-  const dim3 wg(64 * kWavesDefault);
-  switch (gw) {
-    case 1:
-      if constexpr (KT::bits == 16 && NT) {
-        if (a.part_tokens >= kWideMinTokens) {
-          hipLaunchKernelGGL((decode_wave_kernel<QT, KT, D, 1, NT, kWavesWide>), grid,
-                             dim3(64 * kWavesWide), 0, st, a);
-          break;
-        }
-      }
-      hipLaunchKernelGGL((decode_wave_kernel<QT, KT, D, 1, NT, kWavesDefault>), grid, wg, 0, st, a);
-      break;
-    case 2: hipLaunchKernelGGL((decode_wave_kernel<QT, KT, D, 2, NT, kWavesDefault>), grid, wg, 0, st, a); break;
-    default:
-      if constexpr (max_wave_heads<KT>() >= 4)
-        hipLaunchKernelGGL((decode_wave_kernel<QT, KT, D, 4, NT, kWavesDefault>), grid, wg, 0, st, a);
-      break;
+  if (gw == 4) {
+    if constexpr (max_wave_heads<KT>() >= 4)
+      return {reinterpret_cast<const void*>(&decode_wave_kernel<QT, KT, D, 4, NT, kWavesDefault>),
+              64 * kWavesDefault, 4};
+  }
+  if (gw == 2)
+    return {reinterpret_cast<const void*>(&decode_wave_kernel<QT, KT, D, 2, NT, kWavesDefault>),
+            64 * kWavesDefault, 2};
+  if constexpr (KT::bits == 16 && NT) {
+    if (part_tokens >= kWideMinTokens)
+      return {reinterpret_cast<const void*>(&decode_wave_kernel<QT, KT, D, 1, NT, kWavesWide>),
+              64 * kWavesWide, 1};
+  }
+  return {reinterpret_cast<const void*>(&decode_wave_kernel<QT, KT, D, 1, NT, kWavesDefault>),
+          64 * kWavesDefault, 1};
+}
+
+template <typename QT, typename KT>
+WaveKernel pick_qk(int D, int group, int part_tokens, bool nt) {
+  if (!nt)
+    return D == 64 ? pick_d<QT, KT, 64, false>(group, part_tokens)
+                   : pick_d<QT, KT, 128, false>(group, part_tokens);
+  return D == 64 ? pick_d<QT, KT, 64, true>(group, part_tokens)
+                 : pick_d<QT, KT, 128, true>(group, part_tokens);
+}
+
+WaveKernel pick_wave(pkv_dtype q_dt, pkv_dtype kv_dt, int D, int group, int part_tokens, bool nt) {
+  if (kv_dt == PKV_I8) {
+    if (q_dt == PKV_BF16) return pick_qk<BF16, I8>(D, group, part_tokens, nt);
+    if (q_dt == PKV_F16) return pick_qk<F16, I8>(D, group, part_tokens, nt);
+    return pick_qk<F32, I8>(D, group, part_tokens, nt);
+  }
+  if (kv_dt == PKV_I4) {
+    if (q_dt == PKV_BF16) return pick_qk<BF16, I4>(D, group, part_tokens, nt);
+    if (q_dt == PKV_F16) return pick_qk<F16, I4>(D, group, part_tokens, nt);
+    return pick_qk<F32, I4>(D, group, part_tokens, nt);
+  }
+  if (q_dt == PKV_BF16) return pick_qk<BF16, BF16>(D, group, part_tokens, nt);
+  if (q_dt == PKV_F16) return pick_qk<F16, F16>(D, group, part_tokens, nt);
+  return pick_qk<F32, F32>(D, group, part_tokens, nt);
+}
+
+}  // namespace
+
+// Decode reads every K/V tile once, so its loads carry the non-temporal
+// hint and stream through L2 (a.stream_kv); the fp32 prefill rows of one
+// chunk read the same keys, so those loads are cached.
+pkv_status launch_decode_wave(const AttnArgs& a, pkv_dtype q_dt, pkv_dtype kv_dt, int D,
+                              int group, hipStream_t st) {
+  const WaveKernel k = pick_wave(q_dt, kv_dt, D, group, a.part_tokens, a.stream_kv != 0);
+  AttnArgs args = a;
+  void* params[] = {&args};
+  const hipError_t e = hipLaunchKernel(k.fn, dim3(a.num_parts * a.num_rows * (a.hq / k.heads)),
+                                       dim3(k.threads), params, 0, st);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PKV_ERR_DEVICE, "paged attention (wavefront) launch failed: %s", hipGetErrorString(e));
   }
   PKV_LAUNCH_CHECK("paged attention (wavefront)");
   return PKV_OK;
 }
 
-// Decode reads every K/V tile once, so its loads carry the non-temporal
-// hint and stream through L2; the fp32 prefill rows of one chunk read the
-// same keys, so those loads are cached.
-template <typename QT, typename KT>
-pkv_status launch_qk(const AttnArgs& a, int D, int group, hipStream_t st) {
-  if (!a.stream_kv)
-    return D == 64 ? launch_d<QT, KT, 64, false>(a, group, st)
-                   : launch_d<QT, KT, 128, false>(a, group, st);
-  return D == 64 ? launch_d<QT, KT, 64, true>(a, group, st)
-                 : launch_d<QT, KT, 128, true>(a, group, st);
-}
-
-}  // namespace
-
-pkv_status launch_decode_wave(const AttnArgs& a, pkv_dtype q_dt, pkv_dtype kv_dt, int D,
-                              int group, hipStream_t st) {
-  if (kv_dt == PKV_I8) {
-    if (q_dt == PKV_BF16) return launch_qk<BF16, I8>(a, D, group, st);
-    if (q_dt == PKV_F16) return launch_qk<F16, I8>(a, D, group, st);
-    return launch_qk<F32, I8>(a, D, group, st);
-  }
-  if (kv_dt == PKV_I4) {
-    if (q_dt == PKV_BF16) return launch_qk<BF16, I4>(a, D, group, st);
-    if (q_dt == PKV_F16) return launch_qk<F16, I4>(a, D, group, st);
-    return launch_qk<F32, I4>(a, D, group, st);
-  }
-  if (q_dt == PKV_BF16) return launch_qk<BF16, BF16>(a, D, group, st);
-  if (q_dt == PKV_F16) return launch_qk<F16, F16>(a, D, group, st);
-  return launch_qk<F32, F32>(a, D, group, st);
+pkv_status decode_wave_occupancy(pkv_dtype q_dt, pkv_dtype kv_dt, int D, int group,
+                                 int part_tokens, bool nt, int* wg_per_cu, int* heads_per_wg,
+                                 int* min_part_tokens) {
+  const WaveKernel k = pick_wave(q_dt, kv_dt, D, group, part_tokens, nt);
+  *min_part_tokens = k.threads == 64 * kWavesWide ? kWideMinTokens : 0;
+  int n = 0;
+  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k.fn, k.threads, 0);
+  if (e != hipSuccess) return fail(PKV_ERR_DEVICE, "wavefront decode occupancy: %s", hipGetErrorString(e));
+  *wg_per_cu = n;
+  *heads_per_wg = k.heads;
+  return PKV_OK;
 }
 
 }  // namespace pkv

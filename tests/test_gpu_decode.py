@@ -139,6 +139,38 @@ def test_gqa_matches_oracle(gqa, algo, int8):
         assert err <= TOL16, (parts, err)
 
 
+@pytest.mark.parametrize("algo", [WAVE, MFMA], ids=["wave", "mfma"])
+@pytest.mark.parametrize("int8", [False, True], ids=["bf16", "int8"])
+def test_chosen_partition_matches_oracle(gqa, algo, int8):
+    """The partition the library picks for these lengths (3 rows x 2 KV
+    heads fill no round, so the 256-token floor) and a decode run with it."""
+    c, d16, d8 = gqa
+    d = d8 if int8 else d16
+    p = pkv.pkv_decode_partition_tokens(
+        c.context_lens, pkv.PKV_BF16, pkv.PKV_I8 if int8 else pkv.PKV_BF16, c.q.shape[1], c.kv_heads,
+        c.head_dim, c.block_size, c.num_blocks, algo)
+    assert p == 256, p
+    out = d.decode(parts=p, algo=algo)
+    assert np.abs(out_f64(out) - oracle_decode(c, int8=int8)).max() <= TOL16
+
+
+def test_chosen_partition_shapes():
+    """Long-context GQA lengths: one round of the matrix-core kernel's
+    resident workgroups (16 tokens less would not fit in it); the 7B-shape
+    MHA batch needs several rounds unsplit, so no split."""
+    lens = np.random.default_rng(4).integers(8192, 32768 + 1, size=16)
+    props = torch.cuda.get_device_properties(0)
+    for kv in (pkv.PKV_BF16, pkv.PKV_I8, pkv.PKV_I4):
+        p = pkv.pkv_decode_partition_tokens(lens, pkv.PKV_BF16, kv, 64, 8, 128, 16, 30000)
+        n = 8 * sum(-(-int(x) // p) for x in lens)
+        n16 = 8 * sum(-(-int(x) // (p - 16)) for x in lens)
+        # resident workgroups per compute unit: at least one, at most 32
+        assert p % 16 == 0 and n <= 32 * props.multi_processor_count and n16 > n, (kv, p)
+        print(f"kv {kv}: partition {p}, {n} workgroups")
+    assert pkv.pkv_decode_partition_tokens([2048] * 64, pkv.PKV_BF16, pkv.PKV_BF16, 32, 32, 128,
+                                           16, 10000, pkv.PKV_KV_STREAM) == 0
+
+
 def bf16_out_ok(ob, of, ref):
     """A bf16 output run: bit for bit the round-to-nearest-even of the fp32
     run, and within the oracle bar plus half a bf16 ulp of the reference."""

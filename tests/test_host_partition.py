@@ -1,0 +1,80 @@
+"""The decode partition choice on the host: the shortest partition whose
+workgroups fit in the whole rounds of resident workgroups the launch needs
+without a split.  Checked against a brute-force search over every multiple
+of 16, hand-worked cases and its argument checks (no GPU needed)."""
+import numpy as np
+import pytest
+
+import paged_kv_cache_366_amd as pkv
+
+
+def wgs(lens, p, per_part):
+    return per_part * sum(-(-int(n) // p) for n in lens)
+
+
+def brute(lens, per_part, resident, min_tokens):
+    """Every multiple of 16 from the floor up to one partition per context."""
+    mx = max([int(n) for n in lens] + [0])
+    cap = -(-mx // 16) * 16
+    lo = max(16, -(-min_tokens // 16) * 16)
+    if mx == 0 or lo >= cap:
+        return 0
+    target = -(-wgs(lens, cap, per_part) // resident) * resident
+    for p in range(lo, cap + 1, 16):
+        if wgs(lens, p, per_part) <= target:
+            return 0 if p >= cap else p
+    raise AssertionError("the unsplit launch always fits its own rounds")
+
+
+def test_hand_worked_cases():
+    # one 4,096-token context, 8 workgroups per partition, 64 resident: one
+    # round holds 8 partitions of 512 tokens
+    assert pkv.pkv_decode_partition_for_capacity([4096], 8, 64, 256) == 512
+    # 65 resident still gives 512 (9 partitions of 456 would need 72)
+    assert pkv.pkv_decode_partition_for_capacity([4096], 8, 65, 256) == 512
+    # 63 resident: 8 partitions do not fit, so 7 (586 tokens -> 592)
+    assert pkv.pkv_decode_partition_for_capacity([4096], 8, 63, 256) == 592
+    # the floor: 1,000 resident would allow 16-token partitions
+    assert pkv.pkv_decode_partition_for_capacity([4096], 8, 1000, 256) == 256
+    # more than one round without a split (64 x 32 workgroups, 256
+    # resident): any split only adds workgroups, so no split
+    assert pkv.pkv_decode_partition_for_capacity([2048] * 64, 32, 256, 256) == 0
+    # two contexts of 3,000 and 1,000, 4 per partition, 20 resident: at most
+    # 5 partitions; below 1,000 tokens the contexts take at least 4 + 2, so
+    # the least multiple of 16 from 1,000 up (3 + 1 partitions)
+    assert wgs([3000, 1000], 1008, 4) <= 20 < wgs([3000, 1000], 992, 4)
+    assert pkv.pkv_decode_partition_for_capacity([3000, 1000], 4, 20, 256) == 1008
+    # nothing to split
+    assert pkv.pkv_decode_partition_for_capacity([], 8, 64, 256) == 0
+    assert pkv.pkv_decode_partition_for_capacity([0, 0], 8, 64, 256) == 0
+    assert pkv.pkv_decode_partition_for_capacity([200], 8, 64, 256) == 0   # shorter than the floor
+
+
+def test_long_context_grouped_query_shape():
+    """16 contexts U[8192, 32768] (the long-context workload's seed), 8 KV
+    heads: the chosen partition fills one round and 16 tokens less would
+    not fit."""
+    lens = np.random.default_rng(4).integers(8192, 32768 + 1, size=16)
+    for resident in (2048, 768, 2560):
+        p = pkv.pkv_decode_partition_for_capacity(lens, 8, resident, 256)
+        assert p % 16 == 0 and p >= 256
+        assert wgs(lens, p, 8) <= resident < wgs(lens, p - 16, 8)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_matches_brute_force(seed):
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(0, 40))
+    hi = int(rng.choice([16, 300, 2048, 20000]))
+    lens = rng.integers(0, hi + 1, size=n)
+    per_part = int(rng.choice([1, 2, 8, 32]))
+    resident = int(rng.integers(1, 3000))
+    min_tokens = int(rng.choice([0, 15, 256, 1024]))
+    got = pkv.pkv_decode_partition_for_capacity(lens, per_part, resident, min_tokens)
+    assert got == brute(lens, per_part, resident, min_tokens)
+
+
+def test_argument_checks():
+    for args in (([-1, 5], 8, 64, 0), ([5], 0, 64, 0), ([5], 8, 0, 0), ([5], 8, 64, -1)):
+        with pytest.raises(pkv.PkvError):
+            pkv.pkv_decode_partition_for_capacity(*args)
