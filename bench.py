@@ -77,20 +77,22 @@ PAGE_ALLOC_P99_BAR_US = 1000.0   # cnnetsun.cn section 4.2: page allocation P99 
 # profile that records the counts.  Valid only while the kernel sources hash
 # to the measured value; a changed kernel reports null.
 # HBM bytes per step of the dominant kernel(s), from rocprofv3 counter runs:
-# FETCH_SIZE scaled by 1 / 0.500042 (a 1 GiB torch.bitwise_not in the same
-# process reads as 524,332 KiB) plus WRITE_SIZE (exact for the same copy).
+# FETCH_SIZE scaled by 1 / 0.500041 (a 1 GiB torch.bitwise_not in the same
+# process reads as 524,331 KiB) plus WRITE_SIZE (exact for the same copy).
 # Reported only while the kernel sources hash to the value they were taken on.
-_SHA = "6a691601fda9b7b010b28034fa61c1b4ca59d8ef"
+_SHA = "48a7bfeeda972577605a85c2fcc2a94dcc1cd622"
 TRAFFIC = {
-    "decode7b": {"bytes_per_launch": 1120468938, "sources_sha1": _SHA, "partition_tokens": 2048,
+    "decode7b": {"bytes_per_launch": 1120495643, "sources_sha1": _SHA, "partition_tokens": 2048,
                  "profile": "profiles/decode_wave_7b_bf16_p2048_step_kernel_trace.md"},
-    "gqa-bf16": {"bytes_per_launch": 1565989434, "sources_sha1": _SHA, "partition_tokens": 1024,
-                 "profile": "profiles/decode_mfma_gqa_long_bf16_p1024_kernel_trace.md"},
-    "gqa-int8": {"bytes_per_launch": 842334440, "sources_sha1": _SHA, "partition_tokens": 1024,
-                 "profile": "profiles/decode_mfma_gqa_long_int8_p1024_kernel_trace.md"},
+    "gqa-bf16": {"bytes_per_launch": 1546619152, "sources_sha1": _SHA, "partition_tokens": 4272,
+                 "profile": "profiles/decode_mfma_gqa_long_bf16_kernel_trace.md"},
+    "gqa-int8": {"bytes_per_launch": 833862181, "sources_sha1": _SHA, "partition_tokens": 1504,
+                 "profile": "profiles/decode_mfma_gqa_long_int8_kernel_trace.md"},
+    "gqa-int4": {"bytes_per_launch": 447133485, "sources_sha1": _SHA, "partition_tokens": 1504,
+                 "profile": "profiles/decode_mfma_gqa_long_int4_kernel_trace.md"},
 }
-KERNEL_SOURCES = ("decode_wave.hip", "decode_mfma.hip", "attention_common.h", "device_common.h",
-                  "mfma_common.h")
+KERNEL_SOURCES = ("decode_wave.hip", "decode_mfma.hip", "reduce.hip", "attention_common.h",
+                  "device_common.h", "mfma_common.h")
 
 
 def kernel_sources_sha1() -> str:
