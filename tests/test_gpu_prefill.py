@@ -219,9 +219,16 @@ def test_mixed_step_full_size_sampled():
     # 48 decode sequences (contexts U[64, 4096]) and four 512-row chunks over
     # 0/512/1024/1536 cached tokens, 32 heads x 128, bf16
     ms = W.mixed_step(seed=2)
-    # 1,024-token partitions are the step's timed launch shape (its 1.6 GB
-    # pool streams, so the wavefront kernel runs 16-wave workgroups)
-    run_mixed_step(ms, sample_rows=6, decode_parts=(256, 1024))
+    # the step's timed launch shape: the library's partition for these
+    # decode lengths (one partition per context: the 1,536 workgroups need
+    # several rounds unsplit); its 1.6 GB pool streams, so the wavefront
+    # kernel runs 16-wave workgroups.  Plus a split at 256 tokens.
+    dec = ms.new == 1
+    timed = pkv.pkv_decode_partition_tokens(
+        (ms.prior + ms.new)[dec], pkv.PKV_BF16, pkv.PKV_BF16, ms.q_heads, ms.kv_heads,
+        ms.head_dim, W.BLOCK_SIZE, ms.num_blocks)
+    assert timed == 0, timed
+    run_mixed_step(ms, sample_rows=6, decode_parts=(256, timed))
 
 
 # ------------------------------------------------------------ split-K prefill
