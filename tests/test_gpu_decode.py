@@ -171,6 +171,32 @@ def test_chosen_partition_shapes():
                                            16, 10000, pkv.PKV_KV_STREAM) == 0
 
 
+@pytest.mark.parametrize("algo", [WAVE, MFMA], ids=["wave", "mfma"])
+def test_split_grid_over_many_rows(algo):
+    """A split launch lists the used (row, partition) pairs first and each
+    workgroup finds its pair from a scan of every row's length, 256 rows per
+    round of loads: 600 rows of ragged lengths (empty rows, one-token rows,
+    lengths on partition boundaries) take three rounds.  Against the oracle,
+    and within fp32 reassociation of the unsplit launch."""
+    rng = np.random.default_rng(302)
+    lens = rng.integers(1, 900, size=600)
+    lens[rng.choice(600, 40, replace=False)] = 0
+    lens[rng.choice(600, 40, replace=False)] = 1
+    lens[rng.choice(600, 40, replace=False)] = 256
+    lens[599] = 899
+    c = W.decode_case(301, 600, 8, 2, 64, lens=lens.tolist(), dtype="bf16")
+    d = DevCase(c)
+    ref = oracle_decode(c)
+    base = d.decode(parts=0, algo=algo)
+    assert np.abs(out_f64(base) - ref).max() <= TOL16
+    for parts in (16, 64, 256):
+        out = d.decode(parts=parts, algo=algo)
+        got = out_f64(out)
+        assert np.abs(got - ref).max() <= TOL16, parts
+        assert np.abs(got - out_f64(base)).max() <= 1e-5, parts
+        assert np.all(got[lens == 0] == 0.0), parts
+
+
 def bf16_out_ok(ob, of, ref):
     """A bf16 output run: bit for bit the round-to-nearest-even of the fp32
     run, and within the oracle bar plus half a bf16 ulp of the reference."""
