@@ -62,11 +62,12 @@
 //   and lo = p - hi rounded, which keeps about 16 mantissa bits at the cost
 //   of a second MFMA per product; decode is HBM-bound, so it is free.
 // The workgroup's wavefronts take the partition's tiles round-robin and
-// merge through LDS at the end.  16-bit KV: two tiles loaded, then both
-// computed.  Codes: each wave issues the loads of its next tile before it
-// computes the current one (two register buffers; about 1.5% faster for
-// int8 and 4-bit; for 16-bit KV the second buffer costs a wave per SIMD
-// and measured no faster).
+// merge through LDS at the end.  Each wave issues the loads of its next
+// tile before it computes the current one (two register buffers).  For
+// 16-bit KV the second buffer costs a wave per SIMD (172 VGPRs: two
+// workgroups per compute unit instead of three); with the grid sized to
+// one round of resident workgroups that measured 4% faster (long-context
+// GQA 257-260 -> 248 us) than loading two tiles and then computing both.
 #include <type_traits>
 
 #include "attention_common.h"
@@ -92,7 +93,7 @@ constexpr int mfma_waves() {
 // Tiles per load group (a wave computes one group while the next is in
 // flight), by storage width.
 #ifndef PKV_MFMA_UNROLL16
-#define PKV_MFMA_UNROLL16 2
+#define PKV_MFMA_UNROLL16 1
 #endif
 #ifndef PKV_MFMA_UNROLL_CODES
 #define PKV_MFMA_UNROLL_CODES 1
@@ -104,7 +105,7 @@ constexpr int mfma_unroll() {
 // Whether a wave issues the next group's loads before computing the current
 // one (two register buffers), by storage width.
 #ifndef PKV_MFMA_PIPE16
-#define PKV_MFMA_PIPE16 0
+#define PKV_MFMA_PIPE16 1
 #endif
 #ifndef PKV_MFMA_PIPE_CODES
 #define PKV_MFMA_PIPE_CODES 1
