@@ -95,12 +95,18 @@ constexpr int mfma_waves() {
 #ifndef PKV_MFMA_UNROLL16
 #define PKV_MFMA_UNROLL16 1
 #endif
+// int8: two tiles per group (154 VGPRs, six workgroups per compute unit)
+// measured about 1.3% faster than one at one round of workgroups; 4-bit:
+// one (two measured 7% slower).
+#ifndef PKV_MFMA_UNROLL_I8
+#define PKV_MFMA_UNROLL_I8 2
+#endif
 #ifndef PKV_MFMA_UNROLL_CODES
 #define PKV_MFMA_UNROLL_CODES 1
 #endif
 template <typename KT>
 constexpr int mfma_unroll() {
-  return KT::bits == 16 ? PKV_MFMA_UNROLL16 : PKV_MFMA_UNROLL_CODES;
+  return KT::bits == 16 ? PKV_MFMA_UNROLL16 : KT::bits == 8 ? PKV_MFMA_UNROLL_I8 : PKV_MFMA_UNROLL_CODES;
 }
 // Whether a wave issues the next group's loads before computing the current
 // one (two register buffers), by storage width.
