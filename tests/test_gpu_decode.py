@@ -12,6 +12,7 @@ import torch
 
 import paged_kv_cache_366_amd as pkv
 from oracle import attention as A
+from oracle import quantize as Q
 from synth import workloads as W
 
 from gpu_common import DEV, DevCase, i32, out_f64, to_dev
@@ -152,6 +153,48 @@ def test_chosen_partition_matches_oracle(gqa, algo, int8):
     assert p == 256, p
     out = d.decode(parts=p, algo=algo)
     assert np.abs(out_f64(out) - oracle_decode(c, int8=int8)).max() <= TOL16
+
+
+@pytest.mark.parametrize("kv", ["bf16", "int8", "int4"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_chosen_partition_for_every_kv_type(kv, D):
+    """The partition the library picks for each kernel it may launch (both
+    algorithms, bf16 and fp32 q), and a decode with it, against the oracle."""
+    lens = [3000, 1, 0, 2047, 700, 4096, 33]
+    c = W.decode_case(411 + D, len(lens), 16, 2, D, lens=lens, dtype="bf16",
+                      int8=kv == "int8", int4=kv == "int4")
+    if kv == "int8":
+        k, v = torch.from_numpy(c.k_i8).to(DEV), torch.from_numpy(c.v_i8).to(DEV)
+        ks, vs = torch.from_numpy(c.k_scale).to(DEV), torch.from_numpy(c.v_scale).to(DEV)
+        ref = A.decode(c.q, c.k_i8, c.v_i8, c.block_tables, c.context_lens, c.scale,
+                       k_scale=c.k_scale, v_scale=c.v_scale)
+    elif kv == "int4":
+        k, v = torch.from_numpy(c.k_i4).to(DEV), torch.from_numpy(c.v_i4).to(DEV)
+        ks, vs = torch.from_numpy(c.k_scale4).to(DEV), torch.from_numpy(c.v_scale4).to(DEV)
+        ref = A.decode(c.q, Q.unpack_int4(c.k_i4), Q.unpack_int4(c.v_i4), c.block_tables,
+                       c.context_lens, c.scale, c.block_size, k_scale=c.k_scale4,
+                       v_scale=c.v_scale4)
+    else:
+        k, v = to_dev(c.k_cache, "bf16"), to_dev(c.v_cache, "bf16")
+        ks = vs = None
+        ref = oracle_decode(c)
+    kv_code = {"bf16": pkv.PKV_BF16, "int8": pkv.PKV_I8, "int4": pkv.PKV_I4}[kv]
+    tables, lens_d = i32(c.block_tables), i32(c.context_lens)
+    for qdt in ("bf16", "f32"):
+        if qdt == "f32" and kv == "bf16":
+            continue   # 16-bit K/V take a q of their own type
+        q = to_dev(c.q, qdt)
+        q_code = pkv.PKV_BF16 if qdt == "bf16" else pkv.PKV_F32
+        for algo in ((WAVE, MFMA) if qdt == "bf16" else (WAVE,)):
+            p = pkv.pkv_decode_partition_tokens(c.context_lens, q_code, kv_code, 16, 2, D,
+                                                c.block_size, c.num_blocks, algo)
+            assert p == 0 or (p % 16 == 0 and p >= 256), (qdt, algo, p)
+            out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+            pkv.pkv_paged_attention_decode(out, q, k, v, tables, lens_d, 4096, float(c.scale), p,
+                                           algo, ks, vs)
+            torch.cuda.synchronize()
+            err = np.abs(out_f64(out) - ref).max()
+            assert err <= TOL16, (qdt, algo, p, err)
 
 
 def test_chosen_partition_shapes():
