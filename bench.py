@@ -1339,7 +1339,7 @@ def main(argv=None) -> int:
                          "(a known-size kernel for scaling rocprofv3 byte counters)")
     a = ap.parse_args(argv)
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {a.gpus}); this build has no "
+        print(f"bench.py runs on one GPU only (asked for {a.gpus}); the library has no "
               "multi-GPU mode", file=sys.stderr)
         return 2
     a.partition_set = a.partition is not None

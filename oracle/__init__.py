@@ -1,6 +1,6 @@
 """CPU oracle for paged attention — TEST INFRASTRUCTURE ONLY.
 
-Only the tests, the graft smoke check and the benchmark's CPU-baseline leg may
+Only the tests, `__graft_entry__.smoke()` and the benchmark's CPU-baseline leg may
 import this package.  The product path (the HIP library and its binding) never
 imports, links or calls it, and this package never imports the product path.
 
