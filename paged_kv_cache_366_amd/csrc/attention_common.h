@@ -98,11 +98,15 @@ __device__ __forceinline__ void row_context(const AttnArgs& a, int row, int& seq
 // used (row, partition) pairs first, row by row, and the empty workgroups
 // after all of them.  Each wave finds its pair from the partition counts of
 // all rows (a prefix sum over the context lengths, 256 rows per round of
-// loads); `row` is -1 for an empty workgroup.
+// loads); `row` is -1 for an empty workgroup.  Past kCompactRowsMax rows the
+// scan would cost every workgroup more dependent loads than the empty ones
+// cost, so such launches keep the direct map (the library's partition
+// choice splits only batches far smaller).
 
 struct WgCoord {
   int row, part, hg;
 };
+constexpr int kCompactRowsMax = 1024;
 
 __device__ __forceinline__ int wave_incl_scan(int v) {
   const int lane = threadIdx.x & 63;
@@ -119,7 +123,7 @@ __device__ __forceinline__ WgCoord wg_coord(const AttnArgs& a, int ngroups) {
   const int bid = blockIdx.x;
   c.hg = bid % ngroups;
   const int idx = bid / ngroups;
-  if (a.num_parts <= 1 || a.qsl != nullptr) {
+  if (a.num_parts <= 1 || a.qsl != nullptr || a.num_rows > kCompactRowsMax) {
     c.part = idx % a.num_parts;
     c.row = idx / a.num_parts;
     return c;

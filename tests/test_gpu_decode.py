@@ -214,20 +214,23 @@ def test_chosen_partition_shapes():
                                            16, 10000, pkv.PKV_KV_STREAM) == 0
 
 
+@pytest.mark.parametrize("rows", [600, 1100])
 @pytest.mark.parametrize("algo", [WAVE, MFMA], ids=["wave", "mfma"])
-def test_split_grid_over_many_rows(algo):
+def test_split_grid_over_many_rows(algo, rows):
     """A split launch lists the used (row, partition) pairs first and each
     workgroup finds its pair from a scan of every row's length, 256 rows per
     round of loads: 600 rows of ragged lengths (empty rows, one-token rows,
-    lengths on partition boundaries) take three rounds.  Against the oracle,
-    and within fp32 reassociation of the unsplit launch."""
-    rng = np.random.default_rng(302)
-    lens = rng.integers(1, 900, size=600)
-    lens[rng.choice(600, 40, replace=False)] = 0
-    lens[rng.choice(600, 40, replace=False)] = 1
-    lens[rng.choice(600, 40, replace=False)] = 256
-    lens[599] = 899
-    c = W.decode_case(301, 600, 8, 2, 64, lens=lens.tolist(), dtype="bf16")
+    lengths on partition boundaries) take three rounds; past 1,024 rows the
+    launch keeps the direct map.  Against the oracle, and within fp32
+    reassociation of the unsplit launch."""
+    rng = np.random.default_rng(302 + rows)
+    hi = 900 if rows <= 1024 else 400
+    lens = rng.integers(1, hi, size=rows)
+    lens[rng.choice(rows, 40, replace=False)] = 0
+    lens[rng.choice(rows, 40, replace=False)] = 1
+    lens[rng.choice(rows, 40, replace=False)] = 256
+    lens[rows - 1] = hi - 1
+    c = W.decode_case(301, rows, 8, 2, 64, lens=lens.tolist(), dtype="bf16")
     d = DevCase(c)
     ref = oracle_decode(c)
     base = d.decode(parts=0, algo=algo)
