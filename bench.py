@@ -710,7 +710,8 @@ def bench_mixed(a, torch, pkv, algo):
     out_p = torch.empty(q_p.shape, dtype=torch.float32, device=dev)
     ws = torch.empty(max(pkv.pkv_decode_workspace_bytes(len(dec), hq, D, mc_d, part), 1),
                      dtype=torch.uint8, device=dev)
-    ppart = a.prefill_partition
+    ppart = (a.prefill_partition if a.prefill_partition is not None else
+             pkv.pkv_prefill_partition_tokens(ms.new[pre], lens[pre], hq))
     ws_p = torch.empty(max(pkv.pkv_prefill_workspace_bytes(len(rows_p), hq, D, mc_p, ppart), 1),
                        dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
@@ -791,7 +792,7 @@ def bench_mixed(a, torch, pkv, algo):
                     "U[64, 4096]) + 4 prefill chunks of 512 causal rows over 0/512/1024/1536 "
                     "cached tokens; 32 heads x 128; step = reshape_and_cache of 2096 rows + "
                     "decode + reduce + chunked prefill",
-        "partition_tokens": part, "prefill_partition_tokens": a.prefill_partition,
+        "partition_tokens": part, "prefill_partition_tokens": ppart,
         "algo": a.algo})
     result.update({
         "tokens_per_s": (len(dec) + len(rows_p)) / (ms_per_step * 1e-3),
@@ -1133,7 +1134,7 @@ def bench_prefix(a, torch, pkv, algo):
     for b in (hit, full):
         b["out"] = torch.empty(b["q"].shape, dtype=torch.float32, device=dev)
         b["ws"] = torch.empty(max(pkv.pkv_prefill_workspace_bytes(
-            b["q"].shape[0], hq, D, int(lens.max()), a.prefill_partition), 1),
+            b["q"].shape[0], hq, D, int(lens.max()), a.prefill_partition or 0), 1),
             dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     mc = int(lens.max())
@@ -1143,7 +1144,7 @@ def bench_prefix(a, torch, pkv, algo):
         pkv.pkv_reshape_and_cache(b["k"], b["v"], kc, vc, b["slots"])
         pkv.pkv_paged_attention_prefill(b["out"], b["q"], kc, vc, b["tables"], b["qsl"], b["lens"],
                                         b["max_q"], mc, float(c.scale),
-                                        partition_tokens=a.prefill_partition, workspace=b["ws"])
+                                        partition_tokens=a.prefill_partition or 0, workspace=b["ws"])
 
     def step(ev):
         if ev is not None:
@@ -1189,7 +1190,7 @@ def bench_prefix(a, torch, pkv, algo):
                     "a 1024-token system prompt already in the cache, 64-256 own tokens each; "
                     "admission = reshape_and_cache + prefill of the uncached rows, against the "
                     "same requests computed in full",
-        "requests": len(rest), "prefill_partition_tokens": a.prefill_partition})
+        "requests": len(rest), "prefill_partition_tokens": a.prefill_partition or 0})
     result.update({
         "kernel_ms": {"with_prefix_cache": h_avg, "without": f_avg},
         "speedup": f_avg / h_avg,
@@ -1222,7 +1223,10 @@ def bench_prefill_long(a, torch, pkv, algo):
     l = torch.from_numpy(c.context_lens).to(dev)
     qsl = torch.from_numpy(c.query_start_loc).to(dev)
     mc, mq = int(c.context_lens.max()), 64
-    part = a.prefill_partition or 2048
+    # the library's key partition for these chunks (split so that two
+    # workgroups per compute unit are busy), unless --prefill-partition
+    part = (a.prefill_partition if a.prefill_partition is not None else
+            pkv.pkv_prefill_partition_tokens(np.diff(c.query_start_loc), c.context_lens, hq))
     out_s = torch.empty(q.shape, dtype=torch.float32, device=dev)
     out_n = torch.empty_like(out_s)
     ws = torch.empty(max(pkv.pkv_prefill_workspace_bytes(q.shape[0], hq, D, mc, part), 1),
@@ -1324,8 +1328,10 @@ def main(argv=None) -> int:
                          "workload, the library's choice (pkv_decode_partition_tokens) for the "
                          "mixed step and the long-context GQA workloads")
     ap.add_argument("--algo", choices=("auto", "wave", "mfma"), default="auto")
-    ap.add_argument("--prefill-partition", type=int, default=0,
-                    help="key partition size of chunked prefill in tokens (0 = no split)")
+    ap.add_argument("--prefill-partition", type=int, default=None,
+                    help="key partition size of chunked prefill in tokens (0 = no split); "
+                         "default: the library's choice (pkv_prefill_partition_tokens) for the "
+                         "mixed step and long documents, no split for prefix admission")
     ap.add_argument("--block-size", type=int, default=BLOCK, choices=(16, 32, 64, 128),
                     help="KV block size of the decode7b workload (16 is the headline line)")
     ap.add_argument("--seed", type=int, default=1)

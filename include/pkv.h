@@ -608,6 +608,26 @@ pkv_status pkv_paged_attention_reduce(void* out, pkv_dtype out_dtype, const int3
 size_t pkv_prefill_workspace_bytes(int32_t num_query_tokens, int32_t num_q_heads,
                                    int32_t head_dim, int32_t max_context_len,
                                    int32_t partition_tokens);
+
+/* Key partition size for a chunked-prefill launch (host), the counterpart of
+ * pkv_decode_partition_tokens: a matrix-core prefill workgroup owns 64 query
+ * rows of one head, so sequence s takes ceil(query_lens[s] / 64) x
+ * num_q_heads workgroups per partition of its keys; the result is the
+ * shortest partition (a multiple of 16 tokens, at least 256) whose
+ * workgroups fit in the whole rounds of two resident workgroups per compute
+ * unit that the launch needs without a split, or 0 (no split).  Two, not the
+ * three the kernel's LDS allows: with three the per-step time rises more
+ * than the third workgroup adds (measured on long documents).  Many row
+ * tiles already fill the GPU unsplit (0); a few long chunks get split.
+ * fp32 q (the wavefront rows) always gets 0.
+ *   query_lens, context_lens  host int32[num_seqs]: each sequence's chunk
+ *                  length and its keys (context_lens[s] >= query_lens[s])
+ *   partition_tokens  out
+ * Errors: INVALID for NULL pointers or inconsistent lengths, UNSUPPORTED
+ * for a q dtype prefill does not take, DEVICE without a current device. */
+pkv_status pkv_prefill_partition_tokens(const int32_t* query_lens, const int32_t* context_lens,
+                                        int32_t num_seqs, int32_t num_q_heads, pkv_dtype q_dtype,
+                                        int32_t* partition_tokens);
 pkv_status pkv_paged_attention_prefill(
     void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype, const void* k_cache,
     const void* v_cache, pkv_dtype kv_dtype, const float* k_scale, const float* v_scale,

@@ -403,6 +403,20 @@ def pkv_decode_partition_tokens(context_lens, q_dtype: int, kv_dtype: int, num_q
     return out.value
 
 
+def pkv_prefill_partition_tokens(query_lens, context_lens, num_q_heads: int,
+                                 q_dtype: int = PKV_BF16) -> int:
+    """Key partition for a chunked-prefill launch on the current device (0:
+    no split); query_lens and context_lens are host sequences of lengths."""
+    ql = np.ascontiguousarray(query_lens, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    if ql.shape != cl.shape:
+        raise ValueError("query_lens and context_lens differ in length")
+    out = C.c_int32(0)
+    check(load().pkv_prefill_partition_tokens(_i32p(ql), _i32p(cl), len(ql), num_q_heads, q_dtype,
+                                              C.byref(out)))
+    return out.value
+
+
 def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
                  partition_tokens, algo, k_scale, v_scale, workspace, stream, allocate=True):
     torch = _torch()

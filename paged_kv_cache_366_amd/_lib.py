@@ -84,6 +84,7 @@ SIGNATURES = {
     "pkv_decode_partition_for_capacity": (_i32, [_pi32, _i32, _i32, _i64, _i32, _pi32]),
     "pkv_decode_partition_tokens": (_i32, [_pi32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                            _i32, _pi32]),
+    "pkv_prefill_partition_tokens": (_i32, [_pi32, _pi32, _i32, _i32, _i32, _pi32]),
     "pkv_paged_attention_decode": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp,
                                           _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                           _f32, _i32, _i32, _vp, _sz, _vp]),

@@ -21,6 +21,7 @@ pkv_status decode_wave_occupancy(pkv_dtype q_dt, pkv_dtype kv_dt, int D, int gro
                                  int part_tokens, bool nt, int* wg_per_cu, int* heads_per_wg,
                                  int* min_part_tokens);
 pkv_status decode_mfma_occupancy(pkv_dtype q_dt, pkv_dtype kv_dt, int D, bool nt, int* wg_per_cu);
+int prefill_tile_rows();
 }  // namespace pkv
 
 using namespace pkv;
@@ -31,6 +32,11 @@ constexpr size_t kAlign = 256;
 // Shortest partition the automatic choice takes: below it each workgroup's
 // start (table entries, q) and partial-state write outweigh its keys.
 constexpr int32_t kMinAutoPartition = 256;
+// Prefill workgroups per compute unit the partition choice fills: the LDS
+// staging allows three, but with three the per-step time rises more than
+// the third adds (4 long documents, 16,384 keys each: 512 workgroups
+// 202 us, 768 workgroups 212-215 us, 1,024 236-240 us).
+constexpr int kPrefillPerCu = 2;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -276,6 +282,43 @@ pkv_status scratch_address(const char* who, void** addr) {
   return PKV_OK;
 }
 
+// The shortest partition (a multiple of 16 tokens, at least min_tokens)
+// whose workgroups fit in the whole rounds of `resident` that the launch
+// needs without a split; 0 when no split fits (or nothing to split).
+// Sequence s contributes weight(s) workgroups per partition of its keys
+// (partitions past a context's end hold no slot).  The count only falls as
+// the partition grows, so a bisection over multiples of 16 finds it.
+template <typename Weight>
+int32_t partition_for_rounds(const int32_t* lens, int32_t num_seqs, Weight weight,
+                             int64_t resident, int32_t min_tokens) {
+  int32_t max_len = 0;
+  for (int32_t s = 0; s < num_seqs; ++s)
+    if (weight(s) > 0) max_len = std::max(max_len, lens[s]);
+  const int64_t cap = (static_cast<int64_t>(max_len) + 15) / 16 * 16;   // one partition per context
+  const int64_t lo = std::max<int64_t>(16, (static_cast<int64_t>(min_tokens) + 15) / 16 * 16);
+  if (max_len == 0 || lo >= cap) return 0;
+  auto wgs = [&](int64_t p) {
+    int64_t n = 0;
+    for (int32_t s = 0; s < num_seqs; ++s) n += (lens[s] + p - 1) / p * weight(s);
+    return n;
+  };
+  const int64_t rounds = (wgs(cap) + resident - 1) / resident;
+  const int64_t target = rounds * resident;
+  int64_t a = lo / 16, b = cap / 16;   // wgs(16 b) <= target; find the least such
+  while (a < b) {
+    const int64_t m = (a + b) / 2;
+    if (wgs(16 * m) <= target) b = m; else a = m + 1;
+  }
+  return 16 * a < cap ? static_cast<int32_t>(16 * a) : 0;
+}
+
+int device_compute_units(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+  return e == hipSuccess && *cus > 0 ? 0 : -1;
+}
+
 }  // namespace
 
 extern "C" {
@@ -316,33 +359,12 @@ pkv_status pkv_decode_partition_for_capacity(const int32_t* context_lens, int32_
     return fail(PKV_ERR_INVALID, "%s: bad sizes (S=%d per-partition %d resident %lld min %d)", who,
                 num_seqs, workgroups_per_partition, static_cast<long long>(resident_workgroups),
                 min_tokens);
-  int32_t max_len = 0;
-  for (int32_t s = 0; s < num_seqs; ++s) {
+  for (int32_t s = 0; s < num_seqs; ++s)
     if (context_lens[s] < 0)
       return fail(PKV_ERR_INVALID, "%s: context_lens[%d] = %d", who, s, context_lens[s]);
-    max_len = std::max(max_len, context_lens[s]);
-  }
-  *partition_tokens = 0;
-  const int64_t cap = (static_cast<int64_t>(max_len) + 15) / 16 * 16;   // one partition per context
-  const int64_t lo = std::max<int64_t>(16, (static_cast<int64_t>(min_tokens) + 15) / 16 * 16);
-  if (max_len == 0 || lo >= cap) return PKV_OK;
-  // Workgroups holding keys at partitions of p tokens (those of partitions
-  // past a context's end exit at once and hold no slot).
-  auto wgs = [&](int64_t p) {
-    int64_t n = 0;
-    for (int32_t s = 0; s < num_seqs; ++s) n += (context_lens[s] + p - 1) / p;
-    return n * workgroups_per_partition;
-  };
-  // Whole rounds the launch needs without a split; the smallest partition
-  // that still fits in them fills them the most.
-  const int64_t rounds = (wgs(cap) + resident_workgroups - 1) / resident_workgroups;
-  const int64_t target = rounds * resident_workgroups;
-  int64_t a = lo / 16, b = cap / 16;   // wgs(16 b) <= target; find the least such
-  while (a < b) {
-    const int64_t m = (a + b) / 2;
-    if (wgs(16 * m) <= target) b = m; else a = m + 1;
-  }
-  if (16 * a < cap) *partition_tokens = static_cast<int32_t>(16 * a);
+  *partition_tokens = partition_for_rounds(
+      context_lens, num_seqs, [&](int32_t) { return static_cast<int64_t>(workgroups_per_partition); },
+      resident_workgroups, min_tokens);
   return PKV_OK;
 }
 
@@ -392,15 +414,41 @@ pkv_status pkv_decode_partition_tokens(const int32_t* context_lens, int32_t num_
     min_tokens = std::max(min_tokens, wide_min);
   }
   if (st) return st;
-  int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return fail(PKV_ERR_DEVICE, "%s: %s", who, hipGetErrorString(e));
-  if (per_cu <= 0 || cus <= 0)
+  int cus = 0;
+  if (device_compute_units(&cus))
+    return fail(PKV_ERR_DEVICE, "%s: no device to size the launch for", who);
+  if (per_cu <= 0)
     return fail(PKV_ERR_DEVICE, "%s: the decode kernel does not fit a compute unit", who);
   return pkv_decode_partition_for_capacity(context_lens, num_seqs, per_partition,
                                            static_cast<int64_t>(per_cu) * cus, min_tokens,
                                            partition_tokens);
+}
+
+pkv_status pkv_prefill_partition_tokens(const int32_t* query_lens, const int32_t* context_lens,
+                                        int32_t num_seqs, int32_t num_q_heads, pkv_dtype q_dtype,
+                                        int32_t* partition_tokens) {
+  const char* who = "prefill_partition_tokens";
+  if (!partition_tokens || (num_seqs > 0 && (!query_lens || !context_lens)))
+    return fail(PKV_ERR_INVALID, "%s: NULL pointer", who);
+  if (num_seqs < 0 || num_q_heads <= 0)
+    return fail(PKV_ERR_INVALID, "%s: bad sizes (S=%d Hq=%d)", who, num_seqs, num_q_heads);
+  if (q_dtype != PKV_F32 && q_dtype != PKV_F16 && q_dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: q dtype %s", who, dtype_name(q_dtype));
+  for (int32_t s = 0; s < num_seqs; ++s)
+    if (query_lens[s] < 0 || context_lens[s] < query_lens[s])
+      return fail(PKV_ERR_INVALID, "%s: sequence %d has %d query rows over %d keys", who, s,
+                  query_lens[s], context_lens[s]);
+  *partition_tokens = 0;
+  if (q_dtype == PKV_F32) return PKV_OK;   // the wavefront rows: one workgroup per row already
+  int cus = 0;
+  if (device_compute_units(&cus))
+    return fail(PKV_ERR_DEVICE, "%s: no device to size the launch for", who);
+  const int rows = prefill_tile_rows();
+  *partition_tokens = partition_for_rounds(
+      context_lens, num_seqs,
+      [&](int32_t s) { return static_cast<int64_t>((query_lens[s] + rows - 1) / rows) * num_q_heads; },
+      static_cast<int64_t>(kPrefillPerCu) * cus, kMinAutoPartition);
+  return PKV_OK;
 }
 
 pkv_status pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void* q,

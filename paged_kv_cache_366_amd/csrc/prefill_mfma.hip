@@ -491,6 +491,8 @@ pkv_status launch_t(const AttnArgs& a, int D, int max_tiles, hipStream_t st) {
 
 }  // namespace
 
+int prefill_tile_rows() { return kTileRows; }
+
 pkv_status launch_prefill_mfma(const AttnArgs& a, pkv_dtype q_dt, int D, int group,
                                int max_query_len, hipStream_t st) {
   if (max_query_len <= 0 || a.num_seqs <= 0) return PKV_OK;

@@ -246,6 +246,27 @@ def prefill_split(c, part, out_dtype=torch.float32, workspace=None):
     return out, ws
 
 
+def test_prefill_partition_choice():
+    """Four 64-row chunks over 16,384 keys (128 workgroups unsplit) split so
+    that two workgroups per compute unit are busy; the mixed step's chunks
+    fill the GPU unsplit; fp32 q never splits; a chunk longer than its
+    context is refused.  The chosen split of a small batch matches the
+    oracle."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    p = pkv.pkv_prefill_partition_tokens([64] * 4, [16384] * 4, 32)
+    n = lambda pt: 4 * 32 * -(-16384 // pt)
+    assert p % 16 == 0 and p >= 256 and n(p) <= 2 * cus < n(p - 16), p
+    assert pkv.pkv_prefill_partition_tokens([512] * 4, [512, 1024, 1536, 2048], 32) == 0
+    assert pkv.pkv_prefill_partition_tokens([64] * 4, [16384] * 4, 32, pkv.PKV_F32) == 0
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_prefill_partition_tokens([65], [64], 32)
+    c = W.prefill_case(95, 8, 2, 128, LONG_CHUNKS, dtype="bf16")
+    p = pkv.pkv_prefill_partition_tokens(np.diff(c.query_start_loc), c.context_lens, 8)
+    assert p >= 256, p
+    out, _ = prefill_split(c, p)
+    assert np.abs(out_f64(out) - oracle_prefill(c)).max() <= TOL16
+
+
 @pytest.mark.parametrize("dtype,hq,hkv,d", [("bf16", 8, 2, 128), ("f16", 4, 4, 64),
                                             ("f32", 4, 2, 64)])
 def test_split_prefill_matches_oracle_and_unsplit(dtype, hq, hkv, d):
