@@ -80,15 +80,15 @@ PAGE_ALLOC_P99_BAR_US = 1000.0   # cnnetsun.cn section 4.2: page allocation P99 
 # FETCH_SIZE scaled by 1 / 0.500041 (a 1 GiB torch.bitwise_not in the same
 # process reads as 524,331 KiB) plus WRITE_SIZE (exact for the same copy).
 # Reported only while the kernel sources hash to the value they were taken on.
-_SHA = "4e9f5fa97226435080ed9dbadbfe7b3e319af28a"
+_SHA = "f48f9e8ac13d99de29020f47717904dc89d5ee1d"
 TRAFFIC = {
-    "decode7b": {"bytes_per_launch": 1120493418, "sources_sha1": _SHA, "partition_tokens": 2048,
+    "decode7b": {"bytes_per_launch": 1120485706, "sources_sha1": _SHA, "partition_tokens": 2048,
                  "profile": "profiles/decode_wave_7b_bf16_p2048_step_kernel_trace.md"},
-    "gqa-bf16": {"bytes_per_launch": 1544133872, "sources_sha1": _SHA, "partition_tokens": 6448,
+    "gqa-bf16": {"bytes_per_launch": 1544128461, "sources_sha1": _SHA, "partition_tokens": 6448,
                  "profile": "profiles/decode_mfma_gqa_long_bf16_kernel_trace.md"},
-    "gqa-int8": {"bytes_per_launch": 828925108, "sources_sha1": _SHA, "partition_tokens": 2048,
+    "gqa-int8": {"bytes_per_launch": 828921235, "sources_sha1": _SHA, "partition_tokens": 2048,
                  "profile": "profiles/decode_mfma_gqa_long_int8_kernel_trace.md"},
-    "gqa-int4": {"bytes_per_launch": 446595656, "sources_sha1": _SHA, "partition_tokens": 1504,
+    "gqa-int4": {"bytes_per_launch": 446596696, "sources_sha1": _SHA, "partition_tokens": 1504,
                  "profile": "profiles/decode_mfma_gqa_long_int4_kernel_trace.md"},
 }
 KERNEL_SOURCES = ("decode_wave.hip", "decode_mfma.hip", "reduce.hip", "attention_common.h",
