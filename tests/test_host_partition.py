@@ -78,3 +78,32 @@ def test_argument_checks():
     for args in (([-1, 5], 8, 64, 0), ([5], 0, 64, 0), ([5], 8, 0, 0), ([5], 8, 64, -1)):
         with pytest.raises(pkv.PkvError):
             pkv.pkv_decode_partition_for_capacity(*args)
+
+
+def test_device_aware_helpers_check_arguments_without_a_gpu():
+    """Both device-aware partition calls refuse bad arguments before any
+    device query; fp32-q prefill never splits, so it needs no device."""
+    lens = [100, 200]
+    bad_decode = [
+        dict(num_q_heads=0), dict(num_kv_heads=3), dict(head_dim=96), dict(block_size=24),
+        dict(num_blocks=0), dict(algo=7),
+        dict(algo=pkv.PKV_ALGO_AUTO | pkv.PKV_KV_STREAM | pkv.PKV_KV_CACHED),
+        dict(q_dtype=pkv.PKV_I8),
+    ]
+    base = dict(q_dtype=pkv.PKV_BF16, kv_dtype=pkv.PKV_BF16, num_q_heads=8, num_kv_heads=2,
+                head_dim=128, block_size=16, num_blocks=100, algo=pkv.PKV_ALGO_AUTO)
+    for change in bad_decode:
+        args = dict(base, **change)
+        with pytest.raises(pkv.PkvError):
+            pkv.pkv_decode_partition_tokens(lens, **args)
+    # a 32-head group is too large for the matrix-core path when it is forced
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_decode_partition_tokens(lens, **dict(base, num_q_heads=64, algo=pkv.PKV_ALGO_MFMA))
+    for ql, cl in (([65], [64]), ([-1], [10])):
+        with pytest.raises(pkv.PkvError):
+            pkv.pkv_prefill_partition_tokens(ql, cl, 8)
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_prefill_partition_tokens([10], [10], 0)
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_prefill_partition_tokens([10], [10], 8, pkv.PKV_I8)
+    assert pkv.pkv_prefill_partition_tokens([64] * 4, [16384] * 4, 32, pkv.PKV_F32) == 0
