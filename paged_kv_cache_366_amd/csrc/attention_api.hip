@@ -8,6 +8,7 @@
 
 #include "attention_common.h"
 #include "host_checks.h"
+#include "partition.h"
 
 namespace pkv {
 pkv_status launch_decode_wave(const AttnArgs& a, pkv_dtype q_dt, pkv_dtype kv_dt, int D,
@@ -282,36 +283,6 @@ pkv_status scratch_address(const char* who, void** addr) {
   return PKV_OK;
 }
 
-// The shortest partition (a multiple of 16 tokens, at least min_tokens)
-// whose workgroups fit in the whole rounds of `resident` that the launch
-// needs without a split; 0 when no split fits (or nothing to split).
-// Sequence s contributes weight(s) workgroups per partition of its keys
-// (partitions past a context's end hold no slot).  The count only falls as
-// the partition grows, so a bisection over multiples of 16 finds it.
-template <typename Weight>
-int32_t partition_for_rounds(const int32_t* lens, int32_t num_seqs, Weight weight,
-                             int64_t resident, int32_t min_tokens) {
-  int32_t max_len = 0;
-  for (int32_t s = 0; s < num_seqs; ++s)
-    if (weight(s) > 0) max_len = std::max(max_len, lens[s]);
-  const int64_t cap = (static_cast<int64_t>(max_len) + 15) / 16 * 16;   // one partition per context
-  const int64_t lo = std::max<int64_t>(16, (static_cast<int64_t>(min_tokens) + 15) / 16 * 16);
-  if (max_len == 0 || lo >= cap) return 0;
-  auto wgs = [&](int64_t p) {
-    int64_t n = 0;
-    for (int32_t s = 0; s < num_seqs; ++s) n += (lens[s] + p - 1) / p * weight(s);
-    return n;
-  };
-  const int64_t rounds = (wgs(cap) + resident - 1) / resident;
-  const int64_t target = rounds * resident;
-  int64_t a = lo / 16, b = cap / 16;   // wgs(16 b) <= target; find the least such
-  while (a < b) {
-    const int64_t m = (a + b) / 2;
-    if (wgs(16 * m) <= target) b = m; else a = m + 1;
-  }
-  return 16 * a < cap ? static_cast<int32_t>(16 * a) : 0;
-}
-
 int device_compute_units(int* cus) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -346,26 +317,6 @@ size_t pkv_prefill_workspace_bytes(int32_t num_query_tokens, int32_t num_q_heads
   return workspace_layout(num_query_tokens, num_q_heads, head_dim,
                           num_partitions(max_context_len, partition_tokens))
       .total;
-}
-
-pkv_status pkv_decode_partition_for_capacity(const int32_t* context_lens, int32_t num_seqs,
-                                             int32_t workgroups_per_partition,
-                                             int64_t resident_workgroups, int32_t min_tokens,
-                                             int32_t* partition_tokens) {
-  const char* who = "decode_partition_for_capacity";
-  if (!partition_tokens || (num_seqs > 0 && !context_lens))
-    return fail(PKV_ERR_INVALID, "%s: NULL pointer", who);
-  if (num_seqs < 0 || workgroups_per_partition <= 0 || resident_workgroups <= 0 || min_tokens < 0)
-    return fail(PKV_ERR_INVALID, "%s: bad sizes (S=%d per-partition %d resident %lld min %d)", who,
-                num_seqs, workgroups_per_partition, static_cast<long long>(resident_workgroups),
-                min_tokens);
-  for (int32_t s = 0; s < num_seqs; ++s)
-    if (context_lens[s] < 0)
-      return fail(PKV_ERR_INVALID, "%s: context_lens[%d] = %d", who, s, context_lens[s]);
-  *partition_tokens = partition_for_rounds(
-      context_lens, num_seqs, [&](int32_t) { return static_cast<int64_t>(workgroups_per_partition); },
-      resident_workgroups, min_tokens);
-  return PKV_OK;
 }
 
 pkv_status pkv_decode_partition_tokens(const int32_t* context_lens, int32_t num_seqs,
@@ -444,11 +395,15 @@ pkv_status pkv_prefill_partition_tokens(const int32_t* query_lens, const int32_t
   if (device_compute_units(&cus))
     return fail(PKV_ERR_DEVICE, "%s: no device to size the launch for", who);
   const int rows = prefill_tile_rows();
-  *partition_tokens = partition_for_rounds(
-      context_lens, num_seqs,
-      [&](int32_t s) { return static_cast<int64_t>((query_lens[s] + rows - 1) / rows) * num_q_heads; },
-      static_cast<int64_t>(kPrefillPerCu) * cus, kMinAutoPartition);
-  return PKV_OK;
+  PKV_GUARD({
+    std::vector<int64_t> weights(static_cast<size_t>(num_seqs));
+    for (int32_t s = 0; s < num_seqs; ++s)
+      weights[s] = static_cast<int64_t>((query_lens[s] + rows - 1) / rows) * num_q_heads;
+    *partition_tokens = partition_for_rounds(context_lens, weights.data(), 0, num_seqs,
+                                             static_cast<int64_t>(kPrefillPerCu) * cus,
+                                             kMinAutoPartition);
+    return PKV_OK;
+  })
 }
 
 pkv_status pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void* q,

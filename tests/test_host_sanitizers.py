@@ -1,9 +1,11 @@
-"""The host block manager under AddressSanitizer and UndefinedBehaviorSanitizer.
+"""The host block manager and the partition search under AddressSanitizer and
+UndefinedBehaviorSanitizer.
 
-block_manager.cc is compiled on its own with g++ -fsanitize=address,undefined
-into a host-only library, and the host block-manager tests (the C++ manager
-against the allocator model over random operation sequences, the golden
-traces, out-of-blocks atomicity) run against it in a child Python process
+block_manager.cc and partition.cc are compiled on their own with g++
+-fsanitize=address,undefined into a host-only library, and the host tests
+(the C++ manager against the allocator model over random operation
+sequences, the golden traces, out-of-blocks atomicity; the partition search
+against brute force) run against it in a child Python process
 with the ASan runtime preloaded.  Any heap overflow, use after free, double
 free or undefined operation (signed overflow, misaligned or out-of-range
 access) aborts the child with a sanitizer report.  CPU only.
@@ -16,13 +18,14 @@ import sys
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SRC = os.path.join(ROOT, "paged_kv_cache_366_amd", "csrc", "block_manager.cc")
+CSRC = os.path.join(ROOT, "paged_kv_cache_366_amd", "csrc")
+SRCS = [os.path.join(CSRC, f) for f in ("block_manager.cc", "partition.cc")]
 OUT_DIR = os.path.join(ROOT, "_build", "sanitize")
 LIB = os.path.join(OUT_DIR, "libpkv_host_san.so")
 
 # the host-only entry points (block manager and sequences) the tests use
 HOST_PREFIXES = ("pkv_bm_", "pkv_seq_", "pkv_last_error", "pkv_version",
-                 "pkv_adaptive_block_size")
+                 "pkv_adaptive_block_size", "pkv_decode_partition_for_capacity")
 
 CHILD = r"""
 import sys
@@ -36,8 +39,7 @@ assert hasattr(ctypes.CDLL(None), "__asan_report_load4")
 assert hasattr(ctypes.CDLL(L.LIB_PATH), "pkv_bm_create")
 print("sanitizer runtime loaded")
 import pytest
-sys.exit(pytest.main(["-q", "-p", "no:cacheprovider", "-x",
-                      {tests!r}]))
+sys.exit(pytest.main(["-q", "-p", "no:cacheprovider", "-x"] + {tests!r}))
 """
 
 
@@ -46,10 +48,10 @@ def _build():
     if gxx is None:
         pytest.skip("g++ not found")
     os.makedirs(OUT_DIR, exist_ok=True)
-    if os.path.exists(LIB) and os.path.getmtime(LIB) >= os.path.getmtime(SRC):
+    if os.path.exists(LIB) and all(os.path.getmtime(LIB) >= os.path.getmtime(f) for f in SRCS):
         return
     cmd = [gxx, "-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-fno-omit-frame-pointer",
-           "-fsanitize=address,undefined", "-fno-sanitize-recover=all", SRC, "-o", LIB]
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all", *SRCS, "-o", LIB]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
 
@@ -65,7 +67,9 @@ def test_block_manager_tests_clean_under_asan_and_ubsan():
     # the interpreter itself is not instrumented and keeps objects until exit
     env["ASAN_OPTIONS"] = "detect_leaks=0:halt_on_error=1:abort_on_error=1"
     env["UBSAN_OPTIONS"] = "halt_on_error=1:print_stacktrace=1"
-    tests = os.path.join(ROOT, "tests", "test_host_block_manager.py")
+    tests = [os.path.join(ROOT, "tests", "test_host_block_manager.py"),
+             os.path.join(ROOT, "tests", "test_host_partition.py"),
+             "-k", "not device_aware"]
     code = CHILD.format(root=ROOT, lib=LIB, prefixes=HOST_PREFIXES, tests=tests)
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
                        cwd=ROOT, timeout=600)
