@@ -372,6 +372,33 @@ def test_partials_then_reduce_equals_one_call(mha_bf16):
     assert torch.equal(out, one)
 
 
+# Contexts whose rows span hundreds of partitions: 16-token partitions give
+# 313, 257, 257 (one key in the last) and 69 of them, 32-token ones 157, 129,
+# 129 and 35.  The reduce keeps the (max, sum) pairs of partitions 0..255 in
+# four lane registers each and re-reads the later ones, so these rows run
+# every bank and the re-read loop.
+MANY_LENS = [5000, 4112, 4097, 1100, 17, 1]
+
+
+@pytest.mark.parametrize("kind", ["wave-mha-bf16", "mfma-gqa-bf16", "mfma-gqa-int8"])
+def test_hundreds_of_partitions_per_row(kind):
+    algo = WAVE if kind.startswith("wave") else MFMA
+    hq, hkv = (8, 8) if "mha" in kind else (16, 2)
+    int8 = kind.endswith("int8")
+    c = W.decode_case(830 + len(kind), len(MANY_LENS), hq, hkv, 128, lens=MANY_LENS,
+                      dtype="bf16", int8=int8)
+    d = DevCase(c, int8=int8)
+    ref = oracle_decode(c, int8=int8)
+    whole = out_f64(d.decode(parts=0, algo=algo))
+    assert np.abs(whole - ref).max() <= TOL16
+    for parts in (16, 32):
+        got = out_f64(d.decode(parts=parts, algo=algo))
+        err = np.abs(got - ref).max()
+        assert err <= TOL16, (parts, err)
+        # the partition size only reassociates fp32 sums
+        assert np.abs(got - whole).max() <= 1e-5, parts
+
+
 # ---------------------------------------------------------------- full size
 def sampled_oracle(c, pairs, int8=False):
     """Oracle outputs of selected (sequence, head) pairs, one by one."""

@@ -127,6 +127,24 @@ def test_step_equals_reshape_then_decode(kind):
                 assert same_bits(o3, o1)
 
 
+@pytest.mark.parametrize("algo", [WAVE, MFMA], ids=["wave", "mfma"])
+def test_step_merge_over_hundreds_of_partitions(algo):
+    """Rows of up to 313 partitions (16-token partitions over 5,000 keys):
+    the reduce holds the (max, sum) pairs of partitions 0..255 in lane
+    registers and re-reads the rest, the in-launch merge reads them all in
+    order, and both give the same bits."""
+    sc = StepCase(760 + algo, [5000, 4112, 4097, 1100, 17, 1], 16, 2, 128, "bf16")
+    ref64 = sc.oracle()
+    for parts in (16, 32):
+        o2, k2, v2 = sc.two_kernels(parts, algo)
+        for merge in (0, IN):
+            o1, k1, v1, ws = sc.step(parts, algo | merge)
+            assert same_bits(o1, o2), (parts, merge, (o1 - o2).abs().max().item())
+            assert same_bits(k1, k2) and same_bits(v1, v2), (parts, merge)
+            assert np.abs(out_f64(o1) - ref64).max() <= TOL16
+            assert counters_zero(ws, 6, 16, 128, sc.max_ctx, parts)
+
+
 def test_step_workspace_reused_by_a_smaller_batch_and_bf16_output():
     big = StepCase(731, [3000, 5, 2049, 4096, 700, 1600], 16, 2, 128, "bf16")
     small = StepCase(732, [1600, 40, 3100], 16, 2, 128, "bf16")

@@ -287,6 +287,21 @@ def test_split_prefill_matches_oracle_and_unsplit(dtype, hq, hkv, d):
     assert ws is None and torch.equal(same, base)
 
 
+def test_split_prefill_over_hundreds_of_partitions():
+    """Chunks after 4,500 and 4,090 cached tokens at 16-token partitions:
+    their last rows span up to 284 partitions, past the 256 whose (max, sum)
+    pairs the reduce keeps in lane registers."""
+    c = W.prefill_case(97, 8, 2, 128, [(4500, 40), (4090, 8), (0, 20)], dtype="bf16")
+    ref = oracle_prefill(c)
+    base, _ = prefill_split(c, 0)
+    assert np.abs(out_f64(base) - ref).max() <= TOL16
+    for part in (16, 32):
+        out, ws = prefill_split(c, part)
+        assert ws is not None
+        assert np.abs(out_f64(out) - ref).max() <= TOL16, part
+        assert np.abs(out_f64(out) - out_f64(base)).max() <= 1e-5, part
+
+
 def test_split_prefill_bf16_output_and_determinism():
     c = W.prefill_case(95, 8, 8, 128, LONG_CHUNKS, dtype="bf16")
     of, _ = prefill_split(c, 256)
