@@ -345,6 +345,23 @@ def test_group_sizes_wave_only(group):
     assert np.abs(out_f64(out) - ref).max() <= TOL16
 
 
+@pytest.mark.parametrize("group", [3, 5, 6, 7, 12])
+@pytest.mark.parametrize("int8", [False, True], ids=["bf16", "int8"])
+def test_group_sizes_not_powers_of_two(group, int8):
+    """Groups that 4 does not divide: the wavefront kernel takes 2 or 1
+    heads per workgroup, the matrix-core kernel masks its 16 head columns
+    past the group; AUTO picks one of them by the group."""
+    hkv = 2
+    c = W.decode_case(450 + group, 5, hkv * group, hkv, 128, lens=[1, 17, 300, 1500, 3001],
+                      dtype="bf16", int8=int8)
+    d = DevCase(c, int8=int8)
+    ref = oracle_decode(c, int8=int8)
+    for algo in (WAVE, MFMA, pkv.PKV_ALGO_AUTO):
+        for parts in (0, 256):
+            err = np.abs(out_f64(d.decode(parts=parts, algo=algo)) - ref).max()
+            assert err <= TOL16, (algo, parts, err)
+
+
 def test_validation_rejects_bad_tables(mha_bf16, monkeypatch):
     c, d, _ = mha_bf16
     monkeypatch.setenv("PKV_VALIDATE", "1")

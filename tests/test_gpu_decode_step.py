@@ -145,6 +145,23 @@ def test_step_merge_over_hundreds_of_partitions(algo):
             assert counters_zero(ws, 6, 16, 128, sc.max_ctx, parts)
 
 
+@pytest.mark.parametrize("group", [3, 5, 7, 12])
+def test_step_group_sizes_not_powers_of_two(group):
+    """The new row of a KV head is written once, by one of the workgroups
+    that share it, whatever the group: the cache and the output equal the
+    two-kernel path bit for bit."""
+    sc = StepCase(770 + group, [1, 17, 300, 1500, 3001], 2 * group, 2, 128, "bf16")
+    ref64 = sc.oracle()
+    for algo in (WAVE, MFMA):
+        for parts in (0, 256):
+            o2, k2, v2 = sc.two_kernels(parts, algo)
+            for merge in (0, IN):
+                o1, k1, v1, _ = sc.step(parts, algo | merge)
+                assert same_bits(o1, o2), (algo, parts, merge)
+                assert same_bits(k1, k2) and same_bits(v1, v2), (algo, parts, merge)
+                assert np.abs(out_f64(o1) - ref64).max() <= TOL16
+
+
 def test_step_workspace_reused_by_a_smaller_batch_and_bf16_output():
     big = StepCase(731, [3000, 5, 2049, 4096, 700, 1600], 16, 2, 128, "bf16")
     small = StepCase(732, [1600, 40, 3100], 16, 2, 128, "bf16")

@@ -48,7 +48,8 @@ CHUNKS = [(0, 1), (0, 17), (7, 64), (16, 65), (100, 130), (33, 0), (250, 16), (5
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("hq,hkv,d", [(4, 4, 128), (8, 2, 128), (4, 4, 64), (6, 3, 64)])
+@pytest.mark.parametrize("hq,hkv,d", [(4, 4, 128), (8, 2, 128), (4, 4, 64), (6, 3, 64),
+                                      (10, 2, 128), (12, 4, 64)])
 def test_prefill_matches_oracle(dtype, hq, hkv, d):
     c = W.prefill_case(500 + hq + d, hq, hkv, d, CHUNKS, dtype=dtype)
     ref = oracle_prefill(c)
