@@ -201,6 +201,17 @@ def test_decode_over_random_int4_pools(kind, parts):
     assert np.abs(got - oracle_int4(c)).max() <= TOL
 
 
+@pytest.mark.parametrize("group", [3, 5, 6, 7, 12])
+def test_int4_decode_group_sizes_not_powers_of_two(group):
+    c = W.decode_case(470 + group, 5, 2 * group, 2, 128, lens=[1, 17, 300, 1500, 3001],
+                      dtype="bf16", int4=True)
+    ref = oracle_int4(c)
+    for algo in (WAVE, MFMA, AUTO):
+        for parts in (0, 256):
+            err = np.abs(decode_int4(c, "bf16", algo, parts) - ref).max()
+            assert err <= TOL, (algo, parts, err)
+
+
 def test_int4_decode_is_the_same_for_both_kernels_and_outputs():
     c = W.decode_case(95, 4, 16, 2, 128, lens=[33, 250, 7, 512], dtype="bf16", int4=True)
     ref = oracle_int4(c)
