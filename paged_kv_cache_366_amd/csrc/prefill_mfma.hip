@@ -28,10 +28,22 @@
 // (r16, kg) ends with elements 16j + 4kg .. +3 of its row for each block j.
 //
 // Loads: K and V move from global memory to LDS with gfx950's direct loads
-// (no registers in between) into three stages, so the loads of the next two
-// steps are in flight while a step computes.  Rows are unpadded and their
-// 16-byte chunks XOR-swizzled by row, which keeps the rows read at one
-// column in different banks.  Each wave waits for its own loads of a step,
+// (no registers in between) into NST stages, so the loads of the next NST - 1
+// steps are in flight while a step computes.  Three stages of head_dim 128
+// take 48 KiB of LDS, which leaves room for three workgroups per compute
+// unit; two take 32 KiB and leave room for four (the register cap below).
+// The launch takes two when it has more workgroups than compute units and
+// three otherwise: with fewer, each workgroup walks its keys alone and the
+// deeper pipeline hides more of the load latency (long-document chunks
+// unsplit, 128 workgroups: 441-446 us with three stages against 465-467
+// with two), while with more, the fourth resident workgroup pays (mixed
+// step, 1,024 workgroups: 84.6 against 86 us; long-document chunks split
+// 4-way, 512 workgroups: 197.0 against 202.6 us; the prefix-cache
+// admission prefill 268-288 against 288-290 us).  Head_dim 64 keeps three
+// stages (24 KiB: registers, not LDS, bound its occupancy).
+//
+// Rows are unpadded and their 16-byte chunks XOR-swizzled by row, which
+// keeps the rows read at one column in different banks.  Each wave waits for its own loads of a step,
 // then one barrier (without the memory fence of __syncthreads, which would
 // also wait for the steps still loading) makes every wave's loads visible.
 // Rows past the workgroup's last key and rows of blocks outside the pool
@@ -55,7 +67,7 @@
 // Measured on MI355X (mixed step, four 512-row chunks over 0..1536 cached
 // tokens): the transposed value reads took the kernel from 140 to 109 us,
 // the order by context length and four waves per SIMD to about 91 us, the
-// direct loads to 86 us.  What bounds it: without its arithmetic the same
+// direct loads to 86 us, two stages for large grids to 84.6 us.  What bounds it: without its arithmetic the same
 // kernel (loads, LDS, barriers) still takes about 62 us, and with its
 // arithmetic the longest row tiles (2,048 keys, 64 steps) finish last;
 // 8-wave workgroups (half the K/V traffic) and key partitions (fp32 partial
@@ -82,14 +94,15 @@ constexpr int kGroup = PKV_PREFILL_GROUP;     // 16-key tiles per LDS step (one 
 constexpr int kRowTiles = PKV_PREFILL_RTILES; // 16-row tiles per wavefront
 constexpr int kTileRows = kPrefillWaves * 16 * kRowTiles;   // query rows per workgroup
 
-// Registers for four waves per SIMD (at most 128 VGPRs): a compute unit
-// then holds four workgroups (LDS allows four too).  Left to itself the
-// compiler takes 130, which leaves room for three.
+// Registers for four waves per SIMD (at most 128 VGPRs), so that four
+// workgroups fit a compute unit where the LDS allows it (two stages at
+// head_dim 128, or head_dim 64).  Left to itself the compiler took 130 in
+// an earlier form of the kernel, which leaves room for three.
 #ifndef PKV_PREFILL_WPE
 #define PKV_PREFILL_WPE 4
 #endif
 #define PKV_PREFILL_ATTR __attribute__((amdgpu_waves_per_eu(PKV_PREFILL_WPE)))
-template <typename T, int D, int R, int G0>
+template <typename T, int D, int R, int G0, int NST>
 __global__ __launch_bounds__(kPrefillThreads) PKV_PREFILL_ATTR void prefill_mfma_kernel(AttnArgs a, int max_tiles) {
   constexpr int NK = D / 32;              // QK products per block and row tile
   constexpr int NV = D / 16;              // PV products per block and row tile
@@ -97,6 +110,7 @@ __global__ __launch_bounds__(kPrefillThreads) PKV_PREFILL_ATTR void prefill_mfma
   constexpr int CHUNKS = ROWB / 16;       // 16-byte chunks per row
   constexpr int G = G0;                   // 16-key tiles per step
   static_assert(G == 2, "a step is two 16-key tiles: the K = 32 of one value product");
+  static_assert(NST == 2 || NST == 3, "two or three LDS stages");
   constexpr int WROWS = 16 * R;           // rows per wavefront
   constexpr int TROWS = kPrefillWaves * WROWS;
   using M = Mx<T>;
@@ -182,13 +196,13 @@ __global__ __launch_bounds__(kPrefillThreads) PKV_PREFILL_ATTR void prefill_mfma
   const uint8_t* kc = static_cast<const uint8_t*>(a.kc);
   const uint8_t* vc = static_cast<const uint8_t*>(a.vc);
 
-  // ---- K/V staging: direct global -> LDS loads into three stages --------
+  // ---- K/V staging: direct global -> LDS loads into NST stages ----------
   // A stage holds one step (two 16-key tiles) of K and of V: 32 rows of
   // ROWB bytes each, unpadded.  One load instruction of a wave fills 1 KiB
   // (lane l's 16 bytes land at byte 16 l), i.e. RPL whole rows.  The
   // 16-byte chunk c of stage row r sits at chunk position c ^ (r % CHUNKS),
-  // so rows read at one column fall in different banks.  Loads of the step
-  // two ahead are in flight while a step computes, and they hold no
+  // so rows read at one column fall in different banks.  Loads of the next
+  // NST - 1 steps are in flight while a step computes, and they hold no
   // registers.
   constexpr int SROWS = G * 16;
   constexpr int STAGE = SROWS * ROWB;
@@ -201,8 +215,8 @@ __global__ __launch_bounds__(kPrefillThreads) PKV_PREFILL_ATTR void prefill_mfma
                 "loads split evenly over the waves");
   const bool loader = wave * LDW < LPO;          // wave-uniform
   constexpr int NLD = 2 * LDW;                    // vector memory instructions per loading wave and step
-  __shared__ __align__(1024) uint8_t sk0[STAGE], sk1[STAGE], sk2[STAGE];
-  __shared__ __align__(1024) uint8_t sv0[STAGE], sv1[STAGE], sv2[STAGE];
+  __shared__ __align__(1024) uint8_t sk0[STAGE], sk1[STAGE], sk2[NST == 3 ? STAGE : 16];
+  __shared__ __align__(1024) uint8_t sv0[STAGE], sv1[STAGE], sv2[NST == 3 ? STAGE : 16];
 
   // Lane constants.  Load k of this wave (per operand) fills stage rows
   // [RPL (wave LDW + k), +RPL); the lane's chunk comes from row
@@ -249,7 +263,7 @@ __global__ __launch_bounds__(kPrefillThreads) PKV_PREFILL_ATTR void prefill_mfma
     }
     return __builtin_amdgcn_readlane(tv, e - tv_base);
   };
-  bool okst[3][G];
+  bool okst[NST][G];
   auto issue = [&](int st, int u) {
     int64_t toff[G];
 #pragma unroll
@@ -401,8 +415,10 @@ __global__ __launch_bounds__(kPrefillThreads) PKV_PREFILL_ATTR void prefill_mfma
     }
   };
 
-  // vmcnt(n) alone (expcnt and lgkmcnt left at their maxima).
-  constexpr int kWaitOneStep = (NLD & 15) | ((NLD >> 4) << 14) | (7 << 4) | (15 << 8);
+  // vmcnt(n) alone (expcnt and lgkmcnt left at their maxima): with three
+  // stages the loads of the next step stay in flight, with two none do.
+  constexpr int kWaitOneStep =
+      NST == 3 ? (NLD & 15) | ((NLD >> 4) << 14) | (7 << 4) | (15 << 8) : (7 << 4) | (15 << 8);
   static_assert(NLD < 64, "vmcnt range");
   // Barrier without the memory fence __syncthreads adds: that fence waits for
   // every load in flight, including the next steps' staging.  The empty asm
@@ -416,23 +432,24 @@ __global__ __launch_bounds__(kPrefillThreads) PKV_PREFILL_ATTR void prefill_mfma
   const int nstep = (b_end - b_begin + G - 1) / G;
   // (the loads read table entries of blocks b_begin .. b_end - 1 only)
   issue(0, 0);
-  issue(1, 1);
-  // Step st: wait for this wave's loads of step st (those of step st + 1
-  // stay in flight), zero its invalid rows, barrier (every wave's loads of
-  // step st have landed and every wave is done with step st - 1), start the
-  // loads of step st + 2 into the stage step st - 1 used, compute step st.
-  // Whole groups of three steps, so every stage index is static; steps past
-  // the last block load the first tile and compute nothing.
+  if constexpr (NST == 3) issue(1, 1);
+  // Step st: wait for this wave's loads of step st (with three stages those
+  // of step st + 1 stay in flight), zero its invalid rows, barrier (every
+  // wave's loads of step st have landed and every wave is done with step
+  // st - 1), start the loads of step st + NST - 1 into the stage step st - 1
+  // used, compute step st.  Whole groups of NST steps, so every stage index
+  // is static; steps past the last block load the first tile and compute
+  // nothing.
 #pragma unroll 1
-  for (int s0 = 0; s0 < nstep; s0 += 3) {
+  for (int s0 = 0; s0 < nstep; s0 += NST) {
 #pragma unroll
-    for (int u = 0; u < 3; ++u) {
+    for (int u = 0; u < NST; ++u) {
       const int st = s0 + u;
       __builtin_amdgcn_s_waitcnt(kWaitOneStep);
       fixup(st, u);
       __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the zeros are in LDS
       barrier();
-      issue(st + 2, (u + 2) % 3);
+      issue(st + NST - 1, (u + NST - 1) % NST);
       compute(st, u);
     }
   }
@@ -479,12 +496,23 @@ pkv_status launch_t(const AttnArgs& a, int D, int max_tiles, hipStream_t st) {
   if (wgs > 0x7fffffff / kPrefillThreads)
     return fail(PKV_ERR_UNSUPPORTED, "prefill: launch too large");
   dim3 grid(static_cast<unsigned>(wgs));
-  if (D == 64)
-    hipLaunchKernelGGL((prefill_mfma_kernel<T, 64, kRowTiles, kGroup>), grid, dim3(kPrefillThreads), 0, st,
-                       a, max_tiles);
-  else
-    hipLaunchKernelGGL((prefill_mfma_kernel<T, 128, kRowTiles, kGroup>), grid, dim3(kPrefillThreads), 0, st,
-                       a, max_tiles);
+  if (D == 64) {
+    hipLaunchKernelGGL((prefill_mfma_kernel<T, 64, kRowTiles, kGroup, 3>), grid,
+                       dim3(kPrefillThreads), 0, st, a, max_tiles);
+  } else {
+    // two stages once the grid has more workgroups than compute units
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess || cus <= 0)
+      return fail(PKV_ERR_DEVICE, "chunked prefill (MFMA): no device to size the launch for");
+    if (wgs > cus)
+      hipLaunchKernelGGL((prefill_mfma_kernel<T, 128, kRowTiles, kGroup, 2>), grid,
+                         dim3(kPrefillThreads), 0, st, a, max_tiles);
+    else
+      hipLaunchKernelGGL((prefill_mfma_kernel<T, 128, kRowTiles, kGroup, 3>), grid,
+                         dim3(kPrefillThreads), 0, st, a, max_tiles);
+  }
   PKV_LAUNCH_CHECK("chunked prefill (MFMA)");
   return PKV_OK;
 }

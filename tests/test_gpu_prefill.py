@@ -110,6 +110,32 @@ def test_large_scores_stay_finite():
     assert np.abs(out_f64(out) - ref).max() <= TOL16
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_stage_count_changes_no_bit(dtype):
+    """At head_dim 128 a launch with more workgroups than compute units
+    stages K/V in two LDS buffers, a smaller one in three.  The same chunk
+    computed alone (a small grid) and as each of many identical sequences
+    (a grid past the compute-unit count) gives the same bits."""
+    hq = 8
+    one = W.prefill_case(83, hq, 2, 128, [(300, 200)], dtype=dtype)
+    tiles = -(-200 // 64)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n = cus // (tiles * hq) + 2
+    assert one.block_tables.shape[0] == 1 and n * tiles * hq > cus >= tiles * hq
+    alone = gpu_prefill(one)
+    qsl = np.arange(n + 1, dtype=np.int32) * 200
+    qd = to_dev(np.concatenate([one.q] * n), dtype)
+    out = torch.empty(qd.shape, dtype=torch.float32, device=DEV)
+    pkv.pkv_paged_attention_prefill(out, qd, to_dev(one.k_cache, dtype), to_dev(one.v_cache, dtype),
+                                    i32(np.repeat(one.block_tables, n, axis=0)), i32(qsl),
+                                    i32(np.repeat(one.context_lens, n)), 200,
+                                    int(one.context_lens.max()), float(one.scale))
+    torch.cuda.synchronize()
+    for r in range(n):
+        assert torch.equal(out[200 * r:200 * (r + 1)], alone), r
+    assert np.abs(out_f64(alone) - oracle_prefill(one)).max() <= TOL16
+
+
 def test_validation_rejects_a_chunk_longer_than_its_context(monkeypatch):
     c = W.prefill_case(82, 4, 4, 64, [(0, 10), (5, 5)], dtype="bf16")
     monkeypatch.setenv("PKV_VALIDATE", "1")
