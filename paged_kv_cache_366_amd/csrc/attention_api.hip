@@ -33,10 +33,10 @@ constexpr size_t kAlign = 256;
 // Shortest partition the automatic choice takes: below it each workgroup's
 // start (table entries, q) and partial-state write outweigh its keys.
 constexpr int32_t kMinAutoPartition = 256;
-// Prefill workgroups per compute unit the partition choice fills: the LDS
-// staging allows three, but with three the per-step time rises more than
-// the third adds (4 long documents, 16,384 keys each: 512 workgroups
-// 202 us, 768 workgroups 212-215 us, 1,024 236-240 us).
+// Prefill workgroups per compute unit the partition choice fills: a unit
+// holds up to four (two LDS stages), but past two the per-step time rises
+// more than the added workgroups bring (4 long documents, 16,384 keys
+// each: 512 workgroups 197 us, 768 210 us, 1,024 215 us).
 constexpr int kPrefillPerCu = 2;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
