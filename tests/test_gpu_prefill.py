@@ -136,6 +136,25 @@ def test_stage_count_changes_no_bit(dtype):
     assert np.abs(out_f64(alone) - oracle_prefill(one)).max() <= TOL16
 
 
+def test_batches_past_the_ranked_size():
+    """Up to 256 sequences each workgroup ranks the batch by context length
+    (longest first); a larger batch keeps index order.  Both orders give
+    every row its own result: 300 short chunks against the oracle, and the
+    first 200 of them alone (ranked) bit for bit against the same rows."""
+    rng = np.random.default_rng(84)
+    chunks = [(int(p), int(q)) for p, q in zip(rng.integers(0, 90, 300), rng.integers(1, 20, 300))]
+    c = W.prefill_case(84, 4, 2, 128, chunks, dtype="bf16")
+    out = gpu_prefill(c)
+    assert np.abs(out_f64(out) - oracle_prefill(c)).max() <= TOL16
+    n = 200
+    rows = int(c.query_start_loc[n])
+    part = W.prefill_case(84, 4, 2, 128, chunks[:n], dtype="bf16")
+    sub = gpu_prefill(part, q=c.q[:rows], tables=c.block_tables[:n], kc=c.k_cache, vc=c.v_cache)
+    # the same tables, pool and queries: only the batch size differs
+    assert np.array_equal(part.query_start_loc, c.query_start_loc[:n + 1])
+    assert torch.equal(sub, out[:rows])
+
+
 def test_validation_rejects_a_chunk_longer_than_its_context(monkeypatch):
     c = W.prefill_case(82, 4, 4, 64, [(0, 10), (5, 5)], dtype="bf16")
     monkeypatch.setenv("PKV_VALIDATE", "1")
