@@ -180,3 +180,53 @@ def test_reshape_and_cache_and_copy_blocks():
     assert np.array_equal(vb[OFF16:].float().cpu().numpy(), ev)
     del kb, vb
     free()
+
+
+def test_int8_encoder_quantised_writes_and_swaps():
+    """The block encoder, quantise-on-write and swaps to and from a pinned
+    host pool, with the device blocks past 4 GiB of int8 codes (and 9 GB of
+    bf16 source blocks)."""
+    rng = np.random.default_rng(905)
+    nb = 40
+    pk = W.draw_normal(rng, (nb, HKV, BS, D), "bf16")
+    pv = W.draw_normal(rng, (nb, HKV, BS, D), "bf16")
+    sk, sv = to_dev(pk, "bf16"), to_dev(pv, "bf16")
+    skb, svb = big(sk, OFF8), big(sv, OFF8)
+    codes = lambda n: torch.zeros((n, HKV, BS, D), dtype=torch.int8, device=DEV)
+    scales = lambda n: torch.zeros((n, HKV), dtype=torch.float32, device=DEV)
+    dk, dv, ks, vs = codes(nb), codes(nb), scales(nb), scales(nb)
+    dkb, dvb, ksb, vsb = codes(OFF8 + nb), codes(OFF8 + nb), scales(OFF8 + nb), scales(OFF8 + nb)
+    blocks = np.array([3, 17, 0, 39, 22], np.int32)
+    filled = np.array([16, 1, 9, 16, 5], np.int32)
+    pkv.pkv_quantize_blocks(sk, sv, dk, dv, ks, vs, i32(blocks), i32(filled))
+    pkv.pkv_quantize_blocks(skb, svb, dkb, dvb, ksb, vsb, i32(blocks + OFF8), i32(filled))
+    del skb, svb
+    # quantise-on-write: a run continuing block 0 (filled 9), a new block
+    T = 6
+    slots = np.array([9, 10, 11, 5 * BS, 5 * BS + 1, 22 * BS + 5], np.int32)
+    nk = to_dev(W.draw_normal(rng, (T, HKV, D), "bf16"), "bf16")
+    nv = to_dev(W.draw_normal(rng, (T, HKV, D), "bf16"), "bf16")
+    pkv.pkv_reshape_and_cache_int8(nk, nv, dk, dv, ks, vs, i32(slots))
+    pkv.pkv_reshape_and_cache_int8(nk, nv, dkb, dvb, ksb, vsb, i32(slots + OFF8 * BS))
+    torch.cuda.synchronize()
+    assert torch.equal(dkb[OFF8:], dk) and torch.equal(dvb[OFF8:], dv)
+    assert torch.equal(ksb[OFF8:].view(torch.int32), ks.view(torch.int32))
+    assert torch.equal(vsb[OFF8:].view(torch.int32), vs.view(torch.int32))
+    assert not dkb[:OFF8].any().item() and not ksb[:OFF8].any().item()
+    # swap out to a pinned host pool, then back into other device blocks
+    hk = torch.zeros((8, HKV, BS, D), dtype=torch.int8, pin_memory=True)
+    hv = torch.zeros((8, HKV, BS, D), dtype=torch.int8, pin_memory=True)
+    hks = torch.zeros((8, HKV), dtype=torch.float32, pin_memory=True)
+    hvs = torch.zeros((8, HKV), dtype=torch.float32, pin_memory=True)
+    out_pairs = np.array([[3, 0], [17, 1], [22, 2], [0, 7]], np.int32)
+    pkv.pkv_swap_blocks(hk, hv, dkb, dvb, out_pairs + [OFF8, 0], hks, hvs, ksb, vsb)
+    torch.cuda.synchronize()
+    assert torch.equal(hk[[0, 1, 2, 7]], dk[[3, 17, 22, 0]].cpu())
+    assert torch.equal(hks[[0, 1, 2, 7]].view(torch.int32), ks[[3, 17, 22, 0]].cpu().view(torch.int32))
+    in_pairs = np.array([[0, 30], [1, 31], [7, 35]], np.int32)
+    pkv.pkv_swap_blocks(dkb, dvb, hk, hv, in_pairs + [0, OFF8], ksb, vsb, hks, hvs)
+    torch.cuda.synchronize()
+    assert torch.equal(dkb[OFF8 + 30], dk[3]) and torch.equal(dvb[OFF8 + 31], dv[17])
+    assert torch.equal(dkb[OFF8 + 35], dk[0]) and ksb[OFF8 + 31, 0].item() == ks[17, 0].item()
+    del dkb, dvb
+    free()
