@@ -72,6 +72,8 @@
 // arithmetic the longest row tiles (2,048 keys, 64 steps) finish last;
 // 8-wave workgroups (half the K/V traffic) and key partitions (fp32 partial
 // rows) both measured slower.
+#include <atomic>
+
 #include "attention_common.h"
 #include "mfma_common.h"
 
@@ -490,6 +492,23 @@ __global__ __launch_bounds__(kPrefillThreads) PKV_PREFILL_ATTR void prefill_mfma
   }
 }
 
+// Compute units of the current device, looked up once per device.
+int current_compute_units() {
+  constexpr int kDevices = 64;
+  static std::atomic<int> cached[kDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < kDevices) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int c = 0;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (c > 0 && dev < kDevices) cached[dev].store(c, std::memory_order_relaxed);
+  return c;
+}
+
 template <typename T>
 pkv_status launch_t(const AttnArgs& a, int D, int max_tiles, hipStream_t st) {
   const int64_t wgs = static_cast<int64_t>(a.num_seqs) * max_tiles * a.num_parts * a.hq;
@@ -501,10 +520,8 @@ pkv_status launch_t(const AttnArgs& a, int D, int max_tiles, hipStream_t st) {
                        dim3(kPrefillThreads), 0, st, a, max_tiles);
   } else {
     // two stages once the grid has more workgroups than compute units
-    int dev = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess || cus <= 0)
+    const int cus = current_compute_units();
+    if (cus <= 0)
       return fail(PKV_ERR_DEVICE, "chunked prefill (MFMA): no device to size the launch for");
     if (wgs > cus)
       hipLaunchKernelGGL((prefill_mfma_kernel<T, 128, kRowTiles, kGroup, 2>), grid,
