@@ -9,12 +9,16 @@ headline: the 7B-shape decode step (64 sequences, 32 query heads = 32 KV
 heads, head_dim 128, 16-token blocks, contexts uniform on [128, 2048], each
 including the token being decoded; a pool of ceil(1.25 x the blocks needed)
 whose free list starts as a seeded permutation; q/K/V drawn N(0, 1) in fp32
-and rounded to bf16).  One step (timed, inputs resident in HBM):
-reshape_and_cache of the 64 new K/V rows through the slot mapping -> split-K
-paged decode attention (main kernel) -> partition reduce.  `value` is step
-algorithmic bytes (K/V rows every sequence attends to, q, out, the table
-entries and lengths read, the new rows moved by reshape_and_cache) per
-second.  `roofline` is the main kernel's, from HIP events on its stream.
+and rounded to bf16).  One step (timed, inputs resident in HBM) is one
+launch of the decode step kernel: it writes each sequence's new K/V rows at
+its last position through the block table and attends every key, that row
+included (2,048-token partitions cover every context, so there is no split
+and no reduce).  The three-launch form (reshape_and_cache through the slot
+mapping -> split-K decode -> partition reduce) is timed beside it as
+`three_launch_step`.  `value` is step algorithmic bytes (K/V rows every
+sequence attends to, q, out, the table entries and lengths read, the new
+rows written) per second.  `roofline` is the step kernel's, from HIP events
+on its stream.
 
 The same line carries the other four workloads as keys of their own, each
 with its step time, per-kernel times (mean, median, p10, p90), its own
@@ -32,13 +36,16 @@ bounded sample:
                logical bytes (shared blocks once per beam) are reported
                separately against no HBM bound;
   c5_gqa_bf16  16 sequences, 64 query heads over 8 KV heads (group 8,
-               matrix cores), head_dim 128, contexts U[8192, 32768], split-K
-               decode + reduce, bf16 KV, with the partition the library
+               matrix cores), head_dim 128, contexts U[8192, 32768], bf16
+               KV: split-K decode that appends the current token's rows in
+               the same launch, + reduce, with the partition the library
                picks for these lengths (pkv_decode_partition_tokens: the
                shortest whose workgroups fill one round of the resident
                ones; --partition overrides it);
   c5_gqa_int8  the same with int8 KV and per-block fp32 scales (the pool is
-               the library's block encoder output over the bf16 pool).
+               the library's block encoder output over the bf16 pool; the
+               current token goes in by quantise-on-write, then decode +
+               reduce).
 
 Timing: W untimed warm-up steps, then K steps back to back between two
 device synchronisations (the step time), then a second pass of K steps, each
